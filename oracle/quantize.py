@@ -1,0 +1,174 @@
+"""MXFP4 quantizer and dequantizer (oracle; test infrastructure only).
+
+Sources:
+  * "MXFP4", AI Wiki, §Conversion rules: the reference scale is the largest
+    power of two not above the block's max |V_i|, divided by 4 (the largest
+    power of two in E2M1); elements V_i/X are quantized to FP4 with
+    round-to-nearest-ties-to-even and clamped (saturated) to +-6.
+  * "MXFP4", AI Wiki, §Clipping in the reference algorithm: the shared
+    exponent is floor(log2(amax)) - 2, the scaled block max lies in [4, 8), and
+    values that scale into (6, 8) clip to 6 (worked example: amax 7.5 -> X = 1,
+    stored as 6).
+  * "MXFP4", AI Wiki, §Format specification: E8M0 scale (bias 127, range
+    -127..127, NaN code 0xFF poisons the whole block), 32-element blocks.
+  * "MXFP4", AI Wiki, §Use in models / gpt-oss: two FP4 values per byte,
+    block scales stored apart, blocks along the last dimension.
+  * "Training an MoE LLM in MXFP4", summary: hybrid 1D/2D block quantization,
+    randomized Hadamard transform, stochastic rounding.
+
+Steps per block, in the order they are taken (float32 where stated):
+  1. x = float32(source) (bf16 widens exactly).
+  2. optional RHT along the blocking axis (see ``oracle.rht``).
+  3. amax = max |y_i| over the block (1D: 32 elements along K; 2D: the 32x32
+     tile).  A block holding any NaN or +-Inf gets scale 0xFF and all codes 0.
+  4. E = floor(log2 amax) taken exactly from the float32 exponent (subnormals
+     included); e = clamp(E - 2, -127, 127); amax == 0 gives e = -127.
+     Scale byte = e + 127.
+  5. v_i = float32(y_i * 2^-e): one float32 multiply (exact unless the result
+     is a float32 subnormal, which is rounded to nearest even and never flushed).
+  6. Round |v_i| onto the grid {0, .5, 1, 1.5, 2, 3, 4, 6}: |v| >= 6 saturates
+     to 6; otherwise lo <= |v| < hi are the neighbouring grid points and
+     f = (|v| - lo)/(hi - lo) (exact).  RNE: up iff f > 1/2, or f == 1/2 and
+     lo's code is odd (ties go to the even mantissa bit).  SR: up iff
+     r < f * 2^16 for the element's 16 random bits r (``oracle.philox``).
+  7. code = sign(v) << 3 | magnitude index; the sign of a zero is kept.
+  8. two codes per byte, element 2j in the low nibble of byte j.
+
+Readings of points the pages leave open: "flush values below the smallest
+subnormal to zero" is taken as what RNE on the full grid already does
+(|v| <= 0.25 -> 0); the sign of zero is kept; amax == 0 uses the lowest scale;
+NaN/Inf blocks use the NaN scale; SR saturates deterministically above 6.
+"""
+
+import numpy as np
+
+from .formats import BLOCK, E2M1_GRID, E8M0_BIAS, E8M0_NAN, e2m1_decode, e8m0_decode
+from .philox import sr_bits16
+from .rht import rht_forward_f32, rht_inverse_f32
+
+
+def shared_exponent(amax):
+    """e = clamp(floor(log2 amax) - 2, -127, 127) for float32 amax >= 0 (finite);
+    amax == 0 maps to -127.  floor(log2) comes from frexp, which is exact for
+    normal and subnormal float32 inputs."""
+    a = np.asarray(amax, dtype=np.float32)
+    _, ex = np.frexp(a)                      # a = m * 2^ex, m in [0.5, 1)
+    e = (ex.astype(np.int64) - 1) - 2
+    e = np.clip(e, -127, 127)
+    return np.where(a == 0, -127, e)
+
+
+def round_e2m1(v, rounding="rne", r=None):
+    """Round float32 values v (already divided by the block scale) to E2M1 codes."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v).astype(np.float64)
+    sign = np.signbit(v).astype(np.int64)
+    grid = E2M1_GRID                                   # [0, .5, 1, 1.5, 2, 3, 4, 6]
+    i = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 6)
+    lo = grid[i]
+    hi = grid[np.minimum(i + 1, 7)]
+    f = (a - lo) / (hi - lo)
+    if rounding == "rne":
+        up = (f > 0.5) | ((f == 0.5) & (i % 2 == 1))
+    elif rounding == "sr":
+        if r is None:
+            raise ValueError("stochastic rounding needs random bits r")
+        up = np.asarray(r, dtype=np.float64) < f * 65536.0
+    else:
+        raise ValueError(f"unknown rounding {rounding!r}")
+    idx = np.where(a >= 6.0, 7, i + up.astype(np.int64))
+    return (sign << 3) | idx
+
+
+def pack_nibbles(codes):
+    """[R, K] codes 0..15 -> [R, K/2] uint8, element 2j in the low nibble."""
+    c = np.asarray(codes).astype(np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed):
+    """[R, K/2] uint8 -> [R, K] codes."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = p & 0x0F
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
+             seed=0, offset=0):
+    """Quantize a 2-D float array to MXFP4.
+
+    axis="last": blocks along the last dim, output [R, C] with K = C.
+    axis="dim0": blocks along dim 0, output is the quantized transpose [C, R]
+                 (K = R), still with blocks along its last dim.
+    block="1d": one scale per 32 elements along K, scales [rows_out, K/32].
+    block="2d": one scale per 32x32 tile, scales [rows_out/32, K/32].
+    Returns (codes uint8 [rows_out, K/2], scales uint8).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("quantize expects a 2-D array")
+    if axis == "dim0":
+        x = x.T
+    elif axis != "last":
+        raise ValueError(f"unknown axis {axis!r}")
+    rows, K = x.shape
+    if K % BLOCK:
+        raise ValueError("the blocking dimension must be a multiple of 32")
+    if block == "2d" and rows % BLOCK:
+        raise ValueError("2-D blocks need rows_out to be a multiple of 32")
+    nkb = K // BLOCK
+
+    y = x.reshape(rows, nkb, BLOCK)
+    if rht_mask is not None:
+        y = rht_forward_f32(y, rht_mask)
+
+    with np.errstate(invalid="ignore", over="ignore"):
+        finite = np.isfinite(y)
+        absy = np.where(finite, np.abs(y), np.float32(0))
+        if block == "1d":
+            amax = absy.max(axis=-1)                                  # [rows, nkb]
+            bad = ~finite.all(axis=-1)
+        elif block == "2d":
+            amax = absy.reshape(rows // BLOCK, BLOCK, nkb, BLOCK).max(axis=(1, 3))
+            bad = ~finite.reshape(rows // BLOCK, BLOCK, nkb, BLOCK).all(axis=(1, 3))
+        else:
+            raise ValueError(f"unknown block {block!r}")
+
+        e = shared_exponent(amax)
+        scales = np.where(bad, E8M0_NAN, e + E8M0_BIAS).astype(np.uint8)
+
+        if block == "2d":                       # per-element view of the tile scale
+            e_el = np.repeat(e, BLOCK, axis=0)
+            bad_el = np.repeat(bad, BLOCK, axis=0)
+        else:
+            e_el, bad_el = e, bad
+        factor = np.ldexp(np.float32(1.0), (-e_el).astype(np.int32)).astype(np.float32)
+        v = (y * factor[..., None]).astype(np.float32)
+
+        r = None
+        if rounding == "sr":
+            p = (np.arange(rows, dtype=np.uint64)[:, None] * np.uint64(K)
+                 + np.arange(K, dtype=np.uint64)[None, :])
+            r = sr_bits16(p, seed, offset).reshape(rows, nkb, BLOCK)
+        codes = round_e2m1(v, rounding, r)
+        codes = np.where(bad_el[..., None], 0, codes)
+    return pack_nibbles(codes.reshape(rows, K)), scales
+
+
+def dequantize(codes, scales, block="1d", inverse_rht_mask=None, dtype=np.float32):
+    """Decode MXFP4: value = E2M1(code) * 2^(scale - 127); scale 0xFF makes the
+    whole block NaN.  Optional inverse RHT (float32, canonical order)."""
+    vals = e2m1_decode(unpack_nibbles(codes))                       # float64 [R, K]
+    rows, K = vals.shape
+    sc = e8m0_decode(scales)
+    if block == "2d":
+        sc = np.repeat(sc, BLOCK, axis=0)
+    sc = np.repeat(sc, BLOCK, axis=1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        x = vals * sc
+        if inverse_rht_mask is not None:
+            x32 = x.astype(np.float32).reshape(rows, K // BLOCK, BLOCK)
+            return rht_inverse_f32(x32, inverse_rht_mask).reshape(rows, K)
+        return x.astype(dtype)

@@ -1,0 +1,270 @@
+"""Pins for the oracle quantizer.
+
+Each pin comes from the pages or from mathematics independent of the oracle's
+own formulation:
+  * the reference scale rule and its clipping ("MXFP4", AI Wiki, §Conversion
+    rules; §Clipping in the reference algorithm, including the 7.5 -> 6 example
+    and the ~3 % clipped estimate);
+  * RNE / saturation by brute force: nearest of the page's eight E2M1 values,
+    ties to the code with mantissa bit 0 (the page's bit table);
+  * stochastic rounding is unbiased with the binomial variance (closed form);
+  * dim-0 blocking equals last-dim blocking of the transpose; 2-D tiles take
+    their scale from the tile maximum.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from golden_io import e2m1_table, params
+from oracle.formats import BLOCK
+
+
+def _nearest_code_bruteforce(a):
+    """|v| -> magnitude code by exhaustive distance over the page's table;
+    ties go to the code whose mantissa bit (bit 0) is 0; saturate above 6."""
+    table = e2m1_table()
+    best = None
+    for code, val, _ in table:
+        d = abs(a - val)
+        key = (d, code & 1)
+        if best is None or key < best[0]:
+            best = (key, code)
+    return best[1]
+
+
+def _scale_of_block(codes, scales, col):
+    return float(oracle.e8m0_decode(scales[0, col // 32]))
+
+
+# ---------------------------------------------------------------- scale rule
+def test_worked_clipping_example():
+    p = params("clipping_example.txt")
+    amax = float(p["amax"])
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = amax
+    x[0, 1] = 1.0
+    codes, scales = oracle.quantize(x)
+    assert float(oracle.e8m0_decode(scales[0, 0])) == float(p["scale"])
+    deq = oracle.dequantize(codes, scales)
+    assert deq[0, 0] == float(p["stored"])
+    assert deq[0, 1] == 1.0
+
+
+def test_shared_exponent_closed_form_and_block_max_band():
+    rng = np.random.default_rng(1)
+    mags = np.exp(rng.uniform(-80, 80, size=20000)).astype(np.float32)
+    mags = mags[(mags > 0) & np.isfinite(mags)]
+    e = oracle.shared_exponent(mags)
+    expect = np.array([math.floor(math.log2(float(m))) - 2 for m in mags])
+    assert np.array_equal(e, np.clip(expect, -127, 127))
+    ratio = mags.astype(np.float64) / np.ldexp(1.0, e)
+    inrange = (e > -127)
+    assert np.all((ratio[inrange] >= 4.0) & (ratio[inrange] < 8.0))
+
+
+def test_shared_exponent_exact_powers_and_subnormals():
+    for k in range(-149, 128):
+        a = np.float32(2.0 ** k)
+        assert oracle.shared_exponent(a) == max(k - 2, -127)
+        below = np.nextafter(a, np.float32(0))
+        if below > 0:
+            assert oracle.shared_exponent(below) == max(k - 3, -127)
+    assert oracle.shared_exponent(np.float32(0)) == -127
+
+
+def test_scale_rule_on_random_blocks_matches_definition():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((40, 32 * 6)) * np.exp(rng.uniform(-20, 20, (40, 1)))).astype(np.float32)
+    codes, scales = oracle.quantize(x)
+    for r in range(x.shape[0]):
+        for b in range(6):
+            amax = np.abs(x[r, b * 32:(b + 1) * 32]).max()
+            # largest power of two not above amax, divided by 4
+            p2 = 2.0 ** math.floor(math.log2(float(amax)))
+            assert float(oracle.e8m0_decode(scales[r, b])) == p2 / 4
+
+
+def test_clipped_fraction_soft_statistic():
+    """About 3 % of entries land in the clip band (6, 8) ("MXFP4", AI Wiki,
+    §Clipping); accept 1-5 % on Gaussian and Student-t data."""
+    p = params("clipping_example.txt")
+    lo, hi = float(p["clip_band_low"]), float(p["clip_band_high"])
+    rng = np.random.default_rng(3)
+    for x in (rng.standard_normal((512, 1024)), rng.standard_t(3, (512, 1024))):
+        x = x.astype(np.float32)
+        codes, scales = oracle.quantize(x)
+        sc = np.repeat(oracle.e8m0_decode(scales), 32, axis=1)
+        v = np.abs(x) / sc
+        frac = np.mean((v > lo) & (v < hi))
+        assert 0.01 < frac < 0.05
+
+
+# ---------------------------------------------------------------- rounding
+def _grid_probe_values():
+    """Every grid point, every midpoint, +-1..3 float32 ulps around each, the
+    clip band, and the subnormal region."""
+    grid = [v for _, v, _ in e2m1_table()]
+    pts = set(grid)
+    for a, b in zip(grid[:-1], grid[1:]):
+        pts.add((a + b) / 2)
+    pts.update([6.5, 7.0, 7.5, 7.99, 0.1, 0.25, 0.2, 0.3, 0.74, 0.76, 1e-30, 1e-40])
+    out = set()
+    for p in pts:
+        f = np.float32(p)
+        out.add(float(f))
+        up, dn = f, f
+        for _ in range(3):
+            up = np.nextafter(up, np.float32(np.inf))
+            dn = np.nextafter(dn, np.float32(0))
+            out.add(float(up))
+            out.add(float(dn))
+    return sorted(v for v in out if v < 8.0)
+
+
+def test_rne_bruteforce_over_grid_midpoints_and_clip_band():
+    vals = np.array(_grid_probe_values(), dtype=np.float32)
+    got = oracle.round_e2m1(vals, "rne")
+    for v, c in zip(vals, got):
+        assert c == _nearest_code_bruteforce(float(v)), float(v)
+    got_neg = oracle.round_e2m1(-vals, "rne")
+    assert np.array_equal(got_neg, got | 8)
+
+
+def test_rne_specific_ties():
+    ties = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for v, expect in ties.items():
+        c = oracle.round_e2m1(np.float32(v), "rne")
+        assert oracle.e2m1_decode(c) == expect, v
+
+
+def test_signed_zero_and_saturation():
+    c = oracle.round_e2m1(np.array([-0.0, 0.0, -0.1, 1e9, -1e9], dtype=np.float32), "rne")
+    assert list(c) == [8, 0, 8, 7, 15]
+
+
+def test_nonfinite_and_zero_blocks():
+    x = np.zeros((3, 64), dtype=np.float32)
+    x[1, 3] = np.nan
+    x[2, 40] = np.inf
+    x[2, 0] = 1.0
+    x[1, 33] = -2.0
+    codes, scales = oracle.quantize(x)
+    assert scales[0, 0] == 0 and scales[0, 1] == 0        # amax 0 -> lowest scale
+    assert scales[1, 0] == 0xFF and scales[2, 1] == 0xFF
+    assert scales[1, 1] == 126                            # amax 2 -> e = -1
+    assert np.all(oracle.unpack_nibbles(codes)[1, :32] == 0)
+    assert np.all(oracle.unpack_nibbles(codes)[2, 32:] == 0)
+    deq = oracle.dequantize(codes, scales)
+    assert np.isnan(deq[1, :32]).all() and np.isnan(deq[2, 32:]).all()
+    assert deq[1, 33] == -2.0 and deq[2, 0] == 1.0
+
+
+def test_dequantize_error_bound_unclipped():
+    """|x - deq(q(x))| <= half a grid step at that magnitude times the scale,
+    except in the clip band where it is |x| - 6X."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((128, 256)).astype(np.float32)
+    codes, scales = oracle.quantize(x)
+    deq = oracle.dequantize(codes, scales).astype(np.float64)
+    sc = np.repeat(oracle.e8m0_decode(scales), 32, axis=1)
+    v = np.abs(x) / sc
+    step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
+    err = np.abs(x - deq) / sc
+    clip = v > 6
+    assert np.all(err[~clip] <= step[~clip] / 2)
+    assert np.allclose(err[clip], v[clip] - 6.0)
+
+
+def test_subnormal_scaled_value_not_flushed():
+    """A float32 product landing in the subnormal range is rounded, not flushed:
+    its sign survives (-0 code) and in SR it can still round up with r = 0."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = np.float32(2.0 ** 120)
+    x[0, 1] = -np.float32(2.0 ** -10)          # v = -2^-128, a float32 subnormal
+    codes, scales = oracle.quantize(x)
+    c = oracle.unpack_nibbles(codes)[0]
+    assert c[1] == 8
+    r = np.zeros(32, dtype=np.uint32)
+    v = np.zeros(32, dtype=np.float32)
+    v[1] = np.float32(-(2.0 ** -128))
+    assert oracle.round_e2m1(v, "sr", r)[1] == 9      # r = 0 < f * 2^16 > 0
+
+
+# ---------------------------------------------------------------- layouts
+def test_nibble_order_low_first():
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 4.0      # scale 1 -> code 6
+    x[0, 1] = 1.0      # code 2
+    codes, scales = oracle.quantize(x)
+    assert codes[0, 0] == 0x26
+
+
+def test_dim0_equals_transpose_last_rne_and_sr():
+    rng = np.random.default_rng(5)
+    x = rng.standard_t(3, (96, 64)).astype(np.float32)
+    for kw in ({}, {"rounding": "sr", "seed": 123456789, "offset": 7},
+               {"rht_mask": 0xA5A5F00F}, {"block": "2d"}):
+        a = oracle.quantize(x, axis="dim0", **kw)
+        b = oracle.quantize(np.ascontiguousarray(x.T), axis="last", **kw)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_2d_scale_is_tile_max():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((64, 96)).astype(np.float32)
+    x[5, 70] = 300.0
+    codes, scales = oracle.quantize(x, block="2d")
+    assert scales.shape == (2, 3)
+    for tr in range(2):
+        for tc in range(3):
+            amax = np.abs(x[tr * 32:(tr + 1) * 32, tc * 32:(tc + 1) * 32]).max()
+            assert float(oracle.e8m0_decode(scales[tr, tc])) == 2.0 ** math.floor(math.log2(amax)) / 4
+    # every element decodes against its tile's scale
+    deq = oracle.dequantize(codes, scales, block="2d")
+    assert abs(deq[5, 70] - 256.0) < 1e-9       # 300 / 64 = 4.69 -> 4 -> 256
+
+
+def test_2d_transpose_consistency_rne():
+    rng = np.random.default_rng(8)
+    w = rng.standard_normal((64, 96)).astype(np.float32)
+    c1, s1 = oracle.quantize(w, axis="dim0", block="2d")        # quantized W^T
+    c2, s2 = oracle.quantize(w, axis="last", block="2d")        # quantized W
+    d1 = oracle.dequantize(c1, s1, block="2d")
+    d2 = oracle.dequantize(c2, s2, block="2d")
+    assert np.array_equal(s1, s2.T)
+    assert np.array_equal(d1, d2.T)
+
+
+# ---------------------------------------------------------------- stochastic rounding
+@pytest.mark.parametrize("v", [0.1, 0.3, 0.6, 1.2, 1.7, 2.25, 3.9, 4.5, 5.99])
+def test_sr_unbiased_with_binomial_variance(v):
+    n = 200_000
+    rng = np.random.default_rng(int(v * 1000))
+    r = rng.integers(0, 65536, size=n).astype(np.uint32)
+    vals = np.full(n, v, dtype=np.float32)
+    got = oracle.e2m1_decode(oracle.round_e2m1(vals, "sr", r))
+    grid = [g for _, g, _ in e2m1_table()]
+    lo = max(g for g in grid if g <= v)
+    hi = min(g for g in grid if g > v)
+    assert set(np.unique(got)) <= {lo, hi}
+    sigma = math.sqrt((float(np.float32(v)) - lo) * (hi - float(np.float32(v))))
+    tol = 5 * sigma / math.sqrt(n) + (hi - lo) * 2.0 ** -16
+    assert abs(got.mean() - float(np.float32(v))) <= tol
+    assert abs(got.var() - sigma ** 2) <= 0.05 * sigma ** 2 + 1e-6
+
+
+def test_sr_quantize_unbiased_end_to_end():
+    """Mean over many Philox offsets of the SR-dequantized tensor -> x."""
+    rng = np.random.default_rng(9)
+    x = (rng.uniform(-5.9, 5.9, (4, 32))).astype(np.float32)
+    x[:, 0] = 5.95                          # pin the scale to 1 in every block
+    acc = np.zeros_like(x, dtype=np.float64)
+    n = 3000
+    for off in range(n):
+        c, s = oracle.quantize(x, rounding="sr", seed=42, offset=off)
+        acc += oracle.dequantize(c, s).astype(np.float64)
+    mean = acc / n
+    # each element's sd <= max step / 2 = 1; 5-sigma bound
+    assert np.max(np.abs(mean - x)) <= 5 * 1.0 / math.sqrt(n) + 2 * 2.0 ** -16
