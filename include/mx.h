@@ -1,0 +1,186 @@
+/*
+ * libmxfp4 — OCP MX v1.0 MXFP4 quantizer and block-scaled GEMMs for MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument marked "device" is a device (HBM) pointer that
+ * the caller owns; the library never allocates, frees or synchronizes.  Every
+ * call only validates its arguments on the host and enqueues kernels on
+ * `stream` (a hipStream_t; NULL = the null stream), so it returns before the
+ * GPU work finishes.  On an invalid argument a call returns a non-zero
+ * mx_status, records a message for mx_last_error() and launches nothing; a
+ * launch failure reported by the HIP runtime returns MX_ERR_HIP.  No C++
+ * exception crosses this interface.
+ *
+ * Data format ("MXFP4", AI Wiki, §Format specification; §Use in models /
+ * gpt-oss):
+ *   - a block is 32 elements sharing one E8M0 scale byte (value 2^(s-127),
+ *     s = 0xFF is NaN and poisons the whole block);
+ *   - elements are 4-bit E2M1 codes (bit 3 sign, 2 exponent bits, 1 mantissa
+ *     bit, bias 1: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6);
+ *   - an MX operand is K-major: `codes` is [rows, K/2] bytes with element 2j of
+ *     a row in the low nibble of byte j and element 2j+1 in the high nibble;
+ *     `scales` is stored apart, [rows, K/32] bytes for 1-D blocks (32
+ *     consecutive elements of a row) or [rows/32, K/32] bytes for 2-D blocks
+ *     (32x32 tiles of 32 rows by 32 elements).
+ *   136 bits per 1-D block: 4.25 bits per value.
+ */
+#ifndef LIBMXFP4_MX_H
+#define LIBMXFP4_MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_INVALID_ARG = 1,  /* bad shape, stride, pointer, alignment or enum */
+  MX_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement   */
+  MX_ERR_HIP = 3           /* the HIP runtime reported an error             */
+} mx_status;
+
+typedef enum { MX_DT_F32 = 0, MX_DT_BF16 = 1 } mx_dtype;
+
+/* Blocking axis of the SOURCE tensor [R, C] given to mx_quantize. */
+typedef enum {
+  MX_AXIS_LAST = 0,  /* blocks along C: output [R, C], K = C                      */
+  MX_AXIS_DIM0 = 1   /* blocks along R: output is the quantized transpose [C, R], K = R */
+} mx_axis;
+
+typedef enum { MX_BLOCK_1D = 0, MX_BLOCK_2D = 1 } mx_block;
+
+typedef enum {
+  MX_ROUND_RNE = 0,  /* round to nearest, ties to even mantissa bit, saturate at +-6 */
+  MX_ROUND_SR = 1    /* stochastic rounding with Philox4x32-10 bits, saturate at +-6  */
+} mx_round;
+
+/* One MXFP4 operand, K-major (see the format notes above).  All fields are
+ * read-only to the library; the buffers are the caller's. */
+typedef struct {
+  uint8_t* codes;     /* device; [rows, K/2] bytes, row stride ld_codes bytes       */
+  uint8_t* scales;    /* device; 1-D: [rows, K/32]; 2-D: [rows/32, K/32]; row stride ld_scales bytes */
+  int64_t rows;       /* logical rows (M or N of a GEMM)                            */
+  int64_t K;          /* logical elements per row, a multiple of 32                  */
+  int64_t ld_codes;   /* bytes between rows of codes, >= K/2                         */
+  int64_t ld_scales;  /* bytes between rows of scales, >= K/32                       */
+  int32_t block;      /* mx_block                                                    */
+  int32_t reserved;   /* must be 0                                                   */
+} mx_tensor;
+
+/* Quantizer settings. */
+typedef struct {
+  int32_t axis;            /* mx_axis                                             */
+  int32_t block;           /* mx_block                                            */
+  int32_t rounding;        /* mx_round                                            */
+  int32_t use_rht;         /* 1: apply the 32-point randomized Hadamard transform */
+  uint32_t rht_sign_mask;  /* bit i set: negate element i of every block first   */
+  uint32_t reserved;       /* must be 0                                           */
+  uint64_t philox_seed;    /* SR: Philox key = (seed mod 2^32, seed >> 32)        */
+  uint64_t philox_offset;  /* SR: counter words 2,3 = (offset mod 2^32, offset >> 32) */
+} mx_quant_cfg;
+
+/*
+ * mx_quantize — MXFP4 conversion of a bf16/fp32 tensor.
+ *
+ * Follows "MXFP4", AI Wiki, §Conversion rules and §Clipping in the reference
+ * algorithm: per block, the shared exponent is floor(log2(amax)) - 2 clamped
+ * to [-127, 127] (scale byte = exponent + 127; amax = 0 gives byte 0; a block
+ * holding NaN or Inf gets byte 0xFF and all-zero codes); each element is
+ * divided by the scale with one float32 multiply and rounded to E2M1 by RNE
+ * (ties to the even mantissa bit, saturating to +-6, sign of zero kept) or by
+ * stochastic rounding.  Options from "MXFP4", AI Wiki, §Training with MXFP4
+ * and "Training an MoE LLM in MXFP4" (summary): the 32-point randomized
+ * Hadamard transform y = c*H32*(d.x) (Sylvester order, d from rht_sign_mask,
+ * c = float32(1/sqrt(32)), float32 stages h = 1,2,4,8,16 then the multiply by
+ * c), stochastic rounding (element p = row_out*K + k of the output uses the
+ * 16-bit half (p & 1) of word ((p >> 1) & 3) of Philox4x32-10 with counter
+ * (q mod 2^32, q >> 32, offset mod 2^32, offset >> 32), q = p >> 3, and rounds
+ * up iff those bits r satisfy r < f*2^16 for the fraction f of the way from
+ * the lower to the upper grid point), and 1-D or 2-D (32x32) blocks.
+ *
+ *   src      device; R x C elements of src_dtype (mx_dtype), row stride ld_src
+ *            ELEMENTS (>= C), 16-byte aligned base, ld_src a multiple of 8.
+ *   cfg      host; quantizer settings.
+ *   out      host struct describing device buffers the caller allocated:
+ *            rows = R (LAST) or C (DIM0), K = C (LAST) or R (DIM0),
+ *            block = cfg->block, ld_codes >= K/2, ld_scales >= K/32,
+ *            codes 16-byte aligned with ld_codes a multiple of 16.
+ *   Requires K % 32 == 0; 2-D blocks need rows % 32 == 0.  R = 0 or C = 0 is
+ *   a no-op.  Reads only src, writes only out's buffers.
+ */
+mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
+                      const mx_quant_cfg* cfg, const mx_tensor* out, void* stream);
+
+/*
+ * mx_dequantize — decode an MXFP4 operand: value = E2M1(code) * 2^(scale-127)
+ * ("MXFP4", AI Wiki, §Format specification: X times P_i; NaN scale makes the
+ * whole block NaN).  With inverse_rht = 1 the 32-point transform is undone per
+ * block along K in float32: the stages h = 1,2,4,8,16, the multiply by c, then
+ * the sign flips of rht_sign_mask.
+ *
+ *   in       host struct of device buffers (any 1-D/2-D operand).
+ *   dst      device; [in->rows, in->K] of dst_dtype, row stride ld_dst elements
+ *            (>= K), 16-byte aligned, ld_dst a multiple of 8.  bf16 output is
+ *            rounded to nearest even from the float32 value.
+ */
+mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_sign_mask,
+                        void* dst, int32_t dst_dtype, int64_t ld_dst, void* stream);
+
+/*
+ * mx_gemm — C[m, n] = sum_k A[m, k] * B[n, k] for MXFP4 operands A [M, K] and
+ * B [N, K] (both K-major), per "MXFP4", AI Wiki, §Conversion rules: each block
+ * pair contributes X(A) X(B) sum_i P_i(A) P_i(B) and a long dot product is the
+ * sum of block dot products, accumulated in float32 (the order of that float32
+ * sum is the library's); groups of 32 run along the contraction dimension
+ * ("MXFP4", AI Wiki, §Hardware support: scales applied inside the matrix
+ * instruction, float32 or bf16 output).  Runs on gfx950's scaled FP4 MFMA.
+ *
+ *   A, B       host structs of device buffers; A->K == B->K; either may use
+ *              1-D or 2-D scales (2-D requires rows % 32 == 0).
+ *   C          device; [M, N] of c_dtype, row stride ldc elements (>= N).
+ *   workspace  device scratch of ws_bytes bytes, needed only when
+ *              mx_gemm_workspace_size(M, N, K) > 0 (split-K partial sums);
+ *              otherwise may be NULL.
+ *   M, N or K = 0: C is left untouched (K = 0 writes zeros).
+ */
+mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace mx_gemm needs for this problem (0 if none). */
+size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * mx_grouped_gemm — the MoE expert GEMM over rows grouped by expert ("MXFP4",
+ * AI Wiki, §Software support and §Use in models: MoE weights stored in
+ * MXFP4): rows [off[e], off[e+1]) of A and of C belong to expert e, and
+ * C[r, n] = sum_k A[r, k] * B_e[n, k], with the same block arithmetic as
+ * mx_gemm.
+ *
+ *   A                host struct; A->rows is the capacity (rows of A and C).
+ *   d_group_offsets  device; int32 [E+1], off[0] = 0, non-decreasing, read on
+ *                    the device (no host synchronization).  Offsets above
+ *                    A->rows are clamped to A->rows; rows past off[E] are not
+ *                    written.
+ *   E                number of experts (>= 1).
+ *   B                host struct for expert 0: rows = N, K, block, strides;
+ *                    expert e's codes start at B->codes + e*expert_stride_codes
+ *                    bytes and its scales at B->scales + e*expert_stride_scales.
+ *   C                device; [A->rows, N] of c_dtype, row stride ldc.
+ */
+mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, int32_t E,
+                          const mx_tensor* B, int64_t expert_stride_codes,
+                          int64_t expert_stride_scales, void* C, int32_t c_dtype, int64_t ldc,
+                          void* stream);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* mx_last_error(void);
+
+/* Library version string. */
+const char* mx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMXFP4_MX_H */

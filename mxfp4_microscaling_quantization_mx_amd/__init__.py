@@ -1,0 +1,193 @@
+"""MI355X-native MXFP4 (OCP MX v1.0) quantizer and block-scaled GEMMs.
+
+A thin ctypes binding over ``libmxfp4.so`` (declared in ``include/mx.h``).
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  The binding only allocates
+output tensors and marshals pointers, shapes and strides.  If the library is
+missing, every call raises: there is no fallback path.
+
+    q = quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None)
+    y = dequantize(q, torch.float32)
+    c = gemm(qa, qb, torch.bfloat16)                    # C = A * B^T
+    c = grouped_gemm(qa, offsets, qb_stacked, torch.bfloat16)
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxfp4.so")
+
+MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 0, 1, 2, 3
+MX_DT_F32, MX_DT_BF16 = 0, 1
+_AXIS = {"last": 0, "dim0": 1}
+_BLOCK = {"1d": 0, "2d": 1}
+_ROUND = {"rne": 0, "sr": 1}
+_DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
+
+EXPORTED = ("mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
+            "mx_grouped_gemm", "mx_last_error", "mx_version")
+
+
+class MxTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("ld_codes", ctypes.c_int64), ("ld_scales", ctypes.c_int64),
+                ("block", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class QuantCfgC(ctypes.Structure):
+    _fields_ = [("axis", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("rounding", ctypes.c_int32), ("use_rht", ctypes.c_int32),
+                ("rht_sign_mask", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("philox_seed", ctypes.c_uint64), ("philox_offset", ctypes.c_uint64)]
+
+
+class MXError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"libmxfp4 status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libmxfp4.so and declare its signatures (no GPU is touched)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m mxfp4_microscaling_quantization_mx_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+    PT = ctypes.POINTER(MxTensorC)
+    lib.mx_quantize.argtypes = [P, I32, I64, I64, I64, ctypes.POINTER(QuantCfgC), PT, P]
+    lib.mx_dequantize.argtypes = [PT, I32, U32, P, I32, I64, P]
+    lib.mx_gemm.argtypes = [PT, PT, P, I32, I64, P, ctypes.c_size_t, P]
+    lib.mx_gemm_workspace_size.argtypes = [I64, I64, I64]
+    lib.mx_gemm_workspace_size.restype = ctypes.c_size_t
+    lib.mx_grouped_gemm.argtypes = [PT, P, I32, PT, I64, I64, P, I32, I64, P]
+    for f in ("mx_quantize", "mx_dequantize", "mx_gemm", "mx_grouped_gemm"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.mx_last_error.restype = ctypes.c_char_p
+    lib.mx_last_error.argtypes = []
+    lib.mx_version.restype = ctypes.c_char_p
+    lib.mx_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != MX_OK:
+        raise MXError(status, _lib.mx_last_error().decode())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+@dataclass
+class MXTensor:
+    """K-major MXFP4 operand: codes uint8 [rows, K/2], scales uint8 [rows, K/32]
+    (1-D) or [rows/32, K/32] (2-D).  Row strides are taken from the tensors."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    K: int
+    block: str = "1d"
+
+    def c_struct(self):
+        return MxTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.rows, self.K,
+                         self.codes.stride(0) if self.codes.dim() == 2 else self.K // 2,
+                         self.scales.stride(0) if self.scales.dim() == 2 else self.K // 32,
+                         _BLOCK[self.block], 0)
+
+
+def empty_mx(rows, K, block="1d", device="cuda"):
+    """Allocate an uninitialised MX operand (codes + scales) on `device`."""
+    srows = rows // 32 if block == "2d" else rows
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((srows, K // 32), dtype=torch.uint8, device=device)
+    return MXTensor(codes, scales, rows, K, block)
+
+
+def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None, seed=0, offset=0,
+             out=None):
+    """Quantize a 2-D bf16/fp32 CUDA tensor to MXFP4 (see mx_quantize in include/mx.h).
+
+    axis="dim0" blocks along dim 0 and returns the quantized transpose."""
+    lib = load_library()
+    if x.dim() != 2 or x.dtype not in _DTYPE or not x.is_cuda:
+        raise ValueError("quantize expects a 2-D bf16/float32 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("quantize expects a row-major tensor (stride(1) == 1)")
+    R, C = x.shape
+    rows, K = (C, R) if axis == "dim0" else (R, C)
+    if out is None:
+        out = empty_mx(rows, K, block, x.device)
+    cfg = QuantCfgC(_AXIS[axis], _BLOCK[block], _ROUND[rounding], int(rht_mask is not None),
+                    (rht_mask or 0) & 0xFFFFFFFF, 0, seed & (2**64 - 1), offset & (2**64 - 1))
+    ot = out.c_struct()
+    _check(lib.mx_quantize(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), ctypes.byref(cfg),
+                           ctypes.byref(ot), _stream(x)))
+    return out
+
+
+def dequantize(q, dtype=torch.float32, inverse_rht_mask=None, out=None):
+    """Decode an MX operand to a [rows, K] tensor (see mx_dequantize)."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty((q.rows, q.K), dtype=dtype, device=q.codes.device)
+    qt = q.c_struct()
+    _check(lib.mx_dequantize(ctypes.byref(qt), int(inverse_rht_mask is not None),
+                             (inverse_rht_mask or 0) & 0xFFFFFFFF, _ptr(out), _DTYPE[out.dtype],
+                             out.stride(0), _stream(out)))
+    return out
+
+
+def gemm(a, b, out_dtype=torch.float32, out=None, workspace=None):
+    """C = A * B^T for MX operands A [M, K], B [N, K] (see mx_gemm)."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+    ws = lib.mx_gemm_workspace_size(a.rows, b.rows, a.K)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=a.codes.device)
+    at, bt = a.c_struct(), b.c_struct()
+    _check(lib.mx_gemm(ctypes.byref(at), ctypes.byref(bt), _ptr(out), _DTYPE[out.dtype],
+                       out.stride(0), _ptr(workspace), ws, _stream(out)))
+    return out
+
+
+def grouped_gemm(a, offsets, b, out_dtype=torch.bfloat16, out=None):
+    """MoE grouped GEMM (see mx_grouped_gemm).
+
+    a: MXTensor [M, K] with rows grouped by expert; offsets: int32 CUDA tensor
+    [E+1]; b: MXTensor whose codes are [E, N, K/2] and scales [E, N/32, K/32]
+    (2-D) or [E, N, K/32] (1-D)."""
+    lib = load_library()
+    E = b.codes.shape[0]
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.numel() != E + 1:
+        raise ValueError("offsets must be an int32 CUDA tensor with E+1 entries")
+    N = b.codes.shape[1]
+    if out is None:
+        out = torch.empty((a.rows, N), dtype=out_dtype, device=a.codes.device)
+    b0 = MxTensorC(b.codes.data_ptr(), b.scales.data_ptr(), N, b.K, b.codes.stride(1),
+                   b.scales.stride(1), _BLOCK[b.block], 0)
+    at = a.c_struct()
+    _check(lib.mx_grouped_gemm(ctypes.byref(at), _ptr(offsets), E, ctypes.byref(b0),
+                               b.codes.stride(0), b.scales.stride(0), _ptr(out),
+                               _DTYPE[out.dtype], out.stride(0), _stream(out)))
+    return out
+
+
+def version():
+    return load_library().mx_version().decode()

@@ -1,0 +1,63 @@
+"""Build libmxfp4.so (and the test probe library) in-tree with hipcc for gfx950.
+
+    python -m mxfp4_microscaling_quantization_mx_amd.build
+
+Every HIP translation unit is compiled with packed-FP32 instruction selection
+disabled and without floating-point contraction, so the quantizer's float32
+operations happen exactly in the order written.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmxfp4.so")
+PROBE_SRC = os.path.join(ROOT, "tests", "gpu_probes.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "libmxprobe.so")
+
+ARCH = os.environ.get("MX_OFFLOAD_ARCH", "gfx950")
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+CFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-ffp-contract=off", "-Wall", "-Wno-unused-function",
+]
+SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "gemm.hip"]
+
+
+def _run(cmd):
+    print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def _compile(src, obj):
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    _run([HIPCC] + CFLAGS + lang + ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj])
+
+
+def build(verbose=True):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for s in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
+        _compile(os.path.join(CSRC, s), obj)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    if os.path.exists(PROBE_SRC):
+        pobj = os.path.join(BUILD, "gpu_probes.o")
+        _compile(PROBE_SRC, pobj)
+        tmp = PROBE_LIB + ".tmp"
+        _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, pobj])
+        os.replace(tmp, PROBE_LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

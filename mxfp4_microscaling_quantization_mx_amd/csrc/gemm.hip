@@ -1,0 +1,241 @@
+// Block-scaled MXFP4 GEMM and grouped (MoE) GEMM for gfx950.
+//
+// C[m, n] = sum_kb 2^(sa[m,kb]-127) 2^(sb[n,kb]-127) sum_{j<32} P_a P_b
+// ("MXFP4", AI Wiki, §Conversion rules: block dot products X(A) X(B) sum P P,
+// summed over blocks; §Hardware support: 32-element groups along the
+// contraction dimension, scales applied inside the matrix instruction, float32
+// accumulation).  The inner products run on V_MFMA_SCALE_F32_32X32X64_F8F6F4
+// with both operands in FP4 (E2M1) and one E8M0 scale per lane:
+//   lane l holds row (l % 32) of A (column of B) and the 32 K-elements
+//   [32*(l/32), 32*(l/32)+32) of the 64-deep step, i.e. exactly one MX block,
+//   16 bytes; its scale byte is picked from a 32-bit register by op_sel;
+//   the 32x32 float32 result: lane l, register r holds
+//   row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.
+//
+// Tiling: a 256-thread workgroup computes a 128x128 tile with 4 waves (2x2),
+// each wave 64x64 = 2x2 MFMA tiles.  Per 128-deep K stage the workgroup stages
+// 128 rows x 64 bytes of A and of B codes in LDS (row pitch 80 bytes) plus one
+// 32-bit word of 4 scale bytes per row.  Rows past M/N and K past the end are
+// zero codes with scale 1.0, so they add exact zeros (a NaN scale there would
+// otherwise poison the sums).
+#include "mx_device.h"
+#include "mx_launch.h"
+
+namespace mx {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128, BN = 128;
+constexpr int BK = 128;                 // K elements per LDS stage
+constexpr int ROWB = BK / 2;            // code bytes per row per stage
+constexpr int PITCH = ROWB + 16;        // LDS row pitch in bytes
+
+struct Smem {
+  uint8_t a[BM * PITCH];
+  uint8_t b[BN * PITCH];
+  uint32_t sa[BM];
+  uint32_t sb[BN];
+};
+
+// Stage rows [r0, r0 + 128) x K-stage k0 of one operand into LDS.
+template <bool TWO_D>
+__device__ __forceinline__ void stage_operand(const MxOperand& op, int64_t r0, int64_t rows,
+                                              int64_t k0, int64_t K, uint8_t* lds_codes,
+                                              uint32_t* lds_scales, int tid, int stid) {
+  // 128 rows x 4 chunks of 16 bytes: 2 chunks per thread.
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int id = tid + 256 * it;
+    const int r = id >> 2, ch = id & 3;
+    const int64_t gr = r0 + r;
+    const int64_t kk = k0 + 32 * ch;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (gr < rows && kk < K)
+      v = *reinterpret_cast<const uint4*>(op.codes + gr * op.ld_codes + (kk >> 1));
+    *reinterpret_cast<uint4*>(lds_codes + r * PITCH + ch * 16) = v;
+  }
+  // Threads with stid in [0, 128) fetch the 4 scale bytes of one row each.
+  if (stid >= 0 && stid < 128) {
+    const int64_t gr = r0 + stid;
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t kb = (k0 >> 5) + j;
+      uint32_t s = 127u;
+      if (gr < rows && kb * 32 < K) s = op.scales[(TWO_D ? (gr >> 5) : gr) * op.ld_scales + kb];
+      w |= s << (8 * j);
+    }
+    lds_scales[stid] = w;
+  }
+}
+
+template <bool A2D, bool B2D, bool OUT_BF16>
+__device__ __forceinline__ void gemm_tile(const MxOperand& A, const MxOperand& B, int64_t M,
+                                          int64_t N, int64_t K, int64_t m0, int64_t n0, void* C,
+                                          int64_t ldc, Smem& sm) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  for (int64_t k0 = 0; k0 < K; k0 += BK) {
+    stage_operand<A2D>(A, m0, M, k0, K, sm.a, sm.sa, tid, tid);
+    stage_operand<B2D>(B, n0, N, k0, K, sm.b, sm.sb, tid, tid - 128);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v8i a[2], b[2];
+      int sa[2], sb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + l32;
+        const uint4 v = *reinterpret_cast<const uint4*>(sm.a + r * PITCH + 32 * ks + 16 * hi);
+        a[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        sa[i] = (int)(sm.sa[r] >> (8 * hi));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + l32;
+        const uint4 v = *reinterpret_cast<const uint4*>(sm.b + r * PITCH + 32 * ks + 16 * hi);
+        b[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        sb[j] = (int)(sm.sb[r] >> (8 * hi));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (ks == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 0,
+                                                                         sa[i], 0, sb[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 2,
+                                                                         sa[i], 2, sb[j]);
+        }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds column l32; register r holds row 8*(r/4) + 4*hi + r%4.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn * 64 + j * 32 + l32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (row < M) {
+          if (OUT_BF16)
+            static_cast<uint16_t*>(C)[row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+          else
+            static_cast<float*>(C)[row * ldc + col] = acc[i][j][r];
+        }
+      }
+    }
+}
+
+template <bool A2D, bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_gemm(MxOperand A, MxOperand B, int64_t M, int64_t N,
+                                              int64_t K, void* C, int64_t ldc) {
+  __shared__ Smem sm;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  gemm_tile<A2D, B2D, OUT_BF16>(A, B, M, N, K, m0, n0, C, ldc, sm);
+}
+
+// Grouped GEMM: the flat grid enumerates (m-tile slot, n-tile); each
+// workgroup maps its slot to (expert, m-tile within the expert) from the
+// device offsets, so the schedule needs no host synchronization.  Slots past
+// the total number of tiles exit.
+template <bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_grouped_gemm(MxOperand A, MxOperand B, int64_t M_cap,
+                                                      int64_t N, int64_t K,
+                                                      const int32_t* __restrict__ offsets, int E,
+                                                      int64_t stride_codes, int64_t stride_scales,
+                                                      void* C, int64_t ldc) {
+  __shared__ Smem sm;
+  __shared__ int s_expert, s_row0, s_rows;
+  const int64_t slot = blockIdx.y;
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  if (threadIdx.x == 0) {
+    int64_t acc_tiles = 0;
+    int ex = -1, r0 = 0, nr = 0;
+    for (int e = 0; e < E; ++e) {
+      int64_t lo = offsets[e], hi = offsets[e + 1];
+      lo = lo < 0 ? 0 : (lo > M_cap ? M_cap : lo);
+      hi = hi < lo ? lo : (hi > M_cap ? M_cap : hi);
+      const int64_t tiles = (hi - lo + BM - 1) / BM;
+      if (slot < acc_tiles + tiles) {
+        ex = e;
+        r0 = (int)(lo + (slot - acc_tiles) * BM);
+        nr = (int)(hi - r0 < BM ? hi - r0 : BM);
+        break;
+      }
+      acc_tiles += tiles;
+    }
+    s_expert = ex;
+    s_row0 = r0;
+    s_rows = nr;
+  }
+  __syncthreads();
+  const int ex = s_expert;
+  if (ex < 0) return;
+  MxOperand Ae = A;
+  Ae.codes = A.codes + (int64_t)s_row0 * A.ld_codes;
+  Ae.scales = A.scales + (int64_t)s_row0 * A.ld_scales;
+  MxOperand Be = B;
+  Be.codes = B.codes + (int64_t)ex * stride_codes;
+  Be.scales = B.scales + (int64_t)ex * stride_scales;
+  void* Ce = OUT_BF16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)s_row0 * ldc)
+                      : (void*)(static_cast<float*>(C) + (int64_t)s_row0 * ldc);
+  gemm_tile<false, B2D, OUT_BF16>(Ae, Be, s_rows, N, K, 0, n0, Ce, ldc, sm);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
+#define MX_G(A_, B_, O_) \
+  hipLaunchKernelGGL((k_gemm<A_, B_, O_>), grid, dim3(256), 0, st, a.A, a.B, a.M, a.N, a.K, a.C, a.ldc)
+  if (a.out_bf16) {
+    if (a.a_2d) { if (a.b_2d) MX_G(true, true, true); else MX_G(true, false, true); }
+    else { if (a.b_2d) MX_G(false, true, true); else MX_G(false, false, true); }
+  } else {
+    if (a.a_2d) { if (a.b_2d) MX_G(true, true, false); else MX_G(true, false, false); }
+    else { if (a.b_2d) MX_G(false, true, false); else MX_G(false, false, false); }
+  }
+#undef MX_G
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st) {
+  if (a.M_cap == 0 || a.N == 0) return hipSuccess;
+  // Upper bound on m-tiles over all experts: each expert adds at most one partial tile.
+  const int64_t slots = (a.M_cap + BM - 1) / BM + a.E;
+  dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)slots);
+#define MX_GG(B_, O_)                                                                          \
+  hipLaunchKernelGGL((k_grouped_gemm<B_, O_>), grid, dim3(256), 0, st, a.A, a.B, a.M_cap, a.N, a.K, \
+                     a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc)
+  if (a.out_bf16) {
+    if (a.b_2d) MX_GG(true, true); else MX_GG(false, true);
+  } else {
+    if (a.b_2d) MX_GG(true, false); else MX_GG(false, false);
+  }
+#undef MX_GG
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,231 @@
+// C-ABI entry points of libmxfp4: argument validation, error reporting and
+// dispatch to the kernel launchers.  Declarations and the contract of every
+// entry point are in include/mx.h.
+#include "../../include/mx.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "mx_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mx_status fail(mx_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mx_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MX_OK;
+  return fail(MX_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validate one MX operand description; `what` names it in messages.
+mx_status check_tensor(const mx_tensor* t, const char* what) {
+  if (!t) return fail(MX_ERR_INVALID_ARG, "%s: null mx_tensor", what);
+  if (t->rows < 0 || t->K < 0) return fail(MX_ERR_INVALID_ARG, "%s: negative shape", what);
+  if (t->K % 32) return fail(MX_ERR_INVALID_ARG, "%s: K=%lld is not a multiple of 32", what, (long long)t->K);
+  if (t->block != MX_BLOCK_1D && t->block != MX_BLOCK_2D)
+    return fail(MX_ERR_INVALID_ARG, "%s: unknown block kind %d", what, t->block);
+  if (t->reserved != 0) return fail(MX_ERR_INVALID_ARG, "%s: reserved field must be 0", what);
+  if (t->block == MX_BLOCK_2D && t->rows % 32)
+    return fail(MX_ERR_INVALID_ARG, "%s: 2-D blocks need rows %% 32 == 0 (rows=%lld)", what, (long long)t->rows);
+  if (t->rows == 0 || t->K == 0) return MX_OK;
+  if (!t->codes || !t->scales) return fail(MX_ERR_INVALID_ARG, "%s: null codes/scales pointer", what);
+  if (t->ld_codes < t->K / 2 || t->ld_scales < t->K / 32)
+    return fail(MX_ERR_INVALID_ARG, "%s: row strides too small (ld_codes=%lld, ld_scales=%lld)", what,
+                (long long)t->ld_codes, (long long)t->ld_scales);
+  if (!aligned(t->codes, 16) || t->ld_codes % 16)
+    return fail(MX_ERR_INVALID_ARG, "%s: codes must be 16-byte aligned with ld_codes %% 16 == 0", what);
+  return MX_OK;
+}
+
+mx::MxOperand operand(const mx_tensor* t) {
+  return mx::MxOperand{t->codes, t->scales, t->ld_codes, t->ld_scales};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_last_error(void) { return g_err; }
+
+const char* mx_version(void) { return "libmxfp4 0.1.0 (gfx950)"; }
+
+mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
+                      const mx_quant_cfg* cfg, const mx_tensor* out, void* stream) {
+  g_err[0] = '\0';
+  if (!cfg || !out) return fail(MX_ERR_INVALID_ARG, "mx_quantize: null cfg or out");
+  if (src_dtype != MX_DT_F32 && src_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown source dtype %d", src_dtype);
+  if (cfg->axis != MX_AXIS_LAST && cfg->axis != MX_AXIS_DIM0)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown axis %d", cfg->axis);
+  if (cfg->rounding != MX_ROUND_RNE && cfg->rounding != MX_ROUND_SR)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown rounding %d", cfg->rounding);
+  if (cfg->block != MX_BLOCK_1D && cfg->block != MX_BLOCK_2D)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown block kind %d", cfg->block);
+  if (cfg->use_rht != 0 && cfg->use_rht != 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: use_rht must be 0 or 1");
+  if (cfg->reserved != 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize: cfg reserved field must be 0");
+  if (R < 0 || C < 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize: negative shape");
+  const bool dim0 = cfg->axis == MX_AXIS_DIM0;
+  const int64_t rows_out = dim0 ? C : R;
+  const int64_t K = dim0 ? R : C;
+  if (K % 32) return fail(MX_ERR_INVALID_ARG, "mx_quantize: blocking dimension %lld is not a multiple of 32", (long long)K);
+  if (out->rows != rows_out || out->K != K)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: out is [%lld, %lld], expected [%lld, %lld]",
+                (long long)out->rows, (long long)out->K, (long long)rows_out, (long long)K);
+  if (out->block != cfg->block) return fail(MX_ERR_INVALID_ARG, "mx_quantize: out->block differs from cfg->block");
+  mx_status st = check_tensor(out, "mx_quantize: out");
+  if (st != MX_OK) return st;
+  if (R == 0 || C == 0) return MX_OK;
+  if (!src) return fail(MX_ERR_INVALID_ARG, "mx_quantize: null src");
+  if (ld_src < C) return fail(MX_ERR_INVALID_ARG, "mx_quantize: ld_src=%lld < C=%lld", (long long)ld_src, (long long)C);
+  if (!aligned(src, 16) || ld_src % 8)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: src must be 16-byte aligned with ld_src %% 8 == 0");
+  if (dim0 && (R + 127) / 128 > 65535)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: dim-0 blocking supports at most 65535*128 source rows");
+  if (!dim0 && cfg->block == MX_BLOCK_2D && (R + 63) / 64 > 65535)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: 2-D blocking supports at most 65535*64 rows");
+
+  mx::QuantArgs a{};
+  a.src = src;
+  a.R = R;
+  a.C = C;
+  a.ld_src = ld_src;
+  a.bf16 = src_dtype == MX_DT_BF16;
+  a.dim0 = dim0;
+  a.two_d = cfg->block == MX_BLOCK_2D;
+  a.rht = cfg->use_rht == 1;
+  a.sr = cfg->rounding == MX_ROUND_SR;
+  a.mask = cfg->rht_sign_mask;
+  a.seed = cfg->philox_seed;
+  a.offset = cfg->philox_offset;
+  a.codes = out->codes;
+  a.ld_codes = out->ld_codes;
+  a.scales = out->scales;
+  a.ld_scales = out->ld_scales;
+  return hip_status(mx::launch_quantize(a, static_cast<hipStream_t>(stream)), "mx_quantize");
+}
+
+mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_sign_mask, void* dst,
+                        int32_t dst_dtype, int64_t ld_dst, void* stream) {
+  g_err[0] = '\0';
+  mx_status st = check_tensor(in, "mx_dequantize: in");
+  if (st != MX_OK) return st;
+  if (dst_dtype != MX_DT_F32 && dst_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "mx_dequantize: unknown destination dtype %d", dst_dtype);
+  if (inverse_rht != 0 && inverse_rht != 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_dequantize: inverse_rht must be 0 or 1");
+  if (in->rows == 0 || in->K == 0) return MX_OK;
+  if (!dst) return fail(MX_ERR_INVALID_ARG, "mx_dequantize: null dst");
+  if (ld_dst < in->K || ld_dst % 8 || !aligned(dst, 16))
+    return fail(MX_ERR_INVALID_ARG, "mx_dequantize: dst must be 16-byte aligned with ld_dst >= K and ld_dst %% 8 == 0");
+  mx::DequantArgs a{};
+  a.codes = in->codes;
+  a.scales = in->scales;
+  a.rows = in->rows;
+  a.K = in->K;
+  a.ld_codes = in->ld_codes;
+  a.ld_scales = in->ld_scales;
+  a.two_d = in->block == MX_BLOCK_2D;
+  a.inverse_rht = inverse_rht == 1;
+  a.mask = rht_sign_mask;
+  a.dst = dst;
+  a.out_bf16 = dst_dtype == MX_DT_BF16;
+  a.ld_dst = ld_dst;
+  return hip_status(mx::launch_dequantize(a, static_cast<hipStream_t>(stream)), "mx_dequantize");
+}
+
+size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = '\0';
+  (void)workspace;
+  (void)ws_bytes;
+  mx_status st = check_tensor(A, "mx_gemm: A");
+  if (st != MX_OK) return st;
+  st = check_tensor(B, "mx_gemm: B");
+  if (st != MX_OK) return st;
+  if (A->K != B->K)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm: A.K=%lld != B.K=%lld", (long long)A->K, (long long)B->K);
+  if (c_dtype != MX_DT_F32 && c_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm: unknown output dtype %d", c_dtype);
+  const int64_t M = A->rows, N = B->rows;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!C) return fail(MX_ERR_INVALID_ARG, "mx_gemm: null C");
+  if (ldc < N) return fail(MX_ERR_INVALID_ARG, "mx_gemm: ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+  if ((M + 127) / 128 > 65535) return fail(MX_ERR_UNSUPPORTED, "mx_gemm: M too large");
+  mx::GemmArgs a{};
+  a.A = operand(A);
+  a.B = operand(B);
+  a.a_2d = A->block == MX_BLOCK_2D;
+  a.b_2d = B->block == MX_BLOCK_2D;
+  a.M = M;
+  a.N = N;
+  a.K = A->K;
+  a.C = C;
+  a.ldc = ldc;
+  a.out_bf16 = c_dtype == MX_DT_BF16;
+  return hip_status(mx::launch_gemm(a, static_cast<hipStream_t>(stream)), "mx_gemm");
+}
+
+mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, int32_t E,
+                          const mx_tensor* B, int64_t expert_stride_codes,
+                          int64_t expert_stride_scales, void* C, int32_t c_dtype, int64_t ldc,
+                          void* stream) {
+  g_err[0] = '\0';
+  mx_status st = check_tensor(A, "mx_grouped_gemm: A");
+  if (st != MX_OK) return st;
+  st = check_tensor(B, "mx_grouped_gemm: B");
+  if (st != MX_OK) return st;
+  if (A->block != MX_BLOCK_1D)
+    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: A must use 1-D blocks (expert boundaries are arbitrary rows)");
+  if (A->K != B->K)
+    return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: A.K=%lld != B.K=%lld", (long long)A->K, (long long)B->K);
+  if (E < 1) return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: E=%d < 1", E);
+  if (!d_group_offsets) return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: null group offsets");
+  if (c_dtype != MX_DT_F32 && c_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: unknown output dtype %d", c_dtype);
+  if (expert_stride_codes < 0 || expert_stride_scales < 0 || expert_stride_codes % 16)
+    return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: expert strides must be >= 0 (codes stride %% 16 == 0)");
+  const int64_t M = A->rows, N = B->rows;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!C) return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: null C");
+  if (ldc < N) return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+  if ((M + 127) / 128 + E > 65535) return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: too many row tiles");
+  mx::GroupedGemmArgs a{};
+  a.A = operand(A);
+  a.B = operand(B);
+  a.a_2d = false;
+  a.b_2d = B->block == MX_BLOCK_2D;
+  a.M_cap = M;
+  a.N = N;
+  a.K = A->K;
+  a.offsets = d_group_offsets;
+  a.E = E;
+  a.stride_codes = expert_stride_codes;
+  a.stride_scales = expert_stride_scales;
+  a.C = C;
+  a.ldc = ldc;
+  a.out_bf16 = c_dtype == MX_DT_BF16;
+  return hip_status(mx::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)), "mx_grouped_gemm");
+}
+
+}  // extern "C"

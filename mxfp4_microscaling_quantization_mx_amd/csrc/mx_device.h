@@ -1,0 +1,198 @@
+// Device helpers shared by the libmxfp4 kernels (gfx950 / CDNA4).
+//
+// Format facts used here ("MXFP4", AI Wiki, §Format specification and
+// §Conversion rules): E2M1 codes carry magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 in
+// code order 0..7 with the sign in bit 3; E8M0 scale byte s means 2^(s-127)
+// and 0xFF is NaN; the reference shared exponent is floor(log2 amax) - 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// ---------------------------------------------------------------- bit helpers
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return ((b >> 16) | 0x40u) & 0xFFFFu;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Cross-lane reads inside a quad of 4 lanes (DPP quad_perm, one VALU op).
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);   // [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);   // [2,3,0,1]
+}
+__device__ __forceinline__ float quad_xor1f(float v) { return __uint_as_float(quad_xor1(__float_as_uint(v))); }
+__device__ __forceinline__ float quad_xor2f(float v) { return __uint_as_float(quad_xor2(__float_as_uint(v))); }
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Salmon et al., SC'11: ten rounds of two 32x32->64 multiplies, key bumped by
+// the Weyl constants between rounds.
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// The 8 x 16-bit stochastic-rounding draws of Philox call q (elements 8q..8q+7
+// of the output in row-major [rows_out, K] order): element t takes half (t & 1)
+// of word (t >> 1).
+__device__ __forceinline__ void sr_draws8(uint64_t q, uint64_t seed, uint64_t offset, uint32_t r[8]) {
+  u32x4 w = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), (uint32_t)offset,
+                          (uint32_t)(offset >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
+  r[0] = w.x & 0xFFFFu; r[1] = w.x >> 16;
+  r[2] = w.y & 0xFFFFu; r[3] = w.y >> 16;
+  r[4] = w.z & 0xFFFFu; r[5] = w.z >> 16;
+  r[6] = w.w & 0xFFFFu; r[7] = w.w >> 16;
+}
+
+// ---------------------------------------------------------------- scale
+// Scale byte from the largest |y| of a block given as float32 bits with the
+// sign cleared: NaN/Inf -> 0xFF; otherwise biased_exponent(amax) - 2 clamped
+// at 0 (this is floor(log2 amax) - 2 + 127, and covers zero and subnormal
+// amax, whose floor(log2) is below -126).
+__device__ __forceinline__ uint32_t scale_code_from_absmax_bits(uint32_t m) {
+  if (m >= 0x7F800000u) return 0xFFu;
+  const int be = (int)(m >> 23);
+  return (uint32_t)(be > 2 ? be - 2 : 0);
+}
+
+// 2^-(s-127) as float32 for a finite scale byte s <= 252 (always a normal).
+__device__ __forceinline__ float inv_scale_from_code(uint32_t s) {
+  return __uint_as_float((254u - s) << 23);
+}
+
+// ---------------------------------------------------------------- E2M1 rounding
+// v is already divided by the block scale (|v| < 8 for a finite block).
+// Integer form of round-to-nearest-even onto {0,.5,1,1.5,2,3,4,6}:
+//  |v| >= 1: the E2M1 grid is float32 with one mantissa bit, so round the
+//            float32 bits at bit 22 (ties to an even bit 22) and read the code
+//            from the exponent and that bit; codes above 7 saturate to 7.
+//  |v| <  1: step 0.5; (0.25, 0.75) -> 0.5, [0.75, 1) -> 1.0, ties 0.25 -> 0
+//            and 0.75 -> 1.0 (both even mantissa).
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sgn = (b >> 28) & 8u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t idx;
+  if (a >= 0x3F800000u) {
+    const uint32_t t = (a + 0x1FFFFFu + ((a >> 22) & 1u)) >> 22;
+    idx = min(t - 252u, 7u);
+  } else {
+    idx = (uint32_t)(a > 0x3E800000u) + (uint32_t)(a >= 0x3F400000u);
+  }
+  return sgn | idx;
+}
+
+// Stochastic rounding with a 16-bit draw r: the magnitude rounds up from the
+// lower grid point lo to the upper one iff r < f * 2^16, where f is the exact
+// fraction of the way from lo to the next grid point; |v| >= 6 saturates.
+//  |v| >= 1   : lo from the truncated bits, f * 2^22 = the 22 bits below bit 22.
+//  .5 <= |v| < 1: lo = .5, f * 2^23 = the 23 mantissa bits.
+//  |v| < .5   : lo = 0, f = 2|v|; compare in float32 (exact, power-of-two scaling).
+__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t r) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sgn = (b >> 28) & 8u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t idx;
+  if (a >= 0x3F800000u) {
+    const uint32_t lo = (a >> 22) - 252u;
+    idx = min(lo + (uint32_t)((r << 6) < (a & 0x3FFFFFu)), 7u);
+  } else if (a >= 0x3F000000u) {
+    idx = 1u + (uint32_t)((r << 7) < (a & 0x7FFFFFu));
+  } else {
+    idx = (uint32_t)((float)r < __uint_as_float(a) * 131072.0f);
+  }
+  return sgn | idx;
+}
+
+// E2M1 magnitude of a 4-bit code as float32 (sign applied).
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  const uint32_t m = code & 7u;
+  uint32_t bits = (m >= 2u) ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22))
+                            : (m == 1u ? 0x3F000000u : 0u);
+  return __uint_as_float(bits | ((code & 8u) << 28));
+}
+
+// 2^(s-127) as float32 for a scale byte (s = 0 gives the subnormal 2^-127,
+// s = 0xFF gives NaN).
+__device__ __forceinline__ float scale_value(uint32_t s) {
+  if (s == 0xFFu) return __uint_as_float(0x7FC00000u);
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+
+// ---------------------------------------------------------------- Hadamard
+// Radix-2 butterflies of the 32-point fast Walsh-Hadamard transform in
+// Sylvester order: stage h maps (x_i, x_{i+h}) -> (x_i + x_{i+h}, x_i - x_{i+h})
+// for i & h == 0.  Stages 1, 2, 4 act inside 8 consecutive elements.
+__device__ __forceinline__ void fwht8_inlane(float x[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// Stages 8 and 16 when lane j of a quad holds elements 8j..8j+7 of the block:
+// the partner of element i is in lane j ^ 1 (h = 8) or j ^ 2 (h = 16); the lane
+// holding the lower index keeps the sum, the other keeps lower - upper.
+__device__ __forceinline__ void fwht_cross_quad(float x[8], uint32_t quad_lane) {
+  const bool up8 = quad_lane & 1u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = quad_xor1f(x[i]);
+    x[i] = up8 ? (p - x[i]) : (x[i] + p);
+  }
+  const bool up16 = quad_lane & 2u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = quad_xor2f(x[i]);
+    x[i] = up16 ? (p - x[i]) : (x[i] + p);
+  }
+}
+
+// All five stages for a block held by one lane.
+__device__ __forceinline__ void fwht32_inlane(float x[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+}
+
+constexpr uint32_t kRhtCBits = 0x3E3504F3u;   // float32(1/sqrt(32))
+
+}  // namespace mx

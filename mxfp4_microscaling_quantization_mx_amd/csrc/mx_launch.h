@@ -1,0 +1,71 @@
+// Internal launch interface between the C-ABI layer (mx_api.cpp) and the
+// kernel translation units.  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+struct QuantArgs {
+  const void* src;
+  int64_t R, C, ld_src;       // source [R, C], row stride in elements
+  bool bf16;                  // else float32
+  bool dim0;                  // blocks along dim 0 (output = quantized transpose)
+  bool two_d;                 // 32x32 tiles
+  bool rht;
+  bool sr;
+  uint32_t mask;
+  uint64_t seed, offset;
+  uint8_t* codes;
+  int64_t ld_codes;
+  uint8_t* scales;
+  int64_t ld_scales;
+};
+
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t rows, K, ld_codes, ld_scales;
+  bool two_d;
+  bool inverse_rht;
+  uint32_t mask;
+  void* dst;
+  bool out_bf16;
+  int64_t ld_dst;
+};
+
+// One MX operand as the GEMM kernels see it.
+struct MxOperand {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t ld_codes, ld_scales;
+};
+
+struct GemmArgs {
+  MxOperand A, B;
+  bool a_2d, b_2d;
+  int64_t M, N, K;
+  void* C;
+  int64_t ldc;
+  bool out_bf16;
+};
+
+struct GroupedGemmArgs {
+  MxOperand A, B;             // B = expert 0
+  bool a_2d, b_2d;
+  int64_t M_cap, N, K;
+  const int32_t* offsets;     // device, E+1
+  int32_t E;
+  int64_t stride_codes, stride_scales;
+  void* C;
+  int64_t ldc;
+  bool out_bf16;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st);
+
+}  // namespace mx

@@ -1,0 +1,256 @@
+// MXFP4 quantizer kernels for gfx950.
+//
+// Method ("MXFP4", AI Wiki, §Conversion rules and §Clipping in the reference
+// algorithm; options from §Training with MXFP4 and "Training an MoE LLM in
+// MXFP4", summary): per 32-element block (or 32x32 tile) take amax, set the
+// E8M0 exponent to floor(log2 amax) - 2, divide by the scale with one float32
+// multiply, round to E2M1 by RNE or stochastic rounding, saturate at +-6, and
+// optionally rotate each block by the 32-point randomized Hadamard transform
+// first.  The kernels are bound by HBM bandwidth: 2 bytes in (bf16) and 0.53
+// bytes out per element.
+//
+// Two kernel families:
+//  * k_quant_rows_1d — blocks along the contiguous dim.  A quad of 4 lanes
+//    owns one block, 8 elements per lane, so each wave reads 1 KiB of
+//    consecutive bf16 with one 16-byte load per lane and writes 256 consecutive
+//    code bytes.  Hadamard stages 1/2/4 run inside a lane, stages 8/16 across
+//    the quad with DPP quad permutes; amax is a lane max plus two DPP steps.
+//  * k_quant_tile — one lane per block, fed from an LDS tile.  Used for blocks
+//    along dim 0 (the transposed output that wgrad and K x N weights need) and
+//    for 2-D 32x32 tiles, whose amax is a reduction over 32 lanes.
+#include "mx_device.h"
+#include "mx_launch.h"
+
+namespace mx {
+
+namespace {
+
+// ------------------------------------------------------------------ loads
+// 8 consecutive source elements widened to float32, with the Hadamard sign
+// flips applied as an XOR of the sign bits (exact).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* __restrict__ src, int64_t idx, float x[8],
+                                      uint32_t sgn8) {
+  if (BF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + idx);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // bit 15 flips the even element, bit 31 the odd one
+      const uint32_t flip = (((sgn8 >> (2 * i)) & 1u) << 15) | (((sgn8 >> (2 * i + 1)) & 1u) << 31);
+      const uint32_t v = ww[i] ^ flip;
+      x[2 * i] = bf16lo(v);
+      x[2 * i + 1] = bf16hi(v);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + idx);
+    const float4 a = p[0], b = p[1];
+    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(__float_as_uint(f[i]) ^ (((sgn8 >> i) & 1u) << 31));
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* __restrict__ src, int64_t idx) {
+  if (BF16) return bf16lo(static_cast<const uint16_t*>(src)[idx]);
+  return static_cast<const float*>(src)[idx];
+}
+
+// ------------------------------------------------------------------ rows, 1-D
+template <bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ src, int64_t R,
+                                                       int64_t C, int64_t ld_src,
+                                                       uint8_t* __restrict__ codes, int64_t ld_codes,
+                                                       uint8_t* __restrict__ scales,
+                                                       int64_t ld_scales, uint32_t mask,
+                                                       uint64_t seed, uint64_t offset) {
+  const int64_t lanes_per_row = C >> 3;          // multiple of 4 since C % 32 == 0
+  const int64_t total = R * lanes_per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // The grid stride is a multiple of 4, so a lane's position in its quad (and
+  // hence which 8 elements of the block it holds) never changes.
+  const uint32_t ql = threadIdx.x & 3u;
+  const uint32_t sgn8 = RHT ? (mask >> (8 * ql)) & 0xFFu : 0u;
+  const float c = __uint_as_float(kRhtCBits);
+
+  for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l < total; l += stride) {
+    const int64_t row = l / lanes_per_row;
+    const int64_t col0 = (l - row * lanes_per_row) << 3;
+    float x[8];
+    load8<BF16>(src, row * ld_src + col0, x, sgn8);
+    if (RHT) {
+      fwht8_inlane(x);
+      fwht_cross_quad(x, ql);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = x[i] * c;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    m = max(m, quad_xor1(m));
+    m = max(m, quad_xor2(m));
+    const uint32_t s = scale_code_from_absmax_bits(m);
+    uint32_t packed = 0;
+    if (s != 0xFFu) {
+      const float inv = inv_scale_from_code(s);
+      uint32_t r[8];
+      if (SR) sr_draws8((uint64_t)(row * C + col0) >> 3, seed, offset, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = x[i] * inv;
+        packed |= (SR ? e2m1_sr(v, r[i]) : e2m1_rne(v)) << (4 * i);
+      }
+    }
+    *reinterpret_cast<uint32_t*>(codes + row * ld_codes + (col0 >> 1)) = packed;
+    if (ql == 0) scales[row * ld_scales + (col0 >> 5)] = (uint8_t)s;
+  }
+}
+
+// ------------------------------------------------------------------ LDS tiles
+// TRANS: source tile of 128 rows x 64 columns; output rows are source columns
+//        (lane -> column), K runs along source rows (wave w -> K-block w).
+// !TRANS: source tile of 64 rows x 128 columns; lane -> row, wave w -> K-block w.
+template <bool TRANS>
+struct TileShape {
+  static constexpr int TR = TRANS ? 128 : 64;   // source rows per tile
+  static constexpr int TC = TRANS ? 64 : 128;   // source cols per tile
+  static constexpr int LD = TRANS ? 64 : 129;   // LDS row pitch in floats (bank-conflict free reads)
+};
+
+template <bool TRANS, bool TWO_D, bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src, int64_t R,
+                                                    int64_t C, int64_t ld_src,
+                                                    uint8_t* __restrict__ codes, int64_t ld_codes,
+                                                    uint8_t* __restrict__ scales,
+                                                    int64_t ld_scales, uint32_t mask,
+                                                    uint64_t seed, uint64_t offset) {
+  using S = TileShape<TRANS>;
+  __shared__ float tile[S::TR * S::LD];
+
+  const int64_t r0 = (int64_t)blockIdx.y * S::TR;
+  const int64_t c0 = (int64_t)blockIdx.x * S::TC;
+
+  // Stage the tile: 8 consecutive columns per load, TC/8 loads per row.
+  constexpr int CHUNKS = S::TR * S::TC / 8;
+#pragma unroll
+  for (int it = 0; it < CHUNKS / 256; ++it) {
+    const int id = threadIdx.x + 256 * it;
+    const int tr = id / (S::TC / 8);
+    const int tc = (id % (S::TC / 8)) * 8;
+    const int64_t gr = r0 + tr, gc = c0 + tc;
+    float x[8];
+    if (gr < R && gc + 8 <= C) {
+      load8<BF16>(src, gr * ld_src + gc, x, 0u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        x[i] = (gr < R && gc + i < C) ? load1<BF16>(src, gr * ld_src + gc + i) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[tr * S::LD + tc + i] = x[i];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  // Output coordinates of this lane's block.
+  const int64_t K = TRANS ? R : C;
+  const int64_t orow = TRANS ? c0 + lane : r0 + lane;
+  const int64_t kb = (TRANS ? r0 : c0) / 32 + w;
+  const bool valid = (TRANS ? (orow < C) : (orow < R)) && (kb * 32 < K);
+
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    x[i] = TRANS ? tile[(w * 32 + i) * S::LD + lane] : tile[lane * S::LD + w * 32 + i];
+  if (RHT) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((mask >> i) & 1u) << 31));
+    fwht32_inlane(x);
+    const float c = __uint_as_float(kRhtCBits);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = x[i] * c;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  if (!valid) m = 0;
+  if (TWO_D) {
+    // amax over the 32x32 tile = over the 32 lanes of this half-wave.
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
+  }
+  if (!valid) return;
+  const uint32_t s = scale_code_from_absmax_bits(m);
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+  if (s != 0xFFu) {
+    const float inv = inv_scale_from_code(s);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t r[8];
+      if (SR) sr_draws8((uint64_t)(orow * K + kb * 32) / 8 + g, seed, offset, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = x[8 * g + i] * inv;
+        packed[g] |= (SR ? e2m1_sr(v, r[i]) : e2m1_rne(v)) << (4 * i);
+      }
+    }
+  }
+  *reinterpret_cast<uint4*>(codes + orow * ld_codes + kb * 16) =
+      make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  if (!TWO_D) {
+    scales[orow * ld_scales + kb] = (uint8_t)s;
+  } else if ((orow & 31) == 0) {
+    scales[(orow >> 5) * ld_scales + kb] = (uint8_t)s;
+  }
+}
+
+template <bool TRANS, bool TWO_D, bool BF16>
+hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
+  using S = TileShape<TRANS>;
+  dim3 grid((unsigned)((a.C + S::TC - 1) / S::TC), (unsigned)((a.R + S::TR - 1) / S::TR));
+#define MX_TILE(RHT_, SR_)                                                                   \
+  hipLaunchKernelGGL((k_quant_tile<TRANS, TWO_D, BF16, RHT_, SR_>), grid, dim3(256), 0, st, \
+                     a.src, a.R, a.C, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales,  \
+                     a.mask, a.seed, a.offset)
+  if (a.rht) {
+    if (a.sr) MX_TILE(true, true); else MX_TILE(true, false);
+  } else {
+    if (a.sr) MX_TILE(false, true); else MX_TILE(false, false);
+  }
+#undef MX_TILE
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
+  const int64_t lanes = a.R * (a.C / 8);
+  int64_t blocks = (lanes + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;     // grid-stride beyond 64 waves per CU
+#define MX_ROWS(RHT_, SR_)                                                                  \
+  hipLaunchKernelGGL((k_quant_rows_1d<BF16, RHT_, SR_>), dim3((unsigned)blocks), dim3(256), 0, \
+                     st, a.src, a.R, a.C, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, \
+                     a.mask, a.seed, a.offset)
+  if (a.rht) {
+    if (a.sr) MX_ROWS(true, true); else MX_ROWS(true, false);
+  } else {
+    if (a.sr) MX_ROWS(false, true); else MX_ROWS(false, false);
+  }
+#undef MX_ROWS
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
+  if (a.R == 0 || a.C == 0) return hipSuccess;
+  if (!a.dim0 && !a.two_d) return a.bf16 ? launch_rows_1d<true>(a, st) : launch_rows_1d<false>(a, st);
+  if (a.dim0) {
+    if (a.two_d) return a.bf16 ? launch_tile<true, true, true>(a, st) : launch_tile<true, true, false>(a, st);
+    return a.bf16 ? launch_tile<true, false, true>(a, st) : launch_tile<true, false, false>(a, st);
+  }
+  return a.bf16 ? launch_tile<false, true, true>(a, st) : launch_tile<false, true, false>(a, st);
+}
+
+}  // namespace mx

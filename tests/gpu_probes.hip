@@ -1,0 +1,94 @@
+// Test-only probes of gfx950 builtins used by libmxfp4 (not part of the library).
+//
+//  * probe_mfma_scale_32x32x64 / probe_mfma_scale_16x16x128: run one scaled
+//    FP4 MFMA on one wave with per-lane operand registers and scale words
+//    supplied by the caller, and write the raw accumulator registers, so the
+//    tests can check the operand, scale and result lane layouts against a
+//    NumPy model.
+//  * probe_cvt_fp4_sweep: compare the hardware packed FP4 conversion (scale
+//    1.0) with the library's software RNE rounding over every float32 bit
+//    pattern in [lo, hi), counting mismatches and recording the first few.
+// Every launch is one grid over fixed-size buffers the caller allocated.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../mxfp4_microscaling_quantization_mx_amd/csrc/mx_device.h"
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__global__ void k_mfma32(const int* a, const int* b, const int* sa, const int* sb, float* out) {
+  const int l = threadIdx.x;
+  v8i av, bv;
+  for (int i = 0; i < 8; ++i) { av[i] = a[l * 8 + i]; bv[i] = b[l * 8 + i]; }
+  v16f acc;
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, sa[l], 0, sb[l]);
+  for (int i = 0; i < 16; ++i) out[l * 16 + i] = acc[i];
+}
+
+__global__ void k_mfma32_opsel2(const int* a, const int* b, const int* sa, const int* sb, float* out) {
+  const int l = threadIdx.x;
+  v8i av, bv;
+  for (int i = 0; i < 8; ++i) { av[i] = a[l * 8 + i]; bv[i] = b[l * 8 + i]; }
+  v16f acc;
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 2, sa[l], 2, sb[l]);
+  for (int i = 0; i < 16; ++i) out[l * 16 + i] = acc[i];
+}
+
+__global__ void k_mfma16(const int* a, const int* b, const int* sa, const int* sb, float* out) {
+  const int l = threadIdx.x;
+  v8i av, bv;
+  for (int i = 0; i < 8; ++i) { av[i] = a[l * 8 + i]; bv[i] = b[l * 8 + i]; }
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, sa[l], 0, sb[l]);
+  for (int i = 0; i < 4; ++i) out[l * 4 + i] = acc[i];
+}
+
+// Each thread walks a strided subset of [lo, hi); pairs (x, -x) go through the
+// hardware conversion and through mx::e2m1_rne.
+__global__ void k_cvt_sweep(uint64_t lo, uint64_t hi, unsigned long long* mismatches,
+                            uint32_t* first, uint32_t first_cap) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  unsigned long long local = 0;
+  for (uint64_t u = lo + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < hi; u += stride) {
+    const float x = __uint_as_float((uint32_t)u);
+    const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x, -x, 1.0f, 0) & 0xFFu;
+    const uint32_t sw = mx::e2m1_rne(x) | (mx::e2m1_rne(-x) << 4);
+    if (hw != sw) {
+      ++local;
+      const unsigned long long k = atomicAdd(mismatches + 1, 1ull);
+      if (k < first_cap) {
+        first[2 * k] = (uint32_t)u;
+        first[2 * k + 1] = hw | (sw << 8);
+      }
+    }
+  }
+  if (local) atomicAdd(mismatches, local);
+}
+
+extern "C" {
+
+int probe_mfma_scale_32x32x64(const int* a, const int* b, const int* sa, const int* sb, float* out,
+                              int opsel2) {
+  if (opsel2)
+    hipLaunchKernelGGL(k_mfma32_opsel2, dim3(1), dim3(64), 0, 0, a, b, sa, sb, out);
+  else
+    hipLaunchKernelGGL(k_mfma32, dim3(1), dim3(64), 0, 0, a, b, sa, sb, out);
+  return (int)hipGetLastError();
+}
+
+int probe_mfma_scale_16x16x128(const int* a, const int* b, const int* sa, const int* sb, float* out) {
+  hipLaunchKernelGGL(k_mfma16, dim3(1), dim3(64), 0, 0, a, b, sa, sb, out);
+  return (int)hipGetLastError();
+}
+
+int probe_cvt_fp4_sweep(uint64_t lo, uint64_t hi, unsigned long long* mismatches, uint32_t* first,
+                        uint32_t first_cap) {
+  hipLaunchKernelGGL(k_cvt_sweep, dim3(4096), dim3(256), 0, 0, lo, hi, mismatches, first, first_cap);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

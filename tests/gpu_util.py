@@ -1,0 +1,87 @@
+"""Shared helpers for the GPU parity tests (comparison rules and plumbing)."""
+import ctypes
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROBE_LIB = os.path.join(ROOT, "tests", "libmxprobe.so")
+OUT_DIR = os.path.join(ROOT, "gpurun_out")
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def banner(msg):
+    """Name the case on stdout before a GPU step (flushed)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def codes_equal(gpu_codes, ora_codes, what):
+    g = np.asarray(gpu_codes)
+    o = np.asarray(ora_codes)
+    assert g.shape == o.shape, (what, g.shape, o.shape)
+    if not np.array_equal(g, o):
+        bad = np.argwhere(g != o)
+        r, c = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} byte mismatches; first at {tuple(bad[0])}: "
+                             f"gpu={g[r, c]:#04x} oracle={o[r, c]:#04x}")
+
+
+def bf16_half_ulp(x):
+    """Half a bfloat16 ulp at |x| (8 significant bits)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.ldexp(1.0, (e - 8).astype(np.int64)), 0.0)
+
+
+def check_gemm(c, ref, bound, bf16=False, what="gemm"):
+    """|C - ref| <= 1e-5 * sum|a_k b_k| per element; bf16 outputs additionally
+    allow their own rounding (half an ulp of the larger of |C|, |ref|).
+    NaN positions must agree."""
+    c = np.asarray(c, dtype=np.float64)
+    nan_c, nan_r = np.isnan(c), np.isnan(ref)
+    assert np.array_equal(nan_c, nan_r), f"{what}: NaN pattern differs ({nan_c.sum()} vs {nan_r.sum()})"
+    ok = ~nan_r
+    tol = 1e-5 * bound[ok]
+    if bf16:
+        tol = tol + bf16_half_ulp(np.maximum(np.abs(c[ok]), np.abs(ref[ok])))
+    err = np.abs(c[ok] - ref[ok])
+    worst = np.argmax(err - tol) if err.size else 0
+    assert np.all(err <= tol), (f"{what}: {np.sum(err > tol)} elements out of tolerance; worst err "
+                                f"{err[worst]:.3e} tol {tol[worst]:.3e}")
+    return float(np.max(err / np.maximum(bound[ok], 1e-300))) if err.size else 0.0
+
+
+def probe_lib():
+    if not os.path.exists(PROBE_LIB):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(PROBE_LIB)
+    P = ctypes.c_void_p
+    lib.probe_mfma_scale_32x32x64.argtypes = [P, P, P, P, P, ctypes.c_int]
+    lib.probe_mfma_scale_16x16x128.argtypes = [P, P, P, P, P]
+    lib.probe_cvt_fp4_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, P, P, ctypes.c_uint32]
+    return lib
+
+
+def save_npz(name, **arrays):
+    if os.path.isdir(OUT_DIR):
+        np.savez(os.path.join(OUT_DIR, name), **arrays)

@@ -1,0 +1,139 @@
+"""In-bounds checks of the gfx950 builtins the library relies on.
+
+* Scaled FP4 MFMA operand / scale / result lane layouts, checked against a
+  NumPy model of C = sum_k (A[i,k] X_A[i,k/32]) (B[j,k] X_B[j,k/32]).
+* The hardware packed FP4 conversion against the library's software RNE
+  (informational: the library uses the software rounding unless the two agree
+  on every input it can see).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import banner, need_gpu, probe_lib, save_npz
+
+pytestmark = pytest.mark.gpu
+
+
+def _lane_regs(mat_codes, rows_per_tile, kgroups):
+    """Per-lane 8 x int32 operand registers for an FP4 MFMA operand.
+
+    mat_codes: [rows_per_tile, 32*kgroups] codes.  Lane l holds row
+    l % rows_per_tile and K-elements [32*g, 32*g+32) with g = l // rows_per_tile,
+    two codes per byte (even element low nibble) in the first 4 registers."""
+    regs = np.zeros((64, 8), dtype=np.uint32)
+    for l in range(64):
+        r, g = l % rows_per_tile, l // rows_per_tile
+        seg = mat_codes[r, 32 * g:32 * g + 32].astype(np.uint32)
+        by = seg[0::2] | (seg[1::2] << 4)                     # 16 bytes
+        words = by.reshape(4, 4)
+        regs[l, :4] = words[:, 0] | (words[:, 1] << 8) | (words[:, 2] << 16) | (words[:, 3] << 24)
+    return regs.view(np.int32)
+
+
+def _close(got, expect, a, a_sc, b, b_sc):
+    """float32 accumulation of exact products: within K * 2^-24 of sum |a b|
+    (a wrong lane mapping misses by O(1) relative)."""
+    aa = np.abs(oracle.e2m1_decode(a)) * np.repeat(oracle.e8m0_decode(a_sc), 32, axis=1)
+    bb = np.abs(oracle.e2m1_decode(b)) * np.repeat(oracle.e8m0_decode(b_sc), 32, axis=1)
+    bound = aa @ bb.T
+    assert np.all(np.abs(got - expect) <= a.shape[1] * 2.0 ** -24 * bound)
+
+
+def _model(a_codes, a_sc, b_codes, b_sc):
+    a = oracle.e2m1_decode(a_codes) * np.repeat(oracle.e8m0_decode(a_sc), 32, axis=1)
+    b = oracle.e2m1_decode(b_codes) * np.repeat(oracle.e8m0_decode(b_sc), 32, axis=1)
+    return a @ b.T
+
+
+@pytest.mark.parametrize("opsel2", [0, 1])
+def test_mfma_scale_32x32x64_layout(opsel2):
+    need_gpu()
+    lib = probe_lib()
+    rng = np.random.default_rng(100 + opsel2)
+    a = rng.integers(0, 16, size=(32, 64))
+    b = rng.integers(0, 16, size=(32, 64))
+    a_sc = rng.integers(120, 135, size=(32, 2))
+    b_sc = rng.integers(120, 135, size=(32, 2))
+    # scale words: the used byte is 0 (op_sel 0) or 2 (op_sel 2); other bytes are junk
+    sa = rng.integers(0, 2**31, size=64).astype(np.int64)
+    sb = rng.integers(0, 2**31, size=64).astype(np.int64)
+    sh = 16 if opsel2 else 0
+    for l in range(64):
+        sa[l] = (sa[l] & ~(0xFF << sh)) | (int(a_sc[l % 32, l // 32]) << sh)
+        sb[l] = (sb[l] & ~(0xFF << sh)) | (int(b_sc[l % 32, l // 32]) << sh)
+    ar = torch.from_numpy(_lane_regs(a, 32, 2)).cuda()
+    br = torch.from_numpy(_lane_regs(b, 32, 2)).cuda()
+    sat = torch.from_numpy(sa.astype(np.uint32).view(np.int32)).cuda()
+    sbt = torch.from_numpy(sb.astype(np.uint32).view(np.int32)).cuda()
+    out = torch.zeros(64 * 16, dtype=torch.float32, device="cuda")
+    banner(f"mfma 32x32x64 opsel2={opsel2}")
+    assert lib.probe_mfma_scale_32x32x64(ar.data_ptr(), br.data_ptr(), sat.data_ptr(),
+                                         sbt.data_ptr(), out.data_ptr(), opsel2) == 0
+    torch.cuda.synchronize()
+    raw = out.cpu().numpy().reshape(64, 16)
+    expect = _model(a, a_sc, b, b_sc)
+    got = np.zeros((32, 32))
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = raw[l, r]
+    save_npz(f"probe_mfma32_{opsel2}.npz", a=a, b=b, a_sc=a_sc, b_sc=b_sc, raw=raw, expect=expect)
+    _close(got, expect, a, a_sc, b, b_sc)
+
+
+def test_mfma_scale_16x16x128_layout():
+    need_gpu()
+    lib = probe_lib()
+    rng = np.random.default_rng(7)
+    a = rng.integers(0, 16, size=(16, 128))
+    b = rng.integers(0, 16, size=(16, 128))
+    a_sc = rng.integers(120, 135, size=(16, 4))
+    b_sc = rng.integers(120, 135, size=(16, 4))
+    sa = np.array([a_sc[l % 16, l // 16] for l in range(64)], dtype=np.int32)
+    sb = np.array([b_sc[l % 16, l // 16] for l in range(64)], dtype=np.int32)
+    ar = torch.from_numpy(_lane_regs(a, 16, 4)).cuda()
+    br = torch.from_numpy(_lane_regs(b, 16, 4)).cuda()
+    out = torch.zeros(64 * 4, dtype=torch.float32, device="cuda")
+    banner("mfma 16x16x128")
+    assert lib.probe_mfma_scale_16x16x128(ar.data_ptr(), br.data_ptr(),
+                                          torch.from_numpy(sa).cuda().data_ptr(),
+                                          torch.from_numpy(sb).cuda().data_ptr(),
+                                          out.data_ptr()) == 0
+    torch.cuda.synchronize()
+    raw = out.cpu().numpy().reshape(64, 4)
+    expect = _model(a, a_sc, b, b_sc)
+    got = np.zeros((16, 16))
+    for l in range(64):
+        for r in range(4):
+            got[4 * (l // 16) + r, l % 16] = raw[l, r]
+    save_npz("probe_mfma16.npz", a=a, b=b, a_sc=a_sc, b_sc=b_sc, raw=raw, expect=expect)
+    _close(got, expect, a, a_sc, b, b_sc)
+
+
+def _sweep(lib, lo, hi, cap=64):
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    first = torch.zeros(2 * cap, dtype=torch.int32, device="cuda")
+    assert lib.probe_cvt_fp4_sweep(lo, hi, cnt.data_ptr(), first.data_ptr(), cap) == 0
+    torch.cuda.synchronize()
+    n = int(cnt[0].item())
+    f = first.cpu().numpy().view(np.uint32).reshape(cap, 2)[:min(n, cap)]
+    return n, f
+
+
+def test_hw_fp4_cvt_vs_software_rne_report():
+    """Report (and record) where the hardware conversion differs from the
+    library's RNE on |x| < 8 and beyond; the library only switches to the
+    hardware instruction if the first count is zero."""
+    need_gpu()
+    lib = probe_lib()
+    banner("cvt sweep [0, 8)")
+    n_in, f_in = _sweep(lib, 0, 0x41000000)
+    banner("cvt sweep [8, inf]")
+    n_out, f_out = _sweep(lib, 0x41000000, 0x7F800001)
+    save_npz("probe_cvt.npz", n_in=n_in, f_in=f_in, n_out=n_out, f_out=f_out)
+    print(f"hw-vs-sw fp4 cvt mismatches: |x|<8: {n_in}, |x|>=8: {n_out}")
+    for u, code in f_in[:8]:
+        print(f"  x=0x{u:08x} ({np.uint32(u).view(np.float32)!r}) hw=0x{code & 0xFF:02x} sw=0x{code >> 8:02x}")

@@ -1,0 +1,233 @@
+"""GPU parity of mx_quantize / mx_dequantize against the oracle (bit-exact).
+
+Every case feeds identical inputs (bf16 bits or float32) to both sides and
+compares packed codes and scale bytes byte for byte.  The comparison rule
+allows, with the Hadamard transform, codes to differ only where the oracle's
+pre-rounding value lies within 1 float32 ulp of a rounding boundary; the cases
+below require exact equality, which is stronger.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_microscaling_quantization_mx_amd as mx
+import oracle
+import workloads
+from gpu_util import banner, codes_equal, host, need_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quant(x_t, **kw):
+    q = mx.quantize(x_t, **kw)
+    return host(q.codes), host(q.scales), q
+
+
+def _ora_quant(x_np, **kw):
+    return oracle.quantize(x_np, **kw)
+
+
+MODES = [
+    dict(axis=a, block=b, rounding=r, rht_mask=m)
+    for a in ("last", "dim0")
+    for b in ("1d", "2d")
+    for r in ("rne", "sr")
+    for m in (None, 0x9E3779B9)
+]
+
+
+def _mode_id(m):
+    return f"{m['axis']}-{m['block']}-{m['rounding']}-{'rht' if m['rht_mask'] is not None else 'plain'}"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("mode", MODES, ids=_mode_id)
+def test_quantize_modes_ragged(mode, dtype):
+    """Shapes spanning several tiles with ragged tails in every direction."""
+    need_gpu()
+    R, C = (224, 352) if mode["block"] == "2d" else (160, 200)
+    if mode["axis"] == "last" and mode["block"] == "1d":
+        R, C = 77, 480
+    if mode["axis"] == "dim0" and mode["block"] == "1d":
+        R, C = 288, 83
+    if mode["axis"] == "last" and mode["block"] == "2d":
+        R, C = 96, 416
+    if mode["axis"] == "dim0" and mode["block"] == "2d":
+        R, C = 320, 96
+    rng = np.random.default_rng(zlib.crc32(_mode_id(mode).encode()))
+    x = (rng.standard_t(3, (R, C)) * np.exp(rng.uniform(-3, 3, (R, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).to(dtype)
+    xn = xt.float().numpy()
+    kw = dict(mode, seed=0x1234_5678_9ABC_DEF0, offset=5)
+    banner(f"quantize {_mode_id(mode)} {dtype} R={R} C={C}")
+    ld = (C + 7) // 8 * 8                  # row stride: a multiple of 8 elements
+    buf = torch.zeros((R, ld), dtype=dtype)
+    buf[:, :C] = xt
+    gc, gs, _ = _gpu_quant(buf.cuda()[:, :C], **kw)
+    oc, os_ = _ora_quant(xn, **kw)
+    codes_equal(gs, os_, "scales")
+    codes_equal(gc, oc, "codes")
+
+
+def _adversarial_rows():
+    """Blocks built to hit every corner of the conversion: grid points, ties,
+    +-1 ulp around ties, signed zeros, the clip band, exact powers of two,
+    subnormal inputs, huge values, NaN and Inf, all-zero blocks."""
+    rows = []
+    grid = [0, .5, 1, 1.5, 2, 3, 4, 6]
+    ties = [.25, .75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for scale in (1.0, 2.0 ** -20, 2.0 ** 60, 2.0 ** -126, 2.0 ** -133):
+        vals = [6.0]  # fixes amax band [4, 8) -> scale = 1 * scale
+        for t in ties:
+            f = np.float32(t)
+            vals += [t, float(np.nextafter(f, np.float32(0))), float(np.nextafter(f, np.float32(9)))]
+        vals += grid[1:] + [-0.0, 0.0, 6.5, 7.0, 7.99, -7.5, -5.0, -0.25]
+        vals = (vals + [0.1] * 64)[:64]
+        rows.append([v * scale for v in vals])
+    rows.append([0.0] * 64)
+    rows.append([-0.0] * 64)
+    r = [1.0] * 64
+    r[3] = np.nan
+    rows.append(r)
+    r = [2.0] * 64
+    r[40] = -np.inf
+    rows.append(r)
+    r = [3e38] * 32 + [1e-40] * 32
+    rows.append(r)
+    for k in range(-130, 128, 37):
+        rows.append([2.0 ** k] * 32 + [-(2.0 ** k) * 1.5] * 32)
+    return np.array(rows, dtype=np.float32)
+
+
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_quantize_adversarial_blocks(rounding):
+    need_gpu()
+    x = _adversarial_rows()
+    banner(f"quantize adversarial f32 {rounding}")
+    gc, gs, _ = _gpu_quant(to_dev(x), rounding=rounding, seed=99, offset=0)
+    oc, os_ = _ora_quant(x, rounding=rounding, seed=99, offset=0)
+    codes_equal(gs, os_, "scales")
+    codes_equal(gc, oc, "codes")
+
+
+def test_quantize_tiny_config():
+    """The tiny workload: A 256x512 and B 512x256 float32 N(0,1), 1-D blocks
+    along K, RNE, no transform; B is blocked along its dim 0 (K = 512)."""
+    need_gpu()
+    a, b = workloads.tiny()
+    banner("quantize tiny config")
+    gac, gas, _ = _gpu_quant(to_dev(a))
+    gbc, gbs, _ = _gpu_quant(to_dev(b), axis="dim0")
+    oac, oas = _ora_quant(a)
+    obc, obs = _ora_quant(b, axis="dim0")
+    codes_equal(gas, oas, "A scales")
+    codes_equal(gac, oac, "A codes")
+    codes_equal(gbs, obs, "B scales")
+    codes_equal(gbc, obc, "B codes")
+
+
+def test_quantize_empty_and_strided():
+    need_gpu()
+    banner("quantize empty / strided")
+    z = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q = mx.quantize(z)
+    assert q.codes.shape == (0, 32)
+    x = np.random.default_rng(1).standard_normal((40, 96)).astype(np.float32)
+    big = torch.zeros((40, 128), dtype=torch.float32)
+    big[:, :96] = torch.from_numpy(x)
+    view = big.cuda()[:, :96]                        # row stride 128 elements
+    gc, gs, _ = _gpu_quant(view, rounding="sr", seed=5)
+    oc, os_ = _ora_quant(x, rounding="sr", seed=5)
+    codes_equal(gs, os_, "scales")
+    codes_equal(gc, oc, "codes")
+
+
+def test_quantize_invalid_args_raise():
+    need_gpu()
+    x = torch.zeros((32, 48), dtype=torch.float32, device="cuda")
+    with pytest.raises(mx.MXError):
+        mx.quantize(x)                               # K = 48 not a multiple of 32
+    with pytest.raises(mx.MXError):
+        mx.quantize(torch.zeros((48, 64), device="cuda"), block="2d")   # rows 48 % 32
+
+
+def test_quantize_full_size_config_both_axes():
+    """The quantize-only workload at full size: 16384 x 2880 bf16 Student-t(3)
+    with 0.1 % outliers x100, randomized Hadamard transform, Philox stochastic
+    rounding, along the last dim (offset 0) and along dim 0 (offset 1).  The
+    oracle checks a sample of 256 output rows in each direction."""
+    need_gpu()
+    R, C = 16384, 2880
+    xb = workloads.student_t_outliers(R, C)
+    xn = xb.float().numpy()
+    mask = workloads.rht_mask(workloads.CFG_QUANT)
+    seed = workloads.philox_seed(workloads.CFG_QUANT)
+    xd = xb.cuda()
+    rng = np.random.default_rng(0)
+    banner("quantize full size last-dim rht+sr")
+    q = mx.quantize(xd, rht_mask=mask, rounding="sr", seed=seed, offset=0)
+    rows = np.sort(rng.choice(R, 256, replace=False))
+    oc, os_ = oracle.quantize(xn[rows], rht_mask=mask, rounding="sr", seed=seed, offset=0,
+                              row_index=rows)
+    codes_equal(host(q.scales)[rows], os_, "last scales")
+    codes_equal(host(q.codes)[rows], oc, "last codes")
+    banner("quantize full size dim0 rht+sr")
+    qt = mx.quantize(xd, axis="dim0", rht_mask=mask, rounding="sr", seed=seed, offset=1)
+    cols = np.sort(rng.choice(C, 256, replace=False))
+    oc, os_ = oracle.quantize(xn[:, cols], axis="dim0", rht_mask=mask, rounding="sr", seed=seed,
+                              offset=1, row_index=cols)
+    codes_equal(host(qt.scales)[cols], os_, "dim0 scales")
+    codes_equal(host(qt.codes)[cols], oc, "dim0 codes")
+
+
+def test_dim0_equals_transposed_last_on_gpu():
+    """Property that holds at any size: quantizing X along dim 0 equals
+    quantizing X^T along its last dim, Hadamard transform and SR included."""
+    need_gpu()
+    xb = workloads.student_t_outliers(2048, 2880)
+    xd = xb.cuda()
+    kw = dict(rht_mask=0xC0FFEE11, rounding="sr", seed=7, offset=1)
+    banner("dim0 vs transposed last")
+    a = mx.quantize(xd, axis="dim0", **kw)
+    b = mx.quantize(xd.t().contiguous(), axis="last", **kw)
+    codes_equal(host(a.codes), host(b.codes), "codes")
+    codes_equal(host(a.scales), host(b.scales), "scales")
+
+
+@pytest.mark.parametrize("block", ["1d", "2d"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("irht", [None, 0x13572468])
+def test_dequantize_parity(block, out_dtype, irht):
+    need_gpu()
+    rng = np.random.default_rng(3)
+    rows, K = 96, 320
+    codes = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    srows = rows // 32 if block == "2d" else rows
+    scales = rng.integers(0, 255, size=(srows, K // 32), dtype=np.uint8)
+    scales[0, 0] = 0xFF
+    scales[-1, -1] = 0
+    scales[1, 2] = 254
+    q = mx.MXTensor(to_dev(codes), to_dev(scales), rows, K, block)
+    banner(f"dequantize {block} {out_dtype} irht={irht}")
+    got = mx.dequantize(q, out_dtype, inverse_rht_mask=irht).float()
+    ref = oracle.dequantize(codes, scales, block=block, inverse_rht_mask=irht).astype(np.float32)
+    if out_dtype == torch.bfloat16:
+        ref = torch.from_numpy(ref).to(torch.bfloat16).float().numpy()
+    g = host(got)
+    assert np.array_equal(np.isnan(g), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(g[m].view(np.uint32), ref[m].view(np.uint32))
+
+
+def test_quantize_dequantize_round_trip_rht():
+    """Dequantize with the inverse transform recovers the input to MXFP4 accuracy."""
+    need_gpu()
+    x = np.random.default_rng(4).standard_normal((256, 1024)).astype(np.float32)
+    mask = 0xA5A5A5A5
+    banner("round trip rht")
+    q = mx.quantize(to_dev(x), rht_mask=mask)
+    back = host(mx.dequantize(q, torch.float32, inverse_rht_mask=mask))
+    rel = np.linalg.norm(back - x) / np.linalg.norm(x)
+    assert rel < 0.12

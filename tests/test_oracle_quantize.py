@@ -268,3 +268,19 @@ def test_sr_quantize_unbiased_end_to_end():
     mean = acc / n
     # each element's sd <= max step / 2 = 1; 5-sigma bound
     assert np.max(np.abs(mean - x)) <= 5 * 1.0 / math.sqrt(n) + 2 * 2.0 ** -16
+
+
+def test_row_sampling_matches_full_tensor():
+    """Quantizing a sample of rows with their global row numbers reproduces
+    those rows of the full result (stochastic rounding included)."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((96, 64)).astype(np.float32)
+    kw = dict(rounding="sr", seed=77, offset=3, rht_mask=0x0F0F00FF)
+    full_c, full_s = oracle.quantize(x, **kw)
+    rows = np.array([95, 0, 41])
+    c, s = oracle.quantize(x[rows], row_index=rows, **kw)
+    assert np.array_equal(c, full_c[rows]) and np.array_equal(s, full_s[rows])
+    fc, fs = oracle.quantize(x, axis="dim0", **kw)
+    cols = np.array([5, 63, 32])
+    c, s = oracle.quantize(x[:, cols], axis="dim0", row_index=cols, **kw)
+    assert np.array_equal(c, fc[cols]) and np.array_equal(s, fs[cols])
