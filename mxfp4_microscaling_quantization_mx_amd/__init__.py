@@ -112,10 +112,15 @@ class MXTensor:
 
 
 def empty_mx(rows, K, block="1d", device="cuda"):
-    """Allocate an uninitialised MX operand (codes + scales) on `device`."""
+    """Allocate an uninitialised MX operand (codes + scales) on `device`.
+
+    Scale rows are padded to a multiple of 4 bytes (the row stride is carried
+    in the tensor), which lets the GEMMs fetch a stage's scales as one aligned
+    32-bit word per row."""
     srows = rows // 32 if block == "2d" else rows
     codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
-    scales = torch.empty((srows, K // 32), dtype=torch.uint8, device=device)
+    ld = (K // 32 + 3) // 4 * 4
+    scales = torch.empty((srows, ld), dtype=torch.uint8, device=device)[:, :K // 32]
     return MXTensor(codes, scales, rows, K, block)
 
 

@@ -18,11 +18,46 @@
 // 32-bit word of 4 scale bytes per row.  Rows past M/N and K past the end are
 // zero codes with scale 1.0, so they add exact zeros (a NaN scale there would
 // otherwise poison the sums).
+#include "gemm_tile256.h"
 #include "mx_device.h"
 #include "mx_launch.h"
 
 namespace mx {
 namespace {
+
+// ---------------------------------------------------------------- 256x256 tiles
+// Workgroup b runs on XCD b % 8.  Renumber so that consecutive ids share an
+// XCD (and its L2), then walk tiles in groups of 8 M-tiles so that the
+// workgroups resident on one XCD reuse a few A and B panels.
+__device__ __forceinline__ void tile_of(int b, int nwg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per = nwg / 8, rem = nwg % 8;
+  const int x = b % 8, k = b / 8;
+  const int t = x * per + (x < rem ? x : rem) + k;
+  constexpr int GM = 8;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int in = t % (GM * tiles_n);
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+template <bool A2D, bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void k_gemm256(MxOperand A, MxOperand B, int64_t M, int64_t N,
+                                                    int64_t K, void* C, int64_t ldc, int tiles_m,
+                                                    int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * t256::TM, n0 = tn * t256::TN;
+  t256::Acc acc;
+  t256::mainloop<A2D, B2D>(A, B, (int)M, (int)N, (int)K, m0, n0, lds, acc);
+  void* Ct = OUT_BF16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)m0 * ldc + n0)
+                      : (void*)(static_cast<float*>(C) + (int64_t)m0 * ldc + n0);
+  t256::store_tile<OUT_BF16>(acc, Ct, (int)ldc, (int)(M - m0), (int)(N - n0));
+}
+
+// ---------------------------------------------------------------- 128x128 tiles
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -207,6 +242,28 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(MxOperand A, MxOperand B, 
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  // 256x256 tiles: scale rows are fetched as aligned 32-bit words, and the
+  // operands are addressed with 32-bit offsets.
+  const bool words = (a.A.ld_scales % 4 == 0) && (a.B.ld_scales % 4 == 0) &&
+                     ((uintptr_t)a.A.scales % 4 == 0) && ((uintptr_t)a.B.scales % 4 == 0);
+  const bool small = a.M * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
+                     a.M * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31);
+  if (a.M >= 256 && a.N >= 256 && words && small) {
+    const int tiles_m = (int)((a.M + 255) / 256), tiles_n = (int)((a.N + 255) / 256);
+    const unsigned nwg = (unsigned)(tiles_m * tiles_n);
+#define MX_G256(A_, B_, O_)                                                                  \
+  hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(256), 0, st, a.A, a.B, a.M, a.N, \
+                     a.K, a.C, a.ldc, tiles_m, tiles_n)
+    if (a.out_bf16) {
+      if (a.a_2d) { if (a.b_2d) MX_G256(true, true, true); else MX_G256(true, false, true); }
+      else { if (a.b_2d) MX_G256(false, true, true); else MX_G256(false, false, true); }
+    } else {
+      if (a.a_2d) { if (a.b_2d) MX_G256(true, true, false); else MX_G256(true, false, false); }
+      else { if (a.b_2d) MX_G256(false, true, false); else MX_G256(false, false, false); }
+    }
+#undef MX_G256
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
 #define MX_G(A_, B_, O_) \
   hipLaunchKernelGGL((k_gemm<A_, B_, O_>), grid, dim3(256), 0, st, a.A, a.B, a.M, a.N, a.K, a.C, a.ldc)

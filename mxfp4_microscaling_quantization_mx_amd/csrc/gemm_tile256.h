@@ -1,0 +1,262 @@
+// 256x256-tile mainloop of the MXFP4 GEMMs for gfx950 (shared by the dense and
+// grouped kernels).
+//
+// Work split: a 256-thread workgroup owns a 256x256 output tile; its 4 waves
+// form a 2x2 grid and each wave owns 128x128 = 4x4 tiles of
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x FP4, one E8M0 scale per lane and
+// operand, float32 accumulators: 256 per lane).  Operand lane layout of that
+// instruction: lane l supplies row l % 32 and the 32 K-elements
+// [32*(l/32), 32*(l/32)+32) of the 64-deep step (one whole MX block, 16 bytes)
+// with that block's scale byte; result register r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+//
+// Data movement per 128-deep K stage: A and B codes (256 rows x 64 bytes each)
+// and the 4 scale bytes of each row (one aligned 32-bit word: scale rows must
+// have a stride that is a multiple of 4 bytes) go global -> LDS with
+// direct-to-LDS buffer loads (no VGPR round trip) into a ring of NS stages,
+// so NS - 1 stages of loads are in flight while one is multiplied.  Each
+// 64-byte LDS code row is XOR-swizzled in 16-byte chunks (chunk c of row r
+// sits at c ^ ((r >> 1) & 3)) so the 128-bit LDS reads of 8 consecutive rows
+// hit 8 different bank groups.  Raw buffer addressing returns zeros past the
+// end of an operand, so rows past M (or N) read as zeros and are never
+// stored; in the last, partial K stage the missing chunks are pointed past
+// the end (zero codes) and their scale bytes are cleared to 0 (a finite
+// scale), so they add exact zeros.
+#pragma once
+
+#include <type_traits>
+
+#include "mx_device.h"
+#include "mx_launch.h"
+
+namespace mx {
+namespace t256 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+constexpr int TM = 256, TN = 256;
+constexpr int TK = 128;                    // K elements per stage
+constexpr int ROWB = TK / 2;               // code bytes per row per stage
+constexpr int OPB = 256 * ROWB;            // code bytes per operand per stage (16 KiB)
+constexpr int SCB = 256 * 4;               // scale bytes per operand per stage (1 KiB)
+constexpr int STAGE_BYTES = 2 * OPB + 2 * SCB;
+constexpr int NS = 4;                      // stages in the LDS ring
+constexpr int LDS_BYTES = NS * STAGE_BYTES;
+constexpr int LOADS_PER_STAGE = 10;        // per wave: 4 + 4 code DMAs, 1 + 1 scale DMAs
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// and stores past the end are dropped (gfx9 raw buffer addressing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+constexpr uint32_t OOB = 0x80000000u;        // an offset past any operand (validated < 2 GiB)
+
+// Per-lane 32-bit byte offsets, computed once per tile.
+struct LaneOffsets {
+  uint32_t dma_a[4], dma_b[4];   // code chunk this lane loads in each of its 4 code DMAs
+  int chunk[4];                  // logical 16-byte chunk (= K-block within the stage) of each
+  uint32_t sc_a, sc_b;           // this lane's scale row (row 64*wave + lane of the tile)
+};
+
+template <bool A2D, bool B2D>
+__device__ __forceinline__ void lane_offsets(const MxOperand& A, const MxOperand& B, int M, int N,
+                                             int m0, int n0, int wave, int lane, LaneOffsets& o) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = 16 * (wave * 4 + t) + (lane >> 2);
+    const int c = swz(row, lane & 3);
+    o.chunk[t] = c;
+    o.dma_a[t] = (m0 + row < M) ? (uint32_t)(m0 + row) * (uint32_t)A.ld_codes + 16u * c : OOB;
+    o.dma_b[t] = (n0 + row < N) ? (uint32_t)(n0 + row) * (uint32_t)B.ld_codes + 16u * c : OOB;
+  }
+  const int ra = m0 + 64 * wave + lane, rb = n0 + 64 * wave + lane;
+  o.sc_a = ra < M ? (uint32_t)(A2D ? (ra >> 5) : ra) * (uint32_t)A.ld_scales : OOB;
+  o.sc_b = rb < N ? (uint32_t)(B2D ? (rb >> 5) : rb) * (uint32_t)B.ld_scales : OOB;
+}
+
+// Issue one stage's loads (10 per wave): 256 rows x 64 code bytes of each
+// operand as 16 direct-to-LDS loads of 1 KiB (4 per wave), and the 32-bit
+// scale word of each row (64 rows per wave and operand).  In the partial last
+// stage, chunks at or past K point past the end and read as zeros.
+template <bool TAIL>
+__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                            __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
+                                            const LaneOffsets& o, int st, int kchunks, uint8_t* stage,
+                                            int wave) {
+  const uint32_t cs = (uint32_t)st * (TK / 2), ss = (uint32_t)st * (TK / 32);
+  uint8_t* la = stage;
+  uint8_t* lb = stage + OPB;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t va = (TAIL && o.chunk[t] >= kchunks) ? OOB : o.dma_a[t];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(la + 1024 * (wave * 4 + t)), 16, va, cs, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t vb = (TAIL && o.chunk[t] >= kchunks) ? OOB : o.dma_b[t];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lb + 1024 * (wave * 4 + t)), 16, vb, cs, 0, 0);
+  }
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(stage + 2 * OPB + 256 * wave), 4, o.sc_a, ss, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(stage + 2 * OPB + SCB + 256 * wave), 4, o.sc_b, ss,
+                                           0, 0);
+}
+
+struct Acc {
+  v16f t[4][4];
+};
+
+// Multiply one stage held in LDS.  Scale word of row r = 4 scale bytes of the
+// stage's 4 K-blocks; lane l of a K step ks needs K-block 2*ks + l/32, so the
+// word is shifted right by 8*(l/32) and op_sel picks byte 2*ks.  `keep` masks
+// the bytes of K-blocks that exist (all of them except in a partial last
+// stage, whose missing blocks get scale byte 0, a finite scale).
+__device__ __forceinline__ void compute_stage(const uint8_t* stage, int wm, int wn, int lane,
+                                              uint32_t keep, Acc& acc) {
+  const uint8_t* la = stage;
+  const uint8_t* lb = stage + OPB;
+  const uint32_t* lsa = reinterpret_cast<const uint32_t*>(stage + 2 * OPB);
+  const uint32_t* lsb = reinterpret_cast<const uint32_t*>(stage + 2 * OPB + SCB);
+  const int l32 = lane & 31, kh = lane >> 5;
+  int sa[4], sb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wa = lsa[wm * 128 + 32 * i + l32] & keep;
+    const uint32_t wb = lsb[wn * 128 + 32 * i + l32] & keep;
+    sa[i] = (int)(wa >> (8 * kh));
+    sb[i] = (int)(wb >> (8 * kh));
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    v8i a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + 32 * i + l32;
+      const uint4 v = *reinterpret_cast<const uint4*>(la + row * ROWB + 16 * swz(row, 2 * ks + kh));
+      a[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + 32 * j + l32;
+      const uint4 v = *reinterpret_cast<const uint4*>(lb + row * ROWB + 16 * swz(row, 2 * ks + kh));
+      b[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (ks == 0)
+          acc.t[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc.t[i][j], 4, 4, 0,
+                                                                       sa[i], 0, sb[j]);
+        else
+          acc.t[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc.t[i][j], 4, 4, 2,
+                                                                       sa[i], 2, sb[j]);
+      }
+  }
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding
+// (n is one of the values a stage ring can leave in flight).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt encoding (gfx9): vmcnt bits [3:0] and [15:14]; expcnt and
+  // lgkmcnt left at their maxima (no wait).
+#define MX_VMCNT(N_) (((N_) & 0xF) | (((N_) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(MX_VMCNT(0)); break;
+    case LOADS_PER_STAGE: __builtin_amdgcn_s_waitcnt(MX_VMCNT(LOADS_PER_STAGE)); break;
+    default: __builtin_amdgcn_s_waitcnt(MX_VMCNT(2 * LOADS_PER_STAGE)); break;
+  }
+#undef MX_VMCNT
+}
+
+// C tile (rows m0.., cols n0..) = A[m0:m0+256] * B[n0:n0+256]^T over all K.
+// Operand rows past M/N read as zeros; the caller's epilogue stores only
+// valid rows and columns.  Byte extents of the operands must be < 2 GiB.
+template <bool A2D, bool B2D>
+__device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B, int M, int N,
+                                         int K, int m0, int n0, uint8_t* lds, Acc& acc) {
+  static_assert(NS == 4, "wait_vmcnt assumes at most 2 stages queued behind the current one");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc.t[i][j][r] = 0.0f;
+
+  const int nstages = (K + TK - 1) / TK;
+  const int nfull = K / TK;                 // stages without a K tail
+  if (nstages == 0) return;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A.codes, (uint32_t)(M * A.ld_codes));
+  const __amdgpu_buffer_rsrc_t rb = rsrc(B.codes, (uint32_t)(N * B.ld_codes));
+  const __amdgpu_buffer_rsrc_t rsa = rsrc(A.scales, (uint32_t)((A2D ? M / 32 : M) * A.ld_scales));
+  const __amdgpu_buffer_rsrc_t rsb = rsrc(B.scales, (uint32_t)((B2D ? N / 32 : N) * B.ld_scales));
+  LaneOffsets o;
+  lane_offsets<A2D, B2D>(A, B, M, N, m0, n0, wave, lane, o);
+  const int kchunks = (K - nfull * TK) / 32;          // K-blocks in the tail stage (0 if none)
+
+  // prologue: stages 0 .. NS-2
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) {
+    if (p < nfull) issue_stage<false>(ra, rb, rsa, rsb, o, p, 4, lds + p * STAGE_BYTES, wave);
+    else if (p < nstages) issue_stage<true>(ra, rb, rsa, rsb, o, p, kchunks, lds + p * STAGE_BYTES, wave);
+  }
+  const uint32_t tail_keep = (1u << (8 * kchunks)) - 1u;  // valid scale bytes of a partial stage
+  for (int s = 0; s < nstages; ++s) {
+    // loads of the stages after s that are already issued stay in flight
+    const int ahead = (nstages - 1 - s) < (NS - 2) ? (nstages - 1 - s) : (NS - 2);
+    wait_vmcnt(ahead * LOADS_PER_STAGE);
+    __syncthreads();                        // all waves' stage-s data landed; slot s-1 is free
+    const int p = s + NS - 1;
+    if (p < nfull) issue_stage<false>(ra, rb, rsa, rsb, o, p, 4, lds + (p % NS) * STAGE_BYTES, wave);
+    else if (p < nstages)
+      issue_stage<true>(ra, rb, rsa, rsb, o, p, kchunks, lds + (p % NS) * STAGE_BYTES, wave);
+    compute_stage(lds + (s % NS) * STAGE_BYTES, wm, wn, lane, s < nfull ? 0xFFFFFFFFu : tail_keep, acc);
+  }
+  __syncthreads();                          // LDS may be reused by the caller
+}
+
+// Store the wave's 128x128 part of the tile with bounds-checked buffer
+// stores: the resource ends after row mlim (relative to the tile origin C),
+// and lanes whose column is >= nlim point past it, so nothing outside the
+// matrix is written.  Row offsets are wave-uniform (scalar), column offsets
+// per lane.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int mlim, int nlim) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  constexpr int ES = OUT_BF16 ? 2 : 4;
+  const int rows = mlim < 256 ? mlim : 256;
+  const __amdgpu_buffer_rsrc_t r = rsrc(C, (uint32_t)((rows - 1) * ldc * ES + (nlim < 256 ? nlim : 256) * ES));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = wn * 128 + 32 * j + l32;
+    const uint32_t voff = col < nlim ? (uint32_t)(((wm * 128 + 4 * kh) * ldc + col) * ES) : OOB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t soff = (uint32_t)((32 * i + 8 * r4 + q) * ldc * ES);
+          const float v = acc.t[i][j][4 * r4 + q];
+          if (OUT_BF16)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, voff,
+                                                  soff, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+        }
+  }
+}
+
+}  // namespace t256
+}  // namespace mx

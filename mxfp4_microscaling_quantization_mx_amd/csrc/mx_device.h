@@ -142,6 +142,32 @@ __device__ __forceinline__ float scale_value(uint32_t s) {
   return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
 }
 
+// Hardware RNE conversion: V_CVT_SCALEF32_PK_FP4_F32 writes two E2M1 codes
+// (x0 in the low nibble) into byte `sel` of `old`, computing
+// RNE_fp4(RNE_fp32(x / scale)) with saturation to +-6 and the sign of zero
+// kept.  For a power-of-two scale this is exactly the conversion above
+// (verified exhaustively over all float32 inputs for scales 2^-126 .. 2^125 by
+// the probe tests), so the quantizer hands it the block scale directly.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_pk_fp4(uint32_t old, float x0, float x1, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, x0, x1, scale, SEL);
+}
+
+// 8 values -> one 32-bit word of codes (value i in nibble i), RNE.
+__device__ __forceinline__ uint32_t pack8_rne(const float x[8], float scale) {
+  uint32_t w = 0;
+  w = cvt_pk_fp4<0>(w, x[0], x[1], scale);
+  w = cvt_pk_fp4<1>(w, x[2], x[3], scale);
+  w = cvt_pk_fp4<2>(w, x[4], x[5], scale);
+  w = cvt_pk_fp4<3>(w, x[6], x[7], scale);
+  return w;
+}
+
+// Block scale 2^(s-127) as the float32 the conversion divides by.  The lowest
+// byte s = 0 (2^-127, a float32 subnormal) is avoided by the callers: they
+// multiply by 2^127 themselves and convert with scale 1.0.
+__device__ __forceinline__ float scale_f32_normal(uint32_t s) { return __uint_as_float(s << 23); }
+
 // ---------------------------------------------------------------- Hadamard
 // Radix-2 butterflies of the 32-point fast Walsh-Hadamard transform in
 // Sylvester order: stage h maps (x_i, x_{i+h}) -> (x_i + x_{i+h}, x_i - x_{i+h})
@@ -163,6 +189,22 @@ __device__ __forceinline__ void fwht8_inlane(float x[8]) {
 // Stages 8 and 16 when lane j of a quad holds elements 8j..8j+7 of the block:
 // the partner of element i is in lane j ^ 1 (h = 8) or j ^ 2 (h = 16); the lane
 // holding the lower index keeps the sum, the other keeps lower - upper.
+//
+// Fast form: every lane computes x + k * partner with k = +1 (lower lane) or
+// -1 (upper lane) in one fused multiply-add, which is exactly the rounded sum
+// or difference; the upper lane then holds the negated value, and the signs
+// are carried to the end: the returned factor (+-1) times the stored value is
+// the true transform value.
+__device__ __forceinline__ float fwht_cross_quad_signed(float x[8], uint32_t quad_lane) {
+  const float k8 = (quad_lane & 1u) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(quad_xor1f(x[i]), k8, x[i]);
+  const float k16 = (quad_lane & 2u) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(quad_xor2f(x[i]), k16, x[i]);
+  return k8 * k16;
+}
+
 __device__ __forceinline__ void fwht_cross_quad(float x[8], uint32_t quad_lane) {
   const bool up8 = quad_lane & 1u;
 #pragma unroll

@@ -58,53 +58,78 @@ __device__ __forceinline__ float load1(const void* __restrict__ src, int64_t idx
 }
 
 // ------------------------------------------------------------------ rows, 1-D
+// One lane per 32-element block: the lane reads its 64 contiguous source bytes
+// (bf16) with four 16-byte loads, so a wave covers 4 KiB of consecutive input
+// and writes 1 KiB of consecutive codes (one 16-byte store per lane) and 64
+// consecutive scale bytes.  The whole 32-point transform stays in registers.
+template <bool BF16>
+__device__ __forceinline__ void load32(const void* __restrict__ src, int64_t idx, float x[32],
+                                       uint32_t mask) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load8<BF16>(src, idx + 8 * j, x + 8 * j, (mask >> (8 * j)) & 0xFFu);
+}
+
+// Quantize one block held in registers (x already sign-flipped when RHT).
+// Returns the scale byte and writes the 16 code bytes to `packed`.
+template <bool RHT, bool SR>
+__device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packed[4], uint64_t p0,
+                                                     uint64_t seed, uint64_t offset) {
+  const float c = __uint_as_float(kRhtCBits);
+  if (RHT) fwht32_inlane(x);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  if (RHT) {
+    m = __float_as_uint(c * __uint_as_float(m));      // max |c t_i| = c max |t_i|
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = c * x[i];
+  }
+  const uint32_t s = scale_code_from_absmax_bits(m);
+  packed[0] = packed[1] = packed[2] = packed[3] = 0u;
+  if (s == 0xFFu) return s;
+  if (SR) {
+    const float inv = inv_scale_from_code(s);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t r[8];
+      sr_draws8((p0 >> 3) + g, seed, offset, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) packed[g] |= e2m1_sr(x[8 * g + i] * inv, r[i]) << (4 * i);
+    }
+  } else {
+    float sc = scale_f32_normal(s);
+    if (s == 0u) {
+      // scale 2^-127 is a float32 subnormal: multiply by 2^127 instead and
+      // convert at scale 1 (the same single rounding)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = x[i] * __uint_as_float(0x7F000000u);
+      sc = 1.0f;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) packed[g] = pack8_rne(x + 8 * g, sc);
+  }
+  return s;
+}
+
 template <bool BF16, bool RHT, bool SR>
-__global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ src, int64_t R,
-                                                       int64_t C, int64_t ld_src,
+__global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ src, uint32_t nblocks,
+                                                       uint32_t nkb, int64_t ld_src,
                                                        uint8_t* __restrict__ codes, int64_t ld_codes,
                                                        uint8_t* __restrict__ scales,
                                                        int64_t ld_scales, uint32_t mask,
                                                        uint64_t seed, uint64_t offset) {
-  const int64_t lanes_per_row = C >> 3;          // multiple of 4 since C % 32 == 0
-  const int64_t total = R * lanes_per_row;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  // The grid stride is a multiple of 4, so a lane's position in its quad (and
-  // hence which 8 elements of the block it holds) never changes.
-  const uint32_t ql = threadIdx.x & 3u;
-  const uint32_t sgn8 = RHT ? (mask >> (8 * ql)) & 0xFFu : 0u;
-  const float c = __uint_as_float(kRhtCBits);
-
-  for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l < total; l += stride) {
-    const int64_t row = l / lanes_per_row;
-    const int64_t col0 = (l - row * lanes_per_row) << 3;
-    float x[8];
-    load8<BF16>(src, row * ld_src + col0, x, sgn8);
-    if (RHT) {
-      fwht8_inlane(x);
-      fwht_cross_quad(x, ql);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = x[i] * c;
-    }
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-    m = max(m, quad_xor1(m));
-    m = max(m, quad_xor2(m));
-    const uint32_t s = scale_code_from_absmax_bits(m);
-    uint32_t packed = 0;
-    if (s != 0xFFu) {
-      const float inv = inv_scale_from_code(s);
-      uint32_t r[8];
-      if (SR) sr_draws8((uint64_t)(row * C + col0) >> 3, seed, offset, r);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = x[i] * inv;
-        packed |= (SR ? e2m1_sr(v, r[i]) : e2m1_rne(v)) << (4 * i);
-      }
-    }
-    *reinterpret_cast<uint32_t*>(codes + row * ld_codes + (col0 >> 1)) = packed;
-    if (ql == 0) scales[row * ld_scales + (col0 >> 5)] = (uint8_t)s;
-  }
+  const uint32_t g = blockIdx.x * 256u + threadIdx.x;
+  if (g >= nblocks) return;
+  const uint32_t row = g / nkb;
+  const uint32_t kb = g - row * nkb;
+  float x[32];
+  load32<BF16>(src, (int64_t)row * ld_src + 32 * kb, x, RHT ? mask : 0u);
+  uint32_t packed[4];
+  const uint64_t p0 = ((uint64_t)row * nkb + kb) * 32u;         // row * K + 32 kb
+  const uint32_t s = quantize_block32<RHT, SR>(x, packed, p0, seed, offset);
+  *reinterpret_cast<uint4*>(codes + (int64_t)row * ld_codes + 16 * kb) =
+      make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  scales[(int64_t)row * ld_scales + kb] = (uint8_t)s;
 }
 
 // ------------------------------------------------------------------ LDS tiles
@@ -164,17 +189,16 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
 #pragma unroll
   for (int i = 0; i < 32; ++i)
     x[i] = TRANS ? tile[(w * 32 + i) * S::LD + lane] : tile[lane * S::LD + w * 32 + i];
+  const float c = __uint_as_float(kRhtCBits);
   if (RHT) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((mask >> i) & 1u) << 31));
     fwht32_inlane(x);
-    const float c = __uint_as_float(kRhtCBits);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = x[i] * c;
   }
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  if (RHT) m = __float_as_uint(c * __uint_as_float(m));     // max |c t_i| = c max |t_i|
   if (!valid) m = 0;
   if (TWO_D) {
     // amax over the 32x32 tile = over the 32 lanes of this half-wave.
@@ -182,19 +206,31 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
     for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
   }
   if (!valid) return;
+  if (RHT) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = c * x[i];
+  }
   const uint32_t s = scale_code_from_absmax_bits(m);
   uint32_t packed[4] = {0u, 0u, 0u, 0u};
   if (s != 0xFFu) {
-    const float inv = inv_scale_from_code(s);
+    if (SR) {
+      const float inv = inv_scale_from_code(s);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint32_t r[8];
-      if (SR) sr_draws8((uint64_t)(orow * K + kb * 32) / 8 + g, seed, offset, r);
+      for (int g = 0; g < 4; ++g) {
+        uint32_t r[8];
+        sr_draws8((uint64_t)(orow * K + kb * 32) / 8 + g, seed, offset, r);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = x[8 * g + i] * inv;
-        packed[g] |= (SR ? e2m1_sr(v, r[i]) : e2m1_rne(v)) << (4 * i);
+        for (int i = 0; i < 8; ++i) packed[g] |= e2m1_sr(x[8 * g + i] * inv, r[i]) << (4 * i);
       }
+    } else {
+      float sc = scale_f32_normal(s);
+      if (s == 0u) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = x[i] * __uint_as_float(0x7F000000u);
+        sc = 1.0f;
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) packed[g] = pack8_rne(x + 8 * g, sc);
     }
   }
   *reinterpret_cast<uint4*>(codes + orow * ld_codes + kb * 16) =
@@ -225,13 +261,13 @@ hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
 
 template <bool BF16>
 hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
-  const int64_t lanes = a.R * (a.C / 8);
-  int64_t blocks = (lanes + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;     // grid-stride beyond 64 waves per CU
-#define MX_ROWS(RHT_, SR_)                                                                  \
-  hipLaunchKernelGGL((k_quant_rows_1d<BF16, RHT_, SR_>), dim3((unsigned)blocks), dim3(256), 0, \
-                     st, a.src, a.R, a.C, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, \
-                     a.mask, a.seed, a.offset)
+  const uint32_t nkb = (uint32_t)(a.C / 32);
+  const uint32_t nblocks = (uint32_t)(a.R * nkb);
+  const unsigned grid = (nblocks + 255u) / 256u;
+#define MX_ROWS(RHT_, SR_)                                                                   \
+  hipLaunchKernelGGL((k_quant_rows_1d<BF16, RHT_, SR_>), dim3(grid), dim3(256), 0, st, a.src, \
+                     nblocks, nkb, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, \
+                     a.seed, a.offset)
   if (a.rht) {
     if (a.sr) MX_ROWS(true, true); else MX_ROWS(true, false);
   } else {

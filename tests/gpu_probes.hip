@@ -69,6 +69,27 @@ __global__ void k_cvt_sweep(uint64_t lo, uint64_t hi, unsigned long long* mismat
   if (local) atomicAdd(mismatches, local);
 }
 
+// Same comparison with a power-of-two scale 2^k given to the instruction:
+// counts mismatches against RNE(x * 2^-k) (the instruction divides by its
+// scale) in counts[0] and against RNE(x * 2^k) (it multiplies) in counts[1].
+__global__ void k_cvt_scaled_sweep(uint64_t lo, uint64_t hi, int k, unsigned long long* counts) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const float s = __builtin_ldexpf(1.0f, k);
+  const float inv = __builtin_ldexpf(1.0f, -k);
+  unsigned long long mdiv = 0, mmul = 0;
+  for (uint64_t u = lo + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < hi; u += stride) {
+    const float x = __uint_as_float((uint32_t)u);
+    const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x, -x, s, 0) & 0xFFu;
+    const float vd = x * inv, vm = x * s;
+    const uint32_t swd = mx::e2m1_rne(vd) | (mx::e2m1_rne(-vd) << 4);
+    const uint32_t swm = mx::e2m1_rne(vm) | (mx::e2m1_rne(-vm) << 4);
+    mdiv += (hw != swd);
+    mmul += (hw != swm);
+  }
+  if (mdiv) atomicAdd(counts, mdiv);
+  if (mmul) atomicAdd(counts + 1, mmul);
+}
+
 extern "C" {
 
 int probe_mfma_scale_32x32x64(const int* a, const int* b, const int* sa, const int* sb, float* out,
@@ -88,6 +109,11 @@ int probe_mfma_scale_16x16x128(const int* a, const int* b, const int* sa, const 
 int probe_cvt_fp4_sweep(uint64_t lo, uint64_t hi, unsigned long long* mismatches, uint32_t* first,
                         uint32_t first_cap) {
   hipLaunchKernelGGL(k_cvt_sweep, dim3(4096), dim3(256), 0, 0, lo, hi, mismatches, first, first_cap);
+  return (int)hipGetLastError();
+}
+
+int probe_cvt_fp4_scaled_sweep(uint64_t lo, uint64_t hi, int k, unsigned long long* counts) {
+  hipLaunchKernelGGL(k_cvt_scaled_sweep, dim3(4096), dim3(256), 0, 0, lo, hi, k, counts);
   return (int)hipGetLastError();
 }
 

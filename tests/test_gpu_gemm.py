@@ -19,9 +19,18 @@ from gpu_util import banner, check_gemm, host, need_gpu, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _upload(codes, scales, block="1d"):
+def _upload(codes, scales, block="1d", pad=True):
+    """Upload oracle codes/scales; pad=True stores scale rows with a stride
+    rounded up to 4 bytes (the layout the quantizer allocates), pad=False
+    keeps them dense (the GEMM then takes its generic path)."""
     rows = codes.shape[0]
-    return mx.MXTensor(to_dev(codes), to_dev(scales), rows, codes.shape[1] * 2, block)
+    sc = to_dev(scales)
+    if pad:
+        ld = (scales.shape[1] + 3) // 4 * 4
+        buf = torch.full((scales.shape[0], ld), 0xFF, dtype=torch.uint8, device="cuda")
+        buf[:, :scales.shape[1]] = sc
+        sc = buf[:, :scales.shape[1]]
+    return mx.MXTensor(to_dev(codes), sc, rows, codes.shape[1] * 2, block)
 
 
 def _rand_mx(rng, rows, K, block="1d", lo=110, hi=145):
@@ -56,10 +65,17 @@ def test_gemm_single_block_exact():
     assert np.array_equal(c.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 72, 96), (129, 257, 2880), (1, 1, 64), (300, 128, 4128)])
+@pytest.mark.parametrize("M,N,K,pad", [(200, 72, 96, True), (129, 257, 2880, True), (1, 1, 64, True),
+                                       (300, 128, 4128, False), (300, 520, 2880, True),
+                                       (513, 257, 4128, True), (256, 256, 32, True),
+                                       (520, 300, 2880, False), (260, 768, 160, True)])
 @pytest.mark.parametrize("a_block,b_block", [("1d", "1d"), ("1d", "2d"), ("2d", "2d")])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
-def test_gemm_ragged(M, N, K, a_block, b_block, out):
+def test_gemm_ragged(M, N, K, pad, a_block, b_block, out):
+    """Shapes covering several 256x256 tiles with ragged M, N and K tails (the
+    K tails leave 1, 2 or 3 blocks in the last 128-deep stage), the 128x128
+    path, and scale rows padded (the quantizer's layout) or dense.  Padding
+    bytes are 0xFF so reading one would poison the result."""
     need_gpu()
     if a_block == "2d" and M % 32:
         M = (M + 31) // 32 * 32
@@ -68,8 +84,8 @@ def test_gemm_ragged(M, N, K, a_block, b_block, out):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     ac, as_ = _rand_mx(rng, M, K, a_block)
     bc, bs = _rand_mx(rng, N, K, b_block)
-    banner(f"gemm ragged M={M} N={N} K={K} {a_block}/{b_block} {out}")
-    c = host(mx.gemm(_upload(ac, as_, a_block), _upload(bc, bs, b_block), out).float())
+    banner(f"gemm ragged M={M} N={N} K={K} pad={pad} {a_block}/{b_block} {out}")
+    c = host(mx.gemm(_upload(ac, as_, a_block, pad), _upload(bc, bs, b_block, pad), out).float())
     ref, bound = oracle.gemm_ref(ac, as_, bc, bs, a_block, b_block)
     check_gemm(c, ref, bound, bf16=(out == torch.bfloat16), what="ragged")
 

@@ -2,9 +2,9 @@
 
 * Scaled FP4 MFMA operand / scale / result lane layouts, checked against a
   NumPy model of C = sum_k (A[i,k] X_A[i,k/32]) (B[j,k] X_B[j,k/32]).
-* The hardware packed FP4 conversion against the library's software RNE
-  (informational: the library uses the software rounding unless the two agree
-  on every input it can see).
+* The hardware packed FP4 conversion (scale 1.0) against the library's
+  software RNE over every float32 input: the quantizer uses the hardware
+  instruction for RNE, which is only valid while the two agree everywhere.
 """
 import ctypes
 
@@ -123,10 +123,10 @@ def _sweep(lib, lo, hi, cap=64):
     return n, f
 
 
-def test_hw_fp4_cvt_vs_software_rne_report():
-    """Report (and record) where the hardware conversion differs from the
-    library's RNE on |x| < 8 and beyond; the library only switches to the
-    hardware instruction if the first count is zero."""
+def test_hw_fp4_cvt_matches_software_rne_everywhere():
+    """The hardware conversion with scale 1.0 equals the software RNE
+    (saturation, ties to even, signed zero, subnormals) for every non-NaN
+    float32 x and -x."""
     need_gpu()
     lib = probe_lib()
     banner("cvt sweep [0, 8)")
@@ -135,5 +135,25 @@ def test_hw_fp4_cvt_vs_software_rne_report():
     n_out, f_out = _sweep(lib, 0x41000000, 0x7F800001)
     save_npz("probe_cvt.npz", n_in=n_in, f_in=f_in, n_out=n_out, f_out=f_out)
     print(f"hw-vs-sw fp4 cvt mismatches: |x|<8: {n_in}, |x|>=8: {n_out}")
-    for u, code in f_in[:8]:
+    for u, code in list(f_in[:8]) + list(f_out[:8]):
         print(f"  x=0x{u:08x} ({np.uint32(u).view(np.float32)!r}) hw=0x{code & 0xFF:02x} sw=0x{code >> 8:02x}")
+    assert n_in == 0 and n_out == 0
+
+
+@pytest.mark.parametrize("k", [-127, -126, -100, -60, -3, -1, 0, 1, 2, 17, 90, 124, 125])
+def test_hw_fp4_cvt_scale_operand_divides(k):
+    """With a power-of-two scale 2^k the instruction returns exactly
+    RNE_fp4(RNE_fp32(x * 2^-k)) for every non-NaN x: the quantizer hands it the
+    block scale instead of multiplying first (scale bytes >= 1; the lowest
+    scale byte, whose 2^-127 is a float32 subnormal, is checked too)."""
+    need_gpu()
+    lib = probe_lib()
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    banner(f"cvt scaled sweep k={k}")
+    assert lib.probe_cvt_fp4_scaled_sweep(0, 0x7F800001, k, cnt.data_ptr()) == 0
+    torch.cuda.synchronize()
+    c = cnt.cpu().numpy()
+    print(f"cvt scale 2^{k}: mismatches vs divide={c[0]} vs multiply={c[1]}")
+    save_npz(f"probe_cvt_scale_{k}.npz", counts=c)
+    if k >= -126:
+        assert c[0] == 0
