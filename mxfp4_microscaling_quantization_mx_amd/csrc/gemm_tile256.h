@@ -15,9 +15,12 @@
 // have a stride that is a multiple of 4 bytes) go global -> LDS with
 // direct-to-LDS buffer loads (no VGPR round trip) into a ring of NS stages,
 // so NS - 1 stages of loads are in flight while one is multiplied.  Each
-// 64-byte LDS code row is XOR-swizzled in 16-byte chunks (chunk c of row r
-// sits at c ^ ((r >> 1) & 3)) so the 128-bit LDS reads of 8 consecutive rows
-// hit 8 different bank groups.  Raw buffer addressing returns zeros past the
+// 64-byte LDS code row is XOR-swizzled in 16-byte chunks so the 128-bit LDS
+// reads of consecutive rows hit different bank groups.  The operand reads
+// from LDS are issued from asm blocks (each waits for its own reads), so the
+// compiler does not make them wait for the direct-to-LDS loads still in
+// flight into the other ring slots; the ring's own vmcnt waits and barriers
+// order the slots.  Raw buffer addressing returns zeros past the
 // end of an operand, so rows past M (or N) read as zeros and are never
 // stored; in the last, partial K stage the missing chunks are pointed past
 // the end (zero codes) and their scale bytes are cleared to 0 (a finite
@@ -47,7 +50,13 @@ constexpr int NS = 4;                      // stages in the LDS ring
 constexpr int LDS_BYTES = NS * STAGE_BYTES;
 constexpr int LOADS_PER_STAGE = 10;        // per wave: 4 + 4 code DMAs, 1 + 1 scale DMAs
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+// 16-byte chunk swizzle inside a 64-byte LDS row: with f = (b2, b1 ^ b3) of
+// the row number, any 8 consecutive rows (and any 16 consecutive rows) reading
+// the same logical chunk hit distinct 16-byte bank groups of a 128-byte (and
+// 256-byte) bank window.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ ((((row >> 2) & 1) << 1) | (((row >> 1) ^ (row >> 3)) & 1));
+}
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
 // and stores past the end are dropped (gfx9 raw buffer addressing).
@@ -110,40 +119,79 @@ struct Acc {
   v16f t[4][4];
 };
 
-// Multiply one stage held in LDS.  Scale word of row r = 4 scale bytes of the
-// stage's 4 K-blocks; lane l of a K step ks needs K-block 2*ks + l/32, so the
-// word is shifted right by 8*(l/32) and op_sel picks byte 2*ks.  `keep` masks
-// the bytes of K-blocks that exist (all of them except in a partial last
-// stage, whose missing blocks get scale byte 0, a finite scale).
-__device__ __forceinline__ void compute_stage(const uint8_t* stage, int wm, int wn, int lane,
-                                              uint32_t keep, Acc& acc) {
-  const uint8_t* la = stage;
-  const uint8_t* lb = stage + OPB;
-  const uint32_t* lsa = reinterpret_cast<const uint32_t*>(stage + 2 * OPB);
-  const uint32_t* lsb = reinterpret_cast<const uint32_t*>(stage + 2 * OPB + SCB);
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// LDS reads of one K step: 4 A and 4 B 16-byte operand chunks at row tiles
+// 0..3 (2048 bytes apart) from per-lane base addresses, waited for inside the
+// same asm block (outputs are early-clobber: a read may land before a later
+// read of the block has taken its address).  They are written in asm because the compiler cannot tell
+// these reads from the direct-to-LDS loads still in flight into other ring
+// slots and would otherwise wait for all of those first.
+__device__ __forceinline__ void lds_read_kstep(uint32_t addr_a, uint32_t addr_b, v4i a[4], v4i b[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:2048\n\t"
+      "ds_read_b128 %2, %8 offset:4096\n\t"
+      "ds_read_b128 %3, %8 offset:6144\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "ds_read_b128 %5, %9 offset:2048\n\t"
+      "ds_read_b128 %6, %9 offset:4096\n\t"
+      "ds_read_b128 %7, %9 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]),
+        "=&v"(b[3])
+      : "v"(addr_a), "v"(addr_b)
+      : "memory");
+}
+
+// The scale words of the 4 A and 4 B row tiles (128 bytes apart), same rule.
+__device__ __forceinline__ void lds_read_scales(uint32_t addr_a, uint32_t addr_b, uint32_t sa[4],
+                                                uint32_t sb[4]) {
+  asm volatile(
+      "ds_read_b32 %0, %8\n\t"
+      "ds_read_b32 %1, %8 offset:128\n\t"
+      "ds_read_b32 %2, %8 offset:256\n\t"
+      "ds_read_b32 %3, %8 offset:384\n\t"
+      "ds_read_b32 %4, %9\n\t"
+      "ds_read_b32 %5, %9 offset:128\n\t"
+      "ds_read_b32 %6, %9 offset:256\n\t"
+      "ds_read_b32 %7, %9 offset:384\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sb[0]), "=&v"(sb[1]),
+        "=&v"(sb[2]), "=&v"(sb[3])
+      : "v"(addr_a), "v"(addr_b)
+      : "memory");
+}
+
+// Multiply one stage held in LDS at byte address `stage`.  Scale word of row
+// r = 4 scale bytes of the stage's 4 K-blocks; lane l of a K step ks needs
+// K-block 2*ks + l/32, so the word is shifted right by 8*(l/32) and op_sel
+// picks byte 2*ks.  `keep` masks the bytes of K-blocks that exist (all of
+// them except in a partial last stage, whose missing blocks get scale byte 0,
+// a finite scale; their codes are 0).
+__device__ __forceinline__ void compute_stage(uint32_t stage, int wm, int wn, int lane, uint32_t keep,
+                                              Acc& acc) {
   const int l32 = lane & 31, kh = lane >> 5;
+  const int rowa = wm * 128 + l32, rowb = wn * 128 + l32;   // row tile 0; tiles are 32 rows apart
+  uint32_t wa[4], wb[4];
+  lds_read_scales(stage + 2 * OPB + 4 * rowa, stage + 2 * OPB + SCB + 4 * rowb, wa, wb);
   int sa[4], sb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t wa = lsa[wm * 128 + 32 * i + l32] & keep;
-    const uint32_t wb = lsb[wn * 128 + 32 * i + l32] & keep;
-    sa[i] = (int)(wa >> (8 * kh));
-    sb[i] = (int)(wb >> (8 * kh));
+    sa[i] = (int)((wa[i] & keep) >> (8 * kh));
+    sb[i] = (int)((wb[i] & keep) >> (8 * kh));
   }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
+    // the chunk swizzle depends on bits 1..3 of the row only, equal for all 4 tiles
+    v4i av[4], bv[4];
+    lds_read_kstep(stage + rowa * ROWB + 16 * swz(rowa, 2 * ks + kh),
+                   stage + OPB + rowb * ROWB + 16 * swz(rowb, 2 * ks + kh), av, bv);
     v8i a[4], b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + 32 * i + l32;
-      const uint4 v = *reinterpret_cast<const uint4*>(la + row * ROWB + 16 * swz(row, 2 * ks + kh));
-      a[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wn * 128 + 32 * j + l32;
-      const uint4 v = *reinterpret_cast<const uint4*>(lb + row * ROWB + 16 * swz(row, 2 * ks + kh));
-      b[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      a[i] = v8i{av[i].x, av[i].y, av[i].z, av[i].w, 0, 0, 0, 0};
+      b[i] = v8i{bv[i].x, bv[i].y, bv[i].z, bv[i].w, 0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -176,10 +224,10 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // C tile (rows m0.., cols n0..) = A[m0:m0+256] * B[n0:n0+256]^T over all K.
 // Operand rows past M/N read as zeros; the caller's epilogue stores only
 // valid rows and columns.  Byte extents of the operands must be < 2 GiB.
+// `lds` holds the NS ring slots back to back.
 template <bool A2D, bool B2D>
 __device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B, int M, int N,
                                          int K, int m0, int n0, uint8_t* lds, Acc& acc) {
-  static_assert(NS == 4, "wait_vmcnt assumes at most 2 stages queued behind the current one");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -201,24 +249,30 @@ __device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B,
   LaneOffsets o;
   lane_offsets<A2D, B2D>(A, B, M, N, m0, n0, wave, lane, o);
   const int kchunks = (K - nfull * TK) / 32;          // K-blocks in the tail stage (0 if none)
+  const uint32_t tail_keep = (1u << (8 * kchunks)) - 1u;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;   // LDS byte address of slot 0
 
-  // prologue: stages 0 .. NS-2
+  auto issue = [&](int p) {
+    uint8_t* slot = lds + (p % NS) * STAGE_BYTES;
+    if (p < nfull) issue_stage<false>(ra, rb, rsa, rsb, o, p, 4, slot, wave);
+    else if (p < nstages) issue_stage<true>(ra, rb, rsa, rsb, o, p, kchunks, slot, wave);
+  };
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) {
-    if (p < nfull) issue_stage<false>(ra, rb, rsa, rsb, o, p, 4, lds + p * STAGE_BYTES, wave);
-    else if (p < nstages) issue_stage<true>(ra, rb, rsa, rsb, o, p, kchunks, lds + p * STAGE_BYTES, wave);
-  }
-  const uint32_t tail_keep = (1u << (8 * kchunks)) - 1u;  // valid scale bytes of a partial stage
+  for (int p = 0; p < NS - 1; ++p) issue(p);
   for (int s = 0; s < nstages; ++s) {
     // loads of the stages after s that are already issued stay in flight
     const int ahead = (nstages - 1 - s) < (NS - 2) ? (nstages - 1 - s) : (NS - 2);
-    wait_vmcnt(ahead * LOADS_PER_STAGE);
-    __syncthreads();                        // all waves' stage-s data landed; slot s-1 is free
-    const int p = s + NS - 1;
-    if (p < nfull) issue_stage<false>(ra, rb, rsa, rsb, o, p, 4, lds + (p % NS) * STAGE_BYTES, wave);
-    else if (p < nstages)
-      issue_stage<true>(ra, rb, rsa, rsb, o, p, kchunks, lds + (p % NS) * STAGE_BYTES, wave);
-    compute_stage(lds + (s % NS) * STAGE_BYTES, wm, wn, lane, s < nfull ? 0xFFFFFFFFu : tail_keep, acc);
+    wait_vmcnt(ahead * LOADS_PER_STAGE);    // this wave's stage-s loads landed
+    // every wave's did, and the slot of stage s-1 is free.  A bare barrier:
+    // __syncthreads() would add a fence that waits for all loads in flight.
+    // The empty asm statements keep the compiler from moving memory
+    // operations (the next loads into the freed slot) across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(s + NS - 1);
+    compute_stage(lds_addr + (uint32_t)((s % NS) * STAGE_BYTES), wm, wn, lane,
+                  s < nfull ? 0xFFFFFFFFu : tail_keep, acc);
   }
   __syncthreads();                          // LDS may be reused by the caller
 }
