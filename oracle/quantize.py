@@ -96,7 +96,7 @@ def unpack_nibbles(packed):
 
 
 def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
-             seed=0, offset=0):
+             seed=0, offset=0, row_index=None, K_total=None):
     """Quantize a 2-D float array to MXFP4.
 
     axis="last": blocks along the last dim, output [R, C] with K = C.
@@ -105,6 +105,11 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
     block="1d": one scale per 32 elements along K, scales [rows_out, K/32].
     block="2d": one scale per 32x32 tile, scales [rows_out/32, K/32].
     Returns (codes uint8 [rows_out, K/2], scales uint8).
+
+    row_index / K_total let a caller quantize a sample of output rows (or of
+    source columns, for axis="dim0") of a larger tensor: they give the global
+    output-row numbers and the global K used in the stochastic-rounding element
+    index p = row * K + k.  They change nothing else.
     """
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
@@ -149,7 +154,9 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
 
         r = None
         if rounding == "sr":
-            p = (np.arange(rows, dtype=np.uint64)[:, None] * np.uint64(K)
+            ridx = np.arange(rows) if row_index is None else np.asarray(row_index)
+            kt = K if K_total is None else int(K_total)
+            p = (ridx.astype(np.uint64)[:, None] * np.uint64(kt)
                  + np.arange(K, dtype=np.uint64)[None, :])
             r = sr_bits16(p, seed, offset).reshape(rows, nkb, BLOCK)
         codes = round_e2m1(v, rounding, r)
