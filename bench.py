@@ -1,0 +1,268 @@
+"""Throughput of the MXFP4 quantized-linear hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of seeded synthetic
+input (shapes of the GPT-OSS-20B-sized workloads):
+
+  * quantize-only: 16384 x 2880 bf16 Student-t(3) with 0.1 % outliers x100,
+    32-point randomized Hadamard transform + Philox stochastic rounding, along
+    the last dim and along dim 0 (transpose-quantize);
+  * dense fprop: quantize X 16384 x 2880 (transform, RNE) and W 2880 x 5760
+    (dim 0, 2-D 32x32 blocks, same transform), GEMM -> bf16 16384 x 5760;
+  * wgrad: quantize dY and X 16384 x 2880 along the token dim (transform +
+    stochastic rounding), GEMM -> float32 2880 x 2880;
+  * MoE: quantize the 65536 x 2880 routed activations (32 experts, top-4,
+    Zipf(1.1) loads), grouped GEMM against the 32 pre-quantized expert
+    weights 2880 x 5760 -> bf16 65536 x 5760.
+
+`value` is the MXFP4 GEMM throughput of the whole step (dense + wgrad + MoE
+GEMM flops over the step time, quantizers included); per-kernel times, GB/s
+and TFLOP/s are reported alongside, and `roofline` covers the dominant kernel.
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mxfp4_microscaling_quantization_mx_amd as mx  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "MXFP4 GEMM TFLOPS (dense + MoE grouped) and quantize GB/s, % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak
+SRC_DIR = os.path.join(ROOT, "mxfp4_microscaling_quantization_mx_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def quant_bytes(rows, cols, in_bytes=2):
+    """Algorithmic bytes of one quantize: read the source, write codes + scales."""
+    n = rows * cols
+    return n * in_bytes + n // 2 + n // 32
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(SRC_DIR)):
+        with open(os.path.join(SRC_DIR, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    def __init__(self, dev):
+        # quantize-only
+        self.xq = workloads.student_t_outliers(16384, 2880).to(dev)
+        self.q_mask = workloads.rht_mask(workloads.CFG_QUANT)
+        self.q_seed = workloads.philox_seed(workloads.CFG_QUANT)
+        # dense fprop
+        x, w = workloads.fprop()
+        self.fx, self.fw = x.to(dev), w.to(dev)
+        self.f_mask = workloads.rht_mask(workloads.CFG_FPROP)
+        # wgrad
+        dy, xw = workloads.wgrad()
+        self.wdy, self.wx = dy.to(dev), xw.to(dev)
+        self.w_mask = workloads.rht_mask(workloads.CFG_WGRAD)
+        self.w_seed = workloads.philox_seed(workloads.CFG_WGRAD)
+        # MoE: routed activations and pre-quantized expert weights
+        tok, offsets = workloads.moe_routing()
+        xt = workloads.to_bf16(workloads.moe_tokens())
+        self.ma = xt[torch.from_numpy(tok)].to(dev)
+        self.m_offsets = torch.from_numpy(offsets).to(dev)
+        E, K, N = 32, 2880, 5760
+        self.mb = mx.MXTensor(torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev),
+                              torch.empty((E, N // 32, K // 32 + 2), dtype=torch.uint8,
+                                          device=dev)[:, :, :K // 32], N, K, "2d")
+        for e in range(E):
+            we = workloads.to_bf16(workloads.moe_expert_weight(e)).to(dev)
+            mx.quantize(we, axis="dim0", block="2d",
+                        out=mx.MXTensor(self.mb.codes[e], self.mb.scales[e], N, K, "2d"))
+        # outputs (allocated once)
+        self.q_last = mx.empty_mx(16384, 2880, device=dev)
+        self.q_dim0 = mx.empty_mx(2880, 16384, device=dev)
+        self.f_qx = mx.empty_mx(16384, 2880, device=dev)
+        self.f_qw = mx.empty_mx(5760, 2880, "2d", device=dev)
+        self.f_y = torch.empty((16384, 5760), dtype=torch.bfloat16, device=dev)
+        self.w_qdy = mx.empty_mx(2880, 16384, device=dev)
+        self.w_qx = mx.empty_mx(2880, 16384, device=dev)
+        self.w_dw = torch.empty((2880, 2880), dtype=torch.float32, device=dev)
+        self.m_qa = mx.empty_mx(65536, 2880, device=dev)
+        self.m_y = torch.empty((65536, 5760), dtype=torch.bfloat16, device=dev)
+
+    # each entry: (name, callable, kind, algorithmic amount)
+    def kernels(self):
+        q = quant_bytes(16384, 2880)
+        flop_f = 2 * 16384 * 5760 * 2880
+        flop_w = 2 * 2880 * 2880 * 16384
+        flop_m = 2 * 65536 * 5760 * 2880
+        return [
+            ("quantize_rows_rht_sr", lambda: mx.quantize(self.xq, rht_mask=self.q_mask, rounding="sr",
+                                                         seed=self.q_seed, offset=0, out=self.q_last),
+             "hbm", q),
+            ("quantize_dim0_rht_sr", lambda: mx.quantize(self.xq, axis="dim0", rht_mask=self.q_mask,
+                                                         rounding="sr", seed=self.q_seed, offset=1,
+                                                         out=self.q_dim0), "hbm", q),
+            ("fprop_quantize_x", lambda: mx.quantize(self.fx, rht_mask=self.f_mask, out=self.f_qx), "hbm", q),
+            ("fprop_quantize_w", lambda: mx.quantize(self.fw, axis="dim0", block="2d", rht_mask=self.f_mask,
+                                                     out=self.f_qw), "hbm", quant_bytes(2880, 5760)),
+            ("fprop_gemm", lambda: mx.gemm(self.f_qx, self.f_qw, out=self.f_y), "mfma", flop_f),
+            ("wgrad_quantize_dy", lambda: mx.quantize(self.wdy, axis="dim0", rht_mask=self.w_mask,
+                                                      rounding="sr", seed=self.w_seed, offset=0,
+                                                      out=self.w_qdy), "hbm", q),
+            ("wgrad_quantize_x", lambda: mx.quantize(self.wx, axis="dim0", rht_mask=self.w_mask,
+                                                     rounding="sr", seed=self.w_seed, offset=1,
+                                                     out=self.w_qx), "hbm", q),
+            ("wgrad_gemm", lambda: mx.gemm(self.w_qdy, self.w_qx, out=self.w_dw), "mfma", flop_w),
+            ("moe_quantize_a", lambda: mx.quantize(self.ma, out=self.m_qa), "hbm", quant_bytes(65536, 2880)),
+            ("moe_grouped_gemm", lambda: mx.grouped_gemm(self.m_qa, self.m_offsets, self.mb, out=self.m_y),
+             "mfma", flop_m),
+        ]
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle (NumPy, as written) on a bounded sample of the same workload:
+    quantize a slice of the quantize-only tensor both ways (transform + SR)
+    and the float64 reference GEMM of a slice of the fprop rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    xn = w.xq[:256].float().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.quantize(xn, rht_mask=w.q_mask, rounding="sr", seed=w.q_seed)
+    oracle.quantize(xn[:, :256].copy(), axis="dim0", rht_mask=w.q_mask, rounding="sr", seed=w.q_seed)
+    tq = time.perf_counter() - t0
+    qbytes = quant_bytes(256, 2880) + quant_bytes(256, 256)
+    # GEMM reference on oracle-quantized rows (fprop shape, 128 rows x 5760 x 2880)
+    rows = 128
+    xr = w.fx[:rows].float().cpu().numpy()
+    wr = w.fw.float().cpu().numpy()
+    ac, as_ = oracle.quantize(xr, rht_mask=w.f_mask)
+    bc, bs = oracle.quantize(wr, axis="dim0", block="2d", rht_mask=w.f_mask)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.gemm_ref(ac, as_, bc, bs, "1d", "2d")
+        n += 1
+        if time.perf_counter() - t0 > budget_s / 2 or n >= 8:
+            break
+    tg = (time.perf_counter() - t0) / n
+    flops = 2 * rows * 5760 * 2880
+    return {"value": flops / tg / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 reference GEMM of {rows} x 5760 x 2880 fprop rows (dequantize + BLAS "
+                       f"+ |a||b| bound), {n} runs; oracle quantize of 256 x 2880 rows + 256 x 256 "
+                       f"transposed (transform + SR) at {qbytes / tq / 1e9:.4f} GB/s"),
+            "quantize_GBps": qbytes / tq / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path is built and measured on one GPU's share; "
+              f"--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    mx.load_library()
+    w = Workload(dev)
+    ks = w.kernels()
+    for _ in range(args.warmup):
+        for _, fn, _, _ in ks:
+            fn()
+    torch.cuda.synchronize()
+
+    # timed region: K steps; per-kernel HIP events on the launch stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ks]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for s in range(args.steps):
+        for k, (_, fn, _, _) in enumerate(ks):
+            ev[s][k][0].record()
+            fn()
+            ev[s][k][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+
+    comps = {}
+    for k, (name, _, kind, amount) in enumerate(ks):
+        times = np.array([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)])
+        avg_ms = float(times.mean())
+        if kind == "hbm":
+            rate = amount / (avg_ms * 1e-3) / 1e9
+            comps[name] = {"us": avg_ms * 1e3, "GB/s": rate, "frac_hbm": rate / HBM_PEAK_GBS,
+                           "bytes": amount}
+        else:
+            rate = amount / (avg_ms * 1e-3) / 1e12
+            comps[name] = {"us": avg_ms * 1e3, "TFLOP/s": rate, "frac_fp4": rate / FP4_PEAK_TFLOPS,
+                           "flop": amount}
+
+    gemm_flop = sum(a for _, _, kind, a in ks if kind == "mfma")
+    value = gemm_flop / (ms_step * 1e-3) / 1e12
+    dom = max(comps, key=lambda n: comps[n]["us"])
+    dk = next(k for k in ks if k[0] == dom)
+    traffic = None
+    src_hash = kernel_source_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tj = json.load(open(TRAFFIC_FILE))
+            if tj.get("source_hash") == src_hash and dom in tj.get("kernels", {}):
+                traffic = tj["kernels"][dom]
+        except (ValueError, OSError):
+            traffic = None
+    if dk[2] == "mfma":
+        roof = {"bound": "mfma", "achieved": comps[dom]["TFLOP/s"], "peak": FP4_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": comps[dom]["TFLOP/s"] / FP4_PEAK_TFLOPS, "traffic": traffic,
+                "kernel": dom}
+    else:
+        roof = {"bound": "hbm", "achieved": comps[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": comps[dom]["GB/s"] / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom}
+    quant_bytes_total = sum(a for _, _, kind, a in ks if kind == "hbm")
+    quant_us = sum(comps[n]["us"] for n, _, kind, _ in ks if kind == "hbm")
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (e2m1 x e8m0) operands, f32 accumulate; bf16 in",
+        "data": "synthetic (seeded; GPT-OSS-20B-sized shapes, no weights or datasets)",
+        "config": {"workload": "MXFP4 linear hot path: quantize 16384x2880 (RHT+SR, both axes) + dense "
+                               "fprop 16384x5760x2880 + wgrad 2880x2880x16384 + MoE grouped 32 experts "
+                               "65536x5760x2880 (Zipf 1.1 top-4)",
+                   "parallelism": "single GPU"},
+        "quantize_GBps_aggregate": quant_bytes_total / (quant_us * 1e-6) / 1e9,
+        "components": comps,
+        "roofline": roof,
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -42,19 +42,77 @@ __device__ __forceinline__ void tile_of(int b, int nwg, int tiles_m, int tiles_n
   tn = in / gm;
 }
 
+// Waves per 256x256 workgroup: 8 (two per SIMD) unless built otherwise.
+#ifndef MX_GEMM_WAVES
+#define MX_GEMM_WAVES 8
+#endif
+constexpr int GW = MX_GEMM_WAVES;
+
 template <bool A2D, bool B2D, bool OUT_BF16>
-__global__ __launch_bounds__(256, 1) void k_gemm256(MxOperand A, MxOperand B, int64_t M, int64_t N,
-                                                    int64_t K, void* C, int64_t ldc, int tiles_m,
-                                                    int tiles_n) {
+__global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B, int64_t M, int64_t N,
+                                                        int64_t K, void* C, int64_t ldc, int tiles_m,
+                                                        int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * t256::TM, n0 = tn * t256::TN;
-  t256::Acc acc;
-  t256::mainloop<A2D, B2D>(A, B, (int)M, (int)N, (int)K, m0, n0, lds, acc);
+  t256::Acc<GW> acc;
+  t256::mainloop<GW, A2D, B2D>(A, B, (int)M, (int)N, (int)K, m0, n0, lds, acc);
   void* Ct = OUT_BF16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)m0 * ldc + n0)
                       : (void*)(static_cast<float*>(C) + (int64_t)m0 * ldc + n0);
-  t256::store_tile<OUT_BF16>(acc, Ct, (int)ldc, (int)(M - m0), (int)(N - n0));
+  t256::store_tile<GW, OUT_BF16>(acc, Ct, (int)ldc, (int)(M - m0), (int)(N - n0));
+}
+
+// Grouped (MoE) GEMM on 256x256 tiles.  The grid enumerates (row-tile slot,
+// column tile) pairs, renumbered like the dense kernel; a slot is mapped to
+// (expert, 256-row tile of that expert) from the device offsets, so the
+// schedule needs no host synchronization.  The slot count is an upper bound
+// (each expert adds at most one partial tile); slots past the last tile exit.
+template <bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxOperand B, int64_t M_cap,
+                                                                int64_t N, int64_t K,
+                                                                const int32_t* __restrict__ offsets, int E,
+                                                                int64_t stride_codes, int64_t stride_scales,
+                                                                void* C, int64_t ldc, int slots, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
+  __shared__ int s_expert, s_row0, s_rows;
+  int slot, tn;
+  tile_of(blockIdx.x, gridDim.x, slots, tiles_n, slot, tn);
+  if (threadIdx.x == 0) {
+    int64_t acc_tiles = 0;
+    int ex = -1, r0 = 0, nr = 0;
+    for (int e = 0; e < E; ++e) {
+      int64_t lo = offsets[e], hi = offsets[e + 1];
+      lo = lo < 0 ? 0 : (lo > M_cap ? M_cap : lo);
+      hi = hi < lo ? lo : (hi > M_cap ? M_cap : hi);
+      const int64_t tiles = (hi - lo + t256::TM - 1) / t256::TM;
+      if (slot < acc_tiles + tiles) {
+        ex = e;
+        r0 = (int)(lo + (slot - acc_tiles) * t256::TM);
+        nr = (int)(hi - r0 < t256::TM ? hi - r0 : t256::TM);
+        break;
+      }
+      acc_tiles += tiles;
+    }
+    s_expert = ex;
+    s_row0 = r0;
+    s_rows = nr;
+  }
+  __syncthreads();
+  const int ex = s_expert;
+  if (ex < 0) return;
+  MxOperand Ae = A;
+  Ae.codes = A.codes + (int64_t)s_row0 * A.ld_codes;
+  Ae.scales = A.scales + (int64_t)s_row0 * A.ld_scales;
+  MxOperand Be = B;
+  Be.codes = B.codes + (int64_t)ex * stride_codes;
+  Be.scales = B.scales + (int64_t)ex * stride_scales;
+  const int n0 = tn * t256::TN;
+  t256::Acc<GW> acc;
+  t256::mainloop<GW, false, B2D>(Ae, Be, s_rows, (int)N, (int)K, 0, n0, lds, acc);
+  void* Ct = OUT_BF16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)s_row0 * ldc + n0)
+                      : (void*)(static_cast<float*>(C) + (int64_t)s_row0 * ldc + n0);
+  t256::store_tile<GW, OUT_BF16>(acc, Ct, (int)ldc, s_rows, (int)(N - n0));
 }
 
 // ---------------------------------------------------------------- 128x128 tiles
@@ -252,7 +310,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     const int tiles_m = (int)((a.M + 255) / 256), tiles_n = (int)((a.N + 255) / 256);
     const unsigned nwg = (unsigned)(tiles_m * tiles_n);
 #define MX_G256(A_, B_, O_)                                                                  \
-  hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(256), 0, st, a.A, a.B, a.M, a.N, \
+  hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M, a.N, \
                      a.K, a.C, a.ldc, tiles_m, tiles_n)
     if (a.out_bf16) {
       if (a.a_2d) { if (a.b_2d) MX_G256(true, true, true); else MX_G256(true, false, true); }
@@ -280,6 +338,26 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st) {
   if (a.M_cap == 0 || a.N == 0) return hipSuccess;
+  const bool words = (a.A.ld_scales % 4 == 0) && (a.B.ld_scales % 4 == 0) && (a.stride_scales % 4 == 0) &&
+                     ((uintptr_t)a.A.scales % 4 == 0) && ((uintptr_t)a.B.scales % 4 == 0);
+  const bool small = 256 * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
+                     256 * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31);
+  if (a.N >= 256 && words && small) {
+    const int slots = (int)((a.M_cap + 255) / 256 + a.E);
+    const int tiles_n = (int)((a.N + 255) / 256);
+    const unsigned nwg = (unsigned)(slots * tiles_n);
+#define MX_GG256(B_, O_)                                                                       \
+  hipLaunchKernelGGL((k_grouped_gemm256<B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap, \
+                     a.N, a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, slots,     \
+                     tiles_n)
+    if (a.out_bf16) {
+      if (a.b_2d) MX_GG256(true, true); else MX_GG256(false, true);
+    } else {
+      if (a.b_2d) MX_GG256(true, false); else MX_GG256(false, false);
+    }
+#undef MX_GG256
+    return hipGetLastError();
+  }
   // Upper bound on m-tiles over all experts: each expert adds at most one partial tile.
   const int64_t slots = (a.M_cap + BM - 1) / BM + a.E;
   dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)slots);

@@ -212,6 +212,8 @@ mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, in
   if (!C) return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: null C");
   if (ldc < N) return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm: ldc=%lld < N=%lld", (long long)ldc, (long long)N);
   if ((M + 127) / 128 + E > 65535) return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: too many row tiles");
+  if (((M + 255) / 256 + E) * ((N + 255) / 256) > 0x7FFFFFFF)
+    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: too many tiles");
   mx::GroupedGemmArgs a{};
   a.A = operand(A);
   a.B = operand(B);

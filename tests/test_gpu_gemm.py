@@ -134,14 +134,22 @@ def test_gemm_mismatched_k_raises():
 
 
 # ---------------------------------------------------------------- grouped
-def _grouped_case(rng, offsets, N, K, out_dtype):
+def _grouped_case(rng, offsets, N, K, out_dtype, pad=True):
+    """pad=True: scale rows (and the per-expert stride) padded to 4 bytes with
+    0xFF in the padding, the layout the 256x256 path takes."""
     E = len(offsets) - 1
     M = int(offsets[-1])
     ac, as_ = _rand_mx(rng, M, K)
     bcs, bss = zip(*[_rand_mx(rng, N, K, "2d") for _ in range(E)])
     bc, bs = np.stack(bcs), np.stack(bss)
-    a = _upload(ac, as_)
-    b = mx.MXTensor(to_dev(bc), to_dev(bs), N, K, "2d")
+    a = _upload(ac, as_, pad=pad)
+    bsd = to_dev(bs)
+    if pad:
+        ld = (bs.shape[2] + 3) // 4 * 4
+        buf = torch.full((E, bs.shape[1], ld), 0xFF, dtype=torch.uint8, device="cuda")
+        buf[:, :, :bs.shape[2]] = bsd
+        bsd = buf[:, :, :bs.shape[2]]
+    b = mx.MXTensor(to_dev(bc), bsd, N, K, "2d")
     off = to_dev(np.asarray(offsets, dtype=np.int32))
     c = host(mx.grouped_gemm(a, off, b, out_dtype).float())
     ref, bound = oracle.grouped_gemm_ref(ac, as_, offsets, bc, bs)
@@ -155,7 +163,19 @@ def test_grouped_gemm_ragged_experts(offsets, out):
     need_gpu()
     rng = np.random.default_rng(len(offsets) * 11 + offsets[-1])
     banner(f"grouped offsets={offsets} {out}")
-    _grouped_case(rng, offsets, 96, 160, out)
+    _grouped_case(rng, offsets, 96, 160, out, pad=False)
+
+
+@pytest.mark.parametrize("offsets", [[0, 5, 5, 300, 333], [0, 600], [0, 0, 0, 257, 257, 800],
+                                     [0, 1, 2, 3, 4, 260, 261, 700]])
+@pytest.mark.parametrize("N,K", [(288, 2880), (544, 416)])
+def test_grouped_gemm256_ragged_experts(offsets, N, K):
+    """256x256-tile path: empty experts, experts of 1 row, tiles straddling
+    expert boundaries, ragged N and K tails."""
+    need_gpu()
+    rng = np.random.default_rng(len(offsets) * 13 + offsets[-1] + N)
+    banner(f"grouped256 offsets={offsets} N={N} K={K}")
+    _grouped_case(rng, offsets, N, K, torch.bfloat16)
 
 
 def test_grouped_gemm_rows_past_last_offset_untouched():
