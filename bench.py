@@ -77,13 +77,10 @@ class Workload:
         self.ma = xt[torch.from_numpy(tok)].to(dev)
         self.m_offsets = torch.from_numpy(offsets).to(dev)
         E, K, N = 32, 2880, 5760
-        self.mb = mx.MXTensor(torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev),
-                              torch.empty((E, N // 32, K // 32 + 2), dtype=torch.uint8,
-                                          device=dev)[:, :, :K // 32], N, K, "2d")
+        self.mb = mx.empty_mx(N, K, "2d", device=dev, experts=E)
         for e in range(E):
             we = workloads.to_bf16(workloads.moe_expert_weight(e)).to(dev)
-            mx.quantize(we, axis="dim0", block="2d",
-                        out=mx.MXTensor(self.mb.codes[e], self.mb.scales[e], N, K, "2d"))
+            mx.quantize(we, axis="dim0", block="2d", out=mx.expert(self.mb, e))
         # outputs (allocated once)
         self.q_last = mx.empty_mx(16384, 2880, device=dev)
         self.q_dim0 = mx.empty_mx(2880, 16384, device=dev)

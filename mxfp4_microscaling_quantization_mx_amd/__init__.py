@@ -111,17 +111,24 @@ class MXTensor:
                          _BLOCK[self.block], 0)
 
 
-def empty_mx(rows, K, block="1d", device="cuda"):
+def empty_mx(rows, K, block="1d", device="cuda", experts=None):
     """Allocate an uninitialised MX operand (codes + scales) on `device`.
 
-    Scale rows are padded to a multiple of 4 bytes (the row stride is carried
-    in the tensor), which lets the GEMMs fetch a stage's scales as one aligned
-    32-bit word per row."""
+    Scale rows are padded to a multiple of 16 bytes (the row stride is carried
+    in the tensor), which lets the GEMMs fetch scales 16 aligned bytes per row
+    at a time.  With `experts=E` the tensors get a leading expert dimension
+    (the stacked weights of grouped_gemm); expert e is `expert(q, e)`."""
     srows = rows // 32 if block == "2d" else rows
-    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
-    ld = (K // 32 + 3) // 4 * 4
-    scales = torch.empty((srows, ld), dtype=torch.uint8, device=device)[:, :K // 32]
+    lead = () if experts is None else (experts,)
+    codes = torch.empty(lead + (rows, K // 2), dtype=torch.uint8, device=device)
+    ld = (K // 32 + 15) // 16 * 16
+    scales = torch.empty(lead + (srows, ld), dtype=torch.uint8, device=device)[..., :K // 32]
     return MXTensor(codes, scales, rows, K, block)
+
+
+def expert(q, e):
+    """View of expert e of a stacked operand from empty_mx(..., experts=E)."""
+    return MXTensor(q.codes[e], q.scales[e], q.rows, q.K, q.block)
 
 
 def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None, seed=0, offset=0,

@@ -42,11 +42,7 @@ __device__ __forceinline__ void tile_of(int b, int nwg, int tiles_m, int tiles_n
   tn = in / gm;
 }
 
-// Waves per 256x256 workgroup: 8 (two per SIMD) unless built otherwise.
-#ifndef MX_GEMM_WAVES
-#define MX_GEMM_WAVES 8
-#endif
-constexpr int GW = MX_GEMM_WAVES;
+constexpr int GW = t256::WAVES;
 
 template <bool A2D, bool B2D, bool OUT_BF16>
 __global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B, int64_t M, int64_t N,
@@ -56,11 +52,11 @@ __global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * t256::TM, n0 = tn * t256::TN;
-  t256::Acc<GW> acc;
-  t256::mainloop<GW, A2D, B2D>(A, B, (int)M, (int)N, (int)K, m0, n0, lds, acc);
+  t256::Acc acc;
+  t256::mainloop<A2D, B2D>(A, B, (int)M, (int)N, (int)K, m0, n0, lds, acc);
   void* Ct = OUT_BF16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)m0 * ldc + n0)
                       : (void*)(static_cast<float*>(C) + (int64_t)m0 * ldc + n0);
-  t256::store_tile<GW, OUT_BF16>(acc, Ct, (int)ldc, (int)(M - m0), (int)(N - n0));
+  t256::store_tile<OUT_BF16>(acc, Ct, (int)ldc, (int)(M - m0), (int)(N - n0));
 }
 
 // Grouped (MoE) GEMM on 256x256 tiles.  The grid enumerates (row-tile slot,
@@ -108,11 +104,11 @@ __global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxO
   Be.codes = B.codes + (int64_t)ex * stride_codes;
   Be.scales = B.scales + (int64_t)ex * stride_scales;
   const int n0 = tn * t256::TN;
-  t256::Acc<GW> acc;
-  t256::mainloop<GW, false, B2D>(Ae, Be, s_rows, (int)N, (int)K, 0, n0, lds, acc);
+  t256::Acc acc;
+  t256::mainloop<false, B2D>(Ae, Be, s_rows, (int)N, (int)K, 0, n0, lds, acc);
   void* Ct = OUT_BF16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)s_row0 * ldc + n0)
                       : (void*)(static_cast<float*>(C) + (int64_t)s_row0 * ldc + n0);
-  t256::store_tile<GW, OUT_BF16>(acc, Ct, (int)ldc, s_rows, (int)(N - n0));
+  t256::store_tile<OUT_BF16>(acc, Ct, (int)ldc, s_rows, (int)(N - n0));
 }
 
 // ---------------------------------------------------------------- 128x128 tiles
@@ -300,10 +296,10 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(MxOperand A, MxOperand B, 
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  // 256x256 tiles: scale rows are fetched as aligned 32-bit words, and the
-  // operands are addressed with 32-bit offsets.
-  const bool words = (a.A.ld_scales % 4 == 0) && (a.B.ld_scales % 4 == 0) &&
-                     ((uintptr_t)a.A.scales % 4 == 0) && ((uintptr_t)a.B.scales % 4 == 0);
+  // 256x256 tiles: scale rows are fetched 16 bytes at a time (16-byte aligned
+  // rows), and the operands are addressed with 32-bit offsets.
+  const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) &&
+                     ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
   const bool small = a.M * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
                      a.M * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31);
   if (a.M >= 256 && a.N >= 256 && words && small) {
@@ -338,8 +334,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st) {
   if (a.M_cap == 0 || a.N == 0) return hipSuccess;
-  const bool words = (a.A.ld_scales % 4 == 0) && (a.B.ld_scales % 4 == 0) && (a.stride_scales % 4 == 0) &&
-                     ((uintptr_t)a.A.scales % 4 == 0) && ((uintptr_t)a.B.scales % 4 == 0);
+  const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) && (a.stride_scales % 16 == 0) &&
+                     ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
   const bool small = 256 * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
                      256 * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31);
   if (a.N >= 256 && words && small) {

@@ -1,34 +1,43 @@
 // 256x256-tile mainloop of the MXFP4 GEMMs for gfx950 (shared by the dense and
 // grouped kernels).
 //
-// Work split: a workgroup of W waves (4 or 8) owns a 256x256 output tile; the
-// waves form a (W/2) x 2 grid and each owns TI x TJ tiles of
+// Work split: a workgroup of 8 waves (two per SIMD) owns a 256x256 output
+// tile; the waves form a 4 x 2 grid and each owns 2 x 4 tiles of
 // V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x FP4, one E8M0 scale per lane and
-// operand, float32 accumulators in AGPRs).  With 8 waves two waves share each
-// SIMD, so one wave's LDS waits and barrier are covered by the other's matrix
-// work.  Operand lane layout of that instruction: lane l supplies row l % 32
-// and the 32 K-elements [32*(l/32), 32*(l/32)+32) of the 64-deep step (one
-// whole MX block, 16 bytes) with that block's scale byte; result register r of
-// lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+// operand, float32 accumulators).  Operand lane layout of that instruction:
+// lane l supplies row l % 32 and the 32 K-elements [32*(l/32), 32*(l/32)+32)
+// of the 64-deep step (one whole MX block, 16 bytes) with that block's scale
+// byte; result register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column
+// l % 32.
 //
-// Data movement per 128-deep K stage: A and B codes (256 rows x 64 bytes each)
-// and the 4 scale bytes of each row (one aligned 32-bit word: scale rows must
-// have a stride that is a multiple of 4 bytes) go global -> LDS with
-// direct-to-LDS buffer loads (no VGPR round trip) into a ring of NS stages,
-// so NS - 1 stages of loads are in flight while one is multiplied.  Each
-// 64-byte LDS code row is XOR-swizzled in 16-byte chunks so the 128-bit LDS
-// reads of consecutive rows hit different bank groups.  The operand reads
-// from LDS are issued from asm blocks (each waits for its own reads), so the
-// compiler does not make them wait for the direct-to-LDS loads still in
-// flight into the other ring slots; the ring's own vmcnt waits and barriers
-// order the slots.  Raw buffer addressing returns zeros past the end of an
-// operand, so rows past M (or N) read as zeros and are never stored; in the
-// last, partial K stage the missing chunks are pointed past the end (zero
-// codes) and their scale bytes are cleared to 0 (a finite scale), so they add
-// exact zeros.
+// Data movement: a stage is 256 K (four 64-deep steps).  Its A and B codes
+// (256 rows x 128 bytes each) go global -> LDS with direct-to-LDS buffer loads
+// (no VGPR round trip) into a ring of two slots; each load instruction covers
+// 8 whole 128-byte row segments, the request size at which this path runs
+// fastest.  Scale bytes travel the same way, 16 bytes (16 MX blocks, two
+// stages) per row per load, into a ring of two scale slots; scale rows must be
+// 16-byte aligned with a stride that is a multiple of 16 bytes.  Each 128-byte
+// LDS code row is XOR-swizzled in 16-byte chunks so that the 128-bit LDS
+// reads of 16 consecutive rows hit 16 different bank groups.  Raw buffer
+// addressing returns zeros past the end of an operand, so rows past M (or N)
+// read as zeros and are never stored; in the last, partial stage the missing
+// chunks are pointed past the end (zero codes) and their scale bytes are
+// cleared to 0 (a finite scale), so they add exact zeros.
+//
+// Software pipeline inside a wave: the operands of the next step are read from
+// LDS into a second register set while the 8 MFMAs of the current step run,
+// so the LDS latency is hidden behind matrix work.  Each step is one asm block
+// that issues its MFMAs with the next step's LDS reads interleaved and waits
+// for those reads at its end.  (The compiler can neither be told that these
+// reads do not touch the ring slot the direct-to-LDS loads are filling, which
+// would make it wait for every load in flight, nor be made to keep the
+// interleaving.)  The hazards it would otherwise cover are handled here: two
+// wait states between a VALU write of an operand and the MFMA that reads it
+// (an s_nop at the start of each block) and wait states between the last MFMA
+// and the first read of its result (after the loop).  One barrier per stage,
+// before its last step: every wave has then read the stage's codes, so its
+// slot is refilled with the stage two ahead while the last step runs.
 #pragma once
-
-#include <type_traits>
 
 #include "mx_device.h"
 #include "mx_launch.h"
@@ -37,38 +46,27 @@ namespace mx {
 namespace t256 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+constexpr int WAVES = 8;                   // 4 along M x 2 along N
 constexpr int TM = 256, TN = 256;
-constexpr int TK = 128;                    // K elements per stage
-constexpr int ROWB = TK / 2;               // code bytes per row per stage
-constexpr int OPB = 256 * ROWB;            // code bytes per operand per stage (16 KiB)
-constexpr int SCB = 256 * 4;               // scale bytes per operand per stage (1 KiB)
-constexpr int STAGE_BYTES = 2 * OPB + 2 * SCB;
-constexpr int NS = 4;                      // stages in the LDS ring
-constexpr int LDS_BYTES = NS * STAGE_BYTES;
+constexpr int TK = 256;                    // K elements per stage
+constexpr int ROWB = TK / 2;               // code bytes per row per stage (128)
+constexpr int OPB = 256 * ROWB;            // code bytes per operand per stage (32 KiB)
+constexpr int STAGE_BYTES = 2 * OPB;       // one code slot
+constexpr int SROWB = 16;                  // scale bytes per row per scale slot (two stages)
+constexpr int SSLOT = 2 * 256 * SROWB;     // one scale slot: A rows, then B rows (8 KiB)
+constexpr int LDS_BYTES = 2 * STAGE_BYTES + 2 * SSLOT;
+constexpr int TI = 2, TJ = 4;              // 32x32 MFMA tiles per wave along M, N
+constexpr int CODE_LOADS = 8;              // 1 KiB code loads per wave and stage (4 A + 4 B)
 
-template <int W>
-struct Cfg {
-  static_assert(W == 4 || W == 8, "4 or 8 waves");
-  static constexpr int WN = 2;                           // waves along N
-  static constexpr int WM = W / WN;                      // waves along M
-  static constexpr int TI = TM / WM / 32;                // 32-row MFMA tiles per wave along M
-  static constexpr int TJ = TN / WN / 32;                // ... along N
-  static constexpr int DMA = 16 / W;                     // 1 KiB code loads per wave and operand
-  static constexpr int SC_LOADS = (W == 4) ? 2 : 1;      // scale-word loads per wave
-  static constexpr int LOADS = 2 * DMA + SC_LOADS;       // loads per wave and stage
-};
-
-// 16-byte chunk swizzle inside a 64-byte LDS row: with f = (b2, b1 ^ b3) of
-// the row number, any 8 consecutive rows (and any 16 consecutive rows) reading
-// the same logical chunk hit distinct 16-byte bank groups of a 128-byte (and
-// 256-byte) bank window.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((((row >> 2) & 1) << 1) | (((row >> 1) ^ (row >> 3)) & 1));
-}
+// 16-byte chunk swizzle inside a 128-byte LDS row: chunk c of row r sits at
+// c ^ ((r >> 1) & 7).  Rows r and r+1 are 128 bytes apart, so 16 consecutive
+// rows reading one logical chunk land in 16 distinct 16-byte bank groups of
+// the 256-byte bank window.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
 // and stores past the end are dropped (gfx9 raw buffer addressing).
@@ -77,232 +75,226 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 constexpr uint32_t OOB = 0x80000000u;        // an offset past any operand (validated < 2 GiB)
 
-// Per-lane 32-bit byte offsets, computed once per tile.
-template <int W>
+// Per-lane 32-bit byte offsets of the global loads, computed once per tile.
 struct LaneOffsets {
-  uint32_t dma_a[Cfg<W>::DMA], dma_b[Cfg<W>::DMA];   // code chunk of each code load
-  int chunk[Cfg<W>::DMA];                           // its logical chunk (K-block within the stage)
-  uint32_t sc_a, sc_b;                              // this lane's scale row word
+  uint32_t code_a[4], code_b[4];   // code chunk of each code load
+  int chunk[4];                    // its logical chunk (K-block within the stage)
+  uint32_t sc;                     // this lane's scale row (A rows: waves 0-3, B rows: 4-7)
 };
 
-template <int W, bool A2D, bool B2D>
-__device__ __forceinline__ void lane_offsets(const MxOperand& A, const MxOperand& B, int M, int N,
-                                             int m0, int n0, int wave, int lane, LaneOffsets<W>& o) {
+template <bool A2D, bool B2D>
+__device__ __forceinline__ void lane_offsets(const MxOperand& A, const MxOperand& B, int M, int N, int m0,
+                                             int n0, int wave, int lane, LaneOffsets& o) {
 #pragma unroll
-  for (int t = 0; t < Cfg<W>::DMA; ++t) {
-    const int row = 16 * (wave * Cfg<W>::DMA + t) + (lane >> 2);
-    const int c = swz(row, lane & 3);
+  for (int t = 0; t < 4; ++t) {
+    const int row = 8 * (wave * 4 + t) + (lane >> 3);
+    const int c = swz(row, lane & 7);
     o.chunk[t] = c;
-    o.dma_a[t] = (m0 + row < M) ? (uint32_t)(m0 + row) * (uint32_t)A.ld_codes + 16u * c : OOB;
-    o.dma_b[t] = (n0 + row < N) ? (uint32_t)(n0 + row) * (uint32_t)B.ld_codes + 16u * c : OOB;
+    o.code_a[t] = (m0 + row < M) ? (uint32_t)(m0 + row) * (uint32_t)A.ld_codes + 16u * c : OOB;
+    o.code_b[t] = (n0 + row < N) ? (uint32_t)(n0 + row) * (uint32_t)B.ld_codes + 16u * c : OOB;
   }
-  // 4 waves: every wave loads 64 A and 64 B scale rows; 8 waves: waves 0-3
-  // load the A rows, waves 4-7 the B rows.
   const int r = 64 * (wave & 3) + lane;
-  const int ra = m0 + r, rb = n0 + r;
-  o.sc_a = ra < M ? (uint32_t)(A2D ? (ra >> 5) : ra) * (uint32_t)A.ld_scales : OOB;
-  o.sc_b = rb < N ? (uint32_t)(B2D ? (rb >> 5) : rb) * (uint32_t)B.ld_scales : OOB;
-}
-
-// Issue one stage's loads: 256 rows x 64 code bytes of each operand as 16
-// direct-to-LDS loads of 1 KiB, and the 32-bit scale word of each row.  In the
-// partial last stage, chunks at or past K point past the end and read as zeros.
-template <int W, bool TAIL>
-__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                            __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
-                                            const LaneOffsets<W>& o, int st, int kchunks,
-                                            uint8_t* stage, int wave) {
-  const uint32_t cs = (uint32_t)st * (TK / 2), ss = (uint32_t)st * (TK / 32);
-  uint8_t* la = stage;
-  uint8_t* lb = stage + OPB;
-#pragma unroll
-  for (int t = 0; t < Cfg<W>::DMA; ++t) {
-    const uint32_t va = (TAIL && o.chunk[t] >= kchunks) ? OOB : o.dma_a[t];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(la + 1024 * (wave * Cfg<W>::DMA + t)), 16,
-                                             va, cs, 0, 0);
-  }
-#pragma unroll
-  for (int t = 0; t < Cfg<W>::DMA; ++t) {
-    const uint32_t vb = (TAIL && o.chunk[t] >= kchunks) ? OOB : o.dma_b[t];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lb + 1024 * (wave * Cfg<W>::DMA + t)), 16,
-                                             vb, cs, 0, 0);
-  }
-  uint8_t* sa = stage + 2 * OPB + 256 * (wave & 3);
-  if (W == 4) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)sa, 4, o.sc_a, ss, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(sa + SCB), 4, o.sc_b, ss, 0, 0);
-  } else if (wave < 4) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)sa, 4, o.sc_a, ss, 0, 0);
+  if (wave < 4) {
+    const int ra = m0 + r;
+    o.sc = ra < M ? (uint32_t)(A2D ? (ra >> 5) : ra) * (uint32_t)A.ld_scales : OOB;
   } else {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(sa + SCB), 4, o.sc_b, ss, 0, 0);
+    const int rb = n0 + r;
+    o.sc = rb < N ? (uint32_t)(B2D ? (rb >> 5) : rb) * (uint32_t)B.ld_scales : OOB;
   }
 }
 
-template <int W>
+// Issue stage st's code loads into `slot`: 256 rows x 128 bytes of each
+// operand as 32 direct-to-LDS loads of 1 KiB (8 rows each), 4 + 4 per wave.
+// In the partial last stage, chunks at or past K point past the end and read
+// as zeros.
+template <bool TAIL>
+__device__ __forceinline__ void issue_codes(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                            const LaneOffsets& o, int st, int kchunks, uint8_t* slot,
+                                            int wave) {
+  const uint32_t cs = (uint32_t)st * ROWB;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t va = (TAIL && o.chunk[t] >= kchunks) ? OOB : o.code_a[t];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + 1024 * (wave * 4 + t)), 16, va, cs, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t vb = (TAIL && o.chunk[t] >= kchunks) ? OOB : o.code_b[t];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + OPB + 1024 * (wave * 4 + t)), 16, vb, cs,
+                                             0, 0);
+  }
+}
+
+// Issue the scale loads of stages 2p and 2p+1 into `sslot`: 16 bytes per row,
+// 64 rows per wave (`rs` is the A scales for waves 0-3, the B scales for 4-7).
+__device__ __forceinline__ void issue_scales(__amdgpu_buffer_rsrc_t rs, const LaneOffsets& o, int p,
+                                             uint8_t* sslot, int wave) {
+  uint8_t* dst = sslot + (wave < 4 ? 0 : 256 * SROWB) + 64 * SROWB * (wave & 3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, o.sc, (uint32_t)p * SROWB, 0, 0);
+}
+
 struct Acc {
-  v16f t[Cfg<W>::TI][Cfg<W>::TJ];
+  v16f t[TI][TJ];
 };
 
-// ---------------------------------------------------------------- LDS reads
-// The operand reads from LDS sit in asm blocks that wait for their own reads
-// (outputs are early-clobber: a read may land before a later read of the
-// block has taken its address).  Written in asm because the compiler cannot
-// tell these reads from the direct-to-LDS loads still in flight into other
-// ring slots and would otherwise wait for all of those first.
-// Row tiles of one operand are 2048 code bytes / 128 scale-word bytes apart.
+// ------------------------------------------------------------ asm K steps
+// Row tiles of one operand are 32 x 128 = 4096 code bytes and 32 x 16 = 512
+// scale bytes apart in a slot.  Each lane's 32-bit scale word holds the bytes
+// of 4 consecutive K-blocks, already shifted right by 8 * (l / 32); op_sel_hi
+// [0,0,0] then picks the lane's block of an even step, [1,1,0] of an odd step.
+#define MX_OPSEL_LO "0,0,0"
+#define MX_OPSEL_HI "1,1,0"
+#define MX_MFMA(C, A, B, SA, SB, OPSEL)                                                                    \
+  "v_mfma_scale_f32_32x32x64_f8f6f4 %[" #C "], %[" #A "], %[" #B "], %[" #C "], %[" #SA "], %[" #SB \
+  "] op_sel_hi:[" OPSEL "] cbsz:4 blgp:4\n\t"
+#define MX_ACC_OPERANDS(c)                                                                                 \
+  [c00] "+v"(c.t[0][0]), [c01] "+v"(c.t[0][1]), [c02] "+v"(c.t[0][2]), [c03] "+v"(c.t[0][3]),           \
+      [c10] "+v"(c.t[1][0]), [c11] "+v"(c.t[1][1]), [c12] "+v"(c.t[1][2]), [c13] "+v"(c.t[1][3])
+#define MX_NEXT_OPERANDS                                                                                   \
+  [na0] "=&v"(na[0]), [na1] "=&v"(na[1]), [nb0] "=&v"(nb[0]), [nb1] "=&v"(nb[1]), [nb2] "=&v"(nb[2]),    \
+      [nb3] "=&v"(nb[3])
+#define MX_CUR_OPERANDS                                                                                    \
+  [a0] "v"(a[0]), [a1] "v"(a[1]), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),         \
+      [sa0] "v"(sa[0]), [sa1] "v"(sa[1]), [sb0] "v"(sb[0]), [sb1] "v"(sb[1]), [sb2] "v"(sb[2]),           \
+      [sb3] "v"(sb[3])
+// 8 MFMAs of one step with the 6 operand reads of the next one interleaved.
+#define MX_STEP_BODY(OPSEL)                                   \
+  "s_nop 1\n\t"                                              \
+  MX_MFMA(c00, a0, b0, sa0, sb0, OPSEL)                       \
+  "ds_read_b128 %[na0], %[ada]\n\t"                          \
+  "ds_read_b128 %[na1], %[ada] offset:4096\n\t"              \
+  MX_MFMA(c01, a0, b1, sa0, sb1, OPSEL)                       \
+  "ds_read_b128 %[nb0], %[adb]\n\t"                          \
+  "ds_read_b128 %[nb1], %[adb] offset:4096\n\t"              \
+  MX_MFMA(c02, a0, b2, sa0, sb2, OPSEL)                       \
+  "ds_read_b128 %[nb2], %[adb] offset:8192\n\t"              \
+  "ds_read_b128 %[nb3], %[adb] offset:12288\n\t"             \
+  MX_MFMA(c03, a0, b3, sa0, sb3, OPSEL)
 
-// 4 A + 4 B operand chunks of one K step.
-__device__ __forceinline__ void lds_read_k(uint32_t ada, uint32_t adb, v4i a[4], v4i b[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:2048\n\t"
-      "ds_read_b128 %2, %8 offset:4096\n\t"
-      "ds_read_b128 %3, %8 offset:6144\n\t"
-      "ds_read_b128 %4, %9\n\t"
-      "ds_read_b128 %5, %9 offset:2048\n\t"
-      "ds_read_b128 %6, %9 offset:4096\n\t"
-      "ds_read_b128 %7, %9 offset:6144\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]),
-        "=&v"(b[3])
-      : "v"(ada), "v"(adb)
-      : "memory");
-}
-
-// 2 A + 4 B operand chunks of one K step.
-__device__ __forceinline__ void lds_read_k(uint32_t ada, uint32_t adb, v4i a[2], v4i b[4], int) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %6 offset:2048\n\t"
-      "ds_read_b128 %2, %7\n\t"
-      "ds_read_b128 %3, %7 offset:2048\n\t"
-      "ds_read_b128 %4, %7 offset:4096\n\t"
-      "ds_read_b128 %5, %7 offset:6144\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-      : "v"(ada), "v"(adb)
-      : "memory");
-}
-
-// Scale words of 4 A + 4 B row tiles.
-__device__ __forceinline__ void lds_read_scales(uint32_t ada, uint32_t adb, uint32_t sa[4], uint32_t sb[4]) {
-  asm volatile(
-      "ds_read_b32 %0, %8\n\t"
-      "ds_read_b32 %1, %8 offset:128\n\t"
-      "ds_read_b32 %2, %8 offset:256\n\t"
-      "ds_read_b32 %3, %8 offset:384\n\t"
-      "ds_read_b32 %4, %9\n\t"
-      "ds_read_b32 %5, %9 offset:128\n\t"
-      "ds_read_b32 %6, %9 offset:256\n\t"
-      "ds_read_b32 %7, %9 offset:384\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sb[0]), "=&v"(sb[1]),
-        "=&v"(sb[2]), "=&v"(sb[3])
-      : "v"(ada), "v"(adb)
-      : "memory");
-}
-
-// Scale words of 2 A + 4 B row tiles.
-__device__ __forceinline__ void lds_read_scales(uint32_t ada, uint32_t adb, uint32_t sa[2], uint32_t sb[4],
-                                                int) {
-  asm volatile(
-      "ds_read_b32 %0, %6\n\t"
-      "ds_read_b32 %1, %6 offset:128\n\t"
-      "ds_read_b32 %2, %7\n\t"
-      "ds_read_b32 %3, %7 offset:128\n\t"
-      "ds_read_b32 %4, %7 offset:256\n\t"
-      "ds_read_b32 %5, %7 offset:384\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sb[0]), "=&v"(sb[1]), "=&v"(sb[2]), "=&v"(sb[3])
-      : "v"(ada), "v"(adb)
-      : "memory");
-}
-
-template <int W>
-__device__ __forceinline__ void read_k(uint32_t ada, uint32_t adb, v4i* a, v4i* b) {
-  if constexpr (Cfg<W>::TI == 4) lds_read_k(ada, adb, a, b);
-  else lds_read_k(ada, adb, a, b, 0);
-}
-template <int W>
-__device__ __forceinline__ void read_scales(uint32_t ada, uint32_t adb, uint32_t* sa, uint32_t* sb) {
-  if constexpr (Cfg<W>::TI == 4) lds_read_scales(ada, adb, sa, sb);
-  else lds_read_scales(ada, adb, sa, sb, 0);
-}
-
-// Multiply one stage held in LDS at byte address `stage`.  Scale word of a
-// row = 4 scale bytes of the stage's 4 K-blocks; lane l of a K step ks needs
-// K-block 2*ks + l/32, so the word is shifted right by 8*(l/32) and op_sel
-// picks byte 2*ks.  `keep` masks the bytes of K-blocks that exist (all of them
-// except in a partial last stage, whose missing blocks get scale byte 0, a
-// finite scale; their codes are 0).
-template <int W>
-__device__ __forceinline__ void compute_stage(uint32_t stage, int wm, int wn, int lane, uint32_t keep,
-                                              Acc<W>& acc) {
-  constexpr int TI = Cfg<W>::TI, TJ = Cfg<W>::TJ;
-  const int l32 = lane & 31, kh = lane >> 5;
-  const int rowa = wm * TI * 32 + l32, rowb = wn * TJ * 32 + l32;   // row tile 0
-  uint32_t wa[TI], wb[TJ];
-  read_scales<W>(stage + 2 * OPB + 4 * rowa, stage + 2 * OPB + SCB + 4 * rowb, wa, wb);
-  int sa[TI], sb[TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i) sa[i] = (int)((wa[i] & keep) >> (8 * kh));
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) sb[j] = (int)((wb[j] & keep) >> (8 * kh));
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    // the chunk swizzle depends on bits 1..3 of the row only, equal for all tiles
-    v4i av[TI], bv[TJ];
-    read_k<W>(stage + rowa * ROWB + 16 * swz(rowa, 2 * ks + kh),
-              stage + OPB + rowb * ROWB + 16 * swz(rowb, 2 * ks + kh), av, bv);
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const v8i a = v8i{av[i].x, av[i].y, av[i].z, av[i].w, 0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const v8i b = v8i{bv[j].x, bv[j].y, bv[j].z, bv[j].w, 0, 0, 0, 0};
-        if (ks == 0)
-          acc.t[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc.t[i][j], 4, 4, 0, sa[i], 0,
-                                                                       sb[j]);
-        else
-          acc.t[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc.t[i][j], 4, 4, 2, sa[i], 2,
-                                                                       sb[j]);
-      }
-    }
+// One step on operands a, b; reads the next step's operands (LDS byte
+// addresses ada, adb of its row tile 0) into na, nb.
+template <bool ODD>
+__device__ __forceinline__ void step(Acc& c, const v4i a[TI], const v4i b[TJ], const int sa[TI],
+                                     const int sb[TJ], uint32_t ada, uint32_t adb, v4i na[TI], v4i nb[TJ]) {
+  if constexpr (!ODD) {
+    asm volatile(MX_STEP_BODY(MX_OPSEL_LO)
+                 MX_MFMA(c10, a1, b0, sa1, sb0, MX_OPSEL_LO)
+                 MX_MFMA(c11, a1, b1, sa1, sb1, MX_OPSEL_LO)
+                 MX_MFMA(c12, a1, b2, sa1, sb2, MX_OPSEL_LO)
+                 MX_MFMA(c13, a1, b3, sa1, sb3, MX_OPSEL_LO)
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_ACC_OPERANDS(c), MX_NEXT_OPERANDS
+                 : MX_CUR_OPERANDS, [ada] "v"(ada), [adb] "v"(adb)
+                 : "memory");
+  } else {
+    asm volatile(MX_STEP_BODY(MX_OPSEL_HI)
+                 MX_MFMA(c10, a1, b0, sa1, sb0, MX_OPSEL_HI)
+                 MX_MFMA(c11, a1, b1, sa1, sb1, MX_OPSEL_HI)
+                 MX_MFMA(c12, a1, b2, sa1, sb2, MX_OPSEL_HI)
+                 MX_MFMA(c13, a1, b3, sa1, sb3, MX_OPSEL_HI)
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_ACC_OPERANDS(c), MX_NEXT_OPERANDS
+                 : MX_CUR_OPERANDS, [ada] "v"(ada), [adb] "v"(adb)
+                 : "memory");
   }
 }
 
-// Wait until at most `stages_ahead` stages of this wave's vector-memory loads
-// are outstanding (0, 1 or 2 stages).
-template <int W>
-__device__ __forceinline__ void wait_vmcnt(int stages_ahead) {
+// The last (odd) step of a stage; reads the next stage's first-step operands
+// (ada, adb) and its 8 scale bytes per row tile (adsa, adsb) into wa, wb.
+__device__ __forceinline__ void step_last(Acc& c, const v4i a[TI], const v4i b[TJ], const int sa[TI],
+                                          const int sb[TJ], uint32_t ada, uint32_t adb, uint32_t adsa,
+                                          uint32_t adsb, v4i na[TI], v4i nb[TJ], v2u wa[TI], v2u wb[TJ]) {
+  asm volatile(MX_STEP_BODY(MX_OPSEL_HI)
+               "ds_read_b64 %[wa0], %[adsa]\n\t"
+               "ds_read_b64 %[wa1], %[adsa] offset:512\n\t"
+               MX_MFMA(c10, a1, b0, sa1, sb0, MX_OPSEL_HI)
+               "ds_read_b64 %[wb0], %[adsb]\n\t"
+               "ds_read_b64 %[wb1], %[adsb] offset:512\n\t"
+               MX_MFMA(c11, a1, b1, sa1, sb1, MX_OPSEL_HI)
+               "ds_read_b64 %[wb2], %[adsb] offset:1024\n\t"
+               "ds_read_b64 %[wb3], %[adsb] offset:1536\n\t"
+               MX_MFMA(c12, a1, b2, sa1, sb2, MX_OPSEL_HI)
+               MX_MFMA(c13, a1, b3, sa1, sb3, MX_OPSEL_HI)
+               "s_waitcnt lgkmcnt(0)"
+               : MX_ACC_OPERANDS(c), MX_NEXT_OPERANDS, [wa0] "=&v"(wa[0]), [wa1] "=&v"(wa[1]),
+                 [wb0] "=&v"(wb[0]), [wb1] "=&v"(wb[1]), [wb2] "=&v"(wb[2]), [wb3] "=&v"(wb[3])
+               : MX_CUR_OPERANDS, [ada] "v"(ada), [adb] "v"(adb), [adsa] "v"(adsa), [adsb] "v"(adsb)
+               : "memory");
+}
+
+// The first stage's first-step operands and scale bytes.
+__device__ __forceinline__ void read_first(uint32_t ada, uint32_t adb, uint32_t adsa, uint32_t adsb,
+                                           v4i a[TI], v4i b[TJ], v2u wa[TI], v2u wb[TJ]) {
+  asm volatile(
+      "ds_read_b128 %[a0], %[ada]\n\t"
+      "ds_read_b128 %[a1], %[ada] offset:4096\n\t"
+      "ds_read_b128 %[b0], %[adb]\n\t"
+      "ds_read_b128 %[b1], %[adb] offset:4096\n\t"
+      "ds_read_b128 %[b2], %[adb] offset:8192\n\t"
+      "ds_read_b128 %[b3], %[adb] offset:12288\n\t"
+      "ds_read_b64 %[wa0], %[adsa]\n\t"
+      "ds_read_b64 %[wa1], %[adsa] offset:512\n\t"
+      "ds_read_b64 %[wb0], %[adsb]\n\t"
+      "ds_read_b64 %[wb1], %[adsb] offset:512\n\t"
+      "ds_read_b64 %[wb2], %[adsb] offset:1024\n\t"
+      "ds_read_b64 %[wb3], %[adsb] offset:1536\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [a0] "=&v"(a[0]), [a1] "=&v"(a[1]), [b0] "=&v"(b[0]), [b1] "=&v"(b[1]), [b2] "=&v"(b[2]),
+        [b3] "=&v"(b[3]), [wa0] "=&v"(wa[0]), [wa1] "=&v"(wa[1]), [wb0] "=&v"(wb[0]), [wb1] "=&v"(wb[1]),
+        [wb2] "=&v"(wb[2]), [wb3] "=&v"(wb[3])
+      : [ada] "v"(ada), [adb] "v"(adb), [adsa] "v"(adsa), [adsb] "v"(adsb)
+      : "memory");
+}
+
+// Wait states between the last MFMA and any later instruction that reads or
+// writes the accumulators (more than the 16-pass requirement).
+__device__ __forceinline__ void drain(Acc& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : MX_ACC_OPERANDS(c));
+}
+
+#undef MX_STEP_BODY
+#undef MX_CUR_OPERANDS
+#undef MX_NEXT_OPERANDS
+#undef MX_ACC_OPERANDS
+#undef MX_MFMA
+#undef MX_OPSEL_LO
+#undef MX_OPSEL_HI
+
+// Wait until at most n of this wave's vector-memory loads are outstanding
+// (n = 0, the code loads of one stage, or those plus one scale load).
+__device__ __forceinline__ void wait_vmcnt(int n) {
   // s_waitcnt encoding (gfx9): vmcnt bits [3:0] and [15:14]; expcnt and
   // lgkmcnt left at their maxima (no wait).
 #define MX_VMCNT(N_) (((N_) & 0xF) | (((N_) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-  constexpr int L = Cfg<W>::LOADS;
-  switch (stages_ahead) {
-    case 0: __builtin_amdgcn_s_waitcnt(MX_VMCNT(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(MX_VMCNT(L)); break;
-    default: __builtin_amdgcn_s_waitcnt(MX_VMCNT(2 * L)); break;
-  }
+  if (n >= CODE_LOADS + 1) __builtin_amdgcn_s_waitcnt(MX_VMCNT(CODE_LOADS + 1));
+  else if (n >= CODE_LOADS) __builtin_amdgcn_s_waitcnt(MX_VMCNT(CODE_LOADS));
+  else __builtin_amdgcn_s_waitcnt(MX_VMCNT(0));
 #undef MX_VMCNT
+}
+
+// Workgroup barrier without the fence of __syncthreads() (which would wait for
+// every load in flight).  The empty asm statements keep the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // C tile (rows m0.., cols n0..) = A[m0:m0+256] * B[n0:n0+256]^T over all K.
 // Operand rows past M/N read as zeros; the caller's epilogue stores only
 // valid rows and columns.  Byte extents of the operands must be < 2 GiB.
-// `lds` holds the NS ring slots back to back.
-template <int W, bool A2D, bool B2D>
-__device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B, int M, int N, int K,
-                                         int m0, int n0, uint8_t* lds, Acc<W>& acc) {
-  static_assert(NS == 4, "wait_vmcnt assumes at most 2 stages queued behind the current one");
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// `lds` holds LDS_BYTES: the two code slots, then the two scale slots.
+template <bool A2D, bool B2D>
+__device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B, int M, int N, int K, int m0,
+                                         int n0, uint8_t* lds, Acc& acc) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int i = 0; i < Cfg<W>::TI; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg<W>::TJ; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc.t[i][j][r] = 0.0f;
 
@@ -311,36 +303,80 @@ __device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B,
   if (nstages == 0) return;
   const __amdgpu_buffer_rsrc_t ra = rsrc(A.codes, (uint32_t)(M * A.ld_codes));
   const __amdgpu_buffer_rsrc_t rb = rsrc(B.codes, (uint32_t)(N * B.ld_codes));
-  const __amdgpu_buffer_rsrc_t rsa = rsrc(A.scales, (uint32_t)((A2D ? M / 32 : M) * A.ld_scales));
-  const __amdgpu_buffer_rsrc_t rsb = rsrc(B.scales, (uint32_t)((B2D ? N / 32 : N) * B.ld_scales));
-  LaneOffsets<W> o;
-  lane_offsets<W, A2D, B2D>(A, B, M, N, m0, n0, wave, lane, o);
+  const __amdgpu_buffer_rsrc_t rs =
+      wave < 4 ? rsrc(A.scales, (uint32_t)((A2D ? M / 32 : M) * A.ld_scales))
+               : rsrc(B.scales, (uint32_t)((B2D ? N / 32 : N) * B.ld_scales));
+  LaneOffsets o;
+  lane_offsets<A2D, B2D>(A, B, M, N, m0, n0, wave, lane, o);
   const int kchunks = (K - nfull * TK) / 32;          // K-blocks in the tail stage (0 if none)
-  const uint32_t tail_keep = (1u << (8 * kchunks)) - 1u;
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;   // LDS byte address of slot 0
+  // scale bytes of the tail stage's blocks: low word blocks 0-3, high word 4-7
+  const uint32_t tail_lo = kchunks >= 4 ? 0xFFFFFFFFu : (1u << (8 * kchunks)) - 1u;
+  const uint32_t tail_hi = kchunks <= 4 ? 0u : (1u << (8 * (kchunks - 4))) - 1u;
+  uint8_t* const sslots = lds + 2 * STAGE_BYTES;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;   // LDS byte address of code slot 0
+  const uint32_t sl_addr = lds_addr + 2 * STAGE_BYTES;             // ... of scale slot 0
 
-  auto issue = [&](int p) {
-    uint8_t* slot = lds + (p % NS) * STAGE_BYTES;
-    if (p < nfull) issue_stage<W, false>(ra, rb, rsa, rsb, o, p, 4, slot, wave);
-    else if (p < nstages) issue_stage<W, true>(ra, rb, rsa, rsb, o, p, kchunks, slot, wave);
-  };
+  // This lane's LDS read offsets inside a slot (the chunk swizzle depends on
+  // bits 1..3 of the row only, equal for all row tiles of the wave).
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int rowa = wm * TI * 32 + l32, rowb = wn * TJ * 32 + l32;
+  uint32_t ra_k[4], rb_k[4];
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) issue(p);
-  for (int s = 0; s < nstages; ++s) {
-    // loads of the stages after s that are already issued stay in flight
-    const int ahead = (nstages - 1 - s) < (NS - 2) ? (nstages - 1 - s) : (NS - 2);
-    wait_vmcnt<W>(ahead);                   // this wave's stage-s loads landed
-    // every wave's did, and the slot of stage s-1 is free.  A bare barrier:
-    // __syncthreads() would add a fence that waits for all loads in flight.
-    // The empty asm statements keep the compiler from moving memory
-    // operations (the next loads into the freed slot) across it.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue(s + NS - 1);
-    compute_stage<W>(lds_addr + (uint32_t)((s % NS) * STAGE_BYTES), wm, wn, lane,
-                     s < nfull ? 0xFFFFFFFFu : tail_keep, acc);
+  for (int ks = 0; ks < 4; ++ks) {
+    ra_k[ks] = rowa * ROWB + 16 * swz(rowa, 2 * ks + kh);
+    rb_k[ks] = OPB + rowb * ROWB + 16 * swz(rowb, 2 * ks + kh);
   }
+  const uint32_t s_a = rowa * SROWB, s_b = 256 * SROWB + rowb * SROWB;
+  const int sh = 8 * kh;
+
+  // Loads of stage p: its codes, and on even stages the scales of p and p+1.
+  auto issue = [&](int p) {
+    if (p >= nstages) return;
+    uint8_t* slot = lds + (p & 1) * STAGE_BYTES;
+    if (!(p & 1)) issue_scales(rs, o, p >> 1, sslots + ((p >> 1) & 1) * SSLOT, wave);
+    if (p < nfull) issue_codes<false>(ra, rb, o, p, 8, slot, wave);
+    else issue_codes<true>(ra, rb, o, p, kchunks, slot, wave);
+  };
+  auto loads_of = [&](int p) { return p >= nstages ? 0 : CODE_LOADS + ((p & 1) ? 0 : 1); };
+
+  issue(0);
+  issue(1);
+  wait_vmcnt(loads_of(1));                  // this wave's stage-0 loads landed
+  bare_barrier();                           // ... and every wave's
+  v4i a[TI], b[TJ], na[TI], nb[TJ];
+  v2u wa[TI], wb[TJ];
+  read_first(lds_addr + ra_k[0], lds_addr + rb_k[0], sl_addr + s_a, sl_addr + s_b, a, b, wa, wb);
+  for (int s = 0; s < nstages; ++s) {
+    const uint32_t slot = lds_addr + (uint32_t)((s & 1) * STAGE_BYTES);
+    const uint32_t keep_lo = s < nfull ? 0xFFFFFFFFu : tail_lo;
+    const uint32_t keep_hi = s < nfull ? 0xFFFFFFFFu : tail_hi;
+    int sa[TI], sb[TJ], sa2[TI], sb2[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      sa[i] = (int)((wa[i].x & keep_lo) >> sh);
+      sa2[i] = (int)((wa[i].y & keep_hi) >> sh);
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      sb[j] = (int)((wb[j].x & keep_lo) >> sh);
+      sb2[j] = (int)((wb[j].y & keep_hi) >> sh);
+    }
+    step<false>(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb);
+    step<true>(acc, na, nb, sa, sb, slot + ra_k[2], slot + rb_k[2], a, b);
+    step<false>(acc, a, b, sa2, sb2, slot + ra_k[3], slot + rb_k[3], na, nb);
+    // Stage s+1: this wave's loads landed, then every wave's.  Every wave has
+    // also read all of stage s's codes, so its slot takes stage s+2.
+    wait_vmcnt(0);
+    bare_barrier();
+    issue(s + 2);
+    // The next stage's scale bytes: the other half of this scale slot for an
+    // even s, the next scale slot for an odd s.  In the last stage the reads
+    // of the (unused) next slot are harmless.
+    const uint32_t next = lds_addr + (uint32_t)(((s + 1) & 1) * STAGE_BYTES);
+    const uint32_t snext = sl_addr + (uint32_t)((((s + 1) >> 1) & 1) * SSLOT + 8 * ((s + 1) & 1));
+    step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb);
+  }
+  drain(acc);
   __syncthreads();                          // LDS may be reused by the caller
 }
 
@@ -348,9 +384,8 @@ __device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B,
 // resource ends after row mlim (relative to the tile origin C), and lanes
 // whose column is >= nlim point past it, so nothing outside the matrix is
 // written.  Row offsets are wave-uniform (scalar), column offsets per lane.
-template <int W, bool OUT_BF16>
-__device__ __forceinline__ void store_tile(const Acc<W>& acc, void* C, int ldc, int mlim, int nlim) {
-  constexpr int TI = Cfg<W>::TI, TJ = Cfg<W>::TJ;
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int mlim, int nlim) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;

@@ -19,14 +19,15 @@ from gpu_util import banner, check_gemm, host, need_gpu, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _upload(codes, scales, block="1d", pad=True):
-    """Upload oracle codes/scales; pad=True stores scale rows with a stride
-    rounded up to 4 bytes (the layout the quantizer allocates), pad=False
-    keeps them dense (the GEMM then takes its generic path)."""
+def _upload(codes, scales, block="1d", pad=16):
+    """Upload oracle codes/scales.  pad=16 stores scale rows with a stride
+    rounded up to 16 bytes (the layout the quantizer allocates, which the
+    256x256 path needs); pad=4 or 0 (dense) make the GEMM take its generic
+    path."""
     rows = codes.shape[0]
     sc = to_dev(scales)
     if pad:
-        ld = (scales.shape[1] + 3) // 4 * 4
+        ld = (scales.shape[1] + pad - 1) // pad * pad
         buf = torch.full((scales.shape[0], ld), 0xFF, dtype=torch.uint8, device="cuda")
         buf[:, :scales.shape[1]] = sc
         sc = buf[:, :scales.shape[1]]
@@ -65,17 +66,19 @@ def test_gemm_single_block_exact():
     assert np.array_equal(c.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("M,N,K,pad", [(200, 72, 96, True), (129, 257, 2880, True), (1, 1, 64, True),
-                                       (300, 128, 4128, False), (300, 520, 2880, True),
-                                       (513, 257, 4128, True), (256, 256, 32, True),
-                                       (520, 300, 2880, False), (260, 768, 160, True)])
+@pytest.mark.parametrize("M,N,K,pad", [(200, 72, 96, 16), (129, 257, 2880, 16), (1, 1, 64, 16),
+                                       (300, 128, 4128, 0), (300, 520, 2880, 16),
+                                       (513, 257, 4128, 16), (256, 256, 32, 16),
+                                       (520, 300, 2880, 0), (260, 768, 160, 16), (264, 512, 224, 16),
+                                       (512, 256, 2816, 16), (256, 512, 384, 16), (300, 300, 2880, 4)])
 @pytest.mark.parametrize("a_block,b_block", [("1d", "1d"), ("1d", "2d"), ("2d", "2d")])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 def test_gemm_ragged(M, N, K, pad, a_block, b_block, out):
     """Shapes covering several 256x256 tiles with ragged M, N and K tails (the
-    K tails leave 1, 2 or 3 blocks in the last 128-deep stage), the 128x128
-    path, and scale rows padded (the quantizer's layout) or dense.  Padding
-    bytes are 0xFF so reading one would poison the result."""
+    K tails leave 1 to 7 blocks in the last 256-deep stage, after an odd or
+    even number of full stages), the 128x128 path, and scale rows padded to
+    16 bytes (the quantizer's layout), to 4 bytes or dense.  Padding bytes are
+    0xFF so reading one would poison the result."""
     need_gpu()
     if a_block == "2d" and M % 32:
         M = (M + 31) // 32 * 32
@@ -134,9 +137,9 @@ def test_gemm_mismatched_k_raises():
 
 
 # ---------------------------------------------------------------- grouped
-def _grouped_case(rng, offsets, N, K, out_dtype, pad=True):
-    """pad=True: scale rows (and the per-expert stride) padded to 4 bytes with
-    0xFF in the padding, the layout the 256x256 path takes."""
+def _grouped_case(rng, offsets, N, K, out_dtype, pad=16):
+    """pad=16: scale rows (and the per-expert stride) padded to 16 bytes with
+    0xFF in the padding, the layout the 256x256 path takes; pad=0: dense."""
     E = len(offsets) - 1
     M = int(offsets[-1])
     ac, as_ = _rand_mx(rng, M, K)
@@ -145,7 +148,7 @@ def _grouped_case(rng, offsets, N, K, out_dtype, pad=True):
     a = _upload(ac, as_, pad=pad)
     bsd = to_dev(bs)
     if pad:
-        ld = (bs.shape[2] + 3) // 4 * 4
+        ld = (bs.shape[2] + pad - 1) // pad * pad
         buf = torch.full((E, bs.shape[1], ld), 0xFF, dtype=torch.uint8, device="cuda")
         buf[:, :, :bs.shape[2]] = bsd
         bsd = buf[:, :, :bs.shape[2]]
@@ -163,7 +166,7 @@ def test_grouped_gemm_ragged_experts(offsets, out):
     need_gpu()
     rng = np.random.default_rng(len(offsets) * 11 + offsets[-1])
     banner(f"grouped offsets={offsets} {out}")
-    _grouped_case(rng, offsets, 96, 160, out, pad=False)
+    _grouped_case(rng, offsets, 96, 160, out, pad=0)
 
 
 @pytest.mark.parametrize("offsets", [[0, 5, 5, 300, 333], [0, 600], [0, 0, 0, 257, 257, 800],
@@ -266,13 +269,10 @@ def test_moe_grouped_full_size():
     banner("moe full size: quantize experts")
     xg = workloads.to_bf16(xt)[torch.from_numpy(tok)]
     qa = mx.quantize(xg.cuda())
-    bcodes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
-    bscales = torch.empty((E, N // 32, K // 32), dtype=torch.uint8, device="cuda")
+    qb = mx.empty_mx(N, K, "2d", experts=E)
     for e in range(E):
         we = workloads.to_bf16(workloads.moe_expert_weight(e)).cuda()
-        mx.quantize(we, axis="dim0", block="2d",
-                    out=mx.MXTensor(bcodes[e], bscales[e], N, K, "2d"))
-    qb = mx.MXTensor(bcodes, bscales, N, K, "2d")
+        mx.quantize(we, axis="dim0", block="2d", out=mx.expert(qb, e))
     banner("moe full size: grouped gemm")
     y = mx.grouped_gemm(qa, to_dev(offsets), qb, torch.bfloat16)
     yh = host(y.float())
