@@ -114,13 +114,15 @@ class MXTensor:
 def empty_mx(rows, K, block="1d", device="cuda", experts=None):
     """Allocate an uninitialised MX operand (codes + scales) on `device`.
 
-    Scale rows are padded to a multiple of 16 bytes (the row stride is carried
-    in the tensor), which lets the GEMMs fetch scales 16 aligned bytes per row
-    at a time.  With `experts=E` the tensors get a leading expert dimension
+    Code rows are padded to a multiple of 128 bytes and scale rows to a
+    multiple of 16 bytes (the row strides are carried in the tensors), so the
+    GEMMs' row segments start on cache-line boundaries and their scale fetches
+    are aligned.  With `experts=E` the tensors get a leading expert dimension
     (the stacked weights of grouped_gemm); expert e is `expert(q, e)`."""
     srows = rows // 32 if block == "2d" else rows
     lead = () if experts is None else (experts,)
-    codes = torch.empty(lead + (rows, K // 2), dtype=torch.uint8, device=device)
+    ldc = (K // 2 + 127) // 128 * 128
+    codes = torch.empty(lead + (rows, ldc), dtype=torch.uint8, device=device)[..., :K // 2]
     ld = (K // 32 + 15) // 16 * 16
     scales = torch.empty(lead + (srows, ld), dtype=torch.uint8, device=device)[..., :K // 32]
     return MXTensor(codes, scales, rows, K, block)

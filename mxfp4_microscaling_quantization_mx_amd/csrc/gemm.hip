@@ -26,89 +26,168 @@ namespace mx {
 namespace {
 
 // ---------------------------------------------------------------- 256x256 tiles
-// Workgroup b runs on XCD b % 8.  Renumber so that consecutive ids share an
-// XCD (and its L2), then walk tiles in groups of 8 M-tiles so that the
-// workgroups resident on one XCD reuse a few A and B panels.
-__device__ __forceinline__ void tile_of(int b, int nwg, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int per = nwg / 8, rem = nwg % 8;
+// Persistent kernels: one workgroup per CU (G workgroups), each running the
+// tiles t = k*G + l for k = 0, 1, ...  Workgroup b runs on XCD b % 8; its
+// position l makes the workgroups of one XCD take consecutive tile numbers,
+// and tile numbers are walked in groups of 8 M-tiles, so the tiles that one
+// XCD works on at a time share a few A and B panels in its L2.
+__device__ __forceinline__ int xcd_position(int b, int G) {
+  const int per = G / 8, rem = G % 8;
   const int x = b % 8, k = b / 8;
-  const int t = x * per + (x < rem ? x : rem) + k;
+  return x * per + (x < rem ? x : rem) + k;
+}
+
+__device__ __forceinline__ void group_order(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GM = 8;
   const int group = t / (GM * tiles_n);
   const int first_m = group * GM;
   const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-  const int in = t % (GM * tiles_n);
+  const int in = t - group * GM * tiles_n;
   tm = first_m + in % gm;
   tn = in / gm;
 }
 
 constexpr int GW = t256::WAVES;
 
+struct DenseSched {
+  const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
+  int M, N, tiles_m, tiles_n, G, l;
+  __device__ int count() const {
+    const int total = tiles_m * tiles_n;
+    return l < total ? (total - l + G - 1) / G : 0;
+  }
+  __device__ t256::TileInfo tile(int j) const {
+    int tm, tn;
+    group_order(j * G + l, tiles_m, tiles_n, tm, tn);
+    t256::TileInfo ti;
+    ti.a_codes = a_codes;
+    ti.a_scales = a_scales;
+    ti.b_codes = b_codes;
+    ti.b_scales = b_scales;
+    ti.m0 = tm * t256::TM;
+    ti.n0 = tn * t256::TN;
+    ti.M = M;
+    ti.N = N;
+    ti.c_row0 = ti.m0;
+    return ti;
+  }
+};
+
 template <bool A2D, bool B2D, bool OUT_BF16>
-__global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B, int64_t M, int64_t N,
-                                                        int64_t K, void* C, int64_t ldc, int tiles_m,
-                                                        int tiles_n) {
+__global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B, int M, int N, int K, void* C,
+                                                        int64_t ldc, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
-  int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * t256::TM, n0 = tn * t256::TN;
-  t256::Acc acc;
-  t256::mainloop<A2D, B2D>(A, B, (int)M, (int)N, (int)K, m0, n0, lds, acc);
-  void* Ct = OUT_BF16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)m0 * ldc + n0)
-                      : (void*)(static_cast<float*>(C) + (int64_t)m0 * ldc + n0);
-  t256::store_tile<OUT_BF16>(acc, Ct, (int)ldc, (int)(M - m0), (int)(N - n0));
+  const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n, (int)gridDim.x,
+                      xcd_position(blockIdx.x, gridDim.x)};
+  const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
+  t256::run_tiles<A2D, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
 }
 
-// Grouped (MoE) GEMM on 256x256 tiles.  The grid enumerates (row-tile slot,
-// column tile) pairs, renumbered like the dense kernel; a slot is mapped to
-// (expert, 256-row tile of that expert) from the device offsets, so the
-// schedule needs no host synchronization.  The slot count is an upper bound
-// (each expert adds at most one partial tile); slots past the last tile exit.
-template <bool B2D, bool OUT_BF16>
-__global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxOperand B, int64_t M_cap,
-                                                                int64_t N, int64_t K,
-                                                                const int32_t* __restrict__ offsets, int E,
-                                                                int64_t stride_codes, int64_t stride_scales,
-                                                                void* C, int64_t ldc, int slots, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
-  __shared__ int s_expert, s_row0, s_rows;
-  int slot, tn;
-  tile_of(blockIdx.x, gridDim.x, slots, tiles_n, slot, tn);
-  if (threadIdx.x == 0) {
-    int64_t acc_tiles = 0;
-    int ex = -1, r0 = 0, nr = 0;
-    for (int e = 0; e < E; ++e) {
-      int64_t lo = offsets[e], hi = offsets[e + 1];
-      lo = lo < 0 ? 0 : (lo > M_cap ? M_cap : lo);
-      hi = hi < lo ? lo : (hi > M_cap ? M_cap : hi);
-      const int64_t tiles = (hi - lo + t256::TM - 1) / t256::TM;
-      if (slot < acc_tiles + tiles) {
-        ex = e;
-        r0 = (int)(lo + (slot - acc_tiles) * t256::TM);
-        nr = (int)(hi - r0 < t256::TM ? hi - r0 : t256::TM);
+// Grouped (MoE) GEMM.  A row tile ("slot") never straddles two experts: the
+// slots of expert e are the ceil(rows_e / 256) tiles of its rows, numbered in
+// expert order.  Each workgroup first builds, in LDS, the clamped row range of
+// every expert and the exclusive prefix count of slots, from the device
+// offsets (so the schedule needs no host synchronization); a tile's expert is
+// then found by one wave-wide comparison against that prefix.
+constexpr int GG_EMAX = 1024;               // experts the LDS table holds
+
+__device__ __forceinline__ int lds_i32(const int* p) {
+  int v;
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+  // an asm read that waits only for itself (not for loads in flight to LDS)
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+struct GroupedSched {
+  const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
+  int64_t stride_codes, stride_scales;      // between experts of B
+  int lda, ldsa, N, tiles_n, E, total_slots, G, l;
+  const int* tab;                           // LDS: pre [E+1] exclusive prefix of slots, lo [E], hi [E]
+  __device__ int count() const {
+    const int total = total_slots * tiles_n;
+    return l < total ? (total - l + G - 1) / G : 0;
+  }
+  __device__ t256::TileInfo tile(int j) const {
+    int slot, tn;
+    group_order(j * G + l, total_slots, tiles_n, slot, tn);
+    const int* pre = tab;
+    const int* lo = tab + GG_EMAX + 1;
+    const int* hi = lo + GG_EMAX;
+    const int lane = threadIdx.x & 63;
+    int ex = E - 1;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      const int p0 = e < E ? lds_i32(pre + e) : 0x7FFFFFFF;
+      const int p1 = e < E ? lds_i32(pre + e + 1) : 0x7FFFFFFF;
+      const unsigned long long m = __ballot(slot >= p0 && slot < p1);
+      if (m) {
+        ex = base + __ffsll((long long)m) - 1;
         break;
       }
-      acc_tiles += tiles;
     }
-    s_expert = ex;
-    s_row0 = r0;
-    s_rows = nr;
+    ex = __builtin_amdgcn_readfirstlane(ex);
+    const int row0 = __builtin_amdgcn_readfirstlane(lds_i32(lo + ex) + (slot - lds_i32(pre + ex)) * t256::TM);
+    const int end = __builtin_amdgcn_readfirstlane(lds_i32(hi + ex));
+    const int rows = end - row0 < t256::TM ? end - row0 : t256::TM;
+    t256::TileInfo ti;
+    ti.a_codes = a_codes + (int64_t)row0 * lda;
+    ti.a_scales = a_scales + (int64_t)row0 * ldsa;
+    ti.b_codes = b_codes + (int64_t)ex * stride_codes;
+    ti.b_scales = b_scales + (int64_t)ex * stride_scales;
+    ti.m0 = 0;
+    ti.n0 = tn * t256::TN;
+    ti.M = rows;
+    ti.N = N;
+    ti.c_row0 = row0;
+    return ti;
+  }
+};
+
+template <bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxOperand B, int64_t M_cap, int N,
+                                                                int K, const int32_t* __restrict__ offsets, int E,
+                                                                int64_t stride_codes, int64_t stride_scales,
+                                                                void* C, int64_t ldc, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
+  __shared__ int tab[3 * GG_EMAX + 1];
+  int* pre = tab;
+  int* lo = tab + GG_EMAX + 1;
+  int* hi = lo + GG_EMAX;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      int64_t l0 = 0, h0 = 0;
+      if (e < E) {
+        l0 = offsets[e];
+        h0 = offsets[e + 1];
+        l0 = l0 < 0 ? 0 : (l0 > M_cap ? M_cap : l0);
+        h0 = h0 < l0 ? l0 : (h0 > M_cap ? M_cap : h0);
+      }
+      const int tiles = (int)((h0 - l0 + t256::TM - 1) / t256::TM);
+      int incl = tiles;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+      }
+      if (e < E) {
+        pre[e] = carry + incl - tiles;
+        lo[e] = (int)l0;
+        hi[e] = (int)h0;
+      }
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) pre[E] = carry;
   }
   __syncthreads();
-  const int ex = s_expert;
-  if (ex < 0) return;
-  MxOperand Ae = A;
-  Ae.codes = A.codes + (int64_t)s_row0 * A.ld_codes;
-  Ae.scales = A.scales + (int64_t)s_row0 * A.ld_scales;
-  MxOperand Be = B;
-  Be.codes = B.codes + (int64_t)ex * stride_codes;
-  Be.scales = B.scales + (int64_t)ex * stride_scales;
-  const int n0 = tn * t256::TN;
-  t256::Acc acc;
-  t256::mainloop<false, B2D>(Ae, Be, s_rows, (int)N, (int)K, 0, n0, lds, acc);
-  void* Ct = OUT_BF16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)s_row0 * ldc + n0)
-                      : (void*)(static_cast<float*>(C) + (int64_t)s_row0 * ldc + n0);
-  t256::store_tile<OUT_BF16>(acc, Ct, (int)ldc, s_rows, (int)(N - n0));
+  const GroupedSched sc{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
+                        (int)A.ld_scales, N, tiles_n, E, pre[E], (int)gridDim.x,
+                        xcd_position(blockIdx.x, gridDim.x), tab};
+  const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
+  t256::run_tiles<false, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
 }
 
 // ---------------------------------------------------------------- 128x128 tiles
@@ -294,6 +373,19 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(MxOperand A, MxOperand B, 
 
 }  // namespace
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   // 256x256 tiles: scale rows are fetched 16 bytes at a time (16-byte aligned
@@ -301,13 +393,15 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) &&
                      ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
   const bool small = a.M * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
-                     a.M * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31);
+                     a.M * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31) && a.K < (1ll << 31);
   if (a.M >= 256 && a.N >= 256 && words && small) {
     const int tiles_m = (int)((a.M + 255) / 256), tiles_n = (int)((a.N + 255) / 256);
-    const unsigned nwg = (unsigned)(tiles_m * tiles_n);
-#define MX_G256(A_, B_, O_)                                                                  \
-  hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M, a.N, \
-                     a.K, a.C, a.ldc, tiles_m, tiles_n)
+    const int tiles = tiles_m * tiles_n;
+    const int cus = cu_count();
+    const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
+#define MX_G256(A_, B_, O_)                                                                        \
+  hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, (int)a.M, \
+                     (int)a.N, (int)a.K, a.C, a.ldc, tiles_m, tiles_n)
     if (a.out_bf16) {
       if (a.a_2d) { if (a.b_2d) MX_G256(true, true, true); else MX_G256(true, false, true); }
       else { if (a.b_2d) MX_G256(false, true, true); else MX_G256(false, false, true); }
@@ -337,15 +431,17 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st) {
   const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) && (a.stride_scales % 16 == 0) &&
                      ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
   const bool small = 256 * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
-                     256 * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31);
-  if (a.N >= 256 && words && small) {
-    const int slots = (int)((a.M_cap + 255) / 256 + a.E);
-    const int tiles_n = (int)((a.N + 255) / 256);
-    const unsigned nwg = (unsigned)(slots * tiles_n);
-#define MX_GG256(B_, O_)                                                                       \
-  hipLaunchKernelGGL((k_grouped_gemm256<B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap, \
-                     a.N, a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, slots,     \
-                     tiles_n)
+                     256 * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31) && a.K < (1ll << 31);
+  // upper bound on row tiles: each expert adds at most one partial tile
+  const int64_t slot_bound = (a.M_cap + 255) / 256 + a.E;
+  const int tiles_n = (int)((a.N + 255) / 256);
+  if (a.N >= 256 && words && small && a.E <= GG_EMAX && slot_bound * tiles_n < (1ll << 31)) {
+    const int64_t tiles = slot_bound * tiles_n;
+    const int cus = cu_count();
+    const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
+#define MX_GG256(B_, O_)                                                                                  \
+  hipLaunchKernelGGL((k_grouped_gemm256<B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap,     \
+                     (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, tiles_n)
     if (a.out_bf16) {
       if (a.b_2d) MX_GG256(true, true); else MX_GG256(false, true);
     } else {

@@ -37,6 +37,12 @@
 // and the first read of its result (after the loop).  One barrier per stage,
 // before its last step: every wave has then read the stage's codes, so its
 // slot is refilled with the stage two ahead while the last step runs.
+//
+// Persistent schedule: one workgroup per CU walks its list of tiles, and the
+// stage sequence runs on across tile boundaries: the first two stages of the
+// next tile are loaded while the last stage of the current one is multiplied
+// and its result stored, so neither the pipeline fill nor the epilogue leaves
+// the load path idle.
 #pragma once
 
 #include "mx_device.h"
@@ -75,62 +81,84 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 constexpr uint32_t OOB = 0x80000000u;        // an offset past any operand (validated < 2 GiB)
 
-// Per-lane 32-bit byte offsets of the global loads, computed once per tile.
-struct LaneOffsets {
-  uint32_t code_a[4], code_b[4];   // code chunk of each code load
-  int chunk[4];                    // its logical chunk (K-block within the stage)
-  uint32_t sc;                     // this lane's scale row (A rows: waves 0-3, B rows: 4-7)
+// One 256x256 output tile: A rows [m0, m0+256) (valid below M) of the
+// operand at a_codes/a_scales, B rows [n0, n0+256) (valid below N), and the
+// output row of its first row.  All fields are wave-uniform.
+struct TileInfo {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int m0, n0, M, N;
+  int64_t c_row0;
 };
 
-template <bool A2D, bool B2D>
-__device__ __forceinline__ void lane_offsets(const MxOperand& A, const MxOperand& B, int M, int N, int m0,
-                                             int n0, int wave, int lane, LaneOffsets& o) {
+// Row strides (bytes) shared by all tiles of a launch.
+struct Strides {
+  int lda, ldsa, ldb, ldsb;
+};
+
+// Per-lane global offsets of this wave's 8 code loads of a tile (stage 0):
+// load t of each operand covers rows 8*(4*wave+t) .. +8, lane l the swizzled
+// chunk of row l/8 (load_chunk: its K-block within the stage); rows past the
+// limits point past the end (zeros).
+__device__ __forceinline__ int load_chunk(int wave, int lane, int t) {
+  return swz(8 * (wave * 4 + t) + (lane >> 3), lane & 7);
+}
+
+__device__ __forceinline__ void code_offsets(const TileInfo& ti, const Strides& sd, int wave, int lane, uint32_t va[4],
+                                             uint32_t vb[4]) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = 8 * (wave * 4 + t) + (lane >> 3);
-    const int c = swz(row, lane & 7);
-    o.chunk[t] = c;
-    o.code_a[t] = (m0 + row < M) ? (uint32_t)(m0 + row) * (uint32_t)A.ld_codes + 16u * c : OOB;
-    o.code_b[t] = (n0 + row < N) ? (uint32_t)(n0 + row) * (uint32_t)B.ld_codes + 16u * c : OOB;
+    const int c = load_chunk(wave, lane, t);
+    va[t] = (ti.m0 + row < ti.M) ? (uint32_t)(ti.m0 + row) * (uint32_t)sd.lda + 16u * c : OOB;
+    vb[t] = (ti.n0 + row < ti.N) ? (uint32_t)(ti.n0 + row) * (uint32_t)sd.ldb + 16u * c : OOB;
   }
+}
+
+// This lane's scale-row offset for the scale loads of a tile (A rows for
+// waves 0-3, B rows for 4-7), past the end for rows past the limits.
+template <bool A2D, bool B2D>
+__device__ __forceinline__ uint32_t scale_offset(const TileInfo& ti, const Strides& sd, int wave, int lane) {
   const int r = 64 * (wave & 3) + lane;
   if (wave < 4) {
-    const int ra = m0 + r;
-    o.sc = ra < M ? (uint32_t)(A2D ? (ra >> 5) : ra) * (uint32_t)A.ld_scales : OOB;
-  } else {
-    const int rb = n0 + r;
-    o.sc = rb < N ? (uint32_t)(B2D ? (rb >> 5) : rb) * (uint32_t)B.ld_scales : OOB;
+    const int ra = ti.m0 + r;
+    return ra < ti.M ? (uint32_t)(A2D ? (ra >> 5) : ra) * (uint32_t)sd.ldsa : OOB;
   }
+  const int rb = ti.n0 + r;
+  return rb < ti.N ? (uint32_t)(B2D ? (rb >> 5) : rb) * (uint32_t)sd.ldsb : OOB;
 }
 
-// Issue stage st's code loads into `slot`: 256 rows x 128 bytes of each
-// operand as 32 direct-to-LDS loads of 1 KiB (8 rows each), 4 + 4 per wave.
-// In the partial last stage, chunks at or past K point past the end and read
-// as zeros.
-template <bool TAIL>
-__device__ __forceinline__ void issue_codes(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                            const LaneOffsets& o, int st, int kchunks, uint8_t* slot,
-                                            int wave) {
-  const uint32_t cs = (uint32_t)st * ROWB;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t va = (TAIL && o.chunk[t] >= kchunks) ? OOB : o.code_a[t];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + 1024 * (wave * 4 + t)), 16, va, cs, 0, 0);
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t vb = (TAIL && o.chunk[t] >= kchunks) ? OOB : o.code_b[t];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + OPB + 1024 * (wave * 4 + t)), 16, vb, cs,
-                                             0, 0);
-  }
+template <bool A2D, bool B2D>
+__device__ __forceinline__ void tile_rsrc(const TileInfo& ti, const Strides& sd, int wave, __amdgpu_buffer_rsrc_t& ra,
+                                          __amdgpu_buffer_rsrc_t& rb, __amdgpu_buffer_rsrc_t& rs) {
+  ra = rsrc(ti.a_codes, (uint32_t)(ti.M * sd.lda));
+  rb = rsrc(ti.b_codes, (uint32_t)(ti.N * sd.ldb));
+  rs = wave < 4 ? rsrc(ti.a_scales, (uint32_t)((A2D ? ti.M / 32 : ti.M) * sd.ldsa))
+                : rsrc(ti.b_scales, (uint32_t)((B2D ? ti.N / 32 : ti.N) * sd.ldsb));
 }
 
-// Issue the scale loads of stages 2p and 2p+1 into `sslot`: 16 bytes per row,
-// 64 rows per wave (`rs` is the A scales for waves 0-3, the B scales for 4-7).
-__device__ __forceinline__ void issue_scales(__amdgpu_buffer_rsrc_t rs, const LaneOffsets& o, int p,
-                                             uint8_t* sslot, int wave) {
+// Issue the scale loads of stages 2q and 2q+1 of a tile into `sslot`: 16
+// bytes per row at this lane's row offset `off`, 64 rows per wave (A rows for
+// waves 0-3, B rows for 4-7).
+__device__ __forceinline__ void issue_scales(__amdgpu_buffer_rsrc_t rs, uint32_t off, int q, uint8_t* sslot,
+                                             int wave) {
   uint8_t* dst = sslot + (wave < 4 ? 0 : 256 * SROWB) + 64 * SROWB * (wave & 3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, o.sc, (uint32_t)p * SROWB, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, off, (uint32_t)q * SROWB, 0, 0);
+}
+
+// Issue the 8 code loads of one stage with the compiler's load builtin (used
+// before the pipeline runs; inside it the loads sit in the last step's asm).
+__device__ __forceinline__ void issue_codes(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, const uint32_t va[4],
+                                            const uint32_t vb[4], uint32_t cs, uint8_t* slot, int wave) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + 1024 * (wave * 4 + t)), 16, va[t], cs, 0, 0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + OPB + 1024 * (wave * 4 + t)), 16, vb[t], cs, 0,
+                                             0);
 }
 
 struct Acc {
@@ -200,26 +228,61 @@ __device__ __forceinline__ void step(Acc& c, const v4i a[TI], const v4i b[TJ], c
 }
 
 // The last (odd) step of a stage; reads the next stage's first-step operands
-// (ada, adb) and its 8 scale bytes per row tile (adsa, adsb) into wa, wb.
+// (ada, adb) and its 8 scale bytes per row tile (adsa, adsb) into wa, wb, and
+// issues this wave's 8 code loads of the stage two ahead, one after each MFMA
+// (so that load issue never holds up the matrix pipe for long): 4 A loads to
+// LDS addresses m0, m0+1024, m0+2048, m0+3072 and 4 B loads OPB further, at
+// per-lane offsets va, vb plus the stage offset cs.
 __device__ __forceinline__ void step_last(Acc& c, const v4i a[TI], const v4i b[TJ], const int sa[TI],
                                           const int sb[TJ], uint32_t ada, uint32_t adb, uint32_t adsa,
-                                          uint32_t adsb, v4i na[TI], v4i nb[TJ], v2u wa[TI], v2u wb[TJ]) {
-  asm volatile(MX_STEP_BODY(MX_OPSEL_HI)
-               "ds_read_b64 %[wa0], %[adsa]\n\t"
-               "ds_read_b64 %[wa1], %[adsa] offset:512\n\t"
-               MX_MFMA(c10, a1, b0, sa1, sb0, MX_OPSEL_HI)
-               "ds_read_b64 %[wb0], %[adsb]\n\t"
-               "ds_read_b64 %[wb1], %[adsb] offset:512\n\t"
-               MX_MFMA(c11, a1, b1, sa1, sb1, MX_OPSEL_HI)
-               "ds_read_b64 %[wb2], %[adsb] offset:1024\n\t"
-               "ds_read_b64 %[wb3], %[adsb] offset:1536\n\t"
-               MX_MFMA(c12, a1, b2, sa1, sb2, MX_OPSEL_HI)
-               MX_MFMA(c13, a1, b3, sa1, sb3, MX_OPSEL_HI)
-               "s_waitcnt lgkmcnt(0)"
-               : MX_ACC_OPERANDS(c), MX_NEXT_OPERANDS, [wa0] "=&v"(wa[0]), [wa1] "=&v"(wa[1]),
-                 [wb0] "=&v"(wb[0]), [wb1] "=&v"(wb[1]), [wb2] "=&v"(wb[2]), [wb3] "=&v"(wb[3])
-               : MX_CUR_OPERANDS, [ada] "v"(ada), [adb] "v"(adb), [adsa] "v"(adsa), [adsb] "v"(adsb)
-               : "memory");
+                                          uint32_t adsb, v4i na[TI], v4i nb[TJ], v2u wa[TI], v2u wb[TJ],
+                                          uint32_t m0, const uint32_t va[4], const uint32_t vb[4],
+                                          __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t cs) {
+  static_assert(OPB - 3072 == 0x7400, "B loads start OPB after the A loads");
+  asm volatile(
+      "s_nop 1\n\t"
+      MX_MFMA(c00, a0, b0, sa0, sb0, MX_OPSEL_HI)
+      "ds_read_b128 %[na0], %[ada]\n\t"
+      "ds_read_b128 %[na1], %[ada] offset:4096\n\t"
+      "buffer_load_dwordx4 %[va0], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c01, a0, b1, sa0, sb1, MX_OPSEL_HI)
+      "ds_read_b128 %[nb0], %[adb]\n\t"
+      "ds_read_b128 %[nb1], %[adb] offset:4096\n\t"
+      "buffer_load_dwordx4 %[va1], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c02, a0, b2, sa0, sb2, MX_OPSEL_HI)
+      "ds_read_b128 %[nb2], %[adb] offset:8192\n\t"
+      "ds_read_b128 %[nb3], %[adb] offset:12288\n\t"
+      "buffer_load_dwordx4 %[va2], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c03, a0, b3, sa0, sb3, MX_OPSEL_HI)
+      "ds_read_b64 %[wa0], %[adsa]\n\t"
+      "ds_read_b64 %[wa1], %[adsa] offset:512\n\t"
+      "buffer_load_dwordx4 %[va3], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x7400\n\t"
+      MX_MFMA(c10, a1, b0, sa1, sb0, MX_OPSEL_HI)
+      "ds_read_b64 %[wb0], %[adsb]\n\t"
+      "ds_read_b64 %[wb1], %[adsb] offset:512\n\t"
+      "buffer_load_dwordx4 %[vb0], %[rb], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c11, a1, b1, sa1, sb1, MX_OPSEL_HI)
+      "ds_read_b64 %[wb2], %[adsb] offset:1024\n\t"
+      "ds_read_b64 %[wb3], %[adsb] offset:1536\n\t"
+      "buffer_load_dwordx4 %[vb1], %[rb], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c12, a1, b2, sa1, sb2, MX_OPSEL_HI)
+      "buffer_load_dwordx4 %[vb2], %[rb], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c13, a1, b3, sa1, sb3, MX_OPSEL_HI)
+      "buffer_load_dwordx4 %[vb3], %[rb], %[cs] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : MX_ACC_OPERANDS(c), MX_NEXT_OPERANDS, [wa0] "=&v"(wa[0]), [wa1] "=&v"(wa[1]),
+        [wb0] "=&v"(wb[0]), [wb1] "=&v"(wb[1]), [wb2] "=&v"(wb[2]), [wb3] "=&v"(wb[3]), [m0] "+{m0}"(m0)
+      : MX_CUR_OPERANDS, [ada] "v"(ada), [adb] "v"(adb), [adsa] "v"(adsa), [adsb] "v"(adsb),
+        [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [vb0] "v"(vb[0]),
+        [vb1] "v"(vb[1]), [vb2] "v"(vb[2]), [vb3] "v"(vb[3]), [ra] "s"(ra), [rb] "s"(rb), [cs] "s"(cs)
+      : "memory");
 }
 
 // The first stage's first-step operands and scale bytes.
@@ -281,34 +344,49 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// C tile (rows m0.., cols n0..) = A[m0:m0+256] * B[n0:n0+256]^T over all K.
-// Operand rows past M/N read as zeros; the caller's epilogue stores only
-// valid rows and columns.  Byte extents of the operands must be < 2 GiB.
-// `lds` holds LDS_BYTES: the two code slots, then the two scale slots.
-template <bool A2D, bool B2D>
-__device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B, int M, int N, int K, int m0,
-                                         int n0, uint8_t* lds, Acc& acc) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+__device__ __forceinline__ void zero(Acc& acc) {
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc.t[i][j][r] = 0.0f;
+}
 
-  const int nstages = (K + TK - 1) / TK;
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int mlim, int nlim);
+
+// Run this workgroup's tiles: C tile = A[m0:m0+256] * B[n0:n0+256]^T over all
+// K for each tile sc.tile(j), j < sc.count().  The stage sequence g = j * nst
+// + s (s < nst stages of tile j) is pipelined across tiles: code slot g & 1,
+// scale slot P & 1 for the scale pair P = j * npairs + s / 2.  Operand rows
+// past the limits read as zeros and are never stored.  Byte extents of the
+// operands must be < 2 GiB.  `lds` holds LDS_BYTES: the two code slots, then
+// the two scale slots.
+template <bool A2D, bool B2D, bool OUT_BF16, class Sched>
+__device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, int K, void* C, int64_t ldc,
+                                          uint8_t* lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntiles = sc.count();
+  if (ntiles <= 0) return;
+  Acc acc;
+  zero(acc);
+  constexpr int ES = OUT_BF16 ? 2 : 4;
+  auto store = [&](const TileInfo& ti) {
+    store_tile<OUT_BF16>(acc, static_cast<uint8_t*>(C) + (ti.c_row0 * ldc + ti.n0) * ES, (int)ldc, ti.M - ti.m0,
+                         ti.N - ti.n0);
+  };
+  const int nst = (K + TK - 1) / TK;
+  if (nst == 0) {                           // K = 0: every tile is zero
+    for (int j = 0; j < ntiles; ++j) store(sc.tile(j));
+    return;
+  }
   const int nfull = K / TK;                 // stages without a K tail
-  if (nstages == 0) return;
-  const __amdgpu_buffer_rsrc_t ra = rsrc(A.codes, (uint32_t)(M * A.ld_codes));
-  const __amdgpu_buffer_rsrc_t rb = rsrc(B.codes, (uint32_t)(N * B.ld_codes));
-  const __amdgpu_buffer_rsrc_t rs =
-      wave < 4 ? rsrc(A.scales, (uint32_t)((A2D ? M / 32 : M) * A.ld_scales))
-               : rsrc(B.scales, (uint32_t)((B2D ? N / 32 : N) * B.ld_scales));
-  LaneOffsets o;
-  lane_offsets<A2D, B2D>(A, B, M, N, m0, n0, wave, lane, o);
   const int kchunks = (K - nfull * TK) / 32;          // K-blocks in the tail stage (0 if none)
+  const int npairs = (nst + 1) / 2;
+  const int gtotal = ntiles * nst;
   // scale bytes of the tail stage's blocks: low word blocks 0-3, high word 4-7
   const uint32_t tail_lo = kchunks >= 4 ? 0xFFFFFFFFu : (1u << (8 * kchunks)) - 1u;
   const uint32_t tail_hi = kchunks <= 4 ? 0u : (1u << (8 * (kchunks - 4))) - 1u;
@@ -329,25 +407,60 @@ __device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B,
   const uint32_t s_a = rowa * SROWB, s_b = 256 * SROWB + rowb * SROWB;
   const int sh = 8 * kh;
 
-  // Loads of stage p: its codes, and on even stages the scales of p and p+1.
-  auto issue = [&](int p) {
-    if (p >= nstages) return;
-    uint8_t* slot = lds + (p & 1) * STAGE_BYTES;
-    if (!(p & 1)) issue_scales(rs, o, p >> 1, sslots + ((p >> 1) & 1) * SSLOT, wave);
-    if (p < nfull) issue_codes<false>(ra, rb, o, p, 8, slot, wave);
-    else issue_codes<true>(ra, rb, o, p, kchunks, slot, wave);
+  // The stage whose loads are issued next ("prefetch" position j2, s2) and
+  // its tile's load state, refreshed once per tile.
+  int j2 = 0, s2 = 0;
+  TileInfo t2 = sc.tile(0);
+  __amdgpu_buffer_rsrc_t ra2, rb2, rs2;
+  uint32_t pa[4], pb[4], psc;
+  auto load_tile = [&]() {
+    tile_rsrc<A2D, B2D>(t2, sd, wave, ra2, rb2, rs2);
+    code_offsets(t2, sd, wave, lane, pa, pb);
+    psc = scale_offset<A2D, B2D>(t2, sd, wave, lane);
   };
-  auto loads_of = [&](int p) { return p >= nstages ? 0 : CODE_LOADS + ((p & 1) ? 0 : 1); };
+  auto advance = [&]() {
+    if (++s2 == nst) {
+      s2 = 0;
+      if (++j2 < ntiles) {
+        t2 = sc.tile(j2);
+        load_tile();
+      }
+    }
+  };
+  // Code offsets of the prefetch stage (the tail stage masks the chunks past K).
+  auto stage_offsets = [&](uint32_t va[4], uint32_t vb[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bool live = s2 < nfull || load_chunk(wave, lane, t) < kchunks;
+      va[t] = live ? pa[t] : OOB;
+      vb[t] = live ? pb[t] : OOB;
+    }
+  };
+  auto sslot_of = [&](int j, int s) { return ((j * npairs + (s >> 1)) & 1) * SSLOT; };
+  load_tile();
 
-  issue(0);
-  issue(1);
-  wait_vmcnt(loads_of(1));                  // this wave's stage-0 loads landed
+  // Prologue: global stages 0 and 1 with the compiler's load builtins.
+  int loads1 = 0;                           // loads of stage 1
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (g >= gtotal) break;
+    if (!(s2 & 1)) issue_scales(rs2, psc, s2 >> 1, sslots + sslot_of(j2, s2), wave);
+    uint32_t va[4], vb[4];
+    stage_offsets(va, vb);
+    issue_codes(ra2, rb2, va, vb, (uint32_t)s2 * ROWB, lds + (g & 1) * STAGE_BYTES, wave);
+    if (g == 1) loads1 = CODE_LOADS + ((s2 & 1) ? 0 : 1);
+    advance();
+  }
+  wait_vmcnt(loads1);                       // this wave's stage-0 loads landed
   bare_barrier();                           // ... and every wave's
   v4i a[TI], b[TJ], na[TI], nb[TJ];
   v2u wa[TI], wb[TJ];
   read_first(lds_addr + ra_k[0], lds_addr + rb_k[0], sl_addr + s_a, sl_addr + s_b, a, b, wa, wb);
-  for (int s = 0; s < nstages; ++s) {
-    const uint32_t slot = lds_addr + (uint32_t)((s & 1) * STAGE_BYTES);
+
+  int s = 0, j = 0;                         // stage s of tile j is multiplied
+  int s1 = 1 % nst, j1 = 1 / nst;           // the stage after it
+  for (int g = 0; g < gtotal; ++g) {
+    const uint32_t slot = lds_addr + (uint32_t)((g & 1) * STAGE_BYTES);
     const uint32_t keep_lo = s < nfull ? 0xFFFFFFFFu : tail_lo;
     const uint32_t keep_hi = s < nfull ? 0xFFFFFFFFu : tail_hi;
     int sa[TI], sb[TJ], sa2[TI], sb2[TJ];
@@ -357,33 +470,55 @@ __device__ __forceinline__ void mainloop(const MxOperand& A, const MxOperand& B,
       sa2[i] = (int)((wa[i].y & keep_hi) >> sh);
     }
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      sb[j] = (int)((wb[j].x & keep_lo) >> sh);
-      sb2[j] = (int)((wb[j].y & keep_hi) >> sh);
+    for (int jj = 0; jj < TJ; ++jj) {
+      sb[jj] = (int)((wb[jj].x & keep_lo) >> sh);
+      sb2[jj] = (int)((wb[jj].y & keep_hi) >> sh);
     }
     step<false>(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb);
     step<true>(acc, na, nb, sa, sb, slot + ra_k[2], slot + rb_k[2], a, b);
     step<false>(acc, a, b, sa2, sb2, slot + ra_k[3], slot + rb_k[3], na, nb);
-    // Stage s+1: this wave's loads landed, then every wave's.  Every wave has
-    // also read all of stage s's codes, so its slot takes stage s+2.
+    // Stage g+2 (the prefetch position): its code offsets.  Past the last
+    // stage every code load points past the end (zeros into the free slot).
+    const bool more = g + 2 < gtotal;
+    uint32_t va[4], vb[4];
+    stage_offsets(va, vb);
+    if (!more) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) va[t] = vb[t] = OOB;
+    }
+    // Stage g+1: this wave's loads landed, then every wave's.  Every wave has
+    // also read all of stage g (codes and scales), so its slots take stage g+2.
     wait_vmcnt(0);
     bare_barrier();
-    issue(s + 2);
-    // The next stage's scale bytes: the other half of this scale slot for an
-    // even s, the next scale slot for an odd s.  In the last stage the reads
-    // of the (unused) next slot are harmless.
-    const uint32_t next = lds_addr + (uint32_t)(((s + 1) & 1) * STAGE_BYTES);
-    const uint32_t snext = sl_addr + (uint32_t)((((s + 1) >> 1) & 1) * SSLOT + 8 * ((s + 1) & 1));
-    step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb);
+    if (more && !(s2 & 1)) issue_scales(rs2, psc, s2 >> 1, sslots + sslot_of(j2, s2), wave);
+    // The next stage's first-step operands and scale bytes (in the very last
+    // stage these reads of unused slots are harmless).
+    const uint32_t next = lds_addr + (uint32_t)(((g + 1) & 1) * STAGE_BYTES);
+    const uint32_t snext = sl_addr + (uint32_t)(sslot_of(j1, s1) + 8 * (s1 & 1));
+    step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
+              slot + 4096u * wave, va, vb, ra2, rb2, (uint32_t)s2 * ROWB);
+    if (more) advance();
+    if (++s1 == nst) {
+      s1 = 0;
+      ++j1;
+    }
+    if (++s == nst) {                       // tile j is complete
+      drain(acc);
+      store(sc.tile(j));
+      zero(acc);
+      s = 0;
+      ++j;
+    }
   }
-  drain(acc);
   __syncthreads();                          // LDS may be reused by the caller
 }
 
 // Store the wave's part of the tile with bounds-checked buffer stores: the
 // resource ends after row mlim (relative to the tile origin C), and lanes
-// whose column is >= nlim point past it, so nothing outside the matrix is
+// whose columns are >= nlim point past it, so nothing outside the matrix is
 // written.  Row offsets are wave-uniform (scalar), column offsets per lane.
+// (Each store instruction writes two 32-lane row segments; gathering 4
+// columns per lane for wider stores measured slower.)
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int mlim, int nlim) {
   const int lane = threadIdx.x & 63;
