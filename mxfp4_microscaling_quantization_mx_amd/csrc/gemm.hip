@@ -26,17 +26,30 @@ namespace mx {
 namespace {
 
 // ---------------------------------------------------------------- 256x256 tiles
-// Persistent kernels: one workgroup per CU (G workgroups), each running the
-// tiles t = k*G + l for k = 0, 1, ...  Workgroup b runs on XCD b % 8; its
-// position l makes the workgroups of one XCD take consecutive tile numbers,
-// and tile numbers are walked in groups of 8 M-tiles, so the tiles that one
-// XCD works on at a time share a few A and B panels in its L2.
-__device__ __forceinline__ int xcd_position(int b, int G) {
-  const int per = G / 8, rem = G % 8;
-  const int x = b % 8, k = b / 8;
-  return x * per + (x < rem ? x : rem) + k;
-}
+// Persistent kernels: one workgroup per CU (G workgroups).  Workgroup b runs
+// on XCD b % 8, so XCD x holds the step_x workgroups b = x, x+8, ...  The
+// tiles, in the grouped order below, are cut into 8 contiguous ranges sized
+// in proportion to step_x, one per XCD, and the XCD's workgroups take its
+// range round-robin: the tiles one XCD works on at a time are consecutive,
+// and each operand panel is fetched into one XCD's L2 rather than into all.
+struct XcdShare {
+  int first, n, step, k;                   // tiles first + k + j*step < first + n
+  __device__ XcdShare(int b, int G, int T) {
+    const int x = b % 8;
+    step = G / 8 + (x < G % 8 ? 1 : 0);
+    k = b / 8;
+    // workgroups on the XCDs before x and up to x
+    const int64_t w0 = (int64_t)x * (G / 8) + (x < G % 8 ? x : G % 8);
+    const int64_t w1 = w0 + step;
+    first = (int)(w0 * T / G);
+    n = (int)(w1 * T / G) - first;
+  }
+  __device__ int count() const { return k < n ? (n - k + step - 1) / step : 0; }
+  __device__ int tile(int j) const { return first + k + j * step; }
+};
 
+// Tile order: groups of 8 M-tiles, each walked N-tile by N-tile, so that a
+// run of consecutive tiles shares a few A and B panels.
 __device__ __forceinline__ void group_order(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GM = 8;
   const int group = t / (GM * tiles_n);
@@ -51,14 +64,12 @@ constexpr int GW = t256::WAVES;
 
 struct DenseSched {
   const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
-  int M, N, tiles_m, tiles_n, G, l;
-  __device__ int count() const {
-    const int total = tiles_m * tiles_n;
-    return l < total ? (total - l + G - 1) / G : 0;
-  }
+  int M, N, tiles_m, tiles_n;
+  XcdShare share;
+  __device__ int count() const { return share.count(); }
   __device__ t256::TileInfo tile(int j) const {
     int tm, tn;
-    group_order(j * G + l, tiles_m, tiles_n, tm, tn);
+    group_order(share.tile(j), tiles_m, tiles_n, tm, tn);
     t256::TileInfo ti;
     ti.a_codes = a_codes;
     ti.a_scales = a_scales;
@@ -77,8 +88,8 @@ template <bool A2D, bool B2D, bool OUT_BF16>
 __global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B, int M, int N, int K, void* C,
                                                         int64_t ldc, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
-  const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n, (int)gridDim.x,
-                      xcd_position(blockIdx.x, gridDim.x)};
+  const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
+                      XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
   t256::run_tiles<A2D, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
 }
@@ -102,15 +113,13 @@ __device__ __forceinline__ int lds_i32(const int* p) {
 struct GroupedSched {
   const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
   int64_t stride_codes, stride_scales;      // between experts of B
-  int lda, ldsa, N, tiles_n, E, total_slots, G, l;
+  int lda, ldsa, N, tiles_n, E, total_slots;
   const int* tab;                           // LDS: pre [E+1] exclusive prefix of slots, lo [E], hi [E]
-  __device__ int count() const {
-    const int total = total_slots * tiles_n;
-    return l < total ? (total - l + G - 1) / G : 0;
-  }
+  XcdShare share;
+  __device__ int count() const { return share.count(); }
   __device__ t256::TileInfo tile(int j) const {
     int slot, tn;
-    group_order(j * G + l, total_slots, tiles_n, slot, tn);
+    group_order(share.tile(j), total_slots, tiles_n, slot, tn);
     const int* pre = tab;
     const int* lo = tab + GG_EMAX + 1;
     const int* hi = lo + GG_EMAX;
@@ -183,9 +192,10 @@ __global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxO
     if (lane == 0) pre[E] = carry;
   }
   __syncthreads();
+  const int total_slots = pre[E];
   const GroupedSched sc{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
-                        (int)A.ld_scales, N, tiles_n, E, pre[E], (int)gridDim.x,
-                        xcd_position(blockIdx.x, gridDim.x), tab};
+                        (int)A.ld_scales, N, tiles_n, E, total_slots, tab,
+                        XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
   t256::run_tiles<false, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
 }
