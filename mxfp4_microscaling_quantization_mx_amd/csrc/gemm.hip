@@ -18,7 +18,10 @@
 // 32-bit word of 4 scale bytes per row.  Rows past M/N and K past the end are
 // zero codes with scale 1.0, so they add exact zeros (a NaN scale there would
 // otherwise poison the sums).
+#include <stdlib.h>
+
 #include "gemm_tile256.h"
+#include "gemm_w4.h"
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -94,13 +97,23 @@ __global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B
   t256::run_tiles<A2D, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
 }
 
+template <bool A2D, bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * t4::WAVES, 1) void k_gemm256w4(MxOperand A, MxOperand B, int M, int N, int K,
+                                                                 void* C, int64_t ldc, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
+  const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
+                      XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
+  const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
+  t4::run_tiles<A2D, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
+}
+
 // Grouped (MoE) GEMM.  A row tile ("slot") never straddles two experts: the
 // slots of expert e are the ceil(rows_e / 256) tiles of its rows, numbered in
 // expert order.  Each workgroup first builds, in LDS, the clamped row range of
 // every expert and the exclusive prefix count of slots, from the device
 // offsets (so the schedule needs no host synchronization); a tile's expert is
 // then found by one wave-wide comparison against that prefix.
-constexpr int GG_EMAX = 1024;               // experts the LDS table holds
+constexpr int GG_EMAX = 960;                // experts the LDS table holds (it fits beside the ring)
 
 __device__ __forceinline__ int lds_i32(const int* p) {
   int v;
@@ -110,56 +123,98 @@ __device__ __forceinline__ int lds_i32(const int* p) {
   return v;
 }
 
-struct GroupedSched {
+// Per-launch parameters of the grouped GEMM, kept in LDS and read back per
+// tile (holding them in scalar registers across the pipeline would spill).
+struct alignas(16) GroupedParams {
   const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
   int64_t stride_codes, stride_scales;      // between experts of B
-  int lda, ldsa, N, tiles_n, E, total_slots;
+  int lda, ldsa, N, tiles_n, E, total_slots, pad0, pad1;
+};
+static_assert(sizeof(GroupedParams) == 80, "five 16-byte LDS reads");
+
+// Read a wave-uniform GroupedParams from LDS with one wait.
+__device__ __forceinline__ GroupedParams load_params(const GroupedParams* p) {
+  typedef int v4i_ __attribute__((ext_vector_type(4)));
+  v4i_ q[5];
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %5 offset:16\n\t"
+      "ds_read_b128 %2, %5 offset:32\n\t"
+      "ds_read_b128 %3, %5 offset:48\n\t"
+      "ds_read_b128 %4, %5 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4])
+      : "v"(a)
+      : "memory");
+  int w[20];
+#pragma unroll
+  for (int i = 0; i < 5; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[4 * i + k] = __builtin_amdgcn_readfirstlane(q[i][k]);
+  return __builtin_bit_cast(GroupedParams, w);
+}
+
+// Two LDS words at per-lane addresses, one wait.
+__device__ __forceinline__ void lds_i32x2(const int* p0, const int* p1, int& v0, int& v1) {
+  const uint32_t a0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p0;
+  const uint32_t a1 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p1;
+  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(v0), "=&v"(v1)
+               : "v"(a0), "v"(a1)
+               : "memory");
+}
+
+struct GroupedSched {
+  const GroupedParams* prm;                 // LDS
   const int* tab;                           // LDS: pre [E+1] exclusive prefix of slots, lo [E], hi [E]
   XcdShare share;
   __device__ int count() const { return share.count(); }
   __device__ t256::TileInfo tile(int j) const {
+    const GroupedParams P = load_params(prm);
     int slot, tn;
-    group_order(share.tile(j), total_slots, tiles_n, slot, tn);
+    group_order(share.tile(j), P.total_slots, P.tiles_n, slot, tn);
     const int* pre = tab;
     const int* lo = tab + GG_EMAX + 1;
     const int* hi = lo + GG_EMAX;
     const int lane = threadIdx.x & 63;
-    int ex = E - 1;
-    for (int base = 0; base < E; base += 64) {
-      const int e = base + lane;
-      const int p0 = e < E ? lds_i32(pre + e) : 0x7FFFFFFF;
-      const int p1 = e < E ? lds_i32(pre + e + 1) : 0x7FFFFFFF;
-      const unsigned long long m = __ballot(slot >= p0 && slot < p1);
+    int ex = P.E - 1;
+    for (int base = 0; base < P.E; base += 64) {
+      const int e = base + lane < P.E ? base + lane : P.E - 1;
+      int p0, p1;
+      lds_i32x2(pre + e, pre + e + 1, p0, p1);
+      const unsigned long long m = __ballot(base + lane < P.E && slot >= p0 && slot < p1);
       if (m) {
         ex = base + __ffsll((long long)m) - 1;
         break;
       }
     }
     ex = __builtin_amdgcn_readfirstlane(ex);
-    const int row0 = __builtin_amdgcn_readfirstlane(lds_i32(lo + ex) + (slot - lds_i32(pre + ex)) * t256::TM);
-    const int end = __builtin_amdgcn_readfirstlane(lds_i32(hi + ex));
+    int l0, p0, h0;
+    lds_i32x2(lo + ex, pre + ex, l0, p0);
+    h0 = lds_i32(hi + ex);
+    const int row0 = __builtin_amdgcn_readfirstlane(l0 + (slot - p0) * t256::TM);
+    const int end = __builtin_amdgcn_readfirstlane(h0);
     const int rows = end - row0 < t256::TM ? end - row0 : t256::TM;
     t256::TileInfo ti;
-    ti.a_codes = a_codes + (int64_t)row0 * lda;
-    ti.a_scales = a_scales + (int64_t)row0 * ldsa;
-    ti.b_codes = b_codes + (int64_t)ex * stride_codes;
-    ti.b_scales = b_scales + (int64_t)ex * stride_scales;
+    ti.a_codes = P.a_codes + (int64_t)row0 * P.lda;
+    ti.a_scales = P.a_scales + (int64_t)row0 * P.ldsa;
+    ti.b_codes = P.b_codes + (int64_t)ex * P.stride_codes;
+    ti.b_scales = P.b_scales + (int64_t)ex * P.stride_scales;
     ti.m0 = 0;
     ti.n0 = tn * t256::TN;
     ti.M = rows;
-    ti.N = N;
+    ti.N = P.N;
     ti.c_row0 = row0;
     return ti;
   }
 };
 
-template <bool B2D, bool OUT_BF16>
-__global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxOperand B, int64_t M_cap, int N,
-                                                                int K, const int32_t* __restrict__ offsets, int E,
-                                                                int64_t stride_codes, int64_t stride_scales,
-                                                                void* C, int64_t ldc, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
-  __shared__ int tab[3 * GG_EMAX + 1];
+// Fill the LDS expert table: pre [E+1] exclusive prefix of row tiles,
+// lo [E] and hi [E] the clamped row range of each expert (wave 0 computes it;
+// ends with a workgroup barrier).
+__device__ __forceinline__ void build_expert_table(const int32_t* __restrict__ offsets, int E, int64_t M_cap,
+                                                   int* tab) {
   int* pre = tab;
   int* lo = tab + GG_EMAX + 1;
   int* hi = lo + GG_EMAX;
@@ -192,12 +247,43 @@ __global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxO
     if (lane == 0) pre[E] = carry;
   }
   __syncthreads();
-  const int total_slots = pre[E];
-  const GroupedSched sc{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
-                        (int)A.ld_scales, N, tiles_n, E, total_slots, tab,
-                        XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
+}
+
+template <bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxOperand B, int64_t M_cap, int N,
+                                                                int K, const int32_t* __restrict__ offsets, int E,
+                                                                int64_t stride_codes, int64_t stride_scales,
+                                                                void* C, int64_t ldc, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
+  __shared__ int tab[3 * GG_EMAX + 1];
+  __shared__ GroupedParams prm;
+  build_expert_table(offsets, E, M_cap, tab);   // ends with a barrier
+  const int total_slots = tab[E];
+  if (threadIdx.x == 0)
+    prm = GroupedParams{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
+                        (int)A.ld_scales, N, tiles_n, E, total_slots, 0, 0};
+  __syncthreads();
+  const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
   t256::run_tiles<false, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
+}
+
+template <bool B2D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * t4::WAVES, 1) void k_grouped_gemm256w4(
+    MxOperand A, MxOperand B, int64_t M_cap, int N, int K, const int32_t* __restrict__ offsets, int E,
+    int64_t stride_codes, int64_t stride_scales, void* C, int64_t ldc, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
+  __shared__ int tab[3 * GG_EMAX + 1];
+  __shared__ GroupedParams prm;
+  build_expert_table(offsets, E, M_cap, tab);   // ends with a barrier
+  const int total_slots = tab[E];
+  if (threadIdx.x == 0)
+    prm = GroupedParams{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
+                        (int)A.ld_scales, N, tiles_n, E, total_slots, 0, 0};
+  __syncthreads();
+  const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
+  const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
+  t4::run_tiles<false, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
 }
 
 // ---------------------------------------------------------------- 128x128 tiles
@@ -383,6 +469,16 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(MxOperand A, MxOperand B, 
 
 }  // namespace
 
+// Waves per 256x256 workgroup (4 or 8); MXFP4_GEMM_WAVES overrides the default.
+static int gemm_waves() {
+  static int w = 0;
+  if (w == 0) {
+    const char* e = getenv("MXFP4_GEMM_WAVES");
+    w = (e && atoi(e) == 4) ? 4 : 8;
+  }
+  return w;
+}
+
 // Compute units of the current device (cached per device).
 static int cu_count() {
   static int cache[64] = {0};
@@ -409,9 +505,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     const int tiles = tiles_m * tiles_n;
     const int cus = cu_count();
     const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
-#define MX_G256(A_, B_, O_)                                                                        \
-  hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, (int)a.M, \
-                     (int)a.N, (int)a.K, a.C, a.ldc, tiles_m, tiles_n)
+#define MX_G256(A_, B_, O_)                                                                              \
+  if (gemm_waves() == 4)                                                                                  \
+    hipLaunchKernelGGL((k_gemm256w4<A_, B_, O_>), dim3(nwg), dim3(64 * t4::WAVES), 0, st, a.A, a.B,       \
+                       (int)a.M, (int)a.N, (int)a.K, a.C, a.ldc, tiles_m, tiles_n);                        \
+  else                                                                                                    \
+    hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, (int)a.M,       \
+                       (int)a.N, (int)a.K, a.C, a.ldc, tiles_m, tiles_n)
     if (a.out_bf16) {
       if (a.a_2d) { if (a.b_2d) MX_G256(true, true, true); else MX_G256(true, false, true); }
       else { if (a.b_2d) MX_G256(false, true, true); else MX_G256(false, false, true); }
@@ -450,8 +550,14 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st) {
     const int cus = cu_count();
     const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
 #define MX_GG256(B_, O_)                                                                                  \
-  hipLaunchKernelGGL((k_grouped_gemm256<B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap,     \
-                     (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, tiles_n)
+  if (gemm_waves() == 4)                                                                                  \
+    hipLaunchKernelGGL((k_grouped_gemm256w4<B_, O_>), dim3(nwg), dim3(64 * t4::WAVES), 0, st, a.A, a.B,   \
+                       a.M_cap, (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C,  \
+                       a.ldc, tiles_n);                                                                   \
+  else                                                                                                    \
+    hipLaunchKernelGGL((k_grouped_gemm256<B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap,   \
+                       (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc,   \
+                       tiles_n)
     if (a.out_bf16) {
       if (a.b_2d) MX_GG256(true, true); else MX_GG256(false, true);
     } else {

@@ -64,7 +64,8 @@ constexpr int OPB = 256 * ROWB;            // code bytes per operand per stage (
 constexpr int STAGE_BYTES = 2 * OPB;       // one code slot
 constexpr int SROWB = 16;                  // scale bytes per row per scale slot (two stages)
 constexpr int SSLOT = 2 * 256 * SROWB;     // one scale slot: A rows, then B rows (8 KiB)
-constexpr int LDS_BYTES = 2 * STAGE_BYTES + 2 * SSLOT;
+constexpr int DUMMY_BYTES = 4096;          // target of loads that must not land in a live slot
+constexpr int LDS_BYTES = 2 * STAGE_BYTES + 2 * SSLOT + DUMMY_BYTES;
 constexpr int TI = 2, TJ = 4;              // 32x32 MFMA tiles per wave along M, N
 constexpr int CODE_LOADS = 8;              // 1 KiB code loads per wave and stage (4 A + 4 B)
 
@@ -227,18 +228,41 @@ __device__ __forceinline__ void step(Acc& c, const v4i a[TI], const v4i b[TJ], c
   }
 }
 
+// The first step of a stage with 4 code loads interleaved: the B half of the
+// loads of the stage two ahead (issued one step after its A half, so that a
+// stage's loads are spread over two steps), to LDS addresses m0, m0+1024, ...
+// at per-lane offsets v plus the stage offset cs through resource rc.
+__device__ __forceinline__ void step0_ld(Acc& c, const v4i a[TI], const v4i b[TJ], const int sa[TI],
+                                         const int sb[TJ], uint32_t ada, uint32_t adb, v4i na[TI], v4i nb[TJ],
+                                         uint32_t m0, const uint32_t v[4], __amdgpu_buffer_rsrc_t rc, uint32_t cs) {
+  asm volatile(MX_STEP_BODY(MX_OPSEL_LO)
+               "buffer_load_dwordx4 %[v0], %[rc], %[cs] offen lds\n\t"
+               "s_add_u32 m0, m0, 0x400\n\t"
+               MX_MFMA(c10, a1, b0, sa1, sb0, MX_OPSEL_LO)
+               "buffer_load_dwordx4 %[v1], %[rc], %[cs] offen lds\n\t"
+               "s_add_u32 m0, m0, 0x400\n\t"
+               MX_MFMA(c11, a1, b1, sa1, sb1, MX_OPSEL_LO)
+               "buffer_load_dwordx4 %[v2], %[rc], %[cs] offen lds\n\t"
+               "s_add_u32 m0, m0, 0x400\n\t"
+               MX_MFMA(c12, a1, b2, sa1, sb2, MX_OPSEL_LO)
+               "buffer_load_dwordx4 %[v3], %[rc], %[cs] offen lds\n\t"
+               MX_MFMA(c13, a1, b3, sa1, sb3, MX_OPSEL_LO)
+               "s_waitcnt lgkmcnt(0)"
+               : MX_ACC_OPERANDS(c), MX_NEXT_OPERANDS, [m0] "+{m0}"(m0)
+               : MX_CUR_OPERANDS, [ada] "v"(ada), [adb] "v"(adb), [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]),
+                 [v3] "v"(v[3]), [rc] "s"(rc), [cs] "s"(cs)
+               : "memory");
+}
+
 // The last (odd) step of a stage; reads the next stage's first-step operands
 // (ada, adb) and its 8 scale bytes per row tile (adsa, adsb) into wa, wb, and
-// issues this wave's 8 code loads of the stage two ahead, one after each MFMA
-// (so that load issue never holds up the matrix pipe for long): 4 A loads to
-// LDS addresses m0, m0+1024, m0+2048, m0+3072 and 4 B loads OPB further, at
-// per-lane offsets va, vb plus the stage offset cs.
+// issues this wave's 4 A code loads of the stage two ahead, one after every
+// other MFMA, to LDS addresses m0, m0+1024, m0+2048, m0+3072 at per-lane
+// offsets va plus the stage offset cs (the B half follows in the next step).
 __device__ __forceinline__ void step_last(Acc& c, const v4i a[TI], const v4i b[TJ], const int sa[TI],
                                           const int sb[TJ], uint32_t ada, uint32_t adb, uint32_t adsa,
                                           uint32_t adsb, v4i na[TI], v4i nb[TJ], v2u wa[TI], v2u wb[TJ],
-                                          uint32_t m0, const uint32_t va[4], const uint32_t vb[4],
-                                          __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t cs) {
-  static_assert(OPB - 3072 == 0x7400, "B loads start OPB after the A loads");
+                                          uint32_t m0, const uint32_t va[4], __amdgpu_buffer_rsrc_t ra, uint32_t cs) {
   asm volatile(
       "s_nop 1\n\t"
       MX_MFMA(c00, a0, b0, sa0, sb0, MX_OPSEL_HI)
@@ -249,39 +273,30 @@ __device__ __forceinline__ void step_last(Acc& c, const v4i a[TI], const v4i b[T
       MX_MFMA(c01, a0, b1, sa0, sb1, MX_OPSEL_HI)
       "ds_read_b128 %[nb0], %[adb]\n\t"
       "ds_read_b128 %[nb1], %[adb] offset:4096\n\t"
-      "buffer_load_dwordx4 %[va1], %[ra], %[cs] offen lds\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
       MX_MFMA(c02, a0, b2, sa0, sb2, MX_OPSEL_HI)
       "ds_read_b128 %[nb2], %[adb] offset:8192\n\t"
       "ds_read_b128 %[nb3], %[adb] offset:12288\n\t"
-      "buffer_load_dwordx4 %[va2], %[ra], %[cs] offen lds\n\t"
+      "buffer_load_dwordx4 %[va1], %[ra], %[cs] offen lds\n\t"
       "s_add_u32 m0, m0, 0x400\n\t"
       MX_MFMA(c03, a0, b3, sa0, sb3, MX_OPSEL_HI)
       "ds_read_b64 %[wa0], %[adsa]\n\t"
       "ds_read_b64 %[wa1], %[adsa] offset:512\n\t"
-      "buffer_load_dwordx4 %[va3], %[ra], %[cs] offen lds\n\t"
-      "s_add_u32 m0, m0, 0x7400\n\t"
       MX_MFMA(c10, a1, b0, sa1, sb0, MX_OPSEL_HI)
       "ds_read_b64 %[wb0], %[adsb]\n\t"
       "ds_read_b64 %[wb1], %[adsb] offset:512\n\t"
-      "buffer_load_dwordx4 %[vb0], %[rb], %[cs] offen lds\n\t"
+      "buffer_load_dwordx4 %[va2], %[ra], %[cs] offen lds\n\t"
       "s_add_u32 m0, m0, 0x400\n\t"
       MX_MFMA(c11, a1, b1, sa1, sb1, MX_OPSEL_HI)
       "ds_read_b64 %[wb2], %[adsb] offset:1024\n\t"
       "ds_read_b64 %[wb3], %[adsb] offset:1536\n\t"
-      "buffer_load_dwordx4 %[vb1], %[rb], %[cs] offen lds\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
       MX_MFMA(c12, a1, b2, sa1, sb2, MX_OPSEL_HI)
-      "buffer_load_dwordx4 %[vb2], %[rb], %[cs] offen lds\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
+      "buffer_load_dwordx4 %[va3], %[ra], %[cs] offen lds\n\t"
       MX_MFMA(c13, a1, b3, sa1, sb3, MX_OPSEL_HI)
-      "buffer_load_dwordx4 %[vb3], %[rb], %[cs] offen lds\n\t"
       "s_waitcnt lgkmcnt(0)"
       : MX_ACC_OPERANDS(c), MX_NEXT_OPERANDS, [wa0] "=&v"(wa[0]), [wa1] "=&v"(wa[1]),
         [wb0] "=&v"(wb[0]), [wb1] "=&v"(wb[1]), [wb2] "=&v"(wb[2]), [wb3] "=&v"(wb[3]), [m0] "+{m0}"(m0)
       : MX_CUR_OPERANDS, [ada] "v"(ada), [adb] "v"(adb), [adsa] "v"(adsa), [adsb] "v"(adsb),
-        [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [vb0] "v"(vb[0]),
-        [vb1] "v"(vb[1]), [vb2] "v"(vb[2]), [vb3] "v"(vb[3]), [ra] "s"(ra), [rb] "s"(rb), [cs] "s"(cs)
+        [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [ra] "s"(ra), [cs] "s"(cs)
       : "memory");
 }
 
@@ -361,8 +376,8 @@ __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int
 // + s (s < nst stages of tile j) is pipelined across tiles: code slot g & 1,
 // scale slot P & 1 for the scale pair P = j * npairs + s / 2.  Operand rows
 // past the limits read as zeros and are never stored.  Byte extents of the
-// operands must be < 2 GiB.  `lds` holds LDS_BYTES: the two code slots, then
-// the two scale slots.
+// operands must be < 2 GiB.  `lds` holds LDS_BYTES: the two code slots, the
+// two scale slots and a dummy region.
 template <bool A2D, bool B2D, bool OUT_BF16, class Sched>
 __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, int K, void* C, int64_t ldc,
                                           uint8_t* lds) {
@@ -459,6 +474,11 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
 
   int s = 0, j = 0;                         // stage s of tile j is multiplied
   int s1 = 1 % nst, j1 = 1 / nst;           // the stage after it
+  // Pending B-half loads; none before the first stage: those 4 loads point
+  // past the end and land in the dummy region (slots 0 and 1 are live).
+  uint32_t pend_vb[4] = {OOB, OOB, OOB, OOB};
+  __amdgpu_buffer_rsrc_t pend_rb = rb2;
+  uint32_t pend_cs = 0, pend_m0 = lds_addr + 2 * STAGE_BYTES + 2 * SSLOT;
   for (int g = 0; g < gtotal; ++g) {
     const uint32_t slot = lds_addr + (uint32_t)((g & 1) * STAGE_BYTES);
     const uint32_t keep_lo = s < nfull ? 0xFFFFFFFFu : tail_lo;
@@ -474,7 +494,9 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
       sb[jj] = (int)((wb[jj].x & keep_lo) >> sh);
       sb2[jj] = (int)((wb[jj].y & keep_hi) >> sh);
     }
-    step<false>(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb);
+    // the B half of stage g+1's loads (issued by the previous iteration's
+    // prefetch position; dummy loads past the end in the first iteration)
+    step0_ld(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb, pend_m0, pend_vb, pend_rb, pend_cs);
     step<true>(acc, na, nb, sa, sb, slot + ra_k[2], slot + rb_k[2], a, b);
     step<false>(acc, a, b, sa2, sb2, slot + ra_k[3], slot + rb_k[3], na, nb);
     // Stage g+2 (the prefetch position): its code offsets.  Past the last
@@ -496,7 +518,13 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
     const uint32_t next = lds_addr + (uint32_t)(((g + 1) & 1) * STAGE_BYTES);
     const uint32_t snext = sl_addr + (uint32_t)(sslot_of(j1, s1) + 8 * (s1 & 1));
     step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
-              slot + 4096u * wave, va, vb, ra2, rb2, (uint32_t)s2 * ROWB);
+              slot + 4096u * wave, va, ra2, (uint32_t)s2 * ROWB);
+    // the B half goes out in the next iteration's first step
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pend_vb[t] = vb[t];
+    pend_rb = rb2;
+    pend_cs = (uint32_t)s2 * ROWB;
+    pend_m0 = slot + OPB + 4096u * wave;
     if (more) advance();
     if (++s1 == nst) {
       s1 = 0;
