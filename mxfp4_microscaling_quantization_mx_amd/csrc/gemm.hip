@@ -18,10 +18,7 @@
 // 32-bit word of 4 scale bytes per row.  Rows past M/N and K past the end are
 // zero codes with scale 1.0, so they add exact zeros (a NaN scale there would
 // otherwise poison the sums).
-#include <stdlib.h>
-
 #include "gemm_tile256.h"
-#include "gemm_w4.h"
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -95,16 +92,6 @@ __global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B
                       XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
   t256::run_tiles<A2D, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
-}
-
-template <bool A2D, bool B2D, bool OUT_BF16>
-__global__ __launch_bounds__(64 * t4::WAVES, 1) void k_gemm256w4(MxOperand A, MxOperand B, int M, int N, int K,
-                                                                 void* C, int64_t ldc, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
-  const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
-                      XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
-  const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
-  t4::run_tiles<A2D, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
 }
 
 // Grouped (MoE) GEMM.  A row tile ("slot") never straddles two experts: the
@@ -266,24 +253,6 @@ __global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxO
   const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
   t256::run_tiles<false, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
-}
-
-template <bool B2D, bool OUT_BF16>
-__global__ __launch_bounds__(64 * t4::WAVES, 1) void k_grouped_gemm256w4(
-    MxOperand A, MxOperand B, int64_t M_cap, int N, int K, const int32_t* __restrict__ offsets, int E,
-    int64_t stride_codes, int64_t stride_scales, void* C, int64_t ldc, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256::LDS_BYTES];
-  __shared__ int tab[3 * GG_EMAX + 1];
-  __shared__ GroupedParams prm;
-  build_expert_table(offsets, E, M_cap, tab);   // ends with a barrier
-  const int total_slots = tab[E];
-  if (threadIdx.x == 0)
-    prm = GroupedParams{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
-                        (int)A.ld_scales, N, tiles_n, E, total_slots, 0, 0};
-  __syncthreads();
-  const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
-  const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
-  t4::run_tiles<false, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
 }
 
 // ---------------------------------------------------------------- 128x128 tiles
@@ -469,16 +438,6 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(MxOperand A, MxOperand B, 
 
 }  // namespace
 
-// Waves per 256x256 workgroup (4 or 8); MXFP4_GEMM_WAVES overrides the default.
-static int gemm_waves() {
-  static int w = 0;
-  if (w == 0) {
-    const char* e = getenv("MXFP4_GEMM_WAVES");
-    w = (e && atoi(e) == 4) ? 4 : 8;
-  }
-  return w;
-}
-
 // Compute units of the current device (cached per device).
 static int cu_count() {
   static int cache[64] = {0};
@@ -505,13 +464,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     const int tiles = tiles_m * tiles_n;
     const int cus = cu_count();
     const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
-#define MX_G256(A_, B_, O_)                                                                              \
-  if (gemm_waves() == 4)                                                                                  \
-    hipLaunchKernelGGL((k_gemm256w4<A_, B_, O_>), dim3(nwg), dim3(64 * t4::WAVES), 0, st, a.A, a.B,       \
-                       (int)a.M, (int)a.N, (int)a.K, a.C, a.ldc, tiles_m, tiles_n);                        \
-  else                                                                                                    \
-    hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, (int)a.M,       \
-                       (int)a.N, (int)a.K, a.C, a.ldc, tiles_m, tiles_n)
+#define MX_G256(A_, B_, O_)                                                                        \
+  hipLaunchKernelGGL((k_gemm256<A_, B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, (int)a.M, \
+                     (int)a.N, (int)a.K, a.C, a.ldc, tiles_m, tiles_n)
     if (a.out_bf16) {
       if (a.a_2d) { if (a.b_2d) MX_G256(true, true, true); else MX_G256(true, false, true); }
       else { if (a.b_2d) MX_G256(false, true, true); else MX_G256(false, false, true); }
@@ -550,14 +505,8 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st) {
     const int cus = cu_count();
     const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
 #define MX_GG256(B_, O_)                                                                                  \
-  if (gemm_waves() == 4)                                                                                  \
-    hipLaunchKernelGGL((k_grouped_gemm256w4<B_, O_>), dim3(nwg), dim3(64 * t4::WAVES), 0, st, a.A, a.B,   \
-                       a.M_cap, (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C,  \
-                       a.ldc, tiles_n);                                                                   \
-  else                                                                                                    \
-    hipLaunchKernelGGL((k_grouped_gemm256<B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap,   \
-                       (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc,   \
-                       tiles_n)
+  hipLaunchKernelGGL((k_grouped_gemm256<B_, O_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap,     \
+                     (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, tiles_n)
     if (a.out_bf16) {
       if (a.b_2d) MX_GG256(true, true); else MX_GG256(false, true);
     } else {
