@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B
   const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
                       XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
-  t256::run_tiles<A2D, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
+  t256::run_tiles<A2D, B2D, OUT_BF16, true>(sc, sd, K, C, ldc, lds);
 }
 
 // Grouped (MoE) GEMM.  A row tile ("slot") never straddles two experts: the
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxO
   __syncthreads();
   const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
-  t256::run_tiles<false, B2D, OUT_BF16>(sc, sd, K, C, ldc, lds);
+  t256::run_tiles<false, B2D, OUT_BF16, false>(sc, sd, K, C, ldc, lds);
 }
 
 // ---------------------------------------------------------------- 128x128 tiles

@@ -36,7 +36,12 @@
 // (an s_nop at the start of each block) and wait states between the last MFMA
 // and the first read of its result (after the loop).  One barrier per stage,
 // before its last step: every wave has then read the stage's codes, so its
-// slot is refilled with the stage two ahead while the last step runs.
+// slot is refilled with the stage two ahead: its 8 code loads per wave go
+// out one per MFMA of the last step, or (SPLIT) the A half there and the B
+// half in the next stage's first step, so that the load unit never receives
+// a whole stage's loads at once (better for the dense GEMMs; the grouped
+// kernel, whose expert weights come from further away, keeps the earlier
+// issue).
 //
 // Persistent schedule: one workgroup per CU walks its list of tiles, and the
 // stage sequence runs on across tile boundaries: the first two stages of the
@@ -300,6 +305,60 @@ __device__ __forceinline__ void step_last(Acc& c, const v4i a[TI], const v4i b[T
       : "memory");
 }
 
+// As step_last, but issuing all 8 code loads of the stage two ahead (4 A
+// loads at m0, m0+1024, ..., then 4 B loads OPB further), one after each MFMA.
+__device__ __forceinline__ void step_last8(Acc& c, const v4i a[TI], const v4i b[TJ], const int sa[TI],
+                                           const int sb[TJ], uint32_t ada, uint32_t adb, uint32_t adsa,
+                                           uint32_t adsb, v4i na[TI], v4i nb[TJ], v2u wa[TI], v2u wb[TJ],
+                                           uint32_t m0, const uint32_t va[4], const uint32_t vb[4],
+                                           __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t cs) {
+  static_assert(OPB - 3072 == 0x7400, "B loads start OPB after the A loads");
+  asm volatile(
+      "s_nop 1\n\t"
+      MX_MFMA(c00, a0, b0, sa0, sb0, MX_OPSEL_HI)
+      "ds_read_b128 %[na0], %[ada]\n\t"
+      "ds_read_b128 %[na1], %[ada] offset:4096\n\t"
+      "buffer_load_dwordx4 %[va0], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c01, a0, b1, sa0, sb1, MX_OPSEL_HI)
+      "ds_read_b128 %[nb0], %[adb]\n\t"
+      "ds_read_b128 %[nb1], %[adb] offset:4096\n\t"
+      "buffer_load_dwordx4 %[va1], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c02, a0, b2, sa0, sb2, MX_OPSEL_HI)
+      "ds_read_b128 %[nb2], %[adb] offset:8192\n\t"
+      "ds_read_b128 %[nb3], %[adb] offset:12288\n\t"
+      "buffer_load_dwordx4 %[va2], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c03, a0, b3, sa0, sb3, MX_OPSEL_HI)
+      "ds_read_b64 %[wa0], %[adsa]\n\t"
+      "ds_read_b64 %[wa1], %[adsa] offset:512\n\t"
+      "buffer_load_dwordx4 %[va3], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x7400\n\t"
+      MX_MFMA(c10, a1, b0, sa1, sb0, MX_OPSEL_HI)
+      "ds_read_b64 %[wb0], %[adsb]\n\t"
+      "ds_read_b64 %[wb1], %[adsb] offset:512\n\t"
+      "buffer_load_dwordx4 %[vb0], %[rb], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c11, a1, b1, sa1, sb1, MX_OPSEL_HI)
+      "ds_read_b64 %[wb2], %[adsb] offset:1024\n\t"
+      "ds_read_b64 %[wb3], %[adsb] offset:1536\n\t"
+      "buffer_load_dwordx4 %[vb1], %[rb], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c12, a1, b2, sa1, sb2, MX_OPSEL_HI)
+      "buffer_load_dwordx4 %[vb2], %[rb], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      MX_MFMA(c13, a1, b3, sa1, sb3, MX_OPSEL_HI)
+      "buffer_load_dwordx4 %[vb3], %[rb], %[cs] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : MX_ACC_OPERANDS(c), MX_NEXT_OPERANDS, [wa0] "=&v"(wa[0]), [wa1] "=&v"(wa[1]),
+        [wb0] "=&v"(wb[0]), [wb1] "=&v"(wb[1]), [wb2] "=&v"(wb[2]), [wb3] "=&v"(wb[3]), [m0] "+{m0}"(m0)
+      : MX_CUR_OPERANDS, [ada] "v"(ada), [adb] "v"(adb), [adsa] "v"(adsa), [adsb] "v"(adsb),
+        [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [vb0] "v"(vb[0]),
+        [vb1] "v"(vb[1]), [vb2] "v"(vb[2]), [vb3] "v"(vb[3]), [ra] "s"(ra), [rb] "s"(rb), [cs] "s"(cs)
+      : "memory");
+}
+
 // The first stage's first-step operands and scale bytes.
 __device__ __forceinline__ void read_first(uint32_t ada, uint32_t adb, uint32_t adsa, uint32_t adsb,
                                            v4i a[TI], v4i b[TJ], v2u wa[TI], v2u wb[TJ]) {
@@ -378,7 +437,7 @@ __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int
 // past the limits read as zeros and are never stored.  Byte extents of the
 // operands must be < 2 GiB.  `lds` holds LDS_BYTES: the two code slots, the
 // two scale slots and a dummy region.
-template <bool A2D, bool B2D, bool OUT_BF16, class Sched>
+template <bool A2D, bool B2D, bool OUT_BF16, bool SPLIT, class Sched>
 __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, int K, void* C, int64_t ldc,
                                           uint8_t* lds) {
   const int lane = threadIdx.x & 63;
@@ -496,7 +555,10 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
     }
     // the B half of stage g+1's loads (issued by the previous iteration's
     // prefetch position; dummy loads past the end in the first iteration)
-    step0_ld(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb, pend_m0, pend_vb, pend_rb, pend_cs);
+    if constexpr (SPLIT)
+      step0_ld(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb, pend_m0, pend_vb, pend_rb, pend_cs);
+    else
+      step<false>(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb);
     step<true>(acc, na, nb, sa, sb, slot + ra_k[2], slot + rb_k[2], a, b);
     step<false>(acc, a, b, sa2, sb2, slot + ra_k[3], slot + rb_k[3], na, nb);
     // Stage g+2 (the prefetch position): its code offsets.  Past the last
@@ -517,14 +579,19 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
     // stage these reads of unused slots are harmless).
     const uint32_t next = lds_addr + (uint32_t)(((g + 1) & 1) * STAGE_BYTES);
     const uint32_t snext = sl_addr + (uint32_t)(sslot_of(j1, s1) + 8 * (s1 & 1));
-    step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
-              slot + 4096u * wave, va, ra2, (uint32_t)s2 * ROWB);
-    // the B half goes out in the next iteration's first step
+    if constexpr (SPLIT) {
+      step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
+                slot + 4096u * wave, va, ra2, (uint32_t)s2 * ROWB);
+      // the B half goes out in the next iteration's first step
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pend_vb[t] = vb[t];
-    pend_rb = rb2;
-    pend_cs = (uint32_t)s2 * ROWB;
-    pend_m0 = slot + OPB + 4096u * wave;
+      for (int t = 0; t < 4; ++t) pend_vb[t] = vb[t];
+      pend_rb = rb2;
+      pend_cs = (uint32_t)s2 * ROWB;
+      pend_m0 = slot + OPB + 4096u * wave;
+    } else {
+      step_last8(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
+                 slot + 4096u * wave, va, vb, ra2, rb2, (uint32_t)s2 * ROWB);
+    }
     if (more) advance();
     if (++s1 == nst) {
       s1 = 0;
