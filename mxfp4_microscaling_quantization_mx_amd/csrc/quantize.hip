@@ -10,11 +10,9 @@
 // bytes out per element.
 //
 // Two kernel families:
-//  * k_quant_rows_1d — blocks along the contiguous dim.  A quad of 4 lanes
-//    owns one block, 8 elements per lane, so each wave reads 1 KiB of
-//    consecutive bf16 with one 16-byte load per lane and writes 256 consecutive
-//    code bytes.  Hadamard stages 1/2/4 run inside a lane, stages 8/16 across
-//    the quad with DPP quad permutes; amax is a lane max plus two DPP steps.
+//  * k_quant_rows_1d — blocks along the contiguous dim, one lane per block:
+//    four 16-byte loads per lane, the whole 32-point transform and the amax in
+//    registers, one 16-byte code store per lane.
 //  * k_quant_tile — one lane per block, fed from an LDS tile.  Used for blocks
 //    along dim 0 (the transposed output that wgrad and K x N weights need) and
 //    for 2-D 32x32 tiles, whose amax is a reduction over 32 lanes.
@@ -91,10 +89,12 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
     const float inv = inv_scale_from_code(s);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      uint32_t r[8];
-      sr_draws8((p0 >> 3) + g, seed, offset, r);
+      uint32_t w[4];
+      sr_words((p0 >> 3) + g, seed, offset, w);
+      float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) packed[g] |= e2m1_sr(x[8 * g + i] * inv, r[i]) << (4 * i);
+      for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * inv;
+      packed[g] = pack8_sr(v, w);
     }
   } else {
     float sc = scale_f32_normal(s);
@@ -217,10 +217,12 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
       const float inv = inv_scale_from_code(s);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        uint32_t r[8];
-        sr_draws8((uint64_t)(orow * K + kb * 32) / 8 + g, seed, offset, r);
+        uint32_t w[4];
+        sr_words((uint64_t)(orow * K + kb * 32) / 8 + g, seed, offset, w);
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) packed[g] |= e2m1_sr(x[8 * g + i] * inv, r[i]) << (4 * i);
+        for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * inv;
+        packed[g] = pack8_sr(v, w);
       }
     } else {
       float sc = scale_f32_normal(s);

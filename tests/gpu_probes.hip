@@ -8,6 +8,8 @@
 //  * probe_cvt_fp4_sweep: compare the hardware packed FP4 conversion (scale
 //    1.0) with the library's software RNE rounding over every float32 bit
 //    pattern in [lo, hi), counting mismatches and recording the first few.
+//  * probe_cvt_fp4_sr_sweep: the same for the library's hardware stochastic
+//    rounding against its software rule, at draws around each threshold.
 // Every launch is one grid over fixed-size buffers the caller allocated.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -90,6 +92,57 @@ __global__ void k_cvt_scaled_sweep(uint64_t lo, uint64_t hi, int k, unsigned lon
   if (mmul) atomicAdd(counts + 1, mmul);
 }
 
+// Hardware stochastic rounding (mx::pack8_sr) against the library's software
+// rule mx::e2m1_sr for every float32 x in [lo, hi) with |x| < 8.  Each x goes
+// through all four pairs of one packed word as (x, -x) with draws on both sides
+// of its rounding threshold T = floor(f 2^16) (f the exact fraction between
+// grid points), so a rule that is off by one draw or one low bit is caught:
+// pairs (T-1, T+1), (T, T), (T+1, T-1) and two draws hashed from x.
+__device__ uint32_t sr_threshold(float x) {
+  const double a = __builtin_fabs((double)x);
+  const double g[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  int i = 0;
+  while (i < 7 && a >= g[i + 1]) ++i;
+  if (i == 7) return 0u;
+  return (uint32_t)__builtin_floor((a - g[i]) / (g[i + 1] - g[i]) * 65536.0);
+}
+
+__device__ uint32_t clamp16(int64_t r) { return (uint32_t)(r < 0 ? 0 : (r > 65535 ? 65535 : r)); }
+
+__global__ void k_cvt_sr_sweep(uint64_t lo, uint64_t hi, unsigned long long* mismatches, uint32_t* first,
+                               uint32_t first_cap) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  unsigned long long local = 0;
+  for (uint64_t u = lo + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < hi; u += stride) {
+    const float x = __uint_as_float((uint32_t)u);
+    const int64_t t = sr_threshold(x);
+    const uint32_t h = (uint32_t)u * 0x9E3779B9u;
+    const uint32_t r0[4] = {clamp16(t - 1), clamp16(t), clamp16(t + 1), h >> 16};
+    const uint32_t r1[4] = {clamp16(t + 1), clamp16(t), clamp16(t - 1), (h * 0x85EBCA6Bu) >> 16};
+    uint32_t w[4];
+    float v[8];
+    uint32_t sw = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = r0[j] | (r1[j] << 16);
+      v[2 * j] = x;
+      v[2 * j + 1] = -x;
+      sw |= (mx::e2m1_sr(x, r0[j]) | (mx::e2m1_sr(-x, r1[j]) << 4)) << (8 * j);
+    }
+    const uint32_t hw = mx::pack8_sr(v, w);
+    if (hw != sw) {
+      ++local;
+      const unsigned long long k = atomicAdd(mismatches + 1, 1ull);
+      if (k < first_cap) {
+        first[3 * k] = (uint32_t)u;
+        first[3 * k + 1] = hw;
+        first[3 * k + 2] = sw;
+      }
+    }
+  }
+  if (local) atomicAdd(mismatches, local);
+}
+
 extern "C" {
 
 int probe_mfma_scale_32x32x64(const int* a, const int* b, const int* sa, const int* sb, float* out,
@@ -114,6 +167,12 @@ int probe_cvt_fp4_sweep(uint64_t lo, uint64_t hi, unsigned long long* mismatches
 
 int probe_cvt_fp4_scaled_sweep(uint64_t lo, uint64_t hi, int k, unsigned long long* counts) {
   hipLaunchKernelGGL(k_cvt_scaled_sweep, dim3(4096), dim3(256), 0, 0, lo, hi, k, counts);
+  return (int)hipGetLastError();
+}
+
+int probe_cvt_fp4_sr_sweep(uint64_t lo, uint64_t hi, unsigned long long* mismatches, uint32_t* first,
+                           uint32_t first_cap) {
+  hipLaunchKernelGGL(k_cvt_sr_sweep, dim3(4096), dim3(256), 0, 0, lo, hi, mismatches, first, first_cap);
   return (int)hipGetLastError();
 }
 

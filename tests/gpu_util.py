@@ -80,6 +80,7 @@ def probe_lib():
     lib.probe_mfma_scale_16x16x128.argtypes = [P, P, P, P, P]
     lib.probe_cvt_fp4_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, P, P, ctypes.c_uint32]
     lib.probe_cvt_fp4_scaled_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, P]
+    lib.probe_cvt_fp4_sr_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, P, P, ctypes.c_uint32]
     return lib
 
 

@@ -5,6 +5,9 @@
 * The hardware packed FP4 conversion (scale 1.0) against the library's
   software RNE over every float32 input: the quantizer uses the hardware
   instruction for RNE, which is only valid while the two agree everywhere.
+* The hardware stochastic-rounding conversion, as the library drives it,
+  against the library's software SR rule for every float32 |x| < 8 at the
+  draws around each rounding threshold.
 """
 import ctypes
 
@@ -157,3 +160,25 @@ def test_hw_fp4_cvt_scale_operand_divides(k):
     save_npz(f"probe_cvt_scale_{k}.npz", counts=c)
     if k >= -126:
         assert c[0] == 0
+
+
+def test_hw_fp4_sr_matches_software_sr_everywhere():
+    """pack8_sr (the hardware SR conversion on sign(v) ceil(|v| 2^23) with
+    scale 2^23, one draw per element) equals e2m1_sr for every float32 with
+    |x| < 8 (x and -x, all four byte positions), at draws T-1, T, T+1 around
+    the threshold T = floor(f 2^16) and at hashed draws."""
+    need_gpu()
+    lib = probe_lib()
+    cap = 32
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    first = torch.zeros(3 * cap, dtype=torch.int32, device="cuda")
+    banner("cvt sr sweep [0, 8)")
+    assert lib.probe_cvt_fp4_sr_sweep(0, 0x41000000, cnt.data_ptr(), first.data_ptr(), cap) == 0
+    torch.cuda.synchronize()
+    n = int(cnt[0].item())
+    f = first.cpu().numpy().view(np.uint32).reshape(cap, 3)[:min(n, cap)]
+    save_npz("probe_cvt_sr.npz", n=n, first=f)
+    print(f"hw-vs-sw fp4 SR mismatches: {n}")
+    for u, hw, sw in f[:8]:
+        print(f"  x=0x{u:08x} ({np.uint32(u).view(np.float32)!r}) hw=0x{hw:08x} sw=0x{sw:08x}")
+    assert n == 0
