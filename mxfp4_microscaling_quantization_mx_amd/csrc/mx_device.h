@@ -43,8 +43,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-way XORs as one V_BITOP3_B32 each (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -194,7 +195,7 @@ __device__ __forceinline__ uint32_t cvt_sr_pair(float v0, float v1, uint32_t w) 
   const uint32_t R1 = (nw >> 1) | 0x7FFFu;   // bits 30..9 read by element 1: ~r1, then ones
   const uint32_t c0 = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, t, R0, 8388608.0f, 0);
   const uint32_t c1 = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, t, R1, 8388608.0f, 0);
-  return (c0 & 0x0Fu) | (c1 & 0xF0u);
+  return (c0 & 0x0Fu) | (c1 & ~0x0Fu);   // one V_BFI_B32
 }
 
 // 8 values (already divided by the block scale) -> one word of SR codes;

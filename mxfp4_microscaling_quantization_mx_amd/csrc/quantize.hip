@@ -25,7 +25,8 @@ namespace {
 
 // ------------------------------------------------------------------ loads
 // 8 consecutive source elements widened to float32, with the Hadamard sign
-// flips applied as an XOR of the sign bits (exact).
+// flips applied as an XOR of the sign bits (exact).  sgn8 must be uniform
+// across the wave.
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* __restrict__ src, int64_t idx, float x[8],
                                       uint32_t sgn8) {
@@ -34,8 +35,10 @@ __device__ __forceinline__ void load8(const void* __restrict__ src, int64_t idx,
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // bit 15 flips the even element, bit 31 the odd one
-      const uint32_t flip = (((sgn8 >> (2 * i)) & 1u) << 15) | (((sgn8 >> (2 * i + 1)) & 1u) << 31);
+      // bit 15 flips the even element, bit 31 the odd one (sgn8 is the same
+      // in every lane; one scalar register per word keeps it a single XOR)
+      const uint32_t flip = __builtin_amdgcn_readfirstlane(
+          (((sgn8 >> (2 * i)) & 1u) << 15) | (((sgn8 >> (2 * i + 1)) & 1u) << 31));
       const uint32_t v = ww[i] ^ flip;
       x[2 * i] = bf16lo(v);
       x[2 * i + 1] = bf16hi(v);
