@@ -6,16 +6,20 @@
 // E8M0 exponent to floor(log2 amax) - 2, divide by the scale with one float32
 // multiply, round to E2M1 by RNE or stochastic rounding, saturate at +-6, and
 // optionally rotate each block by the 32-point randomized Hadamard transform
-// first.  The kernels are bound by HBM bandwidth: 2 bytes in (bf16) and 0.53
-// bytes out per element.
+// first.  Without stochastic rounding the kernels are bound by HBM bandwidth
+// (2 bytes in (bf16) and 0.53 bytes out per element); with it, by the VALU
+// work of the Philox draws.
 //
-// Two kernel families:
-//  * k_quant_rows_1d — blocks along the contiguous dim, one lane per block:
-//    four 16-byte loads per lane, the whole 32-point transform and the amax in
-//    registers, one 16-byte code store per lane.
-//  * k_quant_tile — one lane per block, fed from an LDS tile.  Used for blocks
-//    along dim 0 (the transposed output that wgrad and K x N weights need) and
-//    for 2-D 32x32 tiles, whose amax is a reduction over 32 lanes.
+// Three kernels, each with one lane per 32-element block and the whole block
+// (transform, amax, rounding) in registers:
+//  * k_quant_rows_1d — blocks along the contiguous dim: four 16-byte loads per
+//    lane, one 16-byte code store per lane.
+//  * k_quant_cols — blocks along dim 0 (the transposed output that wgrad and
+//    K x N weights need), 1-D or 2-D: lane = source column, 32 loads of one
+//    element per lane, each reading 64 consecutive columns across the wave.
+//  * k_quant_tile — 2-D 32x32 tiles along the contiguous dim, fed from an LDS
+//    tile so that a half-wave holds the 32 rows of a tile.
+// For 2-D tiles the amax is a reduction over the 32 lanes of a half-wave.
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -72,7 +76,9 @@ __device__ __forceinline__ void load32(const void* __restrict__ src, int64_t idx
 
 // Quantize one block held in registers (x already sign-flipped when RHT).
 // Returns the scale byte and writes the 16 code bytes to `packed`.
-template <bool RHT, bool SR>
+// With TWO_D the amax is taken over the 32 lanes of the half-wave as well
+// (one lane per column of a 32x32 tile; all 32 lanes must be active).
+template <bool RHT, bool SR, bool TWO_D = false>
 __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packed[4], uint64_t p0,
                                                      uint64_t seed, uint64_t offset) {
   const float c = __uint_as_float(kRhtCBits);
@@ -84,6 +90,10 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
     m = __float_as_uint(c * __uint_as_float(m));      // max |c t_i| = c max |t_i|
 #pragma unroll
     for (int i = 0; i < 32; ++i) x[i] = c * x[i];
+  }
+  if (TWO_D) {
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
   }
   const uint32_t s = scale_code_from_absmax_bits(m);
   packed[0] = packed[1] = packed[2] = packed[3] = 0u;
@@ -135,25 +145,23 @@ __global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ 
   scales[(int64_t)row * ld_scales + kb] = (uint8_t)s;
 }
 
-// ------------------------------------------------------------------ LDS tiles
-// TRANS: source tile of 128 rows x 64 columns; output rows are source columns
-//        (lane -> column), K runs along source rows (wave w -> K-block w).
-// !TRANS: source tile of 64 rows x 128 columns; lane -> row, wave w -> K-block w.
-template <bool TRANS>
+// ------------------------------------------------------------------ 2-D tiles along the last dim
+// Source tile of 64 rows x 128 columns staged through LDS as float32; lane ->
+// row, wave w -> K-block w, so each half-wave holds one 32x32 tile.
 struct TileShape {
-  static constexpr int TR = TRANS ? 128 : 64;   // source rows per tile
-  static constexpr int TC = TRANS ? 64 : 128;   // source cols per tile
-  static constexpr int LD = TRANS ? 64 : 129;   // LDS row pitch in floats (bank-conflict free reads)
+  static constexpr int TR = 64;    // source rows per tile
+  static constexpr int TC = 128;   // source cols per tile
+  static constexpr int LD = 129;   // LDS row pitch in floats (bank-conflict free reads)
 };
 
-template <bool TRANS, bool TWO_D, bool BF16, bool RHT, bool SR>
+template <bool BF16, bool RHT, bool SR>
 __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src, int64_t R,
                                                     int64_t C, int64_t ld_src,
                                                     uint8_t* __restrict__ codes, int64_t ld_codes,
                                                     uint8_t* __restrict__ scales,
                                                     int64_t ld_scales, uint32_t mask,
                                                     uint64_t seed, uint64_t offset) {
-  using S = TileShape<TRANS>;
+  using S = TileShape;
   __shared__ float tile[S::TR * S::LD];
 
   const int64_t r0 = (int64_t)blockIdx.y * S::TR;
@@ -183,76 +191,92 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   // Output coordinates of this lane's block.
-  const int64_t K = TRANS ? R : C;
-  const int64_t orow = TRANS ? c0 + lane : r0 + lane;
-  const int64_t kb = (TRANS ? r0 : c0) / 32 + w;
-  const bool valid = (TRANS ? (orow < C) : (orow < R)) && (kb * 32 < K);
+  const int64_t K = C;
+  const int64_t orow = r0 + lane;
+  const int64_t kb = c0 / 32 + w;
+  const bool valid = orow < R && kb * 32 < K;
 
   float x[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i)
-    x[i] = TRANS ? tile[(w * 32 + i) * S::LD + lane] : tile[lane * S::LD + w * 32 + i];
-  const float c = __uint_as_float(kRhtCBits);
-  if (RHT) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((mask >> i) & 1u) << 31));
-    fwht32_inlane(x);
+  for (int i = 0; i < 32; ++i) {
+    x[i] = tile[lane * S::LD + w * 32 + i];     // zeros past the source edges
+    if (RHT) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((mask >> i) & 1u) << 31));
   }
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-  if (RHT) m = __float_as_uint(c * __uint_as_float(m));     // max |c t_i| = c max |t_i|
-  if (!valid) m = 0;
-  if (TWO_D) {
-    // amax over the 32x32 tile = over the 32 lanes of this half-wave.
-#pragma unroll
-    for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
-  }
+  // every lane takes part in the tile's amax (lanes past the edges hold zeros)
+  uint32_t packed[4];
+  const uint32_t s = quantize_block32<RHT, SR, true>(x, packed, (uint64_t)(orow * K + kb * 32), seed, offset);
   if (!valid) return;
-  if (RHT) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = c * x[i];
-  }
-  const uint32_t s = scale_code_from_absmax_bits(m);
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
-  if (s != 0xFFu) {
-    if (SR) {
-      const float inv = inv_scale_from_code(s);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t w[4];
-        sr_words((uint64_t)(orow * K + kb * 32) / 8 + g, seed, offset, w);
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * inv;
-        packed[g] = pack8_sr(v, w);
-      }
-    } else {
-      float sc = scale_f32_normal(s);
-      if (s == 0u) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = x[i] * __uint_as_float(0x7F000000u);
-        sc = 1.0f;
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) packed[g] = pack8_rne(x + 8 * g, sc);
-    }
-  }
   *reinterpret_cast<uint4*>(codes + orow * ld_codes + kb * 16) =
       make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  if ((orow & 31) == 0) scales[(orow >> 5) * ld_scales + kb] = (uint8_t)s;
+}
+
+// ------------------------------------------------------------------ columns (blocks along dim 0)
+// Blocks along dim 0 without an LDS tile: lane = source column (= output row),
+// wave w of the workgroup = K-block 4*blockIdx.y + w (32 source rows).  Each
+// of the 32 loads of a lane reads one element; across the wave it reads 64
+// consecutive columns of one source row.  The block then goes through the same
+// register path as a row block.  2-D: a half-wave holds one 32x32 tile (output
+// rows are a multiple of 32, so half-waves are whole or empty).
+template <bool TWO_D, bool BF16, bool RHT, bool SR>
+__global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src, int64_t R, int64_t C,
+                                                    int64_t ld_src, uint8_t* __restrict__ codes,
+                                                    int64_t ld_codes, uint8_t* __restrict__ scales,
+                                                    int64_t ld_scales, uint32_t mask, uint64_t seed,
+                                                    uint64_t offset) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t kb = (int64_t)blockIdx.y * 4 + w;
+  if (col >= C || kb * 32 >= R) return;
+  // a raw buffer over the block's 32 source rows: per-lane column offset,
+  // wave-uniform row offsets
+  constexpr int ES = BF16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(src) + kb * 32 * ld_src * ES), 0,
+      (uint32_t)(31 * ld_src * ES + C * ES), 0x00020000);
+  const uint32_t voff = (uint32_t)(col * ES);
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t soff = (uint32_t)(i * ld_src * ES);
+    uint32_t b = BF16 ? ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0) << 16)
+                      : __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+    if (RHT) b ^= ((mask >> i) & 1u) << 31;
+    x[i] = __uint_as_float(b);
+  }
+  uint32_t packed[4];
+  const uint64_t p0 = (uint64_t)col * (uint64_t)R + (uint64_t)kb * 32u;   // output row * K + 32 kb
+  const uint32_t s = quantize_block32<RHT, SR, TWO_D>(x, packed, p0, seed, offset);
+  *reinterpret_cast<uint4*>(codes + col * ld_codes + kb * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   if (!TWO_D) {
-    scales[orow * ld_scales + kb] = (uint8_t)s;
-  } else if ((orow & 31) == 0) {
-    scales[(orow >> 5) * ld_scales + kb] = (uint8_t)s;
+    scales[col * ld_scales + kb] = (uint8_t)s;
+  } else if ((col & 31) == 0) {
+    scales[(col >> 5) * ld_scales + kb] = (uint8_t)s;
   }
 }
 
-template <bool TRANS, bool TWO_D, bool BF16>
+template <bool TWO_D, bool BF16>
+hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)((a.C + 63) / 64), (unsigned)((a.R + 127) / 128));
+#define MX_COLS(RHT_, SR_)                                                                   \
+  hipLaunchKernelGGL((k_quant_cols<TWO_D, BF16, RHT_, SR_>), grid, dim3(256), 0, st, a.src, a.R, a.C, \
+                     a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset)
+  if (a.rht) {
+    if (a.sr) MX_COLS(true, true); else MX_COLS(true, false);
+  } else {
+    if (a.sr) MX_COLS(false, true); else MX_COLS(false, false);
+  }
+#undef MX_COLS
+  return hipGetLastError();
+}
+
+template <bool BF16>
 hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
-  using S = TileShape<TRANS>;
+  using S = TileShape;
   dim3 grid((unsigned)((a.C + S::TC - 1) / S::TC), (unsigned)((a.R + S::TR - 1) / S::TR));
 #define MX_TILE(RHT_, SR_)                                                                   \
-  hipLaunchKernelGGL((k_quant_tile<TRANS, TWO_D, BF16, RHT_, SR_>), grid, dim3(256), 0, st, \
+  hipLaunchKernelGGL((k_quant_tile<BF16, RHT_, SR_>), grid, dim3(256), 0, st,                \
                      a.src, a.R, a.C, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales,  \
                      a.mask, a.seed, a.offset)
   if (a.rht) {
@@ -288,10 +312,10 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   if (a.R == 0 || a.C == 0) return hipSuccess;
   if (!a.dim0 && !a.two_d) return a.bf16 ? launch_rows_1d<true>(a, st) : launch_rows_1d<false>(a, st);
   if (a.dim0) {
-    if (a.two_d) return a.bf16 ? launch_tile<true, true, true>(a, st) : launch_tile<true, true, false>(a, st);
-    return a.bf16 ? launch_tile<true, false, true>(a, st) : launch_tile<true, false, false>(a, st);
+    if (a.two_d) return a.bf16 ? launch_cols<true, true>(a, st) : launch_cols<true, false>(a, st);
+    return a.bf16 ? launch_cols<false, true>(a, st) : launch_cols<false, false>(a, st);
   }
-  return a.bf16 ? launch_tile<false, true, true>(a, st) : launch_tile<false, true, false>(a, st);
+  return a.bf16 ? launch_tile<true>(a, st) : launch_tile<false>(a, st);
 }
 
 }  // namespace mx
