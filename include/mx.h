@@ -107,7 +107,10 @@ typedef struct {
  *            block = cfg->block, ld_codes >= K/2, ld_scales >= K/32,
  *            codes 16-byte aligned with ld_codes a multiple of 16.
  *   Requires K % 32 == 0; 2-D blocks need rows % 32 == 0.  R = 0 or C = 0 is
- *   a no-op.  Reads only src, writes only out's buffers.
+ *   a no-op.  Reads only src, writes only out's buffers.  Size limits (else
+ *   MX_ERR_UNSUPPORTED, nothing launched): last-dim 1-D at most 2^32 - 256
+ *   blocks; last-dim 2-D at most 65535*64 rows; dim-0 at most 65535*128 source
+ *   rows and 32 source rows spanning < 4 GiB.
  */
 mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
                       const mx_quant_cfg* cfg, const mx_tensor* out, void* stream);

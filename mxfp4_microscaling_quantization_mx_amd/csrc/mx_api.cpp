@@ -95,6 +95,8 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
     return fail(MX_ERR_INVALID_ARG, "mx_quantize: src must be 16-byte aligned with ld_src %% 8 == 0");
   if (dim0 && (R + 127) / 128 > 65535)
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize: dim-0 blocking supports at most 65535*128 source rows");
+  if (dim0 && (31 * ld_src + C) * (src_dtype == MX_DT_BF16 ? 2 : 4) > (int64_t)0xFFFFFFFF)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: dim-0 blocking needs 32 source rows to span < 4 GiB");
   if (!dim0 && cfg->block == MX_BLOCK_1D && R * (C / 32) > (int64_t)0xFFFFFF00)
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize: at most 2^32 - 256 blocks per call");
   if (!dim0 && cfg->block == MX_BLOCK_2D && (R + 63) / 64 > 65535)
