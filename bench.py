@@ -49,8 +49,12 @@ def quant_bytes(rows, cols, in_bytes=2):
 
 
 def kernel_source_hash():
+    """Hash of the GPU kernel sources (.hip and device headers; host-side
+    argument checking does not change what the counters measured)."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(SRC_DIR)):
+        if not f.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(SRC_DIR, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
