@@ -48,6 +48,13 @@ def quant_bytes(rows, cols, in_bytes=2):
     return n * in_bytes + n // 2 + n // 32
 
 
+def gather_quant_bytes(src_rows, out_rows, cols, in_bytes=2):
+    """Algorithmic bytes of a gather-quantize: each source row once (routed
+    copies of a token re-read it from cache), codes + scales of every output row."""
+    n = out_rows * cols
+    return src_rows * cols * in_bytes + n // 2 + n // 32
+
+
 def kernel_source_hash():
     """Hash of the GPU kernel sources (.hip and device headers; host-side
     argument checking does not change what the counters measured)."""
@@ -75,10 +82,11 @@ class Workload:
         self.wdy, self.wx = dy.to(dev), xw.to(dev)
         self.w_mask = workloads.rht_mask(workloads.CFG_WGRAD)
         self.w_seed = workloads.philox_seed(workloads.CFG_WGRAD)
-        # MoE: routed activations and pre-quantized expert weights
+        # MoE: token activations, the expert-ordered routing (source token of
+        # each routed row) and pre-quantized expert weights
         tok, offsets = workloads.moe_routing()
-        xt = workloads.to_bf16(workloads.moe_tokens())
-        self.ma = xt[torch.from_numpy(tok)].to(dev)
+        self.mx_tok = workloads.to_bf16(workloads.moe_tokens()).to(dev)
+        self.m_rows = torch.from_numpy(tok.astype(np.int32)).to(dev)
         self.m_offsets = torch.from_numpy(offsets).to(dev)
         E, K, N = 32, 2880, 5760
         self.mb = mx.empty_mx(N, K, "2d", device=dev, experts=E)
@@ -121,7 +129,8 @@ class Workload:
                                                      rounding="sr", seed=self.w_seed, offset=1,
                                                      out=self.w_qx), "hbm", q),
             ("wgrad_gemm", lambda: mx.gemm(self.w_qdy, self.w_qx, out=self.w_dw), "mfma", flop_w),
-            ("moe_quantize_a", lambda: mx.quantize(self.ma, out=self.m_qa), "hbm", quant_bytes(65536, 2880)),
+            ("moe_gather_quantize_a", lambda: mx.quantize_gather(self.mx_tok, self.m_rows, out=self.m_qa), "hbm",
+             gather_quant_bytes(16384, 65536, 2880)),
             ("moe_grouped_gemm", lambda: mx.grouped_gemm(self.m_qa, self.m_offsets, self.mb, out=self.m_y),
              "mfma", flop_m),
         ]

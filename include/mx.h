@@ -116,6 +116,31 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
                       const mx_quant_cfg* cfg, const mx_tensor* out, void* stream);
 
 /*
+ * mx_quantize_gather — mx_quantize of rows gathered by index, 1-D blocks along
+ * the last dim: output row i is the quantization of source row rows[i].  This
+ * is the front end of an MoE layer ("Training an MoE LLM in MXFP4", summary;
+ * "MXFP4", AI Wiki, §Use in models): the routed rows (each token once per
+ * expert it is sent to, grouped by expert) are quantized straight from the
+ * token activations, so the routed bf16 copy is never stored.  The result
+ * equals mx_quantize of the gathered tensor, stochastic-rounding draws
+ * included (they follow the output element index row_out*K + k).
+ *
+ *   src      device; R_src x C elements of src_dtype, row stride ld_src
+ *            elements (>= C), 16-byte aligned, ld_src a multiple of 8.
+ *   rows     device; int32 [rows_out], the source row of each output row.  An
+ *            index outside [0, R_src) gives that output row NaN blocks (scale
+ *            byte 0xFF, codes 0); it is never dereferenced.
+ *   cfg      host; axis must be MX_AXIS_LAST and block MX_BLOCK_1D
+ *            (else MX_ERR_UNSUPPORTED); the other settings as in mx_quantize.
+ *   out      host struct of device buffers: rows = rows_out, K = C, 1-D.
+ *   Requires C % 32 == 0; rows_out = 0 or C = 0 is a no-op; at most
+ *   2^32 - 256 blocks per call.  Reads only src and rows, writes only out.
+ */
+mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, int64_t C, int64_t ld_src,
+                             const int32_t* rows, int64_t rows_out, const mx_quant_cfg* cfg,
+                             const mx_tensor* out, void* stream);
+
+/*
  * mx_dequantize — decode an MXFP4 operand: value = E2M1(code) * 2^(scale-127)
  * ("MXFP4", AI Wiki, §Format specification: X times P_i; NaN scale makes the
  * whole block NaN).  With inverse_rht = 1 the 32-point transform is undone per

@@ -27,7 +27,7 @@ _BLOCK = {"1d": 0, "2d": 1}
 _ROUND = {"rne": 0, "sr": 1}
 _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
-EXPORTED = ("mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
+EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
             "mx_grouped_gemm", "mx_last_error", "mx_version")
 
 
@@ -66,12 +66,13 @@ def load_library(path=LIB_PATH):
     P, I32, I64, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     PT = ctypes.POINTER(MxTensorC)
     lib.mx_quantize.argtypes = [P, I32, I64, I64, I64, ctypes.POINTER(QuantCfgC), PT, P]
+    lib.mx_quantize_gather.argtypes = [P, I32, I64, I64, I64, P, I64, ctypes.POINTER(QuantCfgC), PT, P]
     lib.mx_dequantize.argtypes = [PT, I32, U32, P, I32, I64, P]
     lib.mx_gemm.argtypes = [PT, PT, P, I32, I64, P, ctypes.c_size_t, P]
     lib.mx_gemm_workspace_size.argtypes = [I64, I64, I64]
     lib.mx_gemm_workspace_size.restype = ctypes.c_size_t
     lib.mx_grouped_gemm.argtypes = [PT, P, I32, PT, I64, I64, P, I32, I64, P]
-    for f in ("mx_quantize", "mx_dequantize", "mx_gemm", "mx_grouped_gemm"):
+    for f in ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_gemm", "mx_grouped_gemm"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mx_last_error.restype = ctypes.c_char_p
     lib.mx_last_error.argtypes = []
@@ -152,6 +153,29 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None, seed=0, 
     ot = out.c_struct()
     _check(lib.mx_quantize(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), ctypes.byref(cfg),
                            ctypes.byref(ot), _stream(x)))
+    return out
+
+
+def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0, out=None):
+    """Quantize the rows x[rows[i]] of a 2-D bf16/fp32 CUDA tensor, 1-D blocks
+    along the last dim (see mx_quantize_gather in include/mx.h).  `rows` is an
+    int32 CUDA tensor; indices outside [0, x.shape[0]) give NaN blocks."""
+    lib = load_library()
+    if x.dim() != 2 or x.dtype not in _DTYPE or not x.is_cuda:
+        raise ValueError("quantize_gather expects a 2-D bf16/float32 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("quantize_gather expects a row-major tensor (stride(1) == 1)")
+    if rows.dtype != torch.int32 or rows.dim() != 1 or not rows.is_cuda or not rows.is_contiguous():
+        raise ValueError("quantize_gather expects rows as a contiguous 1-D int32 CUDA tensor")
+    R, C = x.shape
+    n = rows.shape[0]
+    if out is None:
+        out = empty_mx(n, C, "1d", x.device)
+    cfg = QuantCfgC(_AXIS["last"], _BLOCK["1d"], _ROUND[rounding], int(rht_mask is not None),
+                    (rht_mask or 0) & 0xFFFFFFFF, 0, seed & (2**64 - 1), offset & (2**64 - 1))
+    ot = out.c_struct()
+    _check(lib.mx_quantize_gather(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), _ptr(rows), n,
+                                  ctypes.byref(cfg), ctypes.byref(ot), _stream(x)))
     return out
 
 

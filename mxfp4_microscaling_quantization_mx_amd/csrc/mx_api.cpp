@@ -122,6 +122,60 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   return hip_status(mx::launch_quantize(a, static_cast<hipStream_t>(stream)), "mx_quantize");
 }
 
+mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, int64_t C, int64_t ld_src,
+                             const int32_t* rows, int64_t rows_out, const mx_quant_cfg* cfg,
+                             const mx_tensor* out, void* stream) {
+  g_err[0] = '\0';
+  if (!cfg || !out) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: null cfg or out");
+  if (src_dtype != MX_DT_F32 && src_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: unknown source dtype %d", src_dtype);
+  if (cfg->axis != MX_AXIS_LAST || cfg->block != MX_BLOCK_1D)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_gather: only 1-D blocks along the last dim");
+  if (cfg->rounding != MX_ROUND_RNE && cfg->rounding != MX_ROUND_SR)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: unknown rounding %d", cfg->rounding);
+  if (cfg->use_rht != 0 && cfg->use_rht != 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: use_rht must be 0 or 1");
+  if (cfg->reserved != 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: cfg reserved field must be 0");
+  if (R_src < 0 || C < 0 || rows_out < 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: negative shape");
+  if (C % 32) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: C=%lld is not a multiple of 32", (long long)C);
+  if (out->rows != rows_out || out->K != C)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: out is [%lld, %lld], expected [%lld, %lld]",
+                (long long)out->rows, (long long)out->K, (long long)rows_out, (long long)C);
+  if (out->block != MX_BLOCK_1D) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: out must hold 1-D blocks");
+  mx_status st = check_tensor(out, "mx_quantize_gather: out");
+  if (st != MX_OK) return st;
+  if (rows_out == 0 || C == 0) return MX_OK;
+  if (!rows || !aligned(rows, 4)) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: null or unaligned rows");
+  if (R_src > 0) {
+    if (!src) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: null src");
+    if (ld_src < C)
+      return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: ld_src=%lld < C=%lld", (long long)ld_src, (long long)C);
+    if (!aligned(src, 16) || ld_src % 8)
+      return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: src must be 16-byte aligned with ld_src %% 8 == 0");
+  }
+  if (rows_out * (C / 32) > (int64_t)0xFFFFFF00)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_gather: at most 2^32 - 256 blocks per call");
+
+  mx::QuantArgs a{};
+  a.src = src;
+  a.R = rows_out;
+  a.C = C;
+  a.ld_src = ld_src;
+  a.bf16 = src_dtype == MX_DT_BF16;
+  a.rht = cfg->use_rht == 1;
+  a.sr = cfg->rounding == MX_ROUND_SR;
+  a.mask = cfg->rht_sign_mask;
+  a.seed = cfg->philox_seed;
+  a.offset = cfg->philox_offset;
+  a.codes = out->codes;
+  a.ld_codes = out->ld_codes;
+  a.scales = out->scales;
+  a.ld_scales = out->ld_scales;
+  a.gather = rows;
+  a.R_src = R_src;
+  return hip_status(mx::launch_quantize(a, static_cast<hipStream_t>(stream)), "mx_quantize_gather");
+}
+
 mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_sign_mask, void* dst,
                         int32_t dst_dtype, int64_t ld_dst, void* stream) {
   g_err[0] = '\0';

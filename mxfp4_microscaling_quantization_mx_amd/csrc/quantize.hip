@@ -13,7 +13,8 @@
 // Three kernels, each with one lane per 32-element block and the whole block
 // (transform, amax, rounding) in registers:
 //  * k_quant_rows_1d — blocks along the contiguous dim: four 16-byte loads per
-//    lane, one 16-byte code store per lane.
+//    lane, one 16-byte code store per lane; optionally of rows gathered by
+//    index.
 //  * k_quant_cols — blocks along dim 0 (the transposed output that wgrad and
 //    K x N weights need), 1-D or 2-D: lane = source column, 32 loads of one
 //    element per lane, each reading 64 consecutive columns across the wave.
@@ -124,21 +125,34 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
   return s;
 }
 
-template <bool BF16, bool RHT, bool SR>
+// GATHER: output row r quantizes source row gidx[r] (the routed rows of an MoE
+// layer read straight from the token activations); an index outside
+// [0, R_src) gives the row NaN blocks (scale byte 0xFF, codes 0).
+template <bool BF16, bool RHT, bool SR, bool GATHER>
 __global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ src, uint32_t nblocks,
                                                        uint32_t nkb, int64_t ld_src,
                                                        uint8_t* __restrict__ codes, int64_t ld_codes,
                                                        uint8_t* __restrict__ scales,
                                                        int64_t ld_scales, uint32_t mask,
-                                                       uint64_t seed, uint64_t offset) {
+                                                       uint64_t seed, uint64_t offset,
+                                                       const int32_t* __restrict__ gidx, int64_t R_src) {
   const uint32_t g = blockIdx.x * 256u + threadIdx.x;
   if (g >= nblocks) return;
   const uint32_t row = g / nkb;
   const uint32_t kb = g - row * nkb;
+  int64_t srow = row;
+  if (GATHER) {
+    srow = gidx[row];
+    if (srow < 0 || srow >= R_src) {
+      *reinterpret_cast<uint4*>(codes + (int64_t)row * ld_codes + 16 * kb) = make_uint4(0u, 0u, 0u, 0u);
+      scales[(int64_t)row * ld_scales + kb] = 0xFFu;
+      return;
+    }
+  }
   float x[32];
-  load32<BF16>(src, (int64_t)row * ld_src + 32 * kb, x, RHT ? mask : 0u);
+  load32<BF16>(src, srow * ld_src + 32 * kb, x, RHT ? mask : 0u);
   uint32_t packed[4];
-  const uint64_t p0 = ((uint64_t)row * nkb + kb) * 32u;         // row * K + 32 kb
+  const uint64_t p0 = ((uint64_t)row * nkb + kb) * 32u;         // output row * K + 32 kb
   const uint32_t s = quantize_block32<RHT, SR>(x, packed, p0, seed, offset);
   *reinterpret_cast<uint4*>(codes + (int64_t)row * ld_codes + 16 * kb) =
       make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -288,15 +302,15 @@ hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool BF16>
+template <bool BF16, bool GATHER>
 hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
   const uint32_t nkb = (uint32_t)(a.C / 32);
   const uint32_t nblocks = (uint32_t)(a.R * nkb);
   const unsigned grid = (nblocks + 255u) / 256u;
-#define MX_ROWS(RHT_, SR_)                                                                   \
-  hipLaunchKernelGGL((k_quant_rows_1d<BF16, RHT_, SR_>), dim3(grid), dim3(256), 0, st, a.src, \
-                     nblocks, nkb, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, \
-                     a.seed, a.offset)
+#define MX_ROWS(RHT_, SR_)                                                                            \
+  hipLaunchKernelGGL((k_quant_rows_1d<BF16, RHT_, SR_, GATHER>), dim3(grid), dim3(256), 0, st, a.src, \
+                     nblocks, nkb, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask,    \
+                     a.seed, a.offset, a.gather, a.R_src)
   if (a.rht) {
     if (a.sr) MX_ROWS(true, true); else MX_ROWS(true, false);
   } else {
@@ -310,7 +324,8 @@ hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   if (a.R == 0 || a.C == 0) return hipSuccess;
-  if (!a.dim0 && !a.two_d) return a.bf16 ? launch_rows_1d<true>(a, st) : launch_rows_1d<false>(a, st);
+  if (a.gather) return a.bf16 ? launch_rows_1d<true, true>(a, st) : launch_rows_1d<false, true>(a, st);
+  if (!a.dim0 && !a.two_d) return a.bf16 ? launch_rows_1d<true, false>(a, st) : launch_rows_1d<false, false>(a, st);
   if (a.dim0) {
     if (a.two_d) return a.bf16 ? launch_cols<true, true>(a, st) : launch_cols<true, false>(a, st);
     return a.bf16 ? launch_cols<false, true>(a, st) : launch_cols<false, false>(a, st);

@@ -34,6 +34,7 @@ from .philox import philox4x32_10, sr_bits16
 from .rht import rht_forward_f32, rht_inverse_f32, hadamard32_f64
 from .quantize import (
     quantize,
+    quantize_gather,
     dequantize,
     shared_exponent,
     round_e2m1,
@@ -53,6 +54,7 @@ __all__ = [
     "rht_inverse_f32",
     "hadamard32_f64",
     "quantize",
+    "quantize_gather",
     "dequantize",
     "shared_exponent",
     "round_e2m1",

@@ -164,6 +164,27 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
     return pack_nibbles(codes.reshape(rows, K)), scales
 
 
+def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0):
+    """Quantize the gathered rows x[rows[i]] (1-D blocks along the last dim):
+    the MoE front end of "Training an MoE LLM in MXFP4" (summary), where each
+    token's activations are quantized once per expert it is routed to, with
+    the output row number i in the stochastic-rounding element index.  An index
+    outside [0, R) stands for no source row: its output row holds NaN blocks
+    (scale 0xFF, codes 0), the format's only way to mark invalid data
+    ("MXFP4", AI Wiki, §Format specification: the NaN scale poisons the block).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    rows = np.asarray(rows, dtype=np.int64)
+    R, C = x.shape
+    valid = (rows >= 0) & (rows < R)
+    g = np.zeros((rows.shape[0], C), dtype=np.float32)
+    g[valid] = x[rows[valid]]
+    codes, scales = quantize(g, rounding=rounding, rht_mask=rht_mask, seed=seed, offset=offset)
+    codes[~valid] = 0
+    scales[~valid] = E8M0_NAN
+    return codes, scales
+
+
 def dequantize(codes, scales, block="1d", inverse_rht_mask=None, dtype=np.float32):
     """Decode MXFP4: value = E2M1(code) * 2^(scale - 127); scale 0xFF makes the
     whole block NaN.  Optional inverse RHT (float32, canonical order)."""

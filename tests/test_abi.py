@@ -73,6 +73,28 @@ def test_quantize_rejects_bad_arguments(lib):
     assert lib.mx_quantize(None, 1, 0, 64, 64, ctypes.byref(cfg), ctypes.byref(out), None) == mx.MX_OK
 
 
+def test_quantize_gather_rejects_bad_arguments(lib):
+    cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 0, 0, 0)
+    out = _tensor(8, 64)
+    src, rows = ctypes.c_void_p(16), ctypes.c_void_p(16)
+    # only 1-D blocks along the last dim
+    for bad in (mx.QuantCfgC(1, 0, 0, 0, 0, 0, 0, 0), mx.QuantCfgC(0, 1, 0, 0, 0, 0, 0, 0)):
+        st = lib.mx_quantize_gather(src, 1, 32, 64, 64, rows, 8, ctypes.byref(bad), ctypes.byref(out), None)
+        assert st == mx.MX_ERR_UNSUPPORTED and b"1-D" in lib.mx_last_error()
+    st = lib.mx_quantize_gather(src, 1, 32, 48, 48, rows, 8, ctypes.byref(cfg), ctypes.byref(_tensor(8, 48)), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"multiple of 32" in lib.mx_last_error()
+    st = lib.mx_quantize_gather(src, 1, 32, 64, 64, rows, 9, ctypes.byref(cfg), ctypes.byref(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"expected" in lib.mx_last_error()
+    st = lib.mx_quantize_gather(src, 1, 32, 64, 64, None, 8, ctypes.byref(cfg), ctypes.byref(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"rows" in lib.mx_last_error()
+    st = lib.mx_quantize_gather(ctypes.c_void_p(18), 1, 32, 64, 64, rows, 8, ctypes.byref(cfg), ctypes.byref(out),
+                                None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"aligned" in lib.mx_last_error()
+    # no output rows is a no-op
+    assert lib.mx_quantize_gather(None, 1, 32, 64, 64, None, 0, ctypes.byref(cfg), ctypes.byref(_tensor(0, 64)),
+                                  None) == mx.MX_OK
+
+
 def test_gemm_rejects_bad_arguments(lib):
     a = _tensor(32, 64)
     b = _tensor(32, 96)

@@ -231,3 +231,48 @@ def test_quantize_dequantize_round_trip_rht():
     back = host(mx.dequantize(q, torch.float32, inverse_rht_mask=mask))
     rel = np.linalg.norm(back - x) / np.linalg.norm(x)
     assert rel < 0.12
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+@pytest.mark.parametrize("rht", [False, True])
+def test_quantize_gather_parity(dtype, rounding, rht):
+    """mx_quantize_gather against the oracle: repeated, permuted and
+    out-of-range row indices (NaN blocks), a ragged row count, bit-exact."""
+    need_gpu()
+    rng = np.random.default_rng(21 + 2 * int(rht) + (rounding == "sr"))
+    R, C = 61, 416
+    x = (rng.standard_t(3, (R, C)) * np.exp(rng.uniform(-3, 3, (R, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).to(dtype)
+    xn = xt.float().numpy()
+    rows = rng.integers(0, R, 203).astype(np.int32)
+    rows[[0, 17, 202]] = [-1, R, 2**31 - 1]
+    rows[5:9] = rows[4]
+    kw = dict(rounding=rounding, rht_mask=0x2468ACE1 if rht else None, seed=99, offset=4)
+    banner(f"quantize_gather {dtype} {rounding} rht={rht}")
+    q = mx.quantize_gather(xt.cuda(), torch.from_numpy(rows).cuda(), **kw)
+    oc, os_ = oracle.quantize_gather(xn, rows, **kw)
+    codes_equal(host(q.scales), os_, "scales")
+    codes_equal(host(q.codes), oc, "codes")
+
+
+def test_quantize_gather_moe_routing_full_size():
+    """The MoE front end at full size: 16384 tokens x 2880 routed top-4 by the
+    Zipf(1.1) recipe into 65536 expert-ordered rows, quantized straight from the
+    token activations; equal to mx_quantize of the gathered copy (any size
+    property) and to the oracle on 256 sampled output rows."""
+    need_gpu()
+    tok, _ = workloads.moe_routing()
+    xt = workloads.to_bf16(workloads.moe_tokens())
+    xd = xt.cuda()
+    idx = torch.from_numpy(tok.astype(np.int32)).cuda()
+    banner("quantize_gather moe full size")
+    q = mx.quantize_gather(xd, idx)
+    ref = mx.quantize(xd[idx.long()].contiguous())
+    codes_equal(host(q.codes), host(ref.codes), "codes vs gathered copy")
+    codes_equal(host(q.scales), host(ref.scales), "scales vs gathered copy")
+    rng = np.random.default_rng(3)
+    sample = np.sort(rng.choice(tok.shape[0], 256, replace=False))
+    oc, os_ = oracle.quantize_gather(xt.float().numpy(), tok[sample])
+    codes_equal(host(q.codes)[sample], oc, "codes vs oracle")
+    codes_equal(host(q.scales)[sample], os_, "scales vs oracle")

@@ -284,3 +284,31 @@ def test_row_sampling_matches_full_tensor():
     cols = np.array([5, 63, 32])
     c, s = oracle.quantize(x[:, cols], axis="dim0", row_index=cols, **kw)
     assert np.array_equal(c, fc[cols]) and np.array_equal(s, fs[cols])
+
+
+def test_gather_rows_are_quantized_under_their_output_row_number():
+    """quantize_gather: output row i is source row rows[i] quantized with i as
+    its row number in the stochastic-rounding index (checked row by row with
+    the row-sampling form, itself pinned above); the identity gather equals the
+    plain quantizer; out-of-range indices give NaN blocks that dequantize to
+    NaN ("MXFP4", AI Wiki, §Format specification)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((20, 96)).astype(np.float32)
+    kw = dict(rounding="sr", seed=5, offset=9, rht_mask=0x00FF0F0F)
+    ident = np.arange(20)
+    gc, gs = oracle.quantize_gather(x, ident, **kw)
+    fc, fs = oracle.quantize(x, **kw)
+    assert np.array_equal(gc, fc) and np.array_equal(gs, fs)
+    rows = np.array([3, 3, 19, -1, 0, 20, 7])
+    gc, gs = oracle.quantize_gather(x, rows, **kw)
+    for i, r in enumerate(rows):
+        if 0 <= r < 20:
+            c, s = oracle.quantize(x[r:r + 1], row_index=[i], K_total=96, **kw)
+            assert np.array_equal(gc[i:i + 1], c) and np.array_equal(gs[i:i + 1], s)
+        else:
+            assert np.all(gc[i] == 0) and np.all(gs[i] == 0xFF)
+            assert np.all(np.isnan(oracle.dequantize(gc[i:i + 1], gs[i:i + 1])))
+    # the same source row under two output rows: equal scales, and equal codes
+    # under RNE (SR draws differ with the output row number)
+    rc, rs = oracle.quantize_gather(x, rows)
+    assert np.array_equal(rc[0], rc[1]) and np.array_equal(rs[0], rs[1])
