@@ -55,6 +55,32 @@ typedef enum {
   MX_ROUND_SR = 1    /* stochastic rounding with Philox4x32-10 bits, saturate at +-6  */
 } mx_round;
 
+/*
+ * Block scale rule.  The shared exponent of a block with largest magnitude
+ * amax (after the optional transform):
+ *   MX_SCALE_FLOOR        floor(log2 amax) - 2, the reference rule ("MXFP4",
+ *                         AI Wiki, §Conversion rules); the scaled block maximum
+ *                         lies in [4, 8) and values scaling into (6, 8) clip to
+ *                         6 (§Clipping in the reference algorithm).
+ *   MX_SCALE_ROUND_UP     ceil(log2(amax / 6)): the decode scale rounded up to
+ *                         the next power of two so that nothing saturates (the
+ *                         alternative §Clipping in the reference algorithm
+ *                         attributes to NVIDIA's NVFP4 pretraining report); the
+ *                         scaled maximum lies in (3, 6].  Computed exactly as
+ *                         floor(log2 amax) - 2 + (mantissa of amax > 1.5).
+ *   MX_SCALE_PRESCALE_3_4 the reference rule's scale, taken from the block as
+ *                         given; every element is then multiplied by 0.75 (one
+ *                         float32 multiply, after the transform) before it is
+ *                         divided by that scale, so the scaled maximum lies in
+ *                         [3, 6) and no element clips (Tseng, Yu, Park,
+ *                         "Training LLMs with MXFP4", in the table of "MXFP4",
+ *                         AI Wiki, §Training with MXFP4).  The operand then
+ *                         encodes 0.75 x; a product of two such operands is
+ *                         9/16 of x.y and the caller rescales.
+ * All rules clamp the exponent to [-127, 127]; NaN/Inf blocks take 0xFF.
+ */
+typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_ROUND_UP = 1, MX_SCALE_PRESCALE_3_4 = 2 } mx_scale_mode;
+
 /* One MXFP4 operand, K-major (see the format notes above).  All fields are
  * read-only to the library; the buffers are the caller's. */
 typedef struct {
@@ -75,7 +101,7 @@ typedef struct {
   int32_t rounding;        /* mx_round                                            */
   int32_t use_rht;         /* 1: apply the 32-point randomized Hadamard transform */
   uint32_t rht_sign_mask;  /* bit i set: negate element i of every block first   */
-  uint32_t reserved;       /* must be 0                                           */
+  uint32_t scale_mode;     /* mx_scale_mode (0: the reference rule)               */
   uint64_t philox_seed;    /* SR: Philox key = (seed mod 2^32, seed >> 32)        */
   uint64_t philox_offset;  /* SR: counter words 2,3 = (offset mod 2^32, offset >> 32) */
 } mx_quant_cfg;

@@ -25,6 +25,7 @@ MX_DT_F32, MX_DT_BF16 = 0, 1
 _AXIS = {"last": 0, "dim0": 1}
 _BLOCK = {"1d": 0, "2d": 1}
 _ROUND = {"rne": 0, "sr": 1}
+_SCALE = {"floor": 0, "round_up": 1, "prescale_3_4": 2}
 _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
 EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
@@ -41,7 +42,7 @@ class MxTensorC(ctypes.Structure):
 class QuantCfgC(ctypes.Structure):
     _fields_ = [("axis", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("rounding", ctypes.c_int32), ("use_rht", ctypes.c_int32),
-                ("rht_sign_mask", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("rht_sign_mask", ctypes.c_uint32), ("scale_mode", ctypes.c_uint32),
                 ("philox_seed", ctypes.c_uint64), ("philox_offset", ctypes.c_uint64)]
 
 
@@ -135,10 +136,11 @@ def expert(q, e):
 
 
 def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None, seed=0, offset=0,
-             out=None):
+             out=None, scale_mode="floor"):
     """Quantize a 2-D bf16/fp32 CUDA tensor to MXFP4 (see mx_quantize in include/mx.h).
 
-    axis="dim0" blocks along dim 0 and returns the quantized transpose."""
+    axis="dim0" blocks along dim 0 and returns the quantized transpose.
+    scale_mode: "floor" (the reference rule), "round_up" or "prescale_3_4"."""
     lib = load_library()
     if x.dim() != 2 or x.dtype not in _DTYPE or not x.is_cuda:
         raise ValueError("quantize expects a 2-D bf16/float32 CUDA tensor")
@@ -149,14 +151,15 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None, seed=0, 
     if out is None:
         out = empty_mx(rows, K, block, x.device)
     cfg = QuantCfgC(_AXIS[axis], _BLOCK[block], _ROUND[rounding], int(rht_mask is not None),
-                    (rht_mask or 0) & 0xFFFFFFFF, 0, seed & (2**64 - 1), offset & (2**64 - 1))
+                    (rht_mask or 0) & 0xFFFFFFFF, _SCALE[scale_mode], seed & (2**64 - 1),
+                    offset & (2**64 - 1))
     ot = out.c_struct()
     _check(lib.mx_quantize(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), ctypes.byref(cfg),
                            ctypes.byref(ot), _stream(x)))
     return out
 
 
-def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0, out=None):
+def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0, out=None, scale_mode="floor"):
     """Quantize the rows x[rows[i]] of a 2-D bf16/fp32 CUDA tensor, 1-D blocks
     along the last dim (see mx_quantize_gather in include/mx.h).  `rows` is an
     int32 CUDA tensor; indices outside [0, x.shape[0]) give NaN blocks."""
@@ -172,7 +175,8 @@ def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0, ou
     if out is None:
         out = empty_mx(n, C, "1d", x.device)
     cfg = QuantCfgC(_AXIS["last"], _BLOCK["1d"], _ROUND[rounding], int(rht_mask is not None),
-                    (rht_mask or 0) & 0xFFFFFFFF, 0, seed & (2**64 - 1), offset & (2**64 - 1))
+                    (rht_mask or 0) & 0xFFFFFFFF, _SCALE[scale_mode], seed & (2**64 - 1),
+                    offset & (2**64 - 1))
     ot = out.c_struct()
     _check(lib.mx_quantize_gather(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), _ptr(rows), n,
                                   ctypes.byref(cfg), ctypes.byref(ot), _stream(x)))

@@ -76,7 +76,8 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
     return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown block kind %d", cfg->block);
   if (cfg->use_rht != 0 && cfg->use_rht != 1)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize: use_rht must be 0 or 1");
-  if (cfg->reserved != 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize: cfg reserved field must be 0");
+  if (cfg->scale_mode > MX_SCALE_PRESCALE_3_4)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown scale_mode %u", cfg->scale_mode);
   if (R < 0 || C < 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize: negative shape");
   const bool dim0 = cfg->axis == MX_AXIS_DIM0;
   const int64_t rows_out = dim0 ? C : R;
@@ -115,6 +116,7 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   a.mask = cfg->rht_sign_mask;
   a.seed = cfg->philox_seed;
   a.offset = cfg->philox_offset;
+  a.scale_mode = (int)cfg->scale_mode;
   a.codes = out->codes;
   a.ld_codes = out->ld_codes;
   a.scales = out->scales;
@@ -135,7 +137,8 @@ mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, 
     return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: unknown rounding %d", cfg->rounding);
   if (cfg->use_rht != 0 && cfg->use_rht != 1)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: use_rht must be 0 or 1");
-  if (cfg->reserved != 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: cfg reserved field must be 0");
+  if (cfg->scale_mode > MX_SCALE_PRESCALE_3_4)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: unknown scale_mode %u", cfg->scale_mode);
   if (R_src < 0 || C < 0 || rows_out < 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: negative shape");
   if (C % 32) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: C=%lld is not a multiple of 32", (long long)C);
   if (out->rows != rows_out || out->K != C)
@@ -167,6 +170,7 @@ mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, 
   a.mask = cfg->rht_sign_mask;
   a.seed = cfg->philox_seed;
   a.offset = cfg->philox_offset;
+  a.scale_mode = (int)cfg->scale_mode;
   a.codes = out->codes;
   a.ld_codes = out->ld_codes;
   a.scales = out->scales;

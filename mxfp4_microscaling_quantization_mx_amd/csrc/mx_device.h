@@ -76,7 +76,17 @@ __device__ __forceinline__ uint32_t scale_code_from_absmax_bits(uint32_t m) {
   return (uint32_t)(be > 2 ? be - 2 : 0);
 }
 
-// 2^-(s-127) as float32 for a finite scale byte s <= 252 (always a normal).
+// Round-up rule: the smallest power of two X with amax / X <= 6, i.e. the
+// exponent ceil(log2(amax / 6)) = floor(log2 amax) - 2 + (mantissa > 1.5),
+// clamped at 0 (zero and subnormal amax, and amax below 1.5 * 2^-125, give
+// byte 0); NaN/Inf -> 0xFF.
+__device__ __forceinline__ uint32_t scale_code_round_up(uint32_t m) {
+  if (m >= 0x7F800000u) return 0xFFu;
+  const int c = (int)(m >> 23) - 2 + (int)((m & 0x7FFFFFu) > 0x400000u);
+  return (uint32_t)(c > 0 ? c : 0);
+}
+
+// 2^-(s-127) as float32 for a finite scale byte s <= 253 (always a normal).
 __device__ __forceinline__ float inv_scale_from_code(uint32_t s) {
   return __uint_as_float((254u - s) << 23);
 }

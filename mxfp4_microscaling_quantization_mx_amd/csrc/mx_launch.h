@@ -21,6 +21,7 @@ struct QuantArgs {
   int64_t ld_codes;
   uint8_t* scales;
   int64_t ld_scales;
+  int scale_mode = 0;                // 0 reference rule, 1 round up, 2 prescale by 3/4
   const int32_t* gather = nullptr;   // device [R]: source row of each output row (last dim, 1-D only)
   int64_t R_src = 0;                 // source rows when gathering
 };

@@ -79,14 +79,18 @@ __device__ __forceinline__ void load32(const void* __restrict__ src, int64_t idx
 // Returns the scale byte and writes the 16 code bytes to `packed`.
 // With TWO_D the amax is taken over the 32 lanes of the half-wave as well
 // (one lane per column of a 32x32 tile; all 32 lanes must be active).
+// scale_mode (wave-uniform): 0 the reference rule floor(log2 amax) - 2; 1 the
+// round-up rule; 2 the reference rule's scale with every element multiplied by
+// 0.75 (one float32 multiply) before the division, so nothing clips.
 template <bool RHT, bool SR, bool TWO_D = false>
 __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packed[4], uint64_t p0,
-                                                     uint64_t seed, uint64_t offset) {
+                                                     uint64_t seed, uint64_t offset, int scale_mode) {
   const float c = __uint_as_float(kRhtCBits);
   if (RHT) fwht32_inlane(x);
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  // multiplying by a positive constant commutes with the max (rounding is monotone)
   if (RHT) {
     m = __float_as_uint(c * __uint_as_float(m));      // max |c t_i| = c max |t_i|
 #pragma unroll
@@ -96,9 +100,13 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
 #pragma unroll
     for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
   }
-  const uint32_t s = scale_code_from_absmax_bits(m);
+  const uint32_t s = scale_mode == 1 ? scale_code_round_up(m) : scale_code_from_absmax_bits(m);
   packed[0] = packed[1] = packed[2] = packed[3] = 0u;
   if (s == 0xFFu) return s;
+  if (scale_mode == 2) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.75f * x[i];
+  }
   if (SR) {
     const float inv = inv_scale_from_code(s);
 #pragma unroll
@@ -134,7 +142,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ 
                                                        uint8_t* __restrict__ codes, int64_t ld_codes,
                                                        uint8_t* __restrict__ scales,
                                                        int64_t ld_scales, uint32_t mask,
-                                                       uint64_t seed, uint64_t offset,
+                                                       uint64_t seed, uint64_t offset, int scale_mode,
                                                        const int32_t* __restrict__ gidx, int64_t R_src) {
   const uint32_t g = blockIdx.x * 256u + threadIdx.x;
   if (g >= nblocks) return;
@@ -153,7 +161,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ 
   load32<BF16>(src, srow * ld_src + 32 * kb, x, RHT ? mask : 0u);
   uint32_t packed[4];
   const uint64_t p0 = ((uint64_t)row * nkb + kb) * 32u;         // output row * K + 32 kb
-  const uint32_t s = quantize_block32<RHT, SR>(x, packed, p0, seed, offset);
+  const uint32_t s = quantize_block32<RHT, SR>(x, packed, p0, seed, offset, scale_mode);
   *reinterpret_cast<uint4*>(codes + (int64_t)row * ld_codes + 16 * kb) =
       make_uint4(packed[0], packed[1], packed[2], packed[3]);
   scales[(int64_t)row * ld_scales + kb] = (uint8_t)s;
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
                                                     uint8_t* __restrict__ codes, int64_t ld_codes,
                                                     uint8_t* __restrict__ scales,
                                                     int64_t ld_scales, uint32_t mask,
-                                                    uint64_t seed, uint64_t offset) {
+                                                    uint64_t seed, uint64_t offset, int scale_mode) {
   using S = TileShape;
   __shared__ float tile[S::TR * S::LD];
 
@@ -218,7 +226,8 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
   }
   // every lane takes part in the tile's amax (lanes past the edges hold zeros)
   uint32_t packed[4];
-  const uint32_t s = quantize_block32<RHT, SR, true>(x, packed, (uint64_t)(orow * K + kb * 32), seed, offset);
+  const uint32_t s =
+      quantize_block32<RHT, SR, true>(x, packed, (uint64_t)(orow * K + kb * 32), seed, offset, scale_mode);
   if (!valid) return;
   *reinterpret_cast<uint4*>(codes + orow * ld_codes + kb * 16) =
       make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
                                                     int64_t ld_src, uint8_t* __restrict__ codes,
                                                     int64_t ld_codes, uint8_t* __restrict__ scales,
                                                     int64_t ld_scales, uint32_t mask, uint64_t seed,
-                                                    uint64_t offset) {
+                                                    uint64_t offset, int scale_mode) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t col = (int64_t)blockIdx.x * 64 + lane;
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
   }
   uint32_t packed[4];
   const uint64_t p0 = (uint64_t)col * (uint64_t)R + (uint64_t)kb * 32u;   // output row * K + 32 kb
-  const uint32_t s = quantize_block32<RHT, SR, TWO_D>(x, packed, p0, seed, offset);
+  const uint32_t s = quantize_block32<RHT, SR, TWO_D>(x, packed, p0, seed, offset, scale_mode);
   *reinterpret_cast<uint4*>(codes + col * ld_codes + kb * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   if (!TWO_D) {
     scales[col * ld_scales + kb] = (uint8_t)s;
@@ -275,7 +284,8 @@ hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
   dim3 grid((unsigned)((a.C + 63) / 64), (unsigned)((a.R + 127) / 128));
 #define MX_COLS(RHT_, SR_)                                                                   \
   hipLaunchKernelGGL((k_quant_cols<TWO_D, BF16, RHT_, SR_>), grid, dim3(256), 0, st, a.src, a.R, a.C, \
-                     a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset)
+                     a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset,      \
+                     a.scale_mode)
   if (a.rht) {
     if (a.sr) MX_COLS(true, true); else MX_COLS(true, false);
   } else {
@@ -292,7 +302,7 @@ hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
 #define MX_TILE(RHT_, SR_)                                                                   \
   hipLaunchKernelGGL((k_quant_tile<BF16, RHT_, SR_>), grid, dim3(256), 0, st,                \
                      a.src, a.R, a.C, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales,  \
-                     a.mask, a.seed, a.offset)
+                     a.mask, a.seed, a.offset, a.scale_mode)
   if (a.rht) {
     if (a.sr) MX_TILE(true, true); else MX_TILE(true, false);
   } else {
@@ -310,7 +320,7 @@ hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
 #define MX_ROWS(RHT_, SR_)                                                                            \
   hipLaunchKernelGGL((k_quant_rows_1d<BF16, RHT_, SR_, GATHER>), dim3(grid), dim3(256), 0, st, a.src, \
                      nblocks, nkb, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask,    \
-                     a.seed, a.offset, a.gather, a.R_src)
+                     a.seed, a.offset, a.scale_mode, a.gather, a.R_src)
   if (a.rht) {
     if (a.sr) MX_ROWS(true, true); else MX_ROWS(true, false);
   } else {

@@ -15,6 +15,15 @@ Sources:
     block scales stored apart, blocks along the last dimension.
   * "Training an MoE LLM in MXFP4", summary: hybrid 1D/2D block quantization,
     randomized Hadamard transform, stochastic rounding.
+  * Two other scale rules, both named on the MXFP4 page:
+    - "round_up" (§Clipping in the reference algorithm, the rule credited to
+      NVIDIA's NVFP4 pretraining report): the decode scale amax/6 rounded up to
+      a power of two, so that no element saturates.
+    - "prescale_3_4" (§Training with MXFP4, the table's Tseng, Yu, Park
+      row): the inputs are multiplied by 3/4 before quantizing so that nothing
+      clips.  Read as: the
+      reference rule's scale of the block as given, and every element times
+      3/4 (one float32 multiply) before the division by it.
 
 Steps per block, in the order they are taken (float32 where stated):
   1. x = float32(source) (bf16 widens exactly).
@@ -23,8 +32,10 @@ Steps per block, in the order they are taken (float32 where stated):
      tile).  A block holding any NaN or +-Inf gets scale 0xFF and all codes 0.
   4. E = floor(log2 amax) taken exactly from the float32 exponent (subnormals
      included); e = clamp(E - 2, -127, 127); amax == 0 gives e = -127.
-     Scale byte = e + 127.
-  5. v_i = float32(y_i * 2^-e): one float32 multiply (exact unless the result
+     round_up: e = the smallest integer with amax <= 6 * 2^e, clamped the
+     same way.  Scale byte = e + 127.
+  5. prescale_3_4 only: y_i = float32(0.75 * y_i).
+     v_i = float32(y_i * 2^-e): one float32 multiply (exact unless the result
      is a float32 subnormal, which is rounded to nearest even and never flushed).
   6. Round |v_i| onto the grid {0, .5, 1, 1.5, 2, 3, 4, 6}: |v| >= 6 saturates
      to 6; otherwise lo <= |v| < hi are the neighbouring grid points and
@@ -56,6 +67,22 @@ def shared_exponent(amax):
     e = (ex.astype(np.int64) - 1) - 2
     e = np.clip(e, -127, 127)
     return np.where(a == 0, -127, e)
+
+
+def round_up_exponent(amax):
+    """The smallest integer e with amax <= 6 * 2^e, clamped to [-127, 127], for
+    finite float32 amax >= 0 (amax == 0 maps to -127).  The candidate
+    floor(log2 amax) - 2 from frexp is tried first and raised by one when
+    6 * 2^e still falls short; both sides are exact in float64."""
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    _, ex = np.frexp(a)
+    e = ex.astype(np.int64) - 3
+    e = np.where(a > np.ldexp(6.0, e.astype(np.int32)), e + 1, e)
+    e = np.clip(e, -127, 127)
+    return np.where(a == 0, -127, e)
+
+
+SCALE_MODES = ("floor", "round_up", "prescale_3_4")
 
 
 def round_e2m1(v, rounding="rne", r=None):
@@ -96,7 +123,7 @@ def unpack_nibbles(packed):
 
 
 def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
-             seed=0, offset=0, row_index=None, K_total=None):
+             seed=0, offset=0, row_index=None, K_total=None, scale_mode="floor"):
     """Quantize a 2-D float array to MXFP4.
 
     axis="last": blocks along the last dim, output [R, C] with K = C.
@@ -110,6 +137,7 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
     source columns, for axis="dim0") of a larger tensor: they give the global
     output-row numbers and the global K used in the stochastic-rounding element
     index p = row * K + k.  They change nothing else.
+    scale_mode: "floor" (the reference rule), "round_up" or "prescale_3_4".
     """
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
@@ -119,6 +147,8 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
     elif axis != "last":
         raise ValueError(f"unknown axis {axis!r}")
     rows, K = x.shape
+    if scale_mode not in SCALE_MODES:
+        raise ValueError(f"unknown scale_mode {scale_mode!r}")
     if K % BLOCK:
         raise ValueError("the blocking dimension must be a multiple of 32")
     if block == "2d" and rows % BLOCK:
@@ -141,7 +171,7 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
         else:
             raise ValueError(f"unknown block {block!r}")
 
-        e = shared_exponent(amax)
+        e = round_up_exponent(amax) if scale_mode == "round_up" else shared_exponent(amax)
         scales = np.where(bad, E8M0_NAN, e + E8M0_BIAS).astype(np.uint8)
 
         if block == "2d":                       # per-element view of the tile scale
@@ -149,6 +179,8 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
             bad_el = np.repeat(bad, BLOCK, axis=0)
         else:
             e_el, bad_el = e, bad
+        if scale_mode == "prescale_3_4":
+            y = (np.float32(0.75) * y).astype(np.float32)
         factor = np.ldexp(np.float32(1.0), (-e_el).astype(np.int32)).astype(np.float32)
         v = (y * factor[..., None]).astype(np.float32)
 
@@ -164,7 +196,8 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
     return pack_nibbles(codes.reshape(rows, K)), scales
 
 
-def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0):
+def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0,
+                    scale_mode="floor"):
     """Quantize the gathered rows x[rows[i]] (1-D blocks along the last dim):
     the MoE front end of "Training an MoE LLM in MXFP4" (summary), where each
     token's activations are quantized once per expert it is routed to, with
@@ -179,7 +212,8 @@ def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0):
     valid = (rows >= 0) & (rows < R)
     g = np.zeros((rows.shape[0], C), dtype=np.float32)
     g[valid] = x[rows[valid]]
-    codes, scales = quantize(g, rounding=rounding, rht_mask=rht_mask, seed=seed, offset=offset)
+    codes, scales = quantize(g, rounding=rounding, rht_mask=rht_mask, seed=seed, offset=offset,
+                             scale_mode=scale_mode)
     codes[~valid] = 0
     scales[~valid] = E8M0_NAN
     return codes, scales

@@ -52,6 +52,9 @@ def test_quantize_rejects_bad_arguments(lib):
     out = _tensor(32, 64)
     st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(bad_cfg), ctypes.byref(out), None)
     assert st == mx.MX_ERR_INVALID_ARG and b"rounding" in lib.mx_last_error()
+    bad_cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 3, 0, 0)
+    st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(bad_cfg), ctypes.byref(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"scale_mode" in lib.mx_last_error()
     # output shape must match the axis
     cfg = mx.QuantCfgC(1, 0, 0, 0, 0, 0, 0, 0)
     out = _tensor(32, 64)
@@ -81,6 +84,9 @@ def test_quantize_gather_rejects_bad_arguments(lib):
     for bad in (mx.QuantCfgC(1, 0, 0, 0, 0, 0, 0, 0), mx.QuantCfgC(0, 1, 0, 0, 0, 0, 0, 0)):
         st = lib.mx_quantize_gather(src, 1, 32, 64, 64, rows, 8, ctypes.byref(bad), ctypes.byref(out), None)
         assert st == mx.MX_ERR_UNSUPPORTED and b"1-D" in lib.mx_last_error()
+    bad = mx.QuantCfgC(0, 0, 0, 0, 0, 9, 0, 0)
+    st = lib.mx_quantize_gather(src, 1, 32, 64, 64, rows, 8, ctypes.byref(bad), ctypes.byref(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"scale_mode" in lib.mx_last_error()
     st = lib.mx_quantize_gather(src, 1, 32, 48, 48, rows, 8, ctypes.byref(cfg), ctypes.byref(_tensor(8, 48)), None)
     assert st == mx.MX_ERR_INVALID_ARG and b"multiple of 32" in lib.mx_last_error()
     st = lib.mx_quantize_gather(src, 1, 32, 64, 64, rows, 9, ctypes.byref(cfg), ctypes.byref(out), None)

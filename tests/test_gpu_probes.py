@@ -143,12 +143,13 @@ def test_hw_fp4_cvt_matches_software_rne_everywhere():
     assert n_in == 0 and n_out == 0
 
 
-@pytest.mark.parametrize("k", [-127, -126, -100, -60, -3, -1, 0, 1, 2, 17, 90, 124, 125])
+@pytest.mark.parametrize("k", [-127, -126, -100, -60, -3, -1, 0, 1, 2, 17, 90, 124, 125, 126])
 def test_hw_fp4_cvt_scale_operand_divides(k):
     """With a power-of-two scale 2^k the instruction returns exactly
     RNE_fp4(RNE_fp32(x * 2^-k)) for every non-NaN x: the quantizer hands it the
     block scale instead of multiplying first (scale bytes >= 1; the lowest
-    scale byte, whose 2^-127 is a float32 subnormal, is checked too)."""
+    scale byte, whose 2^-127 is a float32 subnormal, is checked too; 2^126 is
+    the largest scale the round-up rule gives)."""
     need_gpu()
     lib = probe_lib()
     cnt = torch.zeros(2, dtype=torch.int64, device="cuda")

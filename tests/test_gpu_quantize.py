@@ -276,3 +276,80 @@ def test_quantize_gather_moe_routing_full_size():
     oc, os_ = oracle.quantize_gather(xt.float().numpy(), tok[sample])
     codes_equal(host(q.codes)[sample], oc, "codes vs oracle")
     codes_equal(host(q.scales)[sample], os_, "scales vs oracle")
+
+
+SCALE_MODES = [dict(m, scale_mode=s) for s in ("round_up", "prescale_3_4") for m in MODES]
+
+
+def _scale_mode_id(m):
+    return f"{m['scale_mode']}-{_mode_id(m)}"
+
+
+@pytest.mark.parametrize("mode", SCALE_MODES, ids=_scale_mode_id)
+def test_quantize_scale_modes_ragged(mode):
+    """The round-up and 3/4-prescale scale rules in every kernel (rows, tile,
+    columns; both roundings; with and without the transform) on ragged bf16
+    shapes, bit-exact against the oracle."""
+    need_gpu()
+    R, C = {("last", "1d"): (45, 352), ("dim0", "1d"): (192, 88),
+            ("last", "2d"): (64, 288), ("dim0", "2d"): (224, 64)}[(mode["axis"], mode["block"])]
+    rng = np.random.default_rng(zlib.crc32(_scale_mode_id(mode).encode()))
+    x = (rng.standard_t(3, (R, C)) * np.exp(rng.uniform(-3, 3, (R, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    kw = dict(mode, seed=0x0F1E_2D3C_4B5A_6978, offset=11)
+    banner(f"quantize {_scale_mode_id(mode)} R={R} C={C}")
+    gc, gs, _ = _gpu_quant(xt.cuda(), **kw)
+    oc, os_ = _ora_quant(xt.float().numpy(), **kw)
+    codes_equal(gs, os_, "scales")
+    codes_equal(gc, oc, "codes")
+
+
+def _scale_boundary_rows():
+    """Block maxima at and one float32 ulp around 1.5 * 2^k (where the round-up
+    rule moves a binade), at the largest finite float32 (scale byte 253 under
+    round-up), in the clip band and in the subnormal range."""
+    rows = []
+    for k in (-140, -126, -125, -124, -60, -1, 0, 1, 3, 40, 126):
+        b = np.float32(1.5 * 2.0 ** k)
+        for m in (np.nextafter(b, np.float32(0)), b, np.nextafter(b, np.float32(np.inf))):
+            r = np.linspace(-1, 1, 32, dtype=np.float32) * np.float32(m)
+            r[7] = -m
+            rows.append(r)
+    big = np.finfo(np.float32).max
+    rows.append((np.linspace(-1, 1, 32) * float(big)).astype(np.float32))
+    rows.append(np.array([7.5, -7.99, 6.5, 5.0] * 8, dtype=np.float32))
+    rows.append(np.full(32, 2.0 ** -149, dtype=np.float32))
+    return np.array(rows, dtype=np.float32).reshape(-1, 64)
+
+
+@pytest.mark.parametrize("scale_mode", ["floor", "round_up", "prescale_3_4"])
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_quantize_scale_mode_boundaries(scale_mode, rounding):
+    need_gpu()
+    x = _scale_boundary_rows()
+    banner(f"quantize scale boundaries {scale_mode} {rounding}")
+    for axis in ("last", "dim0"):
+        xx = x if axis == "last" else np.ascontiguousarray(x.T)
+        R, C = xx.shape
+        buf = np.zeros((R, (C + 7) // 8 * 8), dtype=np.float32)   # row stride: 8 elements
+        buf[:, :C] = xx
+        gc, gs, _ = _gpu_quant(to_dev(buf)[:, :C], axis=axis, rounding=rounding, seed=7, offset=1,
+                               scale_mode=scale_mode)
+        oc, os_ = _ora_quant(xx, axis=axis, rounding=rounding, seed=7, offset=1, scale_mode=scale_mode)
+        codes_equal(gs, os_, f"scales {axis}")
+        codes_equal(gc, oc, f"codes {axis}")
+
+
+@pytest.mark.parametrize("scale_mode", ["round_up", "prescale_3_4"])
+def test_quantize_gather_scale_modes(scale_mode):
+    need_gpu()
+    rng = np.random.default_rng(31)
+    R, C = 40, 288
+    x = (rng.standard_t(3, (R, C)) * np.exp(rng.uniform(-3, 3, (R, 1)))).astype(np.float32)
+    rows = rng.integers(-2, R + 2, 77).astype(np.int32)
+    kw = dict(rounding="sr", rht_mask=0x0BADF00D, seed=3, offset=8, scale_mode=scale_mode)
+    banner(f"quantize_gather {scale_mode}")
+    q = mx.quantize_gather(to_dev(x), torch.from_numpy(rows).cuda(), **kw)
+    oc, os_ = oracle.quantize_gather(x, rows, **kw)
+    codes_equal(host(q.scales), os_, "scales")
+    codes_equal(host(q.codes), oc, "codes")

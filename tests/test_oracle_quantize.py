@@ -312,3 +312,149 @@ def test_gather_rows_are_quantized_under_their_output_row_number():
     # under RNE (SR draws differ with the output row number)
     rc, rs = oracle.quantize_gather(x, rows)
     assert np.array_equal(rc[0], rc[1]) and np.array_equal(rs[0], rs[1])
+
+
+# ---------------------------------------------------------------- scale variants
+def _round_up_exponent_bruteforce(amax):
+    """Smallest integer e in [-127, 127] with amax <= 6 * 2^e, by search
+    (exact rational arithmetic through Python floats: 6 * 2^e is exact)."""
+    for e in range(-127, 128):
+        if amax <= 6.0 * 2.0 ** e:
+            return e
+    return 127
+
+
+def test_round_up_scale_is_smallest_power_of_two_without_saturation():
+    """round_up: the decode scale amax/6 rounded up to a power of two ("MXFP4",
+    AI Wiki, §Clipping in the reference algorithm), by brute force over all
+    exponents, including the boundary amax = 1.5 * 2^k where amax/6 is itself
+    a power of two, and the clamped ends."""
+    p = params("scale_variants.txt")
+    top = float(p["round_up_max_scaled"])
+    rng = np.random.default_rng(21)
+    mags = [float(np.float32(v)) for v in
+            np.ldexp(rng.uniform(1.0, 2.0, 3000), rng.integers(-140, 128, 3000))]
+    for k in range(-149, 128):
+        b = np.float32(1.5 * 2.0 ** k) if k < 127 else np.float32(2.0 ** 127)
+        if b == 0 or not np.isfinite(b):
+            continue
+        mags += [float(b), float(np.nextafter(b, np.float32(np.inf))),
+                 float(np.nextafter(b, np.float32(0)))]
+    mags += [float(np.finfo(np.float32).max), float(np.float32(2.0 ** -149))]
+    for m in mags:
+        x = np.zeros((1, 32), dtype=np.float32)
+        x[0, 5] = -m
+        codes, scales = oracle.quantize(x, scale_mode="round_up")
+        e = _round_up_exponent_bruteforce(m)
+        assert int(scales[0, 0]) == e + 127, m
+        if e > -127:
+            assert m / 2.0 ** e <= top and m / 2.0 ** e > top / 2
+    # the boundary: scaled max exactly 6 stays at 6, one ulp above moves a binade
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 1.5
+    c, s = oracle.quantize(x, scale_mode="round_up")
+    assert oracle.e8m0_decode(s[0, 0]) == 0.25 and oracle.dequantize(c, s)[0, 0] == 1.5
+    x[0, 0] = np.nextafter(np.float32(1.5), np.float32(2))
+    c, s = oracle.quantize(x, scale_mode="round_up")
+    assert oracle.e8m0_decode(s[0, 0]) == 0.5
+
+
+def test_round_up_never_saturates_and_worst_case_binades():
+    """With round_up no element scales above 6, so RNE codes are the nearest
+    grid point by brute force with no clipping; the worst case (amax just
+    above 6 * 2^k) leaves the 4 and 6 magnitudes unused, log2(3/0.5) of
+    log2(6/0.5) binades ("MXFP4", AI Wiki, §Clipping in the reference
+    algorithm: about 2.58 of 3.58)."""
+    p = params("scale_variants.txt")
+    rng = np.random.default_rng(22)
+    x = (rng.standard_t(3, (24, 32 * 4)) * np.exp(rng.uniform(-6, 6, (24, 1)))).astype(np.float32)
+    codes, scales = oracle.quantize(x, scale_mode="round_up")
+    c = oracle.unpack_nibbles(codes)
+    sc = np.repeat(oracle.e8m0_decode(scales), 32, axis=1)
+    for r in range(x.shape[0]):
+        for k in range(x.shape[1]):
+            v = abs(float(x[r, k])) / float(sc[r, k])
+            assert v <= 6.0
+            assert c[r, k] & 7 == _nearest_code_bruteforce(v), (r, k, v)
+            assert (c[r, k] >> 3) == int(np.signbit(x[r, k]))
+    worst = np.zeros((1, 32), dtype=np.float32)
+    worst[0, :] = np.linspace(-1, 1, 32, dtype=np.float32) * np.nextafter(np.float32(6 * 2.0 ** 3),
+                                                                           np.float32(np.inf))
+    wc, ws = oracle.quantize(worst, scale_mode="round_up")
+    used = set(np.abs(oracle.dequantize(wc, ws)[0] / oracle.e8m0_decode(ws[0, 0])).tolist())
+    unused = [float(t) for t in p["round_up_worst_unused_magnitudes"].split()]
+    assert max(used) == 3.0 and not (set(unused) & used)
+    assert abs(math.log2(6 / 0.5) - float(p["fp4_binades"])) < 0.01
+    assert abs(math.log2(max(used) / 0.5) - float(p["round_up_worst_binades"])) < 0.01
+
+
+def test_prescale_keeps_reference_scale_and_nothing_clips():
+    """prescale_3_4: the scale is the reference rule's (largest power of two
+    not above amax, over 4), the elements are 3/4 of the inputs, so the scaled
+    maximum lies in [3, 6) and no element clips (the table row for Tseng, Yu,
+    Park in "MXFP4", AI Wiki, §Training with MXFP4); codes are the
+    brute-force nearest grid point of fl32(0.75 x) / X."""
+    p = params("scale_variants.txt")
+    f = np.float32(p["prescale_factor"])
+    rng = np.random.default_rng(23)
+    x = (rng.standard_t(3, (24, 32 * 4)) * np.exp(rng.uniform(-6, 6, (24, 1)))).astype(np.float32)
+    codes, scales = oracle.quantize(x, scale_mode="prescale_3_4")
+    c = oracle.unpack_nibbles(codes)
+    for r in range(x.shape[0]):
+        for b in range(4):
+            blk = x[r, b * 32:(b + 1) * 32]
+            X = 2.0 ** math.floor(math.log2(float(np.abs(blk).max()))) / 4
+            assert float(oracle.e8m0_decode(scales[r, b])) == X
+            v = np.abs((f * blk).astype(np.float32)).astype(np.float64) / X
+            assert 3.0 <= v.max() < 6.0
+            for k in range(32):
+                assert c[r, b * 32 + k] & 7 == _nearest_code_bruteforce(v[k])
+
+
+def test_clipped_fraction_is_zero_under_both_variants():
+    """The reference rule clips a few percent of entries into the (6, 8) band
+    ("MXFP4", AI Wiki, §Clipping); both variants exist to clip none."""
+    p = params("clipping_example.txt")
+    lo = float(p["clip_band_low"])
+    f = float(params("scale_variants.txt")["prescale_factor"])
+    rng = np.random.default_rng(24)
+    x = rng.standard_t(3, (256, 1024)).astype(np.float32)
+    for mode, mult in (("round_up", 1.0), ("prescale_3_4", f)):
+        codes, scales = oracle.quantize(x, scale_mode=mode)
+        sc = np.repeat(oracle.e8m0_decode(scales), 32, axis=1)
+        assert np.mean(np.abs(x.astype(np.float64)) * mult / sc > lo) == 0.0
+
+
+@pytest.mark.parametrize("mode,mult", [("round_up", 1.0), ("prescale_3_4", 0.75)])
+def test_sr_unbiased_under_variants_where_floor_is_biased(mode, mult):
+    """Nothing saturates under either variant, so stochastic rounding is
+    unbiased for every element, the clipped maximum included: the mean over
+    2048 seeds of the decoded block is mult * x within 5 standard errors
+    (binomial variance <= step^2/4).  The reference rule loses the same
+    property on the clipped element (7.5 -> always 6)."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :] = np.linspace(-7.5, 7.5, 32, dtype=np.float32)
+    n = 2048
+    acc = np.zeros(32)
+    for seed in range(n):
+        c, s = oracle.quantize(x, rounding="sr", seed=seed, offset=3, scale_mode=mode)
+        acc += oracle.dequantize(c, s)[0]
+    mean = acc / n
+    target = (np.float32(mult) * x[0]).astype(np.float64)
+    X = float(oracle.e8m0_decode(s[0, 0]))
+    se = 2.0 * X / 2 / math.sqrt(n)
+    assert np.all(np.abs(mean - target) <= 5 * se + 1e-12)
+    cf, sf = oracle.quantize(x, rounding="sr", seed=0, offset=3)
+    assert oracle.dequantize(cf, sf)[0, -1] == 6.0
+
+
+def test_gather_passes_scale_mode():
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal((10, 64)).astype(np.float32)
+    rows = np.array([9, 2, 2, 0])
+    for mode in ("round_up", "prescale_3_4"):
+        gc, gs = oracle.quantize_gather(x, rows, scale_mode=mode)
+        fc, fs = oracle.quantize(x[rows], scale_mode=mode)
+        assert np.array_equal(gc, fc) and np.array_equal(gs, fs)
+    with pytest.raises(ValueError):
+        oracle.quantize(x, scale_mode="ceil")
