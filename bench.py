@@ -17,7 +17,10 @@ input (shapes of the GPT-OSS-20B-sized workloads):
 `value` is the MXFP4 GEMM throughput of the whole step (dense + wgrad + MoE
 GEMM flops over the step time, quantizers included); per-kernel times, GB/s
 and TFLOP/s are reported alongside, and `roofline` covers the dominant kernel.
-Prints one JSON line.
+`next_rows` times, outside the step, the dgrad product that reuses the forward
+weight: the exact transpose of W quantized along dim 0 in 32x32 tiles, dY
+16384 x 5760 quantized along its last dim (stochastic rounding), and the GEMM
+-> bf16 16384 x 2880.  Prints one JSON line.
 """
 import argparse
 import hashlib
@@ -104,6 +107,16 @@ class Workload:
         self.w_dw = torch.empty((2880, 2880), dtype=torch.float32, device=dev)
         self.m_qa = mx.empty_mx(65536, 2880, device=dev)
         self.m_y = torch.empty((65536, 5760), dtype=torch.bfloat16, device=dev)
+        # dgrad (reported beside the step, not part of it): dY [16384, 5760] and
+        # the forward weight quantized once along dim 0 in 32x32 tiles (RNE, no
+        # transform), transposed into the [2880, 5760] operand
+        dgy, _ = workloads.dgrad()
+        self.d_dy = dgy.to(dev)
+        self.d_seed = workloads.philox_seed(workloads.CFG_DGRAD)
+        self.d_qw = mx.quantize(self.fw, axis="dim0", block="2d")
+        self.d_qwt = mx.empty_mx(2880, 5760, "2d", device=dev)
+        self.d_qdy = mx.empty_mx(16384, 5760, device=dev)
+        self.d_dx = torch.empty((16384, 2880), dtype=torch.bfloat16, device=dev)
 
     # each entry: (name, callable, kind, algorithmic amount)
     def kernels(self):
@@ -134,6 +147,43 @@ class Workload:
             ("moe_grouped_gemm", lambda: mx.grouped_gemm(self.m_qa, self.m_offsets, self.mb, out=self.m_y),
              "mfma", flop_m),
         ]
+
+
+    def extras(self):
+        """Kernels of the next rows, timed beside the step: the dgrad product
+        that reuses the forward weight through its exact 2-D transpose."""
+        t_bytes = 2 * (2880 * 5760 // 2 + (2880 // 32) * (5760 // 32))
+        return [
+            ("dgrad_transpose_w", lambda: mx.transpose(self.d_qw, out=self.d_qwt), "hbm", t_bytes),
+            ("dgrad_quantize_dy", lambda: mx.quantize(self.d_dy, rounding="sr", seed=self.d_seed, out=self.d_qdy),
+             "hbm", quant_bytes(16384, 5760)),
+            ("dgrad_gemm", lambda: mx.gemm(self.d_qdy, self.d_qwt, out=self.d_dx), "mfma",
+             2 * 16384 * 2880 * 5760),
+        ]
+
+
+def rates(name, kind, amount, avg_ms):
+    if kind == "hbm":
+        rate = amount / (avg_ms * 1e-3) / 1e9
+        return {"us": avg_ms * 1e3, "GB/s": rate, "frac_hbm": rate / HBM_PEAK_GBS, "bytes": amount}
+    rate = amount / (avg_ms * 1e-3) / 1e12
+    return {"us": avg_ms * 1e3, "TFLOP/s": rate, "frac_fp4": rate / FP4_PEAK_TFLOPS, "flop": amount}
+
+
+def time_each(ks, steps):
+    """Average duration (ms) of each kernel over `steps` passes, with HIP events
+    around every launch on the launch stream (torch's current stream)."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ks]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for k, (_, fn, _, _) in enumerate(ks):
+            ev[s][k][0].record()
+            fn()
+            ev[s][k][1].record()
+    torch.cuda.synchronize()
+    return [float(np.mean([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(steps)]))
+            for k in range(len(ks))]
 
 
 def cpu_baseline(w, budget_s=20.0):
@@ -208,17 +258,7 @@ def main():
     # Component pass (untimed for the metric): K steps with HIP events around
     # every kernel on the launch stream (torch's current stream), for the
     # per-kernel durations reported under "components".
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ks]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        for k, (_, fn, _, _) in enumerate(ks):
-            ev[s][k][0].record()
-            fn()
-            ev[s][k][1].record()
-    torch.cuda.synchronize()
-    comp_ms = [float(np.mean([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)]))
-               for k in range(len(ks))]
+    comp_ms = time_each(ks, args.steps)
     dom_k = int(np.argmax(comp_ms))
 
     # Timed region: K steps of the whole path, with HIP events only around the
@@ -244,17 +284,14 @@ def main():
     ms_step = total_ms / args.steps
     comp_ms[dom_k] = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
 
-    comps = {}
-    for k, (name, _, kind, amount) in enumerate(ks):
-        avg_ms = comp_ms[k]
-        if kind == "hbm":
-            rate = amount / (avg_ms * 1e-3) / 1e9
-            comps[name] = {"us": avg_ms * 1e3, "GB/s": rate, "frac_hbm": rate / HBM_PEAK_GBS,
-                           "bytes": amount}
-        else:
-            rate = amount / (avg_ms * 1e-3) / 1e12
-            comps[name] = {"us": avg_ms * 1e3, "TFLOP/s": rate, "frac_fp4": rate / FP4_PEAK_TFLOPS,
-                           "flop": amount}
+    comps = {name: rates(name, kind, amount, comp_ms[k]) for k, (name, _, kind, amount) in enumerate(ks)}
+
+    # Next-row kernels, after the timed region (not part of the step or of value).
+    xs = w.extras()
+    for _, fn, _, _ in xs:
+        fn()
+    x_ms = time_each(xs, args.steps)
+    extra = {name: rates(name, kind, amount, x_ms[k]) for k, (name, _, kind, amount) in enumerate(xs)}
 
     gemm_flop = sum(a for _, _, kind, a in ks if kind == "mfma")
     value = gemm_flop / (ms_step * 1e-3) / 1e12
@@ -297,6 +334,7 @@ def main():
                    "parallelism": "single GPU"},
         "quantize_GBps_aggregate": quant_bytes_total / (quant_us * 1e-6) / 1e9,
         "components": comps,
+        "next_rows": extra,
         "roofline": roof,
         "kernel_source_hash": src_hash,
     }

@@ -182,6 +182,27 @@ mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_s
                         void* dst, int32_t dst_dtype, int64_t ld_dst, void* stream);
 
 /*
+ * mx_transpose — the exact transpose of an operand quantized with 2-D (32x32)
+ * blocks: out[c, r] = in[r, c] code for code, and the scale of out's tile
+ * (c/32, r/32) is the scale of in's tile (r/32, c/32).  A 32x32 tile shares
+ * one scale in either orientation, so nothing is re-rounded and the result is
+ * bit-exact whatever rounding produced the input: one 2-D quantization of a
+ * weight serves the forward product and, transposed, the data-gradient
+ * product (dX = dY W needs W blocked along the other axis), the reason for 2-D
+ * weight blocks in the hybrid 1D/2D recipe ("Training an MoE LLM in MXFP4:
+ * How We Closed the Gap to BF16", summary).  A transform applied along the
+ * input's K stays along the output's rows.
+ *
+ *   in    host struct of device buffers; block must be MX_BLOCK_2D ([R, C],
+ *         R and C multiples of 32).
+ *   out   host struct of device buffers; block MX_BLOCK_2D, rows == in->K and
+ *         K == in->rows; must not overlap in.
+ * 1-D operands return MX_ERR_UNSUPPORTED (their blocks run along K only and
+ * cannot be transposed without re-quantizing).  Empty operands are a no-op.
+ */
+mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream);
+
+/*
  * mx_gemm — C[m, n] = sum_k A[m, k] * B[n, k] for MXFP4 operands A [M, K] and
  * B [N, K] (both K-major), per "MXFP4", AI Wiki, §Conversion rules: each block
  * pair contributes X(A) X(B) sum_i P_i(A) P_i(B) and a long dot product is the

@@ -8,6 +8,7 @@ missing, every call raises: there is no fallback path.
 
     q = quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None)
     y = dequantize(q, torch.float32)
+    qt = transpose(q2d)                                 # exact, 2-D blocks only
     c = gemm(qa, qb, torch.bfloat16)                    # C = A * B^T
     c = grouped_gemm(qa, offsets, qb_stacked, torch.bfloat16)
 """
@@ -28,8 +29,8 @@ _ROUND = {"rne": 0, "sr": 1}
 _SCALE = {"floor": 0, "round_up": 1, "prescale_3_4": 2}
 _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
-EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
-            "mx_grouped_gemm", "mx_last_error", "mx_version")
+EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_transpose", "mx_gemm",
+            "mx_gemm_workspace_size", "mx_grouped_gemm", "mx_last_error", "mx_version")
 
 
 class MxTensorC(ctypes.Structure):
@@ -69,11 +70,12 @@ def load_library(path=LIB_PATH):
     lib.mx_quantize.argtypes = [P, I32, I64, I64, I64, ctypes.POINTER(QuantCfgC), PT, P]
     lib.mx_quantize_gather.argtypes = [P, I32, I64, I64, I64, P, I64, ctypes.POINTER(QuantCfgC), PT, P]
     lib.mx_dequantize.argtypes = [PT, I32, U32, P, I32, I64, P]
+    lib.mx_transpose.argtypes = [PT, PT, P]
     lib.mx_gemm.argtypes = [PT, PT, P, I32, I64, P, ctypes.c_size_t, P]
     lib.mx_gemm_workspace_size.argtypes = [I64, I64, I64]
     lib.mx_gemm_workspace_size.restype = ctypes.c_size_t
     lib.mx_grouped_gemm.argtypes = [PT, P, I32, PT, I64, I64, P, I32, I64, P]
-    for f in ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_gemm", "mx_grouped_gemm"):
+    for f in ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_transpose", "mx_gemm", "mx_grouped_gemm"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mx_last_error.restype = ctypes.c_char_p
     lib.mx_last_error.argtypes = []
@@ -192,6 +194,17 @@ def dequantize(q, dtype=torch.float32, inverse_rht_mask=None, out=None):
     _check(lib.mx_dequantize(ctypes.byref(qt), int(inverse_rht_mask is not None),
                              (inverse_rht_mask or 0) & 0xFFFFFFFF, _ptr(out), _DTYPE[out.dtype],
                              out.stride(0), _stream(out)))
+    return out
+
+
+def transpose(q, out=None):
+    """Exact transpose of an operand with 2-D (32x32) blocks: [R, C] -> [C, R]
+    (see mx_transpose)."""
+    lib = load_library()
+    if out is None:
+        out = empty_mx(q.K, q.rows, "2d", device=q.codes.device)
+    it, ot = q.c_struct(), out.c_struct()
+    _check(lib.mx_transpose(ctypes.byref(it), ctypes.byref(ot), _stream(q.codes)))
     return out
 
 

@@ -26,7 +26,7 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "gemm.hip"]
+SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "transpose.hip", "gemm.hip"]
 
 
 def _run(cmd):

@@ -209,6 +209,34 @@ mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_s
   return hip_status(mx::launch_dequantize(a, static_cast<hipStream_t>(stream)), "mx_dequantize");
 }
 
+mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream) {
+  g_err[0] = '\0';
+  mx_status st = check_tensor(in, "mx_transpose: in");
+  if (st != MX_OK) return st;
+  st = check_tensor(out, "mx_transpose: out");
+  if (st != MX_OK) return st;
+  if (in->block != MX_BLOCK_2D || out->block != MX_BLOCK_2D)
+    return fail(MX_ERR_UNSUPPORTED, "mx_transpose: only operands with 2-D (32x32) blocks transpose exactly");
+  if (out->rows != in->K || out->K != in->rows)
+    return fail(MX_ERR_INVALID_ARG, "mx_transpose: out is [%lld, %lld], expected [%lld, %lld]", (long long)out->rows,
+                (long long)out->K, (long long)in->K, (long long)in->rows);
+  if (in->rows == 0 || in->K == 0) return MX_OK;
+  if ((in->rows + 127) / 128 > 65535)
+    return fail(MX_ERR_UNSUPPORTED, "mx_transpose: at most 65535*128 input rows");
+  mx::TransposeArgs a{};
+  a.in_codes = in->codes;
+  a.in_scales = in->scales;
+  a.R = in->rows;
+  a.C = in->K;
+  a.ld_in = in->ld_codes;
+  a.ld_sin = in->ld_scales;
+  a.out_codes = out->codes;
+  a.out_scales = out->scales;
+  a.ld_out = out->ld_codes;
+  a.ld_sout = out->ld_scales;
+  return hip_status(mx::launch_transpose(a, static_cast<hipStream_t>(stream)), "mx_transpose");
+}
+
 size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
   (void)M;
   (void)N;

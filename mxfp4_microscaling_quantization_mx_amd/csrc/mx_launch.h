@@ -66,7 +66,18 @@ struct GroupedGemmArgs {
   bool out_bf16;
 };
 
+struct TransposeArgs {
+  const uint8_t* in_codes;
+  const uint8_t* in_scales;
+  int64_t R, C;               // input [R, C] elements, both multiples of 32
+  int64_t ld_in, ld_sin;
+  uint8_t* out_codes;
+  uint8_t* out_scales;
+  int64_t ld_out, ld_sout;
+};
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st);

@@ -35,6 +35,8 @@ from .rht import rht_forward_f32, rht_inverse_f32, hadamard32_f64
 from .quantize import (
     quantize,
     quantize_gather,
+    transpose_2d,
+    round_up_exponent,
     dequantize,
     shared_exponent,
     round_e2m1,
@@ -55,6 +57,8 @@ __all__ = [
     "hadamard32_f64",
     "quantize",
     "quantize_gather",
+    "transpose_2d",
+    "round_up_exponent",
     "dequantize",
     "shared_exponent",
     "round_e2m1",

@@ -101,6 +101,20 @@ def test_quantize_gather_rejects_bad_arguments(lib):
                                   None) == mx.MX_OK
 
 
+def test_transpose_rejects_bad_arguments(lib):
+    a = _tensor(64, 96, block=1)
+    out = _tensor(96, 64, block=1)
+    for bad_in, bad_out in ((_tensor(64, 96), out), (a, _tensor(96, 64))):
+        st = lib.mx_transpose(ctypes.byref(bad_in), ctypes.byref(bad_out), None)
+        assert st == mx.MX_ERR_UNSUPPORTED and b"2-D" in lib.mx_last_error()
+    st = lib.mx_transpose(ctypes.byref(a), ctypes.byref(_tensor(64, 96, block=1)), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"expected" in lib.mx_last_error()
+    st = lib.mx_transpose(ctypes.byref(a), ctypes.byref(_tensor(96, 64, codes=8, block=1)), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"aligned" in lib.mx_last_error()
+    assert lib.mx_transpose(ctypes.byref(_tensor(0, 64, block=1)), ctypes.byref(_tensor(64, 0, block=1)),
+                            None) == mx.MX_OK
+
+
 def test_gemm_rejects_bad_arguments(lib):
     a = _tensor(32, 64)
     b = _tensor(32, 96)

@@ -1,0 +1,116 @@
+"""GPU parity of mx_transpose (2-D block operands) and of the data-gradient
+product that reuses a transposed weight.
+
+mx_transpose is byte work: codes and scales must equal the oracle's
+transpose_2d exactly.  Inputs are the oracle's own quantized operands (or
+random bytes), uploaded to the GPU with padded row strides.  The dgrad case
+runs the GPU path end to end (quantize W along dim 0 in 32x32 tiles, transpose
+it, quantize dY, GEMM) and compares sampled outputs with the oracle's float64
+reference on the same sampled rows and weight tiles.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_microscaling_quantization_mx_amd as mx
+import oracle
+import workloads
+from gpu_util import banner, check_gemm, codes_equal, host, need_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _upload_2d(codes, scales, code_pad=128, scale_pad=16, fill=0xA5):
+    """Oracle bytes into padded device buffers (the padding holds `fill`, so
+    a kernel that reads or writes past a row shows up)."""
+    rows, cb = codes.shape
+    ldc = (cb + code_pad - 1) // code_pad * code_pad
+    cbuf = torch.full((rows, ldc), fill, dtype=torch.uint8, device="cuda")
+    cbuf[:, :cb] = to_dev(codes)
+    srows, sb = scales.shape
+    lds = (sb + scale_pad - 1) // scale_pad * scale_pad
+    sbuf = torch.full((srows, lds), fill, dtype=torch.uint8, device="cuda")
+    sbuf[:, :sb] = to_dev(scales)
+    return mx.MXTensor(cbuf[:, :cb], sbuf[:, :sb], rows, cb * 2, "2d")
+
+
+def _full_rows(t):
+    """The whole padded rows behind a row-sliced 2-D view."""
+    return t.as_strided((t.shape[0], t.stride(0)), (t.stride(0), 1))
+
+
+def _out_2d(rows, K, fill=0x5A):
+    q = mx.empty_mx(rows, K, "2d")
+    _full_rows(q.codes).fill_(fill)
+    _full_rows(q.scales).fill_(fill)
+    return q
+
+
+@pytest.mark.parametrize("R,C", [(32, 32), (96, 160), (160, 96), (128, 128), (288, 416), (4128, 2080)])
+def test_transpose_random_bytes(R, C):
+    """Every nibble and scale byte lands in its transposed place: random bytes,
+    shapes that are multiples of 32 but not of the 128 x 128 tile, padded row
+    strides on both sides (the padding must stay untouched)."""
+    need_gpu()
+    rng = np.random.default_rng(R * 7919 + C)
+    codes = rng.integers(0, 256, (R, C // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (R // 32, C // 32), dtype=np.uint8)
+    banner(f"transpose random R={R} C={C}")
+    q = _upload_2d(codes, scales)
+    out = _out_2d(C, R)
+    mx.transpose(q, out=out)
+    oc, os_ = oracle.transpose_2d(codes, scales)
+    codes_equal(host(out.codes), oc, "codes")
+    codes_equal(host(out.scales), os_, "scales")
+    # the row padding of the output is untouched
+    assert np.all(host(_full_rows(out.codes))[:, R // 2:] == 0x5A)
+    assert np.all(host(_full_rows(out.scales))[:, R // 32:] == 0x5A)
+
+
+@pytest.mark.parametrize("rounding,rht", [("rne", False), ("sr", True)])
+def test_transpose_of_quantized_weight(rounding, rht):
+    """A quantized operand (the oracle's, SR and transform included: the
+    transpose re-rounds nothing) transposes to the oracle's transpose; with RNE
+    and no transform that is also W quantized along its last dim."""
+    need_gpu()
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((320, 192)) * 0.02).astype(np.float32)
+    kw = dict(rounding=rounding, rht_mask=0x0F0F1234 if rht else None, seed=9)
+    qc, qs = oracle.quantize(w, axis="dim0", block="2d", **kw)         # [192, 320]
+    banner(f"transpose quantized weight {rounding} rht={rht}")
+    t = mx.transpose(_upload_2d(qc, qs))
+    oc, os_ = oracle.transpose_2d(qc, qs)
+    codes_equal(host(t.codes), oc, "codes")
+    codes_equal(host(t.scales), os_, "scales")
+    if rounding == "rne" and not rht:
+        lc, ls = oracle.quantize(w, block="2d")
+        codes_equal(host(t.codes), lc, "codes vs last-dim quantization")
+        codes_equal(host(t.scales), ls, "scales vs last-dim quantization")
+
+
+def test_dgrad_full_size():
+    """Data gradient of the dense layer, reusing the forward weight: W 2880x5760
+    bf16 N(0,0.02) quantized once along dim 0 in 32x32 tiles (the forward
+    operand, RNE, no transform), transposed on the GPU into the [2880, 5760]
+    operand blocked along 5760; dY 16384x5760 bf16 N(0,1e-3) quantized along its
+    last dim with stochastic rounding; dX = dYq Wq^T bf16 16384x2880, checked
+    on 48 sampled rows x 2 weight tiles against the oracle."""
+    need_gpu()
+    dy, w = workloads.dgrad()
+    seed = workloads.philox_seed(workloads.CFG_DGRAD)
+    banner("dgrad full size")
+    qw = mx.quantize(w.cuda(), axis="dim0", block="2d")
+    qwt = mx.transpose(qw)
+    qd = mx.quantize(dy.cuda(), rounding="sr", seed=seed)
+    dx = mx.gemm(qd, qwt, torch.bfloat16)
+    rng = np.random.default_rng(6)
+    rows = np.sort(rng.choice(16384, 48, replace=False))
+    tiles = np.sort(rng.choice(2880 // 32, 2, replace=False))
+    cols = (tiles[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    dyn, wn = dy.float().numpy(), w.float().numpy()
+    odc, ods = oracle.quantize(dyn[rows], rounding="sr", seed=seed, row_index=rows, K_total=5760)
+    owc, ows = oracle.quantize(wn[cols], axis="dim0", block="2d")      # the sampled tiles of W^T
+    owc, ows = oracle.transpose_2d(owc, ows)                            # [64, 5760]
+    ref, bound = oracle.gemm_ref(odc, ods, owc, ows, "1d", "2d")
+    got = host(dx.float())[np.ix_(rows, cols)]
+    check_gemm(got, ref, bound, bf16=True, what="dgrad")

@@ -458,3 +458,26 @@ def test_gather_passes_scale_mode():
         assert np.array_equal(gc, fc) and np.array_equal(gs, fs)
     with pytest.raises(ValueError):
         oracle.quantize(x, scale_mode="ceil")
+
+
+# ---------------------------------------------------------------- 2-D transpose
+def test_transpose_2d_is_quantizing_along_the_other_axis():
+    """transpose_2d of W quantized along its last dim in 32x32 tiles equals W
+    quantized along dim 0 in 32x32 tiles (RNE, no transform): a tile's scale is
+    the same in both orientations and each element rounds alone.  Decoding
+    commutes with it, twice is the identity, and 1-D layouts are refused."""
+    rng = np.random.default_rng(41)
+    for R, C in ((32, 32), (96, 160), (160, 64)):
+        w = (rng.standard_t(3, (R, C)) * np.exp(rng.uniform(-4, 4, (R // 32, 1)).repeat(32, 0)))
+        w = w.astype(np.float32)
+        lc, ls = oracle.quantize(w, block="2d")
+        dc, ds = oracle.quantize(w, axis="dim0", block="2d")
+        tc, ts = oracle.transpose_2d(lc, ls)
+        assert tc.shape == (C, R // 2) and ts.shape == (C // 32, R // 32)
+        assert np.array_equal(tc, dc) and np.array_equal(ts, ds)
+        assert np.array_equal(oracle.dequantize(tc, ts, "2d"), oracle.dequantize(lc, ls, "2d").T)
+        bc, bs = oracle.transpose_2d(tc, ts)
+        assert np.array_equal(bc, lc) and np.array_equal(bs, ls)
+    c1, s1 = oracle.quantize(np.ones((32, 64), np.float32))
+    with pytest.raises(ValueError):
+        oracle.transpose_2d(c1, s1)

@@ -6,8 +6,8 @@ random inputs: tensors, the Hadamard sign mask and the stochastic-rounding
 seed (random numbers the method draws are passed in as inputs).
 
 Every stream is ``np.random.default_rng(SeedSequence([cfg_id, stream_id, ...]))``
-with cfg_id 1..5 for the five workloads (tiny, quantize-only, dense fprop,
-wgrad, MoE grouped) and stream ids 0 = A/X, 1 = B/W/dY, 2 = outlier
+with cfg_id 1..6 for the workloads (tiny, quantize-only, dense fprop,
+wgrad, MoE grouped, dgrad) and stream ids 0 = A/X, 1 = B/W/dY, 2 = outlier
 positions, 3 = Hadamard sign mask, 4 = Philox seed, 5 = MoE routing.
 bfloat16 tensors are made from float32 by round-to-nearest-even (torch's CPU
 cast), so every consumer sees identical bits.
@@ -20,7 +20,7 @@ weights or datasets are used.
 import numpy as np
 import torch
 
-CFG_TINY, CFG_QUANT, CFG_FPROP, CFG_WGRAD, CFG_MOE = 1, 2, 3, 4, 5
+CFG_TINY, CFG_QUANT, CFG_FPROP, CFG_WGRAD, CFG_MOE, CFG_DGRAD = 1, 2, 3, 4, 5, 6
 S_A, S_B, S_OUTLIER, S_MASK, S_SEED, S_ROUTE = 0, 1, 2, 3, 4, 5
 
 
@@ -77,6 +77,14 @@ def wgrad(tokens=16384, k=2880):
     dy = to_bf16(normal_f32(CFG_WGRAD, S_B, (tokens, k), 1e-3))
     x = to_bf16(normal_f32(CFG_WGRAD, S_A, (tokens, k)))
     return dy, x
+
+
+def dgrad(tokens=16384, k=2880, n=5760):
+    """Dgrad of the dense layer: dY [tokens, n] bf16 N(0, 1e-3) and the fprop
+    weight W [k, n] (the same tensor as fprop()'s)."""
+    dy = to_bf16(normal_f32(CFG_DGRAD, S_B, (tokens, n), 1e-3))
+    w = to_bf16(normal_f32(CFG_FPROP, S_B, (k, n), 0.02))
+    return dy, w
 
 
 def moe_routing(tokens=16384, experts=32, topk=4, s=1.1, seed=0):
