@@ -44,6 +44,7 @@ from .quantize import (
     unpack_nibbles,
 )
 from .gemm import gemm_ref, grouped_gemm_ref, block_dot_exact
+from . import elements
 
 __all__ = [
     "E2M1_GRID",

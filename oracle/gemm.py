@@ -20,11 +20,12 @@ from fractions import Fraction
 
 import numpy as np
 
+from . import elements
 from .formats import BLOCK, e2m1_decode, e8m0_decode
 from .quantize import unpack_nibbles
 
 
-def _decode_f64(codes, scales, block, rows=None):
+def _decode_f64(codes, scales, block, rows=None, elem="e2m1"):
     """Dequantize (optionally only some rows) to float64, no RHT."""
     codes = np.asarray(codes)
     scales = np.asarray(scales)
@@ -37,19 +38,28 @@ def _decode_f64(codes, scales, block, rows=None):
         sc = e8m0_decode(scales)
         if block == "2d":
             sc = np.repeat(sc, BLOCK, axis=0)
-    vals = e2m1_decode(unpack_nibbles(codes))
-    return vals * np.repeat(sc, BLOCK, axis=1)
+    if elem == "e2m1":
+        vals = e2m1_decode(unpack_nibbles(codes))
+    else:
+        K = codes.shape[1] * 8 // elements.elem_bits(elem)
+        vals = elements.decode(elements.unpack(codes, elem, K), elem)
+    with np.errstate(invalid="ignore"):
+        return vals * np.repeat(sc, BLOCK, axis=1)
 
 
 def gemm_ref(a_codes, a_scales, b_codes, b_scales, a_block="1d", b_block="1d",
-             rows=None, cols=None):
-    """Reference C = A * B^T for K-major MXFP4 operands A [M, K], B [N, K].
+             rows=None, cols=None, a_elem="e2m1", b_elem="e2m1"):
+    """Reference C = A * B^T for K-major MX operands A [M, K], B [N, K]
+    (element types a_elem, b_elem; MXFP4 by default).
 
     rows/cols optionally restrict the output to a sample (index arrays).
-    Returns (ref, S) as float64 arrays [len(rows), len(cols)].
+    Returns (ref, S) as float64 arrays [len(rows), len(cols)].  A NaN or
+    infinite element, like a NaN scale, makes its outputs NaN.
     """
-    a = _decode_f64(a_codes, a_scales, a_block, rows)
-    b = _decode_f64(b_codes, b_scales, b_block, cols)
+    a = _decode_f64(a_codes, a_scales, a_block, rows, a_elem)
+    b = _decode_f64(b_codes, b_scales, b_block, cols, b_elem)
+    a = np.where(np.isinf(a), np.nan, a)
+    b = np.where(np.isinf(b), np.nan, b)
     nan_a = np.isnan(a).any(axis=1)
     nan_b = np.isnan(b).any(axis=1)
     a0 = np.where(np.isnan(a), 0.0, a)

@@ -53,31 +53,34 @@ NaN/Inf blocks use the NaN scale; SR saturates deterministically above 6.
 
 import numpy as np
 
+from . import elements
 from .formats import BLOCK, E2M1_GRID, E8M0_BIAS, E8M0_NAN, e2m1_decode, e8m0_decode
 from .philox import sr_bits16
 from .rht import rht_forward_f32, rht_inverse_f32
 
 
-def shared_exponent(amax):
-    """e = clamp(floor(log2 amax) - 2, -127, 127) for float32 amax >= 0 (finite);
-    amax == 0 maps to -127.  floor(log2) comes from frexp, which is exact for
-    normal and subnormal float32 inputs."""
+def shared_exponent(amax, emax=2):
+    """e = clamp(floor(log2 amax) - emax, -127, 127) for float32 amax >= 0
+    (finite); amax == 0 maps to -127.  emax is the exponent of the largest
+    power of two of the element type (2 for E2M1).  floor(log2) comes from
+    frexp, which is exact for normal and subnormal float32 inputs."""
     a = np.asarray(amax, dtype=np.float32)
     _, ex = np.frexp(a)                      # a = m * 2^ex, m in [0.5, 1)
-    e = (ex.astype(np.int64) - 1) - 2
+    e = (ex.astype(np.int64) - 1) - emax
     e = np.clip(e, -127, 127)
     return np.where(a == 0, -127, e)
 
 
-def round_up_exponent(amax):
-    """The smallest integer e with amax <= 6 * 2^e, clamped to [-127, 127], for
-    finite float32 amax >= 0 (amax == 0 maps to -127).  The candidate
-    floor(log2 amax) - 2 from frexp is tried first and raised by one when
-    6 * 2^e still falls short; both sides are exact in float64."""
+def round_up_exponent(amax, top=6.0, emax=2):
+    """The smallest integer e with amax <= top * 2^e (top: the element type's
+    largest normal, 6 for E2M1), clamped to [-127, 127], for finite float32
+    amax >= 0 (amax == 0 maps to -127).  The candidate floor(log2 amax) - emax
+    from frexp is tried first and raised by one when top * 2^e still falls
+    short; both sides are exact in float64."""
     a = np.asarray(amax, dtype=np.float32).astype(np.float64)
     _, ex = np.frexp(a)
-    e = ex.astype(np.int64) - 3
-    e = np.where(a > np.ldexp(6.0, e.astype(np.int32)), e + 1, e)
+    e = ex.astype(np.int64) - 1 - emax
+    e = np.where(a > np.ldexp(top, e.astype(np.int32)), e + 1, e)
     e = np.clip(e, -127, 127)
     return np.where(a == 0, -127, e)
 
@@ -123,7 +126,7 @@ def unpack_nibbles(packed):
 
 
 def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
-             seed=0, offset=0, row_index=None, K_total=None, scale_mode="floor"):
+             seed=0, offset=0, row_index=None, K_total=None, scale_mode="floor", elem="e2m1"):
     """Quantize a 2-D float array to MXFP4.
 
     axis="last": blocks along the last dim, output [R, C] with K = C.
@@ -138,6 +141,10 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
     output-row numbers and the global K used in the stochastic-rounding element
     index p = row * K + k.  They change nothing else.
     scale_mode: "floor" (the reference rule), "round_up" or "prescale_3_4".
+    elem: "e2m1" (MXFP4, two codes per byte) or another MX element type of
+    ``oracle.elements`` ("e4m3", "e5m2": one byte per element; "e2m3",
+    "e3m2": 6-bit codes packed little-endian); the scale takes that type's
+    largest power of two and the elements its grid (§Conversion rules).
     """
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
@@ -147,6 +154,8 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
     elif axis != "last":
         raise ValueError(f"unknown axis {axis!r}")
     rows, K = x.shape
+    if elem != "e2m1" and elem not in elements.ELEMS:
+        raise ValueError(f"unknown element type {elem!r}")
     if scale_mode not in SCALE_MODES:
         raise ValueError(f"unknown scale_mode {scale_mode!r}")
     if K % BLOCK:
@@ -171,7 +180,12 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
         else:
             raise ValueError(f"unknown block {block!r}")
 
-        e = round_up_exponent(amax) if scale_mode == "round_up" else shared_exponent(amax)
+        if elem == "e2m1":
+            e = round_up_exponent(amax) if scale_mode == "round_up" else shared_exponent(amax)
+        else:
+            em = elements.emax(elem)
+            e = (round_up_exponent(amax, elements.max_normal(elem), em) if scale_mode == "round_up"
+                 else shared_exponent(amax, em))
         scales = np.where(bad, E8M0_NAN, e + E8M0_BIAS).astype(np.uint8)
 
         if block == "2d":                       # per-element view of the tile scale
@@ -191,8 +205,10 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
             p = (ridx.astype(np.uint64)[:, None] * np.uint64(kt)
                  + np.arange(K, dtype=np.uint64)[None, :])
             r = sr_bits16(p, seed, offset).reshape(rows, nkb, BLOCK)
-        codes = round_e2m1(v, rounding, r)
+        codes = round_e2m1(v, rounding, r) if elem == "e2m1" else elements.round_elem(v, elem, rounding, r)
         codes = np.where(bad_el[..., None], 0, codes)
+    if elem != "e2m1":
+        return elements.pack(codes.reshape(rows, K), elem), scales
     return pack_nibbles(codes.reshape(rows, K)), scales
 
 
@@ -236,10 +252,15 @@ def transpose_2d(codes, scales):
     return pack_nibbles(np.ascontiguousarray(c.T)), np.ascontiguousarray(s.T)
 
 
-def dequantize(codes, scales, block="1d", inverse_rht_mask=None, dtype=np.float32):
+def dequantize(codes, scales, block="1d", inverse_rht_mask=None, dtype=np.float32, elem="e2m1"):
     """Decode MXFP4: value = E2M1(code) * 2^(scale - 127); scale 0xFF makes the
-    whole block NaN.  Optional inverse RHT (float32, canonical order)."""
-    vals = e2m1_decode(unpack_nibbles(codes))                       # float64 [R, K]
+    whole block NaN.  Optional inverse RHT (float32, canonical order).  Other
+    element types (elem) decode their codes with ``oracle.elements``."""
+    if elem == "e2m1":
+        vals = e2m1_decode(unpack_nibbles(codes))                   # float64 [R, K]
+    else:
+        K = np.asarray(codes).shape[1] * 8 // elements.elem_bits(elem)
+        vals = elements.decode(elements.unpack(codes, elem, K), elem)
     rows, K = vals.shape
     sc = e8m0_decode(scales)
     if block == "2d":

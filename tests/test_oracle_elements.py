@@ -1,0 +1,165 @@
+"""Pins for the oracle's other MX element types (FP8 E4M3/E5M2, FP6 E2M3/E3M2).
+
+  * the page's MX family table (element widths, block size, scale type);
+  * FP8 decoding and round-to-nearest-even against torch's own float8_e4m3fn
+    and float8_e5m2 types (a library implementation of the same OCP formats)
+    over every code and over grid midpoints, ties and random values;
+  * FP6 rounding by brute force over the decoded grid;
+  * the page's scale rule (largest power of two not above amax, divided by the
+    largest power of two the element type represents) on random blocks, and
+    saturation at the largest normal;
+  * the FP6 bit packing round-trips and puts element i at bits 6i.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from golden_io import lines
+from oracle import elements as el
+
+FP8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+def test_family_table_widths():
+    rows = [ln.split() for ln in lines("mx_family.txt")]
+    for fmt, et, bits, block, scale in rows:
+        assert int(block) == 32 and scale == "E8M0"
+        name = et.lower()
+        if name == "e2m1":
+            continue
+        e, m = int(name[1]), int(name[3])
+        assert 1 + e + m == int(bits) == el.elem_bits(name)
+        assert el.block_bits(name) == 32 * int(bits) + 8
+        assert (fmt == "MXFP8") == (int(bits) == 8)
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e5m2"])
+def test_fp8_decode_matches_torch_on_every_code(elem):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(FP8_TORCH[elem]).float().numpy().astype(np.float64)
+    got = el.decode(codes, elem)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def _probe_values(elem):
+    g = el.grid(elem)
+    pts = set(g.tolist())
+    pts.update(((g[:-1] + g[1:]) / 2).tolist())
+    out = set()
+    for p in pts:
+        f = np.float32(p)
+        for d in (-2, -1, 0, 1, 2):
+            v = f
+            for _ in range(abs(d)):
+                v = np.nextafter(v, np.float32(np.inf) if d > 0 else np.float32(0))
+            out.add(float(v))
+    return np.array(sorted(v for v in out if v <= g[-1]), dtype=np.float32)
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e5m2"])
+def test_fp8_rne_matches_torch(elem):
+    """Grid points, midpoints (ties) and +-2 ulps around them, both signs, and
+    random values below the largest normal: the oracle's code equals torch's
+    float32 -> float8 cast (round to nearest even)."""
+    rng = np.random.default_rng(1)
+    top = el.max_normal(elem)
+    v = np.concatenate([_probe_values(elem),
+                        (rng.uniform(-1, 1, 20000) * top).astype(np.float32),
+                        np.exp(rng.uniform(-25, math.log(top), 20000)).astype(np.float32)])
+    v = np.concatenate([v, -v])
+    got = el.round_elem(v, elem, "rne")
+    ref = torch.from_numpy(v).to(FP8_TORCH[elem]).view(torch.uint8).numpy().astype(np.int64)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("elem", ["e2m3", "e3m2"])
+def test_fp6_rne_bruteforce(elem):
+    """Nearest grid value by exhaustive distance, ties to the even code,
+    saturating above the largest normal; the grid's end points are the
+    definitions' closed forms."""
+    g = el.grid(elem)
+    e, m, top = el.ELEMS[elem]
+    bias = (1 << (e - 1)) - 1
+    assert g[-1] == (2 - 2.0 ** -m) * 2.0 ** ((1 << e) - 1 - bias)
+    assert g[1] == 2.0 ** (1 - bias - m)
+    v = np.concatenate([_probe_values(elem), np.float32([g[-1] * 1.01, 1e9])])
+    got = el.round_elem(v, elem, "rne")
+    for x, c in zip(v, got):
+        d = np.abs(g - float(x))
+        best = min(range(len(g)), key=lambda i: (d[i], i % 2))
+        assert c == best, (elem, float(x), c, best)
+    assert np.array_equal(el.round_elem(-v, elem, "rne"), got | (1 << (e + m)))
+
+
+@pytest.mark.parametrize("elem", list(el.ELEMS))
+def test_scale_rule_and_saturation(elem):
+    """X = (largest power of two <= amax) / (largest power of two of the type);
+    every scaled element is at most the largest normal after saturation, and
+    a value just below amax keeps its sign and code magnitude <= largest."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_t(3, (16, 32 * 4)) * np.exp(rng.uniform(-8, 8, (16, 1)))).astype(np.float32)
+    codes, scales = oracle.quantize(x, elem=elem)
+    g = el.grid(elem)
+    p2 = 2.0 ** math.floor(math.log2(g[-1]))        # largest power of two of the type, by brute force
+    assert p2 == 2.0 ** el.emax(elem)
+    for r in range(16):
+        for b in range(4):
+            amax = float(np.abs(x[r, b * 32:(b + 1) * 32]).max())
+            X = 2.0 ** math.floor(math.log2(amax)) / p2
+            assert float(oracle.e8m0_decode(scales[r, b])) == X
+    deq = oracle.dequantize(codes, scales, elem=elem).astype(np.float64)
+    sc = np.repeat(oracle.e8m0_decode(scales), 32, axis=1)
+    assert np.all(np.abs(deq) <= g[-1] * sc)
+    assert np.all(np.sign(deq[deq != 0]) == np.sign(x[deq != 0]))
+
+
+def test_fp6_packing():
+    rng = np.random.default_rng(4)
+    c = rng.integers(0, 64, (3, 64))
+    p = el.pack(c, "e2m3")
+    assert p.shape == (3, 48)
+    assert np.array_equal(el.unpack(p, "e2m3", 64), c)
+    one = np.zeros((1, 32), dtype=np.int64)
+    one[0, 1] = 0x3F                        # element 1 -> bits 6..11
+    q = el.pack(one, "e3m2")[0]
+    assert q[0] == 0xC0 and q[1] == 0x0F and not q[2:].any()
+
+
+@pytest.mark.parametrize("elem", list(el.ELEMS))
+def test_quantize_error_bound(elem):
+    """|x - deq(q(x))| <= half a grid step at |x| (no element of these blocks
+    exceeds the largest normal after scaling: amax/X < 2 * 2^emax, and the
+    clip band above the largest normal is counted separately)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    codes, scales = oracle.quantize(x, elem=elem)
+    deq = oracle.dequantize(codes, scales, elem=elem).astype(np.float64)
+    sc = np.repeat(oracle.e8m0_decode(scales), 32, axis=1)
+    g = el.grid(elem)
+    v = np.abs(x) / sc
+    i = np.clip(np.searchsorted(g, v, side="right") - 1, 0, len(g) - 2)
+    step = g[i + 1] - g[i]
+    err = np.abs(x - deq) / sc
+    clip = v > g[-1]
+    assert np.all(err[~clip] <= step[~clip] / 2 + 1e-12)
+    assert np.allclose(err[clip], v[clip] - g[-1])
+
+
+def test_gemm_ref_mixed_types_bruteforce():
+    """A block dot product of an FP8 row with an FP6 row equals the exact
+    rational sum of the decoded products."""
+    from fractions import Fraction
+    rng = np.random.default_rng(6)
+    a = rng.integers(0, 0x7E, (1, 32)) | (rng.integers(0, 2, (1, 32)) << 7)
+    b = rng.integers(0, 64, (1, 32))
+    ac, bc = el.pack(a, "e4m3"), el.pack(b, "e3m2")
+    ref, _ = oracle.gemm_ref(ac, np.array([[125]], np.uint8), bc, np.array([[130]], np.uint8),
+                             a_elem="e4m3", b_elem="e3m2")
+    exact = sum(Fraction(float(p)) * Fraction(float(q))
+                for p, q in zip(el.decode(a[0], "e4m3"), el.decode(b[0], "e3m2"))) * Fraction(2) ** 1
+    assert ref[0, 0] == float(exact)
