@@ -22,6 +22,17 @@
  *     consecutive elements of a row) or [rows/32, K/32] bytes for 2-D blocks
  *     (32x32 tiles of 32 rows by 32 elements).
  *   136 bits per 1-D block: 4.25 bits per value.
+ *
+ * The other MX v1.0 element types ("MXFP4", AI Wiki, §Place in the MX family:
+ * MXFP8 with FP8 E4M3 or E5M2 elements, MXFP6 with FP6 E2M3 or E3M2, all with
+ * 32-element blocks and an E8M0 scale) are selected per operand by
+ * mx_tensor.elem.  Their codes follow the OCP element definitions (bias
+ * 2^(e-1)-1, subnormals; E4M3 has no Inf and S.1111.111 is NaN, largest
+ * normal 448; E5M2 is IEEE-like, largest normal 57344; FP6 has no Inf/NaN,
+ * largest normals 7.5 (E2M3) and 28 (E3M2)).  Storage is K-major like MXFP4:
+ * FP8 rows are K bytes (byte k = element k); FP6 rows are 3K/4 bytes with
+ * element k at bits 6k .. 6k+5 of the row, little-endian (a block fills 24
+ * bytes); scales are laid out as for MXFP4.
  */
 #ifndef LIBMXFP4_MX_H
 #define LIBMXFP4_MX_H
@@ -49,6 +60,15 @@ typedef enum {
 } mx_axis;
 
 typedef enum { MX_BLOCK_1D = 0, MX_BLOCK_2D = 1 } mx_block;
+
+/* Element type of an MX operand (mx_tensor.elem). */
+typedef enum {
+  MX_ELEM_E2M1 = 0,  /* FP4, MXFP4 (the default)   */
+  MX_ELEM_E4M3 = 1,  /* FP8, MXFP8                 */
+  MX_ELEM_E5M2 = 2,  /* FP8, MXFP8                 */
+  MX_ELEM_E2M3 = 3,  /* FP6, MXFP6                 */
+  MX_ELEM_E3M2 = 4   /* FP6, MXFP6                 */
+} mx_elem;
 
 typedef enum {
   MX_ROUND_RNE = 0,  /* round to nearest, ties to even mantissa bit, saturate at +-6 */
@@ -81,17 +101,17 @@ typedef enum {
  */
 typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_ROUND_UP = 1, MX_SCALE_PRESCALE_3_4 = 2 } mx_scale_mode;
 
-/* One MXFP4 operand, K-major (see the format notes above).  All fields are
+/* One MX operand, K-major (see the format notes above).  All fields are
  * read-only to the library; the buffers are the caller's. */
 typedef struct {
-  uint8_t* codes;     /* device; [rows, K/2] bytes, row stride ld_codes bytes       */
+  uint8_t* codes;     /* device; [rows, K*bits/8] bytes (MXFP4: K/2), row stride ld_codes bytes */
   uint8_t* scales;    /* device; 1-D: [rows, K/32]; 2-D: [rows/32, K/32]; row stride ld_scales bytes */
   int64_t rows;       /* logical rows (M or N of a GEMM)                            */
   int64_t K;          /* logical elements per row, a multiple of 32                  */
-  int64_t ld_codes;   /* bytes between rows of codes, >= K/2                         */
+  int64_t ld_codes;   /* bytes between rows of codes, >= K*bits/8                    */
   int64_t ld_scales;  /* bytes between rows of scales, >= K/32                       */
   int32_t block;      /* mx_block                                                    */
-  int32_t reserved;   /* must be 0                                                   */
+  int32_t elem;       /* mx_elem (0: MXFP4); codes rows hold K * bits / 8 bytes       */
 } mx_tensor;
 
 /* Quantizer settings. */
@@ -107,7 +127,8 @@ typedef struct {
 } mx_quant_cfg;
 
 /*
- * mx_quantize — MXFP4 conversion of a bf16/fp32 tensor.
+ * mx_quantize — MX conversion of a bf16/fp32 tensor (MXFP4 by default; the
+ * element type is out->elem).
  *
  * Follows "MXFP4", AI Wiki, §Conversion rules and §Clipping in the reference
  * algorithm: per block, the shared exponent is floor(log2(amax)) - 2 clamped
@@ -137,6 +158,13 @@ typedef struct {
  *   MX_ERR_UNSUPPORTED, nothing launched): last-dim 1-D at most 2^32 - 256
  *   blocks; last-dim 2-D at most 65535*64 rows; dim-0 at most 65535*128 source
  *   rows and 32 source rows spanning < 4 GiB.
+ *   Other element types (out->elem != MX_ELEM_E2M1): the same steps with that
+ *   type's grid: the shared exponent is floor(log2(amax)) - emax, emax the
+ *   exponent of the type's largest power of two (8 E4M3, 15 E5M2, 2 E2M3,
+ *   4 E3M2, per §Conversion rules), elements round to nearest even (or
+ *   stochastically, the same 16-bit draws) and saturate at the largest
+ *   normal; the round-up rule uses the largest normal in place of 6.  1-D
+ *   blocks only (2-D returns MX_ERR_UNSUPPORTED); ld_codes >= K*bits/8.
  */
 mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
                       const mx_quant_cfg* cfg, const mx_tensor* out, void* stream);
@@ -158,7 +186,8 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
  *            byte 0xFF, codes 0); it is never dereferenced.
  *   cfg      host; axis must be MX_AXIS_LAST and block MX_BLOCK_1D
  *            (else MX_ERR_UNSUPPORTED); the other settings as in mx_quantize.
- *   out      host struct of device buffers: rows = rows_out, K = C, 1-D.
+ *   out      host struct of device buffers: rows = rows_out, K = C, 1-D,
+ *            MXFP4 (other element types return MX_ERR_UNSUPPORTED).
  *   Requires C % 32 == 0; rows_out = 0 or C = 0 is a no-op; at most
  *   2^32 - 256 blocks per call.  Reads only src and rows, writes only out.
  */
@@ -167,9 +196,10 @@ mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, 
                              const mx_tensor* out, void* stream);
 
 /*
- * mx_dequantize — decode an MXFP4 operand: value = E2M1(code) * 2^(scale-127)
+ * mx_dequantize — decode an MX operand: value = element(code) * 2^(scale-127)
  * ("MXFP4", AI Wiki, §Format specification: X times P_i; NaN scale makes the
- * whole block NaN).  With inverse_rht = 1 the 32-point transform is undone per
+ * whole block NaN; any element type: NaN and Inf element codes decode as
+ * such).  With inverse_rht = 1 the 32-point transform is undone per
  * block along K in float32: the stages h = 1,2,4,8,16, the multiply by c, then
  * the sign flips of rht_sign_mask.
  *
@@ -194,7 +224,7 @@ mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_s
  * input's K stays along the output's rows.
  *
  *   in    host struct of device buffers; block must be MX_BLOCK_2D ([R, C],
- *         R and C multiples of 32).
+ *         R and C multiples of 32), MXFP4.
  *   out   host struct of device buffers; block MX_BLOCK_2D, rows == in->K and
  *         K == in->rows; must not overlap in.
  * 1-D operands return MX_ERR_UNSUPPORTED (their blocks run along K only and
@@ -203,13 +233,17 @@ mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_s
 mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream);
 
 /*
- * mx_gemm — C[m, n] = sum_k A[m, k] * B[n, k] for MXFP4 operands A [M, K] and
+ * mx_gemm — C[m, n] = sum_k A[m, k] * B[n, k] for MX operands A [M, K] and
  * B [N, K] (both K-major), per "MXFP4", AI Wiki, §Conversion rules: each block
  * pair contributes X(A) X(B) sum_i P_i(A) P_i(B) and a long dot product is the
  * sum of block dot products, accumulated in float32 (the order of that float32
  * sum is the library's); groups of 32 run along the contraction dimension
  * ("MXFP4", AI Wiki, §Hardware support: scales applied inside the matrix
- * instruction, float32 or bf16 output).  Runs on gfx950's scaled FP4 MFMA.
+ * instruction, float32 or bf16 output).  Runs on gfx950's scaled f8f6f4 MFMA:
+ * A and B may each be any element type (MXFP4, MXFP6, MXFP8, mixed).  With an
+ * FP8 or FP6 operand the instruction's internal sum of its 64 products keeps
+ * about 14 binades below the largest product (measured; the spec leaves
+ * internal precision to the implementation).
  *
  *   A, B       host structs of device buffers; A->K == B->K; either may use
  *              1-D or 2-D scales (2-D requires rows % 32 == 0).
@@ -241,6 +275,7 @@ size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  *   B                host struct for expert 0: rows = N, K, block, strides;
  *                    expert e's codes start at B->codes + e*expert_stride_codes
  *                    bytes and its scales at B->scales + e*expert_stride_scales.
+ *                    A and B must be MXFP4 (else MX_ERR_UNSUPPORTED).
  *   C                device; [A->rows, N] of c_dtype, row stride ldc.
  */
 mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, int32_t E,

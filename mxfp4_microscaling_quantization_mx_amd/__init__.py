@@ -27,6 +27,8 @@ _AXIS = {"last": 0, "dim0": 1}
 _BLOCK = {"1d": 0, "2d": 1}
 _ROUND = {"rne": 0, "sr": 1}
 _SCALE = {"floor": 0, "round_up": 1, "prescale_3_4": 2}
+# MX element types: name -> (mx_elem, bits per element)
+_ELEM = {"e2m1": (0, 4), "e4m3": (1, 8), "e5m2": (2, 8), "e2m3": (3, 6), "e3m2": (4, 6)}
 _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
 EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_transpose", "mx_gemm",
@@ -37,7 +39,7 @@ class MxTensorC(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("rows", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("ld_codes", ctypes.c_int64), ("ld_scales", ctypes.c_int64),
-                ("block", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("elem", ctypes.c_int32)]
 
 
 class QuantCfgC(ctypes.Structure):
@@ -100,22 +102,25 @@ def _ptr(t):
 
 @dataclass
 class MXTensor:
-    """K-major MXFP4 operand: codes uint8 [rows, K/2], scales uint8 [rows, K/32]
-    (1-D) or [rows/32, K/32] (2-D).  Row strides are taken from the tensors."""
+    """K-major MX operand: codes uint8 [rows, K*bits/8] (MXFP4: K/2), scales
+    uint8 [rows, K/32] (1-D) or [rows/32, K/32] (2-D).  Row strides are taken
+    from the tensors.  elem: "e2m1" (MXFP4), "e4m3"/"e5m2" (MXFP8) or
+    "e2m3"/"e3m2" (MXFP6)."""
     codes: torch.Tensor
     scales: torch.Tensor
     rows: int
     K: int
     block: str = "1d"
+    elem: str = "e2m1"
 
     def c_struct(self):
         return MxTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.rows, self.K,
-                         self.codes.stride(0) if self.codes.dim() == 2 else self.K // 2,
+                         self.codes.stride(0) if self.codes.dim() == 2 else self.K * _ELEM[self.elem][1] // 8,
                          self.scales.stride(0) if self.scales.dim() == 2 else self.K // 32,
-                         _BLOCK[self.block], 0)
+                         _BLOCK[self.block], _ELEM[self.elem][0])
 
 
-def empty_mx(rows, K, block="1d", device="cuda", experts=None):
+def empty_mx(rows, K, block="1d", device="cuda", experts=None, elem="e2m1"):
     """Allocate an uninitialised MX operand (codes + scales) on `device`.
 
     Code rows are padded to a multiple of 128 bytes and scale rows to a
@@ -125,24 +130,27 @@ def empty_mx(rows, K, block="1d", device="cuda", experts=None):
     (the stacked weights of grouped_gemm); expert e is `expert(q, e)`."""
     srows = rows // 32 if block == "2d" else rows
     lead = () if experts is None else (experts,)
-    ldc = (K // 2 + 127) // 128 * 128
-    codes = torch.empty(lead + (rows, ldc), dtype=torch.uint8, device=device)[..., :K // 2]
+    cb = K * _ELEM[elem][1] // 8
+    ldc = (cb + 127) // 128 * 128
+    codes = torch.empty(lead + (rows, ldc), dtype=torch.uint8, device=device)[..., :cb]
     ld = (K // 32 + 15) // 16 * 16
     scales = torch.empty(lead + (srows, ld), dtype=torch.uint8, device=device)[..., :K // 32]
-    return MXTensor(codes, scales, rows, K, block)
+    return MXTensor(codes, scales, rows, K, block, elem)
 
 
 def expert(q, e):
     """View of expert e of a stacked operand from empty_mx(..., experts=E)."""
-    return MXTensor(q.codes[e], q.scales[e], q.rows, q.K, q.block)
+    return MXTensor(q.codes[e], q.scales[e], q.rows, q.K, q.block, q.elem)
 
 
 def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None, seed=0, offset=0,
-             out=None, scale_mode="floor"):
-    """Quantize a 2-D bf16/fp32 CUDA tensor to MXFP4 (see mx_quantize in include/mx.h).
+             out=None, scale_mode="floor", elem="e2m1"):
+    """Quantize a 2-D bf16/fp32 CUDA tensor to MXFP4 (or, with elem, MXFP8 /
+    MXFP6; see mx_quantize in include/mx.h).
 
     axis="dim0" blocks along dim 0 and returns the quantized transpose.
-    scale_mode: "floor" (the reference rule), "round_up" or "prescale_3_4"."""
+    scale_mode: "floor" (the reference rule), "round_up" or "prescale_3_4".
+    With `out` given, its element type is the one produced."""
     lib = load_library()
     if x.dim() != 2 or x.dtype not in _DTYPE or not x.is_cuda:
         raise ValueError("quantize expects a 2-D bf16/float32 CUDA tensor")
@@ -151,7 +159,7 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None, seed=0, 
     R, C = x.shape
     rows, K = (C, R) if axis == "dim0" else (R, C)
     if out is None:
-        out = empty_mx(rows, K, block, x.device)
+        out = empty_mx(rows, K, block, x.device, elem=elem)
     cfg = QuantCfgC(_AXIS[axis], _BLOCK[block], _ROUND[rounding], int(rht_mask is not None),
                     (rht_mask or 0) & 0xFFFFFFFF, _SCALE[scale_mode], seed & (2**64 - 1),
                     offset & (2**64 - 1))
@@ -236,7 +244,7 @@ def grouped_gemm(a, offsets, b, out_dtype=torch.bfloat16, out=None):
     if out is None:
         out = torch.empty((a.rows, N), dtype=out_dtype, device=a.codes.device)
     b0 = MxTensorC(b.codes.data_ptr(), b.scales.data_ptr(), N, b.K, b.codes.stride(1),
-                   b.scales.stride(1), _BLOCK[b.block], 0)
+                   b.scales.stride(1), _BLOCK[b.block], _ELEM[b.elem][0])
     at = a.c_struct()
     _check(lib.mx_grouped_gemm(ctypes.byref(at), _ptr(offsets), E, ctypes.byref(b0),
                                b.codes.stride(0), b.scales.stride(0), _ptr(out),

@@ -436,6 +436,169 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(MxOperand A, MxOperand B, 
   gemm_tile<false, B2D, OUT_BF16>(Ae, Be, s_rows, N, K, 0, n0, Ce, ldc, sm);
 }
 
+// ---------------------------------------------------------------- other element types
+// The same scaled MFMA with FP8 or FP6 operands (MXFP8, MXFP6; either operand
+// may be any MX element type): a 128x128 tile per 4-wave workgroup, 64x64 per
+// wave, staged through LDS per 128-deep K stage in 8-byte units (an FP6 block
+// is 24 bytes).  Operand registers per lane and 64-deep step (the
+// instruction's layout, checked by the probe tests): FP4 and FP6 take K-block
+// l/32 of the step whole (16 or 24 bytes); FP8 takes the 16-element halves
+// [16g, 16g+16) and [32+16g, 48+16g), g = l/32 (2 x 16 bytes).  Scale bytes are
+// per K-block as for FP4.
+
+// MFMA operand-format field of mx_elem F.
+template <int F>
+constexpr int mfma_fmt() {
+  if constexpr (F == 0) return 4;
+  else return ElemT<F>::MFMA;
+}
+
+// Stage rows [r0, r0 + 128) x K-stage k0 of an operand of element type F:
+// codes into lds (row pitch `pitch` bytes), scale words into lds_scales;
+// bytes past K or rows past `rows` are zeros, their scales 1.0.
+template <int F>
+__device__ __forceinline__ void stage_mx(const MxOperand& op, bool two_d, int64_t r0, int64_t rows, int64_t k0,
+                                         int64_t K, uint8_t* lds, int pitch, uint32_t* lds_scales, int tid,
+                                         int stid) {
+  constexpr int RB = 128 * elem_bits<F>() / 8;   // code bytes per row per stage
+  constexpr int U = RB / 8;
+  const int64_t kbytes = K * elem_bits<F>() / 8;
+  const int64_t kb0 = k0 * elem_bits<F>() / 8;
+#pragma unroll
+  for (int it = 0; it < U / 2; ++it) {
+    const int id = tid + 256 * it;
+    const int r = id / U, u = id - r * U;
+    const int64_t gr = r0 + r;
+    uint2 v = make_uint2(0u, 0u);
+    if (gr < rows && kb0 + 8 * u < kbytes)
+      v = *reinterpret_cast<const uint2*>(op.codes + gr * op.ld_codes + kb0 + 8 * u);
+    *reinterpret_cast<uint2*>(lds + r * pitch + 8 * u) = v;
+  }
+  if (stid >= 0 && stid < 128) {
+    const int64_t gr = r0 + stid;
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t kb = (k0 >> 5) + j;
+      uint32_t sc = 127u;
+      if (gr < rows && kb * 32 < K) sc = op.scales[(two_d ? (gr >> 5) : gr) * op.ld_scales + kb];
+      w |= sc << (8 * j);
+    }
+    lds_scales[stid] = w;
+  }
+}
+
+// This lane's operand registers for 64-deep step ks from its LDS row.
+template <int F>
+__device__ __forceinline__ v8i read_mx(const uint8_t* row, int ks, int hi) {
+  if constexpr (F == 0) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + 32 * ks + 16 * hi);
+    return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  } else if constexpr (elem_bits<F>() == 8) {
+    const uint4 v0 = *reinterpret_cast<const uint4*>(row + 64 * ks + 16 * hi);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(row + 64 * ks + 32 + 16 * hi);
+    return v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+  } else {
+    const uint2* p = reinterpret_cast<const uint2*>(row + 48 * ks + 24 * hi);
+    const uint2 a = p[0], b = p[1], c = p[2];
+    return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+  }
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(256) void k_gemm_mx(MxOperand A, MxOperand B, int64_t M, int64_t N, int64_t K, void* C,
+                                                 int64_t ldc, int a_2d, int b_2d, int out_bf16) {
+  constexpr int PA = 128 * elem_bits<FA>() / 8 + 16, PB = 128 * elem_bits<FB>() / 8 + 16;
+  constexpr int FMA = mfma_fmt<FA>(), FMB = mfma_fmt<FB>();
+  __shared__ __attribute__((aligned(16))) uint8_t la[128 * PA];
+  __shared__ __attribute__((aligned(16))) uint8_t lb[128 * PB];
+  __shared__ uint32_t lsa[128], lsb[128];
+  const int64_t m0 = (int64_t)blockIdx.y * 128, n0 = (int64_t)blockIdx.x * 128;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  for (int64_t k0 = 0; k0 < K; k0 += 128) {
+    stage_mx<FA>(A, a_2d != 0, m0, M, k0, K, la, PA, lsa, tid, tid);
+    stage_mx<FB>(B, b_2d != 0, n0, N, k0, K, lb, PB, lsb, tid, tid - 128);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v8i a[2], b[2];
+      int sa[2], sb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + l32;
+        a[i] = read_mx<FA>(la + r * PA, ks, hi);
+        sa[i] = (int)(lsa[r] >> (8 * hi));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + l32;
+        b[j] = read_mx<FB>(lb + r * PB, ks, hi);
+        sb[j] = (int)(lsb[r] >> (8 * hi));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (ks == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FMA, FMB, 0,
+                                                                         sa[i], 0, sb[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FMA, FMB, 2,
+                                                                         sa[i], 2, sb[j]);
+        }
+    }
+    __syncthreads();
+  }
+  // lane holds column l32; register r holds row 8*(r/4) + 4*hi + r%4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn * 64 + j * 32 + l32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (row < M) {
+          if (out_bf16)
+            static_cast<uint16_t*>(C)[row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+          else
+            static_cast<float*>(C)[row * ldc + col] = acc[i][j][r];
+        }
+      }
+    }
+}
+
+template <int FA, int FB>
+hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)((a.M + 127) / 128));
+  hipLaunchKernelGGL((k_gemm_mx<FA, FB>), grid, dim3(256), 0, st, a.A, a.B, a.M, a.N, a.K, a.C, a.ldc,
+                     (int)a.a_2d, (int)a.b_2d, (int)a.out_bf16);
+  return hipGetLastError();
+}
+
+template <int FA>
+hipError_t launch_gemm_mx_b(const GemmArgs& a, hipStream_t st) {
+  switch (a.b_elem) {
+    case 1: return launch_gemm_mx<FA, 1>(a, st);
+    case 2: return launch_gemm_mx<FA, 2>(a, st);
+    case 3: return launch_gemm_mx<FA, 3>(a, st);
+    case 4: return launch_gemm_mx<FA, 4>(a, st);
+    default: return launch_gemm_mx<FA, 0>(a, st);
+  }
+}
+
 }  // namespace
 
 // Compute units of the current device (cached per device).
@@ -453,6 +616,15 @@ static int cu_count() {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (a.a_elem != 0 || a.b_elem != 0) {
+    switch (a.a_elem) {
+      case 1: return launch_gemm_mx_b<1>(a, st);
+      case 2: return launch_gemm_mx_b<2>(a, st);
+      case 3: return launch_gemm_mx_b<3>(a, st);
+      case 4: return launch_gemm_mx_b<4>(a, st);
+      default: return launch_gemm_mx_b<0>(a, st);
+    }
+  }
   // 256x256 tiles: scale rows are fetched 16 bytes at a time (16-byte aligned
   // rows), and the operands are addressed with 32-bit offsets.
   const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) &&

@@ -31,18 +31,30 @@ mx_status hip_status(hipError_t e, const char* what) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Validate one MX operand description; `what` names it in messages.
+// Bits per element of an mx_elem (0 for an unknown value).
+int elem_bits(int32_t e) {
+  switch (e) {
+    case MX_ELEM_E2M1: return 4;
+    case MX_ELEM_E4M3:
+    case MX_ELEM_E5M2: return 8;
+    case MX_ELEM_E2M3:
+    case MX_ELEM_E3M2: return 6;
+    default: return 0;
+  }
+}
+
 mx_status check_tensor(const mx_tensor* t, const char* what) {
   if (!t) return fail(MX_ERR_INVALID_ARG, "%s: null mx_tensor", what);
   if (t->rows < 0 || t->K < 0) return fail(MX_ERR_INVALID_ARG, "%s: negative shape", what);
   if (t->K % 32) return fail(MX_ERR_INVALID_ARG, "%s: K=%lld is not a multiple of 32", what, (long long)t->K);
   if (t->block != MX_BLOCK_1D && t->block != MX_BLOCK_2D)
     return fail(MX_ERR_INVALID_ARG, "%s: unknown block kind %d", what, t->block);
-  if (t->reserved != 0) return fail(MX_ERR_INVALID_ARG, "%s: reserved field must be 0", what);
+  if (elem_bits(t->elem) == 0) return fail(MX_ERR_INVALID_ARG, "%s: unknown element type %d", what, t->elem);
   if (t->block == MX_BLOCK_2D && t->rows % 32)
     return fail(MX_ERR_INVALID_ARG, "%s: 2-D blocks need rows %% 32 == 0 (rows=%lld)", what, (long long)t->rows);
   if (t->rows == 0 || t->K == 0) return MX_OK;
   if (!t->codes || !t->scales) return fail(MX_ERR_INVALID_ARG, "%s: null codes/scales pointer", what);
-  if (t->ld_codes < t->K / 2 || t->ld_scales < t->K / 32)
+  if (t->ld_codes < t->K * elem_bits(t->elem) / 8 || t->ld_scales < t->K / 32)
     return fail(MX_ERR_INVALID_ARG, "%s: row strides too small (ld_codes=%lld, ld_scales=%lld)", what,
                 (long long)t->ld_codes, (long long)t->ld_scales);
   if (!aligned(t->codes, 16) || t->ld_codes % 16)
@@ -89,6 +101,8 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   if (out->block != cfg->block) return fail(MX_ERR_INVALID_ARG, "mx_quantize: out->block differs from cfg->block");
   mx_status st = check_tensor(out, "mx_quantize: out");
   if (st != MX_OK) return st;
+  if (out->elem != MX_ELEM_E2M1 && cfg->block != MX_BLOCK_1D)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: 2-D blocks are built for MXFP4 only");
   if (R == 0 || C == 0) return MX_OK;
   if (!src) return fail(MX_ERR_INVALID_ARG, "mx_quantize: null src");
   if (ld_src < C) return fail(MX_ERR_INVALID_ARG, "mx_quantize: ld_src=%lld < C=%lld", (long long)ld_src, (long long)C);
@@ -121,6 +135,7 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   a.ld_codes = out->ld_codes;
   a.scales = out->scales;
   a.ld_scales = out->ld_scales;
+  a.elem = out->elem;
   return hip_status(mx::launch_quantize(a, static_cast<hipStream_t>(stream)), "mx_quantize");
 }
 
@@ -147,6 +162,7 @@ mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, 
   if (out->block != MX_BLOCK_1D) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: out must hold 1-D blocks");
   mx_status st = check_tensor(out, "mx_quantize_gather: out");
   if (st != MX_OK) return st;
+  if (out->elem != MX_ELEM_E2M1) return fail(MX_ERR_UNSUPPORTED, "mx_quantize_gather: MXFP4 output only");
   if (rows_out == 0 || C == 0) return MX_OK;
   if (!rows || !aligned(rows, 4)) return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: null or unaligned rows");
   if (R_src > 0) {
@@ -206,6 +222,7 @@ mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_s
   a.dst = dst;
   a.out_bf16 = dst_dtype == MX_DT_BF16;
   a.ld_dst = ld_dst;
+  a.elem = in->elem;
   return hip_status(mx::launch_dequantize(a, static_cast<hipStream_t>(stream)), "mx_dequantize");
 }
 
@@ -217,6 +234,8 @@ mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream) 
   if (st != MX_OK) return st;
   if (in->block != MX_BLOCK_2D || out->block != MX_BLOCK_2D)
     return fail(MX_ERR_UNSUPPORTED, "mx_transpose: only operands with 2-D (32x32) blocks transpose exactly");
+  if (in->elem != MX_ELEM_E2M1 || out->elem != MX_ELEM_E2M1)
+    return fail(MX_ERR_UNSUPPORTED, "mx_transpose: MXFP4 operands only");
   if (out->rows != in->K || out->K != in->rows)
     return fail(MX_ERR_INVALID_ARG, "mx_transpose: out is [%lld, %lld], expected [%lld, %lld]", (long long)out->rows,
                 (long long)out->K, (long long)in->K, (long long)in->rows);
@@ -273,6 +292,8 @@ mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dty
   a.C = C;
   a.ldc = ldc;
   a.out_bf16 = c_dtype == MX_DT_BF16;
+  a.a_elem = A->elem;
+  a.b_elem = B->elem;
   return hip_status(mx::launch_gemm(a, static_cast<hipStream_t>(stream)), "mx_gemm");
 }
 
@@ -285,6 +306,8 @@ mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, in
   if (st != MX_OK) return st;
   st = check_tensor(B, "mx_grouped_gemm: B");
   if (st != MX_OK) return st;
+  if (A->elem != MX_ELEM_E2M1 || B->elem != MX_ELEM_E2M1)
+    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: MXFP4 operands only");
   if (A->block != MX_BLOCK_1D)
     return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: A must use 1-D blocks (expert boundaries are arbitrary rows)");
   if (A->K != B->K)

@@ -294,4 +294,96 @@ __device__ __forceinline__ void fwht32_inlane(float x[32]) {
 
 constexpr uint32_t kRhtCBits = 0x3E3504F3u;   // float32(1/sqrt(32))
 
+// ---------------------------------------------------------------- other MX element types
+// FP8 (E4M3, E5M2) and FP6 (E2M3, E3M2) elements of MXFP8 / MXFP6 ("MXFP4",
+// AI Wiki, §Place in the MX family), with the OCP element definitions: E
+// exponent bits of bias 2^(E-1)-1, M mantissa bits, subnormals at exponent
+// field 0; E4M3's S.1111.111 is NaN (largest normal 448), E5M2's top exponent
+// is Inf/NaN (largest normal 57344), FP6 has no Inf/NaN (largest normals 7.5
+// and 28).  ELEM is the mx_elem value (1..4); E2M1 (0) keeps the code above.
+template <int ELEM>
+struct ElemT;
+template <>
+struct ElemT<1> {   // E4M3
+  static constexpr int E = 4, M = 3, BIAS = 7, MAXCODE = 0x7E, EMAX = 8, BITS = 8, MFMA = 0;
+  static constexpr uint32_t MAXBITS = 0x43E00000u;   // 448 = 1.75 * 2^8
+};
+template <>
+struct ElemT<2> {   // E5M2
+  static constexpr int E = 5, M = 2, BIAS = 15, MAXCODE = 0x7B, EMAX = 15, BITS = 8, MFMA = 1;
+  static constexpr uint32_t MAXBITS = 0x47600000u;   // 57344 = 1.75 * 2^15
+};
+template <>
+struct ElemT<3> {   // E2M3
+  static constexpr int E = 2, M = 3, BIAS = 1, MAXCODE = 0x1F, EMAX = 2, BITS = 6, MFMA = 2;
+  static constexpr uint32_t MAXBITS = 0x40F00000u;   // 7.5 = 1.875 * 2^2
+};
+template <>
+struct ElemT<4> {   // E3M2
+  static constexpr int E = 3, M = 2, BIAS = 3, MAXCODE = 0x1F, EMAX = 4, BITS = 6, MFMA = 3;
+  static constexpr uint32_t MAXBITS = 0x41E00000u;   // 28 = 1.75 * 2^4
+};
+
+// Bits per element of mx_elem ELEM (0 is E2M1).
+template <int ELEM>
+constexpr int elem_bits() {
+  if constexpr (ELEM == 0) return 4;
+  else return ElemT<ELEM>::BITS;
+}
+
+// Scale byte of a block whose largest magnitude has float32 bits m (sign
+// cleared): the reference rule floor(log2 amax) - EMAX, or (ROUND_UP) the
+// smallest exponent e with amax <= largest normal * 2^e; clamped at 0; NaN or
+// Inf give 0xFF.
+template <int ELEM>
+__device__ __forceinline__ uint32_t elem_scale_code(uint32_t m, bool round_up) {
+  using T = ElemT<ELEM>;
+  if (m >= 0x7F800000u) return 0xFFu;
+  const int c = (int)(m >> 23) - T::EMAX + (round_up ? (int)((m & 0x7FFFFFu) > (T::MAXBITS & 0x7FFFFFu)) : 0);
+  return (uint32_t)(c > 0 ? c : 0);
+}
+
+// Magnitude code of a = |v| (v already divided by the block scale, finite):
+// with Ec the binade of a (at least the subnormal binade 1 - BIAS), the grid
+// spacing is 2^(Ec - M) and t = a * 2^(M - Ec) is exact; the code is
+// ((Ec + BIAS - 1) << M) + round(t), continuous across binades, and saturates
+// at the largest normal.  RNE rounds t to even (an even t is an even code);
+// SR rounds up iff the 16 random bits r are below frac(t) * 2^16.
+template <int ELEM, bool SR>
+__device__ __forceinline__ uint32_t elem_mag_code(float a, uint32_t r16) {
+  using T = ElemT<ELEM>;
+  const uint32_t ab = __float_as_uint(a);
+  if (ab >= T::MAXBITS) return T::MAXCODE;
+  const int ev = (int)(ab >> 23) - 127;
+  const int ec = ev > 1 - T::BIAS ? ev : 1 - T::BIAS;
+  const float t = a * __uint_as_float((uint32_t)(127 + T::M - ec) << 23);
+  uint32_t n;
+  if (SR) {
+    const float fl = __builtin_floorf(t);
+    n = (uint32_t)fl + (uint32_t)((float)r16 < (t - fl) * 65536.0f);
+  } else {
+    n = (uint32_t)__builtin_rintf(t);
+  }
+  const uint32_t code = ((uint32_t)(ec + T::BIAS - 1) << T::M) + n;
+  return code < (uint32_t)T::MAXCODE ? code : (uint32_t)T::MAXCODE;
+}
+
+template <int ELEM, bool SR>
+__device__ __forceinline__ uint32_t elem_code(float v, uint32_t r16) {
+  using T = ElemT<ELEM>;
+  return elem_mag_code<ELEM, SR>(__builtin_fabsf(v), r16) | ((__float_as_uint(v) >> 31) << (T::E + T::M));
+}
+
+// Value of a code (NaN and Inf codes decode as such).
+template <int ELEM>
+__device__ __forceinline__ float elem_value(uint32_t c) {
+  using T = ElemT<ELEM>;
+  const uint32_t e = (c >> T::M) & ((1u << T::E) - 1u), f = c & ((1u << T::M) - 1u);
+  float mag = e == 0 ? (float)f * __uint_as_float((uint32_t)(127 + 1 - T::BIAS - T::M) << 23)
+                     : (float)((1u << T::M) | f) * __uint_as_float((uint32_t)(127 + (int)e - T::BIAS - T::M) << 23);
+  if (ELEM == 1 && e == 15u && f == 7u) mag = __builtin_nanf("");
+  if (ELEM == 2 && e == 31u) mag = f == 0 ? __builtin_inff() : __builtin_nanf("");
+  return (c >> (T::E + T::M)) & 1u ? -mag : mag;
+}
+
 }  // namespace mx

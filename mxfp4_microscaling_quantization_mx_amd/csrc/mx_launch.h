@@ -24,6 +24,7 @@ struct QuantArgs {
   int scale_mode = 0;                // 0 reference rule, 1 round up, 2 prescale by 3/4
   const int32_t* gather = nullptr;   // device [R]: source row of each output row (last dim, 1-D only)
   int64_t R_src = 0;                 // source rows when gathering
+  int elem = 0;                      // mx_elem of the output (0: FP4 E2M1)
 };
 
 struct DequantArgs {
@@ -36,6 +37,7 @@ struct DequantArgs {
   void* dst;
   bool out_bf16;
   int64_t ld_dst;
+  int elem = 0;
 };
 
 // One MX operand as the GEMM kernels see it.
@@ -52,6 +54,7 @@ struct GemmArgs {
   void* C;
   int64_t ldc;
   bool out_bf16;
+  int a_elem = 0, b_elem = 0;  // mx_elem of A and B
 };
 
 struct GroupedGemmArgs {

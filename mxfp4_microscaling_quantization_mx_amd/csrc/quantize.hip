@@ -133,10 +133,97 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
   return s;
 }
 
+// The same block step for the other MX element types (ELEM = mx_elem 1..4,
+// FP8 or FP6): scale from the type's largest power of two, elements rounded in
+// software (elem_code: RNE, or SR with the same Philox draws as E2M1), then
+// packed: FP8 one byte per element (8 words), FP6 element e at bits 6e of the
+// block's 192 bits (6 words).  Returns the scale byte.
+template <int ELEM, bool RHT, bool SR>
+__device__ __forceinline__ uint32_t quantize_block32_elem(float x[32], uint32_t out[8], uint64_t p0, uint64_t seed,
+                                                          uint64_t offset, int scale_mode) {
+  using T = ElemT<ELEM>;
+  const float c = __uint_as_float(kRhtCBits);
+  if (RHT) fwht32_inlane(x);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  if (RHT) {
+    m = __float_as_uint(c * __uint_as_float(m));
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = c * x[i];
+  }
+  const uint32_t s = elem_scale_code<ELEM>(m, scale_mode == 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = 0u;
+  if (s == 0xFFu) return s;
+  if (scale_mode == 2) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.75f * x[i];
+  }
+  const float inv = inv_scale_from_code(s);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (SR) sr_words((p0 >> 3) + g, seed, offset, w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 8 * g + i;
+      const uint32_t r16 = SR ? (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu : 0u;
+      const uint32_t code = elem_code<ELEM, SR>(x[e] * inv, r16);
+      if (T::BITS == 8) {
+        out[e >> 2] |= code << (8 * (e & 3));
+      } else {
+        const int bit = 6 * e;
+        out[bit >> 5] |= code << (bit & 31);
+        if ((bit & 31) > 26) out[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+      }
+    }
+  }
+  return s;
+}
+
+// Store one block's codes (E2M1: 16 bytes, FP6: 24, FP8: 32) at dst, which is
+// aligned to the block size's power-of-two part.
+template <int ELEM>
+__device__ __forceinline__ void store_block(uint8_t* dst, const uint32_t w[8]) {
+  if constexpr (ELEM == 0) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (ElemT<ELEM>::BITS == 8) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(w[2], w[3]);
+    *reinterpret_cast<uint2*>(dst + 16) = make_uint2(w[4], w[5]);
+  }
+}
+
+// Code bytes of one 32-element block.
+template <int ELEM>
+constexpr int block_bytes() {
+  return 4 * elem_bits<ELEM>();
+}
+
+// Quantize one block of element type ELEM (E2M1 through the hardware-convert
+// path above) and store its codes at dst; returns the scale byte.
+template <int ELEM, bool RHT, bool SR, bool TWO_D = false>
+__device__ __forceinline__ uint32_t quantize_store(float x[32], uint8_t* dst, uint64_t p0, uint64_t seed,
+                                                   uint64_t offset, int scale_mode) {
+  uint32_t w[8];
+  uint32_t s;
+  if constexpr (ELEM == 0) {
+    s = quantize_block32<RHT, SR, TWO_D>(x, w, p0, seed, offset, scale_mode);
+  } else {
+    s = quantize_block32_elem<ELEM, RHT, SR>(x, w, p0, seed, offset, scale_mode);
+  }
+  store_block<ELEM>(dst, w);
+  return s;
+}
+
 // GATHER: output row r quantizes source row gidx[r] (the routed rows of an MoE
 // layer read straight from the token activations); an index outside
 // [0, R_src) gives the row NaN blocks (scale byte 0xFF, codes 0).
-template <bool BF16, bool RHT, bool SR, bool GATHER>
+template <bool BF16, bool RHT, bool SR, bool GATHER, int ELEM>
 __global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ src, uint32_t nblocks,
                                                        uint32_t nkb, int64_t ld_src,
                                                        uint8_t* __restrict__ codes, int64_t ld_codes,
@@ -159,11 +246,9 @@ __global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ 
   }
   float x[32];
   load32<BF16>(src, srow * ld_src + 32 * kb, x, RHT ? mask : 0u);
-  uint32_t packed[4];
   const uint64_t p0 = ((uint64_t)row * nkb + kb) * 32u;         // output row * K + 32 kb
-  const uint32_t s = quantize_block32<RHT, SR>(x, packed, p0, seed, offset, scale_mode);
-  *reinterpret_cast<uint4*>(codes + (int64_t)row * ld_codes + 16 * kb) =
-      make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  const uint32_t s = quantize_store<ELEM, RHT, SR>(
+      x, codes + (int64_t)row * ld_codes + block_bytes<ELEM>() * kb, p0, seed, offset, scale_mode);
   scales[(int64_t)row * ld_scales + kb] = (uint8_t)s;
 }
 
@@ -241,7 +326,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
 // consecutive columns of one source row.  The block then goes through the same
 // register path as a row block.  2-D: a half-wave holds one 32x32 tile (output
 // rows are a multiple of 32, so half-waves are whole or empty).
-template <bool TWO_D, bool BF16, bool RHT, bool SR>
+template <bool TWO_D, bool BF16, bool RHT, bool SR, int ELEM>
 __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src, int64_t R, int64_t C,
                                                     int64_t ld_src, uint8_t* __restrict__ codes,
                                                     int64_t ld_codes, uint8_t* __restrict__ scales,
@@ -268,10 +353,9 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
     if (RHT) b ^= ((mask >> i) & 1u) << 31;
     x[i] = __uint_as_float(b);
   }
-  uint32_t packed[4];
   const uint64_t p0 = (uint64_t)col * (uint64_t)R + (uint64_t)kb * 32u;   // output row * K + 32 kb
-  const uint32_t s = quantize_block32<RHT, SR, TWO_D>(x, packed, p0, seed, offset, scale_mode);
-  *reinterpret_cast<uint4*>(codes + col * ld_codes + kb * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  const uint32_t s = quantize_store<ELEM, RHT, SR, TWO_D>(x, codes + col * ld_codes + kb * block_bytes<ELEM>(), p0,
+                                                          seed, offset, scale_mode);
   if (!TWO_D) {
     scales[col * ld_scales + kb] = (uint8_t)s;
   } else if ((col & 31) == 0) {
@@ -279,11 +363,11 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
   }
 }
 
-template <bool TWO_D, bool BF16>
+template <bool TWO_D, bool BF16, int ELEM>
 hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
   dim3 grid((unsigned)((a.C + 63) / 64), (unsigned)((a.R + 127) / 128));
 #define MX_COLS(RHT_, SR_)                                                                   \
-  hipLaunchKernelGGL((k_quant_cols<TWO_D, BF16, RHT_, SR_>), grid, dim3(256), 0, st, a.src, a.R, a.C, \
+  hipLaunchKernelGGL((k_quant_cols<TWO_D, BF16, RHT_, SR_, ELEM>), grid, dim3(256), 0, st, a.src, a.R, a.C, \
                      a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset,      \
                      a.scale_mode)
   if (a.rht) {
@@ -312,13 +396,13 @@ hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool GATHER>
+template <bool BF16, bool GATHER, int ELEM>
 hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
   const uint32_t nkb = (uint32_t)(a.C / 32);
   const uint32_t nblocks = (uint32_t)(a.R * nkb);
   const unsigned grid = (nblocks + 255u) / 256u;
 #define MX_ROWS(RHT_, SR_)                                                                            \
-  hipLaunchKernelGGL((k_quant_rows_1d<BF16, RHT_, SR_, GATHER>), dim3(grid), dim3(256), 0, st, a.src, \
+  hipLaunchKernelGGL((k_quant_rows_1d<BF16, RHT_, SR_, GATHER, ELEM>), dim3(grid), dim3(256), 0, st, a.src, \
                      nblocks, nkb, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask,    \
                      a.seed, a.offset, a.scale_mode, a.gather, a.R_src)
   if (a.rht) {
@@ -330,15 +414,31 @@ hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The other element types: 1-D blocks along either axis (validated by the
+// caller).
+template <int ELEM>
+hipError_t launch_quantize_elem(const QuantArgs& a, hipStream_t st) {
+  if (a.dim0) return a.bf16 ? launch_cols<false, true, ELEM>(a, st) : launch_cols<false, false, ELEM>(a, st);
+  return a.bf16 ? launch_rows_1d<true, false, ELEM>(a, st) : launch_rows_1d<false, false, ELEM>(a, st);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   if (a.R == 0 || a.C == 0) return hipSuccess;
-  if (a.gather) return a.bf16 ? launch_rows_1d<true, true>(a, st) : launch_rows_1d<false, true>(a, st);
-  if (!a.dim0 && !a.two_d) return a.bf16 ? launch_rows_1d<true, false>(a, st) : launch_rows_1d<false, false>(a, st);
+  switch (a.elem) {
+    case 1: return launch_quantize_elem<1>(a, st);
+    case 2: return launch_quantize_elem<2>(a, st);
+    case 3: return launch_quantize_elem<3>(a, st);
+    case 4: return launch_quantize_elem<4>(a, st);
+    default: break;
+  }
+  if (a.gather) return a.bf16 ? launch_rows_1d<true, true, 0>(a, st) : launch_rows_1d<false, true, 0>(a, st);
+  if (!a.dim0 && !a.two_d)
+    return a.bf16 ? launch_rows_1d<true, false, 0>(a, st) : launch_rows_1d<false, false, 0>(a, st);
   if (a.dim0) {
-    if (a.two_d) return a.bf16 ? launch_cols<true, true>(a, st) : launch_cols<true, false>(a, st);
-    return a.bf16 ? launch_cols<false, true>(a, st) : launch_cols<false, false>(a, st);
+    if (a.two_d) return a.bf16 ? launch_cols<true, true, 0>(a, st) : launch_cols<true, false, 0>(a, st);
+    return a.bf16 ? launch_cols<false, true, 0>(a, st) : launch_cols<false, false, 0>(a, st);
   }
   return a.bf16 ? launch_tile<true>(a, st) : launch_tile<false>(a, st);
 }

@@ -47,6 +47,11 @@ def _decode_f64(codes, scales, block, rows=None, elem="e2m1"):
         return vals * np.repeat(sc, BLOCK, axis=1)
 
 
+def dequant_f64(codes, scales, elem="e2m1", block="1d"):
+    """The operand's exact values as float64 [rows, K] (no transform)."""
+    return _decode_f64(codes, scales, block, None, elem)
+
+
 def gemm_ref(a_codes, a_scales, b_codes, b_scales, a_block="1d", b_block="1d",
              rows=None, cols=None, a_elem="e2m1", b_elem="e2m1"):
     """Reference C = A * B^T for K-major MX operands A [M, K], B [N, K]

@@ -5,6 +5,8 @@
 //    supplied by the caller, and write the raw accumulator registers, so the
 //    tests can check the operand, scale and result lane layouts against a
 //    NumPy model.
+//  * probe_mfma_scale_32x32x64_fmt: the same 32x32x64 MFMA with FP8, FP6 or
+//    FP4 operands (the element-format fields of the instruction).
 //  * probe_cvt_fp4_sweep: compare the hardware packed FP4 conversion (scale
 //    1.0) with the library's software RNE rounding over every float32 bit
 //    pattern in [lo, hi), counting mismatches and recording the first few.
@@ -47,6 +49,19 @@ __global__ void k_mfma16(const int* a, const int* b, const int* sa, const int* s
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, sa[l], 0, sb[l]);
   for (int i = 0; i < 4; ++i) out[l * 4 + i] = acc[i];
+}
+
+// One scaled MFMA with element formats FA (A) and FB (B): 0 FP8 E4M3, 1 FP8
+// E5M2, 2 FP6 E2M3, 3 FP6 E3M2, 4 FP4 E2M1.
+template <int FA, int FB>
+__global__ void k_mfma32_fmt(const int* a, const int* b, const int* sa, const int* sb, float* out) {
+  const int l = threadIdx.x;
+  v8i av, bv;
+  for (int i = 0; i < 8; ++i) { av[i] = a[l * 8 + i]; bv[i] = b[l * 8 + i]; }
+  v16f acc;
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, FA, FB, 0, sa[l], 0, sb[l]);
+  for (int i = 0; i < 16; ++i) out[l * 16 + i] = acc[i];
 }
 
 // Each thread walks a strided subset of [lo, hi); pairs (x, -x) go through the
@@ -152,6 +167,16 @@ int probe_mfma_scale_32x32x64(const int* a, const int* b, const int* sa, const i
   else
     hipLaunchKernelGGL(k_mfma32, dim3(1), dim3(64), 0, 0, a, b, sa, sb, out);
   return (int)hipGetLastError();
+}
+
+int probe_mfma_scale_32x32x64_fmt(const int* a, const int* b, const int* sa, const int* sb, float* out, int fa,
+                                  int fb) {
+#define MX_PROBE_FMT(A_, B_) \
+  if (fa == A_ && fb == B_) { hipLaunchKernelGGL((k_mfma32_fmt<A_, B_>), dim3(1), dim3(64), 0, 0, a, b, sa, sb, out); return (int)hipGetLastError(); }
+  MX_PROBE_FMT(0, 0) MX_PROBE_FMT(1, 1) MX_PROBE_FMT(2, 2) MX_PROBE_FMT(3, 3) MX_PROBE_FMT(0, 4) MX_PROBE_FMT(4, 3)
+  MX_PROBE_FMT(1, 2) MX_PROBE_FMT(1, 4) MX_PROBE_FMT(2, 4) MX_PROBE_FMT(3, 4) MX_PROBE_FMT(4, 4)
+#undef MX_PROBE_FMT
+  return -1;
 }
 
 int probe_mfma_scale_16x16x128(const int* a, const int* b, const int* sa, const int* sb, float* out) {

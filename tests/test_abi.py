@@ -115,6 +115,41 @@ def test_transpose_rejects_bad_arguments(lib):
                             None) == mx.MX_OK
 
 
+def test_element_types_are_validated(lib):
+    """mx_tensor.elem: unknown values are refused everywhere; MXFP8/MXFP6 rows
+    need K*bits/8 bytes; 2-D quantization, the gather, the transpose and the
+    grouped GEMM are MXFP4-only."""
+    cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 0, 0, 0)
+    bad = _tensor(32, 64)
+    bad.elem = 9
+    st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(cfg), ctypes.byref(bad), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"element type" in lib.mx_last_error()
+    fp8 = _tensor(32, 64, ldc=48)          # needs 64 bytes per row
+    fp8.elem = 1
+    st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(cfg), ctypes.byref(fp8), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"strides" in lib.mx_last_error()
+    fp6_2d = _tensor(32, 64, ldc=48, block=1)
+    fp6_2d.elem = 3
+    cfg2 = mx.QuantCfgC(0, 1, 0, 0, 0, 0, 0, 0)
+    st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(cfg2), ctypes.byref(fp6_2d), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+    fp6 = _tensor(8, 64, ldc=48)
+    fp6.elem = 3
+    st = lib.mx_quantize_gather(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.c_void_p(16), 8, ctypes.byref(cfg),
+                                ctypes.byref(fp6), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+    t_in = _tensor(64, 96, ldc=96, block=1)
+    t_in.elem = 1
+    st = lib.mx_transpose(ctypes.byref(t_in), ctypes.byref(_tensor(96, 64, block=1)), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+    a = _tensor(64, 64, ldc=64)
+    a.elem = 2
+    b = _tensor(64, 64, block=1)
+    st = lib.mx_grouped_gemm(ctypes.byref(a), ctypes.c_void_p(16), 2, ctypes.byref(b), 0, 0, ctypes.c_void_p(16), 0, 64,
+                             None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+
+
 def test_gemm_rejects_bad_arguments(lib):
     a = _tensor(32, 64)
     b = _tensor(32, 96)

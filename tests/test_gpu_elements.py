@@ -1,0 +1,202 @@
+"""GPU parity of the MXFP8 / MXFP6 element types against the oracle.
+
+Quantizer and dequantizer: codes, scales and decoded values bit-exact (the
+quantizer rounds in software on the GPU, so there is no allowance).  GEMM: the
+oracle's float64 reference of the oracle's own operands, within
+1e-5 * sum |a_k b_k| plus the scaled MFMA's internal-precision allowance for
+FP8/FP6 operands (gpu_util.mx_group_bound, measured by the probe tests).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_microscaling_quantization_mx_amd as mx
+import oracle
+from gpu_util import banner, bf16_half_ulp, codes_equal, host, mx_group_bound, need_gpu, to_dev
+from oracle import elements as el
+
+pytestmark = pytest.mark.gpu
+
+ELEMS = ["e4m3", "e5m2", "e2m3", "e3m2"]
+
+
+def _case_id(elem, axis, rounding, rht):
+    return f"{elem}-{axis}-{rounding}-{'rht' if rht else 'plain'}"
+
+
+CASES = [(e, a, r, h) for e in ELEMS for a in ("last", "dim0") for r in ("rne", "sr") for h in (False, True)]
+
+
+@pytest.mark.parametrize("elem,axis,rounding,rht", CASES, ids=[_case_id(*c) for c in CASES])
+def test_quantize_elements(elem, axis, rounding, rht):
+    """Every element type along both axes, RNE and stochastic rounding, with and
+    without the transform, on ragged bf16 shapes: bit-exact."""
+    need_gpu()
+    R, C = (72, 416) if axis == "last" else (224, 88)
+    rng = np.random.default_rng(zlib.crc32(_case_id(elem, axis, rounding, rht).encode()))
+    x = (rng.standard_t(3, (R, C)) * np.exp(rng.uniform(-6, 6, (R, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    kw = dict(axis=axis, rounding=rounding, rht_mask=0x5A5A1234 if rht else None, seed=0xABCDEF12345, offset=3)
+    banner(f"quantize {_case_id(elem, axis, rounding, rht)} R={R} C={C}")
+    q = mx.quantize(xt.cuda(), elem=elem, **kw)
+    oc, os_ = oracle.quantize(xt.float().numpy(), elem=elem, **kw)
+    codes_equal(host(q.scales), os_, "scales")
+    codes_equal(host(q.codes), oc, "codes")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("scale_mode", ["round_up", "prescale_3_4"])
+def test_quantize_elements_scale_modes_f32(elem, scale_mode):
+    need_gpu()
+    rng = np.random.default_rng(7 + ELEMS.index(elem))
+    x = (rng.standard_normal((40, 160)) * np.exp(rng.uniform(-9, 9, (40, 1)))).astype(np.float32)
+    banner(f"quantize {elem} {scale_mode} f32")
+    q = mx.quantize(to_dev(x), elem=elem, scale_mode=scale_mode, rounding="sr", seed=5)
+    oc, os_ = oracle.quantize(x, elem=elem, scale_mode=scale_mode, rounding="sr", seed=5)
+    codes_equal(host(q.scales), os_, "scales")
+    codes_equal(host(q.codes), oc, "codes")
+
+
+def _adversarial(elem):
+    """Blocks whose scaled values sit on grid points, midpoints (ties) and
+    +-1 ulp around them, in the clip band above the largest normal, in the
+    subnormal range, plus zero, NaN and Inf blocks and extreme magnitudes."""
+    g = el.grid(elem)
+    top = g[-1]
+    p2 = 2.0 ** el.emax(elem)
+    vals = [float(v) for v in g] + [float((a + b) / 2) for a, b in zip(g[:-1], g[1:])]
+    vals += [float(np.nextafter(np.float32(v), np.float32(np.inf))) for v in vals[:40]]
+    vals += [top * 1.01, top * 1.1, 2 * p2 * 0.999, -top, -g[1] / 2]
+    rows = []
+    vals = np.array(vals, dtype=np.float64)
+    for i in range(0, len(vals), 31):
+        chunk = list(vals[i:i + 31])
+        chunk = (chunk + [0.0] * 31)[:31] + [p2]            # pins the scale byte at the type's 2^emax
+        rows.append(chunk)
+    rows = [r for r in rows]
+    for scale in (2.0 ** -100, 2.0 ** 60):
+        rows.append([v * scale for v in rows[0]])
+    rows.append([0.0] * 32)
+    r = [1.0] * 32
+    r[5] = np.nan
+    rows.append(r)
+    r = [1.0] * 32
+    r[9] = np.inf
+    rows.append(r)
+    rows.append([3e38] * 16 + [1e-39] * 16)
+    x = np.array(rows, dtype=np.float32)
+    if len(x) % 2:
+        x = np.concatenate([x, np.zeros((1, 32), np.float32)])
+    return x.reshape(-1, 64)
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_quantize_elements_adversarial(elem, rounding):
+    need_gpu()
+    x = _adversarial(elem)
+    banner(f"quantize {elem} adversarial {rounding}")
+    q = mx.quantize(to_dev(x), elem=elem, rounding=rounding, seed=77)
+    oc, os_ = oracle.quantize(x, elem=elem, rounding=rounding, seed=77)
+    codes_equal(host(q.scales), os_, "scales")
+    codes_equal(host(q.codes), oc, "codes")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("block", ["1d", "2d"])
+def test_dequantize_elements(elem, block):
+    """Random code bytes (NaN and Inf codes included) and scales (the NaN
+    scale included), decoded bit-exactly to float32 and to bf16 (RNE)."""
+    need_gpu()
+    rng = np.random.default_rng(11 + ELEMS.index(elem) + 4 * (block == "2d"))
+    R, K = 64, 192
+    cb = K * el.elem_bits(elem) // 8
+    codes = rng.integers(0, 256, (R, cb), dtype=np.uint8)
+    srows = R // 32 if block == "2d" else R
+    scales = rng.integers(100, 150, (srows, K // 32), dtype=np.uint8)
+    scales[0, 1] = 0xFF
+    q = mx.empty_mx(R, K, block, elem=elem)
+    q.codes.copy_(to_dev(codes))
+    q.scales.copy_(to_dev(scales))
+    banner(f"dequantize {elem} {block}")
+    got = host(mx.dequantize(q, torch.float32))
+    ref = oracle.dequantize(codes, scales, block, elem=elem)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    gb = host(mx.dequantize(q, torch.bfloat16).view(torch.int16)).astype(np.int64) & 0xFFFF
+    rb = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().astype(np.int64) & 0xFFFF
+    assert np.array_equal(gb[ok], rb[ok])
+
+
+def _finite_codes(rng, elem, shape):
+    if elem == "e2m1":
+        return rng.integers(0, 16, size=shape)
+    e, m, top = el.ELEMS[elem]
+    return rng.integers(0, top + 1, size=shape) | (rng.integers(0, 2, size=shape) << (e + m))
+
+
+def _pack(codes, elem):
+    return oracle.pack_nibbles(codes) if elem == "e2m1" else el.pack(codes, elem)
+
+
+def _operand(rng, rows, K, elem, block="1d"):
+    codes = _pack(_finite_codes(rng, elem, (rows, K)), elem)
+    srows = rows // 32 if block == "2d" else rows
+    scales = rng.integers(115, 140, (srows, K // 32), dtype=np.uint8)
+    q = mx.empty_mx(rows, K, block, elem=elem)
+    q.codes.copy_(to_dev(codes))
+    q.scales.copy_(to_dev(scales))
+    return q, codes, scales
+
+
+GEMM_CASES = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e4m3", "e2m1"),
+              ("e2m1", "e5m2"), ("e2m3", "e4m3"), ("e3m2", "e2m1")]
+
+
+@pytest.mark.parametrize("fa,fb", GEMM_CASES)
+@pytest.mark.parametrize("M,N,K,b_block,out", [(200, 136, 416, "1d", torch.float32),
+                                               (96, 160, 96, "2d", torch.bfloat16)])
+def test_gemm_elements(fa, fb, M, N, K, b_block, out):
+    """Mixed and uniform element types on ragged shapes (rows, columns and K
+    not multiples of the 128 tile), 1-D and 2-D B scales, float32 and bf16
+    outputs."""
+    need_gpu()
+    rng = np.random.default_rng(zlib.crc32(f"{fa}{fb}{M}{N}{K}".encode()))
+    qa, ac, as_ = _operand(rng, M, K, fa)
+    qb, bc, bs = _operand(rng, N, K, fb, b_block)
+    banner(f"gemm {fa} x {fb} M={M} N={N} K={K} {b_block} {out}")
+    c = host(mx.gemm(qa, qb, out).float()).astype(np.float64)
+    ref, bound = oracle.gemm_ref(ac, as_, bc, bs, "1d", b_block, a_elem=fa, b_elem=fb)
+    av = oracle.gemm.dequant_f64(ac, as_, fa)
+    bv = oracle.gemm.dequant_f64(bc, bs, fb, b_block)
+    tol = 1e-5 * bound + mx_group_bound(av, bv)
+    if out == torch.bfloat16:
+        tol = tol + bf16_half_ulp(np.maximum(np.abs(c), np.abs(ref)))
+    err = np.abs(c - ref)
+    assert np.all(err <= tol), float(np.max(err / tol))
+
+
+def test_gemm_mxfp8_end_to_end():
+    """MXFP8 (E4M3) activations times MXFP8 weights quantized on the GPU (the
+    weights along dim 0), 2048 x 1024 x 2880, against the oracle on sampled
+    rows and columns."""
+    need_gpu()
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2048, 2880)).astype(np.float32)
+    w = (rng.standard_normal((2880, 1024)) * 0.02).astype(np.float32)
+    xt, wt = torch.from_numpy(x).to(torch.bfloat16), torch.from_numpy(w).to(torch.bfloat16)
+    banner("gemm mxfp8 end to end")
+    qx = mx.quantize(xt.cuda(), elem="e4m3")
+    qw = mx.quantize(wt.cuda(), axis="dim0", elem="e4m3")
+    y = host(mx.gemm(qx, qw, torch.float32)).astype(np.float64)
+    rows = np.sort(rng.choice(2048, 32, replace=False))
+    cols = np.sort(rng.choice(1024, 32, replace=False))
+    xc, xs = oracle.quantize(xt.float().numpy()[rows], elem="e4m3")
+    wc, ws = oracle.quantize(wt.float().numpy()[:, cols], axis="dim0", elem="e4m3")
+    ref, bound = oracle.gemm_ref(xc, xs, wc, ws, a_elem="e4m3", b_elem="e4m3")
+    tol = 1e-5 * bound + mx_group_bound(oracle.gemm.dequant_f64(xc, xs, "e4m3"),
+                                        oracle.gemm.dequant_f64(wc, ws, "e4m3"))
+    assert np.all(np.abs(y[np.ix_(rows, cols)] - ref) <= tol)

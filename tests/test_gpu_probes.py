@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import banner, need_gpu, probe_lib, save_npz
+from gpu_util import banner, mx_group_bound, need_gpu, probe_lib, save_npz
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,84 @@ def test_mfma_scale_32x32x64_layout(opsel2):
             got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = raw[l, r]
     save_npz(f"probe_mfma32_{opsel2}.npz", a=a, b=b, a_sc=a_sc, b_sc=b_sc, raw=raw, expect=expect)
     _close(got, expect, a, a_sc, b, b_sc)
+
+
+_FMT = {"e4m3": 0, "e5m2": 1, "e2m3": 2, "e3m2": 3, "e2m1": 4}
+
+
+def _finite_codes(rng, elem, shape):
+    """Random finite codes of an element type (no NaN/Inf encodings)."""
+    if elem == "e2m1":
+        return rng.integers(0, 16, size=shape)
+    e, m, top = oracle.elements.ELEMS[elem]
+    mag = rng.integers(0, top + 1, size=shape)
+    return mag | (rng.integers(0, 2, size=shape) << (e + m))
+
+
+def _pack_row_bytes(codes, elem):
+    if elem == "e2m1":
+        return oracle.pack_nibbles(codes)
+    return oracle.elements.pack(codes, elem)
+
+
+def _fmt_lane_regs(codes, elem):
+    """Per-lane 8 x int32 registers of row l % 32, g = l // 32, taken from the
+    operand's storage bytes: FP4 and FP6, the bytes of K-block g (elements
+    [32g, 32g+32): 16 or 24 bytes); FP8, two 16-element halves, elements
+    [16g, 16g+16) then [32+16g, 48+16g) (2 x 16 bytes); the rest zero."""
+    packed = _pack_row_bytes(codes, elem)            # [32, 64 * bits / 8]
+    bits = 4 if elem == "e2m1" else oracle.elements.elem_bits(elem)
+    regs = np.zeros((64, 32), dtype=np.uint8)
+    for l in range(64):
+        r, g = l % 32, l // 32
+        if bits == 8:
+            regs[l, :16] = packed[r, 16 * g:16 * g + 16]
+            regs[l, 16:32] = packed[r, 32 + 16 * g:48 + 16 * g]
+        else:
+            bpb = 4 * bits                           # bytes per 32 elements
+            regs[l, :bpb] = packed[r, g * bpb:(g + 1) * bpb]
+    return regs.view(np.int32).reshape(64, 8)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e2m3", "e2m3"), ("e3m2", "e3m2"),
+                                   ("e4m3", "e2m1"), ("e2m1", "e3m2"), ("e5m2", "e2m3")])
+def test_mfma_scale_32x32x64_element_formats(fa, fb):
+    """The instruction's FP8 and FP6 operand layout: with the library's storage
+    (FP8: byte i = element i; FP6: element i at bits 6i of the row,
+    little-endian; FP4: two per byte, low nibble first) a lane of K-half g
+    takes, for FP8, the 16-element halves [16g, 16g+16) and [32+16g, 48+16g),
+    for FP6 and FP4 the whole block [32g, 32g+32); its scale byte is that of
+    K-block g either way.  The result equals the oracle's reference within the
+    instruction's internal precision (mx_group_bound), mixed formats included."""
+    need_gpu()
+    lib = probe_lib()
+    rng = np.random.default_rng(_FMT[fa] * 10 + _FMT[fb])
+    a = _finite_codes(rng, fa, (32, 64))
+    b = _finite_codes(rng, fb, (32, 64))
+    a_sc = rng.integers(120, 135, size=(32, 2)).astype(np.uint8)
+    b_sc = rng.integers(120, 135, size=(32, 2)).astype(np.uint8)
+    sa = np.array([a_sc[l % 32, l // 32] for l in range(64)], dtype=np.int32)
+    sb = np.array([b_sc[l % 32, l // 32] for l in range(64)], dtype=np.int32)
+    ar = torch.from_numpy(_fmt_lane_regs(a, fa)).cuda()
+    br = torch.from_numpy(_fmt_lane_regs(b, fb)).cuda()
+    out = torch.zeros(64 * 16, dtype=torch.float32, device="cuda")
+    banner(f"mfma 32x32x64 formats {fa} x {fb}")
+    assert lib.probe_mfma_scale_32x32x64_fmt(ar.data_ptr(), br.data_ptr(), torch.from_numpy(sa).cuda().data_ptr(),
+                                             torch.from_numpy(sb).cuda().data_ptr(), out.data_ptr(),
+                                             _FMT[fa], _FMT[fb]) == 0
+    torch.cuda.synchronize()
+    raw = out.cpu().numpy().reshape(64, 16)
+    got = np.zeros((32, 32))
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + (r % 4), l % 32] = raw[l, r]
+    ref, bound = oracle.gemm_ref(_pack_row_bytes(a, fa), a_sc, _pack_row_bytes(b, fb), b_sc,
+                                 a_elem=fa, b_elem=fb)
+    save_npz(f"probe_mfma_fmt_{fa}_{fb}.npz", raw=raw, ref=ref)
+    av = oracle.gemm.dequant_f64(_pack_row_bytes(a, fa), a_sc, fa)
+    bv = oracle.gemm.dequant_f64(_pack_row_bytes(b, fb), b_sc, fb)
+    tol = 64 * 2.0 ** -24 * bound + mx_group_bound(av, bv)
+    assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) / tol))
 
 
 def test_mfma_scale_16x16x128_layout():
