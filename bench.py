@@ -18,9 +18,10 @@ input (shapes of the GPT-OSS-20B-sized workloads):
 GEMM flops over the step time, quantizers included); per-kernel times, GB/s
 and TFLOP/s are reported alongside, and `roofline` covers the dominant kernel.
 `next_rows` times, outside the step, the dgrad product that reuses the forward
-weight: the exact transpose of W quantized along dim 0 in 32x32 tiles, dY
-16384 x 5760 quantized along its last dim (stochastic rounding), and the GEMM
--> bf16 16384 x 2880.  Prints one JSON line.
+weight (the exact transpose of W quantized along dim 0 in 32x32 tiles, dY
+16384 x 5760 quantized along its last dim with stochastic rounding, and the
+GEMM -> bf16 16384 x 2880) and the dense fprop shape with MXFP8 (E4M3) and
+MXFP6 (E2M3) operands.  Prints one JSON line.
 """
 import argparse
 import hashlib
@@ -40,15 +41,16 @@ import workloads  # noqa: E402
 
 METRIC = "MXFP4 GEMM TFLOPS (dense + MoE grouped) and quantize GB/s, % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 (and MXFP6) matrix peak
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense MXFP8 matrix peak
 SRC_DIR = os.path.join(ROOT, "mxfp4_microscaling_quantization_mx_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def quant_bytes(rows, cols, in_bytes=2):
+def quant_bytes(rows, cols, in_bytes=2, out_bits=4):
     """Algorithmic bytes of one quantize: read the source, write codes + scales."""
     n = rows * cols
-    return n * in_bytes + n // 2 + n // 32
+    return n * in_bytes + n * out_bits // 8 + n // 32
 
 
 def gather_quant_bytes(src_rows, out_rows, cols, in_bytes=2):
@@ -117,6 +119,13 @@ class Workload:
         self.d_qwt = mx.empty_mx(2880, 5760, "2d", device=dev)
         self.d_qdy = mx.empty_mx(16384, 5760, device=dev)
         self.d_dx = torch.empty((16384, 2880), dtype=torch.bfloat16, device=dev)
+        # the dense fprop shape with MXFP8 (E4M3) and MXFP6 (E2M3) operands
+        self.e8_qx = mx.empty_mx(16384, 2880, device=dev, elem="e4m3")
+        self.e8_qw = mx.empty_mx(5760, 2880, device=dev, elem="e4m3")
+        self.e6_qx = mx.empty_mx(16384, 2880, device=dev, elem="e2m3")
+        self.e6_qw = mx.empty_mx(5760, 2880, device=dev, elem="e2m3")
+        self.e_y = torch.empty((16384, 5760), dtype=torch.bfloat16, device=dev)
+        mx.quantize(self.fw, axis="dim0", out=self.e6_qw)
 
     # each entry: (name, callable, kind, algorithmic amount)
     def kernels(self):
@@ -159,6 +168,14 @@ class Workload:
              "hbm", quant_bytes(16384, 5760)),
             ("dgrad_gemm", lambda: mx.gemm(self.d_qdy, self.d_qwt, out=self.d_dx), "mfma",
              2 * 16384 * 2880 * 5760),
+            ("mxfp8_quantize_x", lambda: mx.quantize(self.fx, out=self.e8_qx), "hbm",
+             quant_bytes(16384, 2880, out_bits=8)),
+            ("mxfp8_quantize_w", lambda: mx.quantize(self.fw, axis="dim0", out=self.e8_qw), "hbm",
+             quant_bytes(2880, 5760, out_bits=8)),
+            ("mxfp8_gemm", lambda: mx.gemm(self.e8_qx, self.e8_qw, out=self.e_y), "mfma8", 2 * 16384 * 5760 * 2880),
+            ("mxfp6_quantize_x", lambda: mx.quantize(self.fx, out=self.e6_qx), "hbm",
+             quant_bytes(16384, 2880, out_bits=6)),
+            ("mxfp6_gemm", lambda: mx.gemm(self.e6_qx, self.e6_qw, out=self.e_y), "mfma", 2 * 16384 * 5760 * 2880),
         ]
 
 
@@ -167,6 +184,8 @@ def rates(name, kind, amount, avg_ms):
         rate = amount / (avg_ms * 1e-3) / 1e9
         return {"us": avg_ms * 1e3, "GB/s": rate, "frac_hbm": rate / HBM_PEAK_GBS, "bytes": amount}
     rate = amount / (avg_ms * 1e-3) / 1e12
+    if kind == "mfma8":          # MXFP8 operands: half the FP4/FP6 matrix rate
+        return {"us": avg_ms * 1e3, "TFLOP/s": rate, "frac_fp8": rate / FP8_PEAK_TFLOPS, "flop": amount}
     return {"us": avg_ms * 1e3, "TFLOP/s": rate, "frac_fp4": rate / FP4_PEAK_TFLOPS, "flop": amount}
 
 
