@@ -438,9 +438,9 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(MxOperand A, MxOperand B, 
 
 // ---------------------------------------------------------------- other element types
 // The same scaled MFMA with FP8 or FP6 operands (MXFP8, MXFP6; either operand
-// may be any MX element type): a 128x128 tile per 4-wave workgroup, 64x64 per
-// wave, staged through LDS per 128-deep K stage in 8-byte units (an FP6 block
-// is 24 bytes).  Operand registers per lane and 64-deep step (the
+// may be any MX element type): a 256x256 tile per 8-wave workgroup (64x128 per
+// wave), or 128x128 per 4 waves for small problems, staged through LDS per
+// 128-deep K stage in 16-byte units.  Operand registers per lane and 64-deep step (the
 // instruction's layout, checked by the probe tests): FP4 and FP6 take K-block
 // l/32 of the step whole (16 or 24 bytes); FP8 takes the 16-element halves
 // [16g, 16g+16) and [32+16g, 48+16g), g = l/32 (2 x 16 bytes).  Scale bytes are
@@ -453,28 +453,48 @@ constexpr int mfma_fmt() {
   else return ElemT<F>::MFMA;
 }
 
-// Stage rows [r0, r0 + 128) x K-stage k0 of an operand of element type F:
-// codes into lds (row pitch `pitch` bytes), scale words into lds_scales;
-// bytes past K or rows past `rows` are zeros, their scales 1.0.
-template <int F>
-__device__ __forceinline__ void stage_mx(const MxOperand& op, bool two_d, int64_t r0, int64_t rows, int64_t k0,
-                                         int64_t K, uint8_t* lds, int pitch, uint32_t* lds_scales, int tid,
-                                         int stid) {
-  constexpr int RB = 128 * elem_bits<F>() / 8;   // code bytes per row per stage
-  constexpr int U = RB / 8;
+// One stage (ROWS rows x 128 K-elements) of an operand of element type F held
+// in registers between its global fetch and its LDS store, so that the next
+// stage's loads are in flight while the current one is multiplied: N 16-byte
+// units per thread of a THREADS-thread workgroup (a row stage is RB bytes)
+// and, for threads stid in [0, ROWS), the row's word of 4 scale bytes.
+template <int F, int ROWS, int THREADS>
+struct MxStage {
+  static constexpr int RB = 128 * elem_bits<F>() / 8;
+  static constexpr int U = RB / 16;
+  static constexpr int N = ROWS * U / THREADS;
+  static_assert(ROWS * U % THREADS == 0, "whole units per thread");
+  uint4 v[N];
+  uint32_t sc;
+};
+
+// Bytes past K or rows past `rows` read as zeros and their scales as 1.0 (an
+// FP6 row may end half-way through a 16-byte unit).
+template <int F, int ROWS, int THREADS>
+__device__ __forceinline__ void fetch_mx(MxStage<F, ROWS, THREADS>& f, const MxOperand& op, bool two_d, int64_t r0,
+                                         int64_t rows, int64_t k0, int64_t K, int stid) {
+  using S = MxStage<F, ROWS, THREADS>;
   const int64_t kbytes = K * elem_bits<F>() / 8;
   const int64_t kb0 = k0 * elem_bits<F>() / 8;
 #pragma unroll
-  for (int it = 0; it < U / 2; ++it) {
-    const int id = tid + 256 * it;
-    const int r = id / U, u = id - r * U;
-    const int64_t gr = r0 + r;
-    uint2 v = make_uint2(0u, 0u);
-    if (gr < rows && kb0 + 8 * u < kbytes)
-      v = *reinterpret_cast<const uint2*>(op.codes + gr * op.ld_codes + kb0 + 8 * u);
-    *reinterpret_cast<uint2*>(lds + r * pitch + 8 * u) = v;
+  for (int it = 0; it < S::N; ++it) {
+    const int id = threadIdx.x + THREADS * it;
+    const int r = id / S::U, u = id - r * S::U;
+    const int64_t gr = r0 + r, off = kb0 + 16 * u;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (gr < rows) {
+      const uint8_t* p = op.codes + gr * op.ld_codes + off;
+      if (off + 16 <= kbytes) {
+        v = *reinterpret_cast<const uint4*>(p);
+      } else if (off < kbytes) {
+        const uint2 h = *reinterpret_cast<const uint2*>(p);
+        v = make_uint4(h.x, h.y, 0u, 0u);
+      }
+    }
+    f.v[it] = v;
   }
-  if (stid >= 0 && stid < 128) {
+  f.sc = 0x7F7F7F7Fu;
+  if (stid >= 0 && stid < ROWS) {
     const int64_t gr = r0 + stid;
     uint32_t w = 0;
 #pragma unroll
@@ -484,8 +504,21 @@ __device__ __forceinline__ void stage_mx(const MxOperand& op, bool two_d, int64_
       if (gr < rows && kb * 32 < K) sc = op.scales[(two_d ? (gr >> 5) : gr) * op.ld_scales + kb];
       w |= sc << (8 * j);
     }
-    lds_scales[stid] = w;
+    f.sc = w;
   }
+}
+
+template <int F, int ROWS, int THREADS>
+__device__ __forceinline__ void put_mx(const MxStage<F, ROWS, THREADS>& f, uint8_t* lds, int pitch,
+                                       uint32_t* lds_scales, int stid) {
+  using S = MxStage<F, ROWS, THREADS>;
+#pragma unroll
+  for (int it = 0; it < S::N; ++it) {
+    const int id = threadIdx.x + THREADS * it;
+    const int r = id / S::U, u = id - r * S::U;
+    *reinterpret_cast<uint4*>(lds + r * pitch + 16 * u) = f.v[it];
+  }
+  if (stid >= 0 && stid < ROWS) lds_scales[stid] = f.sc;
 }
 
 // This lane's operand registers for 64-deep step ks from its LDS row.
@@ -505,51 +538,67 @@ __device__ __forceinline__ v8i read_mx(const uint8_t* row, int ks, int hi) {
   }
 }
 
-template <int FA, int FB>
-__global__ __launch_bounds__(256) void k_gemm_mx(MxOperand A, MxOperand B, int64_t M, int64_t N, int64_t K, void* C,
-                                                 int64_t ldc, int a_2d, int b_2d, int out_bf16) {
+// Tile BM x BN per workgroup; each wave owns TI x TJ MFMA tiles of 32x32
+// (waves laid out BM/(32 TI) x BN/(32 TJ)).
+template <int FA, int FB, int BM_, int BN_, int TI, int TJ>
+__global__ __launch_bounds__(64 * (BM_ / (32 * TI)) * (BN_ / (32 * TJ))) void k_gemm_mx(
+    MxOperand A, MxOperand B, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int a_2d, int b_2d,
+    int out_bf16) {
+  constexpr int WN = BN_ / (32 * TJ);
+  constexpr int THREADS = 64 * (BM_ / (32 * TI)) * WN;
+  static_assert(THREADS >= BM_ + BN_, "one scale row per thread");
   constexpr int PA = 128 * elem_bits<FA>() / 8 + 16, PB = 128 * elem_bits<FB>() / 8 + 16;
   constexpr int FMA = mfma_fmt<FA>(), FMB = mfma_fmt<FB>();
-  __shared__ __attribute__((aligned(16))) uint8_t la[128 * PA];
-  __shared__ __attribute__((aligned(16))) uint8_t lb[128 * PB];
-  __shared__ uint32_t lsa[128], lsb[128];
-  const int64_t m0 = (int64_t)blockIdx.y * 128, n0 = (int64_t)blockIdx.x * 128;
+  __shared__ __attribute__((aligned(16))) uint8_t la[BM_ * PA];
+  __shared__ __attribute__((aligned(16))) uint8_t lb[BN_ * PB];
+  __shared__ uint32_t lsa[BM_], lsb[BN_];
+  const int64_t m0 = (int64_t)blockIdx.y * BM_, n0 = (int64_t)blockIdx.x * BN_;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
   const int l32 = lane & 31, hi = lane >> 5;
-  v16f acc[2][2];
+  v16f acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  MxStage<FA, BM_, THREADS> fa;
+  MxStage<FB, BN_, THREADS> fb;
+  if (K > 0) {
+    fetch_mx(fa, A, a_2d != 0, m0, M, 0, K, tid);
+    fetch_mx(fb, B, b_2d != 0, n0, N, 0, K, tid - BM_);
+  }
   for (int64_t k0 = 0; k0 < K; k0 += 128) {
-    stage_mx<FA>(A, a_2d != 0, m0, M, k0, K, la, PA, lsa, tid, tid);
-    stage_mx<FB>(B, b_2d != 0, n0, N, k0, K, lb, PB, lsb, tid, tid - 128);
+    put_mx(fa, la, PA, lsa, tid);
+    put_mx(fb, lb, PB, lsb, tid - BM_);
     __syncthreads();
+    if (k0 + 128 < K) {                 // the next stage's loads fly during this stage's MFMAs
+      fetch_mx(fa, A, a_2d != 0, m0, M, k0 + 128, K, tid);
+      fetch_mx(fb, B, b_2d != 0, n0, N, k0 + 128, K, tid - BM_);
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      v8i a[2], b[2];
-      int sa[2], sb[2];
+      v8i a[TI], b[TJ];
+      int sa[TI], sb[TJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + l32;
+      for (int i = 0; i < TI; ++i) {
+        const int r = wm * 32 * TI + i * 32 + l32;
         a[i] = read_mx<FA>(la + r * PA, ks, hi);
         sa[i] = (int)(lsa[r] >> (8 * hi));
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + l32;
+      for (int j = 0; j < TJ; ++j) {
+        const int r = wn * 32 * TJ + j * 32 + l32;
         b[j] = read_mx<FB>(lb + r * PB, ks, hi);
         sb[j] = (int)(lsb[r] >> (8 * hi));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
           if (ks == 0)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FMA, FMB, 0,
                                                                          sa[i], 0, sb[j]);
@@ -562,14 +611,14 @@ __global__ __launch_bounds__(256) void k_gemm_mx(MxOperand A, MxOperand B, int64
   }
   // lane holds column l32; register r holds row 8*(r/4) + 4*hi + r%4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + l32;
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t col = n0 + wn * 32 * TJ + j * 32 + l32;
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int64_t row = m0 + wm * 32 * TI + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
         if (row < M) {
           if (out_bf16)
             static_cast<uint16_t*>(C)[row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
@@ -580,11 +629,19 @@ __global__ __launch_bounds__(256) void k_gemm_mx(MxOperand A, MxOperand B, int64
     }
 }
 
+// 256x256 tiles (8 waves of 64x128) when both dimensions fill them, else
+// 128x128 (4 waves of 64x64).
 template <int FA, int FB>
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)((a.M + 127) / 128));
-  hipLaunchKernelGGL((k_gemm_mx<FA, FB>), grid, dim3(256), 0, st, a.A, a.B, a.M, a.N, a.K, a.C, a.ldc,
-                     (int)a.a_2d, (int)a.b_2d, (int)a.out_bf16);
+  if (a.M >= 256 && a.N >= 256) {
+    const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)((a.M + 255) / 256));
+    hipLaunchKernelGGL((k_gemm_mx<FA, FB, 256, 256, 2, 4>), grid, dim3(512), 0, st, a.A, a.B, a.M, a.N, a.K, a.C,
+                       a.ldc, (int)a.a_2d, (int)a.b_2d, (int)a.out_bf16);
+  } else {
+    const dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)((a.M + 127) / 128));
+    hipLaunchKernelGGL((k_gemm_mx<FA, FB, 128, 128, 2, 2>), grid, dim3(256), 0, st, a.A, a.B, a.M, a.N, a.K, a.C,
+                       a.ldc, (int)a.a_2d, (int)a.b_2d, (int)a.out_bf16);
+  }
   return hipGetLastError();
 }
 

@@ -153,16 +153,17 @@ def _operand(rng, rows, K, elem, block="1d"):
 
 
 GEMM_CASES = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e4m3", "e2m1"),
-              ("e2m1", "e5m2"), ("e2m3", "e4m3"), ("e3m2", "e2m1")]
+              ("e2m1", "e5m2"), ("e2m3", "e4m3"), ("e3m2", "e2m1"), ("e4m3", "e3m2")]
 
 
 @pytest.mark.parametrize("fa,fb", GEMM_CASES)
 @pytest.mark.parametrize("M,N,K,b_block,out", [(200, 136, 416, "1d", torch.float32),
-                                               (96, 160, 96, "2d", torch.bfloat16)])
+                                               (96, 160, 96, "2d", torch.bfloat16),
+                                               (300, 544, 224, "2d", torch.bfloat16)])
 def test_gemm_elements(fa, fb, M, N, K, b_block, out):
     """Mixed and uniform element types on ragged shapes (rows, columns and K
-    not multiples of the 128 tile), 1-D and 2-D B scales, float32 and bf16
-    outputs."""
+    not multiples of the tile: the 128x128 kernel below 256 rows or columns,
+    the 256x256 one above), 1-D and 2-D B scales, float32 and bf16 outputs."""
     need_gpu()
     rng = np.random.default_rng(zlib.crc32(f"{fa}{fb}{M}{N}{K}".encode()))
     qa, ac, as_ = _operand(rng, M, K, fa)
