@@ -163,8 +163,8 @@ typedef struct {
  *   exponent of the type's largest power of two (8 E4M3, 15 E5M2, 2 E2M3,
  *   4 E3M2, per §Conversion rules), elements round to nearest even (or
  *   stochastically, the same 16-bit draws) and saturate at the largest
- *   normal; the round-up rule uses the largest normal in place of 6.  1-D
- *   blocks only (2-D returns MX_ERR_UNSUPPORTED); ld_codes >= K*bits/8.
+ *   normal; the round-up rule uses the largest normal in place of 6.  1-D or
+ *   2-D blocks, either axis; ld_codes >= K*bits/8.
  */
 mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
                       const mx_quant_cfg* cfg, const mx_tensor* out, void* stream);

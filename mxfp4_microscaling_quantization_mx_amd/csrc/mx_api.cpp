@@ -101,8 +101,6 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   if (out->block != cfg->block) return fail(MX_ERR_INVALID_ARG, "mx_quantize: out->block differs from cfg->block");
   mx_status st = check_tensor(out, "mx_quantize: out");
   if (st != MX_OK) return st;
-  if (out->elem != MX_ELEM_E2M1 && cfg->block != MX_BLOCK_1D)
-    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: 2-D blocks are built for MXFP4 only");
   if (R == 0 || C == 0) return MX_OK;
   if (!src) return fail(MX_ERR_INVALID_ARG, "mx_quantize: null src");
   if (ld_src < C) return fail(MX_ERR_INVALID_ARG, "mx_quantize: ld_src=%lld < C=%lld", (long long)ld_src, (long long)C);

@@ -138,7 +138,7 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
 // software (elem_code: RNE, or SR with the same Philox draws as E2M1), then
 // packed: FP8 one byte per element (8 words), FP6 element e at bits 6e of the
 // block's 192 bits (6 words).  Returns the scale byte.
-template <int ELEM, bool RHT, bool SR>
+template <int ELEM, bool RHT, bool SR, bool TWO_D = false>
 __device__ __forceinline__ uint32_t quantize_block32_elem(float x[32], uint32_t out[8], uint64_t p0, uint64_t seed,
                                                           uint64_t offset, int scale_mode) {
   using T = ElemT<ELEM>;
@@ -151,6 +151,10 @@ __device__ __forceinline__ uint32_t quantize_block32_elem(float x[32], uint32_t 
     m = __float_as_uint(c * __uint_as_float(m));
 #pragma unroll
     for (int i = 0; i < 32; ++i) x[i] = c * x[i];
+  }
+  if (TWO_D) {
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
   }
   const uint32_t s = elem_scale_code<ELEM>(m, scale_mode == 1);
 #pragma unroll
@@ -214,7 +218,7 @@ __device__ __forceinline__ uint32_t quantize_store(float x[32], uint8_t* dst, ui
   if constexpr (ELEM == 0) {
     s = quantize_block32<RHT, SR, TWO_D>(x, w, p0, seed, offset, scale_mode);
   } else {
-    s = quantize_block32_elem<ELEM, RHT, SR>(x, w, p0, seed, offset, scale_mode);
+    s = quantize_block32_elem<ELEM, RHT, SR, TWO_D>(x, w, p0, seed, offset, scale_mode);
   }
   store_block<ELEM>(dst, w);
   return s;
@@ -261,7 +265,7 @@ struct TileShape {
   static constexpr int LD = 129;   // LDS row pitch in floats (bank-conflict free reads)
 };
 
-template <bool BF16, bool RHT, bool SR>
+template <bool BF16, bool RHT, bool SR, int ELEM>
 __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src, int64_t R,
                                                     int64_t C, int64_t ld_src,
                                                     uint8_t* __restrict__ codes, int64_t ld_codes,
@@ -310,12 +314,15 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
     if (RHT) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((mask >> i) & 1u) << 31));
   }
   // every lane takes part in the tile's amax (lanes past the edges hold zeros)
-  uint32_t packed[4];
-  const uint32_t s =
-      quantize_block32<RHT, SR, true>(x, packed, (uint64_t)(orow * K + kb * 32), seed, offset, scale_mode);
+  uint32_t packed[8];
+  uint32_t s;
+  if constexpr (ELEM == 0)
+    s = quantize_block32<RHT, SR, true>(x, packed, (uint64_t)(orow * K + kb * 32), seed, offset, scale_mode);
+  else
+    s = quantize_block32_elem<ELEM, RHT, SR, true>(x, packed, (uint64_t)(orow * K + kb * 32), seed, offset,
+                                                   scale_mode);
   if (!valid) return;
-  *reinterpret_cast<uint4*>(codes + orow * ld_codes + kb * 16) =
-      make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  store_block<ELEM>(codes + orow * ld_codes + kb * block_bytes<ELEM>(), packed);
   if ((orow & 31) == 0) scales[(orow >> 5) * ld_scales + kb] = (uint8_t)s;
 }
 
@@ -379,12 +386,12 @@ hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool BF16>
+template <bool BF16, int ELEM>
 hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
   using S = TileShape;
   dim3 grid((unsigned)((a.C + S::TC - 1) / S::TC), (unsigned)((a.R + S::TR - 1) / S::TR));
 #define MX_TILE(RHT_, SR_)                                                                   \
-  hipLaunchKernelGGL((k_quant_tile<BF16, RHT_, SR_>), grid, dim3(256), 0, st,                \
+  hipLaunchKernelGGL((k_quant_tile<BF16, RHT_, SR_, ELEM>), grid, dim3(256), 0, st,          \
                      a.src, a.R, a.C, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales,  \
                      a.mask, a.seed, a.offset, a.scale_mode)
   if (a.rht) {
@@ -414,11 +421,20 @@ hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// The other element types: 1-D blocks along either axis (validated by the
-// caller).
+// Kernel choice for one element type: gather and 1-D last-dim blocks by rows,
+// dim 0 by columns (1-D or 2-D), 2-D last-dim tiles through LDS.
 template <int ELEM>
 hipError_t launch_quantize_elem(const QuantArgs& a, hipStream_t st) {
-  if (a.dim0) return a.bf16 ? launch_cols<false, true, ELEM>(a, st) : launch_cols<false, false, ELEM>(a, st);
+  if (a.gather) {
+    if constexpr (ELEM == 0)
+      return a.bf16 ? launch_rows_1d<true, true, 0>(a, st) : launch_rows_1d<false, true, 0>(a, st);
+    return hipErrorInvalidValue;                 // validated by the caller: MXFP4 only
+  }
+  if (a.dim0) {
+    if (a.two_d) return a.bf16 ? launch_cols<true, true, ELEM>(a, st) : launch_cols<true, false, ELEM>(a, st);
+    return a.bf16 ? launch_cols<false, true, ELEM>(a, st) : launch_cols<false, false, ELEM>(a, st);
+  }
+  if (a.two_d) return a.bf16 ? launch_tile<true, ELEM>(a, st) : launch_tile<false, ELEM>(a, st);
   return a.bf16 ? launch_rows_1d<true, false, ELEM>(a, st) : launch_rows_1d<false, false, ELEM>(a, st);
 }
 
@@ -431,16 +447,8 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
     case 2: return launch_quantize_elem<2>(a, st);
     case 3: return launch_quantize_elem<3>(a, st);
     case 4: return launch_quantize_elem<4>(a, st);
-    default: break;
+    default: return launch_quantize_elem<0>(a, st);
   }
-  if (a.gather) return a.bf16 ? launch_rows_1d<true, true, 0>(a, st) : launch_rows_1d<false, true, 0>(a, st);
-  if (!a.dim0 && !a.two_d)
-    return a.bf16 ? launch_rows_1d<true, false, 0>(a, st) : launch_rows_1d<false, false, 0>(a, st);
-  if (a.dim0) {
-    if (a.two_d) return a.bf16 ? launch_cols<true, true, 0>(a, st) : launch_cols<true, false, 0>(a, st);
-    return a.bf16 ? launch_cols<false, true, 0>(a, st) : launch_cols<false, false, 0>(a, st);
-  }
-  return a.bf16 ? launch_tile<true>(a, st) : launch_tile<false>(a, st);
 }
 
 }  // namespace mx

@@ -117,8 +117,8 @@ def test_transpose_rejects_bad_arguments(lib):
 
 def test_element_types_are_validated(lib):
     """mx_tensor.elem: unknown values are refused everywhere; MXFP8/MXFP6 rows
-    need K*bits/8 bytes; 2-D quantization, the gather, the transpose and the
-    grouped GEMM are MXFP4-only."""
+    need K*bits/8 bytes and 2-D blocks whole 32-row groups; the gather, the
+    transpose and the grouped GEMM are MXFP4-only."""
     cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 0, 0, 0)
     bad = _tensor(32, 64)
     bad.elem = 9
@@ -128,11 +128,11 @@ def test_element_types_are_validated(lib):
     fp8.elem = 1
     st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(cfg), ctypes.byref(fp8), None)
     assert st == mx.MX_ERR_INVALID_ARG and b"strides" in lib.mx_last_error()
-    fp6_2d = _tensor(32, 64, ldc=48, block=1)
+    fp6_2d = _tensor(48, 64, ldc=48, block=1)
     fp6_2d.elem = 3
     cfg2 = mx.QuantCfgC(0, 1, 0, 0, 0, 0, 0, 0)
-    st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(cfg2), ctypes.byref(fp6_2d), None)
-    assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+    st = lib.mx_quantize(ctypes.c_void_p(16), 1, 48, 64, 64, ctypes.byref(cfg2), ctypes.byref(fp6_2d), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"2-D" in lib.mx_last_error()
     fp6 = _tensor(8, 64, ldc=48)
     fp6.elem = 3
     st = lib.mx_quantize_gather(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.c_void_p(16), 8, ctypes.byref(cfg),

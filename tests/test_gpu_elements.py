@@ -47,6 +47,24 @@ def test_quantize_elements(elem, axis, rounding, rht):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("axis", ["last", "dim0"])
+@pytest.mark.parametrize("rounding,rht", [("rne", False), ("sr", True)])
+def test_quantize_elements_2d(elem, axis, rounding, rht):
+    """32x32 tiles (one scale per tile) for every element type, along the
+    last dim (LDS tile kernel) and dim 0 (column kernel), ragged in K."""
+    need_gpu()
+    R, C = (96, 352) if axis == "last" else (224, 96)
+    rng = np.random.default_rng(zlib.crc32(f"2d{elem}{axis}{rounding}".encode()))
+    x = (rng.standard_t(3, (R, C)) * np.exp(rng.uniform(-6, 6, (R, 1)))).astype(np.float32)
+    kw = dict(axis=axis, block="2d", rounding=rounding, rht_mask=0x13579BDF if rht else None, seed=21, offset=2)
+    banner(f"quantize 2d {elem} {axis} {rounding} rht={rht}")
+    q = mx.quantize(to_dev(x), elem=elem, **kw)
+    oc, os_ = oracle.quantize(x, elem=elem, **kw)
+    codes_equal(host(q.scales), os_, "scales")
+    codes_equal(host(q.codes), oc, "codes")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
 @pytest.mark.parametrize("scale_mode", ["round_up", "prescale_3_4"])
 def test_quantize_elements_scale_modes_f32(elem, scale_mode):
     need_gpu()
