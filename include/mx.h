@@ -275,7 +275,8 @@ size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  *   B                host struct for expert 0: rows = N, K, block, strides;
  *                    expert e's codes start at B->codes + e*expert_stride_codes
  *                    bytes and its scales at B->scales + e*expert_stride_scales.
- *                    A and B must be MXFP4 (else MX_ERR_UNSUPPORTED).
+ *                    A and B may be any element types (MXFP4 runs on the
+ *                    256x256 pipeline, other types on the C++ kernel).
  *   C                device; [A->rows, N] of c_dtype, row stride ldc.
  */
 mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, int32_t E,

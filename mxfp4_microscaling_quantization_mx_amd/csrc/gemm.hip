@@ -541,18 +541,24 @@ __device__ __forceinline__ v8i read_mx(const uint8_t* row, int ks, int hi) {
 // Tile BM x BN per workgroup; each wave owns TI x TJ MFMA tiles of 32x32
 // (waves laid out BM/(32 TI) x BN/(32 TJ)).
 template <int FA, int FB, int BM_, int BN_, int TI, int TJ>
-__global__ __launch_bounds__(64 * (BM_ / (32 * TI)) * (BN_ / (32 * TJ))) void k_gemm_mx(
-    MxOperand A, MxOperand B, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int a_2d, int b_2d,
-    int out_bf16) {
+constexpr int mx_threads() {
+  return 64 * (BM_ / (32 * TI)) * (BN_ / (32 * TJ));
+}
+
+// The output tile [m0, m0 + BM_) x [n0, n0 + BN_) of C = A B^T (rows past M
+// or N are neither read nor written).
+template <int FA, int FB, int BM_, int BN_, int TI, int TJ>
+__device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand& B, int64_t M, int64_t N,
+                                             int64_t K, int64_t m0, int64_t n0, void* C, int64_t ldc, int a_2d,
+                                             int b_2d, int out_bf16) {
   constexpr int WN = BN_ / (32 * TJ);
-  constexpr int THREADS = 64 * (BM_ / (32 * TI)) * WN;
+  constexpr int THREADS = mx_threads<FA, FB, BM_, BN_, TI, TJ>();
   static_assert(THREADS >= BM_ + BN_, "one scale row per thread");
   constexpr int PA = 128 * elem_bits<FA>() / 8 + 16, PB = 128 * elem_bits<FB>() / 8 + 16;
   constexpr int FMA = mfma_fmt<FA>(), FMB = mfma_fmt<FB>();
   __shared__ __attribute__((aligned(16))) uint8_t la[BM_ * PA];
   __shared__ __attribute__((aligned(16))) uint8_t lb[BN_ * PB];
   __shared__ uint32_t lsa[BM_], lsb[BN_];
-  const int64_t m0 = (int64_t)blockIdx.y * BM_, n0 = (int64_t)blockIdx.x * BN_;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -627,6 +633,86 @@ __global__ __launch_bounds__(64 * (BM_ / (32 * TI)) * (BN_ / (32 * TJ))) void k_
         }
       }
     }
+}
+
+template <int FA, int FB, int BM_, int BN_, int TI, int TJ>
+__global__ __launch_bounds__((mx_threads<FA, FB, BM_, BN_, TI, TJ>())) void k_gemm_mx(
+    MxOperand A, MxOperand B, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc, int a_2d, int b_2d,
+    int out_bf16) {
+  gemm_mx_tile<FA, FB, BM_, BN_, TI, TJ>(A, B, M, N, K, (int64_t)blockIdx.y * BM_, (int64_t)blockIdx.x * BN_, C,
+                                         ldc, a_2d, b_2d, out_bf16);
+}
+
+// Grouped (MoE) form: blockIdx.y is a row-tile slot, mapped to (expert, rows)
+// from the device offsets by one thread, as in the MXFP4 grouped kernel.
+template <int FA, int FB, int BM_, int BN_, int TI, int TJ>
+__global__ __launch_bounds__((mx_threads<FA, FB, BM_, BN_, TI, TJ>())) void k_grouped_gemm_mx(
+    MxOperand A, MxOperand B, int64_t M_cap, int64_t N, int64_t K, const int32_t* __restrict__ offsets, int E,
+    int64_t stride_codes, int64_t stride_scales, void* C, int64_t ldc, int b_2d, int out_bf16) {
+  __shared__ int s_expert, s_row0, s_rows;
+  const int64_t slot = blockIdx.y;
+  if (threadIdx.x == 0) {
+    int64_t acc_tiles = 0;
+    int ex = -1, r0 = 0, nr = 0;
+    for (int e = 0; e < E; ++e) {
+      int64_t lo = offsets[e], hi = offsets[e + 1];
+      lo = lo < 0 ? 0 : (lo > M_cap ? M_cap : lo);
+      hi = hi < lo ? lo : (hi > M_cap ? M_cap : hi);
+      const int64_t tiles = (hi - lo + BM_ - 1) / BM_;
+      if (slot < acc_tiles + tiles) {
+        ex = e;
+        r0 = (int)(lo + (slot - acc_tiles) * BM_);
+        nr = (int)(hi - r0 < BM_ ? hi - r0 : BM_);
+        break;
+      }
+      acc_tiles += tiles;
+    }
+    s_expert = ex;
+    s_row0 = r0;
+    s_rows = nr;
+  }
+  __syncthreads();
+  const int ex = s_expert;
+  if (ex < 0) return;
+  MxOperand Ae = A;
+  Ae.codes = A.codes + (int64_t)s_row0 * A.ld_codes;
+  Ae.scales = A.scales + (int64_t)s_row0 * A.ld_scales;
+  MxOperand Be = B;
+  Be.codes = B.codes + (int64_t)ex * stride_codes;
+  Be.scales = B.scales + (int64_t)ex * stride_scales;
+  void* Ce = out_bf16 ? (void*)(static_cast<uint16_t*>(C) + (int64_t)s_row0 * ldc)
+                      : (void*)(static_cast<float*>(C) + (int64_t)s_row0 * ldc);
+  gemm_mx_tile<FA, FB, BM_, BN_, TI, TJ>(Ae, Be, s_rows, N, K, 0, (int64_t)blockIdx.x * BN_, Ce, ldc, 0, b_2d,
+                                         out_bf16);
+}
+
+template <int FA, int FB>
+hipError_t launch_grouped_gemm_mx(const GroupedGemmArgs& a, hipStream_t st) {
+  if (a.N >= 256) {
+    const int64_t slots = (a.M_cap + 255) / 256 + a.E;
+    const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)slots);
+    hipLaunchKernelGGL((k_grouped_gemm_mx<FA, FB, 256, 256, 2, 4>), grid, dim3(512), 0, st, a.A, a.B, a.M_cap, a.N,
+                       a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, (int)a.b_2d,
+                       (int)a.out_bf16);
+  } else {
+    const int64_t slots = (a.M_cap + 127) / 128 + a.E;
+    const dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)slots);
+    hipLaunchKernelGGL((k_grouped_gemm_mx<FA, FB, 128, 128, 2, 2>), grid, dim3(256), 0, st, a.A, a.B, a.M_cap, a.N,
+                       a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, (int)a.b_2d,
+                       (int)a.out_bf16);
+  }
+  return hipGetLastError();
+}
+
+template <int FA>
+hipError_t launch_grouped_gemm_mx_b(const GroupedGemmArgs& a, hipStream_t st) {
+  switch (a.b_elem) {
+    case 1: return launch_grouped_gemm_mx<FA, 1>(a, st);
+    case 2: return launch_grouped_gemm_mx<FA, 2>(a, st);
+    case 3: return launch_grouped_gemm_mx<FA, 3>(a, st);
+    case 4: return launch_grouped_gemm_mx<FA, 4>(a, st);
+    default: return launch_grouped_gemm_mx<FA, 0>(a, st);
+  }
 }
 
 // 256x256 tiles (8 waves of 64x128) when both dimensions fill them, else
@@ -722,6 +808,15 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st) {
   if (a.M_cap == 0 || a.N == 0) return hipSuccess;
+  if (a.a_elem != 0 || a.b_elem != 0) {
+    switch (a.a_elem) {
+      case 1: return launch_grouped_gemm_mx_b<1>(a, st);
+      case 2: return launch_grouped_gemm_mx_b<2>(a, st);
+      case 3: return launch_grouped_gemm_mx_b<3>(a, st);
+      case 4: return launch_grouped_gemm_mx_b<4>(a, st);
+      default: return launch_grouped_gemm_mx_b<0>(a, st);
+    }
+  }
   const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) && (a.stride_scales % 16 == 0) &&
                      ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
   const bool small = 256 * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&

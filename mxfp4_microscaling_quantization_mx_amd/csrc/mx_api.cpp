@@ -304,8 +304,6 @@ mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, in
   if (st != MX_OK) return st;
   st = check_tensor(B, "mx_grouped_gemm: B");
   if (st != MX_OK) return st;
-  if (A->elem != MX_ELEM_E2M1 || B->elem != MX_ELEM_E2M1)
-    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: MXFP4 operands only");
   if (A->block != MX_BLOCK_1D)
     return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: A must use 1-D blocks (expert boundaries are arbitrary rows)");
   if (A->K != B->K)
@@ -338,6 +336,8 @@ mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, in
   a.C = C;
   a.ldc = ldc;
   a.out_bf16 = c_dtype == MX_DT_BF16;
+  a.a_elem = A->elem;
+  a.b_elem = B->elem;
   return hip_status(mx::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)), "mx_grouped_gemm");
 }
 

@@ -67,6 +67,7 @@ struct GroupedGemmArgs {
   void* C;
   int64_t ldc;
   bool out_bf16;
+  int a_elem = 0, b_elem = 0;  // mx_elem of A and B
 };
 
 struct TransposeArgs {

@@ -77,7 +77,7 @@ def gemm_ref(a_codes, a_scales, b_codes, b_scales, a_block="1d", b_block="1d",
 
 
 def grouped_gemm_ref(a_codes, a_scales, offsets, b_codes, b_scales,
-                     a_block="1d", b_block="2d", rows=None, cols=None):
+                     a_block="1d", b_block="2d", rows=None, cols=None, a_elem="e2m1", b_elem="e2m1"):
     """Reference for the MoE grouped GEMM: rows [off[e], off[e+1]) of A and of
     the output belong to expert e and use B[e] ([E, N, K/2] codes, per-expert
     scales).  rows (sorted or not) / cols restrict the output to a sample."""
@@ -92,7 +92,7 @@ def grouped_gemm_ref(a_codes, a_scales, offsets, b_codes, b_scales,
     for e in np.unique(expert):
         sel = np.nonzero(expert == e)[0]
         r, s = gemm_ref(a_codes, a_scales, b_codes[e], b_scales[e], a_block, b_block,
-                        rows=rows[sel], cols=cols)
+                        rows=rows[sel], cols=cols, a_elem=a_elem, b_elem=b_elem)
         ref[sel] = r
         bound[sel] = s
     return ref, bound

@@ -117,8 +117,8 @@ def test_transpose_rejects_bad_arguments(lib):
 
 def test_element_types_are_validated(lib):
     """mx_tensor.elem: unknown values are refused everywhere; MXFP8/MXFP6 rows
-    need K*bits/8 bytes and 2-D blocks whole 32-row groups; the gather, the
-    transpose and the grouped GEMM are MXFP4-only."""
+    need K*bits/8 bytes and 2-D blocks whole 32-row groups; the gather and
+    the transpose are MXFP4-only; the grouped GEMM checks K for any type."""
     cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 0, 0, 0)
     bad = _tensor(32, 64)
     bad.elem = 9
@@ -144,10 +144,10 @@ def test_element_types_are_validated(lib):
     assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
     a = _tensor(64, 64, ldc=64)
     a.elem = 2
-    b = _tensor(64, 64, block=1)
+    b = _tensor(64, 96, block=1)
     st = lib.mx_grouped_gemm(ctypes.byref(a), ctypes.c_void_p(16), 2, ctypes.byref(b), 0, 0, ctypes.c_void_p(16), 0, 64,
                              None)
-    assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+    assert st == mx.MX_ERR_INVALID_ARG and b"A.K" in lib.mx_last_error()
 
 
 def test_gemm_rejects_bad_arguments(lib):

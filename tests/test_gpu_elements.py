@@ -219,3 +219,40 @@ def test_gemm_mxfp8_end_to_end():
     tol = 1e-5 * bound + mx_group_bound(oracle.gemm.dequant_f64(xc, xs, "e4m3"),
                                         oracle.gemm.dequant_f64(wc, ws, "e4m3"))
     assert np.all(np.abs(y[np.ix_(rows, cols)] - ref) <= tol)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m3", "e3m2"), ("e5m2", "e2m1")])
+@pytest.mark.parametrize("N", [160, 288])
+def test_grouped_gemm_elements(fa, fb, N):
+    """MoE grouped GEMM with MXFP8/MXFP6 operands: empty experts, a one-row
+    expert, experts straddling row tiles, rows past the last offset left
+    untouched; B stacked per expert with 2-D scales."""
+    need_gpu()
+    rng = np.random.default_rng(zlib.crc32(f"g{fa}{fb}{N}".encode()))
+    offsets = np.array([0, 0, 1, 300, 300, 557, 700], dtype=np.int32)
+    E, K, M = len(offsets) - 1, 160, 720
+    ac = _pack(_finite_codes(rng, fa, (M, K)), fa)
+    as_ = rng.integers(118, 136, (M, K // 32), dtype=np.uint8)
+    bc = np.stack([_pack(_finite_codes(rng, fb, (N, K)), fb) for _ in range(E)])
+    bs = rng.integers(118, 136, (E, N // 32, K // 32), dtype=np.uint8)
+    qa = mx.empty_mx(M, K, elem=fa)
+    qa.codes.copy_(to_dev(ac))
+    qa.scales.copy_(to_dev(as_))
+    qb = mx.empty_mx(N, K, "2d", experts=E, elem=fb)
+    qb.codes.copy_(to_dev(bc))
+    qb.scales.copy_(to_dev(bs))
+    y = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    banner(f"grouped gemm {fa} x {fb} N={N}")
+    mx.grouped_gemm(qa, torch.from_numpy(offsets).cuda(), qb, out=y)
+    got = host(y).astype(np.float64)
+    ref, bound = oracle.grouped_gemm_ref(ac, as_, offsets, bc, bs, "1d", "2d", rows=np.arange(700),
+                                         a_elem=fa, b_elem=fb)
+    av = oracle.gemm.dequant_f64(ac[:700], as_[:700], fa)
+    tol = 1e-5 * bound
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            bv = oracle.gemm.dequant_f64(bc[e], bs[e], fb, "2d")
+            tol[lo:hi] += mx_group_bound(av[lo:hi], bv)
+    assert np.all(np.abs(got[:700] - ref) <= tol)
+    assert np.all(got[700:] == 7.0)
