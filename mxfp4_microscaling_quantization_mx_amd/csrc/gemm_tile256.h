@@ -37,11 +37,9 @@
 // and the first read of its result (after the loop).  One barrier per stage,
 // before its last step: every wave has then read the stage's codes, so its
 // slot is refilled with the stage two ahead: its 8 code loads per wave go
-// out one per MFMA of the last step, or (SPLIT) the A half there and the B
-// half in the next stage's first step, so that the load unit never receives
-// a whole stage's loads at once (better for the dense GEMMs; the grouped
-// kernel, whose expert weights come from further away, keeps the earlier
-// issue).
+// out one per MFMA of the last step, or (SPLIT, used by the dense and grouped
+// kernels) the A half there and the B half in the next stage's first step, so
+// that the load unit never receives a whole stage's loads at once.
 //
 // Persistent schedule: one workgroup per CU walks its list of tiles, and the
 // stage sequence runs on across tile boundaries: the first two stages of the
