@@ -224,9 +224,9 @@ mx_status mx_dequantize(const mx_tensor* in, int32_t inverse_rht, uint32_t rht_s
  * input's K stays along the output's rows.
  *
  *   in    host struct of device buffers; block must be MX_BLOCK_2D ([R, C],
- *         R and C multiples of 32), MXFP4.
+ *         R and C multiples of 32); any element type.
  *   out   host struct of device buffers; block MX_BLOCK_2D, rows == in->K and
- *         K == in->rows; must not overlap in.
+ *         K == in->rows, the same element type; must not overlap in.
  * 1-D operands return MX_ERR_UNSUPPORTED (their blocks run along K only and
  * cannot be transposed without re-quantizing).  Empty operands are a no-op.
  */

@@ -210,7 +210,7 @@ def transpose(q, out=None):
     (see mx_transpose)."""
     lib = load_library()
     if out is None:
-        out = empty_mx(q.K, q.rows, "2d", device=q.codes.device)
+        out = empty_mx(q.K, q.rows, "2d", device=q.codes.device, elem=q.elem)
     it, ot = q.c_struct(), out.c_struct()
     _check(lib.mx_transpose(ctypes.byref(it), ctypes.byref(ot), _stream(q.codes)))
     return out

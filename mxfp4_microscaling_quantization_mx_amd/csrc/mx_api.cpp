@@ -232,8 +232,8 @@ mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream) 
   if (st != MX_OK) return st;
   if (in->block != MX_BLOCK_2D || out->block != MX_BLOCK_2D)
     return fail(MX_ERR_UNSUPPORTED, "mx_transpose: only operands with 2-D (32x32) blocks transpose exactly");
-  if (in->elem != MX_ELEM_E2M1 || out->elem != MX_ELEM_E2M1)
-    return fail(MX_ERR_UNSUPPORTED, "mx_transpose: MXFP4 operands only");
+  if (in->elem != out->elem)
+    return fail(MX_ERR_INVALID_ARG, "mx_transpose: in and out element types differ");
   if (out->rows != in->K || out->K != in->rows)
     return fail(MX_ERR_INVALID_ARG, "mx_transpose: out is [%lld, %lld], expected [%lld, %lld]", (long long)out->rows,
                 (long long)out->K, (long long)in->K, (long long)in->rows);
@@ -251,6 +251,7 @@ mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream) 
   a.out_scales = out->scales;
   a.ld_out = out->ld_codes;
   a.ld_sout = out->ld_scales;
+  a.bits = elem_bits(in->elem);
   return hip_status(mx::launch_transpose(a, static_cast<hipStream_t>(stream)), "mx_transpose");
 }
 

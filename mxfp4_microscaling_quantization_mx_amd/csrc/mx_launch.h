@@ -78,6 +78,7 @@ struct TransposeArgs {
   uint8_t* out_codes;
   uint8_t* out_scales;
   int64_t ld_out, ld_sout;
+  int bits = 4;               // bits per element code (4, 6 or 8)
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);

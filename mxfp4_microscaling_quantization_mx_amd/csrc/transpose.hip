@@ -1,5 +1,5 @@
-// Exact transpose of an MXFP4 operand quantized with 32x32 (2-D) blocks, for
-// gfx950.  A 32x32 tile has one shared scale, so the transposed tile is the
+// Exact transpose of an MX operand quantized with 32x32 (2-D) blocks, for
+// gfx950 (MXFP4 below; MXFP8 / MXFP6 in k_transpose_2d_bytes).  A 32x32 tile has one shared scale, so the transposed tile is the
 // same block: its codes are the tile's codes transposed and its scale byte is
 // unchanged.  This is what lets one 2-D quantization of a weight serve both
 // the forward product and, transposed, the data-gradient product (the hybrid
@@ -94,13 +94,68 @@ __global__ __launch_bounds__(256) void k_transpose_2d(const uint8_t* __restrict_
   }
 }
 
+// The other element types (FP8: one byte per code; FP6: 4 codes per 3 bytes,
+// element k at bits 6k of the row): the 128 x 128 tile is unpacked to one byte
+// per code in LDS, transposed by reading it column-wise, and packed again.
+// Thread t unpacks / packs groups of 4 codes (3 bytes for FP6, 4 for FP8).
+template <int BITS>
+__global__ __launch_bounds__(256) void k_transpose_2d_bytes(const uint8_t* __restrict__ in_codes, int64_t ld_in,
+                                                            const uint8_t* __restrict__ in_scales, int64_t ld_sin,
+                                                            int64_t R, int64_t C, uint8_t* __restrict__ out_codes,
+                                                            int64_t ld_out, uint8_t* __restrict__ out_scales,
+                                                            int64_t ld_sout) {
+  constexpr int GB = BITS / 2;                     // bytes per group of 4 codes
+  constexpr int PITCH = TT + 4;                    // LDS bytes per row
+  __shared__ uint8_t tile[TT * PITCH];
+  const int64_t r0 = (int64_t)blockIdx.y * TT, c0 = (int64_t)blockIdx.x * TT;
+  const int t = threadIdx.x;
+  // unpack: 128 rows x 32 groups
+  for (int id = t; id < TT * (TT / 4); id += 256) {
+    const int row = id >> 5, g = id & 31;
+    uint32_t w = 0;
+    if (r0 + row < R && c0 + 4 * g < C) {
+      const uint8_t* p = in_codes + (r0 + row) * ld_in + (c0 / 4 + g) * GB;
+#pragma unroll
+      for (int b = 0; b < GB; ++b) w |= (uint32_t)p[b] << (8 * b);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      tile[row * PITCH + 4 * g + j] = (uint8_t)((w >> (BITS * j)) & ((1u << BITS) - 1u));
+  }
+  __syncthreads();
+  // pack: output row o (input column c0 + o), 32 groups of 4 input rows
+  for (int id = t; id < TT * (TT / 4); id += 256) {
+    const int o = id >> 5, g = id & 31;
+    if (c0 + o >= C || r0 + 4 * g >= R) continue;
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w |= (uint32_t)tile[(4 * g + j) * PITCH + o] << (BITS * j);
+    uint8_t* p = out_codes + (c0 + o) * ld_out + (r0 / 4 + g) * GB;
+#pragma unroll
+    for (int b = 0; b < GB; ++b) p[b] = (uint8_t)(w >> (8 * b));
+  }
+  if (t < 16) {
+    const int a = t >> 2, b = t & 3;
+    const int64_t ib = (r0 >> 5) + b, jb = (c0 >> 5) + a;
+    if (ib * 32 < R && jb * 32 < C) out_scales[jb * ld_sout + ib] = in_scales[ib * ld_sin + jb];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st) {
   if (a.R == 0 || a.C == 0) return hipSuccess;
   const dim3 grid((unsigned)((a.C + TT - 1) / TT), (unsigned)((a.R + TT - 1) / TT));
-  hipLaunchKernelGGL(k_transpose_2d, grid, dim3(256), 0, st, a.in_codes, a.ld_in, a.in_scales, a.ld_sin, a.R, a.C,
-                     a.out_codes, a.ld_out, a.out_scales, a.ld_sout);
+  if (a.bits == 8) {
+    hipLaunchKernelGGL(k_transpose_2d_bytes<8>, grid, dim3(256), 0, st, a.in_codes, a.ld_in, a.in_scales, a.ld_sin,
+                       a.R, a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout);
+  } else if (a.bits == 6) {
+    hipLaunchKernelGGL(k_transpose_2d_bytes<6>, grid, dim3(256), 0, st, a.in_codes, a.ld_in, a.in_scales, a.ld_sin,
+                       a.R, a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout);
+  } else {
+    hipLaunchKernelGGL(k_transpose_2d, grid, dim3(256), 0, st, a.in_codes, a.ld_in, a.in_scales, a.ld_sin, a.R,
+                       a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout);
+  }
   return hipGetLastError();
 }
 

@@ -235,21 +235,27 @@ def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0,
     return codes, scales
 
 
-def transpose_2d(codes, scales):
+def transpose_2d(codes, scales, elem="e2m1"):
     """Transpose of an operand quantized with 2-D (32x32) blocks: [R, C] ->
     [C, R].  A 32x32 tile shares one scale whichever way it is read, so element
     (c, r) of the result carries the code of element (r, c) and tile (j, i)
     the scale byte of tile (i, j); nothing is re-rounded.  This is the reading
     behind the 2-D weight blocks of the hybrid 1D/2D recipe ("Training an MoE
     LLM in MXFP4", summary): one quantization of W serves X W and, transposed,
-    dY W^T."""
-    c = unpack_nibbles(codes)
+    dY W^T.  Other element types (elem) transpose their codes the same way."""
+    if elem == "e2m1":
+        c = unpack_nibbles(codes)
+    else:
+        cd = np.asarray(codes)
+        c = elements.unpack(cd, elem, cd.shape[1] * 8 // elements.elem_bits(elem))
     s = np.asarray(scales, dtype=np.uint8)
     if c.shape[0] % BLOCK or c.shape[1] % BLOCK:
         raise ValueError("2-D blocks need both dimensions to be multiples of 32")
     if s.shape != (c.shape[0] // BLOCK, c.shape[1] // BLOCK):
         raise ValueError("expected one scale per 32x32 tile")
-    return pack_nibbles(np.ascontiguousarray(c.T)), np.ascontiguousarray(s.T)
+    ct = np.ascontiguousarray(c.T)
+    packed = pack_nibbles(ct) if elem == "e2m1" else elements.pack(ct, elem)
+    return packed, np.ascontiguousarray(s.T)
 
 
 def dequantize(codes, scales, block="1d", inverse_rht_mask=None, dtype=np.float32, elem="e2m1"):

@@ -117,8 +117,9 @@ def test_transpose_rejects_bad_arguments(lib):
 
 def test_element_types_are_validated(lib):
     """mx_tensor.elem: unknown values are refused everywhere; MXFP8/MXFP6 rows
-    need K*bits/8 bytes and 2-D blocks whole 32-row groups; the gather and
-    the transpose are MXFP4-only; the grouped GEMM checks K for any type."""
+    need K*bits/8 bytes and 2-D blocks whole 32-row groups; the gather is
+    MXFP4-only; the transpose keeps the element type; the grouped GEMM checks
+    K for any type."""
     cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 0, 0, 0)
     bad = _tensor(32, 64)
     bad.elem = 9
@@ -141,7 +142,7 @@ def test_element_types_are_validated(lib):
     t_in = _tensor(64, 96, ldc=96, block=1)
     t_in.elem = 1
     st = lib.mx_transpose(ctypes.byref(t_in), ctypes.byref(_tensor(96, 64, block=1)), None)
-    assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+    assert st == mx.MX_ERR_INVALID_ARG and b"element types differ" in lib.mx_last_error()
     a = _tensor(64, 64, ldc=64)
     a.elem = 2
     b = _tensor(64, 96, block=1)

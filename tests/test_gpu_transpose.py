@@ -114,3 +114,29 @@ def test_dgrad_full_size():
     ref, bound = oracle.gemm_ref(odc, ods, owc, ows, "1d", "2d")
     got = host(dx.float())[np.ix_(rows, cols)]
     check_gemm(got, ref, bound, bf16=True, what="dgrad")
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e5m2", "e2m3", "e3m2"])
+@pytest.mark.parametrize("R,C", [(96, 160), (288, 416)])
+def test_transpose_other_element_types(elem, R, C):
+    """MXFP8 / MXFP6 2-D operands: random code bytes and scales transpose to the
+    oracle's transpose, padding untouched."""
+    need_gpu()
+    from oracle import elements as el
+    rng = np.random.default_rng(R + C + len(elem))
+    cb = C * el.elem_bits(elem) // 8
+    codes = rng.integers(0, 256, (R, cb), dtype=np.uint8)
+    if el.elem_bits(elem) == 6:          # whole 6-bit codes only (the packing has no spare bits)
+        codes = el.pack(el.unpack(codes, elem, C), elem)
+    scales = rng.integers(0, 256, (R // 32, C // 32), dtype=np.uint8)
+    q = mx.empty_mx(R, C, "2d", elem=elem)
+    q.codes.copy_(to_dev(codes))
+    q.scales.copy_(to_dev(scales))
+    out = mx.empty_mx(C, R, "2d", elem=elem)
+    _full_rows(out.codes).fill_(0x5A)
+    banner(f"transpose {elem} R={R} C={C}")
+    mx.transpose(q, out=out)
+    oc, os_ = oracle.transpose_2d(codes, scales, elem)
+    codes_equal(host(out.codes), oc, "codes")
+    codes_equal(host(out.scales), os_, "scales")
+    assert np.all(host(_full_rows(out.codes))[:, R * el.elem_bits(elem) // 8:] == 0x5A)

@@ -481,3 +481,17 @@ def test_transpose_2d_is_quantizing_along_the_other_axis():
     c1, s1 = oracle.quantize(np.ones((32, 64), np.float32))
     with pytest.raises(ValueError):
         oracle.transpose_2d(c1, s1)
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e5m2", "e2m3", "e3m2"])
+def test_transpose_2d_other_element_types(elem):
+    """The same pin for MXFP8 / MXFP6: transposing the last-dim 32x32-tile
+    quantization gives the dim-0 one; twice is the identity."""
+    rng = np.random.default_rng(43)
+    w = (rng.standard_normal((96, 160)) * np.exp(rng.uniform(-3, 3, (3, 1)).repeat(32, 0))).astype(np.float32)
+    lc, ls = oracle.quantize(w, block="2d", elem=elem)
+    dc, ds = oracle.quantize(w, axis="dim0", block="2d", elem=elem)
+    tc, ts = oracle.transpose_2d(lc, ls, elem)
+    assert np.array_equal(tc, dc) and np.array_equal(ts, ds)
+    bc, bs = oracle.transpose_2d(tc, ts, elem)
+    assert np.array_equal(bc, lc) and np.array_equal(bs, ls)
