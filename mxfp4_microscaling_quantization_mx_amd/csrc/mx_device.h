@@ -374,6 +374,59 @@ __device__ __forceinline__ uint32_t elem_code(float v, uint32_t r16) {
   return elem_mag_code<ELEM, SR>(__builtin_fabsf(v), r16) | ((__float_as_uint(v) >> 31) << (T::E + T::M));
 }
 
+// Hardware RNE conversion for the FP8 / FP6 element types.
+// V_CVT_SCALEF32_PK_FP8_F32 / _PK_BF8_F32 (E4M3 / E5M2, two values) and
+// V_CVT_SCALEF32_2XPK16_FP6_F32 / _BF6_F32 (E2M3 / E3M2, 32 values) round
+// x / scale to nearest even.  The FP8 forms do not saturate: from the midpoint
+// above the largest normal they return the NaN / Inf code (the probe tests saw
+// E4M3 0x7F for x / scale = 481.8).  Clamping x to +-(largest normal * scale)
+// first is exact for a power-of-two scale and makes the result equal to
+// elem_code<ELEM, false>(x / scale) for every finite float32 x; the probe
+// tests check these helpers against elem_code over all finite float32 inputs
+// at several scales.  lim is largest normal * scale (Inf when that overflows:
+// then no finite quotient reaches the largest normal).
+__device__ __forceinline__ float elem_clamp(float x, float lim) { return __builtin_amdgcn_fmed3f(x, -lim, lim); }
+
+// Four values -> one word of FP8 codes, value i in byte i.
+template <int ELEM>
+__device__ __forceinline__ uint32_t pack4_fp8(const float x[4], float scale, float lim) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s w = {0, 0};
+  const float a0 = elem_clamp(x[0], lim), a1 = elem_clamp(x[1], lim);
+  const float a2 = elem_clamp(x[2], lim), a3 = elem_clamp(x[3], lim);
+  if constexpr (ELEM == 1) {
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a0, a1, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a2, a3, scale, true);
+  } else {
+    w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, a0, a1, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, a2, a3, scale, true);
+  }
+  return __builtin_bit_cast(uint32_t, w);
+}
+
+// 32 values -> 6 words of FP6 codes, value e at bits 6e .. 6e+5.  The
+// instruction interleaves its two 16-value sources (code 2i from the first
+// source's value i, code 2i+1 from the second's; seen in the probe tests), so
+// the even values go in the first source and the odd values in the second.
+template <int ELEM>
+__device__ __forceinline__ void pack32_fp6(const float x[32], float scale, float lim, uint32_t out[6]) {
+  typedef float v16 __attribute__((ext_vector_type(16)));
+  typedef int v6 __attribute__((ext_vector_type(6)));
+  v16 a, b;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    a[i] = elem_clamp(x[2 * i], lim);
+    b[i] = elem_clamp(x[2 * i + 1], lim);
+  }
+  v6 p;
+  if constexpr (ELEM == 3)
+    p = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, scale);
+  else
+    p = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, scale);
+#pragma unroll
+  for (int j = 0; j < 6; ++j) out[j] = (uint32_t)p[j];
+}
+
 // Value of a code (NaN and Inf codes decode as such).
 template <int ELEM>
 __device__ __forceinline__ float elem_value(uint32_t c) {

@@ -134,10 +134,11 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
 }
 
 // The same block step for the other MX element types (ELEM = mx_elem 1..4,
-// FP8 or FP6): scale from the type's largest power of two, elements rounded in
-// software (elem_code: RNE, or SR with the same Philox draws as E2M1), then
-// packed: FP8 one byte per element (8 words), FP6 element e at bits 6e of the
-// block's 192 bits (6 words).  Returns the scale byte.
+// FP8 or FP6): scale from the type's largest power of two, elements rounded
+// (RNE: the hardware converts; SR: in software by elem_code with the same
+// Philox draws as E2M1) and packed: FP8 one byte per element (8 words), FP6
+// element e at bits 6e of the block's 192 bits (6 words).  Returns the scale
+// byte.
 template <int ELEM, bool RHT, bool SR, bool TWO_D = false>
 __device__ __forceinline__ uint32_t quantize_block32_elem(float x[32], uint32_t out[8], uint64_t p0, uint64_t seed,
                                                           uint64_t offset, int scale_mode) {
@@ -163,6 +164,25 @@ __device__ __forceinline__ uint32_t quantize_block32_elem(float x[32], uint32_t 
   if (scale_mode == 2) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) x[i] = 0.75f * x[i];
+  }
+  if constexpr (!SR) {
+    // RNE through the hardware converts (pack4_fp8 / pack32_fp6), which
+    // divide by the scale themselves; scale byte 0 (2^-127, a float32
+    // subnormal) goes in as x 2^127 at scale 1, the same single rounding.
+    float sc = scale_f32_normal(s);
+    if (s == 0u) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = x[i] * __uint_as_float(0x7F000000u);
+      sc = 1.0f;
+    }
+    const float lim = __uint_as_float(T::MAXBITS) * sc;
+    if constexpr (T::BITS == 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[j] = pack4_fp8<ELEM>(x + 4 * j, sc, lim);
+    } else {
+      pack32_fp6<ELEM>(x, sc, lim, out);
+    }
+    return s;
   }
   const float inv = inv_scale_from_code(s);
 #pragma unroll

@@ -158,7 +158,120 @@ __global__ void k_cvt_sr_sweep(uint64_t lo, uint64_t hi, unsigned long long* mis
   if (local) atomicAdd(mismatches, local);
 }
 
+// The library's hardware FP8 packing mx::pack4_fp8 (scale 2^k, which the
+// instruction divides by; inputs clamped to the largest normal times the
+// scale) against its software rule mx::elem_code (RNE, saturating) for every
+// float32 x in [lo, hi), as the word (x, -x, -x, x): both halves of the word.  counts[0]: mismatches with |x| / 2^k
+// below 2^(emax+1), the range a block's elements fall in after division by its
+// scale (largest normal .. 2^(emax+1) must saturate); counts[1]: at or above
+// it; first: (x bits, hw, sw) of the first mismatches counted in counts[0].
+template <int ELEM>
+__global__ void k_cvt_fp8_sweep(uint64_t lo, uint64_t hi, int k, unsigned long long* counts, uint32_t* first,
+                                uint32_t cap) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const float s = __builtin_ldexpf(1.0f, k), inv = __builtin_ldexpf(1.0f, -k);
+  const float lim = __uint_as_float(mx::ElemT<ELEM>::MAXBITS) * s;
+  unsigned long long m0 = 0, m1 = 0;
+  for (uint64_t u = lo + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u < hi; u += stride) {
+    const float x = __uint_as_float((uint32_t)u);
+    const float xs[4] = {x, -x, -x, x};
+    const uint32_t hw = mx::pack4_fp8<ELEM>(xs, s, lim);
+    const float v = x * inv;
+    const uint32_t cp = mx::elem_code<ELEM, false>(v, 0u), cn = mx::elem_code<ELEM, false>(-v, 0u);
+    const uint32_t sw = cp | (cn << 8) | (cn << 16) | (cp << 24);
+    if (hw != sw) {
+      if (__builtin_fabsf(v) < __uint_as_float((uint32_t)(mx::ElemT<ELEM>::EMAX + 128) << 23)) {
+        ++m0;
+        const unsigned long long n = atomicAdd(counts + 2, 1ull);
+        if (n < cap) {
+          first[3 * n] = (uint32_t)u;
+          first[3 * n + 1] = hw;
+          first[3 * n + 2] = sw;
+        }
+      } else {
+        ++m1;
+      }
+    }
+  }
+  if (m0) atomicAdd(counts, m0);
+  if (m1) atomicAdd(counts + 1, m1);
+}
+
+// The library's hardware FP6 packing mx::pack32_fp6 (32 floats, scale 2^k)
+// against its software rule and 6-bit little-endian packing: thread
+// u takes the 32 consecutive float32 patterns from base lo + 32 u, odd ones
+// negated.  counts as above (a group with a value at or above 2^(emax+1)
+// counted apart); first: per mismatch the base pattern, the 6 hardware
+// words and the 6 software words.
+template <int ELEM>
+__global__ void k_cvt_fp6_sweep(uint64_t lo, uint64_t hi, int k, unsigned long long* counts, uint32_t* first,
+                                uint32_t cap) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * 32;
+  const float s = __builtin_ldexpf(1.0f, k), inv = __builtin_ldexpf(1.0f, -k);
+  const float lim = __uint_as_float(mx::ElemT<ELEM>::MAXBITS) * s;
+  unsigned long long m0 = 0, m1 = 0;
+  for (uint64_t u = lo + ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 32; u + 32 <= hi; u += stride) {
+    float x[32];
+    bool big = false;
+    for (int i = 0; i < 32; ++i) {
+      x[i] = __uint_as_float((uint32_t)(u + i)) * ((i & 1) ? -1.0f : 1.0f);
+      big |= __builtin_fabsf(x[i] * inv) >= __uint_as_float((uint32_t)(mx::ElemT<ELEM>::EMAX + 128) << 23);
+    }
+    uint32_t p[6];
+    mx::pack32_fp6<ELEM>(x, s, lim, p);
+    uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+    for (int e = 0; e < 32; ++e) {
+      const uint32_t code = mx::elem_code<ELEM, false>(x[e] * inv, 0u);
+      const int bit = 6 * e;
+      w[bit >> 5] |= code << (bit & 31);
+      if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+    }
+    bool bad = false;
+    for (int j = 0; j < 6; ++j) bad |= p[j] != w[j];
+    if (bad) {
+      if (big) {
+        ++m1;
+      } else {
+        ++m0;
+        const unsigned long long n = atomicAdd(counts + 2, 1ull);
+        if (n < cap) {
+          first[13 * n] = (uint32_t)u;
+          for (int j = 0; j < 6; ++j) {
+            first[13 * n + 1 + j] = p[j];
+            first[13 * n + 7 + j] = w[j];
+          }
+        }
+      }
+    }
+  }
+  if (m0) atomicAdd(counts, m0);
+  if (m1) atomicAdd(counts + 1, m1);
+}
+
 extern "C" {
+
+int probe_cvt_fp8_sweep(uint64_t lo, uint64_t hi, int elem, int k, unsigned long long* counts, uint32_t* first,
+                        uint32_t cap) {
+  if (elem == 1)
+    hipLaunchKernelGGL(k_cvt_fp8_sweep<1>, dim3(4096), dim3(256), 0, 0, lo, hi, k, counts, first, cap);
+  else if (elem == 2)
+    hipLaunchKernelGGL(k_cvt_fp8_sweep<2>, dim3(4096), dim3(256), 0, 0, lo, hi, k, counts, first, cap);
+  else
+    return -1;
+  return (int)hipGetLastError();
+}
+
+int probe_cvt_fp6_sweep(uint64_t lo, uint64_t hi, int elem, int k, unsigned long long* counts, uint32_t* first,
+                        uint32_t cap) {
+  if (elem == 3)
+    hipLaunchKernelGGL(k_cvt_fp6_sweep<3>, dim3(4096), dim3(256), 0, 0, lo, hi, k, counts, first, cap);
+  else if (elem == 4)
+    hipLaunchKernelGGL(k_cvt_fp6_sweep<4>, dim3(4096), dim3(256), 0, 0, lo, hi, k, counts, first, cap);
+  else
+    return -1;
+  return (int)hipGetLastError();
+}
+
 
 int probe_mfma_scale_32x32x64(const int* a, const int* b, const int* sa, const int* sb, float* out,
                               int opsel2) {

@@ -99,6 +99,9 @@ def probe_lib():
     lib.probe_mfma_scale_32x32x64.argtypes = [P, P, P, P, P, ctypes.c_int]
     lib.probe_mfma_scale_16x16x128.argtypes = [P, P, P, P, P]
     lib.probe_mfma_scale_32x32x64_fmt.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int]
+    U64 = ctypes.c_uint64
+    lib.probe_cvt_fp8_sweep.argtypes = [U64, U64, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_uint32]
+    lib.probe_cvt_fp6_sweep.argtypes = [U64, U64, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_uint32]
     lib.probe_cvt_fp4_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, P, P, ctypes.c_uint32]
     lib.probe_cvt_fp4_scaled_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, P]
     lib.probe_cvt_fp4_sr_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64, P, P, ctypes.c_uint32]

@@ -261,3 +261,52 @@ def test_hw_fp4_sr_matches_software_sr_everywhere():
     for u, hw, sw in f[:8]:
         print(f"  x=0x{u:08x} ({np.uint32(u).view(np.float32)!r}) hw=0x{hw:08x} sw=0x{sw:08x}")
     assert n == 0
+
+
+def _fp_sweep(fn, lo, hi, elem, k, width):
+    cap = 16
+    cnt = torch.zeros(3, dtype=torch.int64, device="cuda")
+    first = torch.zeros(width * cap, dtype=torch.int32, device="cuda")
+    assert fn(lo, hi, elem, k, cnt.data_ptr(), first.data_ptr(), cap) == 0
+    torch.cuda.synchronize()
+    c = cnt.cpu().numpy()
+    f = first.cpu().numpy().view(np.uint32).reshape(cap, width)[:min(int(c[2]), cap)]
+    return c, f
+
+
+@pytest.mark.parametrize("elem", [1, 2])
+@pytest.mark.parametrize("k", [-126, -20, 0, 3, 100, 125])
+def test_hw_fp8_pack_matches_software_rne(elem, k):
+    """mx::pack4_fp8 (V_CVT_SCALEF32_PK_FP8/BF8_F32 with scale 2^k on inputs
+    clamped to +-(largest normal * 2^k)) equals the software RNE codes of
+    x / 2^k (E4M3 / E5M2, saturating) in all four bytes, for every finite
+    float32 x >= 0 (and -x; a block holding Inf or NaN gets the NaN scale and
+    no conversion).  Mismatches are counted apart for
+    |x| / 2^k >= 2^(emax+1), which no block holds after division by its scale."""
+    need_gpu()
+    lib = probe_lib()
+    banner(f"fp8 cvt sweep elem={elem} k={k}")
+    c, f = _fp_sweep(lib.probe_cvt_fp8_sweep, 0, 0x7F800000, elem, k, 3)
+    save_npz(f"probe_cvt_fp8_{elem}_{k}.npz", counts=c, first=f)
+    print(f"fp8 elem {elem} scale 2^{k}: mismatches in range {c[0]}, above {c[1]}")
+    for u, hw, sw in f[:8]:
+        print(f"  x=0x{u:08x} ({np.uint32(u).view(np.float32)!r}) hw=0x{hw:08x} sw=0x{sw:08x}")
+    assert c[0] == 0 and c[1] == 0
+
+
+@pytest.mark.parametrize("elem", [3, 4])
+@pytest.mark.parametrize("k", [-126, 0, 7, 125])
+def test_hw_fp6_pack_matches_software_rne_and_packing(elem, k):
+    """mx::pack32_fp6 (V_CVT_SCALEF32_2XPK16_FP6/BF6_F32, 32 values, scale 2^k,
+    clamped inputs) equals the software RNE codes of x / 2^k packed 6 bits per
+    element, element e at bit 6e (E2M3 / E3M2), over every finite float32
+    pattern in groups of 32 with alternating signs."""
+    need_gpu()
+    lib = probe_lib()
+    banner(f"fp6 cvt sweep elem={elem} k={k}")
+    c, f = _fp_sweep(lib.probe_cvt_fp6_sweep, 0, 0x7F800000, elem, k, 13)
+    save_npz(f"probe_cvt_fp6_{elem}_{k}.npz", counts=c, first=f)
+    print(f"fp6 elem {elem} scale 2^{k}: mismatching groups in range {c[0]}, above {c[1]}")
+    for row in f[:4]:
+        print(f"  x=0x{row[0]:08x} hw={[hex(v) for v in row[1:7]]} sw={[hex(v) for v in row[7:13]]}")
+    assert c[0] == 0 and c[1] == 0
