@@ -126,6 +126,10 @@ class Workload:
         self.e6_qw = mx.empty_mx(5760, 2880, device=dev, elem="e2m3")
         self.e_y = torch.empty((16384, 5760), dtype=torch.bfloat16, device=dev)
         mx.quantize(self.fw, axis="dim0", out=self.e6_qw)
+        # the fprop product quantized in the GEMM epilogue (MXFP4 [16384, 5760]),
+        # and the unfused equivalent's second kernel: quantize of the bf16 output
+        self.g_qy = mx.empty_mx(16384, 5760, device=dev)
+        self.g_qy2 = mx.empty_mx(16384, 5760, device=dev)
 
     # each entry: (name, callable, kind, algorithmic amount)
     def kernels(self):
@@ -160,7 +164,10 @@ class Workload:
 
     def extras(self):
         """Kernels of the next rows, timed beside the step: the dgrad product
-        that reuses the forward weight through its exact 2-D transpose."""
+        that reuses the forward weight through its exact 2-D transpose, the
+        MXFP8 / MXFP6 element types at the fprop shape, and the fprop product
+        quantized in the GEMM epilogue (compare with fprop_gemm plus
+        unfused_quantize_y, the bf16 output's quantization)."""
         t_bytes = 2 * (2880 * 5760 // 2 + (2880 // 32) * (5760 // 32))
         return [
             ("dgrad_transpose_w", lambda: mx.transpose(self.d_qw, out=self.d_qwt), "hbm", t_bytes),
@@ -176,6 +183,9 @@ class Workload:
             ("mxfp6_quantize_x", lambda: mx.quantize(self.fx, out=self.e6_qx), "hbm",
              quant_bytes(16384, 2880, out_bits=6)),
             ("mxfp6_gemm", lambda: mx.gemm(self.e6_qx, self.e6_qw, out=self.e_y), "mfma", 2 * 16384 * 5760 * 2880),
+            ("fused_gemm_quantize_y", lambda: mx.gemm_quantize(self.f_qx, self.f_qw, out=self.g_qy), "mfma",
+             2 * 16384 * 5760 * 2880),
+            ("unfused_quantize_y", lambda: mx.quantize(self.f_y, out=self.g_qy2), "hbm", quant_bytes(16384, 5760)),
         ]
 
 

@@ -256,6 +256,32 @@ mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream);
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
                   void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * mx_gemm_quantize — the product C = A B^T of mx_gemm, quantized in the GEMM's
+ * epilogue into an MXFP4 operand blocked along N, so the float32 product never
+ * reaches memory: the fused output quantization of a low-precision linear
+ * layer ("MXFP4", AI Wiki, §Conversion rules for the block step; "Training an
+ * MoE LLM in MXFP4: How We Closed the Gap to BF16" for MXFP4 GEMM outputs that
+ * feed the next MXFP4 GEMM).  Each 32 consecutive outputs of a row form a
+ * block quantized from their float32 values exactly as mx_quantize does with
+ * RNE, no transform and the given scale mode: the result equals mx_gemm with
+ * float32 output followed by mx_quantize of that output along its last dim.
+ *
+ *   A, B        host structs of device buffers, MXFP4 (E2M1), A->K == B->K,
+ *               1-D or 2-D scales, scale rows 16-byte aligned with a stride
+ *               that is a multiple of 16; codes under 2 GiB.
+ *   scale_mode  an mx_scale_mode.
+ *   out         host struct of device buffers: rows = M = A->rows, K = N =
+ *               B->rows (a multiple of 32), MX_BLOCK_1D, MX_ELEM_E2M1; codes
+ *               [M, N/2], scales [M, N/32] with their row strides (ld_codes a
+ *               multiple of 16, as every mx_tensor).
+ *   M, N >= 256 (the epilogue exists on the 256 x 256 pipeline only); other
+ *   shapes or layouts return MX_ERR_UNSUPPORTED without launching.
+ *   M or N = 0: nothing is written.
+ */
+mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale_mode, mx_tensor* out,
+                           void* stream);
+
 /* Bytes of device workspace mx_gemm needs for this problem (0 if none). */
 size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 

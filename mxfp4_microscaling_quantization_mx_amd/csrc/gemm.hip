@@ -18,7 +18,17 @@
 // 32-bit word of 4 scale bytes per row.  Rows past M/N and K past the end are
 // zero codes with scale 1.0, so they add exact zeros (a NaN scale there would
 // otherwise poison the sums).
+// The 256x256 pipeline in its two MFMA operand orders (see gemm_tile256.h).
+#define MX_T256_NS t256
+#define MX_T256_SWAP 0
 #include "gemm_tile256.h"
+#undef MX_T256_NS
+#undef MX_T256_SWAP
+#define MX_T256_NS t256s
+#define MX_T256_SWAP 1
+#include "gemm_tile256.h"
+#undef MX_T256_NS
+#undef MX_T256_SWAP
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -93,7 +103,20 @@ __global__ __launch_bounds__(64 * GW, 1) void k_gemm256(MxOperand A, MxOperand B
   const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
                       XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
-  t256::run_tiles<A2D, B2D, OUT_BF16, true>(sc, sd, K, C, ldc, lds);
+  t256::run_tiles<A2D, B2D, OUT_BF16 ? t256::OUT_BF16_ : t256::OUT_F32, true>(sc, sd, K, C, ldc, lds);
+}
+
+// The dense kernel with the quantizing epilogue (the pipeline with swapped
+// MFMA operands): C = A B^T is never stored; each tile leaves as MXFP4 codes
+// and scale bytes along N.
+template <bool A2D, bool B2D>
+__global__ __launch_bounds__(64 * GW, 1) void k_gemm256_q(MxOperand A, MxOperand B, int M, int N, int K,
+                                                          t256::QOut qo, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256s::LDS_BYTES];
+  const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
+                      XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
+  const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
+  t256s::run_tiles<A2D, B2D, t256s::OUT_MX, true>(sc, sd, K, nullptr, 0, lds, qo);
 }
 
 // Grouped (MoE) GEMM.  A row tile ("slot") never straddles two experts: the
@@ -254,7 +277,7 @@ __global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxO
   __syncthreads();
   const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
   const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
-  t256::run_tiles<false, B2D, OUT_BF16, true>(sc, sd, K, C, ldc, lds);
+  t256::run_tiles<false, B2D, OUT_BF16 ? t256::OUT_BF16_ : t256::OUT_F32, true>(sc, sd, K, C, ldc, lds);
 }
 
 // ---------------------------------------------------------------- 128x128 tiles
@@ -805,6 +828,33 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     else { if (a.b_2d) MX_G(false, true, false); else MX_G(false, false, false); }
   }
 #undef MX_G
+  return hipGetLastError();
+}
+
+bool gemm_quantize_supported(const GemmQuantArgs& a) {
+  const bool out_ok = a.M >= 256 && a.N >= 256 && a.N % 32 == 0 && a.ld_codes % 4 == 0 &&
+                      (uintptr_t)a.codes % 4 == 0 && 256 * a.ld_codes < (1ll << 31) &&
+                      256 * a.ld_scales < (1ll << 31) && a.ld_codes >= a.N / 2 && a.ld_scales >= a.N / 32;
+  if (a.K == 0) return out_ok;   // the operands are never read
+  return out_ok && a.A.ld_scales % 16 == 0 && a.B.ld_scales % 16 == 0 && (uintptr_t)a.A.scales % 16 == 0 &&
+         (uintptr_t)a.B.scales % 16 == 0 && a.M * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
+         a.K < (1ll << 31);
+}
+
+hipError_t launch_gemm_quantize(const GemmQuantArgs& a, hipStream_t st) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (!gemm_quantize_supported(a)) return hipErrorNotSupported;
+  const int tiles_m = (int)((a.M + 255) / 256), tiles_n = (int)((a.N + 255) / 256);
+  const int tiles = tiles_m * tiles_n;
+  const int cus = cu_count();
+  const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
+  const t256::QOut qo{a.codes, a.scales, (int)a.ld_codes, (int)a.ld_scales, a.scale_mode};
+#define MX_GQ(A_, B_)                                                                                   \
+  hipLaunchKernelGGL((k_gemm256_q<A_, B_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, (int)a.M, (int)a.N, \
+                     (int)a.K, qo, tiles_m, tiles_n)
+  if (a.a_2d) { if (a.b_2d) MX_GQ(true, true); else MX_GQ(true, false); }
+  else { if (a.b_2d) MX_GQ(false, true); else MX_GQ(false, false); }
+#undef MX_GQ
   return hipGetLastError();
 }
 

@@ -46,13 +46,60 @@
 // next tile are loaded while the last stage of the current one is multiplied
 // and its result stored, so neither the pipeline fill nor the epilogue leaves
 // the load path idle.
-#pragma once
+//
+// The file is included twice, with MX_T256_NS naming the namespace and
+// MX_T256_SWAP choosing the MFMA operand order: 0 multiplies A-row x B-row
+// (lane = output column, registers = output rows: the layout of the float32 /
+// bf16 stores), 1 issues every MFMA with the operands and their scales
+// swapped, so that each lane holds 16 columns of one output row (the layout
+// of the quantizing epilogue, which then finds a block's 32 values in two
+// lanes).
+#if !defined(MX_T256_NS) || !defined(MX_T256_SWAP)
+#error "define MX_T256_NS and MX_T256_SWAP before including gemm_tile256.h"
+#endif
 
 #include "mx_device.h"
 #include "mx_launch.h"
 
+#ifndef MX_T256_SHARED_TYPES
+#define MX_T256_SHARED_TYPES
 namespace mx {
-namespace t256 {
+namespace t256c {
+// One 256x256 output tile: A rows [m0, m0+256) (valid below M) of the
+// operand at a_codes/a_scales, B rows [n0, n0+256) (valid below N), and the
+// output row of its first row.  All fields are wave-uniform.
+struct TileInfo {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int m0, n0, M, N;
+  int64_t c_row0;
+};
+
+// Row strides (bytes) shared by all tiles of a launch.
+struct Strides {
+  int lda, ldsa, ldb, ldsb;
+};
+
+// Destination of the quantizing epilogue: the float32 tile quantized along N
+// into MXFP4 blocks of 32 (RNE), codes [M, N/2] and scale bytes [M, N/32]
+// with these row strides; scale_mode as in mx_quantize.
+struct QOut {
+  uint8_t* codes;
+  uint8_t* scales;
+  int ld_codes, ld_scales, scale_mode;
+};
+}  // namespace t256c
+}  // namespace mx
+#endif
+
+namespace mx {
+namespace MX_T256_NS {
+
+using t256c::QOut;
+using t256c::Strides;
+using t256c::TileInfo;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -84,23 +131,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 constexpr uint32_t OOB = 0x80000000u;        // an offset past any operand (validated < 2 GiB)
-
-// One 256x256 output tile: A rows [m0, m0+256) (valid below M) of the
-// operand at a_codes/a_scales, B rows [n0, n0+256) (valid below N), and the
-// output row of its first row.  All fields are wave-uniform.
-struct TileInfo {
-  const uint8_t* a_codes;
-  const uint8_t* a_scales;
-  const uint8_t* b_codes;
-  const uint8_t* b_scales;
-  int m0, n0, M, N;
-  int64_t c_row0;
-};
-
-// Row strides (bytes) shared by all tiles of a launch.
-struct Strides {
-  int lda, ldsa, ldb, ldsb;
-};
 
 // Per-lane global offsets of this wave's 8 code loads of a tile (stage 0):
 // load t of each operand covers rows 8*(4*wave+t) .. +8, lane l the swizzled
@@ -176,9 +206,15 @@ struct Acc {
 // [0,0,0] then picks the lane's block of an even step, [1,1,0] of an odd step.
 #define MX_OPSEL_LO "0,0,0"
 #define MX_OPSEL_HI "1,1,0"
+#if MX_T256_SWAP
+#define MX_MFMA(C, A, B, SA, SB, OPSEL)                                                                    \
+  "v_mfma_scale_f32_32x32x64_f8f6f4 %[" #C "], %[" #B "], %[" #A "], %[" #C "], %[" #SB "], %[" #SA \
+  "] op_sel_hi:[" OPSEL "] cbsz:4 blgp:4\n\t"
+#else
 #define MX_MFMA(C, A, B, SA, SB, OPSEL)                                                                    \
   "v_mfma_scale_f32_32x32x64_f8f6f4 %[" #C "], %[" #A "], %[" #B "], %[" #C "], %[" #SA "], %[" #SB \
   "] op_sel_hi:[" OPSEL "] cbsz:4 blgp:4\n\t"
+#endif
 #define MX_ACC_OPERANDS(c)                                                                                 \
   [c00] "+v"(c.t[0][0]), [c01] "+v"(c.t[0][1]), [c02] "+v"(c.t[0][2]), [c03] "+v"(c.t[0][3]),           \
       [c10] "+v"(c.t[1][0]), [c11] "+v"(c.t[1][1]), [c12] "+v"(c.t[1][2]), [c13] "+v"(c.t[1][3])
@@ -428,6 +464,12 @@ __device__ __forceinline__ void zero(Acc& acc) {
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int mlim, int nlim);
 
+// Output kinds of run_tiles: float32, bf16, or the quantizing epilogue
+// (MX_T256_SWAP = 1 only).
+constexpr int OUT_F32 = 0, OUT_BF16_ = 1, OUT_MX = 2;
+
+__device__ __forceinline__ void store_tile_mx(const Acc& acc, const QOut& q, int m0, int n0, int mlim, int nlim);
+
 // Run this workgroup's tiles: C tile = A[m0:m0+256] * B[n0:n0+256]^T over all
 // K for each tile sc.tile(j), j < sc.count().  The stage sequence g = j * nst
 // + s (s < nst stages of tile j) is pipelined across tiles: code slot g & 1,
@@ -435,9 +477,10 @@ __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int
 // past the limits read as zeros and are never stored.  Byte extents of the
 // operands must be < 2 GiB.  `lds` holds LDS_BYTES: the two code slots, the
 // two scale slots and a dummy region.
-template <bool A2D, bool B2D, bool OUT_BF16, bool SPLIT, class Sched>
+template <bool A2D, bool B2D, int OUT, bool SPLIT, class Sched>
 __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, int K, void* C, int64_t ldc,
-                                          uint8_t* lds) {
+                                          uint8_t* lds, const QOut& qo = QOut{}) {
+  static_assert((OUT == OUT_MX) == (MX_T256_SWAP != 0), "the quantizing epilogue needs the swapped operand order");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -445,10 +488,13 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
   if (ntiles <= 0) return;
   Acc acc;
   zero(acc);
-  constexpr int ES = OUT_BF16 ? 2 : 4;
+  constexpr int ES = OUT == OUT_BF16_ ? 2 : 4;
   auto store = [&](const TileInfo& ti) {
-    store_tile<OUT_BF16>(acc, static_cast<uint8_t*>(C) + (ti.c_row0 * ldc + ti.n0) * ES, (int)ldc, ti.M - ti.m0,
-                         ti.N - ti.n0);
+    if constexpr (OUT == OUT_MX)
+      store_tile_mx(acc, qo, (int)ti.c_row0, ti.n0, ti.M - ti.m0, ti.N - ti.n0);
+    else
+      store_tile<OUT == OUT_BF16_>(acc, static_cast<uint8_t*>(C) + (ti.c_row0 * ldc + ti.n0) * ES, (int)ldc,
+                                   ti.M - ti.m0, ti.N - ti.n0);
   };
   const int nst = (K + TK - 1) / TK;
   if (nst == 0) {                           // K = 0: every tile is zero
@@ -642,5 +688,75 @@ __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int
   }
 }
 
-}  // namespace t256
+#if MX_T256_SWAP
+// ------------------------------------------------------------ quantizing epilogue
+// With the operands swapped, accumulator register r of MFMA tile (i, j) holds
+// in lane (kh = lane / 32, l = lane % 32) the output at row 32i + l and column
+// 32j + 8(r/4) + 4kh + r%4 of the wave's 64 x 128 region: a block of 32
+// columns of one row lies in lanes l and l + 32, 16 values each.  Per block:
+// amax of the sign-cleared bits over the lane's 16 values, then with the
+// partner lane; the scale by the mode's rule (NaN/Inf -> 0xFF with zero
+// codes); the 3/4 prescale after the scale; the hardware RNE convert at the
+// power-of-two scale (2^-127 as the float32 subnormal, which the convert
+// divides by exactly).  Each lane converts its 16 values into two words of
+// code bytes, trades one word with its partner, and stores 8 of the block's
+// 16 code bytes; lane kh = 0 stores the scale byte.  The same arithmetic as
+// the row quantizer without the transform.
+__device__ __forceinline__ void store_tile_mx(const Acc& acc, const QOut& q, int m0, int n0, int mlim, int nlim) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int rows = mlim < 256 ? mlim : 256;
+  const __amdgpu_buffer_rsrc_t rc = rsrc(q.codes + (int64_t)m0 * q.ld_codes, (uint32_t)(rows * q.ld_codes));
+  const __amdgpu_buffer_rsrc_t rs = rsrc(q.scales + (int64_t)m0 * q.ld_scales, (uint32_t)(rows * q.ld_scales));
+  const int partner = (lane ^ 32) << 2;            // ds_bpermute byte address of lane ^ 32
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int row = wm * TI * 32 + 32 * i + l32;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int cb = wn * TJ + j;                   // block column in the tile
+      const v16f& x = acc.t[i][j];
+      uint32_t m = 0;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        m = max(m, max(__float_as_uint(x[r]) & 0x7FFFFFFFu, __float_as_uint(x[r + 1]) & 0x7FFFFFFFu));
+      m = max(m, (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)m));
+      const uint32_t s = q.scale_mode == 1 ? scale_code_round_up(m) : scale_code_from_absmax_bits(m);
+      const float sc = __uint_as_float(max(s << 23, 0x00400000u));
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = q.scale_mode == 2 ? 0.75f * x[r] : x[r];
+      // words p0 (columns 4kh + 0..3 and 8 + 4kh + 0..3) and p1 (16 + ..., 24 + ...)
+      uint32_t p0 = 0u, p1 = 0u;
+      p0 = cvt_pk_fp4<0>(p0, v[0], v[1], sc);
+      p0 = cvt_pk_fp4<1>(p0, v[2], v[3], sc);
+      p0 = cvt_pk_fp4<2>(p0, v[4], v[5], sc);
+      p0 = cvt_pk_fp4<3>(p0, v[6], v[7], sc);
+      p1 = cvt_pk_fp4<0>(p1, v[8], v[9], sc);
+      p1 = cvt_pk_fp4<1>(p1, v[10], v[11], sc);
+      p1 = cvt_pk_fp4<2>(p1, v[12], v[13], sc);
+      p1 = cvt_pk_fp4<3>(p1, v[14], v[15], sc);
+      // lane kh = 0 stores block bytes 0..7 (its p0 with the partner's p0),
+      // lane kh = 1 bytes 8..15 (the partner's p1 with its p1)
+      const uint32_t mine = kh ? p1 : p0;
+      const uint32_t other = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)(kh ? p0 : p1));
+      const uint32_t lo = kh ? other : mine, hi = kh ? mine : other;
+      uint32_t w0 = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      uint32_t w1 = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+      if (s == 0xFFu) w0 = w1 = 0u;
+      const bool colok = 32 * cb < nlim;
+      const uint32_t coff = colok ? (uint32_t)(row * q.ld_codes + (n0 >> 1) + 16 * cb + 8 * kh) : OOB;
+      __builtin_amdgcn_raw_buffer_store_b64(v2u{w0, w1}, rc, coff, 0, 0);
+      if (kh == 0) {
+        const uint32_t soff = colok ? (uint32_t)(row * q.ld_scales + (n0 >> 5) + cb) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)s, rs, soff, 0, 0);
+      }
+    }
+  }
+}
+#endif
+
+}  // namespace MX_T256_NS
 }  // namespace mx

@@ -296,6 +296,48 @@ mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dty
   return hip_status(mx::launch_gemm(a, static_cast<hipStream_t>(stream)), "mx_gemm");
 }
 
+mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale_mode, mx_tensor* out,
+                           void* stream) {
+  g_err[0] = '\0';
+  mx_status st = check_tensor(A, "mx_gemm_quantize: A");
+  if (st != MX_OK) return st;
+  st = check_tensor(B, "mx_gemm_quantize: B");
+  if (st != MX_OK) return st;
+  st = check_tensor(out, "mx_gemm_quantize: out");
+  if (st != MX_OK) return st;
+  if (A->K != B->K)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm_quantize: A.K=%lld != B.K=%lld", (long long)A->K, (long long)B->K);
+  if (scale_mode < MX_SCALE_FLOOR || scale_mode > MX_SCALE_PRESCALE_3_4)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm_quantize: unknown scale mode %d", scale_mode);
+  const int64_t M = A->rows, N = B->rows;
+  if (out->rows != M || out->K != N)
+    return fail(MX_ERR_INVALID_ARG, "mx_gemm_quantize: out is [%lld, %lld], the product is [%lld, %lld]",
+                (long long)out->rows, (long long)out->K, (long long)M, (long long)N);
+  if (A->elem != MX_ELEM_E2M1 || B->elem != MX_ELEM_E2M1 || out->elem != MX_ELEM_E2M1)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_quantize: MXFP4 operands and output only");
+  if (out->block != MX_BLOCK_1D)
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_quantize: the output uses 1-D blocks");
+  if (M == 0 || N == 0) return MX_OK;
+  mx::GemmQuantArgs a{};
+  a.A = operand(A);
+  a.B = operand(B);
+  a.a_2d = A->block == MX_BLOCK_2D;
+  a.b_2d = B->block == MX_BLOCK_2D;
+  a.M = M;
+  a.N = N;
+  a.K = A->K;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  a.ld_codes = out->ld_codes;
+  a.ld_scales = out->ld_scales;
+  a.scale_mode = scale_mode;
+  if (!mx::gemm_quantize_supported(a))
+    return fail(MX_ERR_UNSUPPORTED,
+                "mx_gemm_quantize: needs M, N >= 256, operand scale rows 16-byte aligned with strides %% 16 == 0, "
+                "operands under 2 GiB, out code rows 4-byte aligned");
+  return hip_status(mx::launch_gemm_quantize(a, static_cast<hipStream_t>(stream)), "mx_gemm_quantize");
+}
+
 mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, int32_t E,
                           const mx_tensor* B, int64_t expert_stride_codes,
                           int64_t expert_stride_scales, void* C, int32_t c_dtype, int64_t ldc,

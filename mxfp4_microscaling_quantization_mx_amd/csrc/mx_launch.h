@@ -57,6 +57,17 @@ struct GemmArgs {
   int a_elem = 0, b_elem = 0;  // mx_elem of A and B
 };
 
+// C = A B^T quantized along N (MXFP4, 1-D blocks, RNE) in the GEMM epilogue.
+struct GemmQuantArgs {
+  MxOperand A, B;
+  bool a_2d, b_2d;
+  int64_t M, N, K;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t ld_codes, ld_scales;
+  int scale_mode;
+};
+
 struct GroupedGemmArgs {
   MxOperand A, B;             // B = expert 0
   bool a_2d, b_2d;
@@ -85,6 +96,10 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+// Whether the 256x256 pipeline (the only kernel with the quantizing epilogue)
+// takes this problem; launch_gemm_quantize requires it.
+bool gemm_quantize_supported(const GemmQuantArgs& a);
+hipError_t launch_gemm_quantize(const GemmQuantArgs& a, hipStream_t st);
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st);
 
 }  // namespace mx

@@ -168,6 +168,31 @@ def test_gemm_rejects_bad_arguments(lib):
     assert st == mx.MX_ERR_INVALID_ARG and b"dtype" in lib.mx_last_error()
 
 
+def test_gemm_quantize_rejects_bad_arguments(lib):
+    """Every rejection happens on the host, before any launch."""
+    B = ctypes.byref
+    a, b, out = _tensor(256, 64), _tensor(288, 64), _tensor(256, 288)
+    st = lib.mx_gemm_quantize(B(a), B(_tensor(288, 96)), 0, B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"A.K" in lib.mx_last_error()
+    st = lib.mx_gemm_quantize(B(a), B(b), 7, B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"scale mode" in lib.mx_last_error()
+    st = lib.mx_gemm_quantize(B(a), B(b), 0, B(_tensor(256, 320)), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"out is" in lib.mx_last_error()
+    st = lib.mx_gemm_quantize(B(a), B(b), 0, B(_tensor(256, 288, block=1)), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"1-D" in lib.mx_last_error()
+    a8 = _tensor(256, 64, ldc=64)
+    a8.elem = 1
+    st = lib.mx_gemm_quantize(B(a8), B(b), 0, B(out), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+    # dense scale strides (not a multiple of 16) are not taken by the 256x256 pipeline
+    st = lib.mx_gemm_quantize(B(a), B(b), 0, B(out), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"M, N >= 256" in lib.mx_last_error()
+    st = lib.mx_gemm_quantize(B(_tensor(128, 64, lds=16)), B(_tensor(288, 64, lds=16)), 0,
+                              B(_tensor(128, 288)), None)
+    assert st == mx.MX_ERR_UNSUPPORTED
+    assert lib.mx_gemm_quantize(B(_tensor(0, 64)), B(b), 0, B(_tensor(0, 288)), None) == mx.MX_OK
+
+
 def test_grouped_gemm_rejects_bad_arguments(lib):
     a = _tensor(64, 64)
     b = _tensor(32, 64, block=1)
