@@ -11,7 +11,8 @@ input (shapes of the GPT-OSS-20B-sized workloads):
   * wgrad: quantize dY and X 16384 x 2880 along the token dim (transform +
     stochastic rounding), GEMM -> float32 2880 x 2880;
   * MoE: quantize the 65536 x 2880 routed activations (32 experts, top-4,
-    Zipf(1.1) loads), grouped GEMM against the 32 pre-quantized expert
+    Zipf(1.1) loads; each of the 16384 token rows quantized once and stored
+    to its 4 routed rows), grouped GEMM against the 32 pre-quantized expert
     weights 2880 x 5760 -> bf16 65536 x 5760.
 
 `value` is the MXFP4 GEMM throughput of the whole step (dense + wgrad + MoE
@@ -20,8 +21,9 @@ and TFLOP/s are reported alongside, and `roofline` covers the dominant kernel.
 `next_rows` times, outside the step, the dgrad product that reuses the forward
 weight (the exact transpose of W quantized along dim 0 in 32x32 tiles, dY
 16384 x 5760 quantized along its last dim with stochastic rounding, and the
-GEMM -> bf16 16384 x 2880) and the dense fprop shape with MXFP8 (E4M3) and
-MXFP6 (E2M3) operands.  Prints one JSON line.
+GEMM -> bf16 16384 x 2880), the dense fprop shape with MXFP8 (E4M3) and
+MXFP6 (E2M3) operands, the fprop product quantized in the GEMM epilogue, and
+the gather form of the MoE front end.  Prints one JSON line.
 """
 import argparse
 import hashlib
@@ -92,6 +94,11 @@ class Workload:
         tok, offsets = workloads.moe_routing()
         self.mx_tok = workloads.to_bf16(workloads.moe_tokens()).to(dev)
         self.m_rows = torch.from_numpy(tok.astype(np.int32)).to(dev)
+        # the same routing from the token side: dest[t*4 + j] = the routed rows of token t
+        order = np.argsort(tok, kind="stable")
+        assert np.all(np.bincount(tok, minlength=16384) == 4)
+        self.m_dest = torch.from_numpy(order.astype(np.int32)).to(dev)
+        self.m_qa2 = mx.empty_mx(65536, 2880, device=dev)
         self.m_offsets = torch.from_numpy(offsets).to(dev)
         E, K, N = 32, 2880, 5760
         self.mb = mx.empty_mx(N, K, "2d", device=dev, experts=E)
@@ -155,8 +162,8 @@ class Workload:
                                                      rounding="sr", seed=self.w_seed, offset=1,
                                                      out=self.w_qx), "hbm", q),
             ("wgrad_gemm", lambda: mx.gemm(self.w_qdy, self.w_qx, out=self.w_dw), "mfma", flop_w),
-            ("moe_gather_quantize_a", lambda: mx.quantize_gather(self.mx_tok, self.m_rows, out=self.m_qa), "hbm",
-             gather_quant_bytes(16384, 65536, 2880)),
+            ("moe_scatter_quantize_a", lambda: mx.quantize_scatter(self.mx_tok, self.m_dest, 4, out=self.m_qa),
+             "hbm", gather_quant_bytes(16384, 65536, 2880)),
             ("moe_grouped_gemm", lambda: mx.grouped_gemm(self.m_qa, self.m_offsets, self.mb, out=self.m_y),
              "mfma", flop_m),
         ]
@@ -165,9 +172,11 @@ class Workload:
     def extras(self):
         """Kernels of the next rows, timed beside the step: the dgrad product
         that reuses the forward weight through its exact 2-D transpose, the
-        MXFP8 / MXFP6 element types at the fprop shape, and the fprop product
+        MXFP8 / MXFP6 element types at the fprop shape, the fprop product
         quantized in the GEMM epilogue (compare with fprop_gemm plus
-        unfused_quantize_y, the bf16 output's quantization)."""
+        unfused_quantize_y, the bf16 output's quantization), and the gather
+        form of the MoE front end (the step uses the scatter form: each token
+        row quantized once and stored to its 4 routed rows, the same bytes)."""
         t_bytes = 2 * (2880 * 5760 // 2 + (2880 // 32) * (5760 // 32))
         return [
             ("dgrad_transpose_w", lambda: mx.transpose(self.d_qw, out=self.d_qwt), "hbm", t_bytes),
@@ -186,6 +195,8 @@ class Workload:
             ("fused_gemm_quantize_y", lambda: mx.gemm_quantize(self.f_qx, self.f_qw, out=self.g_qy), "mfma",
              2 * 16384 * 5760 * 2880),
             ("unfused_quantize_y", lambda: mx.quantize(self.f_y, out=self.g_qy2), "hbm", quant_bytes(16384, 5760)),
+            ("moe_gather_quantize_a", lambda: mx.quantize_gather(self.mx_tok, self.m_rows, out=self.m_qa2), "hbm",
+             gather_quant_bytes(16384, 65536, 2880)),
         ]
 
 

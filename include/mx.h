@@ -196,6 +196,34 @@ mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, 
                              const mx_tensor* out, void* stream);
 
 /*
+ * mx_quantize_scatter — the same MoE front end driven from the token side:
+ * each source row is quantized once (1-D blocks along the last dim, RNE) and
+ * its codes and scale bytes are stored to each of its k destination rows
+ * dest[t*k + j].  A row's RNE codes do not depend on its destination, so when
+ * every output row is some dest entry this equals mx_quantize_gather with the
+ * inverse index, while reading each token row once instead of k times
+ * ("MXFP4", AI Wiki, §Use in models: MoE weights and activations in MXFP4).
+ *
+ *   src      device; R x C elements of src_dtype, as in mx_quantize_gather.
+ *   dest     device; int32 [R * k], the destinations of row t at t*k .. t*k+k-1;
+ *            entries outside [0, out->rows) are skipped.  Output rows named by
+ *            no entry are left untouched; a row named twice gets one of the
+ *            writes (both hold the same bytes only if they come from the same
+ *            source row).
+ *   k        destinations per row (>= 0).
+ *   cfg      host; MX_AXIS_LAST, MX_BLOCK_1D and MX_ROUND_RNE (stochastic
+ *            rounding draws follow the destination element index, so SR
+ *            returns MX_ERR_UNSUPPORTED: use mx_quantize_gather); transform and
+ *            scale mode as in mx_quantize.
+ *   out      host struct of device buffers: K = C, 1-D, MXFP4.
+ *   Requires C % 32 == 0; R, C, k or out->rows = 0 is a no-op; at most
+ *   2^32 - 256 source blocks per call.
+ */
+mx_status mx_quantize_scatter(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
+                              const int32_t* dest, int32_t k, const mx_quant_cfg* cfg, const mx_tensor* out,
+                              void* stream);
+
+/*
  * mx_dequantize — decode an MX operand: value = element(code) * 2^(scale-127)
  * ("MXFP4", AI Wiki, §Format specification: X times P_i; NaN scale makes the
  * whole block NaN; any element type: NaN and Inf element codes decode as

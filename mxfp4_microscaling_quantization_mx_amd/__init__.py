@@ -31,7 +31,7 @@ _SCALE = {"floor": 0, "round_up": 1, "prescale_3_4": 2}
 _ELEM = {"e2m1": (0, 4), "e4m3": (1, 8), "e5m2": (2, 8), "e2m3": (3, 6), "e3m2": (4, 6)}
 _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
-EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_transpose", "mx_gemm",
+EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
             "mx_gemm_quantize", "mx_gemm_workspace_size", "mx_grouped_gemm", "mx_last_error",
             "mx_version")
 
@@ -72,6 +72,7 @@ def load_library(path=LIB_PATH):
     PT = ctypes.POINTER(MxTensorC)
     lib.mx_quantize.argtypes = [P, I32, I64, I64, I64, ctypes.POINTER(QuantCfgC), PT, P]
     lib.mx_quantize_gather.argtypes = [P, I32, I64, I64, I64, P, I64, ctypes.POINTER(QuantCfgC), PT, P]
+    lib.mx_quantize_scatter.argtypes = [P, I32, I64, I64, I64, P, I32, ctypes.POINTER(QuantCfgC), PT, P]
     lib.mx_dequantize.argtypes = [PT, I32, U32, P, I32, I64, P]
     lib.mx_transpose.argtypes = [PT, PT, P]
     lib.mx_gemm.argtypes = [PT, PT, P, I32, I64, P, ctypes.c_size_t, P]
@@ -79,8 +80,8 @@ def load_library(path=LIB_PATH):
     lib.mx_gemm_workspace_size.argtypes = [I64, I64, I64]
     lib.mx_gemm_workspace_size.restype = ctypes.c_size_t
     lib.mx_grouped_gemm.argtypes = [PT, P, I32, PT, I64, I64, P, I32, I64, P]
-    for f in ("mx_quantize", "mx_quantize_gather", "mx_dequantize", "mx_transpose", "mx_gemm", "mx_gemm_quantize",
-              "mx_grouped_gemm"):
+    for f in ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
+              "mx_gemm_quantize", "mx_grouped_gemm"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mx_last_error.restype = ctypes.c_char_p
     lib.mx_last_error.argtypes = []
@@ -193,6 +194,29 @@ def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0, ou
     ot = out.c_struct()
     _check(lib.mx_quantize_gather(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), _ptr(rows), n,
                                   ctypes.byref(cfg), ctypes.byref(ot), _stream(x)))
+    return out
+
+
+def quantize_scatter(x, dest, k, rows_out=None, rht_mask=None, out=None, scale_mode="floor"):
+    """Quantize each row of a 2-D bf16/fp32 CUDA tensor once (1-D blocks along
+    the last dim, RNE) and store it to its k destination rows dest[t*k + j]
+    (see mx_quantize_scatter).  `dest` is an int32 CUDA tensor of x.shape[0]*k
+    entries; out (or a new [rows_out, C] operand) receives the rows."""
+    lib = load_library()
+    if x.dim() != 2 or x.dtype not in _DTYPE or not x.is_cuda:
+        raise ValueError("quantize_scatter expects a 2-D bf16/float32 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("quantize_scatter expects a row-major tensor (stride(1) == 1)")
+    R, C = x.shape
+    if dest.dtype != torch.int32 or not dest.is_cuda or not dest.is_contiguous() or dest.numel() != R * k:
+        raise ValueError("quantize_scatter expects dest as a contiguous int32 CUDA tensor of R*k entries")
+    if out is None:
+        out = empty_mx(R * k if rows_out is None else rows_out, C, "1d", x.device)
+    cfg = QuantCfgC(_AXIS["last"], _BLOCK["1d"], _ROUND["rne"], int(rht_mask is not None),
+                    (rht_mask or 0) & 0xFFFFFFFF, _SCALE[scale_mode], 0, 0)
+    ot = out.c_struct()
+    _check(lib.mx_quantize_scatter(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), _ptr(dest), k,
+                                   ctypes.byref(cfg), ctypes.byref(ot), _stream(x)))
     return out
 
 

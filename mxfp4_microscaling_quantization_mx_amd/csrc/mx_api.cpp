@@ -137,6 +137,55 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   return hip_status(mx::launch_quantize(a, static_cast<hipStream_t>(stream)), "mx_quantize");
 }
 
+mx_status mx_quantize_scatter(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
+                              const int32_t* dest, int32_t k, const mx_quant_cfg* cfg, const mx_tensor* out,
+                              void* stream) {
+  g_err[0] = '\0';
+  if (!cfg || !out) return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: null cfg or out");
+  if (src_dtype != MX_DT_F32 && src_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: unknown source dtype %d", src_dtype);
+  if (cfg->axis != MX_AXIS_LAST || cfg->block != MX_BLOCK_1D)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_scatter: only 1-D blocks along the last dim");
+  if (cfg->rounding != MX_ROUND_RNE)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_scatter: RNE only (SR draws depend on the destination row)");
+  if (cfg->use_rht != 0 && cfg->use_rht != 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: use_rht must be 0 or 1");
+  if (cfg->scale_mode > MX_SCALE_PRESCALE_3_4)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: unknown scale_mode %u", cfg->scale_mode);
+  if (R < 0 || C < 0 || k < 0) return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: negative shape or k");
+  if (C % 32) return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: C=%lld is not a multiple of 32", (long long)C);
+  if (out->K != C)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: out.K=%lld != C=%lld", (long long)out->K, (long long)C);
+  if (out->block != MX_BLOCK_1D) return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: out must hold 1-D blocks");
+  mx_status st = check_tensor(out, "mx_quantize_scatter: out");
+  if (st != MX_OK) return st;
+  if (out->elem != MX_ELEM_E2M1) return fail(MX_ERR_UNSUPPORTED, "mx_quantize_scatter: MXFP4 output only");
+  if (R == 0 || C == 0 || k == 0 || out->rows == 0) return MX_OK;
+  if (!dest || !aligned(dest, 4)) return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: null or unaligned dest");
+  if (!src) return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: null src");
+  if (ld_src < C)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: ld_src=%lld < C=%lld", (long long)ld_src, (long long)C);
+  if (!aligned(src, 16) || ld_src % 8)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_scatter: src must be 16-byte aligned with ld_src %% 8 == 0");
+  if (R * (C / 32) > (int64_t)0xFFFFFF00)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_scatter: at most 2^32 - 256 blocks per call");
+  mx::QuantArgs a{};
+  a.src = src;
+  a.R = R;
+  a.C = C;
+  a.ld_src = ld_src;
+  a.bf16 = src_dtype == MX_DT_BF16;
+  a.rht = cfg->use_rht == 1;
+  a.mask = cfg->rht_sign_mask;
+  a.scale_mode = (int)cfg->scale_mode;
+  a.codes = out->codes;
+  a.ld_codes = out->ld_codes;
+  a.scales = out->scales;
+  a.ld_scales = out->ld_scales;
+  return hip_status(mx::launch_quantize_scatter(a, dest, k, out->rows, static_cast<hipStream_t>(stream)),
+                    "mx_quantize_scatter");
+}
+
 mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, int64_t C, int64_t ld_src,
                              const int32_t* rows, int64_t rows_out, const mx_quant_cfg* cfg,
                              const mx_tensor* out, void* stream) {

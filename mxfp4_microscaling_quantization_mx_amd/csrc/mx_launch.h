@@ -93,6 +93,9 @@ struct TransposeArgs {
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+// MXFP4 RNE quantization of the a.R source rows, row t stored to output rows
+// dest[t * k + j], j < k (those in [0, M)).
+hipError_t launch_quantize_scatter(const QuantArgs& a, const int32_t* dest, int k, int64_t M, hipStream_t st);
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);

@@ -460,6 +460,50 @@ hipError_t launch_quantize_elem(const QuantArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Scatter form (MXFP4, RNE): one lane per block of a source row, quantized
+// once and stored to each of the row's k destination rows dest[t * k + j]
+// (destinations outside [0, M) are skipped).  With RNE a row's codes do not
+// depend on where it goes, so this equals quantizing the gathered copy.
+template <bool BF16, bool RHT>
+__global__ __launch_bounds__(256) void k_quant_rows_scatter(const void* __restrict__ src, uint32_t nblocks,
+                                                            uint32_t nkb, int64_t ld_src, uint8_t* __restrict__ codes,
+                                                            int64_t ld_codes, uint8_t* __restrict__ scales,
+                                                            int64_t ld_scales, uint32_t mask, int scale_mode,
+                                                            const int32_t* __restrict__ dest, int k, int64_t M) {
+  const uint32_t g = blockIdx.x * 256u + threadIdx.x;
+  if (g >= nblocks) return;
+  const uint32_t row = g / nkb;
+  const uint32_t kb = g - row * nkb;
+  float x[32];
+  load32<BF16>(src, (int64_t)row * ld_src + 32 * kb, x, RHT ? mask : 0u);
+  uint32_t packed[4];
+  const uint32_t s = quantize_block32<RHT, false>(x, packed, 0u, 0u, 0u, scale_mode);
+  const uint4 v = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  for (int j = 0; j < k; ++j) {
+    const int64_t d = dest[(int64_t)row * k + j];
+    if (d < 0 || d >= M) continue;
+    *reinterpret_cast<uint4*>(codes + d * ld_codes + 16 * kb) = v;
+    scales[d * ld_scales + kb] = (uint8_t)s;
+  }
+}
+
+hipError_t launch_quantize_scatter(const QuantArgs& a, const int32_t* dest, int k, int64_t M, hipStream_t st) {
+  if (a.R == 0 || a.C == 0 || k == 0) return hipSuccess;
+  const uint32_t nkb = (uint32_t)(a.C / 32);
+  const uint32_t nblocks = (uint32_t)(a.R * nkb);
+  const unsigned grid = (nblocks + 255u) / 256u;
+#define MX_SC(BF_, RHT_)                                                                                   \
+  hipLaunchKernelGGL((k_quant_rows_scatter<BF_, RHT_>), dim3(grid), dim3(256), 0, st, a.src, nblocks, nkb, \
+                     a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.scale_mode, dest, k, M)
+  if (a.bf16) {
+    if (a.rht) MX_SC(true, true); else MX_SC(true, false);
+  } else {
+    if (a.rht) MX_SC(false, true); else MX_SC(false, false);
+  }
+#undef MX_SC
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   if (a.R == 0 || a.C == 0) return hipSuccess;
   switch (a.elem) {

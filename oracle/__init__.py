@@ -35,6 +35,7 @@ from .rht import rht_forward_f32, rht_inverse_f32, hadamard32_f64
 from .quantize import (
     quantize,
     quantize_gather,
+    quantize_scatter,
     transpose_2d,
     round_up_exponent,
     dequantize,
@@ -58,6 +59,7 @@ __all__ = [
     "hadamard32_f64",
     "quantize",
     "quantize_gather",
+    "quantize_scatter",
     "transpose_2d",
     "round_up_exponent",
     "dequantize",

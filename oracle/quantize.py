@@ -235,6 +235,29 @@ def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0,
     return codes, scales
 
 
+def quantize_scatter(x, dest, k, rows_out, out_codes=None, out_scales=None, rht_mask=None,
+                     scale_mode="floor"):
+    """The MoE front end from the token side: row t of x is quantized once
+    (1-D blocks along the last dim, RNE) and written to output rows
+    dest[t*k + j], j < k; destinations outside [0, rows_out) are skipped and
+    rows no destination names keep out_codes / out_scales (zeros if not
+    given).  RNE codes depend only on the row's values, so this is the
+    quantization of the routed rows ("Training an MoE LLM in MXFP4", summary)
+    computed once per token."""
+    x = np.asarray(x, dtype=np.float32)
+    dest = np.asarray(dest, dtype=np.int64).reshape(x.shape[0], k)
+    codes, scales = quantize(x, rounding="rne", rht_mask=rht_mask, scale_mode=scale_mode)
+    oc = np.zeros((rows_out, codes.shape[1]), np.uint8) if out_codes is None else np.array(out_codes, np.uint8)
+    os_ = np.zeros((rows_out, scales.shape[1]), np.uint8) if out_scales is None else np.array(out_scales, np.uint8)
+    for t in range(x.shape[0]):
+        for j in range(k):
+            d = dest[t, j]
+            if 0 <= d < rows_out:
+                oc[d] = codes[t]
+                os_[d] = scales[t]
+    return oc, os_
+
+
 def transpose_2d(codes, scales, elem="e2m1"):
     """Transpose of an operand quantized with 2-D (32x32) blocks: [R, C] ->
     [C, R].  A 32x32 tile shares one scale whichever way it is read, so element

@@ -168,6 +168,29 @@ def test_gemm_rejects_bad_arguments(lib):
     assert st == mx.MX_ERR_INVALID_ARG and b"dtype" in lib.mx_last_error()
 
 
+def test_quantize_scatter_rejects_bad_arguments(lib):
+    """Every rejection happens on the host, before any launch."""
+    B = ctypes.byref
+    cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 0, 0, 0)
+    sr = mx.QuantCfgC(0, 0, 1, 0, 0, 0, 0, 0)
+    out = _tensor(64, 64)
+    P = ctypes.c_void_p
+    st = lib.mx_quantize_scatter(P(16), 1, 16, 64, 64, P(16), 4, B(sr), B(out), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"RNE" in lib.mx_last_error()
+    st = lib.mx_quantize_scatter(P(16), 1, 16, 64, 64, P(16), 4, B(mx.QuantCfgC(1, 0, 0, 0, 0, 0, 0, 0)), B(out),
+                                 None)
+    assert st == mx.MX_ERR_UNSUPPORTED
+    st = lib.mx_quantize_scatter(P(16), 1, 16, 96, 96, P(16), 4, B(cfg), B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"out.K" in lib.mx_last_error()
+    st = lib.mx_quantize_scatter(P(16), 1, 16, 64, 64, None, 4, B(cfg), B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"dest" in lib.mx_last_error()
+    st = lib.mx_quantize_scatter(P(16), 1, 16, 64, 60, P(16), 4, B(cfg), B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"ld_src" in lib.mx_last_error()
+    st = lib.mx_quantize_scatter(P(16), 1, 16, 64, 64, P(16), -1, B(cfg), B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG
+    assert lib.mx_quantize_scatter(P(16), 1, 16, 64, 64, P(16), 0, B(cfg), B(out), None) == mx.MX_OK
+
+
 def test_gemm_quantize_rejects_bad_arguments(lib):
     """Every rejection happens on the host, before any launch."""
     B = ctypes.byref

@@ -353,3 +353,61 @@ def test_quantize_gather_scale_modes(scale_mode):
     oc, os_ = oracle.quantize_gather(x, rows, **kw)
     codes_equal(host(q.scales), os_, "scales")
     codes_equal(host(q.codes), oc, "codes")
+
+
+def _scatter_dest(token_of_row, k):
+    """dest[t*k + j]: the output rows of token t (each token named k times)."""
+    order = np.argsort(token_of_row, kind="stable")
+    assert np.all(np.bincount(token_of_row, minlength=len(token_of_row) // k) == k)
+    return order.astype(np.int32)
+
+
+@pytest.mark.parametrize("rht,mode", [(False, "floor"), (True, "floor"), (True, "round_up"), (False, "prescale_3_4")])
+def test_quantize_scatter_matches_oracle_and_gather(rht, mode):
+    """Scatter-quantize of 300 token rows (k = 4, C = 2880, bf16) into a marked
+    output: every routed row equals the oracle's scatter and the GPU gather
+    form with the inverse index; a destination outside the output is
+    skipped and its row keeps the marker."""
+    need_gpu()
+    rng = np.random.default_rng(31 + rht)
+    T, k, C = 300, 4, 2880
+    x = workloads.to_bf16(rng.standard_normal((T, C)).astype(np.float32)).cuda()
+    tok = rng.permutation(np.repeat(np.arange(T), k))          # token of each output row
+    dest = _scatter_dest(tok, k)
+    dest_h = dest.copy()
+    dest_h[7] = T * k + 3                                       # skipped: its row keeps the marker
+    mask = 0x2468ACE1 if rht else None
+    banner(f"quantize_scatter rht={rht} {mode}")
+    out = mx.empty_mx(T * k, C)
+    out.codes.fill_(0x5A)
+    out.scales.fill_(0x5A)
+    mx.quantize_scatter(x, to_dev(dest_h), k, rht_mask=mask, out=out, scale_mode=mode)
+    xf = host(x.float())
+    oc, os_ = oracle.quantize_scatter(xf, dest_h, k, T * k, np.full((T * k, C // 2), 0x5A, np.uint8),
+                                      np.full((T * k, C // 32), 0x5A, np.uint8), rht_mask=mask, scale_mode=mode)
+    codes_equal(host(out.codes), oc, "codes")
+    codes_equal(host(out.scales), os_, "scales")
+    g = mx.quantize_gather(x, to_dev(tok.astype(np.int32)), rht_mask=mask, scale_mode=mode)
+    keep = np.ones(T * k, bool)
+    keep[dest[7]] = False
+    codes_equal(host(out.codes)[keep], host(g.codes)[keep], "codes vs gather")
+    codes_equal(host(out.scales)[keep], host(g.scales)[keep], "scales vs gather")
+
+
+def test_quantize_scatter_moe_full_size():
+    """The MoE front end at full size: 16384 token rows (bf16, C = 2880) routed
+    top-4 to 32 experts (Zipf 1.1); scattering each token once equals the
+    gather form over the 65536 routed rows bit for bit, and 32 sampled routed
+    rows equal the oracle."""
+    need_gpu()
+    tok, _ = workloads.moe_routing()
+    x = workloads.to_bf16(workloads.moe_tokens()).cuda()
+    dest = _scatter_dest(tok, 4)
+    banner("quantize_scatter moe full size")
+    s = mx.quantize_scatter(x, to_dev(dest), 4)
+    g = mx.quantize_gather(x, to_dev(tok.astype(np.int32)))
+    assert torch.equal(s.codes, g.codes) and torch.equal(s.scales, g.scales)
+    rows = np.sort(np.random.default_rng(3).choice(len(tok), 32, replace=False))
+    oc, os_ = oracle.quantize(host(x.float())[tok[rows]])
+    codes_equal(host(s.codes)[rows], oc, "sampled codes")
+    codes_equal(host(s.scales)[rows], os_, "sampled scales")

@@ -495,3 +495,31 @@ def test_transpose_2d_other_element_types(elem):
     assert np.array_equal(tc, dc) and np.array_equal(ts, ds)
     bc, bs = oracle.transpose_2d(tc, ts, elem)
     assert np.array_equal(bc, lc) and np.array_equal(bs, ls)
+
+
+def test_scatter_equals_gather_with_the_inverse_index():
+    """Top-k routing: every output row is named by exactly one (token, slot)
+    pair, so the scatter form (each token quantized once, stored k times)
+    must give the gathered form's bytes with the inverse index, for RNE with
+    and without the transform and in every scale mode; a destination outside
+    the output is skipped and an unnamed row keeps its old bytes."""
+    rng = np.random.default_rng(77)
+    T, k, C = 12, 3, 96
+    x = (rng.standard_normal((T, C)) * np.exp(rng.uniform(-3, 3, (T, 1)))).astype(np.float32)
+    perm = rng.permutation(T * k)                 # output row of (token t, slot j) = perm[t*k + j]
+    inv = np.empty(T * k, np.int64)
+    inv[perm] = np.arange(T * k) // k             # token of each output row
+    for mask, mode in [(None, "floor"), (0x5A5A1234, "round_up"), (None, "prescale_3_4")]:
+        sc, ss = oracle.quantize_scatter(x, perm, k, T * k, rht_mask=mask, scale_mode=mode)
+        gc, gs = oracle.quantize_gather(x, inv, rht_mask=mask, scale_mode=mode)
+        np.testing.assert_array_equal(sc, gc)
+        np.testing.assert_array_equal(ss, gs)
+    dest = perm.copy()
+    dest[4] = T * k + 7                          # outside: skipped
+    old_c = np.full((T * k, C // 2), 0xA5, np.uint8)
+    old_s = np.full((T * k, C // 32), 0x11, np.uint8)
+    sc, ss = oracle.quantize_scatter(x, dest, k, T * k, old_c, old_s)
+    assert np.all(sc[perm[4]] == 0xA5) and np.all(ss[perm[4]] == 0x11)
+    qc, qs = oracle.quantize(x)
+    np.testing.assert_array_equal(sc[perm[5]], qc[5 // k])
+    np.testing.assert_array_equal(ss[perm[5]], qs[5 // k])
