@@ -99,6 +99,7 @@ class Workload:
         assert np.all(np.bincount(tok, minlength=16384) == 4)
         self.m_dest = torch.from_numpy(order.astype(np.int32)).to(dev)
         self.m_qa2 = mx.empty_mx(65536, 2880, device=dev)
+        self.m_qy = mx.empty_mx(65536, 5760, device=dev)
         self.m_offsets = torch.from_numpy(offsets).to(dev)
         E, K, N = 32, 2880, 5760
         self.mb = mx.empty_mx(N, K, "2d", device=dev, experts=E)
@@ -174,9 +175,10 @@ class Workload:
         that reuses the forward weight through its exact 2-D transpose, the
         MXFP8 / MXFP6 element types at the fprop shape, the fprop product
         quantized in the GEMM epilogue (compare with fprop_gemm plus
-        unfused_quantize_y, the bf16 output's quantization), and the gather
-        form of the MoE front end (the step uses the scatter form: each token
-        row quantized once and stored to its 4 routed rows, the same bytes)."""
+        unfused_quantize_y, the bf16 output's quantization), the gather form
+        of the MoE front end (the step uses the scatter form: each token row
+        quantized once and stored to its 4 routed rows, the same bytes), and
+        the MoE grouped product quantized in its epilogue."""
         t_bytes = 2 * (2880 * 5760 // 2 + (2880 // 32) * (5760 // 32))
         return [
             ("dgrad_transpose_w", lambda: mx.transpose(self.d_qw, out=self.d_qwt), "hbm", t_bytes),
@@ -197,6 +199,9 @@ class Workload:
             ("unfused_quantize_y", lambda: mx.quantize(self.f_y, out=self.g_qy2), "hbm", quant_bytes(16384, 5760)),
             ("moe_gather_quantize_a", lambda: mx.quantize_gather(self.mx_tok, self.m_rows, out=self.m_qa2), "hbm",
              gather_quant_bytes(16384, 65536, 2880)),
+            ("moe_fused_grouped_gemm_quantize_y", lambda: mx.grouped_gemm_quantize(self.m_qa, self.m_offsets, self.mb,
+                                                                                   out=self.m_qy), "mfma",
+             2 * 65536 * 5760 * 2880),
         ]
 
 

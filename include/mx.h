@@ -338,6 +338,26 @@ mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, in
                           int64_t expert_stride_scales, void* C, int32_t c_dtype, int64_t ldc,
                           void* stream);
 
+/*
+ * mx_grouped_gemm_quantize — the product of mx_grouped_gemm quantized in the
+ * GEMM epilogue into an MXFP4 operand blocked along N, as mx_gemm_quantize
+ * does for the dense product (the expert outputs never reach memory in
+ * float32 or bf16).  Equal to mx_grouped_gemm with float32 output followed by
+ * mx_quantize of the rows it writes (RNE, no transform, the given scale mode).
+ *
+ *   A, d_group_offsets, E, B, expert strides: as mx_grouped_gemm; MXFP4
+ *               operands, N = B->rows >= 256 and a multiple of 32, scale rows
+ *               16-byte aligned with strides (and the expert scale stride) a
+ *               multiple of 16, E <= 960.
+ *   scale_mode  an mx_scale_mode.
+ *   out         host struct of device buffers: rows = A->rows, K = N, 1-D,
+ *               MXFP4.  Rows past off[E] are not written.
+ *   Other shapes or layouts return MX_ERR_UNSUPPORTED without launching.
+ */
+mx_status mx_grouped_gemm_quantize(const mx_tensor* A, const int32_t* d_group_offsets, int32_t E,
+                                   const mx_tensor* B, int64_t expert_stride_codes, int64_t expert_stride_scales,
+                                   int32_t scale_mode, mx_tensor* out, void* stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* mx_last_error(void);
 

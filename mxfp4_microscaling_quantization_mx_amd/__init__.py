@@ -32,7 +32,7 @@ _ELEM = {"e2m1": (0, 4), "e4m3": (1, 8), "e5m2": (2, 8), "e2m3": (3, 6), "e3m2":
 _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
 EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
-            "mx_gemm_quantize", "mx_gemm_workspace_size", "mx_grouped_gemm", "mx_last_error",
+            "mx_gemm_quantize", "mx_gemm_workspace_size", "mx_grouped_gemm", "mx_grouped_gemm_quantize", "mx_last_error",
             "mx_version")
 
 
@@ -80,8 +80,9 @@ def load_library(path=LIB_PATH):
     lib.mx_gemm_workspace_size.argtypes = [I64, I64, I64]
     lib.mx_gemm_workspace_size.restype = ctypes.c_size_t
     lib.mx_grouped_gemm.argtypes = [PT, P, I32, PT, I64, I64, P, I32, I64, P]
+    lib.mx_grouped_gemm_quantize.argtypes = [PT, P, I32, PT, I64, I64, I32, PT, P]
     for f in ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
-              "mx_gemm_quantize", "mx_grouped_gemm"):
+              "mx_gemm_quantize", "mx_grouped_gemm", "mx_grouped_gemm_quantize"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mx_last_error.restype = ctypes.c_char_p
     lib.mx_last_error.argtypes = []
@@ -288,6 +289,26 @@ def grouped_gemm(a, offsets, b, out_dtype=torch.bfloat16, out=None):
     _check(lib.mx_grouped_gemm(ctypes.byref(at), _ptr(offsets), E, ctypes.byref(b0),
                                b.codes.stride(0), b.scales.stride(0), _ptr(out),
                                _DTYPE[out.dtype], out.stride(0), _stream(out)))
+    return out
+
+
+def grouped_gemm_quantize(a, offsets, b, scale_mode="floor", out=None):
+    """The grouped product quantized along N into an MXFP4 operand [M, N] in
+    the GEMM epilogue (see mx_grouped_gemm_quantize); arguments as
+    grouped_gemm."""
+    lib = load_library()
+    E = b.codes.shape[0]
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.numel() != E + 1:
+        raise ValueError("offsets must be an int32 CUDA tensor with E+1 entries")
+    N = b.codes.shape[1]
+    if out is None:
+        out = empty_mx(a.rows, N, device=a.codes.device)
+    b0 = MxTensorC(b.codes.data_ptr(), b.scales.data_ptr(), N, b.K, b.codes.stride(1),
+                   b.scales.stride(1), _BLOCK[b.block], _ELEM[b.elem][0])
+    at, ot = a.c_struct(), out.c_struct()
+    _check(lib.mx_grouped_gemm_quantize(ctypes.byref(at), _ptr(offsets), E, ctypes.byref(b0), b.codes.stride(0),
+                                        b.scales.stride(0), _SCALE[scale_mode], ctypes.byref(ot),
+                                        _stream(out.codes)))
     return out
 
 

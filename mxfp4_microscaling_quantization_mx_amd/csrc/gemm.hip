@@ -280,6 +280,27 @@ __global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256(MxOperand A, MxO
   t256::run_tiles<false, B2D, OUT_BF16 ? t256::OUT_BF16_ : t256::OUT_F32, true>(sc, sd, K, C, ldc, lds);
 }
 
+// The grouped kernel with the quantizing epilogue (swapped MFMA operands): the
+// rows of each expert's product leave as MXFP4 codes and scale bytes along N.
+template <bool B2D>
+__global__ __launch_bounds__(64 * GW, 1) void k_grouped_gemm256_q(MxOperand A, MxOperand B, int64_t M_cap, int N,
+                                                                int K, const int32_t* __restrict__ offsets, int E,
+                                                                int64_t stride_codes, int64_t stride_scales,
+                                                                t256::QOut qo, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[t256s::LDS_BYTES];
+  __shared__ int tab[3 * GG_EMAX + 1];
+  __shared__ GroupedParams prm;
+  build_expert_table(offsets, E, M_cap, tab);   // ends with a barrier
+  const int total_slots = tab[E];
+  if (threadIdx.x == 0)
+    prm = GroupedParams{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
+                        (int)A.ld_scales, N, tiles_n, E, total_slots, 0, 0};
+  __syncthreads();
+  const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
+  const t256::Strides sd{(int)A.ld_codes, (int)A.ld_scales, (int)B.ld_codes, (int)B.ld_scales};
+  t256s::run_tiles<false, B2D, t256s::OUT_MX, true>(sc, sd, K, nullptr, 0, lds, qo);
+}
+
 // ---------------------------------------------------------------- 128x128 tiles
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -855,6 +876,37 @@ hipError_t launch_gemm_quantize(const GemmQuantArgs& a, hipStream_t st) {
   if (a.a_2d) { if (a.b_2d) MX_GQ(true, true); else MX_GQ(true, false); }
   else { if (a.b_2d) MX_GQ(false, true); else MX_GQ(false, false); }
 #undef MX_GQ
+  return hipGetLastError();
+}
+
+bool grouped_quantize_supported(const GroupedQuantArgs& q) {
+  const GroupedGemmArgs& a = q.g;
+  const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) && (a.stride_scales % 16 == 0) &&
+                     ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
+  const int64_t slot_bound = (a.M_cap + 255) / 256 + a.E;
+  return a.a_elem == 0 && a.b_elem == 0 && !a.a_2d && a.N >= 256 && a.N % 32 == 0 && words && a.E <= GG_EMAX &&
+         256 * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) && a.K < (1ll << 31) &&
+         slot_bound * ((a.N + 255) / 256) < (1ll << 31) && q.ld_codes % 4 == 0 && (uintptr_t)q.codes % 4 == 0 &&
+         256 * q.ld_codes < (1ll << 31) && 256 * q.ld_scales < (1ll << 31) && q.ld_codes >= a.N / 2 &&
+         q.ld_scales >= a.N / 32;
+}
+
+hipError_t launch_grouped_gemm_quantize(const GroupedQuantArgs& q, hipStream_t st) {
+  const GroupedGemmArgs& a = q.g;
+  if (a.M_cap == 0 || a.N == 0) return hipSuccess;
+  if (!grouped_quantize_supported(q)) return hipErrorNotSupported;
+  const int64_t slot_bound = (a.M_cap + 255) / 256 + a.E;
+  const int tiles_n = (int)((a.N + 255) / 256);
+  const int64_t tiles = slot_bound * tiles_n;
+  const int cus = cu_count();
+  const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
+  const t256::QOut qo{q.codes, q.scales, (int)q.ld_codes, (int)q.ld_scales, q.scale_mode};
+  if (a.b_2d)
+    hipLaunchKernelGGL((k_grouped_gemm256_q<true>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap, (int)a.N,
+                       (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, qo, tiles_n);
+  else
+    hipLaunchKernelGGL((k_grouped_gemm256_q<false>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap, (int)a.N,
+                       (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, qo, tiles_n);
   return hipGetLastError();
 }
 

@@ -387,6 +387,60 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale
   return hip_status(mx::launch_gemm_quantize(a, static_cast<hipStream_t>(stream)), "mx_gemm_quantize");
 }
 
+mx_status mx_grouped_gemm_quantize(const mx_tensor* A, const int32_t* d_group_offsets, int32_t E,
+                                   const mx_tensor* B, int64_t expert_stride_codes, int64_t expert_stride_scales,
+                                   int32_t scale_mode, mx_tensor* out, void* stream) {
+  g_err[0] = '\0';
+  mx_status st = check_tensor(A, "mx_grouped_gemm_quantize: A");
+  if (st != MX_OK) return st;
+  st = check_tensor(B, "mx_grouped_gemm_quantize: B");
+  if (st != MX_OK) return st;
+  st = check_tensor(out, "mx_grouped_gemm_quantize: out");
+  if (st != MX_OK) return st;
+  if (A->block != MX_BLOCK_1D) return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm_quantize: A must use 1-D blocks");
+  if (A->K != B->K)
+    return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm_quantize: A.K=%lld != B.K=%lld", (long long)A->K,
+                (long long)B->K);
+  if (E < 1) return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm_quantize: E=%d < 1", E);
+  if (!d_group_offsets) return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm_quantize: null group offsets");
+  if (scale_mode < MX_SCALE_FLOOR || scale_mode > MX_SCALE_PRESCALE_3_4)
+    return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm_quantize: unknown scale mode %d", scale_mode);
+  if (expert_stride_codes < 0 || expert_stride_scales < 0 || expert_stride_codes % 16)
+    return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm_quantize: expert strides must be >= 0 (codes stride %% 16 == 0)");
+  const int64_t M = A->rows, N = B->rows;
+  if (out->rows != M || out->K != N)
+    return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm_quantize: out is [%lld, %lld], the product is [%lld, %lld]",
+                (long long)out->rows, (long long)out->K, (long long)M, (long long)N);
+  if (A->elem != MX_ELEM_E2M1 || B->elem != MX_ELEM_E2M1 || out->elem != MX_ELEM_E2M1)
+    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm_quantize: MXFP4 operands and output only");
+  if (out->block != MX_BLOCK_1D)
+    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm_quantize: the output uses 1-D blocks");
+  if (M == 0 || N == 0) return MX_OK;
+  mx::GroupedQuantArgs q{};
+  q.g.A = operand(A);
+  q.g.B = operand(B);
+  q.g.a_2d = false;
+  q.g.b_2d = B->block == MX_BLOCK_2D;
+  q.g.M_cap = M;
+  q.g.N = N;
+  q.g.K = A->K;
+  q.g.offsets = d_group_offsets;
+  q.g.E = E;
+  q.g.stride_codes = expert_stride_codes;
+  q.g.stride_scales = expert_stride_scales;
+  q.codes = out->codes;
+  q.scales = out->scales;
+  q.ld_codes = out->ld_codes;
+  q.ld_scales = out->ld_scales;
+  q.scale_mode = scale_mode;
+  if (!mx::grouped_quantize_supported(q))
+    return fail(MX_ERR_UNSUPPORTED,
+                "mx_grouped_gemm_quantize: needs N >= 256, 16-byte aligned scale rows with strides %% 16 == 0 (and "
+                "expert scale stride), E <= 960, operands under 2 GiB");
+  return hip_status(mx::launch_grouped_gemm_quantize(q, static_cast<hipStream_t>(stream)),
+                    "mx_grouped_gemm_quantize");
+}
+
 mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, int32_t E,
                           const mx_tensor* B, int64_t expert_stride_codes,
                           int64_t expert_stride_scales, void* C, int32_t c_dtype, int64_t ldc,

@@ -81,6 +81,16 @@ struct GroupedGemmArgs {
   int a_elem = 0, b_elem = 0;  // mx_elem of A and B
 };
 
+// The grouped product quantized along N (MXFP4, 1-D blocks, RNE) in the
+// epilogue: g describes the product (its C, ldc and out_bf16 are unused).
+struct GroupedQuantArgs {
+  GroupedGemmArgs g;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t ld_codes, ld_scales;
+  int scale_mode;
+};
+
 struct TransposeArgs {
   const uint8_t* in_codes;
   const uint8_t* in_scales;
@@ -104,5 +114,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 bool gemm_quantize_supported(const GemmQuantArgs& a);
 hipError_t launch_gemm_quantize(const GemmQuantArgs& a, hipStream_t st);
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st);
+// Whether the 256x256 grouped pipeline (the only grouped kernel with the
+// quantizing epilogue) takes this problem; launch_grouped_gemm_quantize
+// requires it.
+bool grouped_quantize_supported(const GroupedQuantArgs& a);
+hipError_t launch_grouped_gemm_quantize(const GroupedQuantArgs& a, hipStream_t st);
 
 }  // namespace mx

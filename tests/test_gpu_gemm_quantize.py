@@ -118,3 +118,74 @@ def test_gemm_quantize_fprop_full_size():
     oc, os_ = oracle.quantize(host(y)[rows])
     codes_equal(host(fused.codes)[rows], oc, "sampled rows vs oracle")
     codes_equal(host(fused.scales)[rows], os_, "sampled scales vs oracle")
+
+
+# ---------------------------------------------------------------- grouped
+def _grouped_operands(rng, offsets, N, K, M_cap):
+    E = len(offsets) - 1
+    ac, as_ = _rand_mx(rng, M_cap, K)
+    bcs, bss = zip(*[_rand_mx(rng, N, K, "2d") for _ in range(E)])
+    bc, bs = np.stack(bcs), np.stack(bss)
+    a = _upload(ac, as_)
+    ld = (bs.shape[2] + 15) // 16 * 16
+    buf = torch.full((E, bs.shape[1], ld), 0xFF, dtype=torch.uint8, device="cuda")
+    buf[:, :, :bs.shape[2]] = torch.from_numpy(bs).cuda()
+    b = mx.MXTensor(torch.from_numpy(bc).cuda(), buf[:, :, :bs.shape[2]], N, K, "2d")
+    return a, b, (ac, as_, bc, bs)
+
+
+@pytest.mark.parametrize("offsets,M_cap", [([0, 5, 5, 300, 333], 400), ([0, 600], 600),
+                                           ([0, 0, 0, 257, 257, 800], 800), ([0, 1, 2, 3, 4, 260, 261, 700], 720)])
+@pytest.mark.parametrize("N,K", [(288, 2880), (544, 416)])
+@pytest.mark.parametrize("scale_mode", ["floor", "round_up"])
+def test_grouped_gemm_quantize_matches_unfused(offsets, M_cap, N, K, scale_mode):
+    """Grouped product quantized in the epilogue (empty experts, 1-row experts,
+    tiles straddling expert boundaries, ragged N and K): rows [0, off[E])
+    equal mx_grouped_gemm (float32) + mx_quantize bit for bit and the oracle's
+    quantize of that product; rows past off[E] keep the marker."""
+    need_gpu()
+    rng = np.random.default_rng(len(offsets) * 17 + offsets[-1] + N + K)
+    a, b, (ac, as_, bc, bs) = _grouped_operands(rng, offsets, N, K, M_cap)
+    off = torch.from_numpy(np.asarray(offsets, dtype=np.int32)).cuda()
+    banner(f"grouped_gemm_quantize offsets={offsets} N={N} K={K} {scale_mode}")
+    fused = _marked_out(M_cap, N)
+    mx.grouped_gemm_quantize(a, off, b, scale_mode=scale_mode, out=fused)
+    m = offsets[-1]
+    y = mx.grouped_gemm(a, off, b, torch.float32)
+    yh = host(y)[:m]
+    unfused = mx.quantize(y[:m].contiguous(), scale_mode=scale_mode)
+    fc, fs = host(fused.codes), host(fused.scales)
+    codes_equal(fc[:m], host(unfused.codes), "codes vs grouped_gemm + quantize")
+    codes_equal(fs[:m], host(unfused.scales), "scales vs grouped_gemm + quantize")
+    oc, os_ = oracle.quantize(yh, scale_mode=scale_mode)
+    codes_equal(fc[:m], oc, "codes vs oracle")
+    codes_equal(fs[:m], os_, "scales vs oracle")
+    assert np.all(fc[m:] == 0x5A) and np.all(fs[m:] == 0x5A), "rows past the last offset written"
+    ref, bound = oracle.grouped_gemm_ref(ac[:m], as_[:m], offsets, bc, bs)
+    check_gemm(yh, ref, bound, what="grouped product")
+
+
+def test_grouped_gemm_quantize_moe_full_size():
+    """The MoE workload's grouped product (65536 routed rows x 5760, 32 experts,
+    Zipf 1.1 top-4) quantized in the epilogue equals mx_grouped_gemm (float32)
+    + mx_quantize over the whole output, and 32 sampled rows equal the
+    oracle's quantize of those product rows."""
+    need_gpu()
+    tok, offsets = workloads.moe_routing()
+    E, K, N = 32, 2880, 5760
+    banner("grouped_gemm_quantize moe full size")
+    x = workloads.to_bf16(workloads.moe_tokens()).cuda()
+    qa = mx.quantize_gather(x, torch.from_numpy(tok.astype(np.int32)).cuda())
+    qb = mx.empty_mx(N, K, "2d", experts=E)
+    for e in range(E):
+        we = workloads.to_bf16(workloads.moe_expert_weight(e)).cuda()
+        mx.quantize(we, axis="dim0", block="2d", out=mx.expert(qb, e))
+    off = torch.from_numpy(np.asarray(offsets, dtype=np.int32)).cuda()
+    fused = mx.grouped_gemm_quantize(qa, off, qb)
+    y = mx.grouped_gemm(qa, off, qb, torch.float32)
+    unfused = mx.quantize(y)
+    assert torch.equal(fused.codes, unfused.codes) and torch.equal(fused.scales, unfused.scales)
+    rows = np.sort(np.random.default_rng(8).choice(len(tok), 32, replace=False))
+    oc, os_ = oracle.quantize(host(y)[rows])
+    codes_equal(host(fused.codes)[rows], oc, "sampled rows vs oracle")
+    codes_equal(host(fused.scales)[rows], os_, "sampled scales vs oracle")
