@@ -111,3 +111,39 @@ def probe_lib():
 def save_npz(name, **arrays):
     if os.path.isdir(OUT_DIR):
         np.savez(os.path.join(OUT_DIR, name), **arrays)
+
+
+def check_quantized_product(codes, scales, ref, sum_abs, K, scale_mode="floor", what="quantized product"):
+    """MXFP4 codes/scales quantized on the GPU from its float32 GEMM product
+    against the oracle's float64 product `ref` (both [R, N], N a multiple of
+    32), without feeding any GPU value to the oracle.  The float32 product
+    differs from ref by at most (2 ceil(K/64) + 1) 2^-24 sum_abs per element
+    (sum_abs = sum_k |a_k b_k|, from oracle.gemm_ref): each 64-deep scaled
+    MFMA step adds the exact sum of its FP4 products with at most two float32
+    roundings.  Each scale byte must be the oracle's scale of some block amax
+    within that error of max |ref|, and each code the oracle's RNE code of
+    some value within that error of ref at the GPU's scale (times 3/4 in the
+    prescale mode).  Where no boundary lies inside the error, that leaves
+    exactly the oracle's answer."""
+    import oracle
+    bound = (2 * -(-K // 64) + 1) * 2.0 ** -24 * np.asarray(sum_abs, dtype=np.float64)
+    R, N = ref.shape
+    nb = N // 32
+    s = np.asarray(scales, dtype=np.int64)[:, :nb]
+    a = np.abs(ref).reshape(R, nb, 32)
+    b = np.asarray(bound, dtype=np.float64).reshape(R, nb, 32)
+    amax_lo = np.nextafter(np.maximum(a - b, 0.0).max(axis=2).astype(np.float32), np.float32(0))
+    amax_hi = np.nextafter((a + b).max(axis=2).astype(np.float32), np.float32(np.inf))
+    expo = oracle.round_up_exponent if scale_mode == "round_up" else oracle.shared_exponent
+    s_lo, s_hi = expo(amax_lo) + 127, expo(amax_hi) + 127
+    bad = (s < s_lo) | (s > s_hi)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} scale bytes outside the oracle's range; first at "
+                           f"{tuple(np.argwhere(bad)[0])}: gpu={s[bad][0]} oracle {s_lo[bad][0]}..{s_hi[bad][0]}")
+    inv = np.ldexp(1.0, -(np.repeat(s, 32, axis=1) - 127)) * (0.75 if scale_mode == "prescale_3_4" else 1.0)
+    v, bv = ref * inv, np.asarray(bound, dtype=np.float64) * inv
+    lo = oracle.e2m1_decode(oracle.round_e2m1((v - bv).astype(np.float32)))
+    hi = oracle.e2m1_decode(oracle.round_e2m1((v + bv).astype(np.float32)))
+    got = oracle.e2m1_decode(oracle.unpack_nibbles(np.asarray(codes))[:, :N])
+    bad = (got < np.minimum(lo, hi)) | (got > np.maximum(lo, hi))
+    assert not bad.any(), (f"{what}: {int(bad.sum())} codes outside the oracle's rounding of the product; first "
+                           f"at {tuple(np.argwhere(bad)[0])}")

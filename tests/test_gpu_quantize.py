@@ -371,7 +371,8 @@ def test_quantize_scatter_matches_oracle_and_gather(rht, mode):
     need_gpu()
     rng = np.random.default_rng(31 + rht)
     T, k, C = 300, 4, 2880
-    x = workloads.to_bf16(rng.standard_normal((T, C)).astype(np.float32)).cuda()
+    xc = workloads.to_bf16(rng.standard_normal((T, C)).astype(np.float32))
+    x = xc.cuda()
     tok = rng.permutation(np.repeat(np.arange(T), k))          # token of each output row
     dest = _scatter_dest(tok, k)
     dest_h = dest.copy()
@@ -382,7 +383,7 @@ def test_quantize_scatter_matches_oracle_and_gather(rht, mode):
     out.codes.fill_(0x5A)
     out.scales.fill_(0x5A)
     mx.quantize_scatter(x, to_dev(dest_h), k, rht_mask=mask, out=out, scale_mode=mode)
-    xf = host(x.float())
+    xf = xc.float().numpy()
     oc, os_ = oracle.quantize_scatter(xf, dest_h, k, T * k, np.full((T * k, C // 2), 0x5A, np.uint8),
                                       np.full((T * k, C // 32), 0x5A, np.uint8), rht_mask=mask, scale_mode=mode)
     codes_equal(host(out.codes), oc, "codes")
@@ -401,13 +402,14 @@ def test_quantize_scatter_moe_full_size():
     rows equal the oracle."""
     need_gpu()
     tok, _ = workloads.moe_routing()
-    x = workloads.to_bf16(workloads.moe_tokens()).cuda()
+    xc = workloads.to_bf16(workloads.moe_tokens())
+    x = xc.cuda()
     dest = _scatter_dest(tok, 4)
     banner("quantize_scatter moe full size")
     s = mx.quantize_scatter(x, to_dev(dest), 4)
     g = mx.quantize_gather(x, to_dev(tok.astype(np.int32)))
     assert torch.equal(s.codes, g.codes) and torch.equal(s.scales, g.scales)
     rows = np.sort(np.random.default_rng(3).choice(len(tok), 32, replace=False))
-    oc, os_ = oracle.quantize(host(x.float())[tok[rows]])
+    oc, os_ = oracle.quantize(xc.float().numpy()[tok[rows]])
     codes_equal(host(s.codes)[rows], oc, "sampled codes")
     codes_equal(host(s.scales)[rows], os_, "sampled scales")

@@ -144,3 +144,31 @@ def test_quantized_gemm_approximates_float_gemm():
         ref, _ = oracle.gemm_ref(ac, asc, bc, bsc)
         rel = np.linalg.norm(ref - exact) / np.linalg.norm(exact)
         assert rel < 0.25        # MXFP4 noise on both operands (~0.11 relative each)
+
+
+def test_quantized_product_check_accepts_the_oracle_and_rejects_one_bit_errors():
+    """The GPU tests check fused GEMM+quantize outputs with
+    gpu_util.check_quantized_product (the oracle's quantization of the float64
+    product within the float32 accumulation error).  On the CPU: the oracle's
+    own quantization of the product passes in every scale mode, and a single
+    flipped code bit or a scale byte one too large fails."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from gpu_util import check_quantized_product
+    rng = np.random.default_rng(0)
+    ac = rng.integers(0, 256, (48, 1440), dtype=np.uint8)
+    as_ = rng.integers(120, 135, (48, 90), dtype=np.uint8)
+    bc = rng.integers(0, 256, (64, 1440), dtype=np.uint8)
+    bs = rng.integers(120, 135, (64, 90), dtype=np.uint8)
+    ref, S = oracle.gemm_ref(ac, as_, bc, bs)
+    for mode in ("floor", "round_up", "prescale_3_4"):
+        qc, qs = oracle.quantize(ref.astype(np.float32), scale_mode=mode)
+        check_quantized_product(qc, qs, ref, S, 2880, mode)
+        bad = qc.copy()
+        bad[3, 5] ^= 0x01
+        with pytest.raises(AssertionError):
+            check_quantized_product(bad, qs, ref, S, 2880, mode)
+        bads = qs.copy()
+        bads[2, 1] += 1
+        with pytest.raises(AssertionError):
+            check_quantized_product(qc, bads, ref, S, 2880, mode)
