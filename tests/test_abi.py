@@ -216,6 +216,28 @@ def test_gemm_quantize_rejects_bad_arguments(lib):
     assert lib.mx_gemm_quantize(B(_tensor(0, 64)), B(b), 0, B(_tensor(0, 288)), None) == mx.MX_OK
 
 
+def test_grouped_gemm_quantize_rejects_bad_arguments(lib):
+    """Every rejection happens on the host, before any launch."""
+    B = ctypes.byref
+    P = ctypes.c_void_p
+    a, b, out = _tensor(300, 64), _tensor(288, 64, block=1), _tensor(300, 288)
+    st = lib.mx_grouped_gemm_quantize(B(a), None, 2, B(b), 1024, 64, 0, B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"offsets" in lib.mx_last_error()
+    st = lib.mx_grouped_gemm_quantize(B(a), P(16), 0, B(b), 1024, 64, 0, B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"E=0" in lib.mx_last_error()
+    st = lib.mx_grouped_gemm_quantize(B(a), P(16), 2, B(b), 1024, 64, 9, B(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"scale mode" in lib.mx_last_error()
+    st = lib.mx_grouped_gemm_quantize(B(a), P(16), 2, B(b), 1024, 64, 0, B(_tensor(300, 320)), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"out is" in lib.mx_last_error()
+    st = lib.mx_grouped_gemm_quantize(B(_tensor(320, 64, block=1)), P(16), 2, B(b), 1024, 64, 0,
+                                      B(_tensor(320, 288)), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"1-D" in lib.mx_last_error()
+    st = lib.mx_grouped_gemm_quantize(B(a), P(16), 2, B(b), 1024, 64, 0, B(out), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"N >= 256" in lib.mx_last_error()   # dense scale strides
+    assert lib.mx_grouped_gemm_quantize(B(_tensor(0, 64)), P(16), 2, B(b), 1024, 64, 0, B(_tensor(0, 288)),
+                                        None) == mx.MX_OK
+
+
 def test_grouped_gemm_rejects_bad_arguments(lib):
     a = _tensor(64, 64)
     b = _tensor(32, 64, block=1)
