@@ -10,7 +10,7 @@
 // (2 bytes in (bf16) and 0.53 bytes out per element); with it, by the VALU
 // work of the Philox draws.
 //
-// Three kernels, each with one lane per 32-element block and the whole block
+// Four kernels, each with one lane per 32-element block and the whole block
 // (transform, amax, rounding) in registers:
 //  * k_quant_rows_1d — blocks along the contiguous dim: four 16-byte loads per
 //    lane, one 16-byte code store per lane; optionally of rows gathered by
@@ -20,6 +20,8 @@
 //    element per lane, each reading 64 consecutive columns across the wave.
 //  * k_quant_tile — 2-D 32x32 tiles along the contiguous dim, fed from an LDS
 //    tile so that a half-wave holds the 32 rows of a tile.
+//  * k_quant_rows_scatter — the row kernel's block step once per source row,
+//    stored to each of the row's k destination rows (MoE routing, RNE).
 // For 2-D tiles the amax is a reduction over the 32 lanes of a half-wave.
 #include "mx_device.h"
 #include "mx_launch.h"
@@ -458,8 +460,6 @@ hipError_t launch_quantize_elem(const QuantArgs& a, hipStream_t st) {
   return a.bf16 ? launch_rows_1d<true, false, ELEM>(a, st) : launch_rows_1d<false, false, ELEM>(a, st);
 }
 
-}  // namespace
-
 // Scatter form (MXFP4, RNE): one lane per block of a source row, quantized
 // once and stored to each of the row's k destination rows dest[t * k + j]
 // (destinations outside [0, M) are skipped).  With RNE a row's codes do not
@@ -486,6 +486,8 @@ __global__ __launch_bounds__(256) void k_quant_rows_scatter(const void* __restri
     scales[d * ld_scales + kb] = (uint8_t)s;
   }
 }
+
+}  // namespace
 
 hipError_t launch_quantize_scatter(const QuantArgs& a, const int32_t* dest, int k, int64_t M, hipStream_t st) {
   if (a.R == 0 || a.C == 0 || k == 0) return hipSuccess;
