@@ -305,7 +305,8 @@ mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dty
  *               multiple of 16, as every mx_tensor).
  *   M, N >= 256 (the epilogue exists on the 256 x 256 pipeline only); other
  *   shapes or layouts return MX_ERR_UNSUPPORTED without launching.
- *   M or N = 0: nothing is written.
+ *   M or N = 0: nothing is written.  K = 0: the product is zero, so every
+ *   block gets scale byte 0 and zero codes.  Row padding of out is untouched.
  */
 mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale_mode, mx_tensor* out,
                            void* stream);
