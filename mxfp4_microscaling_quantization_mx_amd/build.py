@@ -10,6 +10,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -41,19 +42,21 @@ def _compile(src, obj):
 
 def build(verbose=True):
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    for s in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
-        _compile(os.path.join(CSRC, s), obj)
-        objs.append(obj)
+    jobs = [(os.path.join(CSRC, s), os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES]
+    probe = os.path.exists(PROBE_SRC)
+    if probe:
+        jobs.append((PROBE_SRC, os.path.join(BUILD, "gpu_probes.o")))
+    # the translation units are independent: compile them side by side
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(workers) as pool:
+        for f in [pool.submit(_compile, src, obj) for src, obj in jobs]:
+            f.result()
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + objs)
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + [obj for _, obj in jobs[:len(SOURCES)]])
     os.replace(tmp, LIB)
-    if os.path.exists(PROBE_SRC):
-        pobj = os.path.join(BUILD, "gpu_probes.o")
-        _compile(PROBE_SRC, pobj)
+    if probe:
         tmp = PROBE_LIB + ".tmp"
-        _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, pobj])
+        _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, jobs[-1][1]])
         os.replace(tmp, PROBE_LIB)
     return LIB
 

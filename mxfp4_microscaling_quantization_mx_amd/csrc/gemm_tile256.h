@@ -697,8 +697,9 @@ __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int
 // amax of the sign-cleared bits over the lane's 16 values, then with the
 // partner lane; the scale by the mode's rule (NaN/Inf -> 0xFF with zero
 // codes); the 3/4 prescale after the scale; the hardware RNE convert at the
-// power-of-two scale (2^-127 as the float32 subnormal, which the convert
-// divides by exactly).  Each lane converts its 16 values into two words of
+// power-of-two scale (for the lowest byte, whose 2^-127 is a float32
+// subnormal, the values are multiplied by 2^127 first, exactly, and converted
+// at scale 1, as the row quantizer does).  Each lane converts its 16 values into two words of
 // code bytes, trades one word with its partner, and stores 8 of the block's
 // 16 code bytes; lane kh = 0 stores the scale byte.  The same arithmetic as
 // the row quantizer without the transform.
@@ -724,10 +725,15 @@ __device__ __forceinline__ void store_tile_mx(const Acc& acc, const QOut& q, int
         m = max(m, max(__float_as_uint(x[r]) & 0x7FFFFFFFu, __float_as_uint(x[r + 1]) & 0x7FFFFFFFu));
       m = max(m, (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)m));
       const uint32_t s = q.scale_mode == 1 ? scale_code_round_up(m) : scale_code_from_absmax_bits(m);
-      const float sc = __uint_as_float(max(s << 23, 0x00400000u));
+      float sc = __uint_as_float(s << 23);
       float v[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) v[r] = q.scale_mode == 2 ? 0.75f * x[r] : x[r];
+      if (s == 0u) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = v[r] * __uint_as_float(0x7F000000u);
+        sc = 1.0f;
+      }
       // words p0 (columns 4kh + 0..3 and 8 + 4kh + 0..3) and p1 (16 + ..., 24 + ...)
       uint32_t p0 = 0u, p1 = 0u;
       p0 = cvt_pk_fp4<0>(p0, v[0], v[1], sc);

@@ -199,6 +199,51 @@ def test_grouped_gemm_rows_past_last_offset_untouched():
     check_gemm(c[:100], ref, bound, what="grouped head")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gemm256_writes_nothing_outside_c(out_dtype):
+    """256x256 path with M and N not multiples of 256: C is a view into a
+    larger marker-filled buffer (extra rows below M, extra columns past N in
+    every row); nothing but C[:M, :N] may change."""
+    need_gpu()
+    rng = np.random.default_rng(14)
+    M, N, K = 300, 520, 416
+    ac, as_ = _rand_mx(rng, M, K)
+    bc, bs = _rand_mx(rng, N, K)
+    buf = torch.full((M + 70, N + 40), 7.0, dtype=out_dtype, device="cuda")
+    banner(f"gemm256 guard rows {out_dtype}")
+    mx.gemm(_upload(ac, as_), _upload(bc, bs), out=buf[:M, :N])
+    c = host(buf.float())
+    assert np.all(c[M:] == 7.0) and np.all(c[:, N:] == 7.0), "wrote outside C"
+    ref, bound = oracle.gemm_ref(ac, as_, bc, bs)
+    check_gemm(c[:M, :N], ref, bound, bf16=(out_dtype == torch.bfloat16), what="guarded")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_grouped_gemm256_rows_past_last_offset_untouched(out_dtype):
+    """256x256 grouped path (N >= 256, 16-byte scale rows): rows past off[E]
+    keep their marker for both output types, including the rows of the last
+    expert's partial tile."""
+    need_gpu()
+    rng = np.random.default_rng(15)
+    M_cap, N, K = 700, 288, 416
+    offsets = [0, 3, 260, 390]
+    E = len(offsets) - 1
+    ac, as_ = _rand_mx(rng, M_cap, K)
+    bcs, bss = zip(*[_rand_mx(rng, N, K, "2d") for _ in range(E)])
+    bc, bs = np.stack(bcs), np.stack(bss)
+    ld = (bs.shape[2] + 15) // 16 * 16
+    sbuf = torch.full((E, bs.shape[1], ld), 0xFF, dtype=torch.uint8, device="cuda")
+    sbuf[:, :, :bs.shape[2]] = to_dev(bs)
+    b = mx.MXTensor(to_dev(bc), sbuf[:, :, :bs.shape[2]], N, K, "2d")
+    out = torch.full((M_cap, N), 7.0, dtype=out_dtype, device="cuda")
+    banner(f"grouped256 tail untouched {out_dtype}")
+    mx.grouped_gemm(_upload(ac, as_), to_dev(np.asarray(offsets, dtype=np.int32)), b, out=out)
+    c = host(out.float())
+    assert np.all(c[offsets[-1]:] == 7.0), "rows past the last offset written"
+    ref, bound = oracle.grouped_gemm_ref(ac[:offsets[-1]], as_[:offsets[-1]], offsets, bc, bs)
+    check_gemm(c[:offsets[-1]], ref, bound, bf16=(out_dtype == torch.bfloat16), what="grouped256 head")
+
+
 # ---------------------------------------------------------------- full-size workloads
 def _sample(rng, n, k):
     return np.sort(rng.choice(n, k, replace=False))

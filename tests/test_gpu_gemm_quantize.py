@@ -88,6 +88,28 @@ def test_gemm_quantize_nan_and_zero_rows():
     assert np.all(fs[40] == 0) and np.all(fc[40] == 0)
 
 
+def test_gemm_quantize_scale_byte_zero_blocks():
+    """Products whose 32-column block maximum lies below 2^-124 take the
+    lowest scale byte (exponent -127; "MXFP4", AI Wiki, §Format specification:
+    E8M0 range) and still carry non-zero codes: each value is divided by
+    2^-127 exactly before rounding.  A scales of 17 .. 25 with B scales of 100
+    put the block maxima around 2^-126 .. 2^-121, so both byte 0 and the bytes
+    above it occur, with float32 subnormal products among them."""
+    need_gpu()
+    rng = np.random.default_rng(12)
+    M, N, K = 256, 288, 256
+    ac, as_ = _rand_mx(rng, M, K)
+    bc, bs = _rand_mx(rng, N, K)
+    as_[:] = rng.integers(17, 26, as_.shape).astype(np.uint8)
+    bs[:] = 100
+    banner("gemm_quantize scale byte 0 blocks")
+    fc, fs = _check_fused(_upload(ac, as_), _upload(bc, bs), M, N, "floor", (ac, as_, bc, bs, "1d", "1d"))
+    zero = fs == 0
+    codes = oracle.unpack_nibbles(fc).reshape(M, N // 32, 32)
+    assert zero.sum() > 50 and (~zero).sum() > 50
+    assert np.count_nonzero(codes[zero] & 7) > 1000, "byte-0 blocks should hold non-zero codes"
+
+
 def test_gemm_quantize_zero_k():
     """K = 0: the product is zero, so every block gets scale byte 0 and zero
     codes (what mx_quantize gives for zeros)."""
