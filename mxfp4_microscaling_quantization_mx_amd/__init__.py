@@ -244,17 +244,41 @@ def transpose(q, out=None):
     return out
 
 
+_WORKSPACES = {}
+
+
+def gemm_workspace(M, N, K, device="cuda"):
+    """A workspace for mx_gemm of an M x N x K problem (None if it needs none):
+    one zero-filled buffer per device, grown on demand and reused (every call
+    leaves it fit for the next, see mx_gemm_workspace_size).  Calls that share
+    it must not overlap, so callers on several streams pass their own."""
+    n = load_library().mx_gemm_workspace_size(M, N, K)
+    if not n:
+        return None
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < n:
+        ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def gemm(a, b, out_dtype=torch.float32, out=None, workspace=None):
-    """C = A * B^T for MX operands A [M, K], B [N, K] (see mx_gemm)."""
+    """C = A * B^T for MX operands A [M, K], B [N, K] (see mx_gemm).  Shapes
+    that mx_gemm splits along K use `workspace` (a zero-filled uint8 CUDA
+    tensor of at least mx_gemm_workspace_size bytes) or the per-device one of
+    gemm_workspace."""
     lib = load_library()
     if out is None:
         out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
     ws = lib.mx_gemm_workspace_size(a.rows, b.rows, a.K)
     if ws and workspace is None:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=a.codes.device)
+        workspace = gemm_workspace(a.rows, b.rows, a.K, a.codes.device)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     at, bt = a.c_struct(), b.c_struct()
     _check(lib.mx_gemm(ctypes.byref(at), ctypes.byref(bt), _ptr(out), _DTYPE[out.dtype],
-                       out.stride(0), _ptr(workspace), ws, _stream(out)))
+                       out.stride(0), _ptr(workspace), nbytes, _stream(out)))
     return out
 
 

@@ -58,23 +58,15 @@ struct XcdShare {
   __device__ int tile(int j) const { return first + k + j * step; }
 };
 
-// Tile order: groups of GM M-tiles, each walked N-tile by N-tile, so that a
-// run of consecutive tiles shares a few A and B panels (GM = 8 for the dense
-// GEMM; 2 for the grouped one, whose row tiles belong to different experts'
-// weights, measured ~3 % faster there).
-template <int GM>
-__device__ __forceinline__ void group_order(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int group = t / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-  const int in = t - group * GM * tiles_n;
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
+// Tile order (t256c::group_order): groups of GM M-tiles, each walked N-tile
+// by N-tile (GM = 8 for the dense GEMM; 2 for the grouped one, whose row tiles
+// belong to different experts' weights, measured ~3 % faster there).
+using t256c::group_order;
 
 constexpr int GW = t256::WAVES;
 
 struct DenseSched {
+  static constexpr bool UNITS = false;
   const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
   int M, N, tiles_m, tiles_n;
   XcdShare share;
@@ -178,6 +170,7 @@ __device__ __forceinline__ void lds_i32x2(const int* p0, const int* p1, int& v0,
 }
 
 struct GroupedSched {
+  static constexpr bool UNITS = false;
   const GroupedParams* prm;                 // LDS
   const int* tab;                           // LDS: pre [E+1] exclusive prefix of slots, lo [E], hi [E]
   XcdShare share;
@@ -803,6 +796,16 @@ static int cu_count() {
   return cache[dev];
 }
 
+// 256x256 tiles: scale rows are fetched 16 bytes at a time (16-byte aligned
+// rows), and the operands are addressed with 32-bit offsets.
+bool gemm256_layout_ok(const GemmArgs& a) {
+  const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) &&
+                     ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
+  const bool small = a.M * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
+                     a.M * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31) && a.K < (1ll << 31);
+  return a.M >= 256 && a.N >= 256 && words && small;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.a_elem != 0 || a.b_elem != 0) {
@@ -814,13 +817,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       default: return launch_gemm_mx_b<0>(a, st);
     }
   }
-  // 256x256 tiles: scale rows are fetched 16 bytes at a time (16-byte aligned
-  // rows), and the operands are addressed with 32-bit offsets.
-  const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) &&
-                     ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
-  const bool small = a.M * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
-                     a.M * a.ldc * (a.out_bf16 ? 2 : 4) < (1ll << 31) && a.K < (1ll << 31);
-  if (a.M >= 256 && a.N >= 256 && words && small) {
+  if (gemm256_layout_ok(a)) {
     const int tiles_m = (int)((a.M + 255) / 256), tiles_n = (int)((a.N + 255) / 256);
     const int tiles = tiles_m * tiles_n;
     const int cus = cu_count();

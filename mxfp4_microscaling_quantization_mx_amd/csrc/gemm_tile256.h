@@ -75,12 +75,27 @@ struct TileInfo {
   const uint8_t* b_scales;
   int m0, n0, M, N;
   int64_t c_row0;
+  // Schedules that split K (Sched::UNITS) hand out units = a range of stages
+  // [k0, k0 + ns) of one tile, k0 even; the others always run whole tiles.
+  int k0, ns;
 };
 
 // Row strides (bytes) shared by all tiles of a launch.
 struct Strides {
   int lda, ldsa, ldb, ldsb;
 };
+
+// Tile order: groups of GM M-tiles, each walked N-tile by N-tile, so that a
+// run of consecutive tiles shares a few A and B panels.
+template <int GM>
+__device__ __forceinline__ void group_order(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int in = t - group * GM * tiles_n;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
 
 // Destination of the quantizing epilogue: the float32 tile quantized along N
 // into MXFP4 blocks of 32 (RNE), codes [M, N/2] and scale bytes [M, N/32]
@@ -103,6 +118,7 @@ using t256c::TileInfo;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -464,6 +480,9 @@ __device__ __forceinline__ void zero(Acc& acc) {
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int mlim, int nlim);
 
+template <bool OUT_BF16, class Sched>
+__device__ __forceinline__ void store_unit(Acc& acc, const Sched& sc, int j, void* C, int64_t ldc);
+
 // Output kinds of run_tiles: float32, bf16, or the quantizing epilogue
 // (MX_T256_SWAP = 1 only).
 constexpr int OUT_F32 = 0, OUT_BF16_ = 1, OUT_MX = 2;
@@ -477,10 +496,20 @@ __device__ __forceinline__ void store_tile_mx(const Acc& acc, const QOut& q, int
 // past the limits read as zeros and are never stored.  Byte extents of the
 // operands must be < 2 GiB.  `lds` holds LDS_BYTES: the two code slots, the
 // two scale slots and a dummy region.
+//
+// With Sched::UNITS the schedule hands out units instead of whole tiles: unit
+// j covers stages [k0, k0 + ns) of its tile, k0 and ns even (a tile with an
+// odd stage count gets one more stage, past K, whose codes read as zeros and
+// whose scale bytes are masked to 0, adding exact zeros).  The stage sequence
+// runs through the units back to back; with every unit an even number of
+// stages, global stage g uses scale pair g / 2.  Each unit ends in
+// store_unit (the split-K epilogue) instead of a plain store.
 template <bool A2D, bool B2D, int OUT, bool SPLIT, class Sched>
 __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, int K, void* C, int64_t ldc,
                                           uint8_t* lds, const QOut& qo = QOut{}) {
   static_assert((OUT == OUT_MX) == (MX_T256_SWAP != 0), "the quantizing epilogue needs the swapped operand order");
+  constexpr bool UNITS = Sched::UNITS;
+  static_assert(!UNITS || OUT != OUT_MX, "units end in the split-K epilogue, which stores float32 or bf16");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -504,7 +533,9 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
   const int nfull = K / TK;                 // stages without a K tail
   const int kchunks = (K - nfull * TK) / 32;          // K-blocks in the tail stage (0 if none)
   const int npairs = (nst + 1) / 2;
-  const int gtotal = ntiles * nst;
+  int gtotal;
+  if constexpr (UNITS) gtotal = sc.total_stages();
+  else gtotal = ntiles * nst;
   // scale bytes of the tail stage's blocks: low word blocks 0-3, high word 4-7
   const uint32_t tail_lo = kchunks >= 4 ? 0xFFFFFFFFu : (1u << (8 * kchunks)) - 1u;
   const uint32_t tail_hi = kchunks <= 4 ? 0u : (1u << (8 * (kchunks - 4))) - 1u;
@@ -526,9 +557,15 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
   const int sh = 8 * kh;
 
   // The stage whose loads are issued next ("prefetch" position j2, s2) and
-  // its tile's load state, refreshed once per tile.
+  // its tile's load state, refreshed once per tile.  For units, kb2 is the
+  // first stage of unit j2 within its tile and ns2 its stage count.
   int j2 = 0, s2 = 0;
   TileInfo t2 = sc.tile(0);
+  int kb2 = 0, ns2 = nst;
+  if constexpr (UNITS) {
+    kb2 = t2.k0;
+    ns2 = t2.ns;
+  }
   __amdgpu_buffer_rsrc_t ra2, rb2, rs2;
   uint32_t pa[4], pb[4], psc;
   auto load_tile = [&]() {
@@ -537,24 +574,36 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
     psc = scale_offset<A2D, B2D>(t2, sd, wave, lane);
   };
   auto advance = [&]() {
-    if (++s2 == nst) {
+    if (++s2 == ns2) {
       s2 = 0;
       if (++j2 < ntiles) {
         t2 = sc.tile(j2);
+        if constexpr (UNITS) {
+          kb2 = t2.k0;
+          ns2 = t2.ns;
+        }
         load_tile();
       }
     }
   };
-  // Code offsets of the prefetch stage (the tail stage masks the chunks past K).
+  // Code offsets of the prefetch stage (the tail stage masks the chunks past
+  // K; a unit's padding stage past the tail masks all of them).
   auto stage_offsets = [&](uint32_t va[4], uint32_t vb[4]) {
+    const int k = kb2 + s2;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bool live = s2 < nfull || load_chunk(wave, lane, t) < kchunks;
+      bool live;
+      if constexpr (UNITS) live = k < nfull || (k == nfull && load_chunk(wave, lane, t) < kchunks);
+      else live = k < nfull || load_chunk(wave, lane, t) < kchunks;
       va[t] = live ? pa[t] : OOB;
       vb[t] = live ? pb[t] : OOB;
     }
   };
-  auto sslot_of = [&](int j, int s) { return ((j * npairs + (s >> 1)) & 1) * SSLOT; };
+  // scale slot of global stage gs at prefetch position (j2, s2)
+  auto sslot2 = [&](int gs) {
+    if constexpr (UNITS) return ((gs >> 1) & 1) * SSLOT;
+    else return ((j2 * npairs + (s2 >> 1)) & 1) * SSLOT;
+  };
   load_tile();
 
   // Prologue: global stages 0 and 1 with the compiler's load builtins.
@@ -562,10 +611,10 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     if (g >= gtotal) break;
-    if (!(s2 & 1)) issue_scales(rs2, psc, s2 >> 1, sslots + sslot_of(j2, s2), wave);
+    if (!(s2 & 1)) issue_scales(rs2, psc, (kb2 + s2) >> 1, sslots + sslot2(g), wave);
     uint32_t va[4], vb[4];
     stage_offsets(va, vb);
-    issue_codes(ra2, rb2, va, vb, (uint32_t)s2 * ROWB, lds + (g & 1) * STAGE_BYTES, wave);
+    issue_codes(ra2, rb2, va, vb, (uint32_t)(kb2 + s2) * ROWB, lds + (g & 1) * STAGE_BYTES, wave);
     if (g == 1) loads1 = CODE_LOADS + ((s2 & 1) ? 0 : 1);
     advance();
   }
@@ -576,7 +625,18 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
   read_first(lds_addr + ra_k[0], lds_addr + rb_k[0], sl_addr + s_a, sl_addr + s_b, a, b, wa, wb);
 
   int s = 0, j = 0;                         // stage s of tile j is multiplied
-  int s1 = 1 % nst, j1 = 1 / nst;           // the stage after it
+  int kb = 0, ns = nst;                     // (units: first stage and stage count of unit j)
+  int s1 = 1 % nst, j1 = 1 / nst;           // the stage after it (whole tiles)
+  if constexpr (UNITS) {
+    const TileInfo t0 = sc.tile(0);
+    kb = t0.k0;
+    ns = t0.ns;
+  }
+  // scale slot and word offset of the stage after global stage g
+  auto snext_off = [&](int g) {
+    if constexpr (UNITS) return (((g + 1) >> 1) & 1) * SSLOT + 8 * ((g + 1) & 1);
+    else return ((j1 * npairs + (s1 >> 1)) & 1) * SSLOT + 8 * (s1 & 1);
+  };
   // Pending B-half loads; none before the first stage: those 4 loads point
   // past the end and land in the dummy region (slots 0 and 1 are live).
   uint32_t pend_vb[4] = {OOB, OOB, OOB, OOB};
@@ -584,8 +644,11 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
   uint32_t pend_cs = 0, pend_m0 = lds_addr + 2 * STAGE_BYTES + 2 * SSLOT;
   for (int g = 0; g < gtotal; ++g) {
     const uint32_t slot = lds_addr + (uint32_t)((g & 1) * STAGE_BYTES);
-    const uint32_t keep_lo = s < nfull ? 0xFFFFFFFFu : tail_lo;
-    const uint32_t keep_hi = s < nfull ? 0xFFFFFFFFu : tail_hi;
+    uint32_t keep_lo = kb + s < nfull ? 0xFFFFFFFFu : tail_lo;
+    uint32_t keep_hi = kb + s < nfull ? 0xFFFFFFFFu : tail_hi;
+    if constexpr (UNITS) {
+      if (kb + s > nfull) keep_lo = keep_hi = 0u;   // a padding stage past the tail
+    }
     int sa[TI], sb[TJ], sa2[TI], sb2[TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
@@ -618,32 +681,44 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
     // also read all of stage g (codes and scales), so its slots take stage g+2.
     wait_vmcnt(0);
     bare_barrier();
-    if (more && !(s2 & 1)) issue_scales(rs2, psc, s2 >> 1, sslots + sslot_of(j2, s2), wave);
+    if (more && !(s2 & 1)) issue_scales(rs2, psc, (kb2 + s2) >> 1, sslots + sslot2(g + 2), wave);
     // The next stage's first-step operands and scale bytes (in the very last
     // stage these reads of unused slots are harmless).
     const uint32_t next = lds_addr + (uint32_t)(((g + 1) & 1) * STAGE_BYTES);
-    const uint32_t snext = sl_addr + (uint32_t)(sslot_of(j1, s1) + 8 * (s1 & 1));
+    const uint32_t snext = sl_addr + (uint32_t)snext_off(g);
     if constexpr (SPLIT) {
       step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
-                slot + 4096u * wave, va, ra2, (uint32_t)s2 * ROWB);
+                slot + 4096u * wave, va, ra2, (uint32_t)(kb2 + s2) * ROWB);
       // the B half goes out in the next iteration's first step
 #pragma unroll
       for (int t = 0; t < 4; ++t) pend_vb[t] = vb[t];
       pend_rb = rb2;
-      pend_cs = (uint32_t)s2 * ROWB;
+      pend_cs = (uint32_t)(kb2 + s2) * ROWB;
       pend_m0 = slot + OPB + 4096u * wave;
     } else {
+      static_assert(!UNITS, "units need the split load issue");
       step_last8(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
-                 slot + 4096u * wave, va, vb, ra2, rb2, (uint32_t)s2 * ROWB);
+                 slot + 4096u * wave, va, vb, ra2, rb2, (uint32_t)(kb2 + s2) * ROWB);
     }
     if (more) advance();
-    if (++s1 == nst) {
-      s1 = 0;
-      ++j1;
+    if constexpr (!UNITS) {
+      if (++s1 == nst) {
+        s1 = 0;
+        ++j1;
+      }
     }
-    if (++s == nst) {                       // tile j is complete
+    if (++s == ns) {                        // tile (unit) j is complete
       drain(acc);
-      store(sc.tile(j));
+      if constexpr (UNITS) {
+        store_unit<OUT == OUT_BF16_>(acc, sc, j, C, ldc);
+        if (j + 1 < ntiles) {
+          const TileInfo tn = sc.tile(j + 1);
+          kb = tn.k0;
+          ns = tn.ns;
+        }
+      } else {
+        store(sc.tile(j));
+      }
       zero(acc);
       s = 0;
       ++j;
@@ -652,40 +727,188 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
   __syncthreads();                          // LDS may be reused by the caller
 }
 
-// Store the wave's part of the tile with bounds-checked buffer stores: the
-// resource ends after row mlim (relative to the tile origin C), and lanes
-// whose columns are >= nlim point past it, so nothing outside the matrix is
-// written.  Row offsets are wave-uniform (scalar), column offsets per lane.
-// (Each store instruction writes two 32-lane row segments; gathering 4
-// columns per lane for wider stores measured slower.)
+// Output stores are bounds-checked buffer stores: the resource ends after row
+// mlim (relative to the tile origin C), and lanes whose columns are >= nlim
+// point past it, so nothing outside the matrix is written.  Row offsets are
+// wave-uniform (scalar), column offsets per lane.  (Each store instruction
+// writes two 32-lane row segments; gathering 4 columns per lane for wider
+// stores measured slower.)
+//
+// Buffer resource of the output tile at C: it ends after row mlim (relative
+// to the tile origin) and column nlim of that row.
 template <bool OUT_BF16>
-__device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int mlim, int nlim) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_out_rsrc(void* C, int ldc, int mlim, int nlim) {
+  constexpr int ES = OUT_BF16 ? 2 : 4;
+  const int rows = mlim < 256 ? mlim : 256;
+  return rsrc(C, (uint32_t)((rows - 1) * ldc * ES + (nlim < 256 ? nlim : 256) * ES));
+}
+
+// Store 32x32 MFMA tile (i, j) of the wave's part (values x in the
+// accumulator layout) through the resource r of the output tile.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_subtile(const v16f& x, int i, int j, __amdgpu_buffer_rsrc_t r, int ldc,
+                                              int nlim) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, kh = lane >> 5;
   constexpr int ES = OUT_BF16 ? 2 : 4;
-  const int rows = mlim < 256 ? mlim : 256;
-  const __amdgpu_buffer_rsrc_t r = rsrc(C, (uint32_t)((rows - 1) * ldc * ES + (nlim < 256 ? nlim : 256) * ES));
+  const int col = wn * TJ * 32 + 32 * j + l32;
+  const uint32_t voff = col < nlim ? (uint32_t)(((wm * TI * 32 + 4 * kh) * ldc + col) * ES) : OOB;
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int col = wn * TJ * 32 + 32 * j + l32;
-    const uint32_t voff = col < nlim ? (uint32_t)(((wm * TI * 32 + 4 * kh) * ldc + col) * ES) : OOB;
+  for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t soff = (uint32_t)((32 * i + 8 * r4 + q) * ldc * ES);
+      const float v = x[4 * r4 + q];
+      if (OUT_BF16)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, voff, soff, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    }
+}
+
+// Store the wave's part of the tile.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int mlim, int nlim) {
+  const __amdgpu_buffer_rsrc_t r = tile_out_rsrc<OUT_BF16>(C, ldc, mlim, nlim);
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
+  for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t soff = (uint32_t)((32 * i + 8 * r4 + q) * ldc * ES);
-          const float v = acc.t[i][j][4 * r4 + q];
-          if (OUT_BF16)
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, voff,
-                                                  soff, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
-        }
+    for (int i = 0; i < TI; ++i) store_subtile<OUT_BF16>(acc.t[i][j], i, j, r, ldc, nlim);
+}
+
+// ------------------------------------------------------------ split-K epilogue
+// A unit that covers only part of its tile's K range ends here.  The tile's
+// segments (its K range cut at the unit boundaries, segment 0 first along K)
+// each hold a float32 partial product; the tile is their sum taken in segment
+// order, ((p_0 + p_1) + p_2) + ..., each addition rounded to float32, so the
+// result does not depend on which workgroup gets there last.  No workgroup
+// waits for another: each segment first reads the tile's counter; if every
+// other segment has already published its partial (counter = S - 1) this one
+// is the last and sums; otherwise it writes its partial to its workspace slot,
+// makes it visible at device scope and increments the counter, and the
+// segment that sees S - 1 come back from that increment sums.  The summing
+// segment resets the counter to 0, so the workspace is left as it was found.
+// The summing segment takes its own partial from its accumulators and the
+// others from their slots.
+// Partial slots hold the 256x256 floats in the accumulator layout: float4 q
+// (= 4 (TJ i + j) + r4) of thread tid at float4 index q * 512 + tid.
+constexpr int SLOT_BYTES = TM * TN * 4;    // one partial tile
+
+// The partials pass between workgroups on different XCDs, whose L2 caches are
+// not kept coherent with each other for plain accesses: they are stored and
+// loaded at system scope (cache policy SC0 | SC1), which writes through to
+// memory and reads from it.
+constexpr int CPOL_SYSTEM = 1 | 16;
+
+// A wave-uniform 64-bit address (so buffer resources built from it stay in
+// scalar registers instead of being looped over lane by lane).
+__device__ __forceinline__ float* uniform_ptr(float* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (float*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Partial slot `slot` as a buffer resource (one lane offset, the float4 index
+// in the scalar offset, so no per-load 64-bit addresses are held).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float* parts, int slot) {
+  return rsrc(uniform_ptr(parts + (size_t)__builtin_amdgcn_readfirstlane(slot) * (SLOT_BYTES / 4)),
+              (uint32_t)SLOT_BYTES);
+}
+
+// Write this workgroup's accumulators to partial slot `slot`.
+__device__ __forceinline__ void put_partial(const Acc& acc, float* parts, int slot) {
+  constexpr int NT = 64 * WAVES;
+  const __amdgpu_buffer_rsrc_t r = slot_rsrc(parts, slot);
+  const uint32_t voff = 16u * threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TJ; ++jj)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const v16f& x = acc.t[i][jj];
+        const v4u w = {__float_as_uint(x[4 * r4]), __float_as_uint(x[4 * r4 + 1]), __float_as_uint(x[4 * r4 + 2]),
+                       __float_as_uint(x[4 * r4 + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, (uint32_t)(((i * TJ + jj) * 4 + r4) * NT * 16),
+                                               CPOL_SYSTEM);
+      }
+}
+
+// Publish this workgroup's partial: every wave's stores complete and written
+// back at device scope, then one increment of the counter; returns the
+// counter's value before it (the same in every thread).
+__device__ __forceinline__ int publish(const Acc& acc, float* parts, int slot, int* cnt, volatile int* flag) {
+  put_partial(acc, parts, slot);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __syncthreads();
+  return *flag;
+}
+
+template <bool OUT_BF16, class Sched>
+__device__ __forceinline__ void store_unit(Acc& acc, const Sched& sc, int j, void* C, int64_t ldc) {
+  constexpr int ES = OUT_BF16 ? 2 : 4;
+  const TileInfo ti = sc.tile(j);
+  uint8_t* const ct = static_cast<uint8_t*>(C) + (ti.c_row0 * ldc + ti.n0) * ES;
+  const auto sg = sc.segment(j);
+  if (sg.S == 1) {
+    store_tile<OUT_BF16>(acc, ct, (int)ldc, ti.M - ti.m0, ti.N - ti.n0);
+    return;
+  }
+  int* const cnt = sc.counter(sg.t);
+  volatile int* const aux = sc.aux();      // LDS: [0] counter value
+  float* const parts = sc.parts();
+  __syncthreads();
+  if (threadIdx.x == 0) aux[0] = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (aux[0] != sg.S - 1 && publish(acc, parts, sg.slot, cnt, aux) != sg.S - 1) return;
+  // the last segment: every other partial is published
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // Sum each 32x32 MFMA tile over the segments in order into temporaries (the
+  // accumulators are only read: rewriting all 128 of them on this path would
+  // leave the register allocator two versions to merge) and store it.
+  constexpr int NT = 64 * WAVES;
+  const __amdgpu_buffer_rsrc_t out = tile_out_rsrc<OUT_BF16>(ct, (int)ldc, ti.M - ti.m0, ti.N - ti.n0);
+  const __amdgpu_buffer_rsrc_t whole = rsrc(uniform_ptr(parts), 0xFFFFFFFFu);
+  const uint32_t voff = 16u * threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TJ; ++jj) {
+      v16f r;
+#pragma unroll 1
+      for (int q = 0; q < sg.S; ++q) {
+        v16f p;
+        if (q == sg.k) {
+          p = acc.t[i][jj];
+        } else {
+          const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(sg.slot_of(q)) * (uint32_t)SLOT_BYTES +
+                                (uint32_t)((i * TJ + jj) * 4 * NT * 16);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const v4u v =
+                __builtin_amdgcn_raw_buffer_load_b128(whole, voff, base + (uint32_t)(r4 * NT * 16), CPOL_SYSTEM);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[4 * r4 + e] = __uint_as_float(v[e]);
+          }
+        }
+        if (q == 0) {
+          r = p;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) r[e] = r[e] + p[e];
+        }
+      }
+      store_subtile<OUT_BF16>(r, i, jj, out, (int)ldc, ti.N - ti.n0);
+    }
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 #if MX_T256_SWAP

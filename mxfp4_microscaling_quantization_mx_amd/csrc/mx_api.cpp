@@ -305,17 +305,13 @@ mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream) 
 }
 
 size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return mx::gemm_splitk_workspace(M, N, K);
 }
 
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
                   void* workspace, size_t ws_bytes, void* stream) {
   g_err[0] = '\0';
-  (void)workspace;
-  (void)ws_bytes;
   mx_status st = check_tensor(A, "mx_gemm: A");
   if (st != MX_OK) return st;
   st = check_tensor(B, "mx_gemm: B");
@@ -342,6 +338,15 @@ mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dty
   a.out_bf16 = c_dtype == MX_DT_BF16;
   a.a_elem = A->elem;
   a.b_elem = B->elem;
+  if (a.K > 0 && mx::gemm_splitk_applies(a)) {
+    const size_t need = mx::gemm_splitk_workspace(M, N, a.K);
+    if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+      return fail(MX_ERR_INVALID_ARG,
+                  "mx_gemm: this shape is split along K and needs a 256-byte aligned workspace of %zu bytes "
+                  "(got %zu bytes at %p)",
+                  need, ws_bytes, workspace);
+    return hip_status(mx::launch_gemm_splitk(a, workspace, static_cast<hipStream_t>(stream)), "mx_gemm");
+  }
   return hip_status(mx::launch_gemm(a, static_cast<hipStream_t>(stream)), "mx_gemm");
 }
 

@@ -109,6 +109,16 @@ hipError_t launch_quantize_scatter(const QuantArgs& a, const int32_t* dest, int 
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+// Whether the 256x256 MXFP4 pipeline takes this problem's layout (16-byte
+// scale rows, operands and output under 2 GiB, M and N >= 256).
+bool gemm256_layout_ok(const GemmArgs& a);
+// Split-K form of the 256x256 MXFP4 GEMM (gemm_splitk.hip): the workspace it
+// needs for an M x N x K problem (0 when that shape is not split), whether it
+// takes this problem, and its launch (workspace of that many bytes, 256-byte
+// aligned, zero-filled before its first use and left so by every launch).
+size_t gemm_splitk_workspace(int64_t M, int64_t N, int64_t K);
+bool gemm_splitk_applies(const GemmArgs& a);
+hipError_t launch_gemm_splitk(const GemmArgs& a, void* workspace, hipStream_t st);
 // Whether the 256x256 pipeline (the only kernel with the quantizing epilogue)
 // takes this problem; launch_gemm_quantize requires it.
 bool gemm_quantize_supported(const GemmQuantArgs& a);

@@ -168,6 +168,22 @@ def test_gemm_rejects_bad_arguments(lib):
     assert st == mx.MX_ERR_INVALID_ARG and b"dtype" in lib.mx_last_error()
 
 
+def test_gemm_workspace_contract(lib):
+    """Shapes split along K report their workspace size; mx_gemm then refuses
+    a missing, short or misaligned workspace before launching anything."""
+    assert lib.mx_gemm_workspace_size(2880, 2880, 16384) > 0          # weight gradient: 144 tiles
+    assert lib.mx_gemm_workspace_size(16384, 5760, 2880) == 0         # fprop: whole tiles
+    assert lib.mx_gemm_workspace_size(2880, 2880, 0) == 0
+    assert lib.mx_gemm_workspace_size(0, 2880, 16384) == 0
+    need = lib.mx_gemm_workspace_size(2880, 2880, 16384)
+    a = _tensor(2880, 16384, codes=1 << 20, scales=1 << 21, ldc=8192, lds=512)
+    b = _tensor(2880, 16384, codes=1 << 22, scales=1 << 23, ldc=8192, lds=512)
+    C = ctypes.c_void_p(1 << 24)
+    for ws, nbytes in [(None, 0), (ctypes.c_void_p(1 << 26), need - 1), (ctypes.c_void_p((1 << 26) + 16), need)]:
+        st = lib.mx_gemm(ctypes.byref(a), ctypes.byref(b), C, 0, 2880, ws, nbytes, None)
+        assert st == mx.MX_ERR_INVALID_ARG and b"workspace" in lib.mx_last_error()
+
+
 def test_quantize_scatter_rejects_bad_arguments(lib):
     """Every rejection happens on the host, before any launch."""
     B = ctypes.byref
