@@ -837,15 +837,19 @@ __device__ __forceinline__ void put_partial(const Acc& acc, float* parts, int sl
       }
 }
 
-// Publish this workgroup's partial: every wave's stores complete and written
-// back at device scope, then one increment of the counter; returns the
-// counter's value before it (the same in every thread).
+// Publish this workgroup's partial: every wave's stores complete (they write
+// through at system scope, so completion means visible to every XCD), then
+// one increment of the counter; returns the counter's value before it (the
+// same in every thread).  No fence is needed on either side: the partials
+// never pass through a cache that another XCD could read stale (the summing
+// segment loads them at system scope too), and the compiler's agent-scope
+// fences (a write-back and an invalidate of the whole L2) measured ~70 us on
+// the weight-gradient shape.
 __device__ __forceinline__ int publish(const Acc& acc, float* parts, int slot, int* cnt, volatile int* flag) {
   put_partial(acc, parts, slot);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wave's stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
@@ -870,7 +874,7 @@ __device__ __forceinline__ void store_unit(Acc& acc, const Sched& sc, int j, voi
   __syncthreads();
   if (aux[0] != sg.S - 1 && publish(acc, parts, sg.slot, cnt, aux) != sg.S - 1) return;
   // the last segment: every other partial is published
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
   // Sum each 32x32 MFMA tile over the segments in order into temporaries (the
   // accumulators are only read: rewriting all 128 of them on this path would
   // leave the register allocator two versions to merge) and store it.
