@@ -277,8 +277,11 @@ mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream);
  *              1-D or 2-D scales (2-D requires rows % 32 == 0).
  *   C          device; [M, N] of c_dtype, row stride ldc elements (>= N).
  *   workspace  device scratch of ws_bytes bytes, needed only when
- *              mx_gemm_workspace_size(M, N, K) > 0 (split-K partial sums);
- *              otherwise may be NULL.
+ *              mx_gemm_workspace_size(M, N, K) > 0 (split-K partial sums;
+ *              256-byte aligned, contract at mx_gemm_workspace_size) and
+ *              the problem takes the MXFP4 256 x 256 kernels; otherwise may
+ *              be NULL.  A missing, short or misaligned workspace for a split
+ *              shape returns MX_ERR_INVALID_ARG without launching.
  *   M, N or K = 0: C is left untouched (K = 0 writes zeros).
  */
 mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
@@ -311,8 +314,42 @@ mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dty
 mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale_mode, mx_tensor* out,
                            void* stream);
 
-/* Bytes of device workspace mx_gemm needs for this problem (0 if none). */
+/*
+ * mx_gemm_workspace_size — bytes of device workspace mx_gemm needs for an
+ * M x N x K problem (0 if none).  Problems with too few 256 x 256 output tiles
+ * to fill the GPU, or a K longer than one float32 accumulator may sum while
+ * keeping 1e-5 sum|a b| ("MXFP4", AI Wiki, §Conversion rules: the long dot
+ * product is a sum of block dot products accumulated in float32), are split
+ * along K: each output is accumulated in float32 over K segments of at most
+ * 10240 and the segment sums are added in K order, an order fixed by the
+ * shape alone (the result is the same bit for bit on every run).  With one
+ * rounding per 64-deep step the error of an output is at most
+ * (n - 1 + S - 1) 2^-24 sum|a b| to first order, n the 64-deep steps of its
+ * longest segment (<= 160) and S its segments (<= 8): 8.6e-6 sum|a b| for the
+ * weight gradient 2880 x 2880 x 16384 (n = 144, S <= 3).
+ * Workspace contract: zero-filled before its first use (e.g. by a
+ * hipMemsetAsync right after allocating it); every call leaves it fit for
+ * the next call of any shape (its tile counters back at zero); calls that
+ * share a workspace must not run concurrently.  Layout: 64 KiB of tile
+ * counters, then the float32 partial tiles (256 KiB each).
+ */
 size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * mx_gemm_noalloc — mx_gemm for callers that cannot allocate (code under HIP
+ * graph capture, serving loops, harnesses that forbid allocation): the same
+ * product and the same kernels, with the split-K workspace taken from the
+ * library's own device array (64 KiB + 128 MiB per GPU the library runs on,
+ * held until the process ends) instead of a caller buffer.  Allocates and
+ * frees nothing.  Every call on a GPU shares that GPU's array, so calls that
+ * overlap on one GPU (concurrent streams, other threads) race; the array's
+ * counters start at zero and every call leaves them so.  Shapes whose split
+ * would need more than the array holds (more than 256 workers, see
+ * mx_gemm_workspace_size) return MX_ERR_UNSUPPORTED without launching.  Other
+ * arguments and errors as mx_gemm.
+ */
+mx_status mx_gemm_noalloc(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                          void* stream);
 
 /*
  * mx_grouped_gemm — the MoE expert GEMM over rows grouped by expert ("MXFP4",

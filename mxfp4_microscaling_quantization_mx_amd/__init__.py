@@ -32,8 +32,8 @@ _ELEM = {"e2m1": (0, 4), "e4m3": (1, 8), "e5m2": (2, 8), "e2m3": (3, 6), "e3m2":
 _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
 EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
-            "mx_gemm_quantize", "mx_gemm_workspace_size", "mx_grouped_gemm", "mx_grouped_gemm_quantize", "mx_last_error",
-            "mx_version")
+            "mx_gemm_quantize", "mx_gemm_workspace_size", "mx_gemm_noalloc", "mx_grouped_gemm", "mx_grouped_gemm_quantize",
+            "mx_last_error", "mx_version")
 
 
 class MxTensorC(ctypes.Structure):
@@ -77,12 +77,13 @@ def load_library(path=LIB_PATH):
     lib.mx_transpose.argtypes = [PT, PT, P]
     lib.mx_gemm.argtypes = [PT, PT, P, I32, I64, P, ctypes.c_size_t, P]
     lib.mx_gemm_quantize.argtypes = [PT, PT, I32, PT, P]
+    lib.mx_gemm_noalloc.argtypes = [PT, PT, P, I32, I64, P]
     lib.mx_gemm_workspace_size.argtypes = [I64, I64, I64]
     lib.mx_gemm_workspace_size.restype = ctypes.c_size_t
     lib.mx_grouped_gemm.argtypes = [PT, P, I32, PT, I64, I64, P, I32, I64, P]
     lib.mx_grouped_gemm_quantize.argtypes = [PT, P, I32, PT, I64, I64, I32, PT, P]
     for f in ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
-              "mx_gemm_quantize", "mx_grouped_gemm", "mx_grouped_gemm_quantize"):
+              "mx_gemm_quantize", "mx_gemm_noalloc", "mx_grouped_gemm", "mx_grouped_gemm_quantize"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mx_last_error.restype = ctypes.c_char_p
     lib.mx_last_error.argtypes = []
@@ -279,6 +280,19 @@ def gemm(a, b, out_dtype=torch.float32, out=None, workspace=None):
     at, bt = a.c_struct(), b.c_struct()
     _check(lib.mx_gemm(ctypes.byref(at), ctypes.byref(bt), _ptr(out), _DTYPE[out.dtype],
                        out.stride(0), _ptr(workspace), nbytes, _stream(out)))
+    return out
+
+
+def gemm_noalloc(a, b, out_dtype=torch.float32, out=None):
+    """C = A * B^T through mx_gemm_noalloc: the library's own split-K scratch,
+    no workspace argument (for callers that cannot allocate; the output is
+    still the caller's)."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=out_dtype, device=a.codes.device)
+    at, bt = a.c_struct(), b.c_struct()
+    _check(lib.mx_gemm_noalloc(ctypes.byref(at), ctypes.byref(bt), _ptr(out), _DTYPE[out.dtype], out.stride(0),
+                               _stream(out)))
     return out
 
 

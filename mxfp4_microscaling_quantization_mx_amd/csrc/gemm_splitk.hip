@@ -26,6 +26,8 @@
 #undef MX_T256_SWAP
 #include "mx_launch.h"
 
+#include <mutex>
+
 namespace mx {
 
 namespace {
@@ -225,7 +227,37 @@ __global__ __launch_bounds__(64 * t256k::WAVES, 1) void k_gemm256_sk(MxOperand A
   t256k::run_tiles<A2D, B2D, OUT_BF16 ? t256k::OUT_BF16_ : t256k::OUT_F32, true>(sc, sd, K, C, ldc, lds);
 }
 
+// The workspace of the allocation-free entry point (mx_gemm_noalloc): the
+// counter region and 2 x 256 partial slots, enough for every plan with at most
+// 256 workers (all shapes whose tiles' K ranges fit 256 x SK_MAX_PAIRS pairs,
+// the weight gradient among them).  Zero at load; every call leaves its
+// counters at zero again.  In host code `scratch` names a host-side stand-in:
+// only the address hipGetSymbolAddress returns for the current device is
+// passed to kernels.
+constexpr size_t SK_SCRATCH_BYTES = SK_COUNTER_BYTES + (size_t)2 * SK_ROUND * t256k::SLOT_BYTES;
+static __device__ __align__(256) uint8_t scratch[SK_SCRATCH_BYTES];
+
 }  // namespace
+
+size_t gemm_splitk_scratch_bytes() { return SK_SCRATCH_BYTES; }
+
+hipError_t gemm_splitk_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t gemm_splitk_workspace(int64_t M, int64_t N, int64_t K) {
   SkPlan p;

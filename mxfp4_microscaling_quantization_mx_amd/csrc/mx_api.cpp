@@ -309,37 +309,53 @@ size_t mx_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
   return mx::gemm_splitk_workspace(M, N, K);
 }
 
-mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
-                  void* workspace, size_t ws_bytes, void* stream) {
-  g_err[0] = '\0';
-  mx_status st = check_tensor(A, "mx_gemm: A");
+namespace {
+
+// Validate an mx_gemm call and describe it; M = 0 or N = 0 leaves a.M or a.N 0.
+mx_status gemm_args(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                    const char* what, mx::GemmArgs& a) {
+  char name[64];
+  std::snprintf(name, sizeof(name), "%s: A", what);
+  mx_status st = check_tensor(A, name);
   if (st != MX_OK) return st;
-  st = check_tensor(B, "mx_gemm: B");
+  std::snprintf(name, sizeof(name), "%s: B", what);
+  st = check_tensor(B, name);
   if (st != MX_OK) return st;
   if (A->K != B->K)
-    return fail(MX_ERR_INVALID_ARG, "mx_gemm: A.K=%lld != B.K=%lld", (long long)A->K, (long long)B->K);
+    return fail(MX_ERR_INVALID_ARG, "%s: A.K=%lld != B.K=%lld", what, (long long)A->K, (long long)B->K);
   if (c_dtype != MX_DT_F32 && c_dtype != MX_DT_BF16)
-    return fail(MX_ERR_INVALID_ARG, "mx_gemm: unknown output dtype %d", c_dtype);
+    return fail(MX_ERR_INVALID_ARG, "%s: unknown output dtype %d", what, c_dtype);
   const int64_t M = A->rows, N = B->rows;
+  a = mx::GemmArgs{};
+  a.M = M;
+  a.N = N;
   if (M == 0 || N == 0) return MX_OK;
-  if (!C) return fail(MX_ERR_INVALID_ARG, "mx_gemm: null C");
-  if (ldc < N) return fail(MX_ERR_INVALID_ARG, "mx_gemm: ldc=%lld < N=%lld", (long long)ldc, (long long)N);
-  if ((M + 127) / 128 > 65535) return fail(MX_ERR_UNSUPPORTED, "mx_gemm: M too large");
-  mx::GemmArgs a{};
+  if (!C) return fail(MX_ERR_INVALID_ARG, "%s: null C", what);
+  if (ldc < N) return fail(MX_ERR_INVALID_ARG, "%s: ldc=%lld < N=%lld", what, (long long)ldc, (long long)N);
+  if ((M + 127) / 128 > 65535) return fail(MX_ERR_UNSUPPORTED, "%s: M too large", what);
   a.A = operand(A);
   a.B = operand(B);
   a.a_2d = A->block == MX_BLOCK_2D;
   a.b_2d = B->block == MX_BLOCK_2D;
-  a.M = M;
-  a.N = N;
   a.K = A->K;
   a.C = C;
   a.ldc = ldc;
   a.out_bf16 = c_dtype == MX_DT_BF16;
   a.a_elem = A->elem;
   a.b_elem = B->elem;
+  return MX_OK;
+}
+
+}  // namespace
+
+mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = '\0';
+  mx::GemmArgs a;
+  const mx_status st = gemm_args(A, B, C, c_dtype, ldc, "mx_gemm", a);
+  if (st != MX_OK || a.M == 0 || a.N == 0) return st;
   if (a.K > 0 && mx::gemm_splitk_applies(a)) {
-    const size_t need = mx::gemm_splitk_workspace(M, N, a.K);
+    const size_t need = mx::gemm_splitk_workspace(a.M, a.N, a.K);
     if (!workspace || ws_bytes < need || !aligned(workspace, 256))
       return fail(MX_ERR_INVALID_ARG,
                   "mx_gemm: this shape is split along K and needs a 256-byte aligned workspace of %zu bytes "
@@ -348,6 +364,27 @@ mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dty
     return hip_status(mx::launch_gemm_splitk(a, workspace, static_cast<hipStream_t>(stream)), "mx_gemm");
   }
   return hip_status(mx::launch_gemm(a, static_cast<hipStream_t>(stream)), "mx_gemm");
+}
+
+mx_status mx_gemm_noalloc(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                          void* stream) {
+  g_err[0] = '\0';
+  mx::GemmArgs a;
+  const mx_status st = gemm_args(A, B, C, c_dtype, ldc, "mx_gemm_noalloc", a);
+  if (st != MX_OK || a.M == 0 || a.N == 0) return st;
+  if (a.K > 0 && mx::gemm_splitk_applies(a)) {
+    const size_t need = mx::gemm_splitk_workspace(a.M, a.N, a.K);
+    if (need > mx::gemm_splitk_scratch_bytes())
+      return fail(MX_ERR_UNSUPPORTED,
+                  "mx_gemm_noalloc: this shape's split-K workspace (%zu bytes) exceeds the library's scratch "
+                  "(%zu bytes); use mx_gemm with a workspace",
+                  need, mx::gemm_splitk_scratch_bytes());
+    void* scratch = nullptr;
+    const hipError_t e = mx::gemm_splitk_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "mx_gemm_noalloc: scratch address");
+    return hip_status(mx::launch_gemm_splitk(a, scratch, static_cast<hipStream_t>(stream)), "mx_gemm_noalloc");
+  }
+  return hip_status(mx::launch_gemm(a, static_cast<hipStream_t>(stream)), "mx_gemm_noalloc");
 }
 
 mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale_mode, mx_tensor* out,

@@ -119,6 +119,10 @@ bool gemm256_layout_ok(const GemmArgs& a);
 size_t gemm_splitk_workspace(int64_t M, int64_t N, int64_t K);
 bool gemm_splitk_applies(const GemmArgs& a);
 hipError_t launch_gemm_splitk(const GemmArgs& a, void* workspace, hipStream_t st);
+// The library's own split-K workspace on the current device (a static device
+// array, resolved once per device): its size and its device address.
+size_t gemm_splitk_scratch_bytes();
+hipError_t gemm_splitk_scratch(void** ptr);
 // Whether the 256x256 pipeline (the only kernel with the quantizing epilogue)
 // takes this problem; launch_gemm_quantize requires it.
 bool gemm_quantize_supported(const GemmQuantArgs& a);
