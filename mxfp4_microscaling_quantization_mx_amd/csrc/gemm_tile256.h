@@ -355,6 +355,40 @@ __device__ __forceinline__ void step_last(Acc& c, const v4i a[TI], const v4i b[T
       : "memory");
 }
 
+// step_last without its MFMAs, for a tail stage whose fourth 64-deep step
+// lies past K: the same loads of the stage two ahead and reads of the next
+// stage's first operands and scale bytes.
+__device__ __forceinline__ void step_last_nm(uint32_t ada, uint32_t adb, uint32_t adsa, uint32_t adsb, v4i na[TI],
+                                             v4i nb[TJ], v2u wa[TI], v2u wb[TJ], uint32_t m0, const uint32_t va[4],
+                                             __amdgpu_buffer_rsrc_t ra, uint32_t cs) {
+  asm volatile(
+      "ds_read_b128 %[na0], %[ada]\n\t"
+      "ds_read_b128 %[na1], %[ada] offset:4096\n\t"
+      "buffer_load_dwordx4 %[va0], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "ds_read_b128 %[nb0], %[adb]\n\t"
+      "ds_read_b128 %[nb1], %[adb] offset:4096\n\t"
+      "ds_read_b128 %[nb2], %[adb] offset:8192\n\t"
+      "ds_read_b128 %[nb3], %[adb] offset:12288\n\t"
+      "buffer_load_dwordx4 %[va1], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "ds_read_b64 %[wa0], %[adsa]\n\t"
+      "ds_read_b64 %[wa1], %[adsa] offset:512\n\t"
+      "ds_read_b64 %[wb0], %[adsb]\n\t"
+      "ds_read_b64 %[wb1], %[adsb] offset:512\n\t"
+      "buffer_load_dwordx4 %[va2], %[ra], %[cs] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "ds_read_b64 %[wb2], %[adsb] offset:1024\n\t"
+      "ds_read_b64 %[wb3], %[adsb] offset:1536\n\t"
+      "buffer_load_dwordx4 %[va3], %[ra], %[cs] offen lds\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : MX_NEXT_OPERANDS, [wa0] "=&v"(wa[0]), [wa1] "=&v"(wa[1]), [wb0] "=&v"(wb[0]), [wb1] "=&v"(wb[1]),
+        [wb2] "=&v"(wb[2]), [wb3] "=&v"(wb[3]), [m0] "+{m0}"(m0)
+      : [ada] "v"(ada), [adb] "v"(adb), [adsa] "v"(adsa), [adsb] "v"(adsb), [va0] "v"(va[0]), [va1] "v"(va[1]),
+        [va2] "v"(va[2]), [va3] "v"(va[3]), [ra] "s"(ra), [cs] "s"(cs)
+      : "memory");
+}
+
 // As step_last, but issuing all 8 code loads of the stage two ahead (4 A
 // loads at m0, m0+1024, ..., then 4 B loads OPB further), one after each MFMA.
 __device__ __forceinline__ void step_last8(Acc& c, const v4i a[TI], const v4i b[TJ], const int sa[TI],
@@ -660,14 +694,18 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
       sb[jj] = (int)((wb[jj].x & keep_lo) >> sh);
       sb2[jj] = (int)((wb[jj].y & keep_hi) >> sh);
     }
+    // 64-deep steps of this stage that hold K-blocks below K: all four except
+    // in the tail stage (none in a unit's padding stage, whose first step
+    // still runs on masked scales to carry its loads)
+    const int live = kb + s < nfull ? 4 : (kb + s == nfull ? (kchunks + 1) >> 1 : 0);
     // the B half of stage g+1's loads (issued by the previous iteration's
     // prefetch position; dummy loads past the end in the first iteration)
     if constexpr (SPLIT)
       step0_ld(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb, pend_m0, pend_vb, pend_rb, pend_cs);
     else
       step<false>(acc, a, b, sa, sb, slot + ra_k[1], slot + rb_k[1], na, nb);
-    step<true>(acc, na, nb, sa, sb, slot + ra_k[2], slot + rb_k[2], a, b);
-    step<false>(acc, a, b, sa2, sb2, slot + ra_k[3], slot + rb_k[3], na, nb);
+    if (live >= 2) step<true>(acc, na, nb, sa, sb, slot + ra_k[2], slot + rb_k[2], a, b);
+    if (live >= 3) step<false>(acc, a, b, sa2, sb2, slot + ra_k[3], slot + rb_k[3], na, nb);
     // Stage g+2 (the prefetch position): its code offsets.  Past the last
     // stage every code load points past the end (zeros into the free slot).
     const bool more = g + 2 < gtotal;
@@ -687,8 +725,12 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
     const uint32_t next = lds_addr + (uint32_t)(((g + 1) & 1) * STAGE_BYTES);
     const uint32_t snext = sl_addr + (uint32_t)snext_off(g);
     if constexpr (SPLIT) {
-      step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
-                slot + 4096u * wave, va, ra2, (uint32_t)(kb2 + s2) * ROWB);
+      if (live == 4)
+        step_last(acc, na, nb, sa2, sb2, next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb,
+                  slot + 4096u * wave, va, ra2, (uint32_t)(kb2 + s2) * ROWB);
+      else
+        step_last_nm(next + ra_k[0], next + rb_k[0], snext + s_a, snext + s_b, a, b, wa, wb, slot + 4096u * wave,
+                     va, ra2, (uint32_t)(kb2 + s2) * ROWB);
       // the B half goes out in the next iteration's first step
 #pragma unroll
       for (int t = 0; t < 4; ++t) pend_vb[t] = vb[t];
