@@ -30,7 +30,7 @@ from .formats import (
     e8m0_decode,
     bf16_bits_to_f32,
 )
-from .philox import philox4x32_10, sr_bits16
+from .philox import philox4x32_10, sr_bits8, sr_bits16
 from .rht import rht_forward_f32, rht_inverse_f32, hadamard32_f64
 from .quantize import (
     quantize,
@@ -54,6 +54,7 @@ __all__ = [
     "bf16_bits_to_f32",
     "philox4x32_10",
     "sr_bits16",
+    "sr_bits8",
     "rht_forward_f32",
     "rht_inverse_f32",
     "hadamard32_f64",

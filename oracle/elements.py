@@ -89,10 +89,10 @@ def round_elem(v, elem, rounding="rne", r=None):
     f = (a - lo) / (hi - lo)
     if rounding == "rne":
         up = (f > 0.5) | ((f == 0.5) & (i % 2 == 1))
-    elif rounding == "sr":
+    elif rounding in ("sr", "sr8"):
         if r is None:
             raise ValueError("stochastic rounding needs random bits r")
-        up = np.asarray(r, dtype=np.float64) < f * 65536.0
+        up = np.asarray(r, dtype=np.float64) < f * (65536.0 if rounding == "sr" else 256.0)
     else:
         raise ValueError(f"unknown rounding {rounding!r}")
     idx = np.where(a >= g[-1], top, i + up.astype(np.int64))

@@ -22,6 +22,10 @@ that two independent implementations can agree bit for bit):
 
 The bits therefore do not depend on launch geometry, and quantizing X along
 dim 0 gives the same bits as quantizing X^T along its last dim.
+
+An 8-bit variant ("sr8", an option beside the 16-bit default) spends one
+Philox call on 16 elements: element p uses call q = p >> 4 (the same counter
+and key layout) and takes byte (p & 3) of output word ((p >> 2) & 3).
 """
 
 import numpy as np
@@ -69,3 +73,21 @@ def sr_bits16(p, seed, offset):
     word = np.take_along_axis(words, sel[None, ...], axis=0)[0]
     half = (p & np.uint64(1)) * np.uint64(16)
     return ((word >> half) & np.uint64(0xFFFF)).astype(np.uint32)
+
+
+def sr_bits8(p, seed, offset):
+    """The 8 random bits of output element(s) at flat index p (uint64 array)
+    under the 8-bit mapping: byte (p & 3) of word ((p >> 2) & 3) of Philox
+    call p >> 4."""
+    p = np.asarray(p, dtype=np.uint64)
+    seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    offset = int(offset) & 0xFFFFFFFFFFFFFFFF
+    q = p >> np.uint64(4)
+    w = philox4x32_10(q & MASK32, q >> np.uint64(32),
+                      np.uint64(offset & 0xFFFFFFFF), np.uint64(offset >> 32),
+                      seed & 0xFFFFFFFF, seed >> 32)
+    words = np.stack(w, axis=0).astype(np.uint64)
+    sel = ((p >> np.uint64(2)) & np.uint64(3)).astype(np.int64)
+    word = np.take_along_axis(words, sel[None, ...], axis=0)[0]
+    shift = (p & np.uint64(3)) * np.uint64(8)
+    return ((word >> shift) & np.uint64(0xFF)).astype(np.uint32)

@@ -41,7 +41,9 @@ Steps per block, in the order they are taken (float32 where stated):
      to 6; otherwise lo <= |v| < hi are the neighbouring grid points and
      f = (|v| - lo)/(hi - lo) (exact).  RNE: up iff f > 1/2, or f == 1/2 and
      lo's code is odd (ties go to the even mantissa bit).  SR: up iff
-     r < f * 2^16 for the element's 16 random bits r (``oracle.philox``).
+     r < f * 2^16 for the element's 16 random bits r (``oracle.philox``);
+     "sr8": up iff r < f * 2^8 for its 8 random bits (bias at most 2^-8 of
+     the step: P(up) = ceil(256 f) / 256).
   7. code = sign(v) << 3 | magnitude index; the sign of a zero is kept.
   8. two codes per byte, element 2j in the low nibble of byte j.
 
@@ -55,7 +57,7 @@ import numpy as np
 
 from . import elements
 from .formats import BLOCK, E2M1_GRID, E8M0_BIAS, E8M0_NAN, e2m1_decode, e8m0_decode
-from .philox import sr_bits16
+from .philox import sr_bits8, sr_bits16
 from .rht import rht_forward_f32, rht_inverse_f32
 
 
@@ -100,10 +102,10 @@ def round_e2m1(v, rounding="rne", r=None):
     f = (a - lo) / (hi - lo)
     if rounding == "rne":
         up = (f > 0.5) | ((f == 0.5) & (i % 2 == 1))
-    elif rounding == "sr":
+    elif rounding in ("sr", "sr8"):
         if r is None:
             raise ValueError("stochastic rounding needs random bits r")
-        up = np.asarray(r, dtype=np.float64) < f * 65536.0
+        up = np.asarray(r, dtype=np.float64) < f * (65536.0 if rounding == "sr" else 256.0)
     else:
         raise ValueError(f"unknown rounding {rounding!r}")
     idx = np.where(a >= 6.0, 7, i + up.astype(np.int64))
@@ -199,12 +201,13 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
         v = (y * factor[..., None]).astype(np.float32)
 
         r = None
-        if rounding == "sr":
+        if rounding in ("sr", "sr8"):
             ridx = np.arange(rows) if row_index is None else np.asarray(row_index)
             kt = K if K_total is None else int(K_total)
             p = (ridx.astype(np.uint64)[:, None] * np.uint64(kt)
                  + np.arange(K, dtype=np.uint64)[None, :])
-            r = sr_bits16(p, seed, offset).reshape(rows, nkb, BLOCK)
+            bits = sr_bits16 if rounding == "sr" else sr_bits8
+            r = bits(p, seed, offset).reshape(rows, nkb, BLOCK)
         codes = round_e2m1(v, rounding, r) if elem == "e2m1" else elements.round_elem(v, elem, rounding, r)
         codes = np.where(bad_el[..., None], 0, codes)
     if elem != "e2m1":

@@ -67,3 +67,24 @@ def test_sr_bits_uniform_statistics():
     expected = len(r) / 16
     chi2 = ((counts - expected) ** 2 / expected).sum()
     assert chi2 < 45          # 15 dof, p ~ 1e-4
+
+
+def test_sr_bits8_mapping_rule(rocrand_philox):
+    """8-bit draws: element p takes byte (p & 3) of word ((p >> 2) & 3) of the
+    Philox call p >> 4 (rocRAND's engine, run on the host, supplies the words)."""
+    seed, off = 0xFEDCBA9876543210, 7
+    p = np.arange(96, dtype=np.uint64) + np.uint64(16 * 777 + 5)
+    bits = oracle.sr_bits8(p, seed, off)
+    words = rocrand_philox([(seed, int(pp) >> 4, off) for pp in p])
+    for i, pp in enumerate(p):
+        pp = int(pp)
+        w = int(words[i][(pp >> 2) & 3])
+        assert int(bits[i]) == (w >> (8 * (pp & 3))) & 0xFF
+
+
+def test_sr_bits8_uniform_statistics():
+    r = oracle.sr_bits8(np.arange(1 << 18, dtype=np.uint64), 99, 0).astype(np.int64)
+    counts = np.bincount(r >> 4, minlength=16)
+    expected = len(r) / 16
+    assert ((counts - expected) ** 2 / expected).sum() < 45
+    assert abs(r.mean() / 255.0 - 0.5) < 0.005

@@ -270,6 +270,77 @@ def test_sr_quantize_unbiased_end_to_end():
     assert np.max(np.abs(mean - x)) <= 5 * 1.0 / math.sqrt(n) + 2 * 2.0 ** -16
 
 
+# ---------------------------------------------------------------- 8-bit draws
+def _exact_fraction(v):
+    """(lower grid index, exact fraction f) of a positive float32 v below 6,
+    from the page's table."""
+    from fractions import Fraction
+    grid = [g for _, g, _ in e2m1_table()]
+    i = max(k for k, g in enumerate(grid) if g <= v)
+    return i, (Fraction(float(v)) - Fraction(grid[i])) / (Fraction(grid[i + 1]) - Fraction(grid[i]))
+
+
+def test_sr8_threshold_bruteforce():
+    """8-bit stochastic rounding: up iff r < f * 2^8, checked at the draws
+    T - 1, T, T + 1 around T = floor(256 f) for fractions with and without an
+    exact 8-bit representation, both signs."""
+    rng = np.random.default_rng(51)
+    vals = [np.float32(v) for v in rng.uniform(0.01, 5.99, 300)]
+    vals += [np.float32(v) for v in (0.125, 0.25 + 0.5 / 256, 1.5 + 0.5 * 3 / 8, 3.5, 5.0 + 2.0 * 7 / 256)]
+    for v in vals:
+        i, f = _exact_fraction(v)
+        if f == 0:
+            continue
+        t = int(f * 256)
+        for r in (t - 1, t, t + 1):
+            if not 0 <= r < 256:
+                continue
+            up = r < f * 256
+            code = int(oracle.round_e2m1(np.float32([v]), "sr8", np.uint32([r]))[0])
+            assert code == i + int(up), (float(v), r)
+            assert int(oracle.round_e2m1(np.float32([-v]), "sr8", np.uint32([r]))[0]) == code | 8
+
+
+def test_sr8_is_sr16_at_scaled_draws():
+    """Rounding with an 8-bit draw r equals 16-bit stochastic rounding with the
+    draw 256 r (256 r < f 2^16 exactly when r < f 2^8): the identity that lets
+    a 16-bit implementation serve both."""
+    rng = np.random.default_rng(52)
+    v = rng.uniform(-6.5, 6.5, 200_000).astype(np.float32)
+    r = rng.integers(0, 256, v.shape).astype(np.uint32)
+    assert np.array_equal(oracle.round_e2m1(v, "sr8", r), oracle.round_e2m1(v, "sr", r * 256))
+
+
+@pytest.mark.parametrize("v", [0.1, 0.3, 1.2, 1.7, 2.25, 3.9, 5.99])
+def test_sr8_bias_at_most_a_256th_of_the_step(v):
+    """P(up) = ceil(256 f) / 256 in closed form, so the mean is off v by less
+    than 2^-8 of the step (above it), and the variance is binomial; checked over
+    n Philox draws through the quantizer's own bit mapping."""
+    import math
+    x = np.float32(v)
+    i, f = _exact_fraction(x)
+    grid = [g for _, g, _ in e2m1_table()]
+    lo, hi = grid[i], grid[i + 1]
+    n = 1 << 18
+    r = oracle.sr_bits8(np.arange(n, dtype=np.uint64), 1234, 0)
+    got = oracle.e2m1_decode(oracle.round_e2m1(np.full(n, x), "sr8", r))
+    pu = math.ceil(float(f) * 256) / 256
+    mean_exact = lo + pu * (hi - lo)
+    assert 0 <= mean_exact - float(x) < (hi - lo) / 256
+    sigma = (hi - lo) * math.sqrt(pu * (1 - pu))
+    assert abs(got.mean() - mean_exact) <= 5 * sigma / math.sqrt(n) + 1e-12
+    assert abs(got.var() - sigma ** 2) <= 0.05 * sigma ** 2 + 1e-9
+
+
+def test_sr8_dim0_equals_transpose_last():
+    rng = np.random.default_rng(53)
+    x = rng.standard_normal((64, 96)).astype(np.float32)
+    kw = dict(rounding="sr8", seed=9, offset=2, rht_mask=0x13572468)
+    c0, s0 = oracle.quantize(x, axis="dim0", **kw)
+    c1, s1 = oracle.quantize(np.ascontiguousarray(x.T), **kw)
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+
+
 def test_row_sampling_matches_full_tensor():
     """Quantizing a sample of rows with their global row numbers reproduces
     those rows of the full result (stochastic rounding included)."""
