@@ -215,30 +215,65 @@ def rates(name, kind, amount, avg_ms):
     return {"us": avg_ms * 1e3, "TFLOP/s": rate, "frac_fp4": rate / FP4_PEAK_TFLOPS, "flop": amount}
 
 
-def time_each(ks, steps):
-    """Average duration (ms) of each kernel over `steps` passes, with HIP events
-    around every launch on the launch stream (torch's current stream)."""
+def time_each(ks, steps, flush=None):
+    """Durations (ms) of each kernel over `steps` passes, with HIP events
+    around every launch on the launch stream (torch's current stream): one
+    list per kernel.  With `flush` (a large device buffer) every launch is
+    preceded, outside its events, by a fill of that buffer, which evicts the
+    last-level cache, so each kernel reads its inputs from HBM."""
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ks]
           for _ in range(steps)]
     torch.cuda.synchronize()
     for s in range(steps):
         for k, (_, fn, _, _) in enumerate(ks):
+            if flush is not None:
+                flush.fill_(s * len(ks) + k)
             ev[s][k][0].record()
             fn()
             ev[s][k][1].record()
     torch.cuda.synchronize()
-    return [float(np.mean([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(steps)]))
-            for k in range(len(ks))]
+    return [[ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(steps)] for k in range(len(ks))]
+
+
+def spread(ms_list):
+    """Median, p10 and p90 (us) of a list of durations in ms."""
+    a = np.asarray(ms_list) * 1e3
+    return {"us_median": float(np.median(a)), "us_p10": float(np.percentile(a, 10)),
+            "us_p90": float(np.percentile(a, 90))}
+
+
+def copy_rate(dev, nbytes=1 << 30, reps=5):
+    """Measured device-to-device copy rate (GB/s of read + write traffic) of a
+    plain copy kernel on nbytes, median of reps, the HBM reference beside the
+    8 TB/s published peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    del src, dst
+    return 2 * nbytes / (float(np.median(ts)) * 1e-3) / 1e9
 
 
 def cpu_baseline(w, budget_s=20.0):
     """The oracle (NumPy, as written) on a bounded sample of the same workload:
     quantize a slice of the quantize-only tensor both ways (transform + SR)
-    and the float64 reference GEMM of a slice of the fprop rows."""
+    and the float64 reference GEMM of a slice of the fprop rows.  The oracle
+    treats rows independently, so its cost is linear in the rows it is given;
+    the full-size times are the sample times scaled by that ratio (stated in
+    the output, not measured: the full quantize alone would take about an
+    hour)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] + [1])
     except Exception:
         threads = os.cpu_count()
     xn = w.xq[:256].float().cpu().numpy()
@@ -262,11 +297,22 @@ def cpu_baseline(w, budget_s=20.0):
             break
     tg = (time.perf_counter() - t0) / n
     flops = 2 * rows * 5760 * 2880
-    return {"value": flops / tg / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    gemm_tflops = flops / tg / 1e12
+    q_gbps = qbytes / tq / 1e9
+    full_q = 2 * quant_bytes(16384, 2880) / (q_gbps * 1e9)
+    full_gemm = {name: 2 * m * n_ * k / (gemm_tflops * 1e12)
+                 for name, m, n_, k in [("fprop", 16384, 5760, 2880), ("wgrad", 2880, 2880, 16384),
+                                        ("moe", 65536, 5760, 2880)]}
+    return {"value": gemm_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": (f"float64 reference GEMM of {rows} x 5760 x 2880 fprop rows (dequantize + BLAS "
                        f"+ |a||b| bound), {n} runs; oracle quantize of 256 x 2880 rows + 256 x 256 "
-                       f"transposed (transform + SR) at {qbytes / tq / 1e9:.4f} GB/s"),
-            "quantize_GBps": qbytes / tq / 1e9}
+                       f"transposed (transform + SR) at {q_gbps:.4f} GB/s"),
+            "cpu_count": os.cpu_count(),
+            "threads": {"gemm_reference": threads, "quantize": 1},
+            "quantize_GBps": q_gbps,
+            "full_size_s_extrapolated": {"quantize_both_axes_16384x2880": full_q,
+                                         **{f"{k}_gemm_reference": v for k, v in full_gemm.items()}},
+            "extrapolation": "sample time x (full rows / sample rows): the oracle is row-independent"}
 
 
 def main():
@@ -301,9 +347,12 @@ def main():
     torch.cuda.synchronize()
 
     # Component pass (untimed for the metric): K steps with HIP events around
-    # every kernel on the launch stream (torch's current stream), for the
-    # per-kernel durations reported under "components".
-    comp_ms = time_each(ks, args.steps)
+    # every kernel on the launch stream (torch's current stream), each launch
+    # after a 512 MB fill that evicts the 256 MB last-level cache, for the
+    # per-kernel durations reported under "components" (mean, median, p10, p90).
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    comp_all = time_each(ks, args.steps, flush)
+    comp_ms = [float(np.mean(t)) for t in comp_all]
     dom_k = int(np.argmax(comp_ms))
 
     # Timed region: K steps of the whole path, with HIP events only around the
@@ -327,16 +376,23 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    comp_ms[dom_k] = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+    flushed_ms = comp_ms[dom_k]
+    comp_all[dom_k] = [a.elapsed_time(b) for a, b in dev_ev]      # the dominant kernel inside the step
+    comp_ms[dom_k] = float(np.mean(comp_all[dom_k]))
 
-    comps = {name: rates(name, kind, amount, comp_ms[k]) for k, (name, _, kind, amount) in enumerate(ks)}
+    comps = {name: {**rates(name, kind, amount, comp_ms[k]), **spread(comp_all[k])}
+             for k, (name, _, kind, amount) in enumerate(ks)}
+    comps[ks[dom_k][0]]["us_after_flush"] = flushed_ms * 1e3
 
     # Next-row kernels, after the timed region (not part of the step or of value).
     xs = w.extras()
     for _, fn, _, _ in xs:
         fn()
-    x_ms = time_each(xs, args.steps)
-    extra = {name: rates(name, kind, amount, x_ms[k]) for k, (name, _, kind, amount) in enumerate(xs)}
+    x_all = time_each(xs, args.steps, flush)
+    extra = {name: {**rates(name, kind, amount, float(np.mean(x_all[k]))), **spread(x_all[k])}
+             for k, (name, _, kind, amount) in enumerate(xs)}
+    del flush
+    copy_gbps = copy_rate(dev)
 
     gemm_flop = sum(a for _, _, kind, a in ks if kind == "mfma")
     value = gemm_flop / (ms_step * 1e-3) / 1e12
@@ -378,6 +434,10 @@ def main():
                                "65536x5760x2880 (Zipf 1.1 top-4)",
                    "parallelism": "single GPU"},
         "quantize_GBps_aggregate": quant_bytes_total / (quant_us * 1e-6) / 1e9,
+        "copy_GBps_measured": copy_gbps,
+        "timing": ("per-kernel: HIP events on the launch stream, each launch after a 512 MB cache-evicting "
+                   "fill; dominant kernel: events inside the timed step (us_after_flush: its cache-evicted "
+                   "launches); us = mean, with median/p10/p90"),
         "components": comps,
         "next_rows": extra,
         "roofline": roof,

@@ -72,7 +72,12 @@ typedef enum {
 
 typedef enum {
   MX_ROUND_RNE = 0,  /* round to nearest, ties to even mantissa bit, saturate at +-6 */
-  MX_ROUND_SR = 1    /* stochastic rounding with Philox4x32-10 bits, saturate at +-6  */
+  MX_ROUND_SR = 1,   /* stochastic rounding with 16 Philox4x32-10 bits per element   */
+  MX_ROUND_SR8 = 2   /* stochastic rounding with 8 bits per element (a cheaper option;
+                        rounds up with probability ceil(256 f) / 256, a bias of less
+                        than 2^-8 of the step): element p takes byte (p & 3) of word
+                        ((p >> 2) & 3) of the Philox call with q = p >> 4 and rounds up
+                        iff that byte r satisfies r < f * 2^8                         */
 } mx_round;
 
 /*

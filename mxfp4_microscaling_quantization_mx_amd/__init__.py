@@ -25,7 +25,7 @@ MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 0, 1, 2, 3
 MX_DT_F32, MX_DT_BF16 = 0, 1
 _AXIS = {"last": 0, "dim0": 1}
 _BLOCK = {"1d": 0, "2d": 1}
-_ROUND = {"rne": 0, "sr": 1}
+_ROUND = {"rne": 0, "sr": 1, "sr8": 2}
 _SCALE = {"floor": 0, "round_up": 1, "prescale_3_4": 2}
 # MX element types: name -> (mx_elem, bits per element)
 _ELEM = {"e2m1": (0, 4), "e4m3": (1, 8), "e5m2": (2, 8), "e2m3": (3, 6), "e3m2": (4, 6)}

@@ -82,7 +82,7 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
     return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown source dtype %d", src_dtype);
   if (cfg->axis != MX_AXIS_LAST && cfg->axis != MX_AXIS_DIM0)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown axis %d", cfg->axis);
-  if (cfg->rounding != MX_ROUND_RNE && cfg->rounding != MX_ROUND_SR)
+  if (cfg->rounding != MX_ROUND_RNE && cfg->rounding != MX_ROUND_SR && cfg->rounding != MX_ROUND_SR8)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown rounding %d", cfg->rounding);
   if (cfg->block != MX_BLOCK_1D && cfg->block != MX_BLOCK_2D)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize: unknown block kind %d", cfg->block);
@@ -124,7 +124,7 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   a.dim0 = dim0;
   a.two_d = cfg->block == MX_BLOCK_2D;
   a.rht = cfg->use_rht == 1;
-  a.sr = cfg->rounding == MX_ROUND_SR;
+  a.sr = cfg->rounding == MX_ROUND_SR ? 1 : cfg->rounding == MX_ROUND_SR8 ? 2 : 0;
   a.mask = cfg->rht_sign_mask;
   a.seed = cfg->philox_seed;
   a.offset = cfg->philox_offset;
@@ -195,7 +195,7 @@ mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, 
     return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: unknown source dtype %d", src_dtype);
   if (cfg->axis != MX_AXIS_LAST || cfg->block != MX_BLOCK_1D)
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize_gather: only 1-D blocks along the last dim");
-  if (cfg->rounding != MX_ROUND_RNE && cfg->rounding != MX_ROUND_SR)
+  if (cfg->rounding != MX_ROUND_RNE && cfg->rounding != MX_ROUND_SR && cfg->rounding != MX_ROUND_SR8)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: unknown rounding %d", cfg->rounding);
   if (cfg->use_rht != 0 && cfg->use_rht != 1)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize_gather: use_rht must be 0 or 1");
@@ -229,7 +229,7 @@ mx_status mx_quantize_gather(const void* src, int32_t src_dtype, int64_t R_src, 
   a.ld_src = ld_src;
   a.bf16 = src_dtype == MX_DT_BF16;
   a.rht = cfg->use_rht == 1;
-  a.sr = cfg->rounding == MX_ROUND_SR;
+  a.sr = cfg->rounding == MX_ROUND_SR ? 1 : cfg->rounding == MX_ROUND_SR8 ? 2 : 0;
   a.mask = cfg->rht_sign_mask;
   a.seed = cfg->philox_seed;
   a.offset = cfg->philox_offset;

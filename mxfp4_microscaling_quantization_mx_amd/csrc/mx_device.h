@@ -208,6 +208,15 @@ __device__ __forceinline__ uint32_t cvt_sr_pair(float v0, float v1, uint32_t w) 
   return (c0 & 0x0Fu) | (c1 & ~0x0Fu);   // one V_BFI_B32
 }
 
+// 8-bit draws as 16-bit ones: bytes 2H and 2H + 1 of a Philox word w, the
+// draws of two consecutive elements, as the word (b1 << 24) | (b0 << 8)
+// that pack8_sr reads (draw 256 b in each 16-bit half; V_PERM_B32 selector
+// 0x0C gives a zero byte).
+template <int H>
+__device__ __forceinline__ uint32_t sr8_pair(uint32_t w) {
+  return __builtin_amdgcn_perm(w, w, H ? 0x030C020Cu : 0x010C000Cu);
+}
+
 // 8 values (already divided by the block scale) -> one word of SR codes;
 // value 2j uses the low half of w[j], value 2j+1 the high half.
 __device__ __forceinline__ uint32_t pack8_sr(const float v[8], const uint32_t w[4]) {

@@ -14,7 +14,7 @@ struct QuantArgs {
   bool dim0;                  // blocks along dim 0 (output = quantized transpose)
   bool two_d;                 // 32x32 tiles
   bool rht;
-  bool sr;
+  int sr;                     // stochastic rounding: 0 none, 1 16-bit draws, 2 8-bit draws
   uint32_t mask;
   uint64_t seed, offset;
   uint8_t* codes;

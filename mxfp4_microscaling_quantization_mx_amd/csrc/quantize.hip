@@ -84,7 +84,7 @@ __device__ __forceinline__ void load32(const void* __restrict__ src, int64_t idx
 // scale_mode (wave-uniform): 0 the reference rule floor(log2 amax) - 2; 1 the
 // round-up rule; 2 the reference rule's scale with every element multiplied by
 // 0.75 (one float32 multiply) before the division, so nothing clips.
-template <bool RHT, bool SR, bool TWO_D = false>
+template <bool RHT, int SR, bool TWO_D = false>
 __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packed[4], uint64_t p0,
                                                      uint64_t seed, uint64_t offset, int scale_mode) {
   const float c = __uint_as_float(kRhtCBits);
@@ -114,7 +114,21 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       uint32_t w[4];
-      sr_words((p0 >> 3) + g, seed, offset, w);
+      if constexpr (SR == 2) {
+        // 8-bit draws: one Philox call per 16 elements, element i of the call
+        // taking byte (i & 3) of word i >> 2; each byte b goes in as the
+        // 16-bit draw 256 b, with which the 16-bit rule rounds up exactly
+        // when b < 256 f
+        uint32_t W[4];
+        sr_words((p0 >> 4) + (g >> 1), seed, offset, W);
+        const uint32_t w0 = W[2 * (g & 1)], w1 = W[2 * (g & 1) + 1];
+        w[0] = sr8_pair<0>(w0);
+        w[1] = sr8_pair<1>(w0);
+        w[2] = sr8_pair<0>(w1);
+        w[3] = sr8_pair<1>(w1);
+      } else {
+        sr_words((p0 >> 3) + g, seed, offset, w);
+      }
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * inv;
@@ -141,7 +155,7 @@ __device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packe
 // Philox draws as E2M1) and packed: FP8 one byte per element (8 words), FP6
 // element e at bits 6e of the block's 192 bits (6 words).  Returns the scale
 // byte.
-template <int ELEM, bool RHT, bool SR, bool TWO_D = false>
+template <int ELEM, bool RHT, int SR, bool TWO_D = false>
 __device__ __forceinline__ uint32_t quantize_block32_elem(float x[32], uint32_t out[8], uint64_t p0, uint64_t seed,
                                                           uint64_t offset, int scale_mode) {
   using T = ElemT<ELEM>;
@@ -190,12 +204,17 @@ __device__ __forceinline__ uint32_t quantize_block32_elem(float x[32], uint32_t 
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (SR) sr_words((p0 >> 3) + g, seed, offset, w);
+    if constexpr (SR == 2) sr_words((p0 >> 4) + (g >> 1), seed, offset, w);
+    else if constexpr (SR == 1) sr_words((p0 >> 3) + g, seed, offset, w);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int e = 8 * g + i;
-      const uint32_t r16 = SR ? (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu : 0u;
-      const uint32_t code = elem_code<ELEM, SR>(x[e] * inv, r16);
+      // 16-bit draws: half (i & 1) of word i >> 1; 8-bit: byte (i16 & 3) of
+      // word i16 >> 2 of the call's 16 elements, as the 16-bit draw 256 b
+      const int i16 = 8 * (g & 1) + i;
+      const uint32_t r16 = SR == 2 ? ((w[i16 >> 2] >> (8 * (i16 & 3))) & 0xFFu) << 8
+                           : SR ? (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu : 0u;
+      const uint32_t code = elem_code<ELEM, (SR != 0)>(x[e] * inv, r16);
       if (T::BITS == 8) {
         out[e >> 2] |= code << (8 * (e & 3));
       } else {
@@ -232,7 +251,7 @@ constexpr int block_bytes() {
 
 // Quantize one block of element type ELEM (E2M1 through the hardware-convert
 // path above) and store its codes at dst; returns the scale byte.
-template <int ELEM, bool RHT, bool SR, bool TWO_D = false>
+template <int ELEM, bool RHT, int SR, bool TWO_D = false>
 __device__ __forceinline__ uint32_t quantize_store(float x[32], uint8_t* dst, uint64_t p0, uint64_t seed,
                                                    uint64_t offset, int scale_mode) {
   uint32_t w[8];
@@ -249,7 +268,7 @@ __device__ __forceinline__ uint32_t quantize_store(float x[32], uint8_t* dst, ui
 // GATHER: output row r quantizes source row gidx[r] (the routed rows of an MoE
 // layer read straight from the token activations); an index outside
 // [0, R_src) gives the row NaN blocks (scale byte 0xFF, codes 0).
-template <bool BF16, bool RHT, bool SR, bool GATHER, int ELEM>
+template <bool BF16, bool RHT, int SR, bool GATHER, int ELEM>
 __global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ src, uint32_t nblocks,
                                                        uint32_t nkb, int64_t ld_src,
                                                        uint8_t* __restrict__ codes, int64_t ld_codes,
@@ -287,7 +306,7 @@ struct TileShape {
   static constexpr int LD = 129;   // LDS row pitch in floats (bank-conflict free reads)
 };
 
-template <bool BF16, bool RHT, bool SR, int ELEM>
+template <bool BF16, bool RHT, int SR, int ELEM>
 __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src, int64_t R,
                                                     int64_t C, int64_t ld_src,
                                                     uint8_t* __restrict__ codes, int64_t ld_codes,
@@ -355,7 +374,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
 // consecutive columns of one source row.  The block then goes through the same
 // register path as a row block.  2-D: a half-wave holds one 32x32 tile (output
 // rows are a multiple of 32, so half-waves are whole or empty).
-template <bool TWO_D, bool BF16, bool RHT, bool SR, int ELEM>
+template <bool TWO_D, bool BF16, bool RHT, int SR, int ELEM>
 __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src, int64_t R, int64_t C,
                                                     int64_t ld_src, uint8_t* __restrict__ codes,
                                                     int64_t ld_codes, uint8_t* __restrict__ scales,
@@ -392,6 +411,16 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
   }
 }
 
+// Launch M_ with the stochastic-rounding variant of a.sr (0 none, 1 16-bit
+// draws, 2 8-bit draws).
+#define MX_SR3(M_, RHT_)  \
+  if (a.sr == 2)          \
+    M_(RHT_, 2);          \
+  else if (a.sr == 1)     \
+    M_(RHT_, 1);          \
+  else                    \
+    M_(RHT_, 0)
+
 template <bool TWO_D, bool BF16, int ELEM>
 hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
   dim3 grid((unsigned)((a.C + 63) / 64), (unsigned)((a.R + 127) / 128));
@@ -400,9 +429,9 @@ hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
                      a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset,      \
                      a.scale_mode)
   if (a.rht) {
-    if (a.sr) MX_COLS(true, true); else MX_COLS(true, false);
+    MX_SR3(MX_COLS, true);
   } else {
-    if (a.sr) MX_COLS(false, true); else MX_COLS(false, false);
+    MX_SR3(MX_COLS, false);
   }
 #undef MX_COLS
   return hipGetLastError();
@@ -417,9 +446,9 @@ hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
                      a.src, a.R, a.C, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales,  \
                      a.mask, a.seed, a.offset, a.scale_mode)
   if (a.rht) {
-    if (a.sr) MX_TILE(true, true); else MX_TILE(true, false);
+    MX_SR3(MX_TILE, true);
   } else {
-    if (a.sr) MX_TILE(false, true); else MX_TILE(false, false);
+    MX_SR3(MX_TILE, false);
   }
 #undef MX_TILE
   return hipGetLastError();
@@ -435,9 +464,9 @@ hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
                      nblocks, nkb, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask,    \
                      a.seed, a.offset, a.scale_mode, a.gather, a.R_src)
   if (a.rht) {
-    if (a.sr) MX_ROWS(true, true); else MX_ROWS(true, false);
+    MX_SR3(MX_ROWS, true);
   } else {
-    if (a.sr) MX_ROWS(false, true); else MX_ROWS(false, false);
+    MX_SR3(MX_ROWS, false);
   }
 #undef MX_ROWS
   return hipGetLastError();
@@ -477,7 +506,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_scatter(const void* __restri
   float x[32];
   load32<BF16>(src, (int64_t)row * ld_src + 32 * kb, x, RHT ? mask : 0u);
   uint32_t packed[4];
-  const uint32_t s = quantize_block32<RHT, false>(x, packed, 0u, 0u, 0u, scale_mode);
+  const uint32_t s = quantize_block32<RHT, 0>(x, packed, 0u, 0u, 0u, scale_mode);
   const uint4 v = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   for (int j = 0; j < k; ++j) {
     const int64_t d = dest[(int64_t)row * k + j];

@@ -48,6 +48,11 @@ def test_quantize_rejects_bad_arguments(lib):
     st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 48, 48, ctypes.byref(cfg), ctypes.byref(out), None)
     assert st == mx.MX_ERR_INVALID_ARG
     assert b"multiple of 32" in lib.mx_last_error()
+    for bad_rounding in (3, 7, -1):
+        bad_cfg = mx.QuantCfgC(0, 0, bad_rounding, 0, 0, 0, 0, 0)
+        out = _tensor(32, 64)
+        st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(bad_cfg), ctypes.byref(out), None)
+        assert st == mx.MX_ERR_INVALID_ARG and b"rounding" in lib.mx_last_error()
     bad_cfg = mx.QuantCfgC(0, 0, 7, 0, 0, 0, 0, 0)
     out = _tensor(32, 64)
     st = lib.mx_quantize(ctypes.c_void_p(16), 1, 32, 64, 64, ctypes.byref(bad_cfg), ctypes.byref(out), None)
@@ -192,6 +197,9 @@ def test_quantize_scatter_rejects_bad_arguments(lib):
     out = _tensor(64, 64)
     P = ctypes.c_void_p
     st = lib.mx_quantize_scatter(P(16), 1, 16, 64, 64, P(16), 4, B(sr), B(out), None)
+    assert st == mx.MX_ERR_UNSUPPORTED and b"RNE" in lib.mx_last_error()
+    sr8 = mx.QuantCfgC(0, 0, 2, 0, 0, 0, 0, 0)
+    st = lib.mx_quantize_scatter(P(16), 1, 16, 64, 64, P(16), 4, B(sr8), B(out), None)
     assert st == mx.MX_ERR_UNSUPPORTED and b"RNE" in lib.mx_last_error()
     st = lib.mx_quantize_scatter(P(16), 1, 16, 64, 64, P(16), 4, B(mx.QuantCfgC(1, 0, 0, 0, 0, 0, 0, 0)), B(out),
                                  None)

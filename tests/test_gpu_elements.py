@@ -26,7 +26,7 @@ def _case_id(elem, axis, rounding, rht):
     return f"{elem}-{axis}-{rounding}-{'rht' if rht else 'plain'}"
 
 
-CASES = [(e, a, r, h) for e in ELEMS for a in ("last", "dim0") for r in ("rne", "sr") for h in (False, True)]
+CASES = [(e, a, r, h) for e in ELEMS for a in ("last", "dim0") for r in ("rne", "sr", "sr8") for h in (False, True)]
 
 
 @pytest.mark.parametrize("elem,axis,rounding,rht", CASES, ids=[_case_id(*c) for c in CASES])
@@ -48,7 +48,7 @@ def test_quantize_elements(elem, axis, rounding, rht):
 
 @pytest.mark.parametrize("elem", ELEMS)
 @pytest.mark.parametrize("axis", ["last", "dim0"])
-@pytest.mark.parametrize("rounding,rht", [("rne", False), ("sr", True)])
+@pytest.mark.parametrize("rounding,rht", [("rne", False), ("sr", True), ("sr8", False)])
 def test_quantize_elements_2d(elem, axis, rounding, rht):
     """32x32 tiles (one scale per tile) for every element type, along the
     last dim (LDS tile kernel) and dim 0 (column kernel), ragged in K."""

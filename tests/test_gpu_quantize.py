@@ -33,7 +33,7 @@ MODES = [
     dict(axis=a, block=b, rounding=r, rht_mask=m)
     for a in ("last", "dim0")
     for b in ("1d", "2d")
-    for r in ("rne", "sr")
+    for r in ("rne", "sr", "sr8")
     for m in (None, 0x9E3779B9)
 ]
 
@@ -101,7 +101,7 @@ def _adversarial_rows():
     return np.array(rows, dtype=np.float32)
 
 
-@pytest.mark.parametrize("rounding", ["rne", "sr"])
+@pytest.mark.parametrize("rounding", ["rne", "sr", "sr8"])
 def test_quantize_adversarial_blocks(rounding):
     need_gpu()
     x = _adversarial_rows()
@@ -182,6 +182,37 @@ def test_quantize_full_size_config_both_axes():
     codes_equal(host(qt.codes)[cols], oc, "dim0 codes")
 
 
+def test_quantize_full_size_sr8_both_axes():
+    """The quantize-only workload at full size with the 8-bit stochastic
+    rounding draws (16 elements per Philox call): 256 sampled output rows along
+    the last dim and 256 along dim 0 against the oracle, and along dim 0 the
+    whole output equal to the last-dim quantization of the transpose."""
+    need_gpu()
+    R, C = 16384, 2880
+    xb = workloads.student_t_outliers(R, C)
+    xn = xb.float().numpy()
+    mask = workloads.rht_mask(workloads.CFG_QUANT)
+    seed = workloads.philox_seed(workloads.CFG_QUANT)
+    xd = xb.cuda()
+    rng = np.random.default_rng(8)
+    banner("quantize full size last-dim rht+sr8")
+    q = mx.quantize(xd, rht_mask=mask, rounding="sr8", seed=seed, offset=0)
+    rows = np.sort(rng.choice(R, 256, replace=False))
+    oc, os_ = oracle.quantize(xn[rows], rht_mask=mask, rounding="sr8", seed=seed, offset=0, row_index=rows)
+    codes_equal(host(q.scales)[rows], os_, "last scales")
+    codes_equal(host(q.codes)[rows], oc, "last codes")
+    banner("quantize full size dim0 rht+sr8")
+    qt = mx.quantize(xd, axis="dim0", rht_mask=mask, rounding="sr8", seed=seed, offset=1)
+    cols = np.sort(rng.choice(C, 256, replace=False))
+    oc, os_ = oracle.quantize(xn[:, cols], axis="dim0", rht_mask=mask, rounding="sr8", seed=seed, offset=1,
+                              row_index=cols)
+    codes_equal(host(qt.scales)[cols], os_, "dim0 scales")
+    codes_equal(host(qt.codes)[cols], oc, "dim0 codes")
+    tt = mx.quantize(xd.t().contiguous(), rht_mask=mask, rounding="sr8", seed=seed, offset=1)
+    codes_equal(host(qt.codes), host(tt.codes), "dim0 vs transposed codes")
+    codes_equal(host(qt.scales), host(tt.scales), "dim0 vs transposed scales")
+
+
 def test_dim0_equals_transposed_last_on_gpu():
     """Property that holds at any size: quantizing X along dim 0 equals
     quantizing X^T along its last dim, Hadamard transform and SR included."""
@@ -234,13 +265,13 @@ def test_quantize_dequantize_round_trip_rht():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("rounding", ["rne", "sr"])
+@pytest.mark.parametrize("rounding", ["rne", "sr", "sr8"])
 @pytest.mark.parametrize("rht", [False, True])
 def test_quantize_gather_parity(dtype, rounding, rht):
     """mx_quantize_gather against the oracle: repeated, permuted and
     out-of-range row indices (NaN blocks), a ragged row count, bit-exact."""
     need_gpu()
-    rng = np.random.default_rng(21 + 2 * int(rht) + (rounding == "sr"))
+    rng = np.random.default_rng(21 + 3 * int(rht) + ["rne", "sr", "sr8"].index(rounding))
     R, C = 61, 416
     x = (rng.standard_t(3, (R, C)) * np.exp(rng.uniform(-3, 3, (R, 1)))).astype(np.float32)
     xt = torch.from_numpy(x).to(dtype)
