@@ -171,7 +171,12 @@ class Workload:
 
 
     def extras(self):
-        """Kernels of the next rows, timed beside the step: the dgrad product
+        """Kernels of the next rows, timed beside the step: the quantize-only
+        workload with 8-bit stochastic-rounding draws (16 elements per Philox
+        call instead of 8; the step keeps the 16-bit draws), the dgrad product
+        (and, beside it, dY quantized with RNE and the same product with dY
+        quantized inside the GEMM's operand load, mx_gemm_fused_quant_a, to
+        compare with that quantize plus dgrad_gemm)
         that reuses the forward weight through its exact 2-D transpose, the
         MXFP8 / MXFP6 element types at the fprop shape, the fprop product
         quantized in the GEMM epilogue (compare with fprop_gemm plus
@@ -180,11 +185,20 @@ class Workload:
         quantized once and stored to its 4 routed rows, the same bytes), and
         the MoE grouped product quantized in its epilogue."""
         t_bytes = 2 * (2880 * 5760 // 2 + (2880 // 32) * (5760 // 32))
+        q = quant_bytes(16384, 2880)
         return [
+            ("quantize_rows_rht_sr8", lambda: mx.quantize(self.xq, rht_mask=self.q_mask, rounding="sr8",
+                                                          seed=self.q_seed, offset=0, out=self.q_last), "hbm", q),
+            ("quantize_dim0_rht_sr8", lambda: mx.quantize(self.xq, axis="dim0", rht_mask=self.q_mask,
+                                                          rounding="sr8", seed=self.q_seed, offset=1,
+                                                          out=self.q_dim0), "hbm", q),
             ("dgrad_transpose_w", lambda: mx.transpose(self.d_qw, out=self.d_qwt), "hbm", t_bytes),
             ("dgrad_quantize_dy", lambda: mx.quantize(self.d_dy, rounding="sr", seed=self.d_seed, out=self.d_qdy),
              "hbm", quant_bytes(16384, 5760)),
             ("dgrad_gemm", lambda: mx.gemm(self.d_qdy, self.d_qwt, out=self.d_dx), "mfma",
+             2 * 16384 * 2880 * 5760),
+            ("dgrad_quantize_dy_rne", lambda: mx.quantize(self.d_dy, out=self.d_qdy), "hbm", quant_bytes(16384, 5760)),
+            ("dgrad_fused_quant_a_gemm", lambda: mx.gemm_fused_quant_a(self.d_dy, self.d_qwt, out=self.d_dx), "mfma",
              2 * 16384 * 2880 * 5760),
             ("mxfp8_quantize_x", lambda: mx.quantize(self.fx, out=self.e8_qx), "hbm",
              quant_bytes(16384, 2880, out_bits=8)),
@@ -218,20 +232,24 @@ def rates(name, kind, amount, avg_ms):
 def time_each(ks, steps, flush=None):
     """Durations (ms) of each kernel over `steps` passes, with HIP events
     around every launch on the launch stream (torch's current stream): one
-    list per kernel.  With `flush` (a large device buffer) every launch is
-    preceded, outside its events, by a fill of that buffer, which evicts the
-    last-level cache, so each kernel reads its inputs from HBM."""
+    list per kernel.  With `flush` (a device buffer twice the 256 MB
+    last-level cache) every launch is preceded, outside its events, by a read
+    of that whole buffer, which evicts the caches (writing back what the
+    previous kernel left dirty) and leaves them holding clean lines, so each
+    kernel reads its inputs from HBM and starts with no write-back debt."""
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ks]
           for _ in range(steps)]
+    sink = []
     torch.cuda.synchronize()
     for s in range(steps):
         for k, (_, fn, _, _) in enumerate(ks):
             if flush is not None:
-                flush.fill_(s * len(ks) + k)
+                sink.append(flush.amax())
             ev[s][k][0].record()
             fn()
             ev[s][k][1].record()
     torch.cuda.synchronize()
+    del sink
     return [[ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(steps)] for k in range(len(ks))]
 
 
@@ -348,10 +366,13 @@ def main():
 
     # Component pass (untimed for the metric): K steps with HIP events around
     # every kernel on the launch stream (torch's current stream), each launch
-    # after a 512 MB fill that evicts the 256 MB last-level cache, for the
-    # per-kernel durations reported under "components" (mean, median, p10, p90).
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # after a read of a 512 MB buffer that evicts the 256 MB last-level cache,
+    # for the per-kernel durations reported under "components" (mean, median,
+    # p10, p90); then K steps without the eviction, each kernel right after its
+    # predecessor in the step as in the timed region ("us_in_sequence").
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)          # 512 MB
     comp_all = time_each(ks, args.steps, flush)
+    seq_all = time_each(ks, args.steps)
     comp_ms = [float(np.mean(t)) for t in comp_all]
     dom_k = int(np.argmax(comp_ms))
 
@@ -383,6 +404,8 @@ def main():
     comps = {name: {**rates(name, kind, amount, comp_ms[k]), **spread(comp_all[k])}
              for k, (name, _, kind, amount) in enumerate(ks)}
     comps[ks[dom_k][0]]["us_after_flush"] = flushed_ms * 1e3
+    for k, (name, _, _, _) in enumerate(ks):
+        comps[name]["us_in_sequence"] = float(np.mean(seq_all[k])) * 1e3
 
     # Next-row kernels, after the timed region (not part of the step or of value).
     xs = w.extras()
@@ -436,8 +459,9 @@ def main():
         "quantize_GBps_aggregate": quant_bytes_total / (quant_us * 1e-6) / 1e9,
         "copy_GBps_measured": copy_gbps,
         "timing": ("per-kernel: HIP events on the launch stream, each launch after a 512 MB cache-evicting "
-                   "fill; dominant kernel: events inside the timed step (us_after_flush: its cache-evicted "
-                   "launches); us = mean, with median/p10/p90"),
+                   "read; dominant kernel: events inside the timed step (us_after_flush: its cache-evicted "
+                   "launches); us = mean, with median/p10/p90; us_in_sequence: each kernel "
+                   "timed right after its predecessor in the step, no eviction"),
         "components": comps,
         "next_rows": extra,
         "roofline": roof,

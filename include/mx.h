@@ -320,14 +320,45 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale
                            void* stream);
 
 /*
+ * mx_gemm_fused_quant_a — C = Q(A) B^T with the A operand handed over in bf16
+ * and quantized to MXFP4 inside the GEMM's operand load, so the quantized A
+ * is never written to memory (the fusion of the quantizer into the GEMM that
+ * "Training an MoE LLM in MXFP4: How We Closed the Gap to BF16", summary,
+ * and "MXFP4", AI Wiki, §Training with MXFP4 motivate: MXFP4 GEMMs fed by
+ * activations quantized on the fly).  Each 32-element block of a row of A
+ * along K is quantized exactly as mx_quantize does (same scale rule, RNE,
+ * optional transform), so C equals mx_gemm of mx_quantize(A) and B whenever
+ * both accumulate in K order one 64-deep step at a time (every shape that
+ * mx_gemm_workspace_size does not split).  Every output tile re-reads and
+ * re-quantizes its rows of A: the quantization work is repeated once per
+ * 256 columns of C.
+ *
+ *   a, a_dtype  device; M x K elements, row stride lda elements (>= K, a
+ *               multiple of 8), 16-byte aligned.  a_dtype must be
+ *               MX_DT_BF16 (MX_DT_F32 returns MX_ERR_UNSUPPORTED).
+ *   cfg         host; axis MX_AXIS_LAST, block MX_BLOCK_1D and rounding
+ *               MX_ROUND_RNE (else MX_ERR_UNSUPPORTED); use_rht,
+ *               rht_sign_mask and scale_mode as in mx_quantize.
+ *   B           host struct of device buffers: MXFP4 [N, K], 1-D or 2-D.
+ *   C           device; [M, N] of c_dtype, row stride ldc elements (>= N).
+ *   Requires K % 32 == 0.  M or N = 0: nothing is written; K = 0 writes
+ *   zeros (A is not read and may be NULL).
+ */
+mx_status mx_gemm_fused_quant_a(const void* a, int32_t a_dtype, int64_t M, int64_t K, int64_t lda,
+                                const mx_quant_cfg* cfg, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                                void* stream);
+
+/*
  * mx_gemm_workspace_size — bytes of device workspace mx_gemm needs for an
  * M x N x K problem (0 if none).  Problems with too few 256 x 256 output tiles
  * to fill the GPU, or a K longer than one float32 accumulator may sum while
  * keeping 1e-5 sum|a b| ("MXFP4", AI Wiki, §Conversion rules: the long dot
  * product is a sum of block dot products accumulated in float32), are split
  * along K: each output is accumulated in float32 over K segments of at most
- * 10240 and the segment sums are added in K order, an order fixed by the
- * shape alone (the result is the same bit for bit on every run).  With one
+ * 10240 (each tile walks its K range from a start fixed by the shape,
+ * wrapping around once) and the segment sums are added in that walk's order,
+ * fixed by the shape alone (the result is the same bit for bit on every
+ * run).  With one
  * rounding per 64-deep step the error of an output is at most
  * (n - 1 + S - 1) 2^-24 sum|a b| to first order, n the 64-deep steps of its
  * longest segment (<= 160) and S its segments (<= 8): 8.6e-6 sum|a b| for the

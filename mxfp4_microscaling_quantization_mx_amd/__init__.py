@@ -32,7 +32,8 @@ _ELEM = {"e2m1": (0, 4), "e4m3": (1, 8), "e5m2": (2, 8), "e2m3": (3, 6), "e3m2":
 _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
 EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
-            "mx_gemm_quantize", "mx_gemm_workspace_size", "mx_gemm_noalloc", "mx_grouped_gemm", "mx_grouped_gemm_quantize",
+            "mx_gemm_quantize", "mx_gemm_workspace_size", "mx_gemm_noalloc", "mx_gemm_fused_quant_a", "mx_grouped_gemm",
+            "mx_grouped_gemm_quantize",
             "mx_last_error", "mx_version")
 
 
@@ -78,12 +79,14 @@ def load_library(path=LIB_PATH):
     lib.mx_gemm.argtypes = [PT, PT, P, I32, I64, P, ctypes.c_size_t, P]
     lib.mx_gemm_quantize.argtypes = [PT, PT, I32, PT, P]
     lib.mx_gemm_noalloc.argtypes = [PT, PT, P, I32, I64, P]
+    lib.mx_gemm_fused_quant_a.argtypes = [P, I32, I64, I64, I64, ctypes.POINTER(QuantCfgC), PT, P, I32, I64, P]
     lib.mx_gemm_workspace_size.argtypes = [I64, I64, I64]
     lib.mx_gemm_workspace_size.restype = ctypes.c_size_t
     lib.mx_grouped_gemm.argtypes = [PT, P, I32, PT, I64, I64, P, I32, I64, P]
     lib.mx_grouped_gemm_quantize.argtypes = [PT, P, I32, PT, I64, I64, I32, PT, P]
     for f in ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
-              "mx_gemm_quantize", "mx_gemm_noalloc", "mx_grouped_gemm", "mx_grouped_gemm_quantize"):
+              "mx_gemm_quantize", "mx_gemm_noalloc", "mx_gemm_fused_quant_a", "mx_grouped_gemm",
+              "mx_grouped_gemm_quantize"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mx_last_error.restype = ctypes.c_char_p
     lib.mx_last_error.argtypes = []
@@ -293,6 +296,24 @@ def gemm_noalloc(a, b, out_dtype=torch.float32, out=None):
     at, bt = a.c_struct(), b.c_struct()
     _check(lib.mx_gemm_noalloc(ctypes.byref(at), ctypes.byref(bt), _ptr(out), _DTYPE[out.dtype], out.stride(0),
                                _stream(out)))
+    return out
+
+
+def gemm_fused_quant_a(a, b, out_dtype=torch.float32, out=None, rht_mask=None, scale_mode="floor"):
+    """C = Q(A) * B^T with A a 2-D bf16 CUDA tensor [M, K] quantized to MXFP4
+    inside the GEMM's operand load (RNE, 1-D blocks along K, optional
+    transform; see mx_gemm_fused_quant_a) and B an MXFP4 operand [N, K]."""
+    lib = load_library()
+    if a.dim() != 2 or a.dtype not in _DTYPE or not a.is_cuda or a.stride(1) != 1:
+        raise ValueError("gemm_fused_quant_a expects a row-major 2-D bf16 CUDA tensor")
+    M, K = a.shape
+    if out is None:
+        out = torch.empty((M, b.rows), dtype=out_dtype, device=a.device)
+    cfg = QuantCfgC(_AXIS["last"], _BLOCK["1d"], _ROUND["rne"], int(rht_mask is not None),
+                    (rht_mask or 0) & 0xFFFFFFFF, _SCALE[scale_mode], 0, 0)
+    bt = b.c_struct()
+    _check(lib.mx_gemm_fused_quant_a(_ptr(a), _DTYPE[a.dtype], M, K, a.stride(0), ctypes.byref(cfg), ctypes.byref(bt),
+                                     _ptr(out), _DTYPE[out.dtype], out.stride(0), _stream(out)))
     return out
 
 

@@ -577,6 +577,71 @@ __device__ __forceinline__ v8i read_mx(const uint8_t* row, int ks, int hi) {
   }
 }
 
+// ------------------------------------------ A quantized in the operand load
+// The A operand may arrive as bf16 [M, K] and be quantized to MXFP4 on its way
+// into LDS (RNE, 1-D blocks along K, optionally the 32-point transform with
+// sign mask `mask`), by the same block step the quantizer kernels use, so the
+// codes and scale bytes the MFMAs read are those mx_quantize writes.  A
+// 256-row, 128-deep stage is 64 KiB of bf16: thread t of the 512 holds half a
+// row, row t/2 and blocks 2(t%2), 2(t%2)+1 (128 contiguous bytes, eight
+// 16-byte loads).  Rows past M and blocks past K load as zeros (zero codes).
+struct QaSrc {
+  const uint16_t* a;
+  int64_t lda;          // elements
+  uint32_t mask;
+  int scale_mode;
+};
+
+struct QaStage {
+  uint4 v[8];
+};
+
+__device__ __forceinline__ void fetch_qa(QaStage& f, const QaSrc& q, int64_t m0, int64_t M, int64_t k0, int64_t K) {
+  const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+  const int64_t gr = m0 + r;
+  const int64_t kk = k0 + 64 * h;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) f.v[4 * b + u] = make_uint4(0u, 0u, 0u, 0u);
+    if (gr < M && kk + 32 * b < K) {        // K % 32 == 0: a block is whole or absent
+      const uint4* p = reinterpret_cast<const uint4*>(q.a + gr * q.lda + kk + 32 * b);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) f.v[4 * b + u] = p[u];
+    }
+  }
+}
+
+// Quantize the thread's two blocks and store their codes (16 bytes each, at
+// byte 16 j of the row for block j) and scale bytes (byte j of the row's
+// scale word) to LDS.
+template <bool RHT>
+__device__ __forceinline__ void put_qa(const QaStage& f, const QaSrc& q, uint8_t* la, int pitch, uint32_t* lsa) {
+  const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+  uint32_t sbytes = 0;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float x[32];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w[4] = {f.v[4 * b + u].x, f.v[4 * b + u].y, f.v[4 * b + u].z, f.v[4 * b + u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 8 * u + 2 * i;        // element index in the block
+        uint32_t v = w[i];
+        if (RHT) v ^= (((q.mask >> e) & 1u) << 15) | (((q.mask >> (e + 1)) & 1u) << 31);
+        x[e] = bf16lo(v);
+        x[e + 1] = bf16hi(v);
+      }
+    }
+    uint32_t packed[4];
+    const uint32_t s = quantize_block32<RHT, 0>(x, packed, 0u, 0u, 0u, q.scale_mode);
+    *reinterpret_cast<uint4*>(la + r * pitch + 32 * h + 16 * b) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    sbytes |= s << (8 * b);
+  }
+  reinterpret_cast<uint16_t*>(lsa + r)[h] = (uint16_t)sbytes;
+}
+
 // Tile BM x BN per workgroup; each wave owns TI x TJ MFMA tiles of 32x32
 // (waves laid out BM/(32 TI) x BN/(32 TJ)).
 template <int FA, int FB, int BM_, int BN_, int TI, int TJ>
@@ -586,13 +651,16 @@ constexpr int mx_threads() {
 
 // The output tile [m0, m0 + BM_) x [n0, n0 + BN_) of C = A B^T (rows past M
 // or N are neither read nor written).
-template <int FA, int FB, int BM_, int BN_, int TI, int TJ>
+// QA (1: plain, 2: with the transform): A comes from bf16 through qa and is
+// quantized in the load (FA must be MXFP4, 256-row tiles of 512 threads).
+template <int FA, int FB, int BM_, int BN_, int TI, int TJ, int QA = 0>
 __device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand& B, int64_t M, int64_t N,
                                              int64_t K, int64_t m0, int64_t n0, void* C, int64_t ldc, int a_2d,
-                                             int b_2d, int out_bf16) {
+                                             int b_2d, int out_bf16, const QaSrc& qa = QaSrc{}) {
   constexpr int WN = BN_ / (32 * TJ);
   constexpr int THREADS = mx_threads<FA, FB, BM_, BN_, TI, TJ>();
   static_assert(THREADS >= BM_ + BN_, "one scale row per thread");
+  static_assert(QA == 0 || (FA == 0 && BM_ == 256 && THREADS == 512), "two threads per A row of the stage");
   constexpr int PA = 128 * elem_bits<FA>() / 8 + 16, PB = 128 * elem_bits<FB>() / 8 + 16;
   constexpr int FMA = mfma_fmt<FA>(), FMB = mfma_fmt<FB>();
   __shared__ __attribute__((aligned(16))) uint8_t la[BM_ * PA];
@@ -611,17 +679,21 @@ __device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   MxStage<FA, BM_, THREADS> fa;
+  QaStage fq;
   MxStage<FB, BN_, THREADS> fb;
   if (K > 0) {
-    fetch_mx(fa, A, a_2d != 0, m0, M, 0, K, tid);
+    if constexpr (QA) fetch_qa(fq, qa, m0, M, 0, K);
+    else fetch_mx(fa, A, a_2d != 0, m0, M, 0, K, tid);
     fetch_mx(fb, B, b_2d != 0, n0, N, 0, K, tid - BM_);
   }
   for (int64_t k0 = 0; k0 < K; k0 += 128) {
-    put_mx(fa, la, PA, lsa, tid);
+    if constexpr (QA) put_qa<QA == 2>(fq, qa, la, PA, lsa);
+    else put_mx(fa, la, PA, lsa, tid);
     put_mx(fb, lb, PB, lsb, tid - BM_);
     __syncthreads();
     if (k0 + 128 < K) {                 // the next stage's loads fly during this stage's MFMAs
-      fetch_mx(fa, A, a_2d != 0, m0, M, k0 + 128, K, tid);
+      if constexpr (QA) fetch_qa(fq, qa, m0, M, k0 + 128, K);
+      else fetch_mx(fa, A, a_2d != 0, m0, M, k0 + 128, K, tid);
       fetch_mx(fb, B, b_2d != 0, n0, N, k0 + 128, K, tid - BM_);
     }
 #pragma unroll
@@ -680,6 +752,16 @@ __global__ __launch_bounds__((mx_threads<FA, FB, BM_, BN_, TI, TJ>())) void k_ge
     int out_bf16) {
   gemm_mx_tile<FA, FB, BM_, BN_, TI, TJ>(A, B, M, N, K, (int64_t)blockIdx.y * BM_, (int64_t)blockIdx.x * BN_, C,
                                          ldc, a_2d, b_2d, out_bf16);
+}
+
+// C = Q(A) B^T with A bf16, quantized in the operand load (QA as above); B
+// MXFP4; 256x256 tiles, blockIdx.x the N tile, so the workgroups in flight
+// at once share an A panel.
+template <int QA>
+__global__ __launch_bounds__(512) void k_gemm_qa(QaSrc qa, MxOperand B, int64_t M, int64_t N, int64_t K, void* C,
+                                                  int64_t ldc, int b_2d, int out_bf16) {
+  gemm_mx_tile<0, 0, 256, 256, 2, 4, QA>(MxOperand{}, B, M, N, K, (int64_t)blockIdx.y * 256,
+                                         (int64_t)blockIdx.x * 256, C, ldc, 0, b_2d, out_bf16, qa);
 }
 
 // Grouped (MoE) form: blockIdx.y is a row-tile slot, mapped to (expert, rows)
@@ -846,6 +928,19 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     else { if (a.b_2d) MX_G(false, true, false); else MX_G(false, false, false); }
   }
 #undef MX_G
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_qa(const GemmQaArgs& a, hipStream_t st) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)((a.M + 255) / 256));
+  const QaSrc q{static_cast<const uint16_t*>(a.a), a.lda, a.rht ? a.mask : 0u, a.scale_mode};
+  if (a.rht)
+    hipLaunchKernelGGL((k_gemm_qa<2>), grid, dim3(512), 0, st, q, a.B, a.M, a.N, a.K, a.C, a.ldc, (int)a.b_2d,
+                       (int)a.out_bf16);
+  else
+    hipLaunchKernelGGL((k_gemm_qa<1>), grid, dim3(512), 0, st, q, a.B, a.M, a.N, a.K, a.C, a.ldc, (int)a.b_2d,
+                       (int)a.out_bf16);
   return hipGetLastError();
 }
 

@@ -6,16 +6,19 @@
 // dot products accumulated in float32, with the order of that sum left to the
 // implementation.  Here each output is accumulated in float32 over K ranges
 // ("segments") of at most SK_MAX_PAIRS x 512 K, and the segment results are
-// added in K order (gemm_tile256.h, store_unit), so the order is fixed by the
-// problem shape alone and the result is the same bit for bit on every run.
+// added in segment order (gemm_tile256.h, store_unit; the segments follow the
+// tile's rotated pair order below), so the order is fixed by the problem shape
+// alone and the result is the same bit for bit on every run.
 //
 // Work split: the tiles' K ranges, in units of 512 K (two 256-deep stages, the
 // granule of the scale loads), are laid end to end (tile after tile in the
 // grouped tile order) and cut into W equal contiguous ranges, one per
 // persistent workgroup ("worker"): U pairs in all, worker w takes pairs
-// [floor(w U / W), floor((w + 1) U / W)).  A tile cut by these ranges is
-// summed by its last segment to finish; a tile inside one range is stored as
-// in the plain kernel.  W is a multiple of 256 chosen from the shape only (not
+// [floor(w U / W), floor((w + 1) U / W)).  Each tile walks its pairs from a
+// rotated start (SplitSched::rotation), so that the workers run in step along
+// K and share operand slices in L2.  A tile cut by these ranges is summed by
+// its last segment to finish; a tile inside one range is stored as in the
+// plain kernel.  W is a multiple of 256 chosen from the shape only (not
 // from the device), so the cuts, and with them the rounding, are the same on
 // any GPU.  Worker w runs as workgroup b with b % 8 = its XCD and consecutive
 // workers on one XCD, so the workers that share a tile mostly share an L2.
@@ -154,9 +157,27 @@ struct SplitSched {
     ti.M = P.M;
     ti.N = P.N;
     ti.c_row0 = ti.m0;
-    ti.k0 = 2 * lo;                    // even; a tile with an odd stage count runs one padding stage
+    // even; a tile with an odd stage count runs one padding stage (K stages
+    // [k0, k0 + ns) lie inside [0, 2P): lo + rot < P, or rot = 0)
+    ti.k0 = 2 * ((lo + rotation(P, t)) % P.P);
     ti.ns = 2 * (hi - lo);
     return ti;
+  }
+  // Tile t walks its pairs from pair rot: local pair l (the l-th of the
+  // tile's range in the laid-end-to-end order) is K pair (l + rot) mod P.
+  // rot moves the first cut inside the tile (the start of worker w1 + 1, at
+  // local pair o) to K pair 0, so no unit wraps past the tile's last pair,
+  // and the worker starting there is at K pair 0 when it starts, like every
+  // worker whose range starts inside a tile.  The worker ending in the tile
+  // (local pairs [0, o), K pairs [P - o, P)) is then at K pair P - L, L the
+  // range length, when it gets there: at any moment the workers are in a few
+  // K phases, so the workers of an XCD read the same few 512-K slices of their
+  // operand panels and find them in L2.  A tile without a cut inside keeps
+  // rot = 0.
+  __device__ static int rotation(const SkParams& P, int t) {
+    const int64_t tp = (int64_t)t * P.P;
+    const int64_t c = sk_cut(sk_worker(tp, P.U, P.W) + 1, P.U, P.W);
+    return c > tp && c < tp + P.P ? (int)(tp + P.P - c) : 0;
   }
   __device__ int total_stages() const {
     const SkParams P = load_sk(prm);

@@ -623,7 +623,7 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
   // Code offsets of the prefetch stage (the tail stage masks the chunks past
   // K; a unit's padding stage past the tail masks all of them).
   auto stage_offsets = [&](uint32_t va[4], uint32_t vb[4]) {
-    const int k = kb2 + s2;
+    const int k = (kb2 + s2);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bool live;
@@ -678,10 +678,11 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
   uint32_t pend_cs = 0, pend_m0 = lds_addr + 2 * STAGE_BYTES + 2 * SSLOT;
   for (int g = 0; g < gtotal; ++g) {
     const uint32_t slot = lds_addr + (uint32_t)((g & 1) * STAGE_BYTES);
-    uint32_t keep_lo = kb + s < nfull ? 0xFFFFFFFFu : tail_lo;
-    uint32_t keep_hi = kb + s < nfull ? 0xFFFFFFFFu : tail_hi;
+    const int kc = kb + s;                  // the K stage multiplied now
+    uint32_t keep_lo = kc < nfull ? 0xFFFFFFFFu : tail_lo;
+    uint32_t keep_hi = kc < nfull ? 0xFFFFFFFFu : tail_hi;
     if constexpr (UNITS) {
-      if (kb + s > nfull) keep_lo = keep_hi = 0u;   // a padding stage past the tail
+      if (kc > nfull) keep_lo = keep_hi = 0u;   // a padding stage past the tail
     }
     int sa[TI], sb[TJ], sa2[TI], sb2[TJ];
 #pragma unroll
@@ -697,7 +698,7 @@ __device__ __forceinline__ void run_tiles(const Sched& sc, const Strides& sd, in
     // 64-deep steps of this stage that hold K-blocks below K: all four except
     // in the tail stage (none in a unit's padding stage, whose first step
     // still runs on masked scales to carry its loads)
-    const int live = kb + s < nfull ? 4 : (kb + s == nfull ? (kchunks + 1) >> 1 : 0);
+    const int live = kc < nfull ? 4 : (kc == nfull ? (kchunks + 1) >> 1 : 0);
     // the B half of stage g+1's loads (issued by the previous iteration's
     // prefetch position; dummy loads past the end in the first iteration)
     if constexpr (SPLIT)
@@ -822,8 +823,9 @@ __device__ __forceinline__ void store_tile(const Acc& acc, void* C, int ldc, int
 
 // ------------------------------------------------------------ split-K epilogue
 // A unit that covers only part of its tile's K range ends here.  The tile's
-// segments (its K range cut at the unit boundaries, segment 0 first along K)
-// each hold a float32 partial product; the tile is their sum taken in segment
+// segments (its K range cut at the unit boundaries, segment 0 first in the
+// tile's pair order) each hold a float32 partial product; the tile is their
+// sum taken in segment
 // order, ((p_0 + p_1) + p_2) + ..., each addition rounded to float32, so the
 // result does not depend on which workgroup gets there last.  No workgroup
 // waits for another: each segment first reads the tile's counter; if every

@@ -387,6 +387,56 @@ mx_status mx_gemm_noalloc(const mx_tensor* A, const mx_tensor* B, void* C, int32
   return hip_status(mx::launch_gemm(a, static_cast<hipStream_t>(stream)), "mx_gemm_noalloc");
 }
 
+mx_status mx_gemm_fused_quant_a(const void* a, int32_t a_dtype, int64_t M, int64_t K, int64_t lda,
+                                const mx_quant_cfg* cfg, const mx_tensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                                void* stream) {
+  g_err[0] = '\0';
+  const char* what = "mx_gemm_fused_quant_a";
+  if (!cfg || !B) return fail(MX_ERR_INVALID_ARG, "%s: null cfg or B", what);
+  if (a_dtype != MX_DT_F32 && a_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "%s: unknown A dtype %d", what, a_dtype);
+  if (a_dtype != MX_DT_BF16) return fail(MX_ERR_UNSUPPORTED, "%s: A must be bf16", what);
+  if (cfg->axis != MX_AXIS_LAST || cfg->block != MX_BLOCK_1D || cfg->rounding != MX_ROUND_RNE)
+    return fail(MX_ERR_UNSUPPORTED, "%s: A is quantized along K with 1-D blocks and RNE only", what);
+  if (cfg->use_rht != 0 && cfg->use_rht != 1) return fail(MX_ERR_INVALID_ARG, "%s: use_rht must be 0 or 1", what);
+  if (cfg->scale_mode > MX_SCALE_PRESCALE_3_4)
+    return fail(MX_ERR_INVALID_ARG, "%s: unknown scale_mode %u", what, cfg->scale_mode);
+  mx_status st = check_tensor(B, "mx_gemm_fused_quant_a: B");
+  if (st != MX_OK) return st;
+  if (B->elem != MX_ELEM_E2M1) return fail(MX_ERR_UNSUPPORTED, "%s: B must be MXFP4", what);
+  if (M < 0 || K < 0) return fail(MX_ERR_INVALID_ARG, "%s: negative shape", what);
+  if (K % 32) return fail(MX_ERR_INVALID_ARG, "%s: K=%lld is not a multiple of 32", what, (long long)K);
+  if (B->K != K) return fail(MX_ERR_INVALID_ARG, "%s: K=%lld != B.K=%lld", what, (long long)K, (long long)B->K);
+  if (c_dtype != MX_DT_F32 && c_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "%s: unknown output dtype %d", what, c_dtype);
+  const int64_t N = B->rows;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!C) return fail(MX_ERR_INVALID_ARG, "%s: null C", what);
+  if (ldc < N) return fail(MX_ERR_INVALID_ARG, "%s: ldc=%lld < N=%lld", what, (long long)ldc, (long long)N);
+  if (K > 0) {
+    if (!a) return fail(MX_ERR_INVALID_ARG, "%s: null A", what);
+    if (lda < K) return fail(MX_ERR_INVALID_ARG, "%s: lda=%lld < K=%lld", what, (long long)lda, (long long)K);
+    if (!aligned(a, 16) || lda % 8)
+      return fail(MX_ERR_INVALID_ARG, "%s: A must be 16-byte aligned with lda %% 8 == 0", what);
+  }
+  if ((M + 255) / 256 > 65535) return fail(MX_ERR_UNSUPPORTED, "%s: M too large", what);
+  mx::GemmQaArgs q{};
+  q.a = a;
+  q.lda = lda;
+  q.rht = cfg->use_rht == 1;
+  q.mask = cfg->rht_sign_mask;
+  q.scale_mode = (int)cfg->scale_mode;
+  q.B = operand(B);
+  q.b_2d = B->block == MX_BLOCK_2D;
+  q.M = M;
+  q.N = N;
+  q.K = K;
+  q.C = C;
+  q.ldc = ldc;
+  q.out_bf16 = c_dtype == MX_DT_BF16;
+  return hip_status(mx::launch_gemm_qa(q, static_cast<hipStream_t>(stream)), what);
+}
+
 mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale_mode, mx_tensor* out,
                            void* stream) {
   g_err[0] = '\0';

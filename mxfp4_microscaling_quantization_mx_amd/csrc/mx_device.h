@@ -448,4 +448,77 @@ __device__ __forceinline__ float elem_value(uint32_t c) {
   return (c >> (T::E + T::M)) & 1u ? -mag : mag;
 }
 
+// ------------------------------------------------------ the MXFP4 block step
+// Quantize one block held in registers (x already sign-flipped when RHT).
+// Returns the scale byte and writes the 16 code bytes to `packed`.
+// With TWO_D the amax is taken over the 32 lanes of the half-wave as well
+// (one lane per column of a 32x32 tile; all 32 lanes must be active).
+// scale_mode (wave-uniform): 0 the reference rule floor(log2 amax) - 2; 1 the
+// round-up rule; 2 the reference rule's scale with every element multiplied by
+// 0.75 (one float32 multiply) before the division, so nothing clips.
+template <bool RHT, int SR, bool TWO_D = false>
+__device__ __forceinline__ uint32_t quantize_block32(float x[32], uint32_t packed[4], uint64_t p0,
+                                                     uint64_t seed, uint64_t offset, int scale_mode) {
+  const float c = __uint_as_float(kRhtCBits);
+  if (RHT) fwht32_inlane(x);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  // multiplying by a positive constant commutes with the max (rounding is monotone)
+  if (RHT) {
+    m = __float_as_uint(c * __uint_as_float(m));      // max |c t_i| = c max |t_i|
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = c * x[i];
+  }
+  if (TWO_D) {
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
+  }
+  const uint32_t s = scale_mode == 1 ? scale_code_round_up(m) : scale_code_from_absmax_bits(m);
+  packed[0] = packed[1] = packed[2] = packed[3] = 0u;
+  if (s == 0xFFu) return s;
+  if (scale_mode == 2) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.75f * x[i];
+  }
+  if (SR) {
+    const float inv = inv_scale_from_code(s);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t w[4];
+      if constexpr (SR == 2) {
+        // 8-bit draws: one Philox call per 16 elements, element i of the call
+        // taking byte (i & 3) of word i >> 2; each byte b goes in as the
+        // 16-bit draw 256 b, with which the 16-bit rule rounds up exactly
+        // when b < 256 f
+        uint32_t W[4];
+        sr_words((p0 >> 4) + (g >> 1), seed, offset, W);
+        const uint32_t w0 = W[2 * (g & 1)], w1 = W[2 * (g & 1) + 1];
+        w[0] = sr8_pair<0>(w0);
+        w[1] = sr8_pair<1>(w0);
+        w[2] = sr8_pair<0>(w1);
+        w[3] = sr8_pair<1>(w1);
+      } else {
+        sr_words((p0 >> 3) + g, seed, offset, w);
+      }
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = x[8 * g + i] * inv;
+      packed[g] = pack8_sr(v, w);
+    }
+  } else {
+    float sc = scale_f32_normal(s);
+    if (s == 0u) {
+      // scale 2^-127 is a float32 subnormal: multiply by 2^127 instead and
+      // convert at scale 1 (the same single rounding)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = x[i] * __uint_as_float(0x7F000000u);
+      sc = 1.0f;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) packed[g] = pack8_rne(x + 8 * g, sc);
+  }
+  return s;
+}
+
 }  // namespace mx

@@ -68,6 +68,23 @@ struct GemmQuantArgs {
   int scale_mode;
 };
 
+// C = Q(A) B^T with A bf16 [M, K] (row stride lda elements) quantized to
+// MXFP4 in the GEMM's operand load (RNE, 1-D blocks along K, optional
+// transform with sign mask `mask`, scale_mode as mx_quantize); B MXFP4.
+struct GemmQaArgs {
+  const void* a;
+  int64_t lda;
+  bool rht;
+  uint32_t mask;
+  int scale_mode;
+  MxOperand B;
+  bool b_2d;
+  int64_t M, N, K;
+  void* C;
+  int64_t ldc;
+  bool out_bf16;
+};
+
 struct GroupedGemmArgs {
   MxOperand A, B;             // B = expert 0
   bool a_2d, b_2d;
@@ -109,6 +126,7 @@ hipError_t launch_quantize_scatter(const QuantArgs& a, const int32_t* dest, int 
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_qa(const GemmQaArgs& a, hipStream_t st);
 // Whether the 256x256 MXFP4 pipeline takes this problem's layout (16-byte
 // scale rows, operands and output under 2 GiB, M and N >= 256).
 bool gemm256_layout_ok(const GemmArgs& a);

@@ -294,3 +294,41 @@ def test_last_error_cleared_on_success(lib):
     assert lib.mx_last_error() != b""
     lib.mx_quantize(None, 1, 0, 64, 64, ctypes.byref(cfg), ctypes.byref(out), None)
     assert lib.mx_last_error() == b""
+
+
+def test_gemm_fused_quant_a_rejects_bad_arguments(lib):
+    """Host-side checks of mx_gemm_fused_quant_a, before any launch."""
+    B = ctypes.byref
+    P = ctypes.c_void_p
+    f = lib.mx_gemm_fused_quant_a
+    cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 0, 0, 0)
+    b = _tensor(64, 96)
+    ok = (P(16), mx.MX_DT_BF16, 256, 96, 96, B(cfg), B(b), P(16), 0, 64, None)
+
+    def call(**kw):
+        args = list(ok)
+        names = ["a", "a_dtype", "M", "K", "lda", "cfg", "b", "c", "c_dtype", "ldc", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(a_dtype=0) == mx.MX_ERR_UNSUPPORTED and b"bf16" in lib.mx_last_error()
+    assert call(a_dtype=5) == mx.MX_ERR_INVALID_ARG
+    for bad in (mx.QuantCfgC(1, 0, 0, 0, 0, 0, 0, 0), mx.QuantCfgC(0, 1, 0, 0, 0, 0, 0, 0),
+                mx.QuantCfgC(0, 0, 1, 0, 0, 0, 0, 0), mx.QuantCfgC(0, 0, 2, 0, 0, 0, 0, 0)):
+        assert call(cfg=B(bad)) == mx.MX_ERR_UNSUPPORTED and b"RNE" in lib.mx_last_error()
+    assert call(cfg=B(mx.QuantCfgC(0, 0, 0, 0, 0, 3, 0, 0))) == mx.MX_ERR_INVALID_ARG
+    assert call(cfg=None) == mx.MX_ERR_INVALID_ARG
+    assert call(K=80, lda=80) == mx.MX_ERR_INVALID_ARG and b"multiple of 32" in lib.mx_last_error()
+    assert call(K=128, lda=128) == mx.MX_ERR_INVALID_ARG and b"B.K" in lib.mx_last_error()
+    assert call(lda=64) == mx.MX_ERR_INVALID_ARG and b"lda" in lib.mx_last_error()
+    assert call(lda=100) == mx.MX_ERR_INVALID_ARG and b"aligned" in lib.mx_last_error()
+    assert call(a=P(18)) == mx.MX_ERR_INVALID_ARG and b"aligned" in lib.mx_last_error()
+    assert call(a=None) == mx.MX_ERR_INVALID_ARG
+    assert call(c=None) == mx.MX_ERR_INVALID_ARG
+    assert call(ldc=32) == mx.MX_ERR_INVALID_ARG and b"ldc" in lib.mx_last_error()
+    assert call(c_dtype=7) == mx.MX_ERR_INVALID_ARG
+    fp8 = mx.MxTensorC(16, 16, 64, 96, 96, 3, 0, 1)
+    assert call(b=B(fp8)) == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
+    assert call(M=-1) == mx.MX_ERR_INVALID_ARG
+    assert call(M=0, a=None, c=None) == mx.MX_OK          # empty: nothing launched

@@ -2,7 +2,7 @@
 
 Shapes with too few 256x256 output tiles for the chip (or a K too long for one
 float32 accumulator) are cut along K into segments whose float32 partial
-products are added in K order ("MXFP4", AI Wiki, §Conversion rules: the long
+products are added in a fixed order ("MXFP4", AI Wiki, §Conversion rules: the long
 dot product is a sum of block dot products accumulated in float32).  The rule
 is the GEMM rule of the other tests: |C - ref| <= 1e-5 * sum_k |a_k b_k| per
 output against the oracle's float64 product of the dequantized operands.  On
