@@ -296,46 +296,87 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
 }
 
 // ------------------------------------------------------------------ columns (blocks along dim 0)
-// Blocks along dim 0 without an LDS tile: lane = source column (= output row),
-// wave w of the workgroup = K-block 4*blockIdx.y + w (32 source rows).  Each
-// of the 32 loads of a lane reads one element; across the wave it reads 64
-// consecutive columns of one source row.  The block then goes through the same
-// register path as a row block.  2-D: a half-wave holds one 32x32 tile (output
-// rows are a multiple of 32, so half-waves are whole or empty).
+// Blocks along dim 0 without an LDS input tile: lane = source column (= output
+// row); the 4 waves of a workgroup take the 8 K-blocks [8 y, 8 y + 8) of its
+// 64 columns (256 source rows), two each.  Each of the 32 loads of a block
+// reads one element per lane; across the wave it reads 64 consecutive columns
+// of one source row.  The blocks go through the same register path as a row
+// block.  Their codes and scale bytes are gathered in LDS, so that each output
+// row's 8 blocks (MXFP4: 128 contiguous code bytes, one cache line) leave as
+// whole 16-byte pieces from consecutive lanes, instead of every store
+// instruction putting one 16-byte piece into each of 64 rows.  2-D: a
+// half-wave holds one 32x32 tile (output rows are a multiple of 32, so
+// half-waves are whole or past the end).
+constexpr int COLS_KB = 8;    // K-blocks per workgroup of the dim-0 kernel
+
 template <bool TWO_D, bool BF16, bool RHT, int SR, int ELEM>
 __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src, int64_t R, int64_t C,
                                                     int64_t ld_src, uint8_t* __restrict__ codes,
                                                     int64_t ld_codes, uint8_t* __restrict__ scales,
                                                     int64_t ld_scales, uint32_t mask, uint64_t seed,
                                                     uint64_t offset, int scale_mode) {
+  constexpr int BB = block_bytes<ELEM>();
+  constexpr int RB = COLS_KB * BB;           // code bytes of one output row here (a multiple of 16)
+  constexpr int PITCH = RB + 16;             // LDS row pitch: rows start in different banks
+  __shared__ __attribute__((aligned(16))) uint8_t lc[64 * PITCH];
+  __shared__ uint8_t ls[64 * COLS_KB];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t kb = (int64_t)blockIdx.y * 4 + w;
-  if (col >= C || kb * 32 >= R) return;
-  // a raw buffer over the block's 32 source rows: per-lane column offset,
-  // wave-uniform row offsets
+  const int64_t col0 = (int64_t)blockIdx.x * 64;
+  const int64_t col = col0 + lane;
+  const int64_t kb0 = (int64_t)blockIdx.y * COLS_KB;
+  const int64_t nkb = R / 32;
   constexpr int ES = BF16 ? 2 : 4;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(static_cast<const uint8_t*>(src) + kb * 32 * ld_src * ES), 0,
-      (uint32_t)(31 * ld_src * ES + C * ES), 0x00020000);
-  const uint32_t voff = (uint32_t)(col * ES);
-  float x[32];
+  // lanes past the last column read the last column (their blocks are never
+  // stored; for 2-D they form whole half-waves of their own)
+  const uint32_t voff = (uint32_t)((col < C ? col : C - 1) * ES);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t soff = (uint32_t)(i * ld_src * ES);
-    uint32_t b = BF16 ? ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0) << 16)
-                      : __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
-    if (RHT) b ^= ((mask >> i) & 1u) << 31;
-    x[i] = __uint_as_float(b);
+  for (int h = 0; h < 2; ++h) {
+    const int kl = 2 * w + h;
+    const int64_t kb = kb0 + kl;
+    if (kb >= nkb) break;                    // wave-uniform
+    // a raw buffer over the block's 32 source rows: per-lane column offset,
+    // wave-uniform row offsets
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(src) + kb * 32 * ld_src * ES), 0,
+        (uint32_t)(31 * ld_src * ES + C * ES), 0x00020000);
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t soff = (uint32_t)(i * ld_src * ES);
+      uint32_t b = BF16 ? ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0) << 16)
+                        : __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+      if (RHT) b ^= ((mask >> i) & 1u) << 31;
+      x[i] = __uint_as_float(b);
+    }
+    const uint64_t p0 = (uint64_t)col * (uint64_t)R + (uint64_t)kb * 32u;   // output row * K + 32 kb
+    ls[lane * COLS_KB + kl] =
+        (uint8_t)quantize_store<ELEM, RHT, SR, TWO_D>(x, lc + lane * PITCH + kl * BB, p0, seed, offset, scale_mode);
   }
-  const uint64_t p0 = (uint64_t)col * (uint64_t)R + (uint64_t)kb * 32u;   // output row * K + 32 kb
-  const uint32_t s = quantize_store<ELEM, RHT, SR, TWO_D>(x, codes + col * ld_codes + kb * block_bytes<ELEM>(), p0,
-                                                          seed, offset, scale_mode);
+  __syncthreads();
+  const int nvalid = (int)(nkb - kb0 < COLS_KB ? nkb - kb0 : COLS_KB);
+  const int vbytes = nvalid * BB;            // a multiple of 8
+  constexpr int PIECES = RB / 16;
+#pragma unroll
+  for (int i = threadIdx.x; i < 64 * PIECES; i += 256) {
+    const int r = i / PIECES, off = 16 * (i - r * PIECES);
+    const int64_t orow = col0 + r;
+    if (orow < C && off < vbytes) {
+      uint8_t* g = codes + orow * ld_codes + kb0 * BB + off;
+      const uint4 v = *reinterpret_cast<const uint4*>(lc + r * PITCH + off);
+      if (off + 16 <= vbytes) *reinterpret_cast<uint4*>(g) = v;
+      else *reinterpret_cast<uint2*>(g) = make_uint2(v.x, v.y);   // an FP6 row ending mid-piece
+    }
+  }
   if (!TWO_D) {
-    scales[col * ld_scales + kb] = (uint8_t)s;
-  } else if ((col & 31) == 0) {
-    scales[(col >> 5) * ld_scales + kb] = (uint8_t)s;
+#pragma unroll
+    for (int i = threadIdx.x; i < 64 * COLS_KB; i += 256) {
+      const int r = i / COLS_KB, k = i - r * COLS_KB;
+      if (col0 + r < C && k < nvalid) scales[(col0 + r) * ld_scales + kb0 + k] = ls[i];
+    }
+  } else if (threadIdx.x < 2 * COLS_KB) {
+    const int r = 32 * (threadIdx.x / COLS_KB), k = threadIdx.x % COLS_KB;
+    if (col0 + r < C && k < nvalid) scales[((col0 + r) >> 5) * ld_scales + kb0 + k] = ls[r * COLS_KB + k];
   }
 }
 
@@ -351,7 +392,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ src
 
 template <bool TWO_D, bool BF16, int ELEM>
 hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)((a.C + 63) / 64), (unsigned)((a.R + 127) / 128));
+  dim3 grid((unsigned)((a.C + 63) / 64), (unsigned)((a.R + 32 * COLS_KB - 1) / (32 * COLS_KB)));
 #define MX_COLS(RHT_, SR_)                                                                   \
   hipLaunchKernelGGL((k_quant_cols<TWO_D, BF16, RHT_, SR_, ELEM>), grid, dim3(256), 0, st, a.src, a.R, a.C, \
                      a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset,      \
