@@ -508,40 +508,58 @@ struct MxStage {
 };
 
 // Bytes past K or rows past `rows` read as zeros and their scales as 1.0 (an
-// FP6 row may end half-way through a 16-byte unit).
+// FP6 row may end half-way through a 16-byte unit).  Raw buffer loads over
+// the tile's rows, with out-of-range lanes pointed past the end (they return
+// zeros), so no load sits behind a branch and all of them are in flight at
+// once.
+constexpr uint32_t MX_OOB = 0x80000000u;
+
 template <int F, int ROWS, int THREADS>
 __device__ __forceinline__ void fetch_mx(MxStage<F, ROWS, THREADS>& f, const MxOperand& op, bool two_d, int64_t r0,
                                          int64_t rows, int64_t k0, int64_t K, int stid) {
   using S = MxStage<F, ROWS, THREADS>;
   const int64_t kbytes = K * elem_bits<F>() / 8;
   const int64_t kb0 = k0 * elem_bits<F>() / 8;
+  int64_t nrows = rows - r0;
+  nrows = nrows < 0 ? 0 : (nrows > ROWS ? ROWS : nrows);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(op.codes + r0 * op.ld_codes), 0, (uint32_t)(nrows * op.ld_codes), 0x00020000);
 #pragma unroll
   for (int it = 0; it < S::N; ++it) {
     const int id = threadIdx.x + THREADS * it;
     const int r = id / S::U, u = id - r * S::U;
-    const int64_t gr = r0 + r, off = kb0 + 16 * u;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (gr < rows) {
-      const uint8_t* p = op.codes + gr * op.ld_codes + off;
-      if (off + 16 <= kbytes) {
-        v = *reinterpret_cast<const uint4*>(p);
-      } else if (off < kbytes) {
-        const uint2 h = *reinterpret_cast<const uint2*>(p);
-        v = make_uint4(h.x, h.y, 0u, 0u);
-      }
-    }
+    const int64_t off = kb0 + 16 * u;
+    const uint32_t voff = (r < nrows && off < kbytes) ? (uint32_t)(r * op.ld_codes + off) : MX_OOB;
+    uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff, 0, 0));
+    if (off + 16 > kbytes) v.z = v.w = 0u;     // an FP6 row ending 8 bytes into this unit
     f.v[it] = v;
   }
   f.sc = 0x7F7F7F7Fu;
-  if (stid >= 0 && stid < ROWS) {
+  if (stid >= 0 && stid < ROWS) {             // wave-uniform
     const int64_t gr = r0 + stid;
+    const int64_t s0 = two_d ? (r0 >> 5) : r0;
+    const int64_t srows = two_d ? ROWS / 32 + 1 : ROWS;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(op.scales + s0 * op.ld_scales), 0, (uint32_t)(srows * op.ld_scales), 0x00020000);
+    const int64_t srow = (two_d ? (gr >> 5) : gr) - s0;
+    const int64_t kb0s = k0 >> 5;               // a multiple of 4
+    // blocks of this stage below K (the rest of the word is row padding or
+    // the next row, replaced by scale 1.0)
+    const int64_t nk = (K >> 5) - kb0s;
     uint32_t w = 0;
+    if ((op.ld_scales & 3) == 0 && ((uintptr_t)op.scales & 3) == 0) {   // uniform: one 4-byte load per row
+      const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(
+          rs, gr < rows ? (uint32_t)(srow * op.ld_scales + kb0s) : MX_OOB, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t kb = (k0 >> 5) + j;
-      uint32_t sc = 127u;
-      if (gr < rows && kb * 32 < K) sc = op.scales[(two_d ? (gr >> 5) : gr) * op.ld_scales + kb];
-      w |= sc << (8 * j);
+      for (int j = 0; j < 4; ++j) w |= (gr < rows && j < nk ? (v >> (8 * j)) & 0xFFu : 127u) << (8 * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool valid = gr < rows && j < nk;
+        const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(
+            rs, valid ? (uint32_t)(srow * op.ld_scales + kb0s + j) : MX_OOB, 0, 0);
+        w |= (valid ? b : 127u) << (8 * j);
+      }
     }
     f.sc = w;
   }
@@ -598,17 +616,19 @@ struct QaStage {
 
 __device__ __forceinline__ void fetch_qa(QaStage& f, const QaSrc& q, int64_t m0, int64_t M, int64_t k0, int64_t K) {
   const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
-  const int64_t gr = m0 + r;
+  int64_t nrows = M - m0;
+  nrows = nrows < 0 ? 0 : (nrows > 256 ? 256 : nrows);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(q.a + m0 * q.lda), 0, (uint32_t)(nrows * q.lda * 2), 0x00020000);
   const int64_t kk = k0 + 64 * h;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
+    // K % 32 == 0: a block is whole or absent; absent blocks and rows past M read zeros
+    const bool live = r < nrows && kk + 32 * b < K;
+    const uint32_t base = live ? (uint32_t)((r * q.lda + kk + 32 * b) * 2) : 0x80000000u;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) f.v[4 * b + u] = make_uint4(0u, 0u, 0u, 0u);
-    if (gr < M && kk + 32 * b < K) {        // K % 32 == 0: a block is whole or absent
-      const uint4* p = reinterpret_cast<const uint4*>(q.a + gr * q.lda + kk + 32 * b);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) f.v[4 * b + u] = p[u];
-    }
+    for (int u = 0; u < 4; ++u)
+      f.v[4 * b + u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, base + 16 * u, 0, 0));
   }
 }
 
@@ -663,9 +683,12 @@ __device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand
   static_assert(QA == 0 || (FA == 0 && BM_ == 256 && THREADS == 512), "two threads per A row of the stage");
   constexpr int PA = 128 * elem_bits<FA>() / 8 + 16, PB = 128 * elem_bits<FB>() / 8 + 16;
   constexpr int FMA = mfma_fmt<FA>(), FMB = mfma_fmt<FB>();
-  __shared__ __attribute__((aligned(16))) uint8_t la[BM_ * PA];
-  __shared__ __attribute__((aligned(16))) uint8_t lb[BN_ * PB];
-  __shared__ uint32_t lsa[BM_], lsb[BN_];
+  // two LDS buffers, so one barrier per stage: stage s + 1 (fetched into
+  // registers during stage s - 1) is written to buffer (s + 1) % 2, the loads
+  // of stage s + 2 are issued, and the MFMAs of stage s read buffer s % 2
+  __shared__ __attribute__((aligned(16))) uint8_t la[2][BM_ * PA];
+  __shared__ __attribute__((aligned(16))) uint8_t lb[2][BN_ * PB];
+  __shared__ uint32_t lsa[2][BM_], lsb[2][BN_];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -681,21 +704,28 @@ __device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand
   MxStage<FA, BM_, THREADS> fa;
   QaStage fq;
   MxStage<FB, BN_, THREADS> fb;
-  if (K > 0) {
-    if constexpr (QA) fetch_qa(fq, qa, m0, M, 0, K);
-    else fetch_mx(fa, A, a_2d != 0, m0, M, 0, K, tid);
-    fetch_mx(fb, B, b_2d != 0, n0, N, 0, K, tid - BM_);
-  }
-  for (int64_t k0 = 0; k0 < K; k0 += 128) {
-    if constexpr (QA) put_qa<QA == 2>(fq, qa, la, PA, lsa);
-    else put_mx(fa, la, PA, lsa, tid);
-    put_mx(fb, lb, PB, lsb, tid - BM_);
+  auto fetch = [&](int64_t k0) {
+    if constexpr (QA) fetch_qa(fq, qa, m0, M, k0, K);
+    else fetch_mx(fa, A, a_2d != 0, m0, M, k0, K, tid);
+    fetch_mx(fb, B, b_2d != 0, n0, N, k0, K, tid - BM_);
+  };
+  auto put = [&](int buf) {
+    if constexpr (QA) put_qa<QA == 2>(fq, qa, la[buf], PA, lsa[buf]);
+    else put_mx(fa, la[buf], PA, lsa[buf], tid);
+    put_mx(fb, lb[buf], PB, lsb[buf], tid - BM_);
+  };
+  const int64_t nst = (K + 127) / 128;
+  if (nst > 0) {
+    fetch(0);
+    put(0);
+    if (nst > 1) fetch(128);
     __syncthreads();
-    if (k0 + 128 < K) {                 // the next stage's loads fly during this stage's MFMAs
-      if constexpr (QA) fetch_qa(fq, qa, m0, M, k0 + 128, K);
-      else fetch_mx(fa, A, a_2d != 0, m0, M, k0 + 128, K, tid);
-      fetch_mx(fb, B, b_2d != 0, n0, N, k0 + 128, K, tid - BM_);
-    }
+  }
+  for (int64_t st = 0; st < nst; ++st) {
+    const int cur = (int)(st & 1);
+    // the other buffer was last read in stage st - 1, before the last barrier
+    if (st + 1 < nst) put(cur ^ 1);
+    if (st + 2 < nst) fetch((st + 2) * 128);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       v8i a[TI], b[TJ];
@@ -703,14 +733,14 @@ __device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const int r = wm * 32 * TI + i * 32 + l32;
-        a[i] = read_mx<FA>(la + r * PA, ks, hi);
-        sa[i] = (int)(lsa[r] >> (8 * hi));
+        a[i] = read_mx<FA>(la[cur] + r * PA, ks, hi);
+        sa[i] = (int)(lsa[cur][r] >> (8 * hi));
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int r = wn * 32 * TJ + j * 32 + l32;
-        b[j] = read_mx<FB>(lb + r * PB, ks, hi);
-        sb[j] = (int)(lsb[r] >> (8 * hi));
+        b[j] = read_mx<FB>(lb[cur] + r * PB, ks, hi);
+        sb[j] = (int)(lsb[cur][r] >> (8 * hi));
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i)
@@ -726,22 +756,28 @@ __device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand
     }
     __syncthreads();
   }
-  // lane holds column l32; register r holds row 8*(r/4) + 4*hi + r%4
+  // lane holds column l32; register r holds row 8*(r/4) + 4*hi + r%4.  Buffer
+  // stores through a resource that ends after the tile's last valid row and
+  // column: lanes past N point past the end, rows past M fall past it.
+  constexpr int ES = 4;
+  const int64_t mrows = (M - m0) < BM_ ? (M - m0) : BM_, ncols = (N - n0) < BN_ ? (N - n0) : BN_;
+  if (mrows <= 0 || ncols <= 0) return;
+  const int es = out_bf16 ? 2 : ES;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<uint8_t*>(C) + (m0 * ldc + n0) * es, 0, (uint32_t)(((mrows - 1) * ldc + ncols) * es), 0x00020000);
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const int64_t col = n0 + wn * 32 * TJ + j * 32 + l32;
-      if (col >= N) continue;
+      const int col = wn * 32 * TJ + j * 32 + l32;
+      const uint32_t voff = col < ncols ? (uint32_t)((4 * hi * ldc + col) * es) : MX_OOB;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 32 * TI + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (row < M) {
-          if (out_bf16)
-            static_cast<uint16_t*>(C)[row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-          else
-            static_cast<float*>(C)[row * ldc + col] = acc[i][j][r];
-        }
+        const uint32_t soff = (uint32_t)((wm * 32 * TI + i * 32 + 8 * (r >> 2) + (r & 3)) * ldc * es);
+        if (out_bf16)
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(acc[i][j][r]), rc, voff, soff, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, voff, soff, 0);
       }
     }
 }

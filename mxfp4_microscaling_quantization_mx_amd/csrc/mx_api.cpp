@@ -66,6 +66,14 @@ mx::MxOperand operand(const mx_tensor* t) {
   return mx::MxOperand{t->codes, t->scales, t->ld_codes, t->ld_scales};
 }
 
+// The C++ kernels for MXFP8 / MXFP6 operands (and the operand-load
+// quantizing GEMM) address one 256-row tile of an operand, of its scales and
+// of C with 32-bit buffer offsets.
+bool tile_offsets_fit(const mx_tensor* t, int64_t ldc_bytes) {
+  const int64_t lim = (int64_t)1 << 31;
+  return (t == nullptr || (256 * t->ld_codes < lim && 256 * t->ld_scales < lim)) && 256 * ldc_bytes < lim;
+}
+
 }  // namespace
 
 extern "C" {
@@ -343,6 +351,9 @@ mx_status gemm_args(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_d
   a.out_bf16 = c_dtype == MX_DT_BF16;
   a.a_elem = A->elem;
   a.b_elem = B->elem;
+  if ((a.a_elem != 0 || a.b_elem != 0) &&
+      !(tile_offsets_fit(A, ldc * (a.out_bf16 ? 2 : 4)) && tile_offsets_fit(B, 0)))
+    return fail(MX_ERR_UNSUPPORTED, "%s: row strides too large for the MXFP8/MXFP6 kernels", what);
   return MX_OK;
 }
 
@@ -420,6 +431,8 @@ mx_status mx_gemm_fused_quant_a(const void* a, int32_t a_dtype, int64_t M, int64
       return fail(MX_ERR_INVALID_ARG, "%s: A must be 16-byte aligned with lda %% 8 == 0", what);
   }
   if ((M + 255) / 256 > 65535) return fail(MX_ERR_UNSUPPORTED, "%s: M too large", what);
+  if (256 * lda * 2 >= ((int64_t)1 << 31) || !tile_offsets_fit(B, ldc * (c_dtype == MX_DT_BF16 ? 2 : 4)))
+    return fail(MX_ERR_UNSUPPORTED, "%s: row strides too large", what);
   mx::GemmQaArgs q{};
   q.a = a;
   q.lda = lda;
@@ -576,6 +589,9 @@ mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, in
   a.out_bf16 = c_dtype == MX_DT_BF16;
   a.a_elem = A->elem;
   a.b_elem = B->elem;
+  if ((a.a_elem != 0 || a.b_elem != 0) &&
+      !(tile_offsets_fit(A, ldc * (a.out_bf16 ? 2 : 4)) && tile_offsets_fit(B, 0)))
+    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm: row strides too large for the MXFP8/MXFP6 kernels");
   return hip_status(mx::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)), "mx_grouped_gemm");
 }
 
