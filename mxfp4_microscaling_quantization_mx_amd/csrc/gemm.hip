@@ -679,7 +679,9 @@ __device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand
                                              int b_2d, int out_bf16, const QaSrc& qa = QaSrc{}) {
   constexpr int WN = BN_ / (32 * TJ);
   constexpr int THREADS = mx_threads<FA, FB, BM_, BN_, TI, TJ>();
-  static_assert(THREADS >= BM_ + BN_, "one scale row per thread");
+  static_assert(THREADS >= BM_ && THREADS >= BN_, "one A and one B scale row per thread");
+  // scale rows: with fewer threads than BM_ + BN_ rows, thread t takes A row t and B row t
+  constexpr int BSTID_OFF = THREADS >= BM_ + BN_ ? BM_ : 0;
   static_assert(QA == 0 || (FA == 0 && BM_ == 256 && THREADS == 512), "two threads per A row of the stage");
   constexpr int PA = 128 * elem_bits<FA>() / 8 + 16, PB = 128 * elem_bits<FB>() / 8 + 16;
   constexpr int FMA = mfma_fmt<FA>(), FMB = mfma_fmt<FB>();
@@ -707,12 +709,12 @@ __device__ __forceinline__ void gemm_mx_tile(const MxOperand& A, const MxOperand
   auto fetch = [&](int64_t k0) {
     if constexpr (QA) fetch_qa(fq, qa, m0, M, k0, K);
     else fetch_mx(fa, A, a_2d != 0, m0, M, k0, K, tid);
-    fetch_mx(fb, B, b_2d != 0, n0, N, k0, K, tid - BM_);
+    fetch_mx(fb, B, b_2d != 0, n0, N, k0, K, tid - BSTID_OFF);
   };
   auto put = [&](int buf) {
     if constexpr (QA) put_qa<QA == 2>(fq, qa, la[buf], PA, lsa[buf]);
     else put_mx(fa, la[buf], PA, lsa[buf], tid);
-    put_mx(fb, lb[buf], PB, lsb[buf], tid - BM_);
+    put_mx(fb, lb[buf], PB, lsb[buf], tid - BSTID_OFF);
   };
   const int64_t nst = (K + 127) / 128;
   if (nst > 0) {
