@@ -198,6 +198,30 @@ def test_gemm_elements(fa, fb, M, N, K, b_block, out):
     assert np.all(err <= tol), float(np.max(err / tol))
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m3", "e3m2")])
+@pytest.mark.parametrize("M,N", [(200, 136), (300, 544)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_elements_guard(fa, fb, M, N, out):
+    """C inside a larger buffer filled with a marker, rows and columns ragged
+    against both tile sizes: the kernel's bounds-checked buffer stores write
+    C and nothing else."""
+    need_gpu()
+    K = 224
+    rng = np.random.default_rng(zlib.crc32(f"guard{fa}{fb}{M}{N}".encode()))
+    qa, ac, as_ = _operand(rng, M, K, fa)
+    qb, bc, bs = _operand(rng, N, K, fb)
+    buf = torch.full((M + 37, N + 21), 7.0, dtype=out, device="cuda")
+    banner(f"gemm guard {fa} x {fb} M={M} N={N} {out}")
+    mx.gemm(qa, qb, out=buf[:M, :N])
+    got = host(buf.float()).astype(np.float64)
+    assert np.all(got[M:] == 7.0) and np.all(got[:, N:] == 7.0), "wrote outside C"
+    ref, bound = oracle.gemm_ref(ac, as_, bc, bs, a_elem=fa, b_elem=fb)
+    tol = 1e-5 * bound + mx_group_bound(oracle.gemm.dequant_f64(ac, as_, fa), oracle.gemm.dequant_f64(bc, bs, fb))
+    if out == torch.bfloat16:
+        tol = tol + bf16_half_ulp(np.maximum(np.abs(got[:M, :N]), np.abs(ref)))
+    assert np.all(np.abs(got[:M, :N] - ref) <= tol)
+
+
 def test_gemm_mxfp8_end_to_end():
     """MXFP8 (E4M3) activations times MXFP8 weights quantized on the GPU (the
     weights along dim 0), 2048 x 1024 x 2880, against the oracle on sampled
