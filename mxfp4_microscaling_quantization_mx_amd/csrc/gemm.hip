@@ -874,10 +874,228 @@ hipError_t launch_grouped_gemm_mx_b(const GroupedGemmArgs& a, hipStream_t st) {
   }
 }
 
+// ------------------------------------------- MXFP8 x MXFP8, loads straight to LDS
+// 256x256 tiles of 8 waves (4 along M x 2 along N, 64x128 each as 2 x 4
+// MFMA tiles) over 128-deep stages: a stage row is 128 code bytes (one cache
+// line) and 4 scale bytes.  Each stage goes global -> LDS with direct-to-LDS
+// buffer loads into one of two slots while the stage in the other slot is
+// multiplied, so the codes never pass through VGPRs: per wave and stage, 8
+// loads of 1 KiB (4 of A, 4 of B: 8 whole rows each) and one 4-byte scale
+// load (A rows for waves 0-3, B rows for 4-7).  The 16-byte chunks of an LDS
+// row are XOR-swizzled (chunk c of row r sits at c ^ ((r >> 1) & 7)) so that
+// the operand reads of 16 consecutive rows fall in different banks.  The two
+// slots are separate LDS arrays and the stage loop is unrolled by two, so
+// the loads in flight into one slot are visibly disjoint from the reads of
+// the other and the only wait for them is the one before each barrier.
+namespace f8 {
+constexpr int ROWB = 128;                  // code bytes per row and stage
+constexpr int OPB = 256 * ROWB;            // one operand's stage (32 KiB)
+constexpr int SLOT = 2 * OPB;              // A then B
+constexpr int SWORDS = 512;                // scale words of a stage: A rows, then B rows
+typedef __attribute__((address_space(3))) void* lds_t;
+typedef int v4i __attribute__((ext_vector_type(4)));
+}
+
+struct F8Lane {
+  __amdgpu_buffer_rsrc_t ra, rb, rs;
+  uint32_t va[4], vb[4];                   // code offsets of this lane's 8 loads (stage 0)
+  int c[4];                                // their K chunk (16-byte unit of the stage row)
+  uint32_t so;                             // scale offset of this lane's row (stage 0)
+};
+
+// Issue the loads of stage s into the slot (codes) and sl (scale words).
+// Load t of the wave covers rows 8 (4 wave + t) + lane / 8 and puts this
+// lane's 16 bytes at LDS chunk lane % 8 of its row, which holds the row's
+// K chunk c = (lane % 8) ^ ((row / 2) % 8).
+__device__ __forceinline__ void f8_issue(const F8Lane& L, int s, int K, uint8_t* slot, uint32_t* sl, int wave) {
+  const uint32_t kb = (uint32_t)(128 * s);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bool kin = (int)kb + 16 * L.c[t] < K;             // chunks past K read zeros
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.ra, (f8::lds_t)(slot + 1024 * (4 * wave + t)), 16,
+                                             kin ? L.va[t] : MX_OOB, kb, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rb, (f8::lds_t)(slot + f8::OPB + 1024 * (4 * wave + t)), 16,
+                                             kin ? L.vb[t] : MX_OOB, kb, 0, 0);
+  }
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rs, (f8::lds_t)(sl + 64 * wave), 4, L.so, (uint32_t)(4 * s), 0, 0);
+}
+
+// Multiply the stage held in (slot, sl): 2 steps of 8 MFMAs per wave.
+// (slot, sl: LDS byte addresses of the stage's codes and scale words)
+template <int FA, int FB>
+__device__ __forceinline__ void f8_compute(v16f acc[2][4], uint32_t slot, uint32_t sl, int s, int K, int wm, int wn,
+                                           int l32, int hi) {
+  // blocks of this stage below K; the scale bytes of the others (row padding)
+  // are cleared to 0, a finite scale, since their codes are zero
+  const int nk = (K >> 5) - 4 * s;
+  const uint32_t keep = nk >= 4 ? 0xFFFFFFFFu : (1u << (8 * nk)) - 1u;
+  // the scale words through an asm read (waiting for itself only: the
+  // compiler would wait for the loads in flight into the other slot)
+  const uint32_t wa = sl + 4 * (wm * 64 + l32);
+  const uint32_t wb = sl + 4 * (256 + wn * 128 + l32);
+  uint32_t q[6];
+  asm volatile(
+      "ds_read_b32 %0, %6\n\t"
+      "ds_read_b32 %1, %6 offset:128\n\t"
+      "ds_read_b32 %2, %7\n\t"
+      "ds_read_b32 %3, %7 offset:128\n\t"
+      "ds_read_b32 %4, %7 offset:256\n\t"
+      "ds_read_b32 %5, %7 offset:384\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5])
+      : "v"(wa), "v"(wb)
+      : "memory");
+  int sa[2], sb[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) sa[i] = (int)((q[i] & keep) >> (8 * hi));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sb[j] = (int)((q[2 + j] & keep) >> (8 * hi));
+  const int key = (l32 >> 1) & 7;
+  const uint32_t ra = slot + (wm * 64 + l32) * f8::ROWB;
+  const uint32_t rb = slot + f8::OPB + (wn * 128 + l32) * f8::ROWB;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    // this lane's 32 code bytes of the step: chunks 4 ks + hi and 4 ks + 2 + hi,
+    // read in one asm block that waits for itself only
+    const uint32_t p0 = 16 * ((4 * ks + hi) ^ key), p1 = 16 * ((4 * ks + 2 + hi) ^ key);
+    f8::v4i x[6], y[6];
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %6, %13\n\t"
+        "ds_read_b128 %1, %12 offset:4096\n\t"
+        "ds_read_b128 %7, %13 offset:4096\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %8, %15\n\t"
+        "ds_read_b128 %3, %14 offset:4096\n\t"
+        "ds_read_b128 %9, %15 offset:4096\n\t"
+        "ds_read_b128 %4, %14 offset:8192\n\t"
+        "ds_read_b128 %10, %15 offset:8192\n\t"
+        "ds_read_b128 %5, %14 offset:12288\n\t"
+        "ds_read_b128 %11, %15 offset:12288\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(y[0]), "=&v"(y[1]),
+          "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5])
+        : "v"(ra + p0), "v"(ra + p1), "v"(rb + p0), "v"(rb + p1)
+        : "memory");
+    v8i a[2], b[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = __builtin_shufflevector(x[i], y[i], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = __builtin_shufflevector(x[2 + j], y[2 + j], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (ks == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA == 1 ? 0 : 1,
+                                                                       FB == 1 ? 0 : 1, 0, sa[i], 0, sb[j]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA == 1 ? 0 : 1,
+                                                                       FB == 1 ? 0 : 1, 2, sa[i], 2, sb[j]);
+      }
+  }
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(512) void k_gemm_f8(MxOperand A, MxOperand B, int M, int N, int K, void* C, int64_t ldc,
+                                                int a_2d, int b_2d, int out_bf16) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[f8::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[f8::SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t sw0[f8::SWORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t sw1[f8::SWORDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int m0 = (int)blockIdx.y * 256, n0 = (int)blockIdx.x * 256;
+  const int arows = M - m0 < 256 ? M - m0 : 256, brows = N - n0 < 256 ? N - n0 : 256;
+  F8Lane L;
+  L.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.codes) + (int64_t)m0 * A.ld_codes, 0,
+                                           (uint32_t)(arows * A.ld_codes), 0x00020000);
+  L.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B.codes) + (int64_t)n0 * B.ld_codes, 0,
+                                           (uint32_t)(brows * B.ld_codes), 0x00020000);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = 8 * (4 * wave + t) + (lane >> 3);
+    L.c[t] = (lane & 7) ^ ((row >> 1) & 7);                 // the K chunk this lane's LDS chunk holds
+    L.va[t] = row < arows ? (uint32_t)(row * A.ld_codes + 16 * L.c[t]) : MX_OOB;
+    L.vb[t] = row < brows ? (uint32_t)(row * B.ld_codes + 16 * L.c[t]) : MX_OOB;
+  }
+  {
+    const bool isA = wave < 4;
+    const int r = 64 * (wave & 3) + lane;                   // this lane's scale row within the tile
+    const bool two_d = isA ? a_2d != 0 : b_2d != 0;
+    const int r0 = isA ? m0 : n0, rows = isA ? arows : brows;
+    const int64_t lds_s = isA ? A.ld_scales : B.ld_scales;
+    const uint8_t* sbase = (isA ? A.scales : B.scales) + (int64_t)(two_d ? (r0 >> 5) : r0) * lds_s;
+    L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase), 0, (uint32_t)((two_d ? 8 : 256) * lds_s),
+                                             0x00020000);
+    L.so = r < rows ? (uint32_t)((two_d ? (r >> 5) : r) * lds_s) : MX_OOB;
+  }
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const int nst = (K + 127) / 128;
+  const uint32_t a_slot0 = (uint32_t)(uintptr_t)(f8::lds_t)slot0, a_slot1 = (uint32_t)(uintptr_t)(f8::lds_t)slot1;
+  const uint32_t a_sw0 = (uint32_t)(uintptr_t)(f8::lds_t)sw0, a_sw1 = (uint32_t)(uintptr_t)(f8::lds_t)sw1;
+  if (nst > 0) f8_issue(L, 0, K, slot0, sw0, wave);
+  for (int s = 0; s < nst; s += 2) {
+    // stage s in slot 0; stage s + 1 loads into slot 1
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's loads of stage s landed
+    __syncthreads();                         // ... every wave's; every wave is done with slot 1
+    if (s + 1 < nst) f8_issue(L, s + 1, K, slot1, sw1, wave);
+    f8_compute<FA, FB>(acc, a_slot0, a_sw0, s, K, wm, wn, l32, hi);
+    if (s + 1 >= nst) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (s + 2 < nst) f8_issue(L, s + 2, K, slot0, sw0, wave);
+    f8_compute<FA, FB>(acc, a_slot1, a_sw1, s + 1, K, wm, wn, l32, hi);
+  }
+  // epilogue: bounds-checked buffer stores (lane = column, register r = row
+  // 8 (r / 4) + 4 hi + r % 4 of the MFMA tile)
+  const int es = out_bf16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<uint8_t*>(C) + ((int64_t)m0 * ldc + n0) * es, 0,
+      (uint32_t)(((int64_t)(arows - 1) * ldc + brows) * es), 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = wn * 128 + j * 32 + l32;
+      const uint32_t voff = col < brows ? (uint32_t)((4 * hi * ldc + col) * es) : MX_OOB;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t soff = (uint32_t)((wm * 64 + i * 32 + 8 * (r >> 2) + (r & 3)) * ldc * es);
+        if (out_bf16)
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(acc[i][j][r]), rc, voff, soff, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, voff, soff, 0);
+      }
+    }
+}
+
 // 256x256 tiles (8 waves of 64x128) when both dimensions fill them, else
 // 128x128 (4 waves of 64x64).
 template <int FA, int FB>
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
+  if constexpr ((FA == 1 || FA == 2) && (FB == 1 || FB == 2)) {
+    // MXFP8 x MXFP8 with whole 256x256 tiles available, 4-byte aligned scale
+    // rows and 32-bit tile offsets: the direct-to-LDS kernel
+    const bool words = a.A.ld_scales % 4 == 0 && a.B.ld_scales % 4 == 0 && (uintptr_t)a.A.scales % 4 == 0 &&
+                       (uintptr_t)a.B.scales % 4 == 0;
+    const bool small = 256 * a.A.ld_codes < (1ll << 31) && 256 * a.B.ld_codes < (1ll << 31) &&
+                       256 * a.ldc * 4 < (1ll << 31) && a.M < (1ll << 31) && a.N < (1ll << 31) && a.K < (1ll << 30);
+    if (a.M >= 256 && a.N >= 256 && words && small) {
+      const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)((a.M + 255) / 256));
+      hipLaunchKernelGGL((k_gemm_f8<FA, FB>), grid, dim3(512), 0, st, a.A, a.B, (int)a.M, (int)a.N, (int)a.K, a.C,
+                         a.ldc, (int)a.a_2d, (int)a.b_2d, (int)a.out_bf16);
+      return hipGetLastError();
+    }
+  }
   if (a.M >= 256 && a.N >= 256) {
     const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)((a.M + 255) / 256));
     hipLaunchKernelGGL((k_gemm_mx<FA, FB, 256, 256, 2, 4>), grid, dim3(512), 0, st, a.A, a.B, a.M, a.N, a.K, a.C,
