@@ -874,26 +874,34 @@ hipError_t launch_grouped_gemm_mx_b(const GroupedGemmArgs& a, hipStream_t st) {
   }
 }
 
-// ------------------------------------------- MXFP8 x MXFP8, loads straight to LDS
+// ------------------------------------ MXFP8 / MXFP6 operands, loads straight to LDS
 // 256x256 tiles of 8 waves (4 along M x 2 along N, 64x128 each as 2 x 4
-// MFMA tiles) over 128-deep stages: a stage row is 128 code bytes (one cache
-// line) and 4 scale bytes.  Each stage goes global -> LDS with direct-to-LDS
-// buffer loads into one of two slots while the stage in the other slot is
-// multiplied, so the codes never pass through VGPRs: per wave and stage, 8
-// loads of 1 KiB (4 of A, 4 of B: 8 whole rows each) and one 4-byte scale
-// load (A rows for waves 0-3, B rows for 4-7).  The 16-byte chunks of an LDS
-// row are XOR-swizzled (chunk c of row r sits at c ^ ((r >> 1) & 7)) so that
-// the operand reads of 16 consecutive rows fall in different banks.  The two
-// slots are separate LDS arrays and the stage loop is unrolled by two, so
-// the loads in flight into one slot are visibly disjoint from the reads of
-// the other and the only wait for them is the one before each barrier.
+// MFMA tiles) over 128-deep stages: 4 blocks, 128 code bytes per row for an
+// FP8 operand (one cache line) and 96 for FP6, and 4 scale bytes.  Each stage
+// goes global -> LDS with direct-to-LDS buffer loads into one of two slots
+// while the stage in the other slot is multiplied, so the codes never pass
+// through VGPRs: per wave and stage, 8 loads of 1 KiB (4 of A, 4 of B: 8
+// rows each, a 16-byte chunk per lane; an FP6 row's chunks 6 and 7 read as
+// zeros) and one 4-byte scale load (A rows for waves 0-3, B rows for 4-7).
+// LDS rows are 128 bytes with XOR-swizzled 16-byte chunks (chunk c of row r
+// sits at c ^ ((r >> 1) & 7)), so the operand reads of consecutive rows fall
+// in different banks.  The two slots are separate LDS arrays and the stage
+// loop is unrolled by two, and the LDS reads are asm blocks that wait only
+// for themselves: the compiler would otherwise wait for the loads in flight
+// into the other slot before every read.  FP8 lanes read 2 x 16 bytes per
+// 64-deep step (K-elements [16 g, 16 g + 16) and [32 + 16 g, 48 + 16 g) of
+// the step, g = lane / 32), FP6 lanes 3 x 8 bytes (their whole 24-byte
+// block).
 namespace f8 {
-constexpr int ROWB = 128;                  // code bytes per row and stage
+constexpr int ROWB = 128;                  // LDS bytes per row and stage
 constexpr int OPB = 256 * ROWB;            // one operand's stage (32 KiB)
 constexpr int SLOT = 2 * OPB;              // A then B
 constexpr int SWORDS = 512;                // scale words of a stage: A rows, then B rows
 typedef __attribute__((address_space(3))) void* lds_t;
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+template <int F>
+constexpr int gbytes() { return elem_bits<F>() == 8 ? 128 : 96; }   // global code bytes of a stage row
 }
 
 struct F8Lane {
@@ -906,31 +914,122 @@ struct F8Lane {
 // Issue the loads of stage s into the slot (codes) and sl (scale words).
 // Load t of the wave covers rows 8 (4 wave + t) + lane / 8 and puts this
 // lane's 16 bytes at LDS chunk lane % 8 of its row, which holds the row's
-// K chunk c = (lane % 8) ^ ((row / 2) % 8).
+// K chunk c = (lane % 8) ^ ((row / 2) % 8).  Chunks past the stage row (FP6:
+// 6 and 7) or past K read zeros; an FP6 chunk that K ends half-way through
+// brings 8 bytes of the next block, whose scale byte compute() clears.
+template <int FA, int FB>
 __device__ __forceinline__ void f8_issue(const F8Lane& L, int s, int K, uint8_t* slot, uint32_t* sl, int wave) {
-  const uint32_t kb = (uint32_t)(128 * s);
+  constexpr int RA = f8::gbytes<FA>(), RB = f8::gbytes<FB>();
+  const int ka = RA * s, kbb = RB * s;
+  const int kbytes_a = K * elem_bits<FA>() / 8, kbytes_b = K * elem_bits<FB>() / 8;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const bool kin = (int)kb + 16 * L.c[t] < K;             // chunks past K read zeros
+    const int c16 = 16 * L.c[t];
+    const bool ina = c16 < RA && ka + c16 < kbytes_a, inb = c16 < RB && kbb + c16 < kbytes_b;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.ra, (f8::lds_t)(slot + 1024 * (4 * wave + t)), 16,
-                                             kin ? L.va[t] : MX_OOB, kb, 0, 0);
+                                             ina ? L.va[t] : MX_OOB, (uint32_t)ka, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rb, (f8::lds_t)(slot + f8::OPB + 1024 * (4 * wave + t)), 16,
-                                             kin ? L.vb[t] : MX_OOB, kb, 0, 0);
+                                             inb ? L.vb[t] : MX_OOB, (uint32_t)kbb, 0, 0);
   }
   __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rs, (f8::lds_t)(sl + 64 * wave), 4, L.so, (uint32_t)(4 * s), 0, 0);
 }
 
-// Multiply the stage held in (slot, sl): 2 steps of 8 MFMAs per wave.
-// (slot, sl: LDS byte addresses of the stage's codes and scale words)
+// This lane's operands of 64-deep step ks for NT row tiles (4096 LDS bytes
+// apart) starting at LDS row address `row` (key = the row's chunk swizzle),
+// in one asm block that waits for itself only.
+template <int F, int NT>
+__device__ __forceinline__ void f8_read(uint32_t row, int key, int ks, int hi, v8i out[NT]) {
+  if constexpr (elem_bits<F>() == 8) {
+    const uint32_t q0 = row + 16 * ((4 * ks + hi) ^ key), q1 = row + 16 * ((4 * ks + 2 + hi) ^ key);
+    f8::v4i x[NT], y[NT];
+    if constexpr (NT == 2) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %2, %5\n\t"
+          "ds_read_b128 %1, %4 offset:4096\n\t"
+          "ds_read_b128 %3, %5 offset:4096\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(y[0]), "=&v"(y[1])
+          : "v"(q0), "v"(q1)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %4, %9\n\t"
+          "ds_read_b128 %1, %8 offset:4096\n\t"
+          "ds_read_b128 %5, %9 offset:4096\n\t"
+          "ds_read_b128 %2, %8 offset:8192\n\t"
+          "ds_read_b128 %6, %9 offset:8192\n\t"
+          "ds_read_b128 %3, %8 offset:12288\n\t"
+          "ds_read_b128 %7, %9 offset:12288\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])
+          : "v"(q0), "v"(q1)
+          : "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) out[i] = __builtin_shufflevector(x[i], y[i], 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    // the lane's block: bytes 48 ks + 24 hi + [0, 24) of the stage row, as
+    // three 8-byte reads (each inside one 16-byte chunk)
+    const int o = 48 * ks + 24 * hi;
+    const uint32_t q0 = row + 16 * ((o >> 4) ^ key) + (o & 15);
+    const uint32_t q1 = row + 16 * (((o + 8) >> 4) ^ key) + ((o + 8) & 15);
+    const uint32_t q2 = row + 16 * (((o + 16) >> 4) ^ key) + ((o + 16) & 15);
+    f8::v2i x[NT], y[NT], z[NT];
+    if constexpr (NT == 2) {
+      asm volatile(
+          "ds_read_b64 %0, %6\n\t"
+          "ds_read_b64 %2, %7\n\t"
+          "ds_read_b64 %4, %8\n\t"
+          "ds_read_b64 %1, %6 offset:4096\n\t"
+          "ds_read_b64 %3, %7 offset:4096\n\t"
+          "ds_read_b64 %5, %8 offset:4096\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(y[0]), "=&v"(y[1]), "=&v"(z[0]), "=&v"(z[1])
+          : "v"(q0), "v"(q1), "v"(q2)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64 %0, %12\n\t"
+          "ds_read_b64 %4, %13\n\t"
+          "ds_read_b64 %8, %14\n\t"
+          "ds_read_b64 %1, %12 offset:4096\n\t"
+          "ds_read_b64 %5, %13 offset:4096\n\t"
+          "ds_read_b64 %9, %14 offset:4096\n\t"
+          "ds_read_b64 %2, %12 offset:8192\n\t"
+          "ds_read_b64 %6, %13 offset:8192\n\t"
+          "ds_read_b64 %10, %14 offset:8192\n\t"
+          "ds_read_b64 %3, %12 offset:12288\n\t"
+          "ds_read_b64 %7, %13 offset:12288\n\t"
+          "ds_read_b64 %11, %14 offset:12288\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]),
+            "=&v"(z[0]), "=&v"(z[1]), "=&v"(z[2]), "=&v"(z[3])
+          : "v"(q0), "v"(q1), "v"(q2)
+          : "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const f8::v4i xy = __builtin_shufflevector(x[i], y[i], 0, 1, 2, 3);
+      const f8::v4i zz = {z[i][0], z[i][1], 0, 0};   // an FP6 operand is 6 dwords; the rest zero
+      out[i] = __builtin_shufflevector(xy, zz, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+}
+
+// Multiply the stage held in (slot, sl: LDS byte addresses of its codes and
+// scale words): 2 steps of 8 MFMAs per wave.
 template <int FA, int FB>
 __device__ __forceinline__ void f8_compute(v16f acc[2][4], uint32_t slot, uint32_t sl, int s, int K, int wm, int wn,
                                            int l32, int hi) {
   // blocks of this stage below K; the scale bytes of the others (row padding)
-  // are cleared to 0, a finite scale, since their codes are zero
+  // are cleared to 0, a finite scale: their codes are zero, or for an FP6 row
+  // that K ends inside a chunk, 8 bytes whose products with a scale of 2^-127
+  // on both sides vanish in float32
   const int nk = (K >> 5) - 4 * s;
   const uint32_t keep = nk >= 4 ? 0xFFFFFFFFu : (1u << (8 * nk)) - 1u;
-  // the scale words through an asm read (waiting for itself only: the
-  // compiler would wait for the loads in flight into the other slot)
+  // the scale words through an asm read (waiting for itself only)
   const uint32_t wa = sl + 4 * (wm * 64 + l32);
   const uint32_t wb = sl + 4 * (256 + wn * 128 + l32);
   uint32_t q[6];
@@ -955,43 +1054,19 @@ __device__ __forceinline__ void f8_compute(v16f acc[2][4], uint32_t slot, uint32
   const uint32_t rb = slot + f8::OPB + (wn * 128 + l32) * f8::ROWB;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    // this lane's 32 code bytes of the step: chunks 4 ks + hi and 4 ks + 2 + hi,
-    // read in one asm block that waits for itself only
-    const uint32_t p0 = 16 * ((4 * ks + hi) ^ key), p1 = 16 * ((4 * ks + 2 + hi) ^ key);
-    f8::v4i x[6], y[6];
-    asm volatile(
-        "ds_read_b128 %0, %12\n\t"
-        "ds_read_b128 %6, %13\n\t"
-        "ds_read_b128 %1, %12 offset:4096\n\t"
-        "ds_read_b128 %7, %13 offset:4096\n\t"
-        "ds_read_b128 %2, %14\n\t"
-        "ds_read_b128 %8, %15\n\t"
-        "ds_read_b128 %3, %14 offset:4096\n\t"
-        "ds_read_b128 %9, %15 offset:4096\n\t"
-        "ds_read_b128 %4, %14 offset:8192\n\t"
-        "ds_read_b128 %10, %15 offset:8192\n\t"
-        "ds_read_b128 %5, %14 offset:12288\n\t"
-        "ds_read_b128 %11, %15 offset:12288\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(y[0]), "=&v"(y[1]),
-          "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5])
-        : "v"(ra + p0), "v"(ra + p1), "v"(rb + p0), "v"(rb + p1)
-        : "memory");
     v8i a[2], b[4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = __builtin_shufflevector(x[i], y[i], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = __builtin_shufflevector(x[2 + j], y[2 + j], 0, 1, 2, 3, 4, 5, 6, 7);
+    f8_read<FA, 2>(ra, key, ks, hi, a);
+    f8_read<FB, 4>(rb, key, ks, hi, b);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (ks == 0)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA == 1 ? 0 : 1,
-                                                                       FB == 1 ? 0 : 1, 0, sa[i], 0, sb[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], mfma_fmt<FA>(),
+                                                                       mfma_fmt<FB>(), 0, sa[i], 0, sb[j]);
         else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], FA == 1 ? 0 : 1,
-                                                                       FB == 1 ? 0 : 1, 2, sa[i], 2, sb[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], mfma_fmt<FA>(),
+                                                                       mfma_fmt<FB>(), 2, sa[i], 2, sb[j]);
       }
   }
 }
@@ -1042,17 +1117,17 @@ __global__ __launch_bounds__(512) void k_gemm_f8(MxOperand A, MxOperand B, int M
   const int nst = (K + 127) / 128;
   const uint32_t a_slot0 = (uint32_t)(uintptr_t)(f8::lds_t)slot0, a_slot1 = (uint32_t)(uintptr_t)(f8::lds_t)slot1;
   const uint32_t a_sw0 = (uint32_t)(uintptr_t)(f8::lds_t)sw0, a_sw1 = (uint32_t)(uintptr_t)(f8::lds_t)sw1;
-  if (nst > 0) f8_issue(L, 0, K, slot0, sw0, wave);
+  if (nst > 0) f8_issue<FA, FB>(L, 0, K, slot0, sw0, wave);
   for (int s = 0; s < nst; s += 2) {
     // stage s in slot 0; stage s + 1 loads into slot 1
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's loads of stage s landed
     __syncthreads();                         // ... every wave's; every wave is done with slot 1
-    if (s + 1 < nst) f8_issue(L, s + 1, K, slot1, sw1, wave);
+    if (s + 1 < nst) f8_issue<FA, FB>(L, s + 1, K, slot1, sw1, wave);
     f8_compute<FA, FB>(acc, a_slot0, a_sw0, s, K, wm, wn, l32, hi);
     if (s + 1 >= nst) break;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (s + 2 < nst) f8_issue(L, s + 2, K, slot0, sw0, wave);
+    if (s + 2 < nst) f8_issue<FA, FB>(L, s + 2, K, slot0, sw0, wave);
     f8_compute<FA, FB>(acc, a_slot1, a_sw1, s + 1, K, wm, wn, l32, hi);
   }
   // epilogue: bounds-checked buffer stores (lane = column, register r = row
@@ -1082,9 +1157,9 @@ __global__ __launch_bounds__(512) void k_gemm_f8(MxOperand A, MxOperand B, int M
 // 128x128 (4 waves of 64x64).
 template <int FA, int FB>
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
-  if constexpr ((FA == 1 || FA == 2) && (FB == 1 || FB == 2)) {
-    // MXFP8 x MXFP8 with whole 256x256 tiles available, 4-byte aligned scale
-    // rows and 32-bit tile offsets: the direct-to-LDS kernel
+  if constexpr (FA >= 1 && FA <= 4 && FB >= 1 && FB <= 4) {
+    // MXFP8 / MXFP6 operands with whole 256x256 tiles available, 4-byte
+    // aligned scale rows and 32-bit tile offsets: the direct-to-LDS kernel
     const bool words = a.A.ld_scales % 4 == 0 && a.B.ld_scales % 4 == 0 && (uintptr_t)a.A.scales % 4 == 0 &&
                        (uintptr_t)a.B.scales % 4 == 0;
     const bool small = 256 * a.A.ld_codes < (1ll << 31) && 256 * a.B.ld_codes < (1ll << 31) &&

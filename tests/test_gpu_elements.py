@@ -177,7 +177,8 @@ GEMM_CASES = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e2m3", "e2m3"), ("e3m2", "e3
 @pytest.mark.parametrize("fa,fb", GEMM_CASES)
 @pytest.mark.parametrize("M,N,K,b_block,out", [(200, 136, 416, "1d", torch.float32),
                                                (96, 160, 96, "2d", torch.bfloat16),
-                                               (300, 544, 224, "2d", torch.bfloat16)])
+                                               (300, 544, 224, "2d", torch.bfloat16),
+                                               (520, 288, 800, "1d", torch.float32)])
 def test_gemm_elements(fa, fb, M, N, K, b_block, out):
     """Mixed and uniform element types on ragged shapes (rows, columns and K
     not multiples of the tile: the 128x128 kernel below 256 rows or columns,
@@ -222,8 +223,9 @@ def test_gemm_elements_guard(fa, fb, M, N, out):
     assert np.all(np.abs(got[:M, :N] - ref) <= tol)
 
 
-def test_gemm_mxfp8_end_to_end():
-    """MXFP8 (E4M3) activations times MXFP8 weights quantized on the GPU (the
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m3", "e2m3"), ("e5m2", "e3m2")])
+def test_gemm_mxfp8_end_to_end(fa, fb):
+    """MXFP8 / MXFP6 activations times weights quantized on the GPU (the
     weights along dim 0), 2048 x 1024 x 2880, against the oracle on sampled
     rows and columns."""
     need_gpu()
@@ -231,17 +233,17 @@ def test_gemm_mxfp8_end_to_end():
     x = rng.standard_normal((2048, 2880)).astype(np.float32)
     w = (rng.standard_normal((2880, 1024)) * 0.02).astype(np.float32)
     xt, wt = torch.from_numpy(x).to(torch.bfloat16), torch.from_numpy(w).to(torch.bfloat16)
-    banner("gemm mxfp8 end to end")
-    qx = mx.quantize(xt.cuda(), elem="e4m3")
-    qw = mx.quantize(wt.cuda(), axis="dim0", elem="e4m3")
+    banner(f"gemm {fa} x {fb} end to end")
+    qx = mx.quantize(xt.cuda(), elem=fa)
+    qw = mx.quantize(wt.cuda(), axis="dim0", elem=fb)
     y = host(mx.gemm(qx, qw, torch.float32)).astype(np.float64)
     rows = np.sort(rng.choice(2048, 32, replace=False))
     cols = np.sort(rng.choice(1024, 32, replace=False))
-    xc, xs = oracle.quantize(xt.float().numpy()[rows], elem="e4m3")
-    wc, ws = oracle.quantize(wt.float().numpy()[:, cols], axis="dim0", elem="e4m3")
-    ref, bound = oracle.gemm_ref(xc, xs, wc, ws, a_elem="e4m3", b_elem="e4m3")
-    tol = 1e-5 * bound + mx_group_bound(oracle.gemm.dequant_f64(xc, xs, "e4m3"),
-                                        oracle.gemm.dequant_f64(wc, ws, "e4m3"))
+    xc, xs = oracle.quantize(xt.float().numpy()[rows], elem=fa)
+    wc, ws = oracle.quantize(wt.float().numpy()[:, cols], axis="dim0", elem=fb)
+    ref, bound = oracle.gemm_ref(xc, xs, wc, ws, a_elem=fa, b_elem=fb)
+    tol = 1e-5 * bound + mx_group_bound(oracle.gemm.dequant_f64(xc, xs, fa),
+                                        oracle.gemm.dequant_f64(wc, ws, fb))
     assert np.all(np.abs(y[np.ix_(rows, cols)] - ref) <= tol)
 
 
