@@ -34,6 +34,7 @@ from .philox import philox4x32_10, sr_bits8, sr_bits16
 from .rht import rht_forward_f32, rht_inverse_f32, hadamard32_f64
 from .quantize import (
     quantize,
+    clip_count,
     quantize_gather,
     quantize_scatter,
     transpose_2d,
@@ -59,6 +60,7 @@ __all__ = [
     "rht_inverse_f32",
     "hadamard32_f64",
     "quantize",
+    "clip_count",
     "quantize_gather",
     "quantize_scatter",
     "transpose_2d",

@@ -128,7 +128,8 @@ def unpack_nibbles(packed):
 
 
 def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
-             seed=0, offset=0, row_index=None, K_total=None, scale_mode="floor", elem="e2m1"):
+             seed=0, offset=0, row_index=None, K_total=None, scale_mode="floor", elem="e2m1",
+             stats=None):
     """Quantize a 2-D float array to MXFP4.
 
     axis="last": blocks along the last dim, output [R, C] with K = C.
@@ -147,6 +148,11 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
     ``oracle.elements`` ("e4m3", "e5m2": one byte per element; "e2m3",
     "e3m2": 6-bit codes packed little-endian); the scale takes that type's
     largest power of two and the elements its grid (§Conversion rules).
+    stats: a dict that, when given, receives stats["clipped"], the number of
+    elements of finite blocks whose scaled value (step 5) lies above the
+    element type's largest normal, i.e. that saturate in step 6 (§Clipping in
+    the reference algorithm: with the reference rule, values scaling into
+    (6, 8) clip to 6).
     """
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
@@ -210,9 +216,24 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None,
             r = bits(p, seed, offset).reshape(rows, nkb, BLOCK)
         codes = round_e2m1(v, rounding, r) if elem == "e2m1" else elements.round_elem(v, elem, rounding, r)
         codes = np.where(bad_el[..., None], 0, codes)
+        if stats is not None:
+            top = np.float32(6.0) if elem == "e2m1" else np.float32(elements.max_normal(elem))
+            stats["clipped"] = int(np.count_nonzero((np.abs(v) > top) & ~bad_el[..., None]))
     if elem != "e2m1":
         return elements.pack(codes.reshape(rows, K), elem), scales
     return pack_nibbles(codes.reshape(rows, K)), scales
+
+
+def clip_count(x, axis="last", block="1d", rht_mask=None, scale_mode="floor", elem="e2m1"):
+    """Clipping statistic of one quantization (§Clipping in the reference
+    algorithm): how many elements of x saturate at the element type's largest
+    normal when x is quantized with these settings (the rounding mode does
+    not matter: every mode saturates the same values).  Blocks holding NaN or
+    Inf count nothing (their codes are all zero).  With the round-up rule or
+    the 3/4 prescale the count is 0 by construction."""
+    st = {}
+    quantize(x, axis=axis, block=block, rht_mask=rht_mask, scale_mode=scale_mode, elem=elem, stats=st)
+    return st["clipped"]
 
 
 def quantize_gather(x, rows, rounding="rne", rht_mask=None, seed=0, offset=0,
