@@ -133,6 +133,7 @@ class Workload:
         self.e6_qx = mx.empty_mx(16384, 2880, device=dev, elem="e2m3")
         self.e6_qw = mx.empty_mx(5760, 2880, device=dev, elem="e2m3")
         self.e_y = torch.empty((16384, 5760), dtype=torch.bfloat16, device=dev)
+        self.clip_n = torch.zeros(1, dtype=torch.int64, device=dev)    # clipping statistic (accumulates)
         mx.quantize(self.fw, axis="dim0", out=self.e6_qw)
         # the fprop product quantized in the GEMM epilogue (MXFP4 [16384, 5760]),
         # and the unfused equivalent's second kernel: quantize of the bf16 output
@@ -183,7 +184,8 @@ class Workload:
         unfused_quantize_y, the bf16 output's quantization), the gather form
         of the MoE front end (the step uses the scatter form: each token row
         quantized once and stored to its 4 routed rows, the same bytes), and
-        the MoE grouped product quantized in its epilogue."""
+        the MoE grouped product quantized in its epilogue, and the clipping
+        statistic of the fprop activation's quantization (reads X once)."""
         t_bytes = 2 * (2880 * 5760 // 2 + (2880 // 32) * (5760 // 32))
         q = quant_bytes(16384, 2880)
         return [
@@ -211,6 +213,8 @@ class Workload:
             ("fused_gemm_quantize_y", lambda: mx.gemm_quantize(self.f_qx, self.f_qw, out=self.g_qy), "mfma",
              2 * 16384 * 5760 * 2880),
             ("unfused_quantize_y", lambda: mx.quantize(self.f_y, out=self.g_qy2), "hbm", quant_bytes(16384, 5760)),
+            ("clip_count_x_rht", lambda: mx.clip_count(self.fx, rht_mask=self.f_mask, out=self.clip_n), "hbm",
+             16384 * 2880 * 2),
             ("moe_gather_quantize_a", lambda: mx.quantize_gather(self.mx_tok, self.m_rows, out=self.m_qa2), "hbm",
              gather_quant_bytes(16384, 65536, 2880)),
             ("moe_fused_grouped_gemm_quantize_y", lambda: mx.grouped_gemm_quantize(self.m_qa, self.m_offsets, self.mb,

@@ -432,6 +432,33 @@ mx_status mx_grouped_gemm_quantize(const mx_tensor* A, const int32_t* d_group_of
                                    const mx_tensor* B, int64_t expert_stride_codes, int64_t expert_stride_scales,
                                    int32_t scale_mode, mx_tensor* out, void* stream);
 
+/*
+ * mx_clip_count — clipping statistic of a quantization.  "MXFP4", AI Wiki,
+ * §Clipping in the reference algorithm: under the reference scale rule a
+ * block's maximum can scale to just below twice the element type's largest
+ * power of two, and every element scaling above the largest normal (6 for
+ * E2M1, 448 E4M3, 57344 E5M2, 7.5 E2M3, 28 E3M2) saturates to it; the page
+ * estimates ~3 % of entries on typical matrices.  This adds to *count the
+ * number of elements of src that saturate when src is quantized with cfg and
+ * element type elem: those whose value after the optional sign flips and
+ * transform, the optional 3/4 prescale and the multiply by the inverse block
+ * scale (exactly the quantizer's steps) has a magnitude above the largest
+ * normal.  cfg->rounding is ignored (every mode saturates the same elements);
+ * blocks holding NaN or Inf count nothing.  With MX_SCALE_ROUND_UP or
+ * MX_SCALE_PRESCALE_3_4 the count is 0 by construction.
+ *
+ *   src, src_dtype, R, C, ld_src, cfg  as in mx_quantize (the same alignment
+ *            rules; axis, block, use_rht, rht_sign_mask and scale_mode used).
+ *   elem     an mx_elem.
+ *   count    device; one 64-bit counter, ADDED to (atomically; the caller
+ *            zeroes it, and calls on one stream accumulate).
+ *   Requires K % 32 == 0 (K = C for MX_AXIS_LAST, R for MX_AXIS_DIM0); 2-D
+ *   blocks need rows_out % 32 == 0.  R = 0 or C = 0 adds nothing.  Reads only
+ *   src; allocates nothing.
+ */
+mx_status mx_clip_count(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
+                        const mx_quant_cfg* cfg, int32_t elem, uint64_t* count, void* stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* mx_last_error(void);
 

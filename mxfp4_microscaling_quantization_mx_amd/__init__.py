@@ -33,7 +33,7 @@ _DTYPE = {torch.float32: MX_DT_F32, torch.bfloat16: MX_DT_BF16}
 
 EXPORTED = ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
             "mx_gemm_quantize", "mx_gemm_workspace_size", "mx_gemm_noalloc", "mx_gemm_fused_quant_a", "mx_grouped_gemm",
-            "mx_grouped_gemm_quantize",
+            "mx_grouped_gemm_quantize", "mx_clip_count",
             "mx_last_error", "mx_version")
 
 
@@ -84,6 +84,7 @@ def load_library(path=LIB_PATH):
     lib.mx_gemm_workspace_size.restype = ctypes.c_size_t
     lib.mx_grouped_gemm.argtypes = [PT, P, I32, PT, I64, I64, P, I32, I64, P]
     lib.mx_grouped_gemm_quantize.argtypes = [PT, P, I32, PT, I64, I64, I32, PT, P]
+    lib.mx_clip_count.argtypes = [P, I32, I64, I64, I64, ctypes.POINTER(QuantCfgC), I32, P, P]
     for f in ("mx_quantize", "mx_quantize_gather", "mx_quantize_scatter", "mx_dequantize", "mx_transpose", "mx_gemm",
               "mx_gemm_quantize", "mx_gemm_noalloc", "mx_gemm_fused_quant_a", "mx_grouped_gemm",
               "mx_grouped_gemm_quantize"):
@@ -175,6 +176,28 @@ def quantize(x, axis="last", block="1d", rounding="rne", rht_mask=None, seed=0, 
     ot = out.c_struct()
     _check(lib.mx_quantize(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), ctypes.byref(cfg),
                            ctypes.byref(ot), _stream(x)))
+    return out
+
+
+def clip_count(x, axis="last", block="1d", rht_mask=None, scale_mode="floor", elem="e2m1", out=None):
+    """Clipping statistic of quantizing x with these settings: the number of
+    elements that saturate at the element type's largest normal (see
+    mx_clip_count in include/mx.h).  Returns a one-element int64 CUDA tensor;
+    with `out` given (one int64 element), the count is added to it."""
+    lib = load_library()
+    if x.dim() != 2 or x.dtype not in _DTYPE or not x.is_cuda:
+        raise ValueError("clip_count expects a 2-D bf16/float32 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("clip_count expects a row-major tensor (stride(1) == 1)")
+    if out is None:
+        out = torch.zeros(1, dtype=torch.int64, device=x.device)
+    elif out.dtype != torch.int64 or out.numel() != 1 or not out.is_cuda:
+        raise ValueError("clip_count: out must be a one-element int64 CUDA tensor")
+    R, C = x.shape
+    cfg = QuantCfgC(_AXIS[axis], _BLOCK[block], _ROUND["rne"], int(rht_mask is not None),
+                    (rht_mask or 0) & 0xFFFFFFFF, _SCALE[scale_mode], 0, 0)
+    _check(lib.mx_clip_count(_ptr(x), _DTYPE[x.dtype], R, C, x.stride(0), ctypes.byref(cfg), _ELEM[elem][0],
+                             _ptr(out), _stream(x)))
     return out
 
 

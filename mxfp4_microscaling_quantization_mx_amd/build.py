@@ -27,7 +27,7 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "transpose.hip", "gemm.hip", "gemm_splitk.hip"]
+SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "transpose.hip", "gemm.hip", "gemm_splitk.hip", "clip.hip"]
 
 
 def _run(cmd):

@@ -145,6 +145,52 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   return hip_status(mx::launch_quantize(a, static_cast<hipStream_t>(stream)), "mx_quantize");
 }
 
+mx_status mx_clip_count(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
+                        const mx_quant_cfg* cfg, int32_t elem, uint64_t* count, void* stream) {
+  g_err[0] = '\0';
+  if (!cfg) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: null cfg");
+  if (src_dtype != MX_DT_F32 && src_dtype != MX_DT_BF16)
+    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: unknown source dtype %d", src_dtype);
+  if (cfg->axis != MX_AXIS_LAST && cfg->axis != MX_AXIS_DIM0)
+    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: unknown axis %d", cfg->axis);
+  if (cfg->block != MX_BLOCK_1D && cfg->block != MX_BLOCK_2D)
+    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: unknown block kind %d", cfg->block);
+  if (cfg->use_rht != 0 && cfg->use_rht != 1)
+    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: use_rht must be 0 or 1");
+  if (cfg->scale_mode > MX_SCALE_PRESCALE_3_4)
+    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: unknown scale_mode %u", cfg->scale_mode);
+  if (elem < MX_ELEM_E2M1 || elem > MX_ELEM_E3M2)
+    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: unknown element type %d", elem);
+  if (R < 0 || C < 0) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: negative shape");
+  const bool dim0 = cfg->axis == MX_AXIS_DIM0;
+  const int64_t rows_out = dim0 ? C : R;
+  const int64_t K = dim0 ? R : C;
+  if (K % 32) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: blocking dimension %lld is not a multiple of 32", (long long)K);
+  if (cfg->block == MX_BLOCK_2D && rows_out % 32)
+    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: 2-D blocks need rows_out %% 32 == 0 (got %lld)", (long long)rows_out);
+  if (!count) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: null count");
+  if (!aligned(count, 8)) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: count must be 8-byte aligned");
+  if (R == 0 || C == 0) return MX_OK;
+  if (!src) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: null src");
+  if (ld_src < C) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: ld_src=%lld < C=%lld", (long long)ld_src, (long long)C);
+  if (!aligned(src, 16) || ld_src % 8)
+    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: src must be 16-byte aligned with ld_src %% 8 == 0");
+  mx::ClipArgs a{};
+  a.src = src;
+  a.R = R;
+  a.C = C;
+  a.ld_src = ld_src;
+  a.bf16 = src_dtype == MX_DT_BF16;
+  a.dim0 = dim0;
+  a.two_d = cfg->block == MX_BLOCK_2D;
+  a.rht = cfg->use_rht == 1;
+  a.mask = cfg->rht_sign_mask;
+  a.scale_mode = (int)cfg->scale_mode;
+  a.elem = elem;
+  a.count = reinterpret_cast<unsigned long long*>(count);
+  return hip_status(mx::launch_clip_count(a, static_cast<hipStream_t>(stream)), "mx_clip_count");
+}
+
 mx_status mx_quantize_scatter(const void* src, int32_t src_dtype, int64_t R, int64_t C, int64_t ld_src,
                               const int32_t* dest, int32_t k, const mx_quant_cfg* cfg, const mx_tensor* out,
                               void* stream) {

@@ -120,6 +120,19 @@ struct TransposeArgs {
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+
+// Clipping statistic: the elements that saturate when src is quantized with
+// these settings, added to *count.
+struct ClipArgs {
+  const void* src;
+  int64_t R, C, ld_src;       // source [R, C], row stride in elements
+  bool bf16, dim0, two_d, rht;
+  uint32_t mask;
+  int scale_mode;
+  int elem;
+  unsigned long long* count;  // device
+};
+hipError_t launch_clip_count(const ClipArgs& a, hipStream_t st);
 // MXFP4 RNE quantization of the a.R source rows, row t stored to output rows
 // dest[t * k + j], j < k (those in [0, M)).
 hipError_t launch_quantize_scatter(const QuantArgs& a, const int32_t* dest, int k, int64_t M, hipStream_t st);

@@ -332,3 +332,40 @@ def test_gemm_fused_quant_a_rejects_bad_arguments(lib):
     assert call(b=B(fp8)) == mx.MX_ERR_UNSUPPORTED and b"MXFP4" in lib.mx_last_error()
     assert call(M=-1) == mx.MX_ERR_INVALID_ARG
     assert call(M=0, a=None, c=None) == mx.MX_OK          # empty: nothing launched
+
+
+def test_clip_count_rejects_bad_arguments(lib):
+    """Host-side checks of mx_clip_count, before any launch."""
+    B = ctypes.byref
+    P = ctypes.c_void_p
+    f = lib.mx_clip_count
+    cfg = mx.QuantCfgC(0, 0, 0, 0, 0, 0, 0, 0)
+    ok = (P(16), mx.MX_DT_BF16, 64, 96, 96, B(cfg), 0, P(64), None)
+
+    def call(**kw):
+        args = list(ok)
+        names = ["src", "dtype", "R", "C", "ld", "cfg", "elem", "count", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(cfg=None) == mx.MX_ERR_INVALID_ARG
+    assert call(dtype=5) == mx.MX_ERR_INVALID_ARG and b"dtype" in lib.mx_last_error()
+    assert call(cfg=B(mx.QuantCfgC(2, 0, 0, 0, 0, 0, 0, 0))) == mx.MX_ERR_INVALID_ARG
+    assert call(cfg=B(mx.QuantCfgC(0, 2, 0, 0, 0, 0, 0, 0))) == mx.MX_ERR_INVALID_ARG
+    assert call(cfg=B(mx.QuantCfgC(0, 0, 0, 2, 0, 0, 0, 0))) == mx.MX_ERR_INVALID_ARG
+    assert call(cfg=B(mx.QuantCfgC(0, 0, 0, 0, 0, 3, 0, 0))) == mx.MX_ERR_INVALID_ARG
+    for e in (-1, 5):
+        assert call(elem=e) == mx.MX_ERR_INVALID_ARG and b"element" in lib.mx_last_error()
+    assert call(C=80, ld=80) == mx.MX_ERR_INVALID_ARG and b"multiple of 32" in lib.mx_last_error()
+    assert call(cfg=B(mx.QuantCfgC(0, 1, 0, 0, 0, 0, 0, 0)), R=48) == mx.MX_ERR_INVALID_ARG
+    assert b"2-D" in lib.mx_last_error()
+    assert call(cfg=B(mx.QuantCfgC(1, 1, 0, 0, 0, 0, 0, 0)), R=64, C=48, ld=48) == mx.MX_ERR_INVALID_ARG
+    assert call(count=None) == mx.MX_ERR_INVALID_ARG and b"count" in lib.mx_last_error()
+    assert call(count=P(68)) == mx.MX_ERR_INVALID_ARG and b"aligned" in lib.mx_last_error()
+    assert call(src=P(18)) == mx.MX_ERR_INVALID_ARG and b"aligned" in lib.mx_last_error()
+    assert call(ld=100) == mx.MX_ERR_INVALID_ARG and b"aligned" in lib.mx_last_error()
+    assert call(ld=64) == mx.MX_ERR_INVALID_ARG and b"ld_src" in lib.mx_last_error()
+    assert call(src=None) == mx.MX_ERR_INVALID_ARG
+    assert call(R=-1) == mx.MX_ERR_INVALID_ARG
+    assert call(R=0, src=None) == mx.MX_OK               # empty: nothing launched
