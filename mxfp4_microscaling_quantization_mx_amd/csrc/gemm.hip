@@ -1071,92 +1071,105 @@ __device__ __forceinline__ void f8_compute(v16f acc[2][4], uint32_t slot, uint32
   }
 }
 
-template <int FA, int FB>
-__global__ __launch_bounds__(512) void k_gemm_f8(MxOperand A, MxOperand B, int M, int N, int K, void* C, int64_t ldc,
-                                                int a_2d, int b_2d, int out_bf16) {
-  __shared__ __attribute__((aligned(1024))) uint8_t slot0[f8::SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t slot1[f8::SLOT];
-  __shared__ __attribute__((aligned(16))) uint32_t sw0[f8::SWORDS];
-  __shared__ __attribute__((aligned(16))) uint32_t sw1[f8::SWORDS];
+// Persistent: one workgroup per CU walks its XCD's contiguous range of tiles
+// (groups of 8 M-tiles, as the MXFP4 kernel), and the stage sequence runs on
+// across tiles: the next tile's first stage loads into the free slot while
+// the current tile's last stage is multiplied and its result stored.
+template <int FA, int FB, bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void k_gemm_f8(MxOperand A, MxOperand B, int M, int N, int K, void* C,
+                                                   int64_t ldc, int a_2d, int b_2d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slots[2 * f8::SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t sws[2 * f8::SWORDS];
+  const XcdShare share((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n);
+  const int ntiles = share.count();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int m0 = (int)blockIdx.y * 256, n0 = (int)blockIdx.x * 256;
-  const int arows = M - m0 < 256 ? M - m0 : 256, brows = N - n0 < 256 ? N - n0 : 256;
-  F8Lane L;
-  L.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.codes) + (int64_t)m0 * A.ld_codes, 0,
-                                           (uint32_t)(arows * A.ld_codes), 0x00020000);
-  L.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B.codes) + (int64_t)n0 * B.ld_codes, 0,
-                                           (uint32_t)(brows * B.ld_codes), 0x00020000);
+  // this lane's load offsets (row and K chunk) and its scale row
+  int crow[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = 8 * (4 * wave + t) + (lane >> 3);
-    L.c[t] = (lane & 7) ^ ((row >> 1) & 7);                 // the K chunk this lane's LDS chunk holds
-    L.va[t] = row < arows ? (uint32_t)(row * A.ld_codes + 16 * L.c[t]) : MX_OOB;
-    L.vb[t] = row < brows ? (uint32_t)(row * B.ld_codes + 16 * L.c[t]) : MX_OOB;
+    crow[t] = (lane & 7) ^ ((row >> 1) & 7);               // the K chunk this lane's LDS chunk holds
   }
-  {
-    const bool isA = wave < 4;
-    const int r = 64 * (wave & 3) + lane;                   // this lane's scale row within the tile
-    const bool two_d = isA ? a_2d != 0 : b_2d != 0;
-    const int r0 = isA ? m0 : n0, rows = isA ? arows : brows;
-    const int64_t lds_s = isA ? A.ld_scales : B.ld_scales;
-    const uint8_t* sbase = (isA ? A.scales : B.scales) + (int64_t)(two_d ? (r0 >> 5) : r0) * lds_s;
-    L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase), 0, (uint32_t)((two_d ? 8 : 256) * lds_s),
-                                             0x00020000);
-    L.so = r < rows ? (uint32_t)((two_d ? (r >> 5) : r) * lds_s) : MX_OOB;
-  }
-  v16f acc[2][4];
+  const bool sA = wave < 4;
+  const int srow = 64 * (wave & 3) + lane;                    // this lane's scale row within the tile
+  const bool s2d = sA ? a_2d != 0 : b_2d != 0;
+  const int64_t lds_s = sA ? A.ld_scales : B.ld_scales;
+  // Tile j of this workgroup: origin and the lane's load state.
+  auto setup = [&](int j, F8Lane& L, int& m0, int& n0, int& arows, int& brows) {
+    int tm, tn;
+    group_order<8>(share.tile(j), tiles_m, tiles_n, tm, tn);
+    m0 = tm * 256;
+    n0 = tn * 256;
+    arows = M - m0 < 256 ? M - m0 : 256;
+    brows = N - n0 < 256 ? N - n0 : 256;
+    L.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.codes) + (int64_t)m0 * A.ld_codes, 0,
+                                             (uint32_t)(arows * A.ld_codes), 0x00020000);
+    L.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B.codes) + (int64_t)n0 * B.ld_codes, 0,
+                                             (uint32_t)(brows * B.ld_codes), 0x00020000);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  const int nst = (K + 127) / 128;
-  const uint32_t a_slot0 = (uint32_t)(uintptr_t)(f8::lds_t)slot0, a_slot1 = (uint32_t)(uintptr_t)(f8::lds_t)slot1;
-  const uint32_t a_sw0 = (uint32_t)(uintptr_t)(f8::lds_t)sw0, a_sw1 = (uint32_t)(uintptr_t)(f8::lds_t)sw1;
-  if (nst > 0) f8_issue<FA, FB>(L, 0, K, slot0, sw0, wave);
-  for (int s = 0; s < nst; s += 2) {
-    // stage s in slot 0; stage s + 1 loads into slot 1
-    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's loads of stage s landed
-    __syncthreads();                         // ... every wave's; every wave is done with slot 1
-    if (s + 1 < nst) f8_issue<FA, FB>(L, s + 1, K, slot1, sw1, wave);
-    f8_compute<FA, FB>(acc, a_slot0, a_sw0, s, K, wm, wn, l32, hi);
-    if (s + 1 >= nst) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (s + 2 < nst) f8_issue<FA, FB>(L, s + 2, K, slot0, sw0, wave);
-    f8_compute<FA, FB>(acc, a_slot1, a_sw1, s + 1, K, wm, wn, l32, hi);
-  }
-  // epilogue: bounds-checked buffer stores (lane = column, register r = row
-  // 8 (r / 4) + 4 hi + r % 4 of the MFMA tile)
-  const int es = out_bf16 ? 2 : 4;
-  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<uint8_t*>(C) + ((int64_t)m0 * ldc + n0) * es, 0,
-      (uint32_t)(((int64_t)(arows - 1) * ldc + brows) * es), 0x00020000);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = wn * 128 + j * 32 + l32;
-      const uint32_t voff = col < brows ? (uint32_t)((4 * hi * ldc + col) * es) : MX_OOB;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t soff = (uint32_t)((wm * 64 + i * 32 + 8 * (r >> 2) + (r & 3)) * ldc * es);
-        if (out_bf16)
-          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_rne(acc[i][j][r]), rc, voff, soff, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, voff, soff, 0);
-      }
+    for (int t = 0; t < 4; ++t) {
+      const int row = 8 * (4 * wave + t) + (lane >> 3);
+      L.c[t] = crow[t];
+      L.va[t] = row < arows ? (uint32_t)(row * A.ld_codes + 16 * crow[t]) : MX_OOB;
+      L.vb[t] = row < brows ? (uint32_t)(row * B.ld_codes + 16 * crow[t]) : MX_OOB;
     }
+    const int r0 = sA ? m0 : n0, rows = sA ? arows : brows;
+    const uint8_t* sbase = (sA ? A.scales : B.scales) + (int64_t)(s2d ? (r0 >> 5) : r0) * lds_s;
+    L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase), 0, (uint32_t)((s2d ? 8 : 256) * lds_s),
+                                             0x00020000);
+    L.so = srow < rows ? (uint32_t)((s2d ? (srow >> 5) : srow) * lds_s) : MX_OOB;
+  };
+  const int nst = (K + 127) / 128;
+  const uint32_t a_slots = (uint32_t)(uintptr_t)(f8::lds_t)slots, a_sws = (uint32_t)(uintptr_t)(f8::lds_t)sws;
+  F8Lane L;
+  int m0 = 0, n0 = 0, arows = 0, brows = 0, m0n = 0, n0n = 0, arn = 0, brn = 0;
+  if (ntiles > 0) setup(0, L, m0, n0, arows, brows);
+  if (ntiles > 0 && nst > 0) f8_issue<FA, FB>(L, 0, K, slots, sws, wave);
+  int g = 0;                                                  // stages multiplied so far (slot g & 1)
+  for (int j = 0; j < ntiles; ++j) {
+    t256::Acc acc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc.t[i][jj][r] = 0.0f;
+    for (int s = 0; s < nst; ++s, ++g) {
+      // stage s of tile j is in slot g & 1; the other slot takes the next stage
+      __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's loads of stage s landed
+      __syncthreads();                         // ... every wave's; every wave is done with the other slot
+      const int nx = (g + 1) & 1;
+      if (s + 1 < nst) {
+        f8_issue<FA, FB>(L, s + 1, K, slots + nx * f8::SLOT, sws + nx * f8::SWORDS, wave);
+      } else if (j + 1 < ntiles) {
+        // tile j issues nothing more: its load state becomes tile j + 1's
+        setup(j + 1, L, m0n, n0n, arn, brn);
+        f8_issue<FA, FB>(L, 0, K, slots + nx * f8::SLOT, sws + nx * f8::SWORDS, wave);
+      }
+      f8_compute<FA, FB>(acc.t, a_slots + (uint32_t)((g & 1) * f8::SLOT), a_sws + (uint32_t)((g & 1) * 4 * f8::SWORDS),
+                         s, K, wm, wn, l32, hi);
+    }
+    // epilogue: bounds-checked buffer stores of the tile (the shared store
+    // path of the 256x256 kernels: same wave layout and MFMA tiles)
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    t256::store_tile<OUT_BF16>(acc, static_cast<uint8_t*>(C) + ((int64_t)m0 * ldc + n0) * ES, (int)ldc, M - m0,
+                               N - n0);
+    if (j + 1 < ntiles) {
+      m0 = m0n;
+      n0 = n0n;
+      arows = arn;
+      brows = brn;
+    }
+  }
 }
 
 // 256x256 tiles (8 waves of 64x128) when both dimensions fill them, else
 // 128x128 (4 waves of 64x64).
 template <int FA, int FB>
-hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st, int cus) {
   if constexpr (FA >= 1 && FA <= 4 && FB >= 1 && FB <= 4) {
     // MXFP8 / MXFP6 operands with whole 256x256 tiles available, 4-byte
     // aligned scale rows and 32-bit tile offsets: the direct-to-LDS kernel
@@ -1165,9 +1178,15 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
     const bool small = 256 * a.A.ld_codes < (1ll << 31) && 256 * a.B.ld_codes < (1ll << 31) &&
                        256 * a.ldc * 4 < (1ll << 31) && a.M < (1ll << 31) && a.N < (1ll << 31) && a.K < (1ll << 30);
     if (a.M >= 256 && a.N >= 256 && words && small) {
-      const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)((a.M + 255) / 256));
-      hipLaunchKernelGGL((k_gemm_f8<FA, FB>), grid, dim3(512), 0, st, a.A, a.B, (int)a.M, (int)a.N, (int)a.K, a.C,
-                         a.ldc, (int)a.a_2d, (int)a.b_2d, (int)a.out_bf16);
+      const int tiles_m = (int)((a.M + 255) / 256), tiles_n = (int)((a.N + 255) / 256);
+      const int tiles = tiles_m * tiles_n;
+      const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
+      if (a.out_bf16)
+        hipLaunchKernelGGL((k_gemm_f8<FA, FB, true>), dim3(nwg), dim3(512), 0, st, a.A, a.B, (int)a.M, (int)a.N,
+                           (int)a.K, a.C, a.ldc, (int)a.a_2d, (int)a.b_2d, tiles_m, tiles_n);
+      else
+        hipLaunchKernelGGL((k_gemm_f8<FA, FB, false>), dim3(nwg), dim3(512), 0, st, a.A, a.B, (int)a.M, (int)a.N,
+                           (int)a.K, a.C, a.ldc, (int)a.a_2d, (int)a.b_2d, tiles_m, tiles_n);
       return hipGetLastError();
     }
   }
@@ -1184,13 +1203,13 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
 }
 
 template <int FA>
-hipError_t launch_gemm_mx_b(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm_mx_b(const GemmArgs& a, hipStream_t st, int cus) {
   switch (a.b_elem) {
-    case 1: return launch_gemm_mx<FA, 1>(a, st);
-    case 2: return launch_gemm_mx<FA, 2>(a, st);
-    case 3: return launch_gemm_mx<FA, 3>(a, st);
-    case 4: return launch_gemm_mx<FA, 4>(a, st);
-    default: return launch_gemm_mx<FA, 0>(a, st);
+    case 1: return launch_gemm_mx<FA, 1>(a, st, cus);
+    case 2: return launch_gemm_mx<FA, 2>(a, st, cus);
+    case 3: return launch_gemm_mx<FA, 3>(a, st, cus);
+    case 4: return launch_gemm_mx<FA, 4>(a, st, cus);
+    default: return launch_gemm_mx<FA, 0>(a, st, cus);
   }
 }
 
@@ -1222,12 +1241,13 @@ bool gemm256_layout_ok(const GemmArgs& a) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.a_elem != 0 || a.b_elem != 0) {
+    const int cus = cu_count();
     switch (a.a_elem) {
-      case 1: return launch_gemm_mx_b<1>(a, st);
-      case 2: return launch_gemm_mx_b<2>(a, st);
-      case 3: return launch_gemm_mx_b<3>(a, st);
-      case 4: return launch_gemm_mx_b<4>(a, st);
-      default: return launch_gemm_mx_b<0>(a, st);
+      case 1: return launch_gemm_mx_b<1>(a, st, cus);
+      case 2: return launch_gemm_mx_b<2>(a, st, cus);
+      case 3: return launch_gemm_mx_b<3>(a, st, cus);
+      case 4: return launch_gemm_mx_b<4>(a, st, cus);
+      default: return launch_gemm_mx_b<0>(a, st, cus);
     }
   }
   if (gemm256_layout_ok(a)) {
