@@ -247,6 +247,49 @@ def test_gemm_mxfp8_end_to_end(fa, fb):
     assert np.all(np.abs(y[np.ix_(rows, cols)] - ref) <= tol)
 
 
+# (exponent-field range, E, M) of "narrow" codes: normal values in [1, 16)
+_NARROW = {"e4m3": (7, 10, 4, 3), "e5m2": (15, 18, 5, 2), "e2m3": (1, 3, 2, 3), "e3m2": (3, 6, 3, 2)}
+
+
+def _narrow_codes(rng, elem, shape):
+    """Random signs and mantissas over four binades of normals, so that the
+    products of one 64-deep MFMA step lie within 2^10 of each other, inside
+    the instruction's alignment window: the float32 bound alone applies."""
+    lo, hi, E, M = _NARROW[elem]
+    e = rng.integers(lo, hi + 1, size=shape)
+    m = rng.integers(0, 1 << M, size=shape)
+    sgn = rng.integers(0, 2, size=shape)
+    return _pack((sgn << (E + M)) | (e << M) | m, elem)
+
+
+@pytest.mark.parametrize("fa,fb,out", [("e4m3", "e4m3", torch.bfloat16), ("e2m3", "e3m2", torch.float32),
+                                       ("e5m2", "e2m3", torch.bfloat16)])
+def test_gemm_elements_more_tiles_than_cus(fa, fb, out):
+    """4352 x 4160 x 416: 17 x 17 tiles of 256 (the last column tile 64 wide),
+    more than there are CUs, so workgroups of the persistent direct-to-LDS
+    kernel run a second tile (its first stage loaded during the first tile's
+    last stage and epilogue); K = 416 is 3.25 stages and, for FP6, ends half-way
+    through a 16-byte chunk.  Every output against the oracle."""
+    need_gpu()
+    M, N, K = 4352, 4160, 416
+    rng = np.random.default_rng(zlib.crc32(f"many{fa}{fb}".encode()))
+    ac, bc = _narrow_codes(rng, fa, (M, K)), _narrow_codes(rng, fb, (N, K))
+    as_ = np.full((M, K // 32), 127, dtype=np.uint8)
+    bs = rng.integers(125, 130, (N, K // 32), dtype=np.uint8)
+    as_[:, 1::2] = 126
+    qa, qb = mx.empty_mx(M, K, elem=fa), mx.empty_mx(N, K, elem=fb)
+    qa.codes.copy_(to_dev(ac)); qa.scales.copy_(to_dev(as_))
+    qb.codes.copy_(to_dev(bc)); qb.scales.copy_(to_dev(bs))
+    banner(f"gemm {fa} x {fb} {M}x{N}x{K} {out}")
+    c = host(mx.gemm(qa, qb, out).float()).astype(np.float64)
+    ref, bound = oracle.gemm_ref(ac, as_, bc, bs, a_elem=fa, b_elem=fb)
+    tol = 1e-5 * bound
+    if out == torch.bfloat16:
+        tol = tol + bf16_half_ulp(np.maximum(np.abs(c), np.abs(ref)))
+    err = np.abs(c - ref)
+    assert np.all(err <= tol), float(np.max(err / tol))
+
+
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m3", "e3m2"), ("e5m2", "e2m1")])
 @pytest.mark.parametrize("N", [160, 288])
 def test_grouped_gemm_elements(fa, fb, N):
