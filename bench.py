@@ -103,9 +103,14 @@ class Workload:
         self.m_offsets = torch.from_numpy(offsets).to(dev)
         E, K, N = 32, 2880, 5760
         self.mb = mx.empty_mx(N, K, "2d", device=dev, experts=E)
+        # the same MoE product with MXFP8 (E4M3) operands (beside the step): the
+        # routed rows gathered in bf16 once and quantized, the weights likewise
+        self.mb8 = mx.empty_mx(N, K, "2d", device=dev, experts=E, elem="e4m3")
         for e in range(E):
             we = workloads.to_bf16(workloads.moe_expert_weight(e)).to(dev)
             mx.quantize(we, axis="dim0", block="2d", out=mx.expert(self.mb, e))
+            mx.quantize(we, axis="dim0", block="2d", out=mx.expert(self.mb8, e))
+        self.m_qa8 = mx.quantize(self.mx_tok.index_select(0, self.m_rows.long()), elem="e4m3")
         # outputs (allocated once)
         self.q_last = mx.empty_mx(16384, 2880, device=dev)
         self.q_dim0 = mx.empty_mx(2880, 16384, device=dev)
@@ -184,7 +189,8 @@ class Workload:
         unfused_quantize_y, the bf16 output's quantization), the gather form
         of the MoE front end (the step uses the scatter form: each token row
         quantized once and stored to its 4 routed rows, the same bytes), and
-        the MoE grouped product quantized in its epilogue, and the clipping
+        the MoE grouped product quantized in its epilogue and with MXFP8
+        operands, and the clipping
         statistic of the fprop activation's quantization (reads X once)."""
         t_bytes = 2 * (2880 * 5760 // 2 + (2880 // 32) * (5760 // 32))
         q = quant_bytes(16384, 2880)
@@ -220,6 +226,8 @@ class Workload:
             ("moe_fused_grouped_gemm_quantize_y", lambda: mx.grouped_gemm_quantize(self.m_qa, self.m_offsets, self.mb,
                                                                                    out=self.m_qy), "mfma",
              2 * 65536 * 5760 * 2880),
+            ("moe_grouped_gemm_mxfp8", lambda: mx.grouped_gemm(self.m_qa8, self.m_offsets, self.mb8, out=self.m_y),
+             "mfma8", 2 * 65536 * 5760 * 2880),
         ]
 
 

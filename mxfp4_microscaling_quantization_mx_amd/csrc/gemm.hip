@@ -845,35 +845,6 @@ __global__ __launch_bounds__((mx_threads<FA, FB, BM_, BN_, TI, TJ>())) void k_gr
                                          out_bf16);
 }
 
-template <int FA, int FB>
-hipError_t launch_grouped_gemm_mx(const GroupedGemmArgs& a, hipStream_t st) {
-  if (a.N >= 256) {
-    const int64_t slots = (a.M_cap + 255) / 256 + a.E;
-    const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)slots);
-    hipLaunchKernelGGL((k_grouped_gemm_mx<FA, FB, 256, 256, 2, 4>), grid, dim3(512), 0, st, a.A, a.B, a.M_cap, a.N,
-                       a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, (int)a.b_2d,
-                       (int)a.out_bf16);
-  } else {
-    const int64_t slots = (a.M_cap + 127) / 128 + a.E;
-    const dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)slots);
-    hipLaunchKernelGGL((k_grouped_gemm_mx<FA, FB, 128, 128, 2, 2>), grid, dim3(256), 0, st, a.A, a.B, a.M_cap, a.N,
-                       a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, (int)a.b_2d,
-                       (int)a.out_bf16);
-  }
-  return hipGetLastError();
-}
-
-template <int FA>
-hipError_t launch_grouped_gemm_mx_b(const GroupedGemmArgs& a, hipStream_t st) {
-  switch (a.b_elem) {
-    case 1: return launch_grouped_gemm_mx<FA, 1>(a, st);
-    case 2: return launch_grouped_gemm_mx<FA, 2>(a, st);
-    case 3: return launch_grouped_gemm_mx<FA, 3>(a, st);
-    case 4: return launch_grouped_gemm_mx<FA, 4>(a, st);
-    default: return launch_grouped_gemm_mx<FA, 0>(a, st);
-  }
-}
-
 // ------------------------------------ MXFP8 / MXFP6 operands, loads straight to LDS
 // 256x256 tiles of 8 waves (4 along M x 2 along N, 64x128 each as 2 x 4
 // MFMA tiles) over 128-deep stages: 4 blocks, 128 code bytes per row for an
@@ -1071,22 +1042,20 @@ __device__ __forceinline__ void f8_compute(v16f acc[2][4], uint32_t slot, uint32
   }
 }
 
-// Persistent: one workgroup per CU walks its XCD's contiguous range of tiles
-// (groups of 8 M-tiles, as the MXFP4 kernel), and the stage sequence runs on
-// across tiles: the next tile's first stage loads into the free slot while
-// the current tile's last stage is multiplied and its result stored.
-template <int FA, int FB, bool OUT_BF16>
-__global__ __launch_bounds__(512, 1) void k_gemm_f8(MxOperand A, MxOperand B, int M, int N, int K, void* C,
-                                                   int64_t ldc, int a_2d, int b_2d, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t slots[2 * f8::SLOT];
-  __shared__ __attribute__((aligned(16))) uint32_t sws[2 * f8::SWORDS];
-  const XcdShare share((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n);
-  const int ntiles = share.count();
+// Persistent: one workgroup per CU walks its list of tiles (Sched: the dense
+// XCD-contiguous ranges in groups of 8 M-tiles, or the grouped GEMM's expert
+// row tiles), and the stage sequence runs on across tiles: the next tile's
+// first stage loads into the free slot while the current tile's last stage is
+// multiplied and its result stored.
+template <int FA, int FB, bool OUT_BF16, class Sched>
+__device__ __forceinline__ void run_f8(const Sched& sc, const MxOperand& A, const MxOperand& B, int K, void* C,
+                                       int64_t ldc, int a_2d, int b_2d, uint8_t* slots, uint32_t* sws) {
+  const int ntiles = sc.count();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hi = lane >> 5;
-  // this lane's load offsets (row and K chunk) and its scale row
+  // this lane's K chunks (one per load) and its scale row
   int crow[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -1097,17 +1066,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_f8(MxOperand A, MxOperand B, in
   const int srow = 64 * (wave & 3) + lane;                    // this lane's scale row within the tile
   const bool s2d = sA ? a_2d != 0 : b_2d != 0;
   const int64_t lds_s = sA ? A.ld_scales : B.ld_scales;
-  // Tile j of this workgroup: origin and the lane's load state.
-  auto setup = [&](int j, F8Lane& L, int& m0, int& n0, int& arows, int& brows) {
-    int tm, tn;
-    group_order<8>(share.tile(j), tiles_m, tiles_n, tm, tn);
-    m0 = tm * 256;
-    n0 = tn * 256;
-    arows = M - m0 < 256 ? M - m0 : 256;
-    brows = N - n0 < 256 ? N - n0 : 256;
-    L.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.codes) + (int64_t)m0 * A.ld_codes, 0,
+  // Tile j of this workgroup: the lane's load state, and the tile's output
+  // origin (row of C, column) and extent.
+  auto setup = [&](int j, F8Lane& L, int64_t& crow0, int& n0, int& mlim, int& nlim) {
+    const t256::TileInfo ti = sc.tile(j);
+    mlim = ti.M - ti.m0;
+    nlim = ti.N - ti.n0;
+    const int arows = mlim < 256 ? mlim : 256, brows = nlim < 256 ? nlim : 256;
+    L.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ti.a_codes) + (int64_t)ti.m0 * A.ld_codes, 0,
                                              (uint32_t)(arows * A.ld_codes), 0x00020000);
-    L.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B.codes) + (int64_t)n0 * B.ld_codes, 0,
+    L.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ti.b_codes) + (int64_t)ti.n0 * B.ld_codes, 0,
                                              (uint32_t)(brows * B.ld_codes), 0x00020000);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -1116,17 +1084,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_f8(MxOperand A, MxOperand B, in
       L.va[t] = row < arows ? (uint32_t)(row * A.ld_codes + 16 * crow[t]) : MX_OOB;
       L.vb[t] = row < brows ? (uint32_t)(row * B.ld_codes + 16 * crow[t]) : MX_OOB;
     }
-    const int r0 = sA ? m0 : n0, rows = sA ? arows : brows;
-    const uint8_t* sbase = (sA ? A.scales : B.scales) + (int64_t)(s2d ? (r0 >> 5) : r0) * lds_s;
+    const int r0 = sA ? ti.m0 : ti.n0, rows = sA ? arows : brows;
+    const uint8_t* sbase = (sA ? ti.a_scales : ti.b_scales) + (int64_t)(s2d ? (r0 >> 5) : r0) * lds_s;
     L.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase), 0, (uint32_t)((s2d ? 8 : 256) * lds_s),
                                              0x00020000);
     L.so = srow < rows ? (uint32_t)((s2d ? (srow >> 5) : srow) * lds_s) : MX_OOB;
+    crow0 = ti.c_row0;
+    n0 = ti.n0;
   };
   const int nst = (K + 127) / 128;
   const uint32_t a_slots = (uint32_t)(uintptr_t)(f8::lds_t)slots, a_sws = (uint32_t)(uintptr_t)(f8::lds_t)sws;
   F8Lane L;
-  int m0 = 0, n0 = 0, arows = 0, brows = 0, m0n = 0, n0n = 0, arn = 0, brn = 0;
-  if (ntiles > 0) setup(0, L, m0, n0, arows, brows);
+  int64_t c0 = 0, c0n = 0;
+  int n0 = 0, mlim = 0, nlim = 0, n0n = 0, mln = 0, nln = 0;
+  if (ntiles > 0) setup(0, L, c0, n0, mlim, nlim);
   if (ntiles > 0 && nst > 0) f8_issue<FA, FB>(L, 0, K, slots, sws, wave);
   int g = 0;                                                  // stages multiplied so far (slot g & 1)
   for (int j = 0; j < ntiles; ++j) {
@@ -1146,25 +1117,110 @@ __global__ __launch_bounds__(512, 1) void k_gemm_f8(MxOperand A, MxOperand B, in
         f8_issue<FA, FB>(L, s + 1, K, slots + nx * f8::SLOT, sws + nx * f8::SWORDS, wave);
       } else if (j + 1 < ntiles) {
         // tile j issues nothing more: its load state becomes tile j + 1's
-        setup(j + 1, L, m0n, n0n, arn, brn);
+        setup(j + 1, L, c0n, n0n, mln, nln);
         f8_issue<FA, FB>(L, 0, K, slots + nx * f8::SLOT, sws + nx * f8::SWORDS, wave);
       }
       f8_compute<FA, FB>(acc.t, a_slots + (uint32_t)((g & 1) * f8::SLOT), a_sws + (uint32_t)((g & 1) * 4 * f8::SWORDS),
                          s, K, wm, wn, l32, hi);
     }
-    // epilogue: bounds-checked buffer stores of the tile (the shared store
-    // path of the 256x256 kernels: same wave layout and MFMA tiles)
+    // epilogue: the 256x256 kernels' bounds-checked store path (same wave
+    // layout and MFMA tiles)
     constexpr int ES = OUT_BF16 ? 2 : 4;
-    t256::store_tile<OUT_BF16>(acc, static_cast<uint8_t*>(C) + ((int64_t)m0 * ldc + n0) * ES, (int)ldc, M - m0,
-                               N - n0);
+    t256::store_tile<OUT_BF16>(acc, static_cast<uint8_t*>(C) + (c0 * ldc + n0) * ES, (int)ldc, mlim, nlim);
     if (j + 1 < ntiles) {
-      m0 = m0n;
+      if (nst == 0) setup(j + 1, L, c0n, n0n, mln, nln);
+      c0 = c0n;
       n0 = n0n;
-      arows = arn;
-      brows = brn;
+      mlim = mln;
+      nlim = nln;
     }
   }
 }
+
+template <int FA, int FB, bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void k_gemm_f8(MxOperand A, MxOperand B, int M, int N, int K, void* C,
+                                                   int64_t ldc, int a_2d, int b_2d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slots[2 * f8::SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t sws[2 * f8::SWORDS];
+  const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
+                      XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
+  run_f8<FA, FB, OUT_BF16>(sc, A, B, K, C, ldc, a_2d, b_2d, slots, sws);
+}
+
+// Grouped (MoE) form: the expert table and the schedule of the MXFP4 grouped
+// kernel (row tiles never straddle experts), A with 1-D scales.
+template <int FA, int FB, bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void k_grouped_gemm_f8(MxOperand A, MxOperand B, int64_t M_cap, int N, int K,
+                                                           const int32_t* __restrict__ offsets, int E,
+                                                           int64_t stride_codes, int64_t stride_scales, void* C,
+                                                           int64_t ldc, int b_2d, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slots[2 * f8::SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t sws[2 * f8::SWORDS];
+  __shared__ int tab[3 * GG_EMAX + 1];
+  __shared__ GroupedParams prm;
+  build_expert_table(offsets, E, M_cap, tab);   // ends with a barrier
+  const int total_slots = tab[E];
+  if (threadIdx.x == 0)
+    prm = GroupedParams{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
+                        (int)A.ld_scales, N, tiles_n, E, total_slots, 0, 0};
+  __syncthreads();
+  const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
+  run_f8<FA, FB, OUT_BF16>(sc, A, B, K, C, ldc, 0, b_2d, slots, sws);
+}
+
+template <int FA, int FB>
+hipError_t launch_grouped_gemm_mx(const GroupedGemmArgs& a, hipStream_t st, int cus) {
+  if constexpr (FA >= 1 && FA <= 4 && FB >= 1 && FB <= 4) {
+    // MXFP8 / MXFP6 operands: the persistent direct-to-LDS kernel when the
+    // scale rows are whole 32-bit words and the tile offsets fit 32 bits
+    const bool words = a.A.ld_scales % 4 == 0 && a.B.ld_scales % 4 == 0 && a.stride_scales % 4 == 0 &&
+                       (uintptr_t)a.A.scales % 4 == 0 && (uintptr_t)a.B.scales % 4 == 0;
+    const bool small = 256 * a.A.ld_codes < (1ll << 31) && 256 * a.B.ld_codes < (1ll << 31) &&
+                       256 * a.ldc * 4 < (1ll << 31) && a.N < (1ll << 31) && a.K < (1ll << 30) &&
+                       a.A.ld_codes < (1ll << 31) && a.A.ld_scales < (1ll << 31);
+    const int64_t slot_bound = (a.M_cap + 255) / 256 + a.E;
+    const int tiles_n = (int)((a.N + 255) / 256);
+    if (a.N >= 256 && words && small && a.E <= GG_EMAX && slot_bound * tiles_n < (1ll << 31)) {
+      const int64_t tiles = slot_bound * tiles_n;
+      const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
+      if (a.out_bf16)
+        hipLaunchKernelGGL((k_grouped_gemm_f8<FA, FB, true>), dim3(nwg), dim3(512), 0, st, a.A, a.B, a.M_cap,
+                           (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc,
+                           (int)a.b_2d, tiles_n);
+      else
+        hipLaunchKernelGGL((k_grouped_gemm_f8<FA, FB, false>), dim3(nwg), dim3(512), 0, st, a.A, a.B, a.M_cap,
+                           (int)a.N, (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc,
+                           (int)a.b_2d, tiles_n);
+      return hipGetLastError();
+    }
+  }
+  if (a.N >= 256) {
+    const int64_t slots = (a.M_cap + 255) / 256 + a.E;
+    const dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)slots);
+    hipLaunchKernelGGL((k_grouped_gemm_mx<FA, FB, 256, 256, 2, 4>), grid, dim3(512), 0, st, a.A, a.B, a.M_cap, a.N,
+                       a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, (int)a.b_2d,
+                       (int)a.out_bf16);
+  } else {
+    const int64_t slots = (a.M_cap + 127) / 128 + a.E;
+    const dim3 grid((unsigned)((a.N + 127) / 128), (unsigned)slots);
+    hipLaunchKernelGGL((k_grouped_gemm_mx<FA, FB, 128, 128, 2, 2>), grid, dim3(256), 0, st, a.A, a.B, a.M_cap, a.N,
+                       a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, a.C, a.ldc, (int)a.b_2d,
+                       (int)a.out_bf16);
+  }
+  return hipGetLastError();
+}
+
+template <int FA>
+hipError_t launch_grouped_gemm_mx_b(const GroupedGemmArgs& a, hipStream_t st, int cus) {
+  switch (a.b_elem) {
+    case 1: return launch_grouped_gemm_mx<FA, 1>(a, st, cus);
+    case 2: return launch_grouped_gemm_mx<FA, 2>(a, st, cus);
+    case 3: return launch_grouped_gemm_mx<FA, 3>(a, st, cus);
+    case 4: return launch_grouped_gemm_mx<FA, 4>(a, st, cus);
+    default: return launch_grouped_gemm_mx<FA, 0>(a, st, cus);
+  }
+}
+
 
 // 256x256 tiles (8 waves of 64x128) when both dimensions fill them, else
 // 128x128 (4 waves of 64x64).
@@ -1356,12 +1412,13 @@ hipError_t launch_grouped_gemm_quantize(const GroupedQuantArgs& q, hipStream_t s
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t st) {
   if (a.M_cap == 0 || a.N == 0) return hipSuccess;
   if (a.a_elem != 0 || a.b_elem != 0) {
+    const int cus = cu_count();
     switch (a.a_elem) {
-      case 1: return launch_grouped_gemm_mx_b<1>(a, st);
-      case 2: return launch_grouped_gemm_mx_b<2>(a, st);
-      case 3: return launch_grouped_gemm_mx_b<3>(a, st);
-      case 4: return launch_grouped_gemm_mx_b<4>(a, st);
-      default: return launch_grouped_gemm_mx_b<0>(a, st);
+      case 1: return launch_grouped_gemm_mx_b<1>(a, st, cus);
+      case 2: return launch_grouped_gemm_mx_b<2>(a, st, cus);
+      case 3: return launch_grouped_gemm_mx_b<3>(a, st, cus);
+      case 4: return launch_grouped_gemm_mx_b<4>(a, st, cus);
+      default: return launch_grouped_gemm_mx_b<0>(a, st, cus);
     }
   }
   const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) && (a.stride_scales % 16 == 0) &&

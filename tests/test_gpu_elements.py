@@ -325,3 +325,36 @@ def test_grouped_gemm_elements(fa, fb, N):
             tol[lo:hi] += mx_group_bound(av[lo:hi], bv)
     assert np.all(np.abs(got[:700] - ref) <= tol)
     assert np.all(got[700:] == 7.0)
+
+
+@pytest.mark.parametrize("fa,fb,b_block", [("e4m3", "e4m3", "2d"), ("e2m3", "e3m2", "1d"), ("e5m2", "e2m3", "2d")])
+def test_grouped_gemm_elements_more_tiles_than_cus(fa, fb, b_block):
+    """Grouped MXFP8 / MXFP6 GEMM with skewed experts (an empty one, a
+    one-row one, experts straddling row tiles) over 8192 routed rows, N = 2336
+    (the last column tile 32 wide), K = 416: about 360 tiles, more than there
+    are CUs, so the persistent direct-to-LDS kernel runs second tiles; bf16
+    output; every routed row against the oracle, rows past the last offset
+    untouched."""
+    need_gpu()
+    rng = np.random.default_rng(zlib.crc32(f"gm{fa}{fb}{b_block}".encode()))
+    offsets = np.array([0, 700, 700, 701, 2900, 3000, 5500, 8000, 8100], dtype=np.int32)
+    E, K, N, M = len(offsets) - 1, 416, 2336, 8192
+    ac = _narrow_codes(rng, fa, (M, K))
+    as_ = rng.integers(126, 129, (M, K // 32), dtype=np.uint8)
+    bc = np.stack([_narrow_codes(rng, fb, (N, K)) for _ in range(E)])
+    srows = N // 32 if b_block == "2d" else N
+    bs = rng.integers(125, 129, (E, srows, K // 32), dtype=np.uint8)
+    qa = mx.empty_mx(M, K, elem=fa)
+    qa.codes.copy_(to_dev(ac)); qa.scales.copy_(to_dev(as_))
+    qb = mx.empty_mx(N, K, b_block, experts=E, elem=fb)
+    qb.codes.copy_(to_dev(bc)); qb.scales.copy_(to_dev(bs))
+    y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    banner(f"grouped gemm {fa} x {fb} {b_block} {M}x{N}x{K} E={E}")
+    mx.grouped_gemm(qa, torch.from_numpy(offsets).cuda(), qb, out=y)
+    got = host(y.float()).astype(np.float64)
+    last = int(offsets[-1])
+    ref, bound = oracle.grouped_gemm_ref(ac, as_, offsets, bc, bs, "1d", b_block, rows=np.arange(last),
+                                         a_elem=fa, b_elem=fb)
+    tol = 1e-5 * bound + bf16_half_ulp(np.maximum(np.abs(got[:last]), np.abs(ref)))
+    assert np.all(np.abs(got[:last] - ref) <= tol)
+    assert np.all(got[last:] == 7.0)
