@@ -11,19 +11,23 @@
 // enter (every mode saturates the same elements), and blocks holding NaN or
 // Inf count nothing.
 //
-// One lane per block: lanes 32 g .. 32 g + 31 take the 32 output rows of one
-// tile row and one K-block, so a 2-D tile's maximum is a 32-lane reduction.
-// Rows-axis blocks are read as four 16-byte loads per lane, dim-0 blocks one
-// element per load (consecutive lanes, consecutive columns).  Per-lane counts
-// are summed per workgroup and added to the 64-bit total with one atomic.
+// One lane per block, with the block-to-lane maps below chosen so that a
+// wave's loads are contiguous; per-lane counts are summed per workgroup and
+// added to the 64-bit total with one atomic.
 #include "mx_device.h"
 #include "mx_launch.h"
 
 namespace mx {
 namespace {
 
-constexpr int CLIP_THREADS = 256;
-constexpr int CLIP_MAX_GROUPS = 8192;
+// Workgroup sizes and grid caps: every workgroup ends in one 64-bit atomic
+// add on the same address, and those serialize (8192 of them took ~80 us), so
+// the grids are capped near the CU count, with large workgroups for the
+// streaming kernels (measured at 16384 x 2880 bf16: 1-D rows 22-25 us, dim 0
+// 25-28 us) and 4 workgroups of 256 per CU for the 2-D tile kernel, whose
+// barrier per unit favours smaller groups (29-31 us).
+constexpr int CLIP_STREAM_THREADS = 1024, CLIP_STREAM_GROUPS = 256;
+constexpr int CLIP_TILE_THREADS = 256, CLIP_TILE_GROUPS = 1024;
 
 template <bool BF16>
 __device__ __forceinline__ float clip_load1(const void* __restrict__ src, int64_t i) {
@@ -64,62 +68,48 @@ constexpr uint32_t clip_top_bits() {
   else return ElemT<ELEM>::MAXBITS;
 }
 
-template <int ELEM, bool BF16, bool DIM0, bool TWO_D, bool RHT>
-__global__ __launch_bounds__(CLIP_THREADS) void k_clip_count(const void* __restrict__ src, int64_t ld,
-                                                             int64_t rows_out, int64_t nkb, int64_t lanes,
-                                                             uint32_t mask, int scale_mode,
-                                                             unsigned long long* count) {
-  __shared__ uint32_t wsum[CLIP_THREADS / 64];
-  const float top = __uint_as_float(clip_top_bits<ELEM>());
-  const float c = __uint_as_float(kRhtCBits);
-  uint32_t n = 0;
-  const int64_t stride = (int64_t)gridDim.x * CLIP_THREADS;
-  // `lanes` is a multiple of 32 and so is the stride: the 32 lanes of a tile
-  // row are in or out of the loop together (the 2-D reduction needs all 32)
-  for (int64_t t = (int64_t)blockIdx.x * CLIP_THREADS + threadIdx.x; t < lanes; t += stride) {
-    const int64_t g = t >> 5;
-    const int64_t tr = g / nkb, kb = g - tr * nkb;
-    const int64_t r = 32 * tr + (t & 31);
-    const bool valid = r < rows_out;
-    float x[32];
-    if (!valid) {
+// The block's values after the optional sign flips, transform and constant
+// (in place), and the float32 bits of its largest magnitude.
+template <bool RHT>
+__device__ __forceinline__ uint32_t clip_prepare(float x[32], uint32_t mask) {
+  uint32_t m = 0;
+  if (RHT) {
+    const float c = __uint_as_float(kRhtCBits);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = 0.0f;
-    } else if (DIM0) {
+    for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((mask >> i) & 1u) << 31));
+    fwht32_inlane(x);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = clip_load1<BF16>(src, (32 * kb + i) * ld + r);
-    } else {
+    for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    m = __float_as_uint(c * __uint_as_float(m));   // max |c t_i| = c max |t_i| (rounding is monotone)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) clip_load8<BF16>(src, r * ld + 32 * kb + 8 * j, x + 8 * j);
-    }
-    uint32_t m = 0;
-    if (RHT) {
+    for (int i = 0; i < 32; ++i) x[i] = c * x[i];
+  } else {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((mask >> i) & 1u) << 31));
-      fwht32_inlane(x);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-      m = __float_as_uint(c * __uint_as_float(m));
-#pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = c * x[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-    }
-    if (TWO_D) {
-#pragma unroll
-      for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
-    }
-    const uint32_t s = clip_scale_code<ELEM>(m, scale_mode);
-    if (valid && s != 0xFFu) {
-      const float inv = inv_scale_from_code(s);   // 2^(127 - s), a normal float for s <= 253
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float y = scale_mode == 2 ? 0.75f * x[i] : x[i];
-        n += fabsf(y * inv) > top ? 1u : 0u;
-      }
-    }
+    for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
   }
+  return m;
+}
+
+// Elements of a prepared block that saturate, given the largest magnitude m
+// of its block (1-D) or tile (2-D).
+template <int ELEM>
+__device__ __forceinline__ uint32_t clip_block(const float x[32], uint32_t m, int scale_mode) {
+  const uint32_t s = clip_scale_code<ELEM>(m, scale_mode);
+  if (s == 0xFFu) return 0;
+  const float top = __uint_as_float(clip_top_bits<ELEM>());
+  const float inv = inv_scale_from_code(s);   // 2^(127 - s), a normal float for s <= 253
+  uint32_t n = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float y = scale_mode == 2 ? 0.75f * x[i] : x[i];
+    n += fabsf(y * inv) > top ? 1u : 0u;
+  }
+  return n;
+}
+
+// Sum the lanes' counts of a workgroup of T threads and add them to the total.
+template <int T>
+__device__ __forceinline__ void clip_commit(uint32_t n, uint32_t* wsum, unsigned long long* count) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) n += (uint32_t)__shfl_xor((int)n, d, 64);
   if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = n;
@@ -127,35 +117,137 @@ __global__ __launch_bounds__(CLIP_THREADS) void k_clip_count(const void* __restr
   if (threadIdx.x == 0) {
     unsigned long long tot = 0;
 #pragma unroll
-    for (int w = 0; w < CLIP_THREADS / 64; ++w) tot += wsum[w];
+    for (int w = 0; w < T / 64; ++w) tot += wsum[w];
     if (tot) atomicAdd(count, tot);
   }
 }
 
-template <int ELEM, bool BF16, bool DIM0, bool TWO_D>
-hipError_t launch_clip4(const ClipArgs& a, hipStream_t st) {
+// Blocks along the rows, 1-D: lane t takes block t of the row-major block
+// order, so a wave reads 64 consecutive blocks (4 KiB of bf16) of a row.
+template <int ELEM, bool BF16, bool RHT>
+__global__ __launch_bounds__(CLIP_STREAM_THREADS) void k_clip_rows(const void* __restrict__ src, int64_t ld,
+                                                                   int64_t rows, int64_t nkb, uint32_t mask,
+                                                                   int scale_mode, unsigned long long* count) {
+  constexpr int T = CLIP_STREAM_THREADS;
+  __shared__ uint32_t wsum[T / 64];
+  uint32_t n = 0;
+  const int64_t total = rows * nkb, stride = (int64_t)gridDim.x * T;
+  for (int64_t b = (int64_t)blockIdx.x * T + threadIdx.x; b < total; b += stride) {
+    const int64_t r = b / nkb, kb = b - r * nkb;
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) clip_load8<BF16>(src, r * ld + 32 * kb + 8 * j, x + 8 * j);
+    const uint32_t m = clip_prepare<RHT>(x, mask);
+    n += clip_block<ELEM>(x, m, scale_mode);
+  }
+  clip_commit<T>(n, wsum, count);
+}
+
+// Blocks along the rows, 2-D (32x32 tiles): a workgroup takes 32 rows x KB
+// K-blocks at a time, thread (row rr = t / KB, block kk = t % KB), so a wave
+// reads runs of KB consecutive blocks of a row; the tile maxima go through LDS.
+template <int ELEM, bool BF16, bool RHT>
+__global__ __launch_bounds__(CLIP_TILE_THREADS) void k_clip_rows_2d(const void* __restrict__ src, int64_t ld,
+                                                                    int64_t rows, int64_t nkb, uint32_t mask,
+                                                                    int scale_mode, unsigned long long* count) {
+  constexpr int T = CLIP_TILE_THREADS;
+  constexpr int KB = T / 32;                  // K-blocks per unit
+  __shared__ uint32_t wsum[T / 64];
+  __shared__ uint32_t bm[32][KB + 1];
+  const int rr = threadIdx.x / KB, kk = threadIdx.x % KB;
+  const int64_t groups_k = (nkb + KB - 1) / KB, units = rows / 32 * groups_k;
+  uint32_t n = 0;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t tr = u / groups_k, kg = u - tr * groups_k;
+    const int64_t r = 32 * tr + rr, kb = KB * kg + kk;
+    const bool valid = kb < nkb;
+    float x[32];
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) clip_load8<BF16>(src, r * ld + 32 * kb + 8 * j, x + 8 * j);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+    }
+    bm[rr][kk] = clip_prepare<RHT>(x, mask);
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll 8
+    for (int q = 0; q < 32; ++q) m = max(m, bm[q][kk]);
+    if (valid) n += clip_block<ELEM>(x, m, scale_mode);
+    __syncthreads();                          // bm is rewritten by the next unit
+  }
+  clip_commit<T>(n, wsum, count);
+}
+
+// Blocks along dim 0: lanes 32 g .. 32 g + 31 take 32 consecutive source
+// columns (output rows) of one K-block, each reading its column's 32 elements
+// (consecutive lanes, consecutive addresses); a 2-D tile's maximum is a
+// 32-lane reduction.
+template <int ELEM, bool BF16, bool TWO_D, bool RHT>
+__global__ __launch_bounds__(CLIP_STREAM_THREADS) void k_clip_dim0(const void* __restrict__ src, int64_t ld,
+                                                                   int64_t rows_out, int64_t nkb, int64_t lanes,
+                                                                   uint32_t mask, int scale_mode,
+                                                                   unsigned long long* count) {
+  constexpr int T = CLIP_STREAM_THREADS;
+  __shared__ uint32_t wsum[T / 64];
+  uint32_t n = 0;
+  const int64_t stride = (int64_t)gridDim.x * T;
+  // `lanes` is a multiple of 32 and so is the stride: the 32 lanes of a tile
+  // row are in or out of the loop together (the 2-D reduction needs all 32)
+  for (int64_t t = (int64_t)blockIdx.x * T + threadIdx.x; t < lanes; t += stride) {
+    const int64_t g = t >> 5;
+    const int64_t tr = g / nkb, kb = g - tr * nkb;
+    const int64_t r = 32 * tr + (t & 31);
+    const bool valid = r < rows_out;
+    float x[32];
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = clip_load1<BF16>(src, (32 * kb + i) * ld + r);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+    }
+    uint32_t m = clip_prepare<RHT>(x, mask);
+    if (TWO_D) {
+#pragma unroll
+      for (int d = 1; d < 32; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 32));
+    }
+    if (valid) n += clip_block<ELEM>(x, m, scale_mode);
+  }
+  clip_commit<T>(n, wsum, count);
+}
+
+template <int ELEM, bool BF16, bool RHT>
+hipError_t launch_clip3(const ClipArgs& a, hipStream_t st) {
   const int64_t rows_out = a.dim0 ? a.C : a.R, K = a.dim0 ? a.R : a.C;
   const int64_t nkb = K / 32;
-  const int64_t lanes = (rows_out + 31) / 32 * nkb * 32;
-  const int64_t groups = (lanes + CLIP_THREADS - 1) / CLIP_THREADS;
-  const unsigned grid = (unsigned)(groups < CLIP_MAX_GROUPS ? groups : CLIP_MAX_GROUPS);
-  if (a.rht)
-    hipLaunchKernelGGL((k_clip_count<ELEM, BF16, DIM0, TWO_D, true>), dim3(grid), dim3(CLIP_THREADS), 0, st, a.src,
-                       a.ld_src, rows_out, nkb, lanes, a.mask, a.scale_mode, a.count);
-  else
-    hipLaunchKernelGGL((k_clip_count<ELEM, BF16, DIM0, TWO_D, false>), dim3(grid), dim3(CLIP_THREADS), 0, st, a.src,
-                       a.ld_src, rows_out, nkb, lanes, a.mask, a.scale_mode, a.count);
+  auto grid_for = [](int64_t work, int cap) { return (unsigned)(work < cap ? (work > 0 ? work : 1) : cap); };
+  constexpr int TS = CLIP_STREAM_THREADS, TT = CLIP_TILE_THREADS;
+  if (!a.dim0 && !a.two_d) {
+    hipLaunchKernelGGL((k_clip_rows<ELEM, BF16, RHT>), dim3(grid_for((rows_out * nkb + TS - 1) / TS, CLIP_STREAM_GROUPS)),
+                       dim3(TS), 0, st, a.src, a.ld_src, rows_out, nkb, a.mask, a.scale_mode, a.count);
+  } else if (!a.dim0) {
+    hipLaunchKernelGGL((k_clip_rows_2d<ELEM, BF16, RHT>),
+                       dim3(grid_for(rows_out / 32 * ((nkb + TT / 32 - 1) / (TT / 32)), CLIP_TILE_GROUPS)), dim3(TT),
+                       0, st, a.src, a.ld_src, rows_out, nkb, a.mask, a.scale_mode, a.count);
+  } else {
+    const int64_t lanes = (rows_out + 31) / 32 * nkb * 32;
+    const unsigned grid = grid_for((lanes + TS - 1) / TS, CLIP_STREAM_GROUPS);
+    if (a.two_d)
+      hipLaunchKernelGGL((k_clip_dim0<ELEM, BF16, true, RHT>), dim3(grid), dim3(TS), 0, st, a.src, a.ld_src,
+                         rows_out, nkb, lanes, a.mask, a.scale_mode, a.count);
+    else
+      hipLaunchKernelGGL((k_clip_dim0<ELEM, BF16, false, RHT>), dim3(grid), dim3(TS), 0, st, a.src, a.ld_src,
+                         rows_out, nkb, lanes, a.mask, a.scale_mode, a.count);
+  }
   return hipGetLastError();
 }
 
 template <int ELEM>
 hipError_t launch_clip_elem(const ClipArgs& a, hipStream_t st) {
-  if (a.bf16) {
-    if (a.dim0) return a.two_d ? launch_clip4<ELEM, true, true, true>(a, st) : launch_clip4<ELEM, true, true, false>(a, st);
-    return a.two_d ? launch_clip4<ELEM, true, false, true>(a, st) : launch_clip4<ELEM, true, false, false>(a, st);
-  }
-  if (a.dim0) return a.two_d ? launch_clip4<ELEM, false, true, true>(a, st) : launch_clip4<ELEM, false, true, false>(a, st);
-  return a.two_d ? launch_clip4<ELEM, false, false, true>(a, st) : launch_clip4<ELEM, false, false, false>(a, st);
+  if (a.bf16) return a.rht ? launch_clip3<ELEM, true, true>(a, st) : launch_clip3<ELEM, true, false>(a, st);
+  return a.rht ? launch_clip3<ELEM, false, true>(a, st) : launch_clip3<ELEM, false, false>(a, st);
 }
 
 }  // namespace
