@@ -358,3 +358,20 @@ def test_grouped_gemm_elements_more_tiles_than_cus(fa, fb, b_block):
     tol = 1e-5 * bound + bf16_half_ulp(np.maximum(np.abs(got[:last]), np.abs(ref)))
     assert np.all(np.abs(got[:last] - ref) <= tol)
     assert np.all(got[last:] == 7.0)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m3", "e3m2")])
+def test_gemm_elements_zero_k(fa, fb):
+    """K = 0 on the direct-to-LDS kernels (dense 300 x 544 and grouped with
+    N = 288): every output is zero (no stage is loaded or multiplied), rows
+    past the last expert offset untouched."""
+    need_gpu()
+    banner(f"gemm K=0 {fa} x {fb}")
+    y = torch.full((300, 544), 7.0, dtype=torch.float32, device="cuda")
+    mx.gemm(mx.empty_mx(300, 0, elem=fa), mx.empty_mx(544, 0, elem=fb), out=y)
+    assert np.all(host(y) == 0.0)
+    offsets = torch.tensor([0, 0, 260, 290], dtype=torch.int32, device="cuda")
+    g = torch.full((300, 288), 7.0, dtype=torch.bfloat16, device="cuda")
+    mx.grouped_gemm(mx.empty_mx(300, 0, elem=fa), offsets, mx.empty_mx(288, 0, "2d", experts=3, elem=fb), out=g)
+    gh = host(g.float())
+    assert np.all(gh[:290] == 0.0) and np.all(gh[290:] == 7.0)
