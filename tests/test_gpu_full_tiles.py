@@ -110,3 +110,30 @@ def test_moe_whole_tiles():
             lambda c: (*oracle.quantize(wn[:, c], axis="dim0", block="2d"), "2d"), f"moe expert {e}"))
     print(f"moe whole tiles (experts {big}: {sizes[big]} rows, {small}: {sizes[small]} rows): "
           f"max |err| / sum|ab| = {worst:.2e}")
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m3"])
+def test_fprop_mxfp8_mxfp6_whole_tiles(elem):
+    """The fprop shape with MXFP8 (E4M3) or MXFP6 (E2M3) operands, quantized
+    on the GPU (X along its last dim, W along dim 0, RNE): rows 4096..4351
+    against the interior tile of columns 2560..2815 and the edge tile
+    5632..5759, within the float32 bound plus the scaled MFMA's
+    internal-precision allowance for FP8/FP6 operands and half a bf16 ulp."""
+    need_gpu()
+    from gpu_util import bf16_half_ulp, mx_group_bound
+    x, w = workloads.fprop()
+    banner(f"fprop {elem} whole tiles")
+    qx = mx.quantize(x.cuda(), elem=elem)
+    qw = mx.quantize(w.cuda(), axis="dim0", elem=elem)
+    y = host(mx.gemm(qx, qw, torch.bfloat16).float()).astype(np.float64)
+    xn, wn = x.float().numpy(), w.float().numpy()
+    rows = np.arange(4096, 4352)
+    ac, as_ = oracle.quantize(xn[rows], elem=elem)
+    av = oracle.gemm.dequant_f64(ac, as_, elem)
+    for cols in (np.arange(2560, 2816), np.arange(5632, 5760)):
+        bc, bs = oracle.quantize(wn[:, cols], axis="dim0", elem=elem)
+        ref, bound = oracle.gemm_ref(ac, as_, bc, bs, a_elem=elem, b_elem=elem)
+        got = y[np.ix_(rows, cols)]
+        tol = 1e-5 * bound + mx_group_bound(av, oracle.gemm.dequant_f64(bc, bs, elem))
+        tol = tol + bf16_half_ulp(np.maximum(np.abs(got), np.abs(ref)))
+        assert np.all(np.abs(got - ref) <= tol), f"{elem} cols {cols[0]}..{cols[-1]}"
