@@ -192,11 +192,21 @@ def test_gemm_elements(fa, fb, M, N, K, b_block, out):
     ref, bound = oracle.gemm_ref(ac, as_, bc, bs, "1d", b_block, a_elem=fa, b_elem=fb)
     av = oracle.gemm.dequant_f64(ac, as_, fa)
     bv = oracle.gemm.dequant_f64(bc, bs, fb, b_block)
-    tol = 1e-5 * bound + mx_group_bound(av, bv)
+    gb = mx_group_bound(av, bv)
+    tol = 1e-5 * bound + gb
     if out == torch.bfloat16:
         tol = tol + bf16_half_ulp(np.maximum(np.abs(c), np.abs(ref)))
     err = np.abs(c - ref)
     assert np.all(err <= tol), float(np.max(err / tol))
+    if out == torch.float32 and fa + fb != "e2m1e2m1":
+        # the error beyond the float32 accumulation bound, as a fraction of
+        # the instruction's alignment allowance: the truncation is real (the
+        # allowance is used) but stays well inside it; on these seeded cases
+        # (deterministic results) it reaches 0.43 (e2m3 x e4m3, K = 800)
+        excess = np.maximum(err - 1e-5 * bound, 0.0)
+        ratio = float(np.max(excess / np.maximum(gb, 1e-300)))
+        print(f"[excess/allowance] {fa} x {fb} M={M} N={N} K={K}: {ratio:.4f}")
+        assert ratio <= 0.5, ratio
 
 
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m3", "e3m2")])
