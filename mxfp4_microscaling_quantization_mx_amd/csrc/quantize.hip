@@ -297,8 +297,9 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
 
 // ------------------------------------------------------------------ columns (blocks along dim 0)
 // Blocks along dim 0 without an LDS input tile: lane = source column (= output
-// row); the 8 waves of a workgroup take the 16 K-blocks [16 y, 16 y + 16) of
-// its 64 columns (512 source rows), two each.  Each of the 32 loads of a block
+// row); the 16 waves of a workgroup take the 16 K-blocks [16 y, 16 y + 16) of
+// its 64 columns (512 source rows), one each (two blocks per wave in turn
+// measured 5-12 % slower: half the loads in flight).  Each of the 32 loads of a block
 // reads one element per lane; across the wave it reads 64 consecutive columns
 // of one source row.  The blocks go through the same register path as a row
 // block.  Their codes and scale bytes are gathered in LDS, so that each output
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src
 // holds one 32x32 tile (output rows are a multiple of 32, so half-waves are
 // whole or past the end).
 constexpr int COLS_KB = 16;                   // K-blocks per workgroup of the dim-0 kernel
-constexpr int COLS_THREADS = 64 * COLS_KB / 2;  // two K-blocks per wave
+constexpr int COLS_THREADS = 64 * COLS_KB;    // one K-block per wave
 
 template <bool TWO_D, bool BF16, bool RHT, int SR, int ELEM>
 __global__ __launch_bounds__(COLS_THREADS) void k_quant_cols(const void* __restrict__ src, int64_t R, int64_t C,
@@ -332,11 +333,9 @@ __global__ __launch_bounds__(COLS_THREADS) void k_quant_cols(const void* __restr
   // lanes past the last column read the last column (their blocks are never
   // stored; for 2-D they form whole half-waves of their own)
   const uint32_t voff = (uint32_t)((col < C ? col : C - 1) * ES);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int kl = 2 * w + h;
-    const int64_t kb = kb0 + kl;
-    if (kb >= nkb) break;                    // wave-uniform
+  const int kl = w;                          // this wave's K-block
+  const int64_t kb = kb0 + kl;
+  if (kb < nkb) {                            // wave-uniform
     // a raw buffer over the block's 32 source rows: per-lane column offset,
     // wave-uniform row offsets
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
