@@ -190,7 +190,8 @@ class Workload:
         of the MoE front end (the step uses the scatter form: each token row
         quantized once and stored to its 4 routed rows, the same bytes), and
         the MoE grouped product quantized in its epilogue and with MXFP8
-        operands, and the clipping
+        operands, the MXFP8 fprop product quantized to MXFP4 in its epilogue,
+        and the clipping
         statistic of the fprop activation's quantization (reads X once)."""
         t_bytes = 2 * (2880 * 5760 // 2 + (2880 // 32) * (5760 // 32))
         q = quant_bytes(16384, 2880)
@@ -216,6 +217,8 @@ class Workload:
             ("mxfp6_quantize_x", lambda: mx.quantize(self.fx, out=self.e6_qx), "hbm",
              quant_bytes(16384, 2880, out_bits=6)),
             ("mxfp6_gemm", lambda: mx.gemm(self.e6_qx, self.e6_qw, out=self.e_y), "mfma", 2 * 16384 * 5760 * 2880),
+            ("mxfp8_gemm_quantize_y", lambda: mx.gemm_quantize(self.e8_qx, self.e8_qw, out=self.g_qy), "mfma8",
+             2 * 16384 * 5760 * 2880),
             ("fused_gemm_quantize_y", lambda: mx.gemm_quantize(self.f_qx, self.f_qw, out=self.g_qy), "mfma",
              2 * 16384 * 5760 * 2880),
             ("unfused_quantize_y", lambda: mx.quantize(self.f_y, out=self.g_qy2), "hbm", quant_bytes(16384, 5760)),

@@ -303,9 +303,13 @@ mx_status mx_gemm(const mx_tensor* A, const mx_tensor* B, void* C, int32_t c_dty
  * RNE, no transform and the given scale mode: the result equals mx_gemm with
  * float32 output followed by mx_quantize of that output along its last dim.
  *
- *   A, B        host structs of device buffers, MXFP4 (E2M1), A->K == B->K,
- *               1-D or 2-D scales, scale rows 16-byte aligned with a stride
- *               that is a multiple of 16; codes under 2 GiB.
+ *   A, B        host structs of device buffers, A->K == B->K, 1-D or 2-D
+ *               scales: both MXFP4 (E2M1; scale rows 16-byte aligned with a
+ *               stride that is a multiple of 16; codes under 2 GiB), or both
+ *               MXFP8 / MXFP6 of any pair of E4M3, E5M2, E2M3, E3M2 ("MXFP4",
+ *               AI Wiki, §Place in the MX family; scale rows 4-byte aligned
+ *               with a stride that is a multiple of 4, 256 code rows under
+ *               2 GiB); one MXFP4 and one other type: MX_ERR_UNSUPPORTED.
  *   scale_mode  an mx_scale_mode.
  *   out         host struct of device buffers: rows = M = A->rows, K = N =
  *               B->rows (a multiple of 32), MX_BLOCK_1D, MX_ELEM_E2M1; codes

@@ -990,8 +990,11 @@ __device__ __forceinline__ void f8_read(uint32_t row, int key, int ks, int hi, v
 }
 
 // Multiply the stage held in (slot, sl: LDS byte addresses of its codes and
-// scale words): 2 steps of 8 MFMAs per wave.
-template <int FA, int FB>
+// scale words): 2 steps of 8 MFMAs per wave.  SWAP issues every MFMA with the
+// operands (and their formats and scales) exchanged, so that tile (i, j)
+// accumulates its transpose: each lane then holds 16 columns of one output
+// row, the layout of the quantizing epilogue.
+template <int FA, int FB, bool SWAP = false>
 __device__ __forceinline__ void f8_compute(v16f acc[2][4], uint32_t slot, uint32_t sl, int s, int K, int wm, int wn,
                                            int l32, int hi) {
   // blocks of this stage below K; the scale bytes of the others (row padding)
@@ -1032,12 +1035,21 @@ __device__ __forceinline__ void f8_compute(v16f acc[2][4], uint32_t slot, uint32
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (ks == 0)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], mfma_fmt<FA>(),
-                                                                       mfma_fmt<FB>(), 0, sa[i], 0, sb[j]);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], mfma_fmt<FA>(),
-                                                                       mfma_fmt<FB>(), 2, sa[i], 2, sb[j]);
+        if constexpr (SWAP) {
+          if (ks == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], mfma_fmt<FB>(),
+                                                                         mfma_fmt<FA>(), 0, sb[j], 0, sa[i]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], mfma_fmt<FB>(),
+                                                                         mfma_fmt<FA>(), 2, sb[j], 2, sa[i]);
+        } else {
+          if (ks == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], mfma_fmt<FA>(),
+                                                                         mfma_fmt<FB>(), 0, sa[i], 0, sb[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], mfma_fmt<FA>(),
+                                                                         mfma_fmt<FB>(), 2, sa[i], 2, sb[j]);
+        }
       }
   }
 }
@@ -1047,9 +1059,14 @@ __device__ __forceinline__ void f8_compute(v16f acc[2][4], uint32_t slot, uint32
 // row tiles), and the stage sequence runs on across tiles: the next tile's
 // first stage loads into the free slot while the current tile's last stage is
 // multiplied and its result stored.
-template <int FA, int FB, bool OUT_BF16, class Sched>
+// OUT: 0 float32, 1 bf16, 2 the quantizing epilogue (MXFP4 codes and scale
+// bytes along N into qo, from the swapped-operand accumulators).
+template <int FA, int FB, int OUT, class Sched>
 __device__ __forceinline__ void run_f8(const Sched& sc, const MxOperand& A, const MxOperand& B, int K, void* C,
-                                       int64_t ldc, int a_2d, int b_2d, uint8_t* slots, uint32_t* sws) {
+                                       int64_t ldc, int a_2d, int b_2d, uint8_t* slots, uint32_t* sws,
+                                       const t256::QOut& qo = t256::QOut{}) {
+  constexpr bool OUT_BF16 = OUT == 1;
+  constexpr bool SWAP = OUT == 2;
   const int ntiles = sc.count();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1120,13 +1137,22 @@ __device__ __forceinline__ void run_f8(const Sched& sc, const MxOperand& A, cons
         setup(j + 1, L, c0n, n0n, mln, nln);
         f8_issue<FA, FB>(L, 0, K, slots + nx * f8::SLOT, sws + nx * f8::SWORDS, wave);
       }
-      f8_compute<FA, FB>(acc.t, a_slots + (uint32_t)((g & 1) * f8::SLOT), a_sws + (uint32_t)((g & 1) * 4 * f8::SWORDS),
-                         s, K, wm, wn, l32, hi);
+      f8_compute<FA, FB, SWAP>(acc.t, a_slots + (uint32_t)((g & 1) * f8::SLOT),
+                               a_sws + (uint32_t)((g & 1) * 4 * f8::SWORDS), s, K, wm, wn, l32, hi);
     }
     // epilogue: the 256x256 kernels' bounds-checked store path (same wave
-    // layout and MFMA tiles)
-    constexpr int ES = OUT_BF16 ? 2 : 4;
-    t256::store_tile<OUT_BF16>(acc, static_cast<uint8_t*>(C) + (c0 * ldc + n0) * ES, (int)ldc, mlim, nlim);
+    // layout and MFMA tiles), or their quantizing epilogue
+    if constexpr (SWAP) {
+      t256s::Acc q;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) q.t[i][jj] = acc.t[i][jj];
+      t256s::store_tile_mx(q, qo, (int)c0, n0, mlim, nlim);
+    } else {
+      constexpr int ES = OUT_BF16 ? 2 : 4;
+      t256::store_tile<OUT_BF16>(acc, static_cast<uint8_t*>(C) + (c0 * ldc + n0) * ES, (int)ldc, mlim, nlim);
+    }
     if (j + 1 < ntiles) {
       if (nst == 0) setup(j + 1, L, c0n, n0n, mln, nln);
       c0 = c0n;
@@ -1145,6 +1171,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_f8(MxOperand A, MxOperand B, in
   const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
                       XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
   run_f8<FA, FB, OUT_BF16>(sc, A, B, K, C, ldc, a_2d, b_2d, slots, sws);
+}
+
+// The dense MXFP8 / MXFP6 product quantized along N in the epilogue (MXFP4
+// codes and scale bytes; the operands swapped in every MFMA).
+template <int FA, int FB>
+__global__ __launch_bounds__(512, 1) void k_gemm_f8_q(MxOperand A, MxOperand B, int M, int N, int K, t256::QOut qo,
+                                                     int a_2d, int b_2d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slots[2 * f8::SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t sws[2 * f8::SWORDS];
+  const DenseSched sc{A.codes, A.scales, B.codes, B.scales, M, N, tiles_m, tiles_n,
+                      XcdShare((int)blockIdx.x, (int)gridDim.x, tiles_m * tiles_n)};
+  run_f8<FA, FB, 2>(sc, A, B, K, nullptr, 0, a_2d, b_2d, slots, sws, qo);
 }
 
 // Grouped (MoE) form: the expert table and the schedule of the MXFP4 grouped
@@ -1351,10 +1389,50 @@ hipError_t launch_gemm_qa(const GemmQaArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int FA, int FB>
+hipError_t launch_gemm_f8_q(const GemmQuantArgs& a, const t256::QOut& qo, unsigned nwg, int tiles_m, int tiles_n,
+                            hipStream_t st) {
+  hipLaunchKernelGGL((k_gemm_f8_q<FA, FB>), dim3(nwg), dim3(512), 0, st, a.A, a.B, (int)a.M, (int)a.N, (int)a.K, qo,
+                     (int)a.a_2d, (int)a.b_2d, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int FA>
+hipError_t launch_gemm_f8_q_b(const GemmQuantArgs& a, const t256::QOut& qo, unsigned nwg, int tiles_m, int tiles_n,
+                              hipStream_t st) {
+  switch (a.b_elem) {
+    case 1: return launch_gemm_f8_q<FA, 1>(a, qo, nwg, tiles_m, tiles_n, st);
+    case 2: return launch_gemm_f8_q<FA, 2>(a, qo, nwg, tiles_m, tiles_n, st);
+    case 3: return launch_gemm_f8_q<FA, 3>(a, qo, nwg, tiles_m, tiles_n, st);
+    case 4: return launch_gemm_f8_q<FA, 4>(a, qo, nwg, tiles_m, tiles_n, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_gemm_f8_q_a(const GemmQuantArgs& a, const t256::QOut& qo, unsigned nwg, int tiles_m, int tiles_n,
+                              hipStream_t st) {
+  switch (a.a_elem) {
+    case 1: return launch_gemm_f8_q_b<1>(a, qo, nwg, tiles_m, tiles_n, st);
+    case 2: return launch_gemm_f8_q_b<2>(a, qo, nwg, tiles_m, tiles_n, st);
+    case 3: return launch_gemm_f8_q_b<3>(a, qo, nwg, tiles_m, tiles_n, st);
+    case 4: return launch_gemm_f8_q_b<4>(a, qo, nwg, tiles_m, tiles_n, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 bool gemm_quantize_supported(const GemmQuantArgs& a) {
   const bool out_ok = a.M >= 256 && a.N >= 256 && a.N % 32 == 0 && a.ld_codes % 4 == 0 &&
                       (uintptr_t)a.codes % 4 == 0 && 256 * a.ld_codes < (1ll << 31) &&
                       256 * a.ld_scales < (1ll << 31) && a.ld_codes >= a.N / 2 && a.ld_scales >= a.N / 32;
+  if (a.a_elem != 0 || a.b_elem != 0) {
+    // MXFP8 / MXFP6 operands (both): the direct-to-LDS kernel's conditions
+    const bool types = a.a_elem >= 1 && a.a_elem <= 4 && a.b_elem >= 1 && a.b_elem <= 4;
+    const bool words = a.A.ld_scales % 4 == 0 && a.B.ld_scales % 4 == 0 && (uintptr_t)a.A.scales % 4 == 0 &&
+                       (uintptr_t)a.B.scales % 4 == 0;
+    const bool small = 256 * a.A.ld_codes < (1ll << 31) && 256 * a.B.ld_codes < (1ll << 31) &&
+                       a.M < (1ll << 31) && a.N < (1ll << 31) && a.K < (1ll << 30);
+    return out_ok && types && words && small;
+  }
   if (a.K == 0) return out_ok;   // the operands are never read
   return out_ok && a.A.ld_scales % 16 == 0 && a.B.ld_scales % 16 == 0 && (uintptr_t)a.A.scales % 16 == 0 &&
          (uintptr_t)a.B.scales % 16 == 0 && a.M * a.A.ld_codes < (1ll << 31) && a.N * a.B.ld_codes < (1ll << 31) &&
@@ -1369,6 +1447,7 @@ hipError_t launch_gemm_quantize(const GemmQuantArgs& a, hipStream_t st) {
   const int cus = cu_count();
   const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
   const t256::QOut qo{a.codes, a.scales, (int)a.ld_codes, (int)a.ld_scales, a.scale_mode};
+  if (a.a_elem != 0 || a.b_elem != 0) return launch_gemm_f8_q_a(a, qo, nwg, tiles_m, tiles_n, st);
 #define MX_GQ(A_, B_)                                                                                   \
   hipLaunchKernelGGL((k_gemm256_q<A_, B_>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, (int)a.M, (int)a.N, \
                      (int)a.K, qo, tiles_m, tiles_n)

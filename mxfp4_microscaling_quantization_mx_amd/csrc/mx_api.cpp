@@ -513,8 +513,9 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale
   if (out->rows != M || out->K != N)
     return fail(MX_ERR_INVALID_ARG, "mx_gemm_quantize: out is [%lld, %lld], the product is [%lld, %lld]",
                 (long long)out->rows, (long long)out->K, (long long)M, (long long)N);
-  if (A->elem != MX_ELEM_E2M1 || B->elem != MX_ELEM_E2M1 || out->elem != MX_ELEM_E2M1)
-    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_quantize: MXFP4 operands and output only");
+  if (out->elem != MX_ELEM_E2M1) return fail(MX_ERR_UNSUPPORTED, "mx_gemm_quantize: the output is MXFP4");
+  if ((A->elem == MX_ELEM_E2M1) != (B->elem == MX_ELEM_E2M1))
+    return fail(MX_ERR_UNSUPPORTED, "mx_gemm_quantize: both operands MXFP4, or both MXFP8 / MXFP6");
   if (out->block != MX_BLOCK_1D)
     return fail(MX_ERR_UNSUPPORTED, "mx_gemm_quantize: the output uses 1-D blocks");
   if (M == 0 || N == 0) return MX_OK;
@@ -531,6 +532,8 @@ mx_status mx_gemm_quantize(const mx_tensor* A, const mx_tensor* B, int32_t scale
   a.ld_codes = out->ld_codes;
   a.ld_scales = out->ld_scales;
   a.scale_mode = scale_mode;
+  a.a_elem = A->elem;
+  a.b_elem = B->elem;
   if (!mx::gemm_quantize_supported(a))
     return fail(MX_ERR_UNSUPPORTED,
                 "mx_gemm_quantize: needs M, N >= 256, operand scale rows 16-byte aligned with strides %% 16 == 0, "

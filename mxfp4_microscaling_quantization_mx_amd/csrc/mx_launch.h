@@ -66,6 +66,7 @@ struct GemmQuantArgs {
   uint8_t* scales;
   int64_t ld_codes, ld_scales;
   int scale_mode;
+  int a_elem = 0, b_elem = 0;  // mx_elem of A and B (E2M1, or both MXFP8 / MXFP6)
 };
 
 // C = Q(A) B^T with A bf16 [M, K] (row stride lda elements) quantized to

@@ -113,7 +113,8 @@ def save_npz(name, **arrays):
         np.savez(os.path.join(OUT_DIR, name), **arrays)
 
 
-def check_quantized_product(codes, scales, ref, sum_abs, K, scale_mode="floor", what="quantized product"):
+def check_quantized_product(codes, scales, ref, sum_abs, K, scale_mode="floor", what="quantized product",
+                            extra=None):
     """MXFP4 codes/scales quantized on the GPU from its float32 GEMM product
     against the oracle's float64 product `ref` (both [R, N], N a multiple of
     32), without feeding any GPU value to the oracle.  The float32 product
@@ -124,9 +125,13 @@ def check_quantized_product(codes, scales, ref, sum_abs, K, scale_mode="floor", 
     within that error of max |ref|, and each code the oracle's RNE code of
     some value within that error of ref at the GPU's scale (times 3/4 in the
     prescale mode).  Where no boundary lies inside the error, that leaves
-    exactly the oracle's answer."""
+    exactly the oracle's answer.  `extra` (per element) widens the error for
+    FP8 / FP6 operands by the matrix instruction's alignment allowance
+    (mx_group_bound)."""
     import oracle
     bound = (2 * -(-K // 64) + 1) * 2.0 ** -24 * np.asarray(sum_abs, dtype=np.float64)
+    if extra is not None:
+        bound = bound + np.asarray(extra, dtype=np.float64)
     R, N = ref.shape
     nb = N // 32
     s = np.asarray(scales, dtype=np.int64)[:, :nb]
