@@ -423,10 +423,11 @@ mx_status mx_grouped_gemm(const mx_tensor* A, const int32_t* d_group_offsets, in
  * float32 or bf16).  Equal to mx_grouped_gemm with float32 output followed by
  * mx_quantize of the rows it writes (RNE, no transform, the given scale mode).
  *
- *   A, d_group_offsets, E, B, expert strides: as mx_grouped_gemm; MXFP4
- *               operands, N = B->rows >= 256 and a multiple of 32, scale rows
- *               16-byte aligned with strides (and the expert scale stride) a
- *               multiple of 16, E <= 960.
+ *   A, d_group_offsets, E, B, expert strides: as mx_grouped_gemm; N =
+ *               B->rows >= 256 and a multiple of 32, E <= 960; both operands
+ *               MXFP4 (scale rows 16-byte aligned with strides, and the expert
+ *               scale stride, a multiple of 16), or both MXFP8 / MXFP6 of any
+ *               pair of E4M3, E5M2, E2M3, E3M2 (the same with 4 for 16).
  *   scale_mode  an mx_scale_mode.
  *   out         host struct of device buffers: rows = A->rows, K = N, 1-D,
  *               MXFP4.  Rows past off[E] are not written.

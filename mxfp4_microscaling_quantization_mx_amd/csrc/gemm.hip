@@ -1206,6 +1206,26 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm_f8(MxOperand A, MxOpera
   run_f8<FA, FB, OUT_BF16>(sc, A, B, K, C, ldc, 0, b_2d, slots, sws);
 }
 
+// The grouped MXFP8 / MXFP6 product quantized along N in the epilogue.
+template <int FA, int FB>
+__global__ __launch_bounds__(512, 1) void k_grouped_gemm_f8_q(MxOperand A, MxOperand B, int64_t M_cap, int N, int K,
+                                                             const int32_t* __restrict__ offsets, int E,
+                                                             int64_t stride_codes, int64_t stride_scales,
+                                                             t256::QOut qo, int b_2d, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slots[2 * f8::SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t sws[2 * f8::SWORDS];
+  __shared__ int tab[3 * GG_EMAX + 1];
+  __shared__ GroupedParams prm;
+  build_expert_table(offsets, E, M_cap, tab);   // ends with a barrier
+  const int total_slots = tab[E];
+  if (threadIdx.x == 0)
+    prm = GroupedParams{A.codes, A.scales, B.codes, B.scales, stride_codes, stride_scales, (int)A.ld_codes,
+                        (int)A.ld_scales, N, tiles_n, E, total_slots, 0, 0};
+  __syncthreads();
+  const GroupedSched sc{&prm, tab, XcdShare((int)blockIdx.x, (int)gridDim.x, total_slots * tiles_n)};
+  run_f8<FA, FB, 2>(sc, A, B, K, nullptr, 0, 0, b_2d, slots, sws, qo);
+}
+
 template <int FA, int FB>
 hipError_t launch_grouped_gemm_mx(const GroupedGemmArgs& a, hipStream_t st, int cus) {
   if constexpr (FA >= 1 && FA <= 4 && FB >= 1 && FB <= 4) {
@@ -1457,8 +1477,42 @@ hipError_t launch_gemm_quantize(const GemmQuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int FA, int FB>
+hipError_t launch_grouped_f8_q(const GroupedQuantArgs& q, const t256::QOut& qo, unsigned nwg, int tiles_n,
+                               hipStream_t st) {
+  const GroupedGemmArgs& a = q.g;
+  hipLaunchKernelGGL((k_grouped_gemm_f8_q<FA, FB>), dim3(nwg), dim3(512), 0, st, a.A, a.B, a.M_cap, (int)a.N,
+                     (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, qo, (int)a.b_2d, tiles_n);
+  return hipGetLastError();
+}
+
+template <int FA>
+hipError_t launch_grouped_f8_q_b(const GroupedQuantArgs& q, const t256::QOut& qo, unsigned nwg, int tiles_n,
+                                 hipStream_t st) {
+  switch (q.g.b_elem) {
+    case 1: return launch_grouped_f8_q<FA, 1>(q, qo, nwg, tiles_n, st);
+    case 2: return launch_grouped_f8_q<FA, 2>(q, qo, nwg, tiles_n, st);
+    case 3: return launch_grouped_f8_q<FA, 3>(q, qo, nwg, tiles_n, st);
+    case 4: return launch_grouped_f8_q<FA, 4>(q, qo, nwg, tiles_n, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
 bool grouped_quantize_supported(const GroupedQuantArgs& q) {
   const GroupedGemmArgs& a = q.g;
+  if (a.a_elem != 0 || a.b_elem != 0) {
+    // MXFP8 / MXFP6 operands (both): the grouped direct-to-LDS kernel's conditions
+    const bool types = a.a_elem >= 1 && a.a_elem <= 4 && a.b_elem >= 1 && a.b_elem <= 4;
+    const bool words = a.A.ld_scales % 4 == 0 && a.B.ld_scales % 4 == 0 && a.stride_scales % 4 == 0 &&
+                       (uintptr_t)a.A.scales % 4 == 0 && (uintptr_t)a.B.scales % 4 == 0;
+    const bool small = 256 * a.A.ld_codes < (1ll << 31) && 256 * a.B.ld_codes < (1ll << 31) && a.N < (1ll << 31) &&
+                       a.K < (1ll << 30) && a.A.ld_codes < (1ll << 31) && a.A.ld_scales < (1ll << 31);
+    const int64_t slot_bound = (a.M_cap + 255) / 256 + a.E;
+    return types && words && small && !a.a_2d && a.N >= 256 && a.N % 32 == 0 && a.E <= GG_EMAX &&
+           slot_bound * ((a.N + 255) / 256) < (1ll << 31) && q.ld_codes % 4 == 0 && (uintptr_t)q.codes % 4 == 0 &&
+           256 * q.ld_codes < (1ll << 31) && 256 * q.ld_scales < (1ll << 31) && q.ld_codes >= a.N / 2 &&
+           q.ld_scales >= a.N / 32;
+  }
   const bool words = (a.A.ld_scales % 16 == 0) && (a.B.ld_scales % 16 == 0) && (a.stride_scales % 16 == 0) &&
                      ((uintptr_t)a.A.scales % 16 == 0) && ((uintptr_t)a.B.scales % 16 == 0);
   const int64_t slot_bound = (a.M_cap + 255) / 256 + a.E;
@@ -1479,6 +1533,15 @@ hipError_t launch_grouped_gemm_quantize(const GroupedQuantArgs& q, hipStream_t s
   const int cus = cu_count();
   const unsigned nwg = (unsigned)(tiles < cus ? tiles : cus);
   const t256::QOut qo{q.codes, q.scales, (int)q.ld_codes, (int)q.ld_scales, q.scale_mode};
+  if (a.a_elem != 0 || a.b_elem != 0) {
+    switch (a.a_elem) {
+      case 1: return launch_grouped_f8_q_b<1>(q, qo, nwg, tiles_n, st);
+      case 2: return launch_grouped_f8_q_b<2>(q, qo, nwg, tiles_n, st);
+      case 3: return launch_grouped_f8_q_b<3>(q, qo, nwg, tiles_n, st);
+      case 4: return launch_grouped_f8_q_b<4>(q, qo, nwg, tiles_n, st);
+      default: return hipErrorNotSupported;
+    }
+  }
   if (a.b_2d)
     hipLaunchKernelGGL((k_grouped_gemm256_q<true>), dim3(nwg), dim3(64 * GW), 0, st, a.A, a.B, a.M_cap, (int)a.N,
                        (int)a.K, a.offsets, a.E, a.stride_codes, a.stride_scales, qo, tiles_n);

@@ -565,8 +565,9 @@ mx_status mx_grouped_gemm_quantize(const mx_tensor* A, const int32_t* d_group_of
   if (out->rows != M || out->K != N)
     return fail(MX_ERR_INVALID_ARG, "mx_grouped_gemm_quantize: out is [%lld, %lld], the product is [%lld, %lld]",
                 (long long)out->rows, (long long)out->K, (long long)M, (long long)N);
-  if (A->elem != MX_ELEM_E2M1 || B->elem != MX_ELEM_E2M1 || out->elem != MX_ELEM_E2M1)
-    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm_quantize: MXFP4 operands and output only");
+  if (out->elem != MX_ELEM_E2M1) return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm_quantize: the output is MXFP4");
+  if ((A->elem == MX_ELEM_E2M1) != (B->elem == MX_ELEM_E2M1))
+    return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm_quantize: both operands MXFP4, or both MXFP8 / MXFP6");
   if (out->block != MX_BLOCK_1D)
     return fail(MX_ERR_UNSUPPORTED, "mx_grouped_gemm_quantize: the output uses 1-D blocks");
   if (M == 0 || N == 0) return MX_OK;
@@ -587,6 +588,8 @@ mx_status mx_grouped_gemm_quantize(const mx_tensor* A, const int32_t* d_group_of
   q.ld_codes = out->ld_codes;
   q.ld_scales = out->ld_scales;
   q.scale_mode = scale_mode;
+  q.g.a_elem = A->elem;
+  q.g.b_elem = B->elem;
   if (!mx::grouped_quantize_supported(q))
     return fail(MX_ERR_UNSUPPORTED,
                 "mx_grouped_gemm_quantize: needs N >= 256, 16-byte aligned scale rows with strides %% 16 == 0 (and "

@@ -272,3 +272,49 @@ def test_gemm_quantize_mixed_fp4_rejected():
     with pytest.raises(mx.MXError):
         mx.gemm_quantize(qa, qb, out=out)
     assert np.all(host(_full_rows(out.codes)) == 0x5A)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m3", "e5m2")])
+@pytest.mark.parametrize("N", [256, 544])
+def test_grouped_gemm_quantize_mxfp8_mxfp6(fa, fb, N):
+    """Grouped MXFP8 / MXFP6 product quantized to MXFP4 in the epilogue
+    (empty experts, a one-row expert, experts straddling row tiles): routed
+    rows equal mx_grouped_gemm (float32) + mx_quantize bit for bit and the
+    oracle's quantization of the reference within its bound plus the
+    alignment allowance; rows past the last offset keep the marker."""
+    from test_gpu_elements import _finite_codes, _pack
+    from gpu_util import to_dev
+    need_gpu()
+    rng = np.random.default_rng(zlib.crc32(f"gq{fa}{fb}{N}".encode()))
+    offsets = np.array([0, 0, 1, 300, 300, 557, 700], dtype=np.int32)
+    E, K, M = len(offsets) - 1, 224, 720
+    ac = _pack(_finite_codes(rng, fa, (M, K)), fa)
+    as_ = rng.integers(118, 136, (M, K // 32), dtype=np.uint8)
+    bc = np.stack([_pack(_finite_codes(rng, fb, (N, K)), fb) for _ in range(E)])
+    bs = rng.integers(118, 136, (E, N // 32, K // 32), dtype=np.uint8)
+    qa = mx.empty_mx(M, K, elem=fa)
+    qa.codes.copy_(to_dev(ac))
+    qa.scales.copy_(to_dev(as_))
+    qb = mx.empty_mx(N, K, "2d", experts=E, elem=fb)
+    qb.codes.copy_(to_dev(bc))
+    qb.scales.copy_(to_dev(bs))
+    off = torch.from_numpy(offsets).cuda()
+    banner(f"grouped_gemm_quantize {fa} x {fb} N={N}")
+    fused = _marked_out(M, N)
+    mx.grouped_gemm_quantize(qa, off, qb, out=fused)
+    m = int(offsets[-1])
+    y = mx.grouped_gemm(qa, off, qb, torch.float32)
+    unfused = mx.quantize(y[:m].contiguous())
+    fc, fs = host(fused.codes), host(fused.scales)
+    codes_equal(fc[:m], host(unfused.codes), "codes vs grouped_gemm + quantize")
+    codes_equal(fs[:m], host(unfused.scales), "scales vs grouped_gemm + quantize")
+    assert np.all(fc[m:] == 0x5A) and np.all(fs[m:] == 0x5A), "rows past the last offset written"
+    ref, bound = oracle.grouped_gemm_ref(ac, as_, offsets, bc, bs, "1d", "2d", rows=np.arange(m),
+                                         a_elem=fa, b_elem=fb)
+    av = oracle.gemm.dequant_f64(ac[:m], as_[:m], fa)
+    gb = np.zeros_like(bound)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            gb[lo:hi] = mx_group_bound(av[lo:hi], oracle.gemm.dequant_f64(bc[e], bs[e], fb, "2d"))
+    check_quantized_product(fc[:m], fs[:m], ref, bound, K, extra=gb, what="grouped mxfp8/6")
