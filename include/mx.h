@@ -152,7 +152,9 @@ typedef struct {
  * the lower to the upper grid point), and 1-D or 2-D (32x32) blocks.
  *
  *   src      device; R x C elements of src_dtype (mx_dtype), row stride ld_src
- *            ELEMENTS (>= C), 16-byte aligned base, ld_src a multiple of 8.
+ *            ELEMENTS (>= C); blocks along the last dim: 16-byte aligned base,
+ *            ld_src a multiple of 8; along dim 0: any element-aligned base
+ *            and stride.
  *   cfg      host; quantizer settings.
  *   out      host struct describing device buffers the caller allocated:
  *            rows = R (LAST) or C (DIM0), K = C (LAST) or R (DIM0),

@@ -112,8 +112,12 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
   if (R == 0 || C == 0) return MX_OK;
   if (!src) return fail(MX_ERR_INVALID_ARG, "mx_quantize: null src");
   if (ld_src < C) return fail(MX_ERR_INVALID_ARG, "mx_quantize: ld_src=%lld < C=%lld", (long long)ld_src, (long long)C);
-  if (!aligned(src, 16) || ld_src % 8)
-    return fail(MX_ERR_INVALID_ARG, "mx_quantize: src must be 16-byte aligned with ld_src %% 8 == 0");
+  // along the last dim the kernels read 16-byte pieces of a row; along dim 0
+  // one element per lane, so any element-aligned base and row stride will do
+  if (dim0 ? !aligned(src, src_dtype == MX_DT_BF16 ? 2 : 4) : (!aligned(src, 16) || ld_src % 8))
+    return fail(MX_ERR_INVALID_ARG,
+                dim0 ? "mx_quantize: src must be aligned to its element size"
+                     : "mx_quantize: src must be 16-byte aligned with ld_src %% 8 == 0 (blocks along the last dim)");
   if (dim0 && (R + 127) / 128 > 65535)
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize: dim-0 blocking supports at most 65535*128 source rows");
   if (dim0 && (31 * ld_src + C) * (src_dtype == MX_DT_BF16 ? 2 : 4) > (int64_t)0xFFFFFFFF)

@@ -70,6 +70,13 @@ def test_quantize_rejects_bad_arguments(lib):
     out = _tensor(32, 64)
     st = lib.mx_quantize(ctypes.c_void_p(18), 1, 32, 64, 64, ctypes.byref(cfg), ctypes.byref(out), None)
     assert st == mx.MX_ERR_INVALID_ARG and b"aligned" in lib.mx_last_error()
+    # along dim 0 any element-aligned source will do, but not a split element
+    cfg = mx.QuantCfgC(1, 0, 0, 0, 0, 0, 0, 0)
+    out = _tensor(64, 32)
+    st = lib.mx_quantize(ctypes.c_void_p(17), 1, 32, 64, 64, ctypes.byref(cfg), ctypes.byref(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"element size" in lib.mx_last_error()
+    st = lib.mx_quantize(ctypes.c_void_p(18), 0, 32, 64, 64, ctypes.byref(cfg), ctypes.byref(out), None)
+    assert st == mx.MX_ERR_INVALID_ARG and b"element size" in lib.mx_last_error()
     # 2-D blocks need rows % 32 == 0
     cfg = mx.QuantCfgC(0, 1, 0, 0, 0, 0, 0, 0)
     out = _tensor(48, 64, block=1)

@@ -144,6 +144,31 @@ def test_quantize_empty_and_strided():
     codes_equal(gc, oc, "codes")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("block", ["1d", "2d"])
+def test_quantize_dim0_any_row_stride(dt, block):
+    """Along dim 0 the kernel reads one element per lane, so an odd width, an
+    odd row stride and a base offset by a few elements are all accepted:
+    224 x 261 contiguous, and columns 3..259 of a 224 x 300 tensor (256
+    output rows for the 2-D tiles), bit-exact against the oracle with the
+    transform and stochastic rounding."""
+    need_gpu()
+    rng = np.random.default_rng(17)
+    banner(f"quantize dim0 any row stride {dt} {block}")
+    wide = (rng.standard_t(3, (224, 300)) * 3).astype(np.float32)
+    cases = [(wide[:, :261], torch.from_numpy(np.ascontiguousarray(wide[:, :261])).to(dt).cuda())]
+    full = torch.from_numpy(wide).to(dt).cuda()
+    cases.append((wide[:, 3:259], full[:, 3:259]))
+    for xn, xd in cases:
+        if block == "2d" and xn.shape[1] % 32:
+            continue
+        kw = dict(axis="dim0", block=block, rounding="sr", rht_mask=0x2468ACE1, seed=99, offset=1)
+        q = mx.quantize(xd, **kw)
+        oc, os_ = oracle.quantize(torch.from_numpy(np.ascontiguousarray(xn)).to(dt).float().numpy(), **kw)
+        codes_equal(host(q.scales), os_, "scales")
+        codes_equal(host(q.codes), oc, "codes")
+
+
 def test_quantize_invalid_args_raise():
     need_gpu()
     x = torch.zeros((32, 48), dtype=torch.float32, device="cuda")
