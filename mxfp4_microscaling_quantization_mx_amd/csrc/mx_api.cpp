@@ -177,8 +177,11 @@ mx_status mx_clip_count(const void* src, int32_t src_dtype, int64_t R, int64_t C
   if (R == 0 || C == 0) return MX_OK;
   if (!src) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: null src");
   if (ld_src < C) return fail(MX_ERR_INVALID_ARG, "mx_clip_count: ld_src=%lld < C=%lld", (long long)ld_src, (long long)C);
-  if (!aligned(src, 16) || ld_src % 8)
-    return fail(MX_ERR_INVALID_ARG, "mx_clip_count: src must be 16-byte aligned with ld_src %% 8 == 0");
+  // (along dim 0 the kernel reads one element per lane, as the quantizer does)
+  if (dim0 ? !aligned(src, src_dtype == MX_DT_BF16 ? 2 : 4) : (!aligned(src, 16) || ld_src % 8))
+    return fail(MX_ERR_INVALID_ARG,
+                dim0 ? "mx_clip_count: src must be aligned to its element size"
+                     : "mx_clip_count: src must be 16-byte aligned with ld_src %% 8 == 0 (blocks along the last dim)");
   mx::ClipArgs a{};
   a.src = src;
   a.R = R;

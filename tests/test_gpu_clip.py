@@ -58,6 +58,21 @@ def test_clip_count_matches_oracle(elem, axis, block, rht, mode):
             assert got > 0
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_clip_count_dim0_any_row_stride(dtype):
+    """Along dim 0 an odd width and a column view offset by a few elements are
+    accepted (one element per lane) and counted as the oracle counts them."""
+    need_gpu()
+    x = _data(zlib.crc32(b"clip-stride"), 96, 300)
+    full = torch.from_numpy(x).to(dtype)
+    banner(f"clip_count dim0 any row stride {dtype}")
+    for view in (full[:, :261].contiguous(), full[:, 3:259]):
+        got = int(host(mx.clip_count(view.cuda() if view.is_contiguous() else full.cuda()[:, 3:259],
+                                     axis="dim0", rht_mask=0x9E3779B9))[0])
+        want = oracle.clip_count(view.float().numpy(), axis="dim0", rht_mask=0x9E3779B9)
+        assert got == want and got > 0
+
+
 def test_clip_count_accumulates_and_splits_by_rows():
     """The count is added to `out`: two calls give twice the count, and the
     counts of row slices add up to the whole tensor's."""
