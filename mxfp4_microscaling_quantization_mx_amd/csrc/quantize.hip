@@ -18,8 +18,8 @@
 //  * k_quant_cols — blocks along dim 0 (the transposed output that wgrad and
 //    K x N weights need), 1-D or 2-D: lane = source column, 32 loads of one
 //    element per lane, each reading 64 consecutive columns across the wave.
-//  * k_quant_tile — 2-D 32x32 tiles along the contiguous dim, fed from an LDS
-//    tile so that a half-wave holds the 32 rows of a tile.
+//  * k_quant_rows_2d — 2-D 32x32 tiles along the contiguous dim: a half-wave
+//    per tile, lane l the block of its row l, loaded as in the row kernel.
 //  * k_quant_rows_scatter — the row kernel's block step once per source row,
 //    stored to each of the row's k destination rows (MoE routing, RNE).
 // For 2-D tiles the amax is a reduction over the 32 lanes of a half-wave.
@@ -225,74 +225,29 @@ __global__ __launch_bounds__(256) void k_quant_rows_1d(const void* __restrict__ 
   scales[(int64_t)row * ld_scales + kb] = (uint8_t)s;
 }
 
-// ------------------------------------------------------------------ 2-D tiles along the last dim
-// Source tile of 64 rows x 128 columns staged through LDS as float32; lane ->
-// row, wave w -> K-block w, so each half-wave holds one 32x32 tile.
-struct TileShape {
-  static constexpr int TR = 64;    // source rows per tile
-  static constexpr int TC = 128;   // source cols per tile
-  static constexpr int LD = 129;   // LDS row pitch in floats (bank-conflict free reads)
-};
-
+// ------------------------------------------------------------------ rows, 2-D
+// 32x32 tiles along the last dim straight from global memory: each half-wave
+// takes one tile and lane l of it the block of tile row l (its 32 source
+// elements in four 16-byte loads for bf16, as in the 1-D row kernel), so the
+// tile's amax is a reduction over the 32 lanes of the half-wave (the same
+// register path as the dim-0 2-D kernel).  Consecutive half-waves take
+// consecutive K-blocks of the same 32 rows, so a wave reads whole 128-byte
+// pieces of each row.  The rows are a multiple of 32 (2-D blocks).
 template <bool BF16, bool RHT, int SR, int ELEM>
-__global__ __launch_bounds__(256) void k_quant_tile(const void* __restrict__ src, int64_t R,
-                                                    int64_t C, int64_t ld_src,
-                                                    uint8_t* __restrict__ codes, int64_t ld_codes,
-                                                    uint8_t* __restrict__ scales,
-                                                    int64_t ld_scales, uint32_t mask,
-                                                    uint64_t seed, uint64_t offset, int scale_mode) {
-  using S = TileShape;
-  __shared__ float tile[S::TR * S::LD];
-
-  const int64_t r0 = (int64_t)blockIdx.y * S::TR;
-  const int64_t c0 = (int64_t)blockIdx.x * S::TC;
-
-  // Stage the tile: 8 consecutive columns per load, TC/8 loads per row.
-  constexpr int CHUNKS = S::TR * S::TC / 8;
-#pragma unroll
-  for (int it = 0; it < CHUNKS / 256; ++it) {
-    const int id = threadIdx.x + 256 * it;
-    const int tr = id / (S::TC / 8);
-    const int tc = (id % (S::TC / 8)) * 8;
-    const int64_t gr = r0 + tr, gc = c0 + tc;
-    float x[8];
-    if (gr < R && gc + 8 <= C) {
-      load8<BF16>(src, gr * ld_src + gc, x, 0u);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        x[i] = (gr < R && gc + i < C) ? load1<BF16>(src, gr * ld_src + gc + i) : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tile[tr * S::LD + tc + i] = x[i];
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  // Output coordinates of this lane's block.
-  const int64_t K = C;
-  const int64_t orow = r0 + lane;
-  const int64_t kb = c0 / 32 + w;
-  const bool valid = orow < R && kb * 32 < K;
-
+__global__ __launch_bounds__(256) void k_quant_rows_2d(const void* __restrict__ src, uint32_t ntiles, uint32_t nkb,
+                                                       int64_t ld_src, uint8_t* __restrict__ codes, int64_t ld_codes,
+                                                       uint8_t* __restrict__ scales, int64_t ld_scales, uint32_t mask,
+                                                       uint64_t seed, uint64_t offset, int scale_mode) {
+  const uint32_t t = blockIdx.x * 8u + (threadIdx.x >> 5);   // this half-wave's tile
+  if (t >= ntiles) return;                                   // whole half-waves leave together
+  const uint32_t tr = t / nkb, kb = t - tr * nkb;
+  const int64_t row = (int64_t)tr * 32 + (threadIdx.x & 31);
   float x[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    x[i] = tile[lane * S::LD + w * 32 + i];     // zeros past the source edges
-    if (RHT) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((mask >> i) & 1u) << 31));
-  }
-  // every lane takes part in the tile's amax (lanes past the edges hold zeros)
-  uint32_t packed[8];
-  uint32_t s;
-  if constexpr (ELEM == 0)
-    s = quantize_block32<RHT, SR, true>(x, packed, (uint64_t)(orow * K + kb * 32), seed, offset, scale_mode);
-  else
-    s = quantize_block32_elem<ELEM, RHT, SR, true>(x, packed, (uint64_t)(orow * K + kb * 32), seed, offset,
-                                                   scale_mode);
-  if (!valid) return;
-  store_block<ELEM>(codes + orow * ld_codes + kb * block_bytes<ELEM>(), packed);
-  if ((orow & 31) == 0) scales[(orow >> 5) * ld_scales + kb] = (uint8_t)s;
+  load32<BF16>(src, row * ld_src + 32 * (int64_t)kb, x, RHT ? mask : 0u);
+  const uint64_t p0 = ((uint64_t)row * nkb + kb) * 32u;      // output row * K + 32 kb
+  const uint32_t s = quantize_store<ELEM, RHT, SR, true>(x, codes + row * ld_codes + block_bytes<ELEM>() * kb, p0,
+                                                          seed, offset, scale_mode);
+  if ((threadIdx.x & 31) == 0) scales[(int64_t)tr * ld_scales + kb] = (uint8_t)s;
 }
 
 // ------------------------------------------------------------------ columns (blocks along dim 0)
@@ -409,18 +364,18 @@ hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
 
 template <bool BF16, int ELEM>
 hipError_t launch_tile(const QuantArgs& a, hipStream_t st) {
-  using S = TileShape;
-  dim3 grid((unsigned)((a.C + S::TC - 1) / S::TC), (unsigned)((a.R + S::TR - 1) / S::TR));
-#define MX_TILE(RHT_, SR_)                                                                   \
-  hipLaunchKernelGGL((k_quant_tile<BF16, RHT_, SR_, ELEM>), grid, dim3(256), 0, st,          \
-                     a.src, a.R, a.C, a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales,  \
-                     a.mask, a.seed, a.offset, a.scale_mode)
+  const uint32_t nkb = (uint32_t)(a.C / 32);
+  const uint32_t ntiles = (uint32_t)(a.R / 32) * nkb;
+  const unsigned grid = (ntiles + 7u) / 8u;
+#define MX_R2D(RHT_, SR_)                                                                                    \
+  hipLaunchKernelGGL((k_quant_rows_2d<BF16, RHT_, SR_, ELEM>), dim3(grid), dim3(256), 0, st, a.src, ntiles, nkb,   \
+                     a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset, a.scale_mode)
   if (a.rht) {
-    MX_SR3(MX_TILE, true);
+    MX_SR3(MX_R2D, true);
   } else {
-    MX_SR3(MX_TILE, false);
+    MX_SR3(MX_R2D, false);
   }
-#undef MX_TILE
+#undef MX_R2D
   return hipGetLastError();
 }
 
@@ -443,7 +398,7 @@ hipError_t launch_rows_1d(const QuantArgs& a, hipStream_t st) {
 }
 
 // Kernel choice for one element type: gather and 1-D last-dim blocks by rows,
-// dim 0 by columns (1-D or 2-D), 2-D last-dim tiles through LDS.
+// dim 0 by columns (1-D or 2-D), 2-D last-dim tiles by half-waves.
 template <int ELEM>
 hipError_t launch_quantize_elem(const QuantArgs& a, hipStream_t st) {
   if (a.gather) {
