@@ -252,27 +252,30 @@ __global__ __launch_bounds__(256) void k_quant_rows_2d(const void* __restrict__ 
 
 // ------------------------------------------------------------------ columns (blocks along dim 0)
 // Blocks along dim 0 without an LDS input tile: lane = source column (= output
-// row); the 16 waves of a workgroup take the 16 K-blocks [16 y, 16 y + 16) of
-// its 64 columns (512 source rows), one each (two blocks per wave in turn
+// row); the COLS_KB waves of a workgroup take the K-blocks
+// [COLS_KB y, COLS_KB (y + 1)) of its 64 columns, one each (two blocks per wave in turn
 // measured 5-12 % slower: half the loads in flight).  Each of the 32 loads of a block
 // reads one element per lane; across the wave it reads 64 consecutive columns
 // of one source row.  The blocks go through the same register path as a row
 // block.  Their codes and scale bytes are gathered in LDS, so that each output
-// row's 16 blocks (MXFP4: 256 contiguous code bytes, two cache lines, and 16
-// scale bytes) leave as whole 16-byte pieces from consecutive lanes, instead
+// row's COLS_KB blocks (MXFP4, 16 blocks: 256 contiguous code bytes, two cache
+// lines, and 16 scale bytes) leave as whole 16-byte pieces from consecutive lanes, instead
 // of every store instruction putting one 16-byte piece into each of 64 rows
 // (the bytes written drop from 1.63x to 1.06x the output).  2-D: a half-wave
 // holds one 32x32 tile (output rows are a multiple of 32, so half-waves are
 // whole or past the end).
-constexpr int COLS_KB = 16;                   // K-blocks per workgroup of the dim-0 kernel
-constexpr int COLS_THREADS = 64 * COLS_KB;    // one K-block per wave
-
-template <bool TWO_D, bool BF16, bool RHT, int SR, int ELEM>
-__global__ __launch_bounds__(COLS_THREADS) void k_quant_cols(const void* __restrict__ src, int64_t R, int64_t C,
+// COLS_KB K-blocks per workgroup, one per wave: 16, or 8 where 16 would give
+// fewer than 4 workgroups per CU (a 5760 x 2880 weight: 540 workgroups of 16
+// waves took 15.1 us after a cache-evicting read, 1080 of 8 waves 13.7 us, 2160
+// of 4 waves no better; the 16384 x 2880 activations run 0.4-1.4 us faster
+// with 16).
+template <int COLS_KB, bool TWO_D, bool BF16, bool RHT, int SR, int ELEM>
+__global__ __launch_bounds__(64 * COLS_KB) void k_quant_cols(const void* __restrict__ src, int64_t R, int64_t C,
                                                     int64_t ld_src, uint8_t* __restrict__ codes,
                                                     int64_t ld_codes, uint8_t* __restrict__ scales,
                                                     int64_t ld_scales, uint32_t mask, uint64_t seed,
                                                     uint64_t offset, int scale_mode) {
+  constexpr int COLS_THREADS = 64 * COLS_KB;
   constexpr int BB = block_bytes<ELEM>();
   constexpr int RB = COLS_KB * BB;           // code bytes of one output row here (a multiple of 16)
   constexpr int PITCH = RB + 16;             // LDS row pitch: rows start in different banks
@@ -346,13 +349,12 @@ __global__ __launch_bounds__(COLS_THREADS) void k_quant_cols(const void* __restr
   else                    \
     M_(RHT_, 0)
 
-template <bool TWO_D, bool BF16, int ELEM>
-hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)((a.C + 63) / 64), (unsigned)((a.R + 32 * COLS_KB - 1) / (32 * COLS_KB)));
-#define MX_COLS(RHT_, SR_)                                                                   \
-  hipLaunchKernelGGL((k_quant_cols<TWO_D, BF16, RHT_, SR_, ELEM>), grid, dim3(COLS_THREADS), 0, st, a.src, a.R, a.C, \
-                     a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset,      \
-                     a.scale_mode)
+template <int KB, bool TWO_D, bool BF16, int ELEM>
+hipError_t launch_cols_kb(const QuantArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)((a.C + 63) / 64), (unsigned)((a.R + 32 * KB - 1) / (32 * KB)));
+#define MX_COLS(RHT_, SR_)                                                                                      \
+  hipLaunchKernelGGL((k_quant_cols<KB, TWO_D, BF16, RHT_, SR_, ELEM>), grid, dim3(64 * KB), 0, st, a.src, a.R, a.C, \
+                     a.ld_src, a.codes, a.ld_codes, a.scales, a.ld_scales, a.mask, a.seed, a.offset, a.scale_mode)
   if (a.rht) {
     MX_SR3(MX_COLS, true);
   } else {
@@ -360,6 +362,12 @@ hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
   }
 #undef MX_COLS
   return hipGetLastError();
+}
+
+template <bool TWO_D, bool BF16, int ELEM>
+hipError_t launch_cols(const QuantArgs& a, hipStream_t st) {
+  const int64_t wg16 = ((a.C + 63) / 64) * ((a.R + 511) / 512);
+  return wg16 < 4 * 256 ? launch_cols_kb<8, TWO_D, BF16, ELEM>(a, st) : launch_cols_kb<16, TWO_D, BF16, ELEM>(a, st);
 }
 
 template <bool BF16, int ELEM>
