@@ -23,14 +23,29 @@ constexpr int TT = 128;        // tile edge in elements
 constexpr int IP = 18;         // input tile row pitch in words (16 + 2: conflict-free block reads)
 constexpr int OP = 17;         // output tile row pitch in words
 
+// Tile origin (r0, c0) of this workgroup.  Workgroups go to the 8 XCDs in
+// turn by launch index, so launch index L takes tile (L mod 8) * q + L / 8 of
+// the row-major tile order (q tiles per XCD, the first n mod 8 XCDs one
+// more): neighbouring tiles of a tile row, which read the two halves of the
+// same 128-byte input lines (MXFP4), then run on one XCD at about the same
+// time and share its L2, instead of each XCD fetching whole lines for half
+// of them.
+__device__ __forceinline__ void tile_origin(int64_t gx, int64_t n, int64_t& r0, int64_t& c0) {
+  const int64_t L = blockIdx.x, x = L & 7, base = n >> 3, rem = n & 7;
+  const int64_t T = x * base + (x < rem ? x : rem) + (L >> 3);
+  r0 = (T / gx) * TT;
+  c0 = (T % gx) * TT;
+}
+
 __global__ __launch_bounds__(256) void k_transpose_2d(const uint8_t* __restrict__ in_codes, int64_t ld_in,
                                                       const uint8_t* __restrict__ in_scales, int64_t ld_sin,
                                                       int64_t R, int64_t C, uint8_t* __restrict__ out_codes,
                                                       int64_t ld_out, uint8_t* __restrict__ out_scales,
-                                                      int64_t ld_sout) {
+                                                      int64_t ld_sout, int64_t gx, int64_t ntiles) {
   __shared__ uint32_t tin[TT * IP];
   __shared__ uint32_t tout[TT * OP];
-  const int64_t r0 = (int64_t)blockIdx.y * TT, c0 = (int64_t)blockIdx.x * TT;
+  int64_t r0, c0;
+  tile_origin(gx, ntiles, r0, c0);
   const int t = threadIdx.x;
   // 128 input rows x 4 chunks of 16 bytes (32 elements each); chunks past the
   // matrix read as zeros (R and C are multiples of 32)
@@ -103,11 +118,12 @@ __global__ __launch_bounds__(256) void k_transpose_2d_bytes(const uint8_t* __res
                                                             const uint8_t* __restrict__ in_scales, int64_t ld_sin,
                                                             int64_t R, int64_t C, uint8_t* __restrict__ out_codes,
                                                             int64_t ld_out, uint8_t* __restrict__ out_scales,
-                                                            int64_t ld_sout) {
+                                                            int64_t ld_sout, int64_t gx, int64_t ntiles) {
   constexpr int GB = BITS / 2;                     // bytes per group of 4 codes
   constexpr int PITCH = TT + 4;                    // LDS bytes per row
   __shared__ uint8_t tile[TT * PITCH];
-  const int64_t r0 = (int64_t)blockIdx.y * TT, c0 = (int64_t)blockIdx.x * TT;
+  int64_t r0, c0;
+  tile_origin(gx, ntiles, r0, c0);
   const int t = threadIdx.x;
   // unpack: 128 rows x 32 groups
   for (int id = t; id < TT * (TT / 4); id += 256) {
@@ -145,16 +161,18 @@ __global__ __launch_bounds__(256) void k_transpose_2d_bytes(const uint8_t* __res
 
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st) {
   if (a.R == 0 || a.C == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.C + TT - 1) / TT), (unsigned)((a.R + TT - 1) / TT));
+  const int64_t gx = (a.C + TT - 1) / TT, n = gx * ((a.R + TT - 1) / TT);
+  if (n > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)n);
   if (a.bits == 8) {
     hipLaunchKernelGGL(k_transpose_2d_bytes<8>, grid, dim3(256), 0, st, a.in_codes, a.ld_in, a.in_scales, a.ld_sin,
-                       a.R, a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout);
+                       a.R, a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout, gx, n);
   } else if (a.bits == 6) {
     hipLaunchKernelGGL(k_transpose_2d_bytes<6>, grid, dim3(256), 0, st, a.in_codes, a.ld_in, a.in_scales, a.ld_sin,
-                       a.R, a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout);
+                       a.R, a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout, gx, n);
   } else {
     hipLaunchKernelGGL(k_transpose_2d, grid, dim3(256), 0, st, a.in_codes, a.ld_in, a.in_scales, a.ld_sin, a.R,
-                       a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout);
+                       a.C, a.out_codes, a.ld_out, a.out_scales, a.ld_sout, gx, n);
   }
   return hipGetLastError();
 }
