@@ -162,9 +162,9 @@ typedef struct {
  *            codes 16-byte aligned with ld_codes a multiple of 16.
  *   Requires K % 32 == 0; 2-D blocks need rows % 32 == 0.  R = 0 or C = 0 is
  *   a no-op.  Reads only src, writes only out's buffers.  Size limits (else
- *   MX_ERR_UNSUPPORTED, nothing launched): last-dim 1-D at most 2^32 - 256
- *   blocks; last-dim 2-D at most 65535*64 rows; dim-0 at most 65535*128 source
- *   rows and 32 source rows spanning < 4 GiB.
+ *   MX_ERR_UNSUPPORTED, nothing launched): last dim at most 2^32 - 256
+ *   blocks; dim-0 at most 65535*128 source rows and 32 source rows spanning
+ *   < 4 GiB.
  *   Other element types (out->elem != MX_ELEM_E2M1): the same steps with that
  *   type's grid: the shared exponent is floor(log2(amax)) - emax, emax the
  *   exponent of the type's largest power of two (8 E4M3, 15 E5M2, 2 E2M3,

@@ -122,10 +122,8 @@ mx_status mx_quantize(const void* src, int32_t src_dtype, int64_t R, int64_t C, 
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize: dim-0 blocking supports at most 65535*128 source rows");
   if (dim0 && (31 * ld_src + C) * (src_dtype == MX_DT_BF16 ? 2 : 4) > (int64_t)0xFFFFFFFF)
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize: dim-0 blocking needs 32 source rows to span < 4 GiB");
-  if (!dim0 && cfg->block == MX_BLOCK_1D && R * (C / 32) > (int64_t)0xFFFFFF00)
+  if (!dim0 && R * (C / 32) > (int64_t)0xFFFFFF00)
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize: at most 2^32 - 256 blocks per call");
-  if (!dim0 && cfg->block == MX_BLOCK_2D && (R + 63) / 64 > 65535)
-    return fail(MX_ERR_UNSUPPORTED, "mx_quantize: 2-D blocking supports at most 65535*64 rows");
 
   mx::QuantArgs a{};
   a.src = src;
@@ -348,8 +346,8 @@ mx_status mx_transpose(const mx_tensor* in, const mx_tensor* out, void* stream) 
     return fail(MX_ERR_INVALID_ARG, "mx_transpose: out is [%lld, %lld], expected [%lld, %lld]", (long long)out->rows,
                 (long long)out->K, (long long)in->K, (long long)in->rows);
   if (in->rows == 0 || in->K == 0) return MX_OK;
-  if ((in->rows + 127) / 128 > 65535)
-    return fail(MX_ERR_UNSUPPORTED, "mx_transpose: at most 65535*128 input rows");
+  if (((in->rows + 127) / 128) * ((in->K + 127) / 128) > (int64_t)0x7FFFFFFF)
+    return fail(MX_ERR_UNSUPPORTED, "mx_transpose: at most 2^31 - 1 tiles of 128 x 128");
   mx::TransposeArgs a{};
   a.in_codes = in->codes;
   a.in_scales = in->scales;
