@@ -469,3 +469,27 @@ def test_quantize_scatter_moe_full_size():
     oc, os_ = oracle.quantize(xc.float().numpy()[tok[rows]])
     codes_equal(host(s.codes)[rows], oc, "sampled codes")
     codes_equal(host(s.scales)[rows], os_, "sampled scales")
+
+
+def test_quantize_2d_last_dim_past_65535_row_groups():
+    """2-D blocks along the last dim on 65536 * 64 + 32 rows, more than a grid
+    of 65535 row groups of 64 would reach (the kernel is launched on a 1-D
+    grid of tiles): 32-row bands at the start, on both sides of row
+    65535 * 64 and at the end, against the oracle with SR + RHT and the
+    global row numbers in the Philox element index."""
+    need_gpu()
+    R, C = 65536 * 64 + 32, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4194336)
+    x = torch.randn((R, C), generator=g, device="cuda").to(torch.bfloat16)
+    mask, seed = 0x5A5A1234, 99
+    banner(f"quantize 2d last-dim R={R} C={C} rht+sr")
+    q = mx.quantize(x, block="2d", rounding="sr", rht_mask=mask, seed=seed, offset=7)
+    for r0 in (0, 65535 * 64 - 32, 65535 * 64, R - 32):
+        rows = np.arange(r0, r0 + 32)
+        oc, os_ = oracle.quantize(host(x[r0:r0 + 32].float()), block="2d", rounding="sr", rht_mask=mask,
+                                  seed=seed, offset=7, row_index=rows)
+        codes_equal(host(q.codes[r0:r0 + 32]), oc, f"codes rows {r0}..")
+        codes_equal(host(q.scales[r0 // 32:r0 // 32 + 1]), os_, f"scales rows {r0}..")
+    del x, q
+    torch.cuda.empty_cache()

@@ -140,3 +140,27 @@ def test_transpose_other_element_types(elem, R, C):
     codes_equal(host(out.codes), oc, "codes")
     codes_equal(host(out.scales), os_, "scales")
     assert np.all(host(_full_rows(out.codes))[:, R * el.elem_bits(elem) // 8:] == 0x5A)
+
+
+def test_transpose_past_65535_row_tiles():
+    """A 2-D operand of 65536 * 128 + 32 rows (more row tiles than a 65535
+    grid rows could hold; the kernel runs on a 1-D grid of tiles) and 96
+    columns: sampled 256-row bands, the last one ragged, transposed against the
+    oracle's transpose of the same band, codes and scale bytes exactly."""
+    need_gpu()
+    R, C = 65536 * 128 + 32, 96
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8388640)
+    codes = torch.randint(0, 256, (R, C // 2), generator=g, device="cuda", dtype=torch.uint8)
+    scales = torch.randint(0, 256, (R // 32, C // 32), generator=g, device="cuda", dtype=torch.uint8)
+    q = mx.MXTensor(codes, scales, R, C, "2d")
+    banner(f"transpose R={R} C={C}")
+    out = _out_2d(C, R)
+    mx.transpose(q, out=out)
+    for r0 in (0, 65535 * 128 - 128, 65535 * 128, R - 160):
+        r1 = min(r0 + 256, R)
+        oc, os_ = oracle.transpose_2d(host(codes[r0:r1]), host(scales[r0 // 32:r1 // 32]))
+        codes_equal(host(out.codes[:, r0 // 2:r1 // 2]), oc, f"codes band {r0}")
+        codes_equal(host(out.scales[:, r0 // 32:r1 // 32]), os_, f"scales band {r0}")
+    del codes, scales, q, out
+    torch.cuda.empty_cache()
