@@ -185,9 +185,11 @@ hipError_t launch_dequantize_elem(const DequantArgs& a, hipStream_t st) {
   int64_t blocks = (lanes + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
   const bool small = lanes < (1ll << 32) - 256ll * 64 * 256;
+  // (with the transform this path only sees more than 2^32 - 256 blocks, so
+  // never 32-bit indices)
 #define MX_DQ(B_, I_, T_)                                                                                   \
-  if (small)                                                                                                \
-    hipLaunchKernelGGL((k_dequant<B_, I_, T_, ELEM, uint32_t>), dim3((unsigned)blocks), dim3(256), 0, st,   \
+  if (!(I_) && small)                                                                                       \
+    hipLaunchKernelGGL((k_dequant<B_, false, T_, ELEM, uint32_t>), dim3((unsigned)blocks), dim3(256), 0, st, \
                        a.codes, a.ld_codes, a.scales, a.ld_scales, a.rows, a.K, a.dst, a.ld_dst, a.mask);   \
   else                                                                                                      \
     hipLaunchKernelGGL((k_dequant<B_, I_, T_, ELEM, int64_t>), dim3((unsigned)blocks), dim3(256), 0, st,    \
