@@ -149,6 +149,37 @@ def test_dequantize_elements(elem, block):
     assert np.array_equal(gb[ok], rb[ok])
 
 
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("block", ["1d", "2d"])
+def test_dequantize_elements_inverse_rht(elem, block):
+    """The decode followed by the inverse 32-point transform (a lane per block,
+    all five butterfly stages in registers) on random code bytes and scales
+    of every element type: float32 bit-exact against the oracle's transform in
+    its fixed stage order (NaN wherever the oracle has NaN), bf16 its RNE
+    rounding."""
+    need_gpu()
+    rng = np.random.default_rng(71 + ELEMS.index(elem) + 4 * (block == "2d"))
+    R, K = 96, 224
+    cb = K * el.elem_bits(elem) // 8
+    codes = rng.integers(0, 256, (R, cb), dtype=np.uint8)
+    srows = R // 32 if block == "2d" else R
+    scales = rng.integers(110, 140, (srows, K // 32), dtype=np.uint8)
+    scales[-1, 2] = 0xFF
+    mask = 0x9E3779B9
+    q = mx.empty_mx(R, K, block, elem=elem)
+    q.codes.copy_(to_dev(codes))
+    q.scales.copy_(to_dev(scales))
+    banner(f"dequantize {elem} {block} inverse rht")
+    got = host(mx.dequantize(q, torch.float32, inverse_rht_mask=mask))
+    ref = oracle.dequantize(codes, scales, block, inverse_rht_mask=mask, elem=elem).astype(np.float32)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    gb = host(mx.dequantize(q, torch.bfloat16, inverse_rht_mask=mask).view(torch.int16)).astype(np.int64) & 0xFFFF
+    rb = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().astype(np.int64) & 0xFFFF
+    assert np.array_equal(gb[ok], rb[ok])
+
 def _finite_codes(rng, elem, shape):
     if elem == "e2m1":
         return rng.integers(0, 16, size=shape)
