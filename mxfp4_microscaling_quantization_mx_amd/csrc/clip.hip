@@ -27,6 +27,10 @@ namespace {
 // 25-28 us) and 4 workgroups of 256 per CU for the 2-D tile kernel, whose
 // barrier per unit favours smaller groups (29-31 us).
 constexpr int CLIP_STREAM_THREADS = 1024, CLIP_STREAM_GROUPS = 256;
+// the 1-D row kernel: 2 workgroups per CU (16384 x 2880 with the transform
+// 23.7 -> 22.5 us against 1 per CU; two blocks per lane and pass with both
+// loads first measured 28.5 us)
+constexpr int CLIP_ROWS_GROUPS = 512;
 constexpr int CLIP_TILE_THREADS = 256, CLIP_TILE_GROUPS = 1024;
 
 template <bool BF16>
@@ -124,16 +128,20 @@ __device__ __forceinline__ void clip_commit(uint32_t n, uint32_t* wsum, unsigned
 
 // Blocks along the rows, 1-D: lane t takes block t of the row-major block
 // order, so a wave reads 64 consecutive blocks (4 KiB of bf16) of a row.
-template <int ELEM, bool BF16, bool RHT>
+template <int ELEM, bool BF16, bool RHT, class IDX>
 __global__ __launch_bounds__(CLIP_STREAM_THREADS) void k_clip_rows(const void* __restrict__ src, int64_t ld,
-                                                                   int64_t rows, int64_t nkb, uint32_t mask,
+                                                                   int64_t rows, int64_t nkb_, uint32_t mask,
                                                                    int scale_mode, unsigned long long* count) {
   constexpr int T = CLIP_STREAM_THREADS;
   __shared__ uint32_t wsum[T / 64];
   uint32_t n = 0;
-  const int64_t total = rows * nkb, stride = (int64_t)gridDim.x * T;
-  for (int64_t b = (int64_t)blockIdx.x * T + threadIdx.x; b < total; b += stride) {
-    const int64_t r = b / nkb, kb = b - r * nkb;
+  // block indices in IDX: 32 bits while total + stride < 2^32 (a 64-bit
+  // division per block is a long VALU sequence)
+  const IDX nkb = (IDX)nkb_;
+  const IDX total = (IDX)(rows * nkb_), stride = (IDX)gridDim.x * T;
+  for (IDX b = (IDX)blockIdx.x * T + threadIdx.x; b < total; b += stride) {
+    const IDX rq = b / nkb;
+    const int64_t r = rq, kb = b - rq * nkb;
     float x[32];
 #pragma unroll
     for (int j = 0; j < 4; ++j) clip_load8<BF16>(src, r * ld + 32 * kb + 8 * j, x + 8 * j);
@@ -225,8 +233,13 @@ hipError_t launch_clip3(const ClipArgs& a, hipStream_t st) {
   auto grid_for = [](int64_t work, int cap) { return (unsigned)(work < cap ? (work > 0 ? work : 1) : cap); };
   constexpr int TS = CLIP_STREAM_THREADS, TT = CLIP_TILE_THREADS;
   if (!a.dim0 && !a.two_d) {
-    hipLaunchKernelGGL((k_clip_rows<ELEM, BF16, RHT>), dim3(grid_for((rows_out * nkb + TS - 1) / TS, CLIP_STREAM_GROUPS)),
-                       dim3(TS), 0, st, a.src, a.ld_src, rows_out, nkb, a.mask, a.scale_mode, a.count);
+    const unsigned grid = grid_for((rows_out * nkb + TS - 1) / TS, CLIP_ROWS_GROUPS);
+    if (rows_out * nkb < (1ll << 32) - (int64_t)CLIP_ROWS_GROUPS * TS)
+      hipLaunchKernelGGL((k_clip_rows<ELEM, BF16, RHT, uint32_t>), dim3(grid), dim3(TS), 0, st, a.src, a.ld_src,
+                         rows_out, nkb, a.mask, a.scale_mode, a.count);
+    else
+      hipLaunchKernelGGL((k_clip_rows<ELEM, BF16, RHT, int64_t>), dim3(grid), dim3(TS), 0, st, a.src, a.ld_src,
+                         rows_out, nkb, a.mask, a.scale_mode, a.count);
   } else if (!a.dim0) {
     hipLaunchKernelGGL((k_clip_rows_2d<ELEM, BF16, RHT>),
                        dim3(grid_for(rows_out / 32 * ((nkb + TT / 32 - 1) / (TT / 32)), CLIP_TILE_GROUPS)), dim3(TT),
